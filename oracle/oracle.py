@@ -1,0 +1,282 @@
+"""Plain fp64 CPU oracle for the batched composite multi-LoRA apply.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The library
+path never calls it, and it shares no code with the library: no kernels, no
+headers, no helpers, no constants.  It is slow on purpose; every function is
+the plainest statement of what the pages define.
+
+What is computed (pages cited by title and section):
+
+* DyMerge-LoRA, section 3.1 (M1): a composite update is the weighted sum of
+  low-rank adapter updates, Delta W = sum_i alpha_i B_i A_i^T, with alpha fixed
+  per request (static composition) or per token (dynamic composition).
+  Evaluated after the merge point, token t receives
+      y_t = y_base_t + sum_{(i, alpha) in C_t} alpha * B_i (A_i^T x_t).
+* ELORA, section III-A, Eq. 1 / Eq. 2: the single-adapter case W' = W + A B.
+  ELORA writes the update as A_t B_t with A_t of size d x r; in the
+  orientation used here that is B_i (d_out x r) times A_i^T (r x d_in).
+* LoRAForge, approach (1): the retained-rank contract.  Each adapter of a
+  module keeps an ordered factor prefix and an effective rank k_m; only the
+  first k_m rank directions take part and a padded store holds zeros beyond.
+* DyMerge-LoRA, section 4.3: token-adapter pairs become mapping tuples and are
+  reordered by adapter (LoRA) id so one adapter's tokens are contiguous.  The
+  tuple's fields are not spelled out on the page; they are read here as
+  (token, adapter, alpha, out-slot), with the out-slot being the pair's
+  position inside its token's composite once that composite is ordered by
+  adapter id, and ties in the reorder broken by (token, slot).
+
+Storage conventions (shared by every consumer, stated not imported):
+pools are rank-major, ``A_t[a, j, :]`` = row j of A_a^T (length d_in) and
+``B_t[a, j, :]`` = row j of B_a^T (length d_out); bf16 arrays arrive as uint16
+bit patterns and are widened exactly; composites are a group CSR
+(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha).
+
+Status codes returned by :func:`validate` use the same numbering as the
+library's documented status codes so that the two can be compared.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+OK = 0
+EINVAL = -1
+ENOSPC = -3
+EUNSUPPORTED = -4
+
+
+# ---------------------------------------------------------------------------
+# input handling
+# ---------------------------------------------------------------------------
+
+def widen(a: np.ndarray) -> np.ndarray:
+    """float64 view of an input array.  uint16 arrays are bfloat16 bit
+    patterns: the 16 bits are the top half of an IEEE float32, so the value is
+    exact once placed there."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def validate(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+             n_tokens: int, n_adapters: int, max_pairs_per_group: int = 64,
+             max_tuples: Optional[int] = None) -> int:
+    """Status of a composite table.
+
+    EINVAL: CSR pointers that do not start at 0, end at the token / pair
+    count, or decrease; an adapter id outside [0, n_adapters); a non-finite
+    alpha; the same adapter twice in one composite.  EUNSUPPORTED: a group
+    with more than ``max_pairs_per_group`` pairs.  ENOSPC: more tuples than
+    ``max_tuples``.  EINVAL outranks EUNSUPPORTED, which outranks ENOSPC."""
+    gt = [int(v) for v in group_tok_ptr]
+    gp = [int(v) for v in group_pair_ptr]
+    ad = [int(v) for v in pair_adapter]
+    al = [float(v) for v in np.asarray(pair_alpha, dtype=np.float32)]
+    if n_tokens < 0 or n_adapters < 1 or len(gt) < 1 or len(gt) != len(gp):
+        return EINVAL
+    if gt[0] != 0 or gt[-1] != n_tokens or gp[0] != 0 or gp[-1] != len(ad):
+        return EINVAL
+    if len(al) != len(ad):
+        return EINVAL
+    for g in range(len(gt) - 1):
+        if gt[g + 1] < gt[g] or gp[g + 1] < gp[g]:
+            return EINVAL
+    for a in ad:
+        if a < 0 or a >= n_adapters:
+            return EINVAL
+    for w in al:
+        if not math.isfinite(w):
+            return EINVAL
+    for g in range(len(gt) - 1):
+        ids = ad[gp[g]:gp[g + 1]]
+        if len(set(ids)) != len(ids):
+            return EINVAL
+    for g in range(len(gt) - 1):
+        if gp[g + 1] - gp[g] > max_pairs_per_group:
+            return EUNSUPPORTED
+    if max_tuples is not None:
+        P = sum((gt[g + 1] - gt[g]) * (gp[g + 1] - gp[g]) for g in range(len(gt) - 1))
+        if P > max_tuples:
+            return ENOSPC
+    return OK
+
+
+def canonical_composite(group_pair_ptr, pair_adapter, pair_alpha, g: int):
+    """Pairs of group g ordered by adapter id; position in this list is the
+    pair's out-slot.  Returns a list of (adapter, alpha) with alpha kept as
+    its float32 value."""
+    lo, hi = int(group_pair_ptr[g]), int(group_pair_ptr[g + 1])
+    pairs = [(int(pair_adapter[q]), np.float32(pair_alpha[q])) for q in range(lo, hi)]
+    return sorted(pairs, key=lambda p: p[0])
+
+
+def group_of_token(group_tok_ptr) -> np.ndarray:
+    T = int(group_tok_ptr[-1])
+    owner = np.empty(T, dtype=np.int64)
+    for g in range(len(group_tok_ptr) - 1):
+        owner[int(group_tok_ptr[g]):int(group_tok_ptr[g + 1])] = g
+    return owner
+
+
+# ---------------------------------------------------------------------------
+# mapping stage: tuples reordered by adapter id (DyMerge-LoRA, section 4.3)
+# ---------------------------------------------------------------------------
+
+def plan(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha) -> Dict[str, np.ndarray]:
+    """Expand composites into (token, adapter, alpha, slot) tuples and reorder
+    them by adapter id.
+
+    Tuples are first listed token-major (token ascending, slot ascending) and
+    then stably sorted by adapter id, which makes the order the total order on
+    (adapter, token, slot).  Also returns the segment table (one entry per
+    adapter that owns tuples, ascending) and the per-token index
+    (``tok_tuple[tok_ptr[t] + s]`` is the sorted position of token t's slot s).
+    """
+    T = int(group_tok_ptr[-1])
+    tokens, adapters, alphas, slots = [], [], [], []
+    n_per_token = np.zeros(T, dtype=np.int64)
+    owner = group_of_token(group_tok_ptr)
+    for t in range(T):
+        comp = canonical_composite(group_pair_ptr, pair_adapter, pair_alpha, int(owner[t]))
+        n_per_token[t] = len(comp)
+        for s, (a, w) in enumerate(comp):
+            tokens.append(t)
+            adapters.append(a)
+            alphas.append(w)
+            slots.append(s)
+    tokens = np.array(tokens, dtype=np.int32)
+    adapters = np.array(adapters, dtype=np.int32)
+    alphas = np.array(alphas, dtype=np.float32)
+    slots = np.array(slots, dtype=np.int32)
+    order = np.argsort(adapters, kind="stable")
+    tup_token = tokens[order]
+    tup_adapter = adapters[order]
+    tup_alpha = alphas[order]
+    tup_slot = slots[order]
+    P = len(order)
+
+    seg_adapter, seg_begin = [], []
+    for p in range(P):
+        if p == 0 or tup_adapter[p] != tup_adapter[p - 1]:
+            seg_adapter.append(int(tup_adapter[p]))
+            seg_begin.append(p)
+    seg_begin.append(P)
+
+    tok_ptr = np.zeros(T + 1, dtype=np.int32)
+    tok_ptr[1:] = np.cumsum(n_per_token)
+    tok_tuple = np.full(P, -1, dtype=np.int32)
+    for p in range(P):
+        tok_tuple[tok_ptr[tup_token[p]] + tup_slot[p]] = p
+    return {
+        "tup_token": tup_token, "tup_adapter": tup_adapter,
+        "tup_alpha": tup_alpha, "tup_slot": tup_slot,
+        "seg_adapter": np.array(seg_adapter, dtype=np.int32),
+        "seg_begin": np.array(seg_begin, dtype=np.int32),
+        "tok_ptr": tok_ptr, "tok_tuple": tok_tuple,
+    }
+
+
+# ---------------------------------------------------------------------------
+# the apply, straight from the definition
+# ---------------------------------------------------------------------------
+
+def effective_rank(k, a: int, r_max: int) -> int:
+    """k_m of adapter a (LoRAForge retained-rank contract); r_max if absent."""
+    return r_max if k is None else int(k[a])
+
+
+def apply(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+          A_t, B_t, k, x, y_base):
+    """y_t = y_base_t + sum over token t's composite, in slot order, of
+    alpha * B_a[:, :k_a] (A_a[:, :k_a]^T x_t), all in float64.
+
+    Returns (y, delta) as float64 arrays of shape [T, d_out]."""
+    T = int(group_tok_ptr[-1])
+    r_max = A_t.shape[1]
+    d_out = B_t.shape[2]
+    delta = np.zeros((T, d_out), dtype=np.float64)
+    owner = group_of_token(group_tok_ptr)
+    for t in range(T):
+        xt = widen(x[t])
+        for a, w in canonical_composite(group_pair_ptr, pair_adapter, pair_alpha, int(owner[t])):
+            kk = effective_rank(k, a, r_max)
+            if kk == 0:
+                continue
+            A_a_T = widen(A_t[a, :kk, :])      # A_a^T restricted to the retained prefix
+            B_a_T = widen(B_t[a, :kk, :])      # B_a^T restricted likewise
+            z = A_a_T @ xt                     # A_a^T x_t   (length k)
+            delta[t] += float(w) * (B_a_T.T @ z)   # alpha * B_a z
+    return widen(y_base) + delta, delta
+
+
+def shrink(pl: Dict[str, np.ndarray], A_t, k, x) -> np.ndarray:
+    """z_p = A_{a_p}[:, :k]^T x_{t_p} for every tuple p, in sorted-tuple order;
+    float64 [P, r_max] with zeros beyond each adapter's effective rank.
+    alpha is not applied."""
+    P = pl["tup_token"].shape[0]
+    r_max = A_t.shape[1]
+    z = np.zeros((P, r_max), dtype=np.float64)
+    for p in range(P):
+        a, t = int(pl["tup_adapter"][p]), int(pl["tup_token"][p])
+        kk = effective_rank(k, a, r_max)
+        if kk:
+            z[p, :kk] = widen(A_t[a, :kk, :]) @ widen(x[t])
+    return z
+
+
+def expand(pl: Dict[str, np.ndarray], B_t, k, z, y_base) -> np.ndarray:
+    """y_t = y_base_t + sum over token t's slots s of alpha * B_a[:, :k] z_(t,s),
+    where z is given per sorted tuple.  float64 [T, d_out]."""
+    T = pl["tok_ptr"].shape[0] - 1
+    r_max = B_t.shape[1]
+    y = widen(y_base).copy()
+    z = np.asarray(z, dtype=np.float64)
+    for t in range(T):
+        acc = np.zeros(y.shape[1], dtype=np.float64)
+        for i in range(int(pl["tok_ptr"][t]), int(pl["tok_ptr"][t + 1])):
+            p = int(pl["tok_tuple"][i])
+            a = int(pl["tup_adapter"][p])
+            kk = effective_rank(k, a, r_max)
+            if kk:
+                acc += float(pl["tup_alpha"][p]) * (widen(B_t[a, :kk, :]).T @ z[p, :kk])
+        y[t] += acc
+    return y
+
+
+def apply_rows(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+               A_t, B_t, k, x, y_base, rows, cols=None):
+    """The apply for selected tokens (and optionally selected output columns)
+    only: float64 [len(rows), len(cols) or d_out].  Same arithmetic as
+    :func:`apply`, used to sample outputs of full-size problems."""
+    r_max = A_t.shape[1]
+    owner = group_of_token(group_tok_ptr)
+    cols = slice(None) if cols is None else np.asarray(cols)
+    out = []
+    for t in rows:
+        t = int(t)
+        xt = widen(x[t])
+        acc = None
+        for a, w in canonical_composite(group_pair_ptr, pair_adapter, pair_alpha, int(owner[t])):
+            kk = effective_rank(k, a, r_max)
+            if kk == 0:
+                continue
+            z = widen(A_t[a, :kk, :]) @ xt
+            term = float(w) * (widen(B_t[a, :kk, :][:, cols]).T @ z)
+            acc = term if acc is None else acc + term
+        base = widen(y_base[t][cols])
+        out.append(base + (acc if acc is not None else 0.0))
+    return np.array(out)
+
+
+# ---------------------------------------------------------------------------
+# sizes (ELORA, section III-A: adapter size next to the base weight)
+# ---------------------------------------------------------------------------
+
+def adapter_fraction(d_in: int, d_out: int, r: int) -> float:
+    """Values of one rank-r adapter (A: d_in x r, B: d_out x r) as a fraction
+    of the d_out x d_in base weight it modifies."""
+    return (d_in + d_out) * r / (d_in * d_out)

@@ -1,0 +1,391 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes the oracle module ``O`` and raises
+AssertionError if the oracle disagrees with the fact.  The same functions run
+against the real oracle (tests/test_oracle_pins.py) and against deliberately
+broken copies of it (tests/test_oracle_mutants.py), which shows that a
+plausible mistake anywhere in the oracle is caught by at least one pin.
+"""
+import json
+import os
+
+import numpy as np
+import torch
+
+from tenant_composite_lora_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+_MODULE_K = object()
+
+
+def _apply(O, c, m, x, yb, k=_MODULE_K):
+    kk = m.k if k is _MODULE_K else k
+    return O.apply(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha,
+                   m.A_t, m.B_t, kk, x, yb)
+
+
+def _plan(O, c):
+    return O.plan(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha)
+
+
+def _f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _rel(a, b):
+    den = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / den) if a.size else 0.0
+
+
+# ---------------------------------------------------------------------------
+# X1: ELORA worked example (single LoRA, d = 2, r = 1), exact small integers
+# ---------------------------------------------------------------------------
+
+def pin_x1_elora_example(O):
+    g = json.load(open(os.path.join(GOLDEN, "elora_worked_example.json")))
+    WK = np.array(g["W_K"], dtype=np.float64)
+    h = np.array(g["h"], dtype=np.float64)
+    yb = (WK @ h)[None, :]
+    assert np.array_equal(yb[0], np.array(g["K_base"], dtype=np.float64))
+    pool_A, pool_B = [], []
+    for ad in g["adapters"]:
+        A_page = np.array(ad["A_page"], dtype=np.float64)    # d x r
+        B_page = np.array(ad["B_page"], dtype=np.float64)    # r x d
+        pool_A.append(B_page)          # A_t[a] = A_a^T = B_page   (r x d_in)
+        pool_B.append(A_page.T)        # B_t[a] = B_a^T = A_page^T (r x d_out)
+    A_t = np.stack(pool_A).astype(np.float32)
+    B_t = np.stack(pool_B).astype(np.float32)
+    x = h[None, :].astype(np.float32)
+    for i, ad in enumerate(g["adapters"]):
+        c = W.csr_from_token_lists([[i]], [[1.0]], len(pool_A))
+        y, _ = O.apply(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha,
+                       A_t, B_t, None, x, yb.astype(np.float32))
+        assert np.array_equal(y[0], np.array(ad["K"], dtype=np.float64)), (ad["name"], y[0])
+    names = [a["name"] for a in g["adapters"]]
+    dc = g["derived_composite"]
+    ids = [names.index(n) for n, _ in dc["pairs"]]
+    als = [w for _, w in dc["pairs"]]
+    c = W.csr_from_token_lists([ids], [als], len(pool_A))
+    y, _ = O.apply(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha,
+                   A_t, B_t, None, x, yb.astype(np.float32))
+    assert np.array_equal(y[0], np.array(dc["K"], dtype=np.float64)), y[0]
+
+
+# ---------------------------------------------------------------------------
+# X2: composite = dense pre-merged Delta W (DyMerge-LoRA section 3.1, M1)
+# ---------------------------------------------------------------------------
+
+def _dense_delta_w(c, m, t):
+    """Delta W of token t built the pre-merge way: sum_i alpha_i B_i A_i^T as
+    dense d_out x d_in matrices, then applied to x in one product."""
+    g = int(np.searchsorted(c.group_tok_ptr, t, side="right") - 1)
+    A = _f64(m.A_t)
+    B = _f64(m.B_t)
+    dW = np.zeros((m.d_out, m.d_in))
+    for q in range(int(c.group_pair_ptr[g]), int(c.group_pair_ptr[g + 1])):
+        a = int(c.pair_adapter[q])
+        k = m.r_max if m.k is None else int(m.k[a])
+        Bi = B[a, :k, :].T            # d_out x k
+        Ai = A[a, :k, :].T            # d_in  x k
+        dW += float(np.float32(c.pair_alpha[q])) * (Bi @ Ai.T)
+    return dW
+
+
+def pin_x2_dense_premerge(O):
+    cases = [W.config1(0),
+             W.random_case(3, T=9, N=5, d_in=24, d_out=40, r_max=4, max_pairs=4),
+             W.random_case(4, T=7, N=6, d_in=32, d_out=16, r_max=8, max_pairs=5,
+                           with_k=True, tokens_per_group=3, empty_frac=0.2)]
+    for wl in cases:
+        c, m = wl.composites, wl.modules[0]
+        y, delta = _apply(O, c, m, wl.x[0], wl.y_base[0])
+        X = _f64(wl.x[0])
+        ref = np.stack([_dense_delta_w(c, m, t) @ X[t] for t in range(c.n_tokens)])
+        assert _rel(delta, ref) < 1e-12, (wl.name, _rel(delta, ref))
+        assert _rel(y, _f64(wl.y_base[0]) + ref) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# X3: one adapter, alpha = 1, is textbook LoRA (ELORA Eq. 1)
+# ---------------------------------------------------------------------------
+
+def pin_x3_textbook_lora(O):
+    wl = W.random_case(5, T=6, N=3, d_in=48, d_out=20, r_max=8, max_pairs=1, dtype=W.F32)
+    m = wl.modules[0]
+    T = wl.n_tokens
+    a = 1
+    c = W.csr_from_token_lists([[a]] * T, [[1.0]] * T, 3)
+    y, _ = _apply(O, c, m, wl.x[0], wl.y_base[0])
+    x = torch.from_numpy(_f64(wl.x[0]))
+    A_i_T = torch.from_numpy(_f64(m.A_t)[a])       # r x d_in, the down projection weight
+    B_i = torch.from_numpy(_f64(m.B_t)[a].T.copy())   # d_out x r, the up projection weight
+    ref = torch.from_numpy(_f64(wl.y_base[0])) + torch.nn.functional.linear(
+        torch.nn.functional.linear(x, A_i_T), B_i)
+    assert _rel(y, ref.numpy()) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# X4: linearity in alpha; X5: alpha = 0 and k = 0 are no-ops
+# ---------------------------------------------------------------------------
+
+def pin_x4_linearity(O):
+    wl = W.random_case(6, T=10, N=6, d_in=32, d_out=24, r_max=8, max_pairs=4, with_k=True)
+    c, m = wl.composites, wl.modules[0]
+    rng = np.random.default_rng(11)
+    # multiples of 1/64 below 1: sums and scalings stay exact in float32
+    al = (rng.integers(0, 64, c.n_pairs) / 64).astype(np.float32)
+    be = (rng.integers(0, 64, c.n_pairs) / 64).astype(np.float32)
+
+    def delta(alpha):
+        cc = W.Composites(c.n_tokens, c.n_adapters, c.group_tok_ptr, c.group_pair_ptr,
+                          c.pair_adapter, alpha.astype(np.float32))
+        return _apply(O, cc, m, wl.x[0], wl.y_base[0])[1]
+
+    d_a, d_b, d_ab = delta(al), delta(be), delta(al + be)
+    assert _rel(d_ab, d_a + d_b) < 1e-12
+    assert _rel(delta(3 * al), 3 * d_a) < 1e-12
+    assert np.max(np.abs(d_a)) > 0
+
+
+def pin_x5_noop(O):
+    wl = W.random_case(7, T=8, N=4, d_in=16, d_out=16, r_max=4, max_pairs=3)
+    c, m = wl.composites, wl.modules[0]
+    zero = W.Composites(c.n_tokens, c.n_adapters, c.group_tok_ptr, c.group_pair_ptr,
+                        c.pair_adapter, np.zeros_like(c.pair_alpha))
+    y, d = _apply(O, zero, m, wl.x[0], wl.y_base[0])
+    assert np.all(d == 0) and np.array_equal(y, _f64(wl.y_base[0]))
+    y, d = _apply(O, c, m, wl.x[0], wl.y_base[0], k=np.zeros(4, dtype=np.int32))
+    assert np.all(d == 0) and np.array_equal(y, _f64(wl.y_base[0]))
+    y, d = _apply(O, c, m, wl.x[0], wl.y_base[0])
+    assert np.max(np.abs(d)) > 0
+    empty = W.csr_from_token_lists([[]] * c.n_tokens, [[]] * c.n_tokens, 4)
+    y, d = _apply(O, empty, m, wl.x[0], wl.y_base[0])
+    assert np.all(d == 0)
+
+
+# ---------------------------------------------------------------------------
+# X6: truncating to k_m equals zero-padding and equals a dense rank-k copy
+#     (LoRAForge retained-rank contract, approach (1))
+# ---------------------------------------------------------------------------
+
+def pin_x6_truncation(O):
+    wl = W.random_case(8, T=12, N=6, d_in=40, d_out=24, r_max=8, max_pairs=4)
+    c, m = wl.composites, wl.modules[0]
+    rng = np.random.default_rng(12)
+    k = rng.integers(0, 9, size=6).astype(np.int32)
+    y_k, d_k = _apply(O, c, m, wl.x[0], wl.y_base[0], k=k)
+    keep = (np.arange(8)[None, :] < k[:, None])[:, :, None]
+    A0 = np.where(keep, _f64(m.A_t), 0.0)
+    B0 = np.where(keep, _f64(m.B_t), 0.0)
+    y_pad, d_pad = O.apply(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha,
+                           A0, B0, None, wl.x[0], wl.y_base[0])
+    assert _rel(d_k, d_pad) < 1e-12
+    # dense rank-k copy: explicit rank-k factors per adapter, no padding at all
+    X = _f64(wl.x[0])
+    ref = np.zeros_like(d_k)
+    owner = np.repeat(np.arange(c.n_groups), np.diff(c.group_tok_ptr))
+    for t in range(c.n_tokens):
+        g = owner[t]
+        for q in range(int(c.group_pair_ptr[g]), int(c.group_pair_ptr[g + 1])):
+            a = int(c.pair_adapter[q])
+            Ai = _f64(m.A_t)[a, :k[a], :].T     # d_in x k
+            Bi = _f64(m.B_t)[a, :k[a], :].T     # d_out x k
+            ref[t] += float(c.pair_alpha[q]) * (Bi @ (Ai.T @ X[t]))
+    assert _rel(d_k, ref) < 1e-12
+    # and k = r_max is the untruncated apply
+    y_full, _ = _apply(O, c, m, wl.x[0], wl.y_base[0], k=np.full(6, 8, np.int32))
+    y_none, _ = _apply(O, c, m, wl.x[0], wl.y_base[0], k=None)
+    assert np.array_equal(y_full, y_none)
+
+
+# ---------------------------------------------------------------------------
+# X7: the merged update of a composite has rank <= sum of its ranks
+#     (DyMerge-LoRA section 3.1: merging k rank-r adapters gives rank up to k*r)
+# ---------------------------------------------------------------------------
+
+def pin_x7_rank_bound(O):
+    rng = np.random.default_rng(13)
+    d = 40
+    wl = W.random_case(9, T=1, N=6, d_in=d, d_out=d, r_max=3, max_pairs=1, dtype=W.F32)
+    m = wl.modules[0]
+    for ids in ([0], [1, 4], [0, 2, 5], [0, 1, 2, 3, 4, 5]):
+        al = rng.random(len(ids)).astype(np.float32) + 0.1
+        # one group covering d tokens with x = identity: token j receives column j
+        c = W.Composites(d, 6, np.array([0, d], np.int32), np.array([0, len(ids)], np.int32),
+                         np.array(ids, np.int32), al)
+        eye = np.eye(d, dtype=np.float32)
+        _, delta = O.apply(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha,
+                           m.A_t, m.B_t, None, eye, np.zeros((d, d), np.float32))
+        dW = delta.T                     # column j = Delta W e_j
+        rank = np.linalg.matrix_rank(dW, tol=1e-9)
+        assert rank <= 3 * len(ids)
+        assert rank == min(3 * len(ids), d)   # random factors: the bound is attained
+        ref = np.zeros((d, d))
+        for a, w in zip(ids, al):
+            ref += float(w) * (_f64(m.B_t)[a].T @ _f64(m.A_t)[a])
+        assert _rel(dW, ref) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# X8: mapping stage — hand-worked example and brute force on random inputs
+# ---------------------------------------------------------------------------
+
+def pin_x8_mapping(O):
+    g = json.load(open(os.path.join(GOLDEN, "mapping_hand_example.json")))
+    ads = [[a for a, _ in row] for row in g["token_pairs"]]
+    als = [[w for _, w in row] for row in g["token_pairs"]]
+    c = W.csr_from_token_lists(ads, als, g["n_adapters"])
+    pl = _plan(O, c)
+    for key, val in g["expected"].items():
+        got = pl[key]
+        want = np.array(val, dtype=got.dtype)
+        assert np.array_equal(got, want), (key, got, want)
+    for seed in range(4):
+        wl = W.random_case(20 + seed, T=13, N=7, d_in=8, d_out=8, r_max=2, max_pairs=5,
+                           tokens_per_group=1 + seed % 3, empty_frac=0.15)
+        _check_plan_brute(_plan(O, wl.composites), wl.composites)
+
+
+def _check_plan_brute(pl, c):
+    """Position of each tuple = number of tuples with a smaller
+    (adapter, token, slot) key, computed by direct counting."""
+    T = c.n_tokens
+    owner = np.repeat(np.arange(c.n_groups), np.diff(c.group_tok_ptr))
+    tuples = []
+    for t in range(T):
+        g = owner[t]
+        ids = c.pair_adapter[c.group_pair_ptr[g]:c.group_pair_ptr[g + 1]]
+        w = c.pair_alpha[c.group_pair_ptr[g]:c.group_pair_ptr[g + 1]]
+        for q in range(len(ids)):
+            slot = int(np.sum(ids < ids[q]))          # rank among the composite's ids
+            tuples.append((int(ids[q]), t, slot, np.float32(w[q])))
+    P = len(tuples)
+    assert pl["tup_token"].shape[0] == P
+    for (a, t, s, w) in tuples:
+        pos = sum(1 for (a2, t2, s2, _) in tuples if (a2, t2, s2) < (a, t, s))
+        assert pl["tup_adapter"][pos] == a and pl["tup_token"][pos] == t
+        assert pl["tup_slot"][pos] == s
+        assert pl["tup_alpha"][pos].view(np.uint32) == w.view(np.uint32)
+    counts = {}
+    for (a, _, _, _) in tuples:
+        counts[a] = counts.get(a, 0) + 1
+    assert pl["seg_adapter"].tolist() == sorted(counts)
+    assert np.diff(pl["seg_begin"]).tolist() == [counts[a] for a in sorted(counts)]
+    assert pl["seg_begin"][0] == 0 and pl["seg_begin"][-1] == P
+    n_t = np.array([np.sum(np.array([tt for (_, tt, _, _) in tuples]) == t) for t in range(T)])
+    assert pl["tok_ptr"].tolist() == [0] + np.cumsum(n_t).tolist()
+    for t in range(T):
+        for s in range(n_t[t]):
+            p = pl["tok_tuple"][pl["tok_ptr"][t] + s]
+            assert pl["tup_token"][p] == t and pl["tup_slot"][p] == s
+
+
+# ---------------------------------------------------------------------------
+# X9: adapter size next to the base weight (ELORA section III-A size example)
+# ---------------------------------------------------------------------------
+
+def pin_x9_adapter_fraction(O):
+    d, r = 4096, 32
+    assert d * d == 16_777_216                      # "about 16.8 million values"
+    assert 2 * d * r == 262_144                     # "about 260 thousand values"
+    f = O.adapter_fraction(d, d, r)
+    assert f == 0.015625
+    assert abs(round(100 * f, 1) - 1.6) < 1e-9      # "about 1.6 %"
+
+
+# ---------------------------------------------------------------------------
+# X10: permutation invariance
+# ---------------------------------------------------------------------------
+
+def pin_x10_permutation(O):
+    wl = W.random_case(10, T=11, N=8, d_in=24, d_out=24, r_max=4, max_pairs=5)
+    c, m = wl.composites, wl.modules[0]
+    y, _ = _apply(O, c, m, wl.x[0], wl.y_base[0])
+    pl = _plan(O, c)
+    rng = np.random.default_rng(14)
+    # shuffle the pairs inside every composite: nothing changes, bit for bit
+    ad, al = c.pair_adapter.copy(), c.pair_alpha.copy()
+    for g in range(c.n_groups):
+        lo, hi = c.group_pair_ptr[g], c.group_pair_ptr[g + 1]
+        perm = rng.permutation(hi - lo) + lo
+        ad[lo:hi], al[lo:hi] = c.pair_adapter[perm], c.pair_alpha[perm]
+    c2 = W.Composites(c.n_tokens, c.n_adapters, c.group_tok_ptr, c.group_pair_ptr, ad, al)
+    y2, _ = _apply(O, c2, m, wl.x[0], wl.y_base[0])
+    assert np.array_equal(y, y2)
+    pl2 = _plan(O, c2)
+    for key in pl:
+        assert np.array_equal(pl[key], pl2[key]), key
+    # permute tokens: rows permute
+    tperm = rng.permutation(c.n_tokens)
+    rows_a = [c.pair_adapter[c.group_pair_ptr[t]:c.group_pair_ptr[t + 1]].tolist() for t in tperm]
+    rows_w = [c.pair_alpha[c.group_pair_ptr[t]:c.group_pair_ptr[t + 1]].tolist() for t in tperm]
+    c3 = W.csr_from_token_lists(rows_a, rows_w, c.n_adapters)
+    y3, _ = O.apply(c3.group_tok_ptr, c3.group_pair_ptr, c3.pair_adapter, c3.pair_alpha,
+                    m.A_t, m.B_t, m.k, wl.x[0][tperm], wl.y_base[0][tperm])
+    assert np.array_equal(y3, y[tperm])
+
+
+# ---------------------------------------------------------------------------
+# shrink / expand split agrees with the one-pass apply; sampled rows agree
+# ---------------------------------------------------------------------------
+
+def pin_split_and_rows(O):
+    for wl in (W.config1(0),
+               W.random_case(15, T=9, N=5, d_in=32, d_out=48, r_max=8, max_pairs=4,
+                             with_k=True, tokens_per_group=2, empty_frac=0.2)):
+        c, m = wl.composites, wl.modules[0]
+        y, _ = _apply(O, c, m, wl.x[0], wl.y_base[0])
+        pl = _plan(O, c)
+        z = O.shrink(pl, m.A_t, m.k, wl.x[0])
+        # z is A^T x, checked against a direct product per tuple
+        A = _f64(m.A_t)
+        X = _f64(wl.x[0])
+        for p in range(z.shape[0]):
+            a, t = pl["tup_adapter"][p], pl["tup_token"][p]
+            kk = m.r_max if m.k is None else m.k[a]
+            want = np.zeros(m.r_max)
+            want[:kk] = A[a, :kk] @ X[t]
+            assert _rel(z[p], want) < 1e-12 or np.all(want == 0) and np.all(z[p] == 0)
+        y2 = O.expand(pl, m.B_t, m.k, z, wl.y_base[0])
+        assert _rel(y2 - _f64(wl.y_base[0]), y - _f64(wl.y_base[0])) < 1e-12
+        rows = [0, c.n_tokens - 1, c.n_tokens // 2]
+        cols = [0, 3, m.d_out - 1]
+        ys = O.apply_rows(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha,
+                          m.A_t, m.B_t, m.k, wl.x[0], wl.y_base[0], rows, cols)
+        assert _rel(ys, y[np.ix_(rows, cols)]) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# validation codes
+# ---------------------------------------------------------------------------
+
+def pin_validation(O):
+    def v(tp, pp, ad, al, T=3, N=4, **kw):
+        return O.validate(np.array(tp), np.array(pp), np.array(ad, np.int32),
+                          np.array(al, np.float32), T, N, **kw)
+    good = ([0, 1, 3], [0, 2, 3], [0, 1, 3], [0.5, 0.5, 1.0])
+    assert v(*good) == O.OK
+    assert v([0, 1, 2], [0, 2, 3], [0, 1, 3], [.5, .5, 1.]) == O.EINVAL        # tokens != T
+    assert v([0, 2, 1], [0, 2, 3], [0, 1, 3], [.5, .5, 1.]) == O.EINVAL        # decreasing
+    assert v([0, 1, 3], [0, 2, 2], [0, 1, 3], [.5, .5, 1.]) == O.EINVAL        # pairs != n
+    assert v([0, 1, 3], [0, 2, 3], [0, 4, 3], [.5, .5, 1.]) == O.EINVAL        # id >= N
+    assert v([0, 1, 3], [0, 2, 3], [0, -1, 3], [.5, .5, 1.]) == O.EINVAL       # id < 0
+    assert v([0, 1, 3], [0, 2, 3], [1, 1, 3], [.5, .5, 1.]) == O.EINVAL        # duplicate
+    assert v([0, 1, 3], [0, 2, 3], [0, 1, 3], [.5, np.nan, 1.]) == O.EINVAL    # nan
+    assert v([0, 1, 3], [0, 2, 3], [0, 1, 3], [.5, np.inf, 1.]) == O.EINVAL    # inf
+    assert v(*good, max_pairs_per_group=1) == O.EUNSUPPORTED
+    assert v(*good, max_tuples=3) == O.ENOSPC                                  # P = 2 + 2
+    assert v(*good, max_tuples=4) == O.OK
+    assert v([0, 1, 3], [0, 2, 3], [1, 1, 3], [.5, .5, 1.], max_tuples=0) == O.EINVAL
+    assert v([0], [0], [], [], T=0) == O.OK                                    # empty batch
+
+
+ALL_PINS = [pin_x1_elora_example, pin_x2_dense_premerge, pin_x3_textbook_lora,
+            pin_x4_linearity, pin_x5_noop, pin_x6_truncation, pin_x7_rank_bound,
+            pin_x8_mapping, pin_x9_adapter_fraction, pin_x10_permutation,
+            pin_split_and_rows, pin_validation]
