@@ -1,0 +1,267 @@
+"""Benchmark of the composite multi-LoRA apply on one MI355X.
+
+One step = one pass of the whole path over one batch: the mapping stage
+(tcl_plan_map's kernel: validation, canonical slots, counting sort by adapter
+id, token index, work list) followed by the fused apply (shrink + expand) of
+every module of the workload.  Inputs are synthetic, drawn by
+tenant_composite_lora_amd.workloads, and resident in HBM before timing starts.
+Each step uses the next of R replicas of {adapter pools, x, y} so that the
+working set of consecutive steps exceeds the 256 MB Infinity Cache and the
+adapter bytes really come from HBM.
+
+Default workload: 32 decode tokens, each a composite of 3 distinct adapters
+(alpha = softmax of N(0,1) logits), on a 4096 -> 4096 projection with 64
+rank-8 bf16 adapters.
+
+Prints one JSON line.  Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--eager]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "composite-LoRA apply tokens/s + achieved HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def algorithmic_bytes(wl) -> int:
+    """Bytes the method must move for one step: every touched adapter's
+    retained rows of A and B once, x once, y read and written once, and the
+    16-byte tuple records of the plan once."""
+    c = wl.composites
+    used = np.unique(c.pair_adapter[:c.n_pairs]) if c.n_pairs else np.zeros(0, np.int64)
+    # only adapters that own at least one tuple count
+    owner_tokens = np.diff(c.group_tok_ptr)
+    pair_tokens = np.repeat(owner_tokens, np.diff(c.group_pair_ptr))
+    used = np.unique(c.pair_adapter[pair_tokens > 0]) if c.n_pairs else used
+    T = c.n_tokens
+    total = 0
+    for mi, m in enumerate(wl.modules):
+        e_w = 2 if m.A_t.dtype == np.uint16 else 4
+        e_x = 2 if wl.x[mi].dtype == np.uint16 else 4
+        k = np.full(m.A_t.shape[0], m.r_max) if m.k is None else m.k
+        total += int(np.sum(k[used])) * (m.d_in + m.d_out) * e_w
+        total += T * m.d_in * e_x + 2 * T * m.d_out * 4
+    total += c.n_tuples() * 16
+    return total
+
+
+def algorithmic_flops(wl) -> int:
+    c = wl.composites
+    owner_tokens = np.diff(c.group_tok_ptr)
+    pair_tokens = np.repeat(owner_tokens, np.diff(c.group_pair_ptr))
+    total = 0
+    for m in wl.modules:
+        k = np.full(m.A_t.shape[0], m.r_max) if m.k is None else m.k
+        total += int(np.sum(pair_tokens * k[c.pair_adapter])) * 2 * (m.d_in + m.d_out)
+    return total
+
+
+def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle timed on this host: the whole batch (mapping stage and
+    the apply of every module) repeated until ``budget_s`` seconds of work."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    c = wl.composites
+    reps, t_used = 0, 0.0
+    sample_tokens = c.n_tokens
+    with threadpool_limits(limits=1):
+        while t_used < budget_s and reps < 1000:
+            t0 = time.perf_counter()
+            O.plan(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha)
+            for mi, m in enumerate(wl.modules):
+                O.apply(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha,
+                        m.A_t, m.B_t, m.k, wl.x[mi], wl.y_base[mi])
+            t_used += time.perf_counter() - t0
+            reps += 1
+    return {"value": sample_tokens * reps / t_used, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"whole batch ({sample_tokens} tokens, all modules, mapping + apply) "
+                      f"repeated {reps}x, {t_used:.1f} s, fp64 numpy, 1 BLAS thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=256)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--eager", action="store_true", help="no HIP graph capture")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replicas", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by data parallelism with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tenant_composite_lora_amd import tclora
+    from tenant_composite_lora_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating config {args.config}", file=sys.stderr, flush=True)
+    wl = W.make(args.config)
+    c = wl.composites
+    T = c.n_tokens
+    B_alg = algorithmic_bytes(wl)
+    F_alg = algorithmic_flops(wl)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # replicas of everything a step reads from HBM
+    ws_bytes = sum(m.A_t.nbytes + m.B_t.nbytes for m in wl.modules) + \
+        sum(x.nbytes for x in wl.x) + sum(y.nbytes for y in wl.y_base)
+    R = args.replicas or max(1, min(256, -(-4 * MALL_BYTES // ws_bytes)))
+    base_mods = [tclora.Module(up(m.A_t), up(m.B_t), m.k) for m in wl.modules]
+    base_x = [up(x) for x in wl.x]
+    base_y = [up(y) for y in wl.y_base]
+    reps = []
+    for r in range(R):
+        if r == 0:
+            mods, xs, ys = base_mods, base_x, base_y
+        else:
+            mods = [tclora.Module(m.A_t.clone(), m.B_t.clone(), wl.modules[i].k)
+                    for i, m in enumerate(base_mods)]
+            xs = [x.clone() for x in base_x]
+            ys = [y.clone() for y in base_y]
+        reps.append((mods, xs, ys))
+    gtp, gpp, pa, pw = (up(c.group_tok_ptr.astype(np.int32)), up(c.group_pair_ptr.astype(np.int32)),
+                        up(c.pair_adapter.astype(np.int32)), up(c.pair_alpha.astype(np.float32)))
+    P = c.n_tuples()
+    plan = tclora.Plan(gtp, gpp, pa, pw, wl.n_adapters, n_tokens=T, max_tuples=P)
+    rc, P_dev, U_dev = plan.status()
+    tclora.check(rc)
+    ws = torch.empty(tclora.workspace_bytes(plan, base_mods), dtype=torch.uint8, device=dev)
+    calls = [tclora.FusedCall(plan, mods, xs, ys, ws) for (mods, xs, ys) in reps]
+    comp_c = tclora.Composites(T, c.n_groups, c.n_pairs, wl.n_adapters, P, gtp.data_ptr(),
+                               gpp.data_ptr(), pa.data_ptr(), pw.data_ptr())
+    L = tclora.lib()
+    import ctypes
+
+    def step(i, stream_ptr):
+        tclora.check(L.tcl_plan_remap(plan.handle, ctypes.byref(comp_c), stream_ptr))
+        calls[i % R](stream_ptr)
+
+    stream = torch.cuda.Stream(device=dev)
+    sp = int(stream.cuda_stream)
+    S = R  # steps per graph: one pass over the replicas
+    print(f"[bench] {wl.name}: T={T} P={P_dev} U={U_dev} replicas={R} "
+          f"alg bytes={B_alg} flops={F_alg}", file=sys.stderr, flush=True)
+
+    def timed(fn_graphs, n_iters):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            fn_graphs(n_iters)
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3
+
+    with torch.cuda.stream(stream):
+        if args.eager:
+            def run_steps(n):
+                for i in range(n):
+                    step(i, sp)
+
+            def run_apply(n):
+                for i in range(n):
+                    calls[i % R](sp)
+            graphs_needed = False
+        else:
+            graphs_needed = True
+
+    if graphs_needed:
+        # capture one pass over the replicas, twice: full steps and apply only
+        g_step = torch.cuda.CUDAGraph()
+        g_apply = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for i in range(2):          # warm the allocator before capture
+                step(i, sp)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g_step, stream=stream):
+            cs = int(torch.cuda.current_stream().cuda_stream)
+            for i in range(S):
+                step(i, cs)
+        with torch.cuda.graph(g_apply, stream=stream):
+            cs = int(torch.cuda.current_stream().cuda_stream)
+            for i in range(S):
+                calls[i % R](cs)
+        torch.cuda.synchronize()
+
+        def run_steps(n):
+            for _ in range(max(1, n // S)):
+                g_step.replay()
+
+        def run_apply(n):
+            for _ in range(max(1, n // S)):
+                g_apply.replay()
+
+    K = args.steps if args.eager else max(S, (args.steps // S) * S)
+    Wu = args.warmup if args.eager else max(S, (args.warmup // S) * S)
+    print(f"[bench] warmup {Wu} steps", file=sys.stderr, flush=True)
+    timed(run_steps, Wu)
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    t_steps = timed(run_steps, K)
+    print(f"[bench] timing {K} applies (dominant kernels, no mapping stage)", file=sys.stderr,
+          flush=True)
+    t_apply = timed(run_apply, K)
+    # a plan-only pass for the record
+    ms_step = 1e3 * t_steps / K
+    apply_s = t_apply / K
+    achieved = B_alg / apply_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": T * K / t_steps,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wu,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == W.BF16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "tokens": T, "tuples": int(P_dev), "adapters_touched": int(U_dev),
+            "modules": [f"{m.name}:{m.d_in}->{m.d_out}" for m in wl.modules],
+            "n_adapters": wl.n_adapters, "r_max": wl.modules[0].r_max,
+            "accumulate": "f32", "replicas": R, "graph": not args.eager,
+            "alg_bytes_per_step": B_alg, "alg_flops_per_step": F_alg,
+            "hbm_gbs_per_step": B_alg / (t_steps / K) / 1e9,
+            "apply_us": apply_s * 1e6, "step_us": ms_step * 1e3,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "tcl_fused_apply (shrink + expand)",
+            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * tcl.h -- C ABI of the batched composite multi-LoRA apply for MI355X (gfx950).
+ *
+ * What the library computes (pages cited by title and section):
+ *
+ *   DyMerge-LoRA, section 3.1 (M1): a composite update is the weighted sum of
+ *   low-rank adapter updates, Delta W = sum_i alpha_i B_i A_i^T.  Evaluating it
+ *   after the merge point (DyMerge-LoRA, one-minute summary: on-GPU post-merge
+ *   fusion) gives, for every token t with composite C_t = {(i, alpha)},
+ *
+ *       y_t = y_t + sum_{(i, alpha) in C_t} alpha * B_i (A_i^T x_t)
+ *
+ *   with A_i of size d_in x r and B_i of size d_out x r.  ELORA (section III-A,
+ *   Eq. 1) is the one-adapter case with alpha = 1.
+ *
+ *   LoRAForge, approach (1): retained-rank contract.  Each adapter of a module
+ *   keeps an ordered factor prefix and an effective rank k (0 <= k <= r_max);
+ *   only the first k rank directions are read and used.  Stores padded to
+ *   r_max are accepted; rows at and beyond k are never read.
+ *
+ *   DyMerge-LoRA, section 4.3: the mapping stage turns token-adapter pairs
+ *   into tuples and reorders them by adapter (LoRA) id so that one adapter's
+ *   tokens are contiguous; aggregation then sums each token's pairs.
+ *   LoRAForge, approach (4)/(5): shrink (A_i^T x) and expand (B_i z) kernels,
+ *   chosen by phase, rank and shape.
+ *
+ * Conventions
+ *   - Adapter pools are rank-major: A_t[a][j][0..d_in) is row j of A_a^T and
+ *     B_t[a][j][0..d_out) is row j of B_a^T, a in [0, n_adapters),
+ *     j in [0, r_max).  The retained prefix of adapter a is rows 0..k_a-1.
+ *   - Tuples are (token, adapter, alpha, slot).  The slot of a pair is its
+ *     position in its composite after the composite is ordered by adapter id.
+ *     The plan lists tuples in ascending (adapter, token, slot) order.
+ *   - Each output element y[t][n] is produced by one thread which sums its
+ *     token's pairs in slot order in fp32 (alpha * z_j * B[j][n], j ascending)
+ *     and adds the result to y once.  No atomics; results are bitwise
+ *     reproducible run to run.
+ *   - dtypes: TCL_BF16 mode = bf16 x / A_t / B_t with fp32 or bf16 y;
+ *     TCL_F32 mode = fp32 everywhere.  z and accumulation are fp32.
+ *   - Device pointers are caller-owned (e.g. allocated by PyTorch) and must be
+ *     16-byte aligned; d_in, d_out and leading dimensions must be multiples of
+ *     8 elements.  Host pointers are only read during the call.
+ *   - Every GPU call is asynchronous on the caller's stream (a hipStream_t
+ *     passed as void*, NULL = the default stream).  Only tcl_plan_copy_out and
+ *     tcl_plan_status synchronise (they read plan data back to the host).
+ *   - Every function returns a status code (TCL_OK = 0 or a negative TCL_E*).
+ *     Host-side checks run before any HIP call, so they need no GPU.  The
+ *     message of the last failure on the calling thread is tcl_last_error().
+ *     The library never aborts and prints only when TCL_LOG is set.
+ */
+#ifndef TCL_H
+#define TCL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TCL_OK = 0,
+  TCL_EINVAL = -1,       /* bad argument or malformed composite table        */
+  TCL_EALIGN = -2,       /* pointer not 16-B aligned, size not multiple of 8 */
+  TCL_ENOSPC = -3,       /* buffer or capacity too small                     */
+  TCL_EUNSUPPORTED = -4, /* dtype combination, rank or group size not built  */
+  TCL_EHIP = -5          /* a HIP runtime call failed                        */
+};
+
+typedef enum { TCL_BF16 = 0, TCL_F32 = 1 } tcl_dtype;
+
+/* Largest r_max the kernels are built for, and the most pairs one
+ * composite (group) may hold. */
+#define TCL_MAX_RANK 64
+#define TCL_MAX_PAIRS_PER_GROUP 64
+
+/*
+ * Composite table (DyMerge-LoRA section 3.1: static composition fixes alpha per
+ * request, dynamic composition per token).  A group is a run of consecutive
+ * tokens sharing one list of (adapter, alpha) pairs; one group per token is
+ * token-level (dynamic) composition.  All arrays are DEVICE memory so that a
+ * gate running on the GPU can feed the plan directly.
+ *
+ *   group_tok_ptr [n_groups+1]: group g covers tokens [ptr[g], ptr[g+1]);
+ *                               ptr[0] = 0, non-decreasing, ptr[G] = n_tokens.
+ *   group_pair_ptr[n_groups+1]: group g owns pairs [ptr[g], ptr[g+1]);
+ *                               ptr[0] = 0, non-decreasing, ptr[G] = n_pairs.
+ *   pair_adapter [n_pairs]    : adapter id in [0, n_adapters), no id twice in
+ *                               one group.
+ *   pair_alpha   [n_pairs]    : finite fp32 weight (copied bit for bit).
+ *   max_tuples                : capacity for P = sum_g tokens_g * pairs_g.
+ *
+ * The table's contents are validated on the device by tcl_plan_map; a bad table
+ * leaves an error in the plan's device status (see tcl_plan_status) and every
+ * later call on that plan does nothing.
+ */
+typedef struct {
+  int32_t n_tokens;
+  int32_t n_groups;
+  int32_t n_pairs;
+  int32_t n_adapters;
+  int32_t max_tuples;
+  const int32_t *group_tok_ptr;
+  const int32_t *group_pair_ptr;
+  const int32_t *pair_adapter;
+  const float *pair_alpha;
+} tcl_composites;
+
+/*
+ * One projection's adapter pool (the loader output of the LoRAForge
+ * retained-rank contract).  k_dev is DEVICE int32 [n_adapters] of effective
+ * ranks in [0, r_max], or NULL for "every adapter uses r_max"; fill it with
+ * tcl_module_load_ranks.
+ */
+typedef struct {
+  int32_t n_adapters;
+  int32_t d_in;
+  int32_t d_out;
+  int32_t r_max;       /* 1..TCL_MAX_RANK */
+  tcl_dtype wdtype;    /* dtype of A_t and B_t */
+  const void *A_t;     /* device [n_adapters][r_max][d_in]  */
+  const void *B_t;     /* device [n_adapters][r_max][d_out] */
+  const int32_t *k_dev;
+} tcl_module;
+
+typedef struct tcl_plan tcl_plan; /* opaque host handle; device arrays live in
+                                     the caller's plan buffer */
+
+/* Message of the last non-OK return on the calling thread ("" if none). */
+const char *tcl_last_error(void);
+
+/* Library version string. */
+const char *tcl_version(void);
+
+/*
+ * Device bytes a plan buffer needs for these sizes (host only, no GPU).
+ * Errors: TCL_EINVAL for negative sizes, n_adapters < 1, or a count that
+ * overflows 32-bit indexing.
+ */
+int tcl_plan_bytes(int32_t n_tokens, int32_t n_groups, int32_t n_pairs,
+                   int32_t n_adapters, int32_t max_tuples, size_t *bytes);
+
+/*
+ * Mapping stage (DyMerge-LoRA section 4.3).  Validates the composite table,
+ * orders each composite by adapter id (which fixes the slots), expands the
+ * groups into tuples and stably counting-sorts them by adapter id, then
+ * builds the segment table (one run per adapter that has tuples, ascending),
+ * the per-token tuple index and the work lists of the apply kernels.
+ *
+ * dev_buf: caller-owned device buffer of at least tcl_plan_bytes() bytes,
+ * 256-B aligned; it holds every device array of the plan and must outlive it.
+ * *out receives a new host handle (free with tcl_plan_free).  One plan serves
+ * every module and layer of the batch.  Asynchronous on `stream`.
+ * Host errors: TCL_EINVAL (null pointer, sizes), TCL_EALIGN (dev_buf),
+ * TCL_ENOSPC (dev_bytes too small), TCL_EHIP.
+ * Device-detected errors (reported by tcl_plan_status): TCL_EINVAL (malformed
+ * CSR, adapter id out of range, non-finite alpha, duplicate adapter in a
+ * group), TCL_EUNSUPPORTED (a group with more than TCL_MAX_PAIRS_PER_GROUP
+ * pairs), TCL_ENOSPC (more tuples than max_tuples), in that precedence.
+ */
+int tcl_plan_map(const tcl_composites *c, void *dev_buf, size_t dev_bytes,
+                 void *stream, tcl_plan **out);
+
+/* Re-run the mapping stage of an existing plan with a new table of the same
+ * or smaller sizes (no host allocation).  Same errors as tcl_plan_map. */
+int tcl_plan_remap(tcl_plan *p, const tcl_composites *c, void *stream);
+
+/* Synchronises `stream` and returns the device-detected status of the plan
+ * (TCL_OK or a code listed under tcl_plan_map), with its tuple and segment
+ * counts (either pointer may be NULL). */
+int tcl_plan_status(const tcl_plan *p, void *stream, int32_t *n_tuples,
+                    int32_t *n_segments);
+
+/*
+ * Copies the plan to host arrays (synchronises `stream`).  Capacities: the
+ * tuple arrays and tok_tuple hold max_tuples entries, seg_adapter n_adapters,
+ * seg_begin n_adapters+1, tok_ptr n_tokens+1; only the first P (tuples), U
+ * (segments) entries are meaningful.  Any pointer may be NULL to skip it.
+ */
+int tcl_plan_copy_out(const tcl_plan *p, int32_t *tup_token, int32_t *tup_adapter,
+                      float *tup_alpha, int32_t *tup_slot, int32_t *seg_adapter,
+                      int32_t *seg_begin, int32_t *tok_ptr, int32_t *tok_tuple,
+                      void *stream);
+
+void tcl_plan_free(tcl_plan *p);
+
+/*
+ * Loader step of the retained-rank contract (LoRAForge approach (1)): checks
+ * host ranks k_host[n_adapters] in [0, r_max] and copies them to the device
+ * array k_dev (caller-owned, n_adapters int32), then sets m->k_dev = k_dev.
+ * Errors: TCL_EINVAL (null, rank out of range), TCL_EHIP.
+ */
+int tcl_module_load_ranks(tcl_module *m, const int32_t *k_host, int32_t *k_dev,
+                          void *stream);
+
+/* Device workspace tcl_fused_apply needs for these modules (host only). */
+int tcl_workspace_bytes(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
+                        size_t *bytes);
+
+/*
+ * Shrink (LoRAForge approach (4)): z[p][j] = sum_d A_t[a_p][j][d] * x[t_p][d]
+ * for j < k_{a_p}, zero for k_{a_p} <= j < r_max, for every tuple p in the
+ * plan's sorted order.  alpha is not applied.  x: device [n_tokens][ldx] of
+ * dtype xd (= module dtype).  z: device fp32 [max_tuples][r_max].
+ * Errors: TCL_EINVAL, TCL_EALIGN, TCL_EUNSUPPORTED, TCL_EHIP.
+ */
+int tcl_shrink(const tcl_plan *p, const tcl_module *m, const void *x, int64_t ldx,
+               tcl_dtype xd, float *z, void *stream);
+
+/*
+ * Expand and aggregate (LoRAForge approach (4), RowExpand; DyMerge-LoRA
+ * aggregation stage): y[t][n] += sum over token t's slots s, in order, of
+ * alpha_s * sum_{j < k} B_t[a_s][j][n] * z[p_s][j].  z is the tcl_shrink
+ * layout.  y: device [n_tokens][ldy] of dtype yd, updated in place; tokens
+ * with an empty composite are not written.
+ */
+int tcl_expand(const tcl_plan *p, const tcl_module *m, const float *z, void *y,
+               int64_t ldy, tcl_dtype yd, void *stream);
+
+/*
+ * Shrink + expand for n_mods modules that share the plan (e.g. the seven
+ * projections of a transformer layer), each with its own x[i] (leading
+ * dimension ldx[i]) and y[i] (ldy[i]).  ws: device workspace of at least
+ * tcl_workspace_bytes() bytes, 256-B aligned.  Same arithmetic as tcl_shrink
+ * followed by tcl_expand, except that the shrink may split d_in into chunks
+ * whose partial sums the expand adds in a fixed order.
+ */
+int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
+                    const void *const *x, const int64_t *ldx, tcl_dtype xd,
+                    void *const *y, const int64_t *ldy, tcl_dtype yd, void *ws,
+                    size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TCL_H */

@@ -1,0 +1,312 @@
+"""Python binding of libtclora (ctypes).
+
+Argument marshalling only: every step of the apply runs in the library's HIP
+kernels.  PyTorch supplies device memory and the stream (the current torch
+stream of the tensors' device).  The library must be built
+(``python -m tenant_composite_lora_amd.build``); nothing here computes a
+result on the host, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtclora.so")
+
+OK, EINVAL, EALIGN, ENOSPC, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5
+BF16, F32 = 0, 1
+MAX_RANK = 64
+MAX_PAIRS_PER_GROUP = 64
+
+_NAMES = {OK: "OK", EINVAL: "EINVAL", EALIGN: "EALIGN", ENOSPC: "ENOSPC",
+          EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP"}
+
+EXPORTS = ["tcl_last_error", "tcl_version", "tcl_plan_bytes", "tcl_plan_map", "tcl_plan_remap",
+           "tcl_plan_status", "tcl_plan_copy_out", "tcl_plan_free", "tcl_module_load_ranks",
+           "tcl_workspace_bytes", "tcl_shrink", "tcl_expand", "tcl_fused_apply"]
+
+
+class TclError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Composites(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("n_pairs", ctypes.c_int32), ("n_adapters", ctypes.c_int32),
+                ("max_tuples", ctypes.c_int32),
+                ("group_tok_ptr", ctypes.c_void_p), ("group_pair_ptr", ctypes.c_void_p),
+                ("pair_adapter", ctypes.c_void_p), ("pair_alpha", ctypes.c_void_p)]
+
+
+class ModuleDesc(ctypes.Structure):
+    _fields_ = [("n_adapters", ctypes.c_int32), ("d_in", ctypes.c_int32),
+                ("d_out", ctypes.c_int32), ("r_max", ctypes.c_int32),
+                ("wdtype", ctypes.c_int32), ("A_t", ctypes.c_void_p),
+                ("B_t", ctypes.c_void_p), ("k_dev", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib(path: Optional[str] = None):
+    """Load libtclora.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} not found: build it with `python -m tenant_composite_lora_amd.build`")
+    L = ctypes.CDLL(p)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.tcl_last_error.restype = ctypes.c_char_p
+    L.tcl_version.restype = ctypes.c_char_p
+    L.tcl_plan_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.tcl_plan_map.argtypes = [ctypes.POINTER(Composites), vp, sz, vp, ctypes.POINTER(vp)]
+    L.tcl_plan_remap.argtypes = [vp, ctypes.POINTER(Composites), vp]
+    L.tcl_plan_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.tcl_plan_copy_out.argtypes = [vp] * 9 + [vp]
+    L.tcl_plan_free.argtypes = [vp]
+    L.tcl_plan_free.restype = None
+    L.tcl_module_load_ranks.argtypes = [ctypes.POINTER(ModuleDesc), vp, vp, vp]
+    L.tcl_workspace_bytes.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, ctypes.POINTER(sz)]
+    L.tcl_shrink.argtypes = [vp, ctypes.POINTER(ModuleDesc), vp, i64, i32, vp, vp]
+    L.tcl_expand.argtypes = [vp, ctypes.POINTER(ModuleDesc), vp, vp, i64, i32, vp]
+    L.tcl_fused_apply.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, ctypes.POINTER(vp),
+                                  ctypes.POINTER(i64), i32, ctypes.POINTER(vp),
+                                  ctypes.POINTER(i64), i32, vp, sz, vp]
+    if path is None:
+        _lib = L
+    return L
+
+
+def check(rc: int) -> None:
+    if rc != OK:
+        raise TclError(rc, lib().tcl_last_error().decode(errors="replace"))
+
+
+def _stream(dev: torch.device, stream=None) -> int:
+    if stream is not None:
+        return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+    return int(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return BF16
+    if t == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def plan_bytes(n_tokens: int, n_groups: int, n_pairs: int, n_adapters: int,
+               max_tuples: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(lib().tcl_plan_bytes(n_tokens, n_groups, n_pairs, n_adapters, max_tuples,
+                               ctypes.byref(out)))
+    return out.value
+
+
+class Plan:
+    """A mapped batch: tuples reordered by adapter id plus the token index.
+
+    ``group_tok_ptr``, ``group_pair_ptr``, ``pair_adapter`` (int32) and
+    ``pair_alpha`` (float32) are device tensors.  ``max_tuples`` bounds the
+    tuple count; if omitted it is taken as n_tokens * max pairs per group
+    computed from ``group_pair_ptr`` on the device (a small reduction)."""
+
+    def __init__(self, group_tok_ptr: torch.Tensor, group_pair_ptr: torch.Tensor,
+                 pair_adapter: torch.Tensor, pair_alpha: torch.Tensor, n_adapters: int,
+                 n_tokens: Optional[int] = None, max_tuples: Optional[int] = None,
+                 buf: Optional[torch.Tensor] = None, stream=None):
+        dev = group_tok_ptr.device
+        self.device = dev
+        G = int(group_tok_ptr.shape[0]) - 1
+        NP = int(pair_adapter.shape[0])
+        if n_tokens is None:
+            # the token count is the last CSR entry (a 4-byte read-back)
+            n_tokens = int(group_tok_ptr[-1].item()) if group_tok_ptr.numel() else 0
+        if max_tuples is None:
+            if G > 0:
+                tl = (group_tok_ptr[1:] - group_tok_ptr[:-1]).to(torch.int64)
+                pl = (group_pair_ptr[1:] - group_pair_ptr[:-1]).to(torch.int64)
+                max_tuples = int((tl * pl).sum().item())
+            else:
+                max_tuples = 0
+        T = int(n_tokens)
+        self.n_tokens, self.n_groups, self.n_pairs = T, G, NP
+        self.n_adapters, self.max_tuples = int(n_adapters), int(max_tuples)
+        nbytes = plan_bytes(T, G, NP, n_adapters, self.max_tuples)
+        if buf is None:
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.buf = buf
+        # keep the inputs alive until the mapping kernel has run
+        self._inputs = (group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha)
+        self._c = Composites(T, G, NP, int(n_adapters), self.max_tuples,
+                             _ptr(group_tok_ptr), _ptr(group_pair_ptr), _ptr(pair_adapter),
+                             _ptr(pair_alpha))
+        h = ctypes.c_void_p(0)
+        check(lib().tcl_plan_map(ctypes.byref(self._c), buf.data_ptr(), buf.numel(),
+                                 _stream(dev, stream), ctypes.byref(h)))
+        self.handle = h
+
+    def remap(self, group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha, n_tokens: int,
+              stream=None) -> None:
+        G = int(group_tok_ptr.shape[0]) - 1
+        NP = int(pair_adapter.shape[0])
+        self._inputs = (group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha)
+        self._c = Composites(int(n_tokens), G, NP, self.n_adapters, self.max_tuples,
+                             _ptr(group_tok_ptr), _ptr(group_pair_ptr), _ptr(pair_adapter),
+                             _ptr(pair_alpha))
+        check(lib().tcl_plan_remap(self.handle, ctypes.byref(self._c), _stream(self.device, stream)))
+        self.n_tokens, self.n_groups, self.n_pairs = int(n_tokens), G, NP
+
+    def status(self, stream=None):
+        P, U = ctypes.c_int32(0), ctypes.c_int32(0)
+        rc = lib().tcl_plan_status(self.handle, _stream(self.device, stream), ctypes.byref(P),
+                                   ctypes.byref(U))
+        return rc, P.value, U.value
+
+    def copy_out(self, stream=None) -> dict:
+        """Host copy of the plan arrays (synchronises)."""
+        import numpy as np
+        rc, P, U = self.status(stream)
+        check(rc)
+        cap, N, T = self.max_tuples, self.n_adapters, self.n_tokens
+        arrs = {
+            "tup_token": np.zeros(cap, np.int32), "tup_adapter": np.zeros(cap, np.int32),
+            "tup_alpha": np.zeros(cap, np.float32), "tup_slot": np.zeros(cap, np.int32),
+            "seg_adapter": np.zeros(N, np.int32), "seg_begin": np.zeros(N + 1, np.int32),
+            "tok_ptr": np.zeros(T + 1, np.int32), "tok_tuple": np.zeros(cap, np.int32),
+        }
+        order = ["tup_token", "tup_adapter", "tup_alpha", "tup_slot", "seg_adapter",
+                 "seg_begin", "tok_ptr", "tok_tuple"]
+        ptrs = [arrs[k].ctypes.data_as(ctypes.c_void_p) if arrs[k].size else None for k in order]
+        check(lib().tcl_plan_copy_out(self.handle, *ptrs, _stream(self.device, stream)))
+        return {
+            "tup_token": arrs["tup_token"][:P], "tup_adapter": arrs["tup_adapter"][:P],
+            "tup_alpha": arrs["tup_alpha"][:P], "tup_slot": arrs["tup_slot"][:P],
+            "seg_adapter": arrs["seg_adapter"][:U], "seg_begin": arrs["seg_begin"][:U + 1],
+            "tok_ptr": arrs["tok_ptr"], "tok_tuple": arrs["tok_tuple"][:P],
+        }
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            try:
+                lib().tcl_plan_free(h)
+            except Exception:  # noqa: BLE001 - interpreter shutdown
+                pass
+            self.handle = None
+
+
+class Module:
+    """One projection's adapter pool: A_t [N, r_max, d_in], B_t [N, r_max,
+    d_out] (rank-major, bf16 or fp32, on the GPU) and optional effective
+    ranks k (host ints, loaded to the device once)."""
+
+    def __init__(self, A_t: torch.Tensor, B_t: torch.Tensor, k=None, stream=None):
+        if A_t.dim() != 3 or B_t.dim() != 3 or A_t.shape[:2] != B_t.shape[:2]:
+            raise ValueError("A_t and B_t must be [N, r_max, d] with equal N and r_max")
+        if A_t.dtype != B_t.dtype:
+            raise ValueError("A_t and B_t must share a dtype")
+        self.A_t = A_t.contiguous()
+        self.B_t = B_t.contiguous()
+        N, r, d_in = self.A_t.shape
+        d_out = self.B_t.shape[2]
+        self.desc = ModuleDesc(N, d_in, d_out, r, _dtype_code(A_t.dtype), self.A_t.data_ptr(),
+                               self.B_t.data_ptr(), None)
+        self.k_dev = None
+        if k is not None:
+            import numpy as np
+            kh = np.ascontiguousarray(np.asarray(k, dtype=np.int32))
+            if kh.shape != (N,):
+                raise ValueError("k must have one entry per adapter")
+            self.k_dev = torch.empty(N, dtype=torch.int32, device=A_t.device)
+            check(lib().tcl_module_load_ranks(ctypes.byref(self.desc),
+                                              kh.ctypes.data_as(ctypes.c_void_p),
+                                              self.k_dev.data_ptr(),
+                                              _stream(A_t.device, stream)))
+
+    @property
+    def n_adapters(self):
+        return self.desc.n_adapters
+
+    @property
+    def d_in(self):
+        return self.desc.d_in
+
+    @property
+    def d_out(self):
+        return self.desc.d_out
+
+    @property
+    def r_max(self):
+        return self.desc.r_max
+
+
+def shrink(plan: Plan, m: Module, x: torch.Tensor, z: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """z [max_tuples, r_max] fp32 in the plan's sorted-tuple order."""
+    if z is None:
+        z = torch.empty((max(plan.max_tuples, 1), m.r_max), dtype=torch.float32, device=x.device)
+    check(lib().tcl_shrink(plan.handle, ctypes.byref(m.desc), x.data_ptr(), x.stride(0),
+                           _dtype_code(x.dtype), z.data_ptr(), _stream(x.device, stream)))
+    return z
+
+
+def expand(plan: Plan, m: Module, z: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """y += aggregated alpha * B z, in place."""
+    check(lib().tcl_expand(plan.handle, ctypes.byref(m.desc), z.data_ptr(), y.data_ptr(),
+                           y.stride(0), _dtype_code(y.dtype), _stream(y.device, stream)))
+    return y
+
+
+def workspace_bytes(plan: Plan, mods: Sequence[Module]) -> int:
+    arr = (ModuleDesc * len(mods))(*[m.desc for m in mods])
+    out = ctypes.c_size_t(0)
+    check(lib().tcl_workspace_bytes(plan.handle, arr, len(mods), ctypes.byref(out)))
+    return out.value
+
+
+class FusedCall:
+    """Pre-marshalled arguments of tcl_fused_apply for repeated calls."""
+
+    def __init__(self, plan: Plan, mods: Sequence[Module], xs: Sequence[torch.Tensor],
+                 ys: Sequence[torch.Tensor], ws: Optional[torch.Tensor] = None):
+        n = len(mods)
+        assert len(xs) == n and len(ys) == n
+        self.plan, self.mods, self.xs, self.ys = plan, list(mods), list(xs), list(ys)
+        self.descs = (ModuleDesc * n)(*[m.desc for m in mods])
+        self.xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+        self.yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+        self.ldx = (ctypes.c_int64 * n)(*[x.stride(0) for x in xs])
+        self.ldy = (ctypes.c_int64 * n)(*[y.stride(0) for y in ys])
+        self.xd = _dtype_code(xs[0].dtype)
+        self.yd = _dtype_code(ys[0].dtype)
+        need = workspace_bytes(plan, mods)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device=xs[0].device)
+        self.ws = ws
+        self.n = n
+
+    def __call__(self, stream=None):
+        check(lib().tcl_fused_apply(self.plan.handle, self.descs, self.n, self.xp, self.ldx,
+                                    self.xd, self.yp, self.ldy, self.yd, self.ws.data_ptr(),
+                                    self.ws.numel(), _stream(self.xs[0].device, stream)))
+
+
+def fused_apply(plan: Plan, mods: Sequence[Module], xs: Sequence[torch.Tensor],
+                ys: Sequence[torch.Tensor], ws: Optional[torch.Tensor] = None,
+                stream=None) -> List[torch.Tensor]:
+    FusedCall(plan, mods, xs, ys, ws)(stream)
+    return list(ys)
