@@ -1,21 +1,20 @@
 // Shrink, expand and the fused apply of the composite multi-LoRA path.
 //
 //   shrink  (LoRAForge approach (4), segmented shrink): for one adapter's run
-//           of tuples, z_p = A_a[:, :k]^T x_{t_p}.  One workgroup owns a work
-//           item (an adapter, up to kTile consecutive tuples of its segment)
-//           and a chunk of d_in; every wave owns a quarter of the rank rows,
-//           every lane a 16-byte column granule, so A_a rows stream through
-//           with coalesced 16-B loads and are reused across the item's
-//           tokens.  Each lane keeps fp32 partial dot products that a
-//           64-lane butterfly reduction folds in a fixed order.
+//           of tuples, z_p = A_a[:, :k]^T x_{t_p}.  A wave owns one rank row j
+//           of one work item (an adapter and up to kTile consecutive tuples
+//           of its segment) and streams that row of A_a^T with coalesced
+//           16-byte loads, reusing it across the item's tokens; each lane
+//           keeps fp32 partial dot products that a 64-lane butterfly folds in
+//           a fixed order.  z is written final (no split-K partials).
 //   expand  (LoRAForge approach (4), RowExpand; DyMerge-LoRA aggregation
 //           stage): one wave owns 512 consecutive outputs of one token and
 //           adds alpha_s * B_a[n, :k] z_s for the token's slots in order, in
 //           fp32, then adds the total to y once.  Each output element has
 //           exactly one owner; there are no atomics.
 //
-// All kernels first read the plan's device status and do nothing when the
-// mapping stage rejected the composite table.
+// A plan whose composite table was rejected has an empty token index and no
+// work items, so every kernel below finds nothing to do.
 
 #include <cstdint>
 
@@ -76,55 +75,6 @@ struct Gran<float> {
   }
 };
 
-// 8 consecutive weights of one B row, widened to fp32
-template <typename TW>
-__device__ inline void load8(const TW *p, float (&b)[8]);
-
-template <>
-__device__ inline void load8<bf16_t>(const bf16_t *p, float (&b)[8]) {
-  const uint4 v = *reinterpret_cast<const uint4 *>(p);
-  b[0] = bf16_lo(v.x); b[1] = bf16_hi(v.x);
-  b[2] = bf16_lo(v.y); b[3] = bf16_hi(v.y);
-  b[4] = bf16_lo(v.z); b[5] = bf16_hi(v.z);
-  b[6] = bf16_lo(v.w); b[7] = bf16_hi(v.w);
-}
-
-template <>
-__device__ inline void load8<float>(const float *p, float (&b)[8]) {
-  const float4 u = reinterpret_cast<const float4 *>(p)[0];
-  const float4 v = reinterpret_cast<const float4 *>(p)[1];
-  b[0] = u.x; b[1] = u.y; b[2] = u.z; b[3] = u.w;
-  b[4] = v.x; b[5] = v.y; b[6] = v.z; b[7] = v.w;
-}
-
-// y[0..8) += acc[0..8)
-template <typename TY>
-__device__ inline void add_store8(TY *p, const float (&acc)[8]);
-
-template <>
-__device__ inline void add_store8<float>(float *p, const float (&acc)[8]) {
-  float4 *q = reinterpret_cast<float4 *>(p);
-  float4 u = q[0], v = q[1];
-  u.x += acc[0]; u.y += acc[1]; u.z += acc[2]; u.w += acc[3];
-  v.x += acc[4]; v.y += acc[5]; v.z += acc[6]; v.w += acc[7];
-  q[0] = u;
-  q[1] = v;
-}
-
-template <>
-__device__ inline void add_store8<bf16_t>(bf16_t *p, const float (&acc)[8]) {
-  uint4 *q = reinterpret_cast<uint4 *>(p);
-  uint4 v = *q;
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint16_t lo = f32_to_bf16(bf16_lo(w[i]) + acc[2 * i]);
-    const uint16_t hi = f32_to_bf16(bf16_hi(w[i]) + acc[2 * i + 1]);
-    w[i] = uint32_t(lo) | (uint32_t(hi) << 16);
-  }
-  *q = make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -138,85 +88,217 @@ __device__ inline int eff_rank(const int32_t *k_dev, int a, int r_max) {
 }
 
 // ---------------------------------------------------------------------------
-// shrink
+// multi-module launch tables
 // ---------------------------------------------------------------------------
-struct ShrinkArgs {
-  const int32_t *status;
-  const int4 *items;
-  const int32_t *tup_token;
-  const int32_t *k_dev;
-  const void *A_t;
-  const void *x;
-  int64_t ldx;
-  int32_t d_in, r_max, cap;
-  int32_t n_chunks, chunk_gran;  // chunk width in 16-byte granules
-  int32_t zero_tail;             // write zeros for k <= j < r_max
-  float *z;                      // [n_chunks][cap][r_max]
+// One launch covers up to kMaxMods modules that share the plan (e.g. the
+// seven projections of a transformer layer).
+constexpr int kMaxMods = 8;
+
+struct ModArgs {
+  const void *W;          // shrink: A_t, expand: B_t
+  void *io;               // shrink: x, expand: y
+  const int32_t *k_dev;   // effective ranks or NULL
+  float *z;               // [cap][zld]
+  int64_t ld;             // leading dimension of io (elements)
+  int32_t zld;            // row stride of z (r_max, or r_max rounded up to 4)
+  int32_t d;              // shrink: d_in, expand: d_out
+  int32_t r_max;
+  int32_t first;          // shrink: first rank group, expand: first job
+  int32_t n_ct;           // expand: column tiles of 512 outputs
 };
 
-template <int R, typename TIN>
+struct ShrinkArgs {
+  const int32_t *status;
+  const Item *items;
+  int32_t n_mods, rg_total, items_cap;
+  int32_t zero_tail;  // write zeros for k <= j < r_max
+  ModArgs m[kMaxMods];
+};
+
+// Granules each lane has in flight per token pass.
+constexpr int kShrinkUnroll = 8;
+
+// fp32 path.  One workgroup = 4 waves = 4 consecutive rank rows j of one work
+// item of one module.  A wave streams row j of A_a^T once per pair of tokens
+// (the second pass over a row comes from L1/L2) together with the item's x
+// rows, with kShrinkUnroll 16-byte granules per lane in flight, then folds
+// each token's 64 lane partials with a butterfly in a fixed order and writes
+// z final.
+template <typename TIN>
 __global__ __launch_bounds__(256) void shrink_valu(ShrinkArgs s) {
-  if (s.status[ST_CODE] != TCL_OK) return;
   constexpr int VEC = Gran<TIN>::kElems;
-  constexpr int RW = (R + 3) / 4;  // rank rows per wave
+  constexpr int U = kShrinkUnroll;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n_items = s.status[ST_ITEMS];
-  const int total = n_items * s.n_chunks;
-  const int n_gran = s.d_in / VEC;
-  const TIN *A = static_cast<const TIN *>(s.A_t);
-  const TIN *X = static_cast<const TIN *>(s.x);
+  const int total = n_items * s.rg_total;
 
   for (int job = blockIdx.x; job < total; job += gridDim.x) {
-    const int item = job / s.n_chunks, chunk = job - item * s.n_chunks;
-    const int4 it = s.items[item];
-    const int a = it.x, p0 = it.y, ntok = it.z - it.y;
-    const int k = eff_rank(s.k_dev, a, s.r_max);
-    int tok[kTile];
+    const int item = job / s.rg_total, rgg = job - item * s.rg_total;
+    int mi = 0;
 #pragma unroll
-    for (int tt = 0; tt < kTile; ++tt) tok[tt] = tt < ntok ? s.tup_token[p0 + tt] : 0;
-
-    float acc[RW][kTile];
-#pragma unroll
-    for (int i = 0; i < RW; ++i)
-#pragma unroll
-      for (int tt = 0; tt < kTile; ++tt) acc[i][tt] = 0.f;
-
-    const int g0 = chunk * s.chunk_gran;
-    const int g1 = min(n_gran, g0 + s.chunk_gran);
-    for (int g = g0 + lane; g < g1; g += 64) {
-      Gran<TIN> xv[kTile];
-#pragma unroll
-      for (int tt = 0; tt < kTile; ++tt)
-        if (tt < ntok) xv[tt].load(X + int64_t(tok[tt]) * s.ldx + int64_t(g) * VEC);
-#pragma unroll
-      for (int i = 0; i < RW; ++i) {
-        const int j = w + 4 * i;
-        if (j < k) {
-          Gran<TIN> av;
-          av.load(A + (int64_t(a) * s.r_max + j) * s.d_in + int64_t(g) * VEC);
-#pragma unroll
-          for (int tt = 0; tt < kTile; ++tt)
-            if (tt < ntok) acc[i][tt] = av.dot(xv[tt], acc[i][tt]);
-        }
-      }
+    for (int i = 1; i < kMaxMods; ++i)
+      if (i < s.n_mods && rgg >= s.m[i].first) mi = i;
+    const ModArgs M = s.m[mi];
+    const int j = (rgg - M.first) * 4 + w;
+    if (j >= M.r_max) continue;
+    const Item it = s.items[item];
+    const int a = it.head.x, p0 = it.head.y, ntok = it.head.z;
+    const int k = eff_rank(M.k_dev, a, M.r_max);
+    if (j >= k) {
+      if (s.zero_tail && lane < ntok) M.z[int64_t(p0 + lane) * M.zld + j] = 0.f;
+      continue;
     }
+    const int n_gran = M.d / VEC;
+    const int *tok = it.tok;
+    const TIN *Arow = static_cast<const TIN *>(M.W) + (int64_t(a) * M.r_max + j) * M.d;
+    const TIN *X = static_cast<const TIN *>(M.io);
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const int j = w + 4 * i;
-      if (j >= s.r_max) continue;
-      if (j < k) {
+    for (int tb = 0; tb < kTile; tb += 2) {
+      if (tb >= ntok) break;
+      const bool two = tb + 1 < ntok;
+      const TIN *X0 = X + int64_t(tok[tb]) * M.ld;
+      const TIN *X1 = X + int64_t(tok[two ? tb + 1 : tb]) * M.ld;
+      float acc0 = 0.f, acc1 = 0.f;
+      for (int g0 = lane; g0 < n_gran; g0 += 64 * U) {
+        Gran<TIN> av[U], xa[U], xb[U];
 #pragma unroll
-        for (int tt = 0; tt < kTile; ++tt) {
-          if (tt < ntok) {
-            const float v = wave_sum(acc[i][tt]);
-            if (lane == 0) s.z[(int64_t(chunk) * s.cap + p0 + tt) * s.r_max + j] = v;
+        for (int u = 0; u < U; ++u) {
+          const int g = g0 + 64 * u;
+          if (g < n_gran) {
+            av[u].load(Arow + int64_t(g) * VEC);
+            xa[u].load(X0 + int64_t(g) * VEC);
+            if (two) xb[u].load(X1 + int64_t(g) * VEC);
           }
         }
-      } else if (s.zero_tail && lane == 0) {
-        for (int tt = 0; tt < ntok; ++tt)
-          s.z[(int64_t(chunk) * s.cap + p0 + tt) * s.r_max + j] = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int g = g0 + 64 * u;
+          if (g < n_gran) {
+            acc0 = av[u].dot(xa[u], acc0);
+            if (two) acc1 = av[u].dot(xb[u], acc1);
+          }
+        }
+      }
+      acc0 = wave_sum(acc0);
+      if (lane == 0) M.z[int64_t(p0 + tb) * M.zld + j] = acc0;
+      if (two) {
+        acc1 = wave_sum(acc1);
+        if (lane == 0) M.z[int64_t(p0 + tb + 1) * M.zld + j] = acc1;
       }
     }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// bf16 shrink on the matrix cores
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr int kShrinkWaves = 8;   // waves per workgroup, splitting d_in
+constexpr int kShrinkSteps = 16;  // 32-element K steps each lane has in flight
+
+// z[tokens x ranks] = X[tokens x d_in] . A_a^T[d_in x ranks] for one work item
+// (up to 16 tuples of one adapter) and one tile of 16 rank rows, with
+// v_mfma_f32_16x16x32_bf16.  Both operands load straight from memory: lane l
+// holds 8 consecutive d of token row (l % 16) for the first operand and of rank
+// row (l % 16) of A_a^T (rank-major, so 16 contiguous bytes) for the second;
+// rows past the item's tuple count or the adapter's effective rank are zero
+// and never read.  The 8 waves split the K steps of d_in, each keeping
+// kShrinkSteps steps of loads in flight, and their partial tiles are summed
+// through LDS in wave order.  z is written final.
+__global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
+  __shared__ f32x4_t red[kShrinkWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  // The item record of the first job is fetched together with the item count
+  // (the grid never exceeds items_cap * rg_total, so the read is in bounds),
+  // which saves one dependent memory round trip.
+  int job = blockIdx.x;
+  int4 head = s.items[job / s.rg_total].head;
+  int tokl = s.items[job / s.rg_total].tok[row];
+  const int n_items = s.status[ST_ITEMS];
+  const int total = n_items * s.rg_total;
+
+  for (; job < total; job += gridDim.x) {
+    const int item = job / s.rg_total, rgg = job - item * s.rg_total;
+    if (job != int(blockIdx.x)) {
+      head = s.items[item].head;
+      tokl = s.items[item].tok[row];
+    }
+    int mi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxMods; ++i)
+      if (i < s.n_mods && rgg >= s.m[i].first) mi = i;
+    const int first = s.m[mi].first, dd = s.m[mi].d, r_max = s.m[mi].r_max, zld = s.m[mi].zld;
+    const int64_t ld = s.m[mi].ld;
+    const int32_t *k_dev = s.m[mi].k_dev;
+    float *Z = s.m[mi].z;
+    const bf16_t *Aw = static_cast<const bf16_t *>(s.m[mi].W);
+    const bf16_t *Xw = static_cast<const bf16_t *>(s.m[mi].io);
+    const int j0 = (rgg - first) * 16;
+    const int a = head.x, p0 = head.y, ntok = head.z;
+    const int k = eff_rank(k_dev, a, r_max);
+    if (j0 >= k) {
+      // whole rank tile beyond the effective rank
+      if (s.zero_tail && w == 0) {
+        const int j = j0 + row;
+        for (int tt = kg; tt < ntok; tt += 4)
+          if (j < r_max) Z[int64_t(p0 + tt) * zld + j] = 0.f;
+      }
+      continue;
+    }
+    const int tok = row < ntok ? tokl : -1;
+    const int jr = j0 + row;  // rank row this lane feeds
+    const bf16_t *Xr = tok >= 0 ? Xw + int64_t(tok) * ld + kg * 8 : nullptr;
+    const bf16_t *Ar = jr < k ? Aw + (int64_t(a) * r_max + jr) * dd + kg * 8 : nullptr;
+    const int nsteps = (dd + 31) / 32;
+    const int per = (nsteps + kShrinkWaves - 1) / kShrinkWaves;
+    const int s0 = w * per, s1 = min(nsteps, s0 + per);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int st = s0; st < s1; st += kShrinkSteps) {
+      bf16x8_t xv[kShrinkSteps], av[kShrinkSteps];
+#pragma unroll
+      for (int u = 0; u < kShrinkSteps; ++u) {
+        const int e0 = (st + u) * 32 + kg * 8;  // first element of this lane's granule
+        const bool in = st + u < s1 && e0 < dd;
+        uint4 xb = make_uint4(0, 0, 0, 0), ab = make_uint4(0, 0, 0, 0);
+        if (in && Xr) xb = *reinterpret_cast<const uint4 *>(Xr + (st + u) * 32);
+        if (in && Ar) ab = *reinterpret_cast<const uint4 *>(Ar + (st + u) * 32);
+        xv[u] = __builtin_bit_cast(bf16x8_t, xb);
+        av[u] = __builtin_bit_cast(bf16x8_t, ab);
+      }
+#pragma unroll
+      for (int u = 0; u < kShrinkSteps; ++u)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[u], av[u], acc, 0, 0, 0);
+    }
+    red[w][lane] = acc;
+    __syncthreads();
+    if (w == 0) {
+      f32x4_t sum = red[0][lane];
+#pragma unroll
+      for (int v = 1; v < kShrinkWaves; ++v) {
+        const f32x4_t o = red[v][lane];
+        sum[0] += o[0];
+        sum[1] += o[1];
+        sum[2] += o[2];
+        sum[3] += o[3];
+      }
+      // lane holds tokens 4*kg .. 4*kg+3 of rank column j0 + row
+      const int j = j0 + row;
+      if (j < r_max) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tt = 4 * kg + i;
+          if (tt < ntok) {
+            if (j < k) Z[int64_t(p0 + tt) * zld + j] = sum[i];
+            else if (s.zero_tail) Z[int64_t(p0 + tt) * zld + j] = 0.f;
+          }
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -224,48 +306,188 @@ __global__ __launch_bounds__(256) void shrink_valu(ShrinkArgs s) {
 // expand
 // ---------------------------------------------------------------------------
 struct ExpandArgs {
-  const int32_t *status;
-  const int32_t *tok_ptr, *tok_tuple, *tup_adapter;
-  const float *tup_alpha;
-  const int32_t *k_dev;
-  const void *B_t;
-  const float *z;  // [n_chunks][cap][r_max]
-  void *y;
-  int64_t ldy;
-  int32_t d_out, r_max, cap, n_chunks, n_coltiles;
+  const int32_t *tok_n;
+  const int4 *tok_rec;  // [T][kSlotPad]
+  int32_t T, n_mods, jobs, jobs_per_xcd;
+  ModArgs m[kMaxMods];
 };
 
+// 8 consecutive weights of one B row
+template <typename TW>
+struct Row8;
+
+template <>
+struct Row8<bf16_t> {
+  uint4 v;
+  __device__ inline void load(const bf16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
+  __device__ inline void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ inline void fma_into(float w, float (&acc)[8]) const {
+    acc[0] = fmaf(w, bf16_lo(v.x), acc[0]);
+    acc[1] = fmaf(w, bf16_hi(v.x), acc[1]);
+    acc[2] = fmaf(w, bf16_lo(v.y), acc[2]);
+    acc[3] = fmaf(w, bf16_hi(v.y), acc[3]);
+    acc[4] = fmaf(w, bf16_lo(v.z), acc[4]);
+    acc[5] = fmaf(w, bf16_hi(v.z), acc[5]);
+    acc[6] = fmaf(w, bf16_lo(v.w), acc[6]);
+    acc[7] = fmaf(w, bf16_hi(v.w), acc[7]);
+  }
+};
+
+template <>
+struct Row8<float> {
+  float4 u, v;
+  __device__ inline void load(const float *p) {
+    u = reinterpret_cast<const float4 *>(p)[0];
+    v = reinterpret_cast<const float4 *>(p)[1];
+  }
+  __device__ inline void zero() { u = v = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ inline void fma_into(float w, float (&acc)[8]) const {
+    acc[0] = fmaf(w, u.x, acc[0]);
+    acc[1] = fmaf(w, u.y, acc[1]);
+    acc[2] = fmaf(w, u.z, acc[2]);
+    acc[3] = fmaf(w, u.w, acc[3]);
+    acc[4] = fmaf(w, v.x, acc[4]);
+    acc[5] = fmaf(w, v.y, acc[5]);
+    acc[6] = fmaf(w, v.z, acc[6]);
+    acc[7] = fmaf(w, v.w, acc[7]);
+  }
+};
+
+// 8 consecutive outputs
+template <typename TY>
+struct Out8;
+
+template <>
+struct Out8<float> {
+  float4 u, v;
+  __device__ inline void load(const float *p) {
+    u = reinterpret_cast<const float4 *>(p)[0];
+    v = reinterpret_cast<const float4 *>(p)[1];
+  }
+  __device__ inline void add_store(float *p, const float (&acc)[8]) {
+    u.x += acc[0]; u.y += acc[1]; u.z += acc[2]; u.w += acc[3];
+    v.x += acc[4]; v.y += acc[5]; v.z += acc[6]; v.w += acc[7];
+    reinterpret_cast<float4 *>(p)[0] = u;
+    reinterpret_cast<float4 *>(p)[1] = v;
+  }
+};
+
+template <>
+struct Out8<bf16_t> {
+  uint4 v;
+  __device__ inline void load(const bf16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
+  __device__ inline void add_store(bf16_t *p, const float (&acc)[8]) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t lo = f32_to_bf16(bf16_lo(w[i]) + acc[2 * i]);
+      const uint16_t hi = f32_to_bf16(bf16_hi(w[i]) + acc[2 * i + 1]);
+      w[i] = uint32_t(lo) | (uint32_t(hi) << 16);
+    }
+    *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+// One wave = 512 consecutive outputs (8 per lane) of one token of one module.
+// Block ids are spread so that every XCD owns a contiguous range of
+// (module, column tile) and all tokens of it: the B rows of a column tile are
+// fetched into one XCD's L2 once and reused by every token that needs them.
+// The token's slot records (padded table, one per lane), its slot count and
+// its y values are loaded together at the start; then the B rows of up to 32
+// (slot, rank) pairs are loaded before any of them is used.  Accumulation is
+// fp32 in slot order, rank order within a slot; y is added once at the end.
 template <int R, typename TW, typename TY>
-__global__ __launch_bounds__(64) void expand_valu(ExpandArgs e) {
-  if (e.status[ST_CODE] != TCL_OK) return;
+__global__ __launch_bounds__(64) void expand_kernel(ExpandArgs e) {
+  constexpr int RB = R < 32 ? R : 32;  // ranks per batch
+  constexpr int SB = 32 / RB;          // slots per batch
   const int lane = threadIdx.x;
-  const int t = blockIdx.x / e.n_coltiles, ct = blockIdx.x - t * e.n_coltiles;
-  const int s0 = e.tok_ptr[t], s1 = e.tok_ptr[t + 1];
-  if (s0 == s1) return;
+  // XCD-aware job index: workgroups are dealt to the 8 XCDs round-robin
+  const int job = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
+  if (job >= e.jobs) return;
+  int mi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMods; ++i)
+    if (i < e.n_mods && job >= e.m[i].first) mi = i;
+  // uniform copies of the selected module's fields (kept in SGPRs, loaded once)
+  const int first = e.m[mi].first, d = e.m[mi].d, r_max = e.m[mi].r_max, zld = e.m[mi].zld;
+  const int64_t ld = e.m[mi].ld;
+  const int32_t *k_dev = e.m[mi].k_dev;
+  const float *Z = e.m[mi].z;
+  const TW *B = static_cast<const TW *>(e.m[mi].W);
+  TY *Y = static_cast<TY *>(e.m[mi].io);
+  const int local = job - first;
+  const int ct = local / e.T, t = local - ct * e.T;
   const int n0 = (ct * 64 + lane) * 8;
-  if (n0 >= e.d_out) return;
-  const TW *B = static_cast<const TW *>(e.B_t);
+  const bool active = n0 < d;
+  TY *Yp = Y + int64_t(t) * ld + n0;
+  Out8<TY> yv;
+  if (active) yv.load(Yp);
+  const int ns = e.tok_n[t];
+  const int4 rec = e.tok_rec[int64_t(t) * kSlotPad + lane];
+  if (ns <= 0) return;
 
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int i = s0; i < s1; ++i) {
-    const int p = e.tok_tuple[i];
-    const int a = e.tup_adapter[p];
-    const float al = e.tup_alpha[p];
-    const int k = eff_rank(e.k_dev, a, e.r_max);
-    for (int j = 0; j < k; ++j) {
-      float zj = 0.f;
-      for (int c = 0; c < e.n_chunks; ++c) zj += e.z[(int64_t(c) * e.cap + p) * e.r_max + j];
-      const float wj = al * zj;
-      float b[8];
-      load8<TW>(B + (int64_t(a) * e.r_max + j) * e.d_out + n0, b);
+  for (int sb = 0; sb < ns; sb += SB) {
+    int pp[SB], aa[SB], kk[SB];
+    float al[SB];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, b[q], acc[q]);
+    for (int b = 0; b < SB; ++b) {
+      const int sl = sb + b;
+      if (sl < ns) {
+        pp[b] = __builtin_amdgcn_readlane(rec.x, sl);
+        aa[b] = __builtin_amdgcn_readlane(rec.y, sl);
+        al[b] = __int_as_float(__builtin_amdgcn_readlane(rec.z, sl));
+        kk[b] = eff_rank(k_dev, aa[b], r_max);
+      } else {
+        pp[b] = 0;
+        aa[b] = 0;
+        al[b] = 0.f;
+        kk[b] = 0;
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < R; jb += RB) {
+      Row8<TW> bv[SB][RB];
+      float zv[SB][RB];
+      // all loads of the batch first: z rows as whole vectors (entries at or
+      // beyond the effective rank are loaded but never used), B rows of the
+      // retained ranks only
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const float *zrow = Z + int64_t(pp[b]) * zld + jb;
+        if ((zld & 3) == 0) {
+          // padded rows: whole float4s stay inside the row
+          const float4 *zr = reinterpret_cast<const float4 *>(zrow);
+#pragma unroll
+          for (int jj = 0; jj < RB; jj += 4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (jb + jj < kk[b]) v = zr[jj / 4];
+            zv[b][jj] = v.x;
+            zv[b][jj + 1] = v.y;
+            zv[b][jj + 2] = v.z;
+            zv[b][jj + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < RB; ++jj) zv[b][jj] = jb + jj < kk[b] ? zrow[jj] : 0.f;
+        }
+#pragma unroll
+        for (int jj = 0; jj < RB; ++jj) {
+          const int j = jb + jj;
+          if (j < kk[b] && active) bv[b][jj].load(B + (int64_t(aa[b]) * r_max + j) * d + n0);
+          else bv[b][jj].zero();
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < SB; ++b)
+#pragma unroll
+        for (int jj = 0; jj < RB; ++jj)
+          if (jb + jj < kk[b]) bv[b][jj].fma_into(al[b] * zv[b][jj], acc);
     }
   }
-  TY *Y = static_cast<TY *>(e.y);
-  add_store8<TY>(Y + int64_t(t) * e.ldy + n0, acc);
+  if (active) yv.add_store(Yp, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -320,110 +542,92 @@ static int check_dtypes(const tcl_module *m, tcl_dtype xd, tcl_dtype yd, bool ne
   return TCL_OK;
 }
 
-// d_in chunks for the shrink: enough work items to fill the chip, chunks of
-// at least one wave-step (64 granules).
-static int shrink_chunks(const tcl_plan *p, const tcl_module *m, int allow_split) {
-  if (!allow_split) return 1;
-  const int vec = m->wdtype == TCL_BF16 ? 8 : 4;
-  const int n_gran = m->d_in / vec;
-  const int max_chunks = (n_gran + 63) / 64;
-  int est_items = p->L.cap < p->L.N ? p->L.cap : p->L.N;
-  est_items += p->L.cap / (4 * kTile);
-  if (est_items < 1) est_items = 1;
-  int c = (1024 + est_items - 1) / est_items;
-  if (c > max_chunks) c = max_chunks;
-  if (c < 1) c = 1;
-  return c;
-}
-
-static int chunk_gran(const tcl_module *m, int n_chunks) {
-  const int vec = m->wdtype == TCL_BF16 ? 8 : 4;
-  const int n_gran = m->d_in / vec;
-  int g = (n_gran + n_chunks - 1) / n_chunks;
-  return (g + 63) / 64 * 64;
-}
-
-template <int R, typename TIN>
-static void launch_shrink_t(const ShrinkArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((shrink_valu<R, TIN>), dim3(grid), dim3(256), 0, s, a);
-}
-
-static int launch_shrink(const tcl_plan *p, const tcl_module *m, const void *x, int64_t ldx,
-                         float *z, int n_chunks, int zero_tail, hipStream_t s) {
-  ShrinkArgs a;
+// Shrink of n (<= kMaxMods) modules in one launch; z[i] is module i's output.
+static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
+                         const void *const *x, const int64_t *ldx, float *const *z,
+                         const int *zld, int zero_tail, hipStream_t s) {
+  const bool bf = mods[0].wdtype == TCL_BF16;
+  const int rows = bf ? 16 : 4;  // rank rows per workgroup job
+  ShrinkArgs a{};
   a.status = p->d.status;
   a.items = p->d.items;
-  a.tup_token = p->d.tup_token;
-  a.k_dev = m->k_dev;
-  a.A_t = m->A_t;
-  a.x = x;
-  a.ldx = ldx;
-  a.d_in = m->d_in;
-  a.r_max = m->r_max;
-  a.cap = p->L.cap;
-  a.n_chunks = n_chunks;
-  a.chunk_gran = chunk_gran(m, n_chunks);
+  a.n_mods = n;
+  a.items_cap = p->L.items_cap;
   a.zero_tail = zero_tail;
-  a.z = z;
-  int64_t grid = int64_t(p->L.items_cap) * n_chunks;
-  if (grid > 16384) grid = 16384;
-  if (grid < 1) grid = 1;
-  const int R = rank_bucket(m->r_max);
-  logf("shrink: d_in=%d r_max=%d R=%d chunks=%d gran=%d grid=%lld", m->d_in, m->r_max, R,
-       n_chunks, a.chunk_gran, (long long)grid);
-  const bool bf = m->wdtype == TCL_BF16;
-#define TCL_SHRINK_CASE(RR)                                           \
-  case RR:                                                            \
-    if (bf) launch_shrink_t<RR, bf16_t>(a, int(grid), s);             \
-    else launch_shrink_t<RR, float>(a, int(grid), s);                 \
-    break;
-  switch (R) {
-    TCL_SHRINK_CASE(8)
-    TCL_SHRINK_CASE(16)
-    TCL_SHRINK_CASE(32)
-    TCL_SHRINK_CASE(64)
+  int rg = 0;
+  for (int i = 0; i < n; ++i) {
+    ModArgs &M = a.m[i];
+    M.W = mods[i].A_t;
+    M.io = const_cast<void *>(x[i]);
+    M.k_dev = mods[i].k_dev;
+    M.z = z[i];
+    M.zld = zld[i];
+    M.ld = ldx[i];
+    M.d = mods[i].d_in;
+    M.r_max = mods[i].r_max;
+    M.first = rg;
+    M.n_ct = 0;
+    rg += (mods[i].r_max + rows - 1) / rows;
   }
-#undef TCL_SHRINK_CASE
+  a.rg_total = rg;
+  int64_t grid = int64_t(p->L.items_cap) * rg;
+  if (grid > 32768) grid = 32768;
+  if (grid < 1) grid = 1;
+  logf("shrink(%s): modules=%d rank tiles=%d grid=%lld", bf ? "mfma" : "valu", n, rg,
+       (long long)grid);
+  if (bf)
+    hipLaunchKernelGGL(shrink_mfma, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL((shrink_valu<float>), dim3(int(grid)), dim3(256), 0, s, a);
   TCL_HIP(hipGetLastError());
   return TCL_OK;
 }
 
 template <int R, typename TW, typename TY>
 static void launch_expand_t(const ExpandArgs &e, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((expand_valu<R, TW, TY>), dim3(grid), dim3(64), 0, s, e);
+  hipLaunchKernelGGL((expand_kernel<R, TW, TY>), dim3(grid), dim3(64), 0, s, e);
 }
 
-static int launch_expand(const tcl_plan *p, const tcl_module *m, const float *z, int n_chunks,
-                         void *y, int64_t ldy, tcl_dtype yd, hipStream_t s) {
+// Expand of n (<= kMaxMods) modules in one launch.
+static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
+                         float *const *z, const int *zld, void *const *y, const int64_t *ldy,
+                         tcl_dtype yd, hipStream_t s) {
   if (p->L.T == 0) return TCL_OK;
-  ExpandArgs e;
-  e.status = p->d.status;
-  e.tok_ptr = p->d.tok_ptr;
-  e.tok_tuple = p->d.tok_tuple;
-  e.tup_adapter = p->d.tup_adapter;
-  e.tup_alpha = p->d.tup_alpha;
-  e.k_dev = m->k_dev;
-  e.B_t = m->B_t;
-  e.z = z;
-  e.y = y;
-  e.ldy = ldy;
-  e.d_out = m->d_out;
-  e.r_max = m->r_max;
-  e.cap = p->L.cap;
-  e.n_chunks = n_chunks;
-  e.n_coltiles = (m->d_out + 511) / 512;
-  const int64_t grid = int64_t(p->L.T) * e.n_coltiles;
-  if (grid > 0x7fffffff) return fail(TCL_EUNSUPPORTED, "expand grid too large");
-  const int R = rank_bucket(m->r_max);
-  logf("expand: d_out=%d R=%d coltiles=%d grid=%lld chunks=%d", m->d_out, R, e.n_coltiles,
-       (long long)grid, n_chunks);
-  const bool bf = m->wdtype == TCL_BF16;
+  ExpandArgs e{};
+  e.tok_n = p->d.tok_n;
+  e.tok_rec = p->d.tok_rec;
+  e.T = p->L.T;
+  e.n_mods = n;
+  int64_t jobs = 0;
+  int rmax = 1;
+  for (int i = 0; i < n; ++i) {
+    ModArgs &M = e.m[i];
+    M.W = mods[i].B_t;
+    M.io = y[i];
+    M.k_dev = mods[i].k_dev;
+    M.z = z[i];
+    M.zld = zld[i];
+    M.ld = ldy[i];
+    M.d = mods[i].d_out;
+    M.r_max = mods[i].r_max;
+    M.n_ct = (mods[i].d_out + 511) / 512;
+    M.first = int32_t(jobs);
+    jobs += int64_t(M.n_ct) * p->L.T;
+    if (mods[i].r_max > rmax) rmax = mods[i].r_max;
+  }
+  if (jobs > (int64_t(1) << 30)) return fail(TCL_EUNSUPPORTED, "expand grid too large");
+  e.jobs = int32_t(jobs);
+  e.jobs_per_xcd = int32_t((jobs + 7) / 8);
+  const int grid = 8 * e.jobs_per_xcd;
+  const int R = rank_bucket(rmax);
+  logf("expand: modules=%d R=%d jobs=%lld grid=%d", n, R, (long long)jobs, grid);
+  const bool bf = mods[0].wdtype == TCL_BF16;
   const bool ybf = yd == TCL_BF16;
-#define TCL_EXPAND_CASE(RR)                                                   \
-  case RR:                                                                    \
-    if (bf && ybf) launch_expand_t<RR, bf16_t, bf16_t>(e, int(grid), s);      \
-    else if (bf) launch_expand_t<RR, bf16_t, float>(e, int(grid), s);         \
-    else launch_expand_t<RR, float, float>(e, int(grid), s);                  \
+#define TCL_EXPAND_CASE(RR)                                                \
+  case RR:                                                                 \
+    if (bf && ybf) launch_expand_t<RR, bf16_t, bf16_t>(e, grid, s);        \
+    else if (bf) launch_expand_t<RR, bf16_t, float>(e, grid, s);           \
+    else launch_expand_t<RR, float, float>(e, grid, s);                    \
     break;
   switch (R) {
     TCL_EXPAND_CASE(8)
@@ -436,9 +640,12 @@ static int launch_expand(const tcl_plan *p, const tcl_module *m, const float *z,
   return TCL_OK;
 }
 
-static size_t zpart_bytes(const tcl_plan *p, const tcl_module *m) {
-  const int c = shrink_chunks(p, m, 1);
-  return (size_t(c) * size_t(p->L.cap) * size_t(m->r_max) * 4 + 255) & ~size_t(255);
+// z rows in the workspace are padded to a multiple of 4 floats so the expand
+// can read them as whole float4s
+static int z_ld(const tcl_module *m) { return (m->r_max + 3) / 4 * 4; }
+
+static size_t z_bytes(const tcl_plan *p, const tcl_module *m) {
+  return (size_t(p->L.cap) * size_t(z_ld(m)) * 4 + 255) & ~size_t(255);
 }
 
 }  // namespace tcl
@@ -469,8 +676,7 @@ int tcl_workspace_bytes(const tcl_plan *p, const tcl_module *mods, int32_t n_mod
   for (int i = 0; i < n_mods; ++i) {
     int rc = check_plan_module(p, &mods[i]);
     if (rc) return rc;
-    const size_t b = zpart_bytes(p, &mods[i]);
-    if (b > need) need = b;
+    need += z_bytes(p, &mods[i]);
   }
   *bytes = need;
   return TCL_OK;
@@ -484,7 +690,8 @@ int tcl_shrink(const tcl_plan *p, const tcl_module *m, const void *x, int64_t ld
   if ((rc = check_io(x, ldx, m->d_in, "x"))) return rc;
   if (!z) return fail(TCL_EINVAL, "z is NULL");
   if (reinterpret_cast<uintptr_t>(z) & 15) return fail(TCL_EALIGN, "z must be 16-byte aligned");
-  return launch_shrink(p, m, x, ldx, z, 1, 1, static_cast<hipStream_t>(stream));
+  const int zld = m->r_max;
+  return launch_shrink(p, m, 1, &x, &ldx, &z, &zld, 1, static_cast<hipStream_t>(stream));
 }
 
 int tcl_expand(const tcl_plan *p, const tcl_module *m, const float *z, void *y, int64_t ldy,
@@ -494,7 +701,9 @@ int tcl_expand(const tcl_plan *p, const tcl_module *m, const float *z, void *y, 
   if ((rc = check_dtypes(m, m->wdtype, yd, true))) return rc;
   if ((rc = check_io(y, ldy, m->d_out, "y"))) return rc;
   if (!z) return fail(TCL_EINVAL, "z is NULL");
-  return launch_expand(p, m, z, 1, y, ldy, yd, static_cast<hipStream_t>(stream));
+  float *zz = const_cast<float *>(z);
+  const int zld = m->r_max;
+  return launch_expand(p, m, 1, &zz, &zld, &y, &ldy, yd, static_cast<hipStream_t>(stream));
 }
 
 int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
@@ -504,27 +713,35 @@ int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
   if (!p) return fail(TCL_EINVAL, "plan is NULL");
   if (n_mods < 1 || !mods || !x || !ldx || !y || !ldy)
     return fail(TCL_EINVAL, "module, x and y lists are required");
-  size_t need = 0;
+  size_t need = 256;
   for (int i = 0; i < n_mods; ++i) {
     int rc = check_plan_module(p, &mods[i]);
     if (rc) return rc;
     if ((rc = check_dtypes(&mods[i], xd, yd, true))) return rc;
     if ((rc = check_io(x[i], ldx[i], mods[i].d_in, "x"))) return rc;
     if ((rc = check_io(y[i], ldy[i], mods[i].d_out, "y"))) return rc;
-    const size_t b = zpart_bytes(p, &mods[i]);
-    if (b > need) need = b;
+    if (mods[i].wdtype != mods[0].wdtype)
+      return fail(TCL_EUNSUPPORTED, "modules of one call must share a weight dtype");
+    need += z_bytes(p, &mods[i]);
   }
   if (!ws) return fail(TCL_EINVAL, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) & 255)
     return fail(TCL_EALIGN, "workspace must be 256-byte aligned");
   if (ws_bytes < need) return fail(TCL_ENOSPC, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float *zp = static_cast<float *>(ws);
-  for (int i = 0; i < n_mods; ++i) {
-    const int c = shrink_chunks(p, &mods[i], 1);
-    int rc = launch_shrink(p, &mods[i], x[i], ldx[i], zp, c, 0, s);
+  char *wp = static_cast<char *>(ws);
+  for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
+    const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
+    float *z[kMaxMods];
+    int zld[kMaxMods];
+    for (int i = 0; i < n; ++i) {
+      z[i] = reinterpret_cast<float *>(wp);
+      zld[i] = z_ld(&mods[i0 + i]);
+      wp += z_bytes(p, &mods[i0 + i]);
+    }
+    int rc = launch_shrink(p, mods + i0, n, x + i0, ldx + i0, z, zld, 0, s);
     if (rc) return rc;
-    rc = launch_expand(p, &mods[i], zp, c, y[i], ldy[i], yd, s);
+    rc = launch_expand(p, mods + i0, n, z, zld, y + i0, ldy + i0, yd, s);
     if (rc) return rc;
   }
   return TCL_OK;

@@ -3,9 +3,9 @@
 // mapping step of the MAF-MVM kernel; the reorder by LoRA id is what lets one
 // workgroup stream one adapter's factors over a contiguous token run).
 //
-// One workgroup of 1024 threads does the whole stage: validation, canonical
-// slots, a stable counting sort keyed by adapter id, the segment table, the
-// per-token tuple index and the shrink work list.  The sort is deterministic
+// One workgroup does the whole stage: validation, canonical slots, a stable
+// counting sort keyed by adapter id, the segment table, the per-token tuple
+// index (also as packed records for the expand) and the shrink work list.  The sort is deterministic
 // and uses no atomics: groups are split into C contiguous chunks, every chunk
 // counts its tuples per adapter, one exclusive scan over the (adapter, chunk)
 // matrix in adapter-major order gives every (adapter, chunk) its first output
@@ -15,8 +15,10 @@
 // adapter at most once.
 //
 // When the composite table is small (every decode batch) it is copied to LDS
-// first with coalesced loads, so that the serial parts of the stage run on LDS
-// latency instead of a chain of global-memory round trips.
+// first with coalesced loads, and positions are counted directly: every pair
+// scans all pairs and adds up the tuples of smaller adapters and of earlier
+// pairs of its own adapter.  That is O(P^2) work on LDS but needs no scans and
+// no serial chunk walks, which is what a latency-bound decode batch wants.
 
 #include <cstdarg>
 #include <cstdio>
@@ -81,26 +83,37 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.cap = cap;
   l.items_cap = (cap < N ? cap : N) + cap / kTile + 1;
 
-  // LDS staging: gtp, gpp (G+1 each), adapter, alpha, slot, group, pos (NP
-  // each), group tuple base (G), histogram (N * chunks).
+  // Direct path: gtp, gpp (G+1 each), adapter, alpha, slot, group, pos,
+  // tokens-per-pair, head count (NP each) and group tuple base (G) in LDS.
+  const int64_t np16 = (int64_t(NP) + 15) / 16 * 16;
+  const int64_t direct_ints = 3 * int64_t(G) + 2 + 3 * np16 + 3 * int64_t(NP) + 4 * int64_t(N) + 16;
+  // Counting path in LDS: the same without the last two pair arrays, plus
+  // the (adapter, chunk) histogram.
   const int64_t fixed = 3 * int64_t(G) + 2 + 5 * int64_t(NP);
-  int64_t c_small = (NP + 1) / 2;
-  if (c_small < 1) c_small = 1;
-  if (c_small > kPlanThreads) c_small = kPlanThreads;
-  if (fixed + int64_t(N) * c_small > kPlanLdsInts) {
-    int64_t room = kPlanLdsInts - fixed;
-    c_small = room > 0 ? room / N : 0;
-  }
-  if (c_small >= 1) {
-    l.small = 1;
-    l.chunks = int32_t(c_small);
+  if (NP <= kDirectMaxPairs && direct_ints <= kPlanLdsInts) {
+    l.mode = PLAN_DIRECT;
+    l.threads = NP <= 256 ? 256 : kPlanThreads;
+    l.chunks = 1;
   } else {
-    l.small = 0;
+    l.threads = kPlanThreads;
     int64_t c = (NP + 7) / 8;
-    int64_t cmax = 65536 / N;
-    if (c > cmax) c = cmax;
     if (c > kPlanThreads) c = kPlanThreads;
     if (c < 1) c = 1;
+    if (fixed + int64_t(N) * c <= kPlanLdsInts) {
+      l.mode = PLAN_COUNT_LDS;
+    } else {
+      int64_t room = kPlanLdsInts - fixed;
+      int64_t cl = room > 0 ? room / N : 0;
+      if (cl >= 16 || (cl >= 1 && cl >= c)) {
+        l.mode = PLAN_COUNT_LDS;
+        c = cl < c ? cl : c;
+      } else {
+        l.mode = PLAN_COUNT_GLOBAL;
+        int64_t cmax = 65536 / N;
+        if (c > cmax) c = cmax;
+        if (c < 1) c = 1;
+      }
+    }
     l.chunks = int32_t(c);
   }
 
@@ -116,25 +129,25 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.o_slot = take(size_t(cap) * 4);
   l.o_alpha = take(size_t(cap) * 4);
   l.o_toktuple = take(size_t(cap) * 4);
+  l.o_tokrec = take(size_t(T) * kSlotPad * 16);
+  l.o_tokn = take(size_t(T) * 4);
   l.o_tokptr = take(size_t(T + 1) * 4);
   l.o_segad = take(size_t(N) * 4);
   l.o_segbeg = take(size_t(N + 1) * 4);
-  l.o_items = take(size_t(l.items_cap) * 16);
+  l.o_items = take(size_t(l.items_cap) * sizeof(Item));
   l.o_sslot = take(size_t(NP) * 4);
   l.o_sgroup = take(size_t(NP) * 4);
   l.o_spos = take(size_t(NP) * 4);
   l.o_sgbase = take(size_t(G) * 4);
-  l.o_shist = take(l.small ? 4 : size_t(N) * size_t(l.chunks) * 4);
+  l.o_shist = take(l.mode == PLAN_COUNT_GLOBAL ? size_t(N) * size_t(l.chunks) * 4 : 4);
   l.total = o;
   *L = l;
   return TCL_OK;
 }
 
 // ---------------------------------------------------------------------------
-// block-wide helpers (1024 threads = 16 waves of 64)
+// block-wide helpers (NT threads = NT/64 waves of 64)
 // ---------------------------------------------------------------------------
-constexpr int kWaves = kPlanThreads / 64;
-
 __device__ inline int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -145,9 +158,12 @@ __device__ inline int wave_incl_scan(int v) {
   return v;
 }
 
+template <int NT>
 __device__ inline int block_or(int v, int *tmp) {
+  constexpr int kWaves = NT / 64;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off, 64);
+  if (kWaves == 1) return v;
   if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
   __syncthreads();
   int r = 0;
@@ -158,9 +174,15 @@ __device__ inline int block_or(int v, int *tmp) {
 }
 
 // Exclusive prefix of v over thread order; *total receives the block sum.
+template <int NT>
 __device__ inline int block_excl_scan(int v, int *tmp, int *total) {
+  constexpr int kWaves = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int incl = wave_incl_scan(v);
+  if (kWaves == 1) {
+    *total = __shfl(incl, 63, 64);
+    return incl - v;
+  }
   if (lane == 63) tmp[w] = incl;
   __syncthreads();
   if (w == 0) {
@@ -177,52 +199,146 @@ __device__ inline int block_excl_scan(int v, int *tmp, int *total) {
 }
 
 struct PlanArgs {
-  int32_t T, G, NP, N, cap, C, small;
+  int32_t T, G, NP, N, cap, C, mode;
   const int32_t *gtp, *gpp, *pa;
   const float *pw;
   PlanDev d;
 };
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs A) {
-  __shared__ int lds[kPlanLdsInts];
-  __shared__ int tmp[kWaves + 1];
-  const int tid = threadIdx.x;
-  const int T = A.T, G = A.G, NP = A.NP, N = A.N, C = A.C;
+template <int NT>
+__device__ inline void plan_fail(const PlanArgs &A, int code, int P) {
+  for (int t = threadIdx.x; t <= A.T; t += NT) A.d.tok_ptr[t] = 0;
+  for (int t = threadIdx.x; t < A.T; t += NT) A.d.tok_n[t] = 0;
+  if (threadIdx.x == 0) {
+    A.d.status[ST_CODE] = code;
+    A.d.status[ST_TUPLES] = P;
+    A.d.status[ST_SEGMENTS] = 0;
+    A.d.status[ST_ITEMS] = 0;
+  }
+}
 
-  const int32_t *gtp = A.gtp, *gpp = A.gpp, *pa = A.pa;
-  const float *pw = A.pw;
-  int32_t *slot = A.d.s_slot, *grp = A.d.s_group, *pos = A.d.s_pos, *gbase = A.d.s_gbase,
-          *hist = A.d.s_hist;
-  if (A.small) {
+// Device arrays of the mapping stage: the staged composite table and the
+// per-pair / per-group scratch.  In the LDS paths every pointer is derived
+// from the kernel's __shared__ block only, so the compiler emits LDS (ds_*)
+// instructions rather than flat ones.
+struct PlanView {
+  const int32_t *gtp, *gpp, *pa;
+  const float *pw;
+  int32_t *slot, *grp, *pos, *gbase, *hist, *ptl, *hcnt, *ssm, *sib;
+  int32_t *cnt, *sst, *su;  // direct path: per-adapter count, segment start, segment index
+};
+
+template <int NT, int MODE>
+__device__ inline PlanView plan_view(const PlanArgs &A, int *lds) {
+  PlanView v;
+  const int G = A.G, NP = A.NP;
+  if constexpr (MODE == PLAN_COUNT_GLOBAL) {
+    v.gtp = A.gtp;
+    v.gpp = A.gpp;
+    v.pa = A.pa;
+    v.pw = A.pw;
+    v.slot = A.d.s_slot;
+    v.grp = A.d.s_group;
+    v.pos = A.d.s_pos;
+    v.gbase = A.d.s_gbase;
+    v.hist = A.d.s_hist;
+    v.ptl = nullptr;
+    v.hcnt = nullptr;
+    v.ssm = nullptr;
+    v.sib = nullptr;
+    v.cnt = v.sst = v.su = nullptr;
+  } else if constexpr (MODE == PLAN_DIRECT) {
+    // Per-pair arrays first, each padded to a multiple of 16 entries so the
+    // O(P^2) scan can read them 4 at a time; padding holds adapter INT_MAX and
+    // zero tokens so it never counts.
+    const int np16 = (NP + 15) / 16 * 16;
+    const int N = A.N;
+    int *p = lds;
+    int *l_pa = p; p += np16;
+    v.ptl = p; p += np16;
+    v.pos = p; p += np16;  // first the same-adapter rank, then the position
+    float *l_pw = reinterpret_cast<float *>(p); p += NP;
+    v.slot = p; p += NP;
+    v.grp = p; p += NP;
+    int *l_gtp = p; p += G + 1;
+    int *l_gpp = p; p += G + 1;
+    v.gbase = p; p += G;
+    v.cnt = p; p += N;
+    v.sst = p; p += N;
+    v.sib = p; p += N;
+    v.su = p; p += N;
+    v.hist = nullptr;
+    v.hcnt = nullptr;
+    v.ssm = nullptr;
+    for (int i = threadIdx.x; i <= G; i += NT) {
+      l_gtp[i] = A.gtp[i];
+      l_gpp[i] = A.gpp[i];
+    }
+    for (int i = threadIdx.x; i < np16; i += NT) {
+      l_pa[i] = i < NP ? A.pa[i] : 0x7fffffff;
+      v.ptl[i] = 0;
+      v.pos[i] = 0;
+      if (i < NP) l_pw[i] = A.pw[i];
+    }
+    for (int i = threadIdx.x; i < N; i += NT) v.cnt[i] = 0;
+    __syncthreads();
+    v.gtp = l_gtp;
+    v.gpp = l_gpp;
+    v.pa = l_pa;
+    v.pw = l_pw;
+  } else {
+    // stage the composite table in LDS with coalesced loads
     int *p = lds;
     int *l_gtp = p; p += G + 1;
     int *l_gpp = p; p += G + 1;
     int *l_pa = p; p += NP;
     float *l_pw = reinterpret_cast<float *>(p); p += NP;
-    slot = p; p += NP;
-    grp = p; p += NP;
-    pos = p; p += NP;
-    gbase = p; p += G;
-    hist = p;
-    for (int i = tid; i <= G; i += kPlanThreads) {
+    v.slot = p; p += NP;
+    v.grp = p; p += NP;
+    v.pos = p; p += NP;
+    v.gbase = p; p += G;
+    v.ptl = nullptr;
+    v.hcnt = nullptr;
+    v.ssm = nullptr;
+    v.sib = nullptr;
+    v.cnt = v.sst = v.su = nullptr;
+    v.hist = p;
+    for (int i = threadIdx.x; i <= G; i += NT) {
       l_gtp[i] = A.gtp[i];
       l_gpp[i] = A.gpp[i];
     }
-    for (int i = tid; i < NP; i += kPlanThreads) {
+    for (int i = threadIdx.x; i < NP; i += NT) {
       l_pa[i] = A.pa[i];
       l_pw[i] = A.pw[i];
     }
     __syncthreads();
-    gtp = l_gtp;
-    gpp = l_gpp;
-    pa = l_pa;
-    pw = l_pw;
+    v.gtp = l_gtp;
+    v.gpp = l_gpp;
+    v.pa = l_pa;
+    v.pw = l_pw;
   }
+  return v;
+}
 
-  // ---- phase 0: validation, canonical slots ------------------------------
+template <int NT, int MODE>
+__global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
+  constexpr int kWaves = NT / 64;
+  constexpr bool direct = MODE == PLAN_DIRECT;
+  __shared__ __align__(16) int lds[MODE == PLAN_COUNT_GLOBAL ? 4 : kPlanLdsInts];
+  __shared__ int tmp[kWaves + 1];
+  const int tid = threadIdx.x;
+  const int T = A.T, G = A.G, NP = A.NP, N = A.N, C = A.C;
+
+  const PlanView V = plan_view<NT, MODE>(A, lds);
+  const int32_t *gtp = V.gtp, *gpp = V.gpp, *pa = V.pa;
+  const float *pw = V.pw;
+  int32_t *slot = V.slot, *grp = V.grp, *pos = V.pos, *gbase = V.gbase, *hist = V.hist,
+          *ptl = V.ptl, *cnt = V.cnt, *sst = V.sst, *sib = V.sib, *su = V.su;
+
+  // ---- validation and canonical slots ------------------------------------
   int err = 0;
   if (tid == 0 && (gtp[0] != 0 || gtp[G] != T || gpp[0] != 0 || gpp[G] != NP)) err |= EB_INVAL;
-  for (int g = tid; g < G; g += kPlanThreads) {
+  for (int g = tid; g < G; g += NT) {
     const int t0 = gtp[g], t1 = gtp[g + 1], q0 = gpp[g], q1 = gpp[g + 1];
     if (!(0 <= t0 && t0 <= t1 && t1 <= T && 0 <= q0 && q0 <= q1 && q1 <= NP)) {
       err |= EB_INVAL;
@@ -243,128 +359,198 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs A) {
       if (dup) err |= EB_INVAL;
       slot[q] = s;
       grp[q] = g;
+      if constexpr (direct) ptl[q] = t1 - t0;
     }
   }
-  for (int q = tid; q < NP; q += kPlanThreads) {
+  for (int q = tid; q < NP; q += NT) {
     const int aq = pa[q];
     if (aq < 0 || aq >= N) err |= EB_INVAL;
     const uint32_t bits = __float_as_uint(pw[q]);
     if ((bits & 0x7f800000u) == 0x7f800000u) err |= EB_INVAL;
   }
-  err = block_or(err, tmp);
+  err = block_or<NT>(err, tmp);
   if (err) {
-    if (tid == 0) {
-      A.d.status[ST_CODE] = (err & EB_INVAL) ? TCL_EINVAL : TCL_EUNSUPPORTED;
-      A.d.status[ST_TUPLES] = 0;
-      A.d.status[ST_SEGMENTS] = 0;
-      A.d.status[ST_ITEMS] = 0;
-    }
+    plan_fail<NT>(A, (err & EB_INVAL) ? TCL_EINVAL : TCL_EUNSUPPORTED, 0);
     return;
   }
 
-  // ---- phase 1: tuples per group -> group base, token index --------------
+  // ---- tuples per group -> group base, token index -------------------------
   int P = 0;
   {
-    const int per = (G + kPlanThreads - 1) / kPlanThreads;
+    const int per = (G + NT - 1) / NT;
     const int g0 = min(G, tid * per), g1 = min(G, g0 + per);
     int local = 0;
     for (int g = g0; g < g1; ++g) local += (gtp[g + 1] - gtp[g]) * (gpp[g + 1] - gpp[g]);
-    int run = block_excl_scan(local, tmp, &P);
-    for (int g = g0; g < g1; ++g) {
-      const int t0 = gtp[g], t1 = gtp[g + 1], pl = gpp[g + 1] - gpp[g];
-      gbase[g] = run;
-      for (int t = t0; t < t1; ++t) A.d.tok_ptr[t] = run + (t - t0) * pl;
-      run += (t1 - t0) * pl;
+    int run = block_excl_scan<NT>(local, tmp, &P);
+    if (P <= A.cap) {
+      for (int g = g0; g < g1; ++g) {
+        const int t0 = gtp[g], t1 = gtp[g + 1], pl = gpp[g + 1] - gpp[g];
+        gbase[g] = run;
+        for (int t = t0; t < t1; ++t) {
+          A.d.tok_ptr[t] = run + (t - t0) * pl;
+          A.d.tok_n[t] = pl;
+        }
+        run += (t1 - t0) * pl;
+      }
+      if (tid == 0) A.d.tok_ptr[T] = P;
     }
-    if (tid == 0) A.d.tok_ptr[T] = P;
   }
   if (P > A.cap) {
-    if (tid == 0) {
-      A.d.status[ST_CODE] = TCL_ENOSPC;
-      A.d.status[ST_TUPLES] = P;
-      A.d.status[ST_SEGMENTS] = 0;
-      A.d.status[ST_ITEMS] = 0;
-    }
+    plan_fail<NT>(A, TCL_ENOSPC, P);
     return;
   }
 
-  // ---- phase 2: per-chunk tuple counts per adapter ------------------------
-  const int M = N * C;
-  for (int i = tid; i < M; i += kPlanThreads) hist[i] = 0;
-  __syncthreads();
-  const int cg0 = int((int64_t(tid) * G) / C), cg1 = int((int64_t(tid + 1) * G) / C);
-  if (tid < C) {
-    for (int g = cg0; g < cg1; ++g) {
-      const int tl = gtp[g + 1] - gtp[g];
-      for (int q = gpp[g]; q < gpp[g + 1]; ++q) hist[pa[q] * C + tid] += tl;
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 3: exclusive scan over (adapter, chunk), adapter-major -------
-  {
-    const int per = (M + kPlanThreads - 1) / kPlanThreads;
-    const int i0 = min(M, tid * per), i1 = min(M, i0 + per);
-    int local = 0;
-    for (int i = i0; i < i1; ++i) local += hist[i];
-    int tot;
-    int run = block_excl_scan(local, tmp, &tot);
-    for (int i = i0; i < i1; ++i) {
-      const int v = hist[i];
-      hist[i] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 4: segment table and shrink work items -----------------------
-  {
-    const int per = (N + kPlanThreads - 1) / kPlanThreads;
-    const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
-    int nseg = 0, nitem = 0;
-    for (int a = a0; a < a1; ++a) {
-      const int beg = hist[a * C], end = (a + 1 < N) ? hist[(a + 1) * C] : P;
-      const int cnt = end - beg;
-      nseg += cnt > 0;
-      nitem += (cnt + kTile - 1) / kTile;
-    }
-    int U, NI;
-    int u = block_excl_scan(nseg, tmp, &U);
-    int it = block_excl_scan(nitem, tmp, &NI);
-    for (int a = a0; a < a1; ++a) {
-      const int beg = hist[a * C], end = (a + 1 < N) ? hist[(a + 1) * C] : P;
-      if (end > beg) {
-        A.d.seg_adapter[u] = a;
-        A.d.seg_begin[u] = beg;
-        for (int p0 = beg; p0 < end; p0 += kTile)
-          A.d.items[it++] = make_int4(a, p0, min(end, p0 + kTile), u);
-        ++u;
+  int n_items = 0;
+  if constexpr (direct) {
+    // ---- direct count.  position = (tuples of smaller adapters) + (tuples
+    //      of the same adapter in earlier pairs; earlier pairs hold earlier
+    //      tokens).  The first term and the segment/item tables come from
+    //      per-adapter counts and scans over adapters; only the second term
+    //      is a pairwise count, split into (pair, 64-pair chunk) units over
+    //      all threads.  Integer LDS additions make it order-independent.
+    for (int q = tid; q < NP; q += NT) atomicAdd(&cnt[pa[q]], ptl[q]);
+    __syncthreads();
+    {
+      const int per = (N + NT - 1) / NT;
+      const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
+      int c_loc = 0, n_loc = 0, i_loc = 0;
+      for (int a = a0; a < a1; ++a) {
+        const int c = cnt[a];
+        c_loc += c;
+        n_loc += c > 0;
+        i_loc += (c + kTile - 1) / kTile;
+      }
+      int tot, U, NI;
+      int ec = block_excl_scan<NT>(c_loc, tmp, &tot);
+      int en = block_excl_scan<NT>(n_loc, tmp, &U);
+      int ei = block_excl_scan<NT>(i_loc, tmp, &NI);
+      for (int a = a0; a < a1; ++a) {
+        const int c = cnt[a];
+        sst[a] = ec;
+        sib[a] = ei;
+        su[a] = en;
+        if (c > 0) {
+          A.d.seg_adapter[en] = a;
+          A.d.seg_begin[en] = ec;
+          for (int p0 = ec, i = ei; p0 < ec + c; p0 += kTile, ++i)
+            A.d.items[i].head = make_int4(a, p0, min(ec + c, p0 + kTile) - p0, en);
+          ++en;
+          ei += (c + kTile - 1) / kTile;
+        }
+        ec += c;
+      }
+      n_items = NI;
+      if (tid == 0) {
+        A.d.seg_begin[U] = P;
+        A.d.status[ST_TUPLES] = P;
+        A.d.status[ST_SEGMENTS] = U;
+        A.d.status[ST_ITEMS] = NI;
       }
     }
-    if (tid == 0) {
-      A.d.seg_begin[U] = P;
-      A.d.status[ST_TUPLES] = P;
-      A.d.status[ST_SEGMENTS] = U;
-      A.d.status[ST_ITEMS] = NI;
+    {
+      const int nch = (NP + 63) / 64;
+      const int4 *pa4 = reinterpret_cast<const int4 *>(pa);
+      const int4 *tl4 = reinterpret_cast<const int4 *>(ptl);
+      for (int u = tid; u < NP * nch; u += NT) {
+        const int q = u / nch, c = u - q * nch;
+        const int lo = c * 64;
+        if (lo >= q) continue;
+        const int a = pa[q];
+        const int hi = min(q, lo + 64);
+        int part = 0;
+        for (int q2 = lo; q2 < hi; q2 += 16) {
+          int av[16], tv[16];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int4 x = pa4[q2 / 4 + v], y = tl4[q2 / 4 + v];
+            av[4 * v] = x.x; av[4 * v + 1] = x.y; av[4 * v + 2] = x.z; av[4 * v + 3] = x.w;
+            tv[4 * v] = y.x; tv[4 * v + 1] = y.y; tv[4 * v + 2] = y.z; tv[4 * v + 3] = y.w;
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) part += (av[v] == a && q2 + v < hi) ? tv[v] : 0;
+        }
+        if (part) atomicAdd(&pos[q], part);
+      }
     }
-  }
-  __syncthreads();
-
-  // ---- phase 5: each chunk hands out consecutive positions in pair order --
-  if (tid < C) {
-    for (int g = cg0; g < cg1; ++g) {
-      const int tl = gtp[g + 1] - gtp[g];
-      for (int q = gpp[g]; q < gpp[g + 1]; ++q) {
-        const int h = pa[q] * C + tid;
-        pos[q] = hist[h];
-        hist[h] += tl;
+    __syncthreads();
+    for (int q = tid; q < NP; q += NT) pos[q] += sst[pa[q]];
+  } else {
+    // ---- counting sort: per-chunk counts per adapter ----------------------
+    const int M = N * C;
+    for (int i = tid; i < M; i += NT) hist[i] = 0;
+    __syncthreads();
+    const int cg0 = int((int64_t(tid) * G) / C), cg1 = int((int64_t(tid + 1) * G) / C);
+    if (tid < C) {
+      for (int g = cg0; g < cg1; ++g) {
+        const int tl = gtp[g + 1] - gtp[g];
+        for (int q = gpp[g]; q < gpp[g + 1]; ++q) hist[pa[q] * C + tid] += tl;
+      }
+    }
+    __syncthreads();
+    // exclusive scan over (adapter, chunk), adapter-major
+    {
+      const int per = (M + NT - 1) / NT;
+      const int i0 = min(M, tid * per), i1 = min(M, i0 + per);
+      int local = 0;
+      for (int i = i0; i < i1; ++i) local += hist[i];
+      int tot;
+      int run = block_excl_scan<NT>(local, tmp, &tot);
+      for (int i = i0; i < i1; ++i) {
+        const int v = hist[i];
+        hist[i] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    // segment table and shrink work items
+    {
+      const int per = (N + NT - 1) / NT;
+      const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
+      int nseg = 0, nitem = 0;
+      for (int a = a0; a < a1; ++a) {
+        const int beg = hist[a * C], end = (a + 1 < N) ? hist[(a + 1) * C] : P;
+        const int cnt = end - beg;
+        nseg += cnt > 0;
+        nitem += (cnt + kTile - 1) / kTile;
+      }
+      int U, NI;
+      int u = block_excl_scan<NT>(nseg, tmp, &U);
+      int it = block_excl_scan<NT>(nitem, tmp, &NI);
+      for (int a = a0; a < a1; ++a) {
+        const int beg = hist[a * C], end = (a + 1 < N) ? hist[(a + 1) * C] : P;
+        if (end > beg) {
+          A.d.seg_adapter[u] = a;
+          A.d.seg_begin[u] = beg;
+          for (int p0 = beg; p0 < end; p0 += kTile)
+            A.d.items[it++].head = make_int4(a, p0, min(end, p0 + kTile) - p0, u);
+          ++u;
+        }
+      }
+      n_items = NI;
+      if (tid == 0) {
+        A.d.seg_begin[U] = P;
+        A.d.status[ST_TUPLES] = P;
+        A.d.status[ST_SEGMENTS] = U;
+        A.d.status[ST_ITEMS] = NI;
+      }
+    }
+    __syncthreads();
+    // each chunk hands out consecutive positions in pair order
+    if (tid < C) {
+      for (int g = cg0; g < cg1; ++g) {
+        const int tl = gtp[g + 1] - gtp[g];
+        for (int q = gpp[g]; q < gpp[g + 1]; ++q) {
+          const int h = pa[q] * C + tid;
+          pos[q] = hist[h];
+          hist[h] += tl;
+        }
       }
     }
   }
   __syncthreads();
 
-  // ---- phase 6: write the tuples and the per-token index -----------------
-  for (int q = tid; q < NP; q += kPlanThreads) {
+  // ---- write the tuples and the per-token index ---------------------------
+  for (int q = tid; q < NP; q += NT) {
     const int g = grp[q];
     const int t0 = gtp[g], tl = gtp[g + 1] - t0, pl = gpp[g + 1] - gpp[g];
     const int a = pa[q], s = slot[q], base = pos[q], gb = gbase[g];
@@ -376,7 +562,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs A) {
       A.d.tup_alpha[p] = w;
       A.d.tup_slot[p] = s;
       A.d.tok_tuple[gb + i * pl + s] = p;
+      A.d.tok_rec[int64_t(t0 + i) * kSlotPad + s] = make_int4(p, a, __float_as_int(w), s);
+      if constexpr (direct) {
+        const int local = p - sst[a];
+        A.d.items[sib[a] + local / kTile].tok[local % kTile] = t0 + i;
+      }
     }
+  }
+  if constexpr (direct) {
+    if (tid == 0) A.d.status[ST_CODE] = TCL_OK;
+    return;
+  }
+  __syncthreads();
+
+  // ---- inline the token ids of every work item -----------------------------
+  for (int i = tid; i < n_items; i += NT) {
+    const int4 h = A.d.items[i].head;
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) A.d.items[i].tok[j] = A.d.tup_token[h.y + (j < h.z ? j : 0)];
   }
   if (tid == 0) A.d.status[ST_CODE] = TCL_OK;
 }
@@ -392,9 +595,11 @@ static void bind(tcl_plan *p) {
   d.tup_alpha = reinterpret_cast<float *>(b + L.o_alpha);
   d.tok_tuple = reinterpret_cast<int32_t *>(b + L.o_toktuple);
   d.tok_ptr = reinterpret_cast<int32_t *>(b + L.o_tokptr);
+  d.tok_rec = reinterpret_cast<int4 *>(b + L.o_tokrec);
+  d.tok_n = reinterpret_cast<int32_t *>(b + L.o_tokn);
   d.seg_adapter = reinterpret_cast<int32_t *>(b + L.o_segad);
   d.seg_begin = reinterpret_cast<int32_t *>(b + L.o_segbeg);
-  d.items = reinterpret_cast<int4 *>(b + L.o_items);
+  d.items = reinterpret_cast<Item *>(b + L.o_items);
   d.s_slot = reinterpret_cast<int32_t *>(b + L.o_sslot);
   d.s_group = reinterpret_cast<int32_t *>(b + L.o_sgroup);
   d.s_pos = reinterpret_cast<int32_t *>(b + L.o_spos);
@@ -419,15 +624,24 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
   A.N = p->L.N;
   A.cap = p->L.cap;
   A.C = p->L.chunks;
-  A.small = p->L.small;
+  A.mode = p->L.mode;
   A.gtp = c->group_tok_ptr;
   A.gpp = c->group_pair_ptr;
   A.pa = c->pair_adapter;
   A.pw = c->pair_alpha;
   A.d = p->d;
-  logf("plan: T=%d G=%d pairs=%d N=%d cap=%d chunks=%d lds=%d", A.T, A.G, A.NP, A.N, A.cap, A.C,
-       A.small);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, A);
+  logf("plan: T=%d G=%d pairs=%d N=%d cap=%d chunks=%d mode=%d threads=%d", A.T, A.G, A.NP, A.N,
+       A.cap, A.C, A.mode, p->L.threads);
+  if (A.mode == PLAN_DIRECT && p->L.threads == 64)
+    hipLaunchKernelGGL((plan_kernel<64, PLAN_DIRECT>), dim3(1), dim3(64), 0, s, A);
+  else if (A.mode == PLAN_DIRECT)
+    hipLaunchKernelGGL((plan_kernel<256, PLAN_DIRECT>), dim3(1), dim3(256), 0, s, A);
+  else if (A.mode == PLAN_COUNT_LDS)
+    hipLaunchKernelGGL((plan_kernel<kPlanThreads, PLAN_COUNT_LDS>), dim3(1), dim3(kPlanThreads),
+                       0, s, A);
+  else
+    hipLaunchKernelGGL((plan_kernel<kPlanThreads, PLAN_COUNT_GLOBAL>), dim3(1),
+                       dim3(kPlanThreads), 0, s, A);
   TCL_HIP(hipGetLastError());
   return TCL_OK;
 }

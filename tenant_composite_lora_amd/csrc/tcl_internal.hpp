@@ -29,13 +29,20 @@ void logf(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
 // plan layout
 // ---------------------------------------------------------------------------
 
-// Tokens per shrink work item: a segment of L tuples is cut into ceil(L/kTile)
-// items of at most kTile consecutive tuples.
-constexpr int kTile = 8;
-// Threads of the single-workgroup mapping kernel.
+// Tuples per shrink work item: a segment of L tuples is cut into
+// ceil(L/kTile) items of at most kTile consecutive tuples (the M dimension of
+// a 16x16 MFMA tile).
+constexpr int kTile = 16;
+// Largest workgroup of the single-workgroup mapping kernel.
 constexpr int kPlanThreads = 1024;
+// Largest pair count handled by the direct-count mapping path.
+constexpr int kDirectMaxPairs = 512;
+// Slot records per token in the padded token table (= the most pairs a
+// composite may hold).
+constexpr int kSlotPad = TCL_MAX_PAIRS_PER_GROUP;
 // int32 words of LDS the mapping kernel may use to stage the composite table.
-constexpr int kPlanLdsInts = 14336;
+// gfx950 gives a workgroup up to 160 KiB of LDS; the mapping stage uses 128.
+constexpr int kPlanLdsInts = 32768;
 
 // device status words
 enum { ST_CODE = 0, ST_TUPLES = 1, ST_SEGMENTS = 2, ST_ITEMS = 3, ST_WORDS = 64 };
@@ -46,22 +53,37 @@ enum { EB_INVAL = 1, EB_UNSUP = 2, EB_NOSPC = 4 };
 struct PlanLayout {
   // sizes
   int32_t T, G, NP, N, cap, items_cap;
-  int32_t chunks;   // groups are split into this many contiguous chunks
-  int32_t small;    // 1: stage the table and scratch in LDS
+  int32_t chunks;   // counting path: groups are split into this many chunks
+  int32_t mode;     // PLAN_DIRECT, PLAN_COUNT_LDS or PLAN_COUNT_GLOBAL
+  int32_t threads;  // workgroup size of the mapping kernel (64, 256 or 1024)
   // byte offsets inside the device buffer
-  size_t o_status, o_tok, o_ad, o_slot, o_alpha, o_toktuple, o_tokptr, o_segad, o_segbeg,
-      o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, total;
+  size_t o_status, o_tok, o_ad, o_slot, o_alpha, o_toktuple, o_tokrec, o_tokn, o_tokptr,
+      o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, total;
 };
 
+// Mapping-stage algorithms: small tables count positions directly (every pair
+// scans all pairs, O(P^2) on LDS, no scans); larger ones run the chunked
+// counting sort with its scratch in LDS or, beyond LDS, in the plan buffer.
+enum { PLAN_DIRECT = 0, PLAN_COUNT_LDS = 1, PLAN_COUNT_GLOBAL = 2 };
+
 int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLayout *L);
+
+// A shrink work item: up to kTile consecutive tuples of one adapter's
+// segment, with their token ids inlined so a wave needs one load to start.
+struct Item {
+  int4 head;    // adapter, first tuple, tuple count, segment index
+  int tok[kTile];  // token ids of the tuples (unused entries repeat the first)
+};
 
 struct PlanDev {
   int32_t *status;
   int32_t *tup_token, *tup_adapter, *tup_slot;
   float *tup_alpha;
   int32_t *tok_tuple, *tok_ptr;
+  int4 *tok_rec;   // [T][kSlotPad]: {tuple index, adapter, alpha bits, slot}
+  int32_t *tok_n;  // [T] slots per token
   int32_t *seg_adapter, *seg_begin;
-  int4 *items;
+  Item *items;
   int32_t *s_slot, *s_group, *s_pos, *s_gbase, *s_hist;
 };
 
