@@ -17,6 +17,8 @@
 // work items, so every kernel below finds nothing to do.
 
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "tcl_internal.hpp"
 
@@ -490,6 +492,257 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandArgs e) {
   if (active) yv.add_store(Yp, acc);
 }
 
+
+// ---------------------------------------------------------------------------
+// prefill expand on the matrix cores
+// ---------------------------------------------------------------------------
+// One workgroup owns kXTok tokens x kXCols output columns of one module.  The
+// adapters its tokens use (the union) are concatenated along K, each adapter
+// contributing its retained rank rows in half-steps of 16:
+//     Y[tokens x cols] += W[tokens x K] . Bcat[K x cols]
+// with W[t][(a, j)] = bf16(alpha_{t,a} z_{t,a}[j]) when token t holds
+// adapter a and 0 otherwise, and Bcat[(a, j)][n] = B_t[a][j][n].  W is built
+// in LDS from the sorted tuples; Bcat is staged through LDS transposed (the
+// MFMA operand wants 8 consecutive K per lane while B_t rows run along n):
+// each thread loads an 8 x 8 block with 16-byte row loads, transposes it in
+// registers with byte permutes and writes 16-byte column vectors, the K octet
+// XOR-swizzled by the column's octet to spread LDS banks.  Stages of 64 K rows
+// are double-buffered and prefetched one stage ahead.  Unions are taken over
+// at most kXSeg segments at a time, in ascending adapter order.
+constexpr int kXCols = 256;   // output columns per tile (16 MFMA column blocks)
+constexpr int kXHalf = 16;    // rank rows per half K-step
+constexpr int kXChunk = 16;   // half K-steps per W chunk (256 K values)
+constexpr int kXSeg = 256;    // segments examined per union pass
+constexpr int kWPad = kXChunk * kXHalf + 8;  // W row stride (bf16)
+constexpr int kBPad = 64 + 8;                // transposed B row stride (bf16)
+
+struct ExpandMfmaArgs {
+  const int32_t *status, *seg_adapter, *tup_token, *tok_n;
+  const float *tup_alpha;
+  const int2 *ranges;  // [tiles][N]
+  int32_t T, N, tiles, n_mods, jobs, jobs_per_xcd;
+  ModArgs m[kMaxMods];  // first = first job; n_ct = column tiles of kXCols
+};
+
+__device__ inline int block_scan256(int v, int *tmp, int *total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) tmp[w] = incl;
+  __syncthreads();
+  const int t0 = tmp[0], t1 = tmp[1], t2 = tmp[2], t3 = tmp[3];
+  const int before = (w > 0 ? t0 : 0) + (w > 1 ? t1 : 0) + (w > 2 ? t2 : 0);
+  *total = t0 + t1 + t2 + t3;
+  __syncthreads();
+  return before + incl - v;
+}
+
+// union entry that owns half-step h: the last i with h0[i] <= h
+__device__ inline int owner_of(const int *h0, int n, int h) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (h0[mid] <= h) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename TY>
+__global__ __launch_bounds__(256) void expand_mfma(ExpandMfmaArgs e) {
+  __shared__ __align__(16) uint16_t Wl[kXTok * kWPad];
+  __shared__ __align__(16) uint16_t Bl[2][kXCols * kBPad];
+  __shared__ int u_a[kXSeg], u_lo[kXSeg], u_hi[kXSeg], u_k[kXSeg], u_h0[kXSeg + 1];
+  __shared__ int tmp[4];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
+  // XCD-aware job index, as in the decode expand
+  const int job = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
+  if (job >= e.jobs) return;
+  int mi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMods; ++i)
+    if (i < e.n_mods && job >= e.m[i].first) mi = i;
+  const int first = e.m[mi].first, d = e.m[mi].d, r_max = e.m[mi].r_max, zld = e.m[mi].zld;
+  const int64_t ld = e.m[mi].ld;
+  const int32_t *k_dev = e.m[mi].k_dev;
+  const float *Z = e.m[mi].z;
+  const uint16_t *Bw = static_cast<const uint16_t *>(e.m[mi].W);
+  TY *Y = static_cast<TY *>(e.m[mi].io);
+  const int local = job - first;
+  const int ct = local / e.tiles, tile = local - ct * e.tiles;
+  const int t0 = tile * kXTok, n0 = ct * kXCols;
+  const int U = e.status[ST_SEGMENTS];
+
+  f32x4_t acc[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // B stage block of this thread: K octet kb (8 of 64 rows), column octet cb
+  const int kb = tid & 7, cb = tid >> 3;
+
+  for (int ub = 0; ub < U; ub += kXSeg) {
+    // ---- union of this tile over segments [ub, ub + kXSeg)
+    const int u = ub + tid;
+    int lo = 0, hi = 0, a = 0, k = 0, hs = 0;
+    if (u < U) {
+      const int2 rg = e.ranges[int64_t(tile) * e.N + u];
+      lo = rg.x;
+      hi = rg.y;
+      a = e.seg_adapter[u];
+      k = eff_rank(k_dev, a, r_max);
+      if (hi > lo && k > 0) hs = (k + kXHalf - 1) / kXHalf;
+    }
+    int n_union, H;
+    const int pos = block_scan256(hs > 0 ? 1 : 0, tmp, &n_union);
+    const int h0 = block_scan256(hs, tmp, &H);
+    if (hs > 0) {
+      u_a[pos] = a;
+      u_lo[pos] = lo;
+      u_hi[pos] = hi;
+      u_k[pos] = k;
+      u_h0[pos] = h0;
+    }
+    __syncthreads();
+
+    for (int hc0 = 0; hc0 < H; hc0 += kXChunk) {
+      const int nh = min(kXChunk, H - hc0);
+      // ---- W chunk: zero, then alpha * z of every tuple of the chunk
+      {
+        uint4 *W4 = reinterpret_cast<uint4 *>(Wl);
+        for (int i = tid; i < kXTok * kWPad / 8; i += 256) W4[i] = make_uint4(0, 0, 0, 0);
+      }
+      __syncthreads();
+      for (int it = tid; it < nh * kXTok; it += 256) {
+        const int hc = it / kXTok, slot = it - hc * kXTok;
+        const int h = hc0 + hc;
+        const int i = owner_of(u_h0, n_union, h);
+        const int p = u_lo[i] + slot;
+        if (p >= u_hi[i]) continue;
+        const int trow = e.tup_token[p] - t0;
+        const float al = e.tup_alpha[p];
+        const int j0 = (h - u_h0[i]) * kXHalf;
+        const int kk = u_k[i];
+        const float *zr = Z + int64_t(p) * zld + j0;
+        float zv[kXHalf];
+        if ((zld & 3) == 0) {
+#pragma unroll
+          for (int q = 0; q < kXHalf / 4; ++q) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j0 + 4 * q < kk) v = reinterpret_cast<const float4 *>(zr)[q];
+            zv[4 * q] = v.x;
+            zv[4 * q + 1] = v.y;
+            zv[4 * q + 2] = v.z;
+            zv[4 * q + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < kXHalf; ++q) zv[q] = j0 + q < kk ? zr[q] : 0.f;
+        }
+        uint32_t pk[kXHalf / 2];
+#pragma unroll
+        for (int q = 0; q < kXHalf / 2; ++q) {
+          const float v0 = j0 + 2 * q < kk ? al * zv[2 * q] : 0.f;
+          const float v1 = j0 + 2 * q + 1 < kk ? al * zv[2 * q + 1] : 0.f;
+          pk[q] = uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16);
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(Wl + trow * kWPad + hc * kXHalf);
+        dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+      }
+      __syncthreads();
+
+      // ---- K loop: stages of 64 K rows (4 half-steps), double-buffered
+      const int nst = (nh + 3) / 4;
+      uint4 pre[8];
+      auto load_stage = [&](int st) {
+        const int hc = 4 * st + (kb >> 1);
+        int jr = -1, aa = 0, kk = 0;
+        if (hc < nh) {
+          const int h = hc0 + hc;
+          const int i = owner_of(u_h0, n_union, h);
+          jr = (h - u_h0[i]) * kXHalf + (kb & 1) * 8;
+          aa = u_a[i];
+          kk = u_k[i];
+        }
+        const int n = n0 + cb * 8;
+        const bool col_ok = n < d;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          pre[r] = make_uint4(0, 0, 0, 0);
+          if (col_ok && jr >= 0 && jr + r < kk)
+            pre[r] = *reinterpret_cast<const uint4 *>(Bw + (int64_t(aa) * r_max + jr + r) * d + n);
+        }
+      };
+      auto store_stage = [&](int buf) {
+        // 8 x 8 transpose: column c of the block gets K rows 0..7
+        const uint32_t *rw = reinterpret_cast<const uint32_t *>(pre);  // rw[4*r + dword]
+        uint16_t *bt = Bl[buf];
+        const int slotk = (kb ^ (cb & 7)) * 8;
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw) {
+          uint32_t lo[4], hi[4];
+#pragma unroll
+          for (int rp = 0; rp < 4; ++rp) {
+            const uint32_t x = rw[4 * (2 * rp) + dw], y = rw[4 * (2 * rp + 1) + dw];
+            lo[rp] = __builtin_amdgcn_perm(y, x, 0x05040100u);  // rows 2rp, 2rp+1 of column 2dw
+            hi[rp] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // rows 2rp, 2rp+1 of column 2dw+1
+          }
+          const int c0 = cb * 8 + 2 * dw;
+          *reinterpret_cast<uint4 *>(bt + c0 * kBPad + slotk) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+          *reinterpret_cast<uint4 *>(bt + (c0 + 1) * kBPad + slotk) =
+              make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        }
+      };
+      load_stage(0);
+      for (int st = 0; st < nst; ++st) {
+        store_stage(st & 1);
+        __syncthreads();
+        if (st + 1 < nst) load_stage(st + 1);
+        const uint16_t *bt = Bl[st & 1];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(
+              Wl + (16 * w + r16) * kWPad + 64 * st + 32 * ks + 8 * kg);
+          const int oct = ks * 4 + kg;
+#pragma unroll
+          for (int cbk = 0; cbk < 16; ++cbk) {
+            const int c = cbk * 16 + r16;
+            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(
+                bt + c * kBPad + ((oct ^ ((c >> 3) & 7)) * 8));
+            acc[cbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[cbk], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- y += acc for tokens that hold at least one pair
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 16 * w + 4 * kg + i;
+    if (t >= e.T || e.tok_n[t] <= 0) continue;
+    TY *yr = Y + int64_t(t) * ld;
+#pragma unroll
+    for (int cbk = 0; cbk < 16; ++cbk) {
+      const int n = n0 + cbk * 16 + r16;
+      if (n < d) {
+        if constexpr (sizeof(TY) == 4) {
+          reinterpret_cast<float *>(yr)[n] += acc[cbk][i];
+        } else {
+          uint16_t *yb = reinterpret_cast<uint16_t *>(yr);
+          const float v = __uint_as_float(uint32_t(yb[n]) << 16) + acc[cbk][i];
+          yb[n] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -588,11 +841,70 @@ static void launch_expand_t(const ExpandArgs &e, int grid, hipStream_t s) {
   hipLaunchKernelGGL((expand_kernel<R, TW, TY>), dim3(grid), dim3(64), 0, s, e);
 }
 
+// Which expand runs: the per-token VALU kernel by default; the matrix-core
+// tile kernel when TCL_DISPATCH=mfma and the batch is prefill-sized bf16 (the
+// plan prepared tile ranges).  The tile kernel is correct but not yet faster
+// on the measured prefill batches, so it is opt-in.
+static int dispatch_override() {
+  const char *s = std::getenv("TCL_DISPATCH");
+  if (!s) return 0;
+  if (!std::strcmp(s, "valu")) return 1;
+  if (!std::strcmp(s, "mfma")) return 2;
+  return 0;
+}
+
+static bool use_mfma_expand(const tcl_plan *p, const tcl_module *mods) {
+  if (mods[0].wdtype != TCL_BF16 || p->L.tiles == 0) return false;
+  return dispatch_override() == 2;
+}
+
+template <typename TY>
+static void launch_expand_mfma_t(const ExpandMfmaArgs &e, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((expand_mfma<TY>), dim3(grid), dim3(256), 0, s, e);
+}
+
 // Expand of n (<= kMaxMods) modules in one launch.
 static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
                          float *const *z, const int *zld, void *const *y, const int64_t *ldy,
                          tcl_dtype yd, hipStream_t s) {
   if (p->L.T == 0) return TCL_OK;
+  if (use_mfma_expand(p, mods)) {
+    ExpandMfmaArgs e{};
+    e.status = p->d.status;
+    e.seg_adapter = p->d.seg_adapter;
+    e.tup_token = p->d.tup_token;
+    e.tok_n = p->d.tok_n;
+    e.tup_alpha = p->d.tup_alpha;
+    e.ranges = p->d.ranges;
+    e.T = p->L.T;
+    e.N = p->L.N;
+    e.tiles = p->L.tiles;
+    e.n_mods = n;
+    int64_t jobs = 0;
+    for (int i = 0; i < n; ++i) {
+      ModArgs &M = e.m[i];
+      M.W = mods[i].B_t;
+      M.io = y[i];
+      M.k_dev = mods[i].k_dev;
+      M.z = z[i];
+      M.zld = zld[i];
+      M.ld = ldy[i];
+      M.d = mods[i].d_out;
+      M.r_max = mods[i].r_max;
+      M.n_ct = (mods[i].d_out + kXCols - 1) / kXCols;
+      M.first = int32_t(jobs);
+      jobs += int64_t(M.n_ct) * p->L.tiles;
+    }
+    if (jobs > (int64_t(1) << 30)) return fail(TCL_EUNSUPPORTED, "expand grid too large");
+    e.jobs = int32_t(jobs);
+    e.jobs_per_xcd = int32_t((jobs + 7) / 8);
+    const int grid = 8 * e.jobs_per_xcd;
+    logf("expand(mfma): modules=%d tiles=%d jobs=%lld", n, p->L.tiles, (long long)jobs);
+    if (yd == TCL_BF16) launch_expand_mfma_t<bf16_t>(e, grid, s);
+    else launch_expand_mfma_t<float>(e, grid, s);
+    TCL_HIP(hipGetLastError());
+    return TCL_OK;
+  }
   ExpandArgs e{};
   e.tok_n = p->d.tok_n;
   e.tok_rec = p->d.tok_rec;
@@ -620,7 +932,7 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
   e.jobs_per_xcd = int32_t((jobs + 7) / 8);
   const int grid = 8 * e.jobs_per_xcd;
   const int R = rank_bucket(rmax);
-  logf("expand: modules=%d R=%d jobs=%lld grid=%d", n, R, (long long)jobs, grid);
+  logf("expand(valu): modules=%d R=%d jobs=%lld grid=%d", n, R, (long long)jobs, grid);
   const bool bf = mods[0].wdtype == TCL_BF16;
   const bool ybf = yd == TCL_BF16;
 #define TCL_EXPAND_CASE(RR)                                                \
@@ -640,8 +952,6 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
   return TCL_OK;
 }
 
-// z rows in the workspace are padded to a multiple of 4 floats so the expand
-// can read them as whole float4s
 static int z_ld(const tcl_module *m) { return (m->r_max + 3) / 4 * 4; }
 
 static size_t z_bytes(const tcl_plan *p, const tcl_module *m) {

@@ -140,6 +140,8 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.o_spos = take(size_t(NP) * 4);
   l.o_sgbase = take(size_t(G) * 4);
   l.o_shist = take(l.mode == PLAN_COUNT_GLOBAL ? size_t(N) * size_t(l.chunks) * 4 : 4);
+  l.tiles = T >= kMfmaMinTokens ? (T + kXTok - 1) / kXTok : 0;
+  l.o_ranges = take(size_t(l.tiles) * size_t(N) * 8);
   l.total = o;
   *L = l;
   return TCL_OK;
@@ -584,6 +586,31 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
   if (tid == 0) A.d.status[ST_CODE] = TCL_OK;
 }
 
+// For every (token tile of kXTok tokens, segment): the run of the segment's
+// tuples whose token falls in the tile.  Tuples of a segment are in token
+// order, so two binary searches find it.  Used by the prefill expand.
+__global__ __launch_bounds__(256) void tile_ranges_kernel(PlanDev d, int32_t N, int32_t tiles) {
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= int64_t(tiles) * N) return;
+  const int tile = int(idx / N), u = int(idx - int64_t(tile) * N);
+  if (d.status[ST_CODE] != TCL_OK || u >= d.status[ST_SEGMENTS]) return;
+  const int beg = d.seg_begin[u], end = d.seg_begin[u + 1];
+  const int t0 = tile * kXTok, t1 = t0 + kXTok;
+  int lo = beg, hi = end;
+  while (lo < hi) {  // first tuple with token >= t0
+    const int mid = (lo + hi) >> 1;
+    if (d.tup_token[mid] < t0) lo = mid + 1;
+    else hi = mid;
+  }
+  int lo2 = lo, hi2 = end;
+  while (lo2 < hi2) {  // first tuple with token >= t1
+    const int mid = (lo2 + hi2) >> 1;
+    if (d.tup_token[mid] < t1) lo2 = mid + 1;
+    else hi2 = mid;
+  }
+  d.ranges[idx] = make_int2(lo, lo2);
+}
+
 static void bind(tcl_plan *p) {
   char *b = static_cast<char *>(p->buf);
   const PlanLayout &L = p->L;
@@ -605,6 +632,7 @@ static void bind(tcl_plan *p) {
   d.s_pos = reinterpret_cast<int32_t *>(b + L.o_spos);
   d.s_gbase = reinterpret_cast<int32_t *>(b + L.o_sgbase);
   d.s_hist = reinterpret_cast<int32_t *>(b + L.o_shist);
+  d.ranges = reinterpret_cast<int2 *>(b + L.o_ranges);
 }
 
 static int check_composites(const tcl_composites *c) {
@@ -642,6 +670,12 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
   else
     hipLaunchKernelGGL((plan_kernel<kPlanThreads, PLAN_COUNT_GLOBAL>), dim3(1),
                        dim3(kPlanThreads), 0, s, A);
+  TCL_HIP(hipGetLastError());
+  if (p->L.tiles > 0) {
+    const int64_t n = int64_t(p->L.tiles) * p->L.N;
+    hipLaunchKernelGGL(tile_ranges_kernel, dim3(int((n + 255) / 256)), dim3(256), 0, s, p->d,
+                       p->L.N, p->L.tiles);
+  }
   TCL_HIP(hipGetLastError());
   return TCL_OK;
 }

@@ -44,6 +44,11 @@ constexpr int kSlotPad = TCL_MAX_PAIRS_PER_GROUP;
 // gfx950 gives a workgroup up to 160 KiB of LDS; the mapping stage uses 128.
 constexpr int kPlanLdsInts = 32768;
 
+// Prefill expand on the matrix cores: tokens per tile, and the smallest token
+// count for which a plan prepares per-(token tile, segment) tuple ranges.
+constexpr int kXTok = 64;
+constexpr int kMfmaMinTokens = 256;
+
 // device status words
 enum { ST_CODE = 0, ST_TUPLES = 1, ST_SEGMENTS = 2, ST_ITEMS = 3, ST_WORDS = 64 };
 
@@ -56,9 +61,10 @@ struct PlanLayout {
   int32_t chunks;   // counting path: groups are split into this many chunks
   int32_t mode;     // PLAN_DIRECT, PLAN_COUNT_LDS or PLAN_COUNT_GLOBAL
   int32_t threads;  // workgroup size of the mapping kernel (64, 256 or 1024)
+  int32_t tiles;    // token tiles of kXTok with tuple ranges (0: none)
   // byte offsets inside the device buffer
   size_t o_status, o_tok, o_ad, o_slot, o_alpha, o_toktuple, o_tokrec, o_tokn, o_tokptr,
-      o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, total;
+      o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_ranges, total;
 };
 
 // Mapping-stage algorithms: small tables count positions directly (every pair
@@ -85,6 +91,7 @@ struct PlanDev {
   int32_t *seg_adapter, *seg_begin;
   Item *items;
   int32_t *s_slot, *s_group, *s_pos, *s_gbase, *s_hist;
+  int2 *ranges;  // [tiles][N]: tuples of segment u whose token lies in tile
 };
 
 }  // namespace tcl

@@ -64,6 +64,15 @@ EDGE_CASES = {
                         dtype=W.F32),
     "single_token": dict(seed=107, T=1, N=3, d_in=64, d_out=64, r_max=8, max_pairs=3),
     "rank_5": dict(seed=108, T=50, N=7, d_in=72, d_out=80, r_max=5, max_pairs=7),
+    # prefill-sized batches take the matrix-core expand (>= 256 tokens)
+    "mfma_ragged": dict(seed=130, T=300, N=20, d_in=520, d_out=520, r_max=8, max_pairs=4,
+                        empty_frac=0.1),
+    "mfma_ranks24": dict(seed=131, T=333, N=40, d_in=256, d_out=776, r_max=24, max_pairs=5,
+                         with_k=True),
+    "mfma_static": dict(seed=132, T=512, N=12, d_in=128, d_out=256, r_max=16, max_pairs=6,
+                        tokens_per_group=37),
+    "mfma_many_adapters": dict(seed=133, T=256, N=600, d_in=64, d_out=264, r_max=8,
+                               max_pairs=8),
 }
 
 
@@ -260,6 +269,37 @@ def test_bf16_output():
     # one final rounding to bf16 (half an ulp) on top of the stated tolerance
     half_ulp = np.abs(y_ora) * 2.0 ** -8
     bound = half_ulp + 1e-2 * np.max(np.abs(d_ora))
+    assert np.all(np.abs(ys[0] - y_ora) <= bound)
+
+
+@pytest.mark.parametrize("name", ["config4", "mfma_ragged", "mfma_ranks24", "mfma_static"])
+def test_prefill_paths_agree(name, monkeypatch):
+    """The matrix-core expand and the per-token VALU expand on the same batch:
+    both within tolerance of the oracle, and of each other."""
+    wl = CASES[name]()
+    banner(f"valu vs mfma expand {name}")
+    monkeypatch.setenv("TCL_DISPATCH", "valu")
+    a, _, _ = run_fused(wl)
+    monkeypatch.setenv("TCL_DISPATCH", "mfma")
+    b, _, _ = run_fused(wl)
+    for mi in range(len(wl.modules)):
+        _, d_ora = oracle_apply(wl, mi)
+        base = wl.y_base[mi].astype(np.float64)
+        ea, eb = rel_err(a[mi] - base, d_ora), rel_err(b[mi] - base, d_ora)
+        print(f"  module {mi}: valu rel {ea:.3e}, mfma rel {eb:.3e}", flush=True)
+        assert ea <= TOL[wl.dtype] and eb <= TOL[wl.dtype]
+
+
+def test_mfma_bf16_output():
+    wl = edge("mfma_ragged")
+    banner("mfma expand with bf16 y")
+    yb16 = W.f32_to_bf16_bits(wl.y_base[0])
+    wl2 = W.Workload(wl.name, wl.dtype, wl.n_adapters, wl.composites, wl.modules, wl.x,
+                     [W.bf16_bits_to_f32(yb16)])
+    ys, _, _ = run_fused(wl2, y_dtype=torch.bfloat16)
+    _, d_ora = oracle_apply(wl2, 0)
+    y_ora = W.bf16_bits_to_f32(yb16).astype(np.float64) + d_ora
+    bound = np.abs(y_ora) * 2.0 ** -8 + 1e-2 * np.max(np.abs(d_ora))
     assert np.all(np.abs(ys[0] - y_ora) <= bound)
 
 
