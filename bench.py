@@ -56,6 +56,94 @@ def algorithmic_bytes(wl) -> int:
     return total
 
 
+def kernel_bytes(wl) -> dict:
+    """Algorithmic bytes of each kernel of the step (their sum is the step's
+    algorithmic bytes): shrink reads the touched adapters' retained A rows and
+    x; expand reads their retained B rows and reads and writes y; the mapping
+    stage reads the composite table and writes 16-byte tuple records."""
+    c = wl.composites
+    owner_tokens = np.diff(c.group_tok_ptr)
+    pair_tokens = np.repeat(owner_tokens, np.diff(c.group_pair_ptr))
+    used = np.unique(c.pair_adapter[pair_tokens > 0]) if c.n_pairs else np.zeros(0, np.int64)
+    T = c.n_tokens
+    out = {"shrink": 0, "expand": 0, "plan": c.n_tuples() * 16}
+    for mi, m in enumerate(wl.modules):
+        e_w = 2 if m.A_t.dtype == np.uint16 else 4
+        e_x = 2 if wl.x[mi].dtype == np.uint16 else 4
+        k = np.full(m.A_t.shape[0], m.r_max) if m.k is None else m.k
+        ranks = int(np.sum(k[used]))
+        out["shrink"] += ranks * m.d_in * e_w + T * m.d_in * e_x
+        out["expand"] += ranks * m.d_out * e_w + 2 * T * m.d_out * 4
+    return out
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; a stored counter summary is only valid for the
+    kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tenant_composite_lora_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/pmc_traffic.txt), or None when there is none for this
+    workload or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    ent = rec.get("entries", {}).get(f"{workload}:{kernel}")
+    if not ent or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
+    """HBM traffic per launch of each library kernel from two rocprofv3 --pmc
+    runs of the same bench command (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch).  Each counter is scaled by what it reads for the 256 MiB
+    calibration copy of that run (the largest __amd_rocclr_copyBuffer
+    dispatch): factor = 256 MiB / measured."""
+    import csv
+    import collections
+    calib = 256 << 20
+
+    def load(path):
+        per = collections.defaultdict(list)
+        biggest_copy = 0.0
+        for r in csv.DictReader(open(path)):
+            v = float(r["Counter_Value"]) * 1024.0
+            name = r["Kernel_Name"]
+            if name.startswith("__amd_rocclr_copyBuffer"):
+                biggest_copy = max(biggest_copy, v)
+            for short in ("shrink_mfma", "shrink_valu", "expand_kernel", "expand_mfma",
+                          "plan_kernel", "tile_ranges_kernel"):
+                if short in name:
+                    per[short].append(v)
+        return per, calib / biggest_copy
+
+    f, ff = load(fetch_csv)
+    w, fw = load(write_csv)
+    out = {"source_hash": kernel_source_hash(),
+           "calibration": {"copy_bytes": calib, "fetch_factor": ff, "write_factor": fw},
+           "entries": {}}
+    for k in sorted(set(f) | set(w)):
+        fb = sum(f[k]) / len(f[k]) * ff if f.get(k) else 0.0
+        wb = sum(w[k]) / len(w[k]) * fw if w.get(k) else 0.0
+        out["entries"][f"{workload}:{k}"] = {
+            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+            "hbm_bytes_per_launch": fb + wb, "launches": len(f.get(k, []))}
+    return out
+
+
 def algorithmic_flops(wl) -> int:
     c = wl.composites
     owner_tokens = np.diff(c.group_tok_ptr)
@@ -77,7 +165,7 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
     reps, t_used = 0, 0.0
     sample_tokens = c.n_tokens
     with threadpool_limits(limits=1):
-        while t_used < budget_s and reps < 1000:
+        while t_used < budget_s and reps < 100000:
             t0 = time.perf_counter()
             O.plan(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha)
             for mi, m in enumerate(wl.modules):
@@ -100,10 +188,21 @@ def main():
     ap.add_argument("--eager", action="store_true", help="no HIP graph capture")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the counter summary of two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        names = {1: "tiny_f32_256", 2: "distinct_decode_q4096_n64_r8_t32",
+                 3: "skewed_decode_llama3_8b_7proj_n128_r8_t64",
+                 4: "sparse_prefill_gated_8x256_n128_r16",
+                 5: "retained_rank_mixed_n256_r32_t4224"}
+        print(json.dumps(pmc_summary(*args.pmc_summary, names[args.config]), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by data parallelism with no exchange; see DESIGN.md)",
+              "(one GPU holds one data-parallel shard of the batch)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -166,69 +265,61 @@ def main():
     print(f"[bench] {wl.name}: T={T} P={P_dev} U={U_dev} replicas={R} "
           f"alg bytes={B_alg} flops={F_alg}", file=sys.stderr, flush=True)
 
-    def timed(fn_graphs, n_iters):
+    def timed(run, n_iters):
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             ev0.record(stream)
-            fn_graphs(n_iters)
+            run(n_iters)
             ev1.record(stream)
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / 1e3
 
+    def plan_only(i, spp):
+        tclora.check(L.tcl_plan_remap(plan.handle, ctypes.byref(comp_c), spp))
+
+    phases = {
+        "step": step,
+        "plan": plan_only,
+        "shrink": lambda i, spp: calls[i % R].shrink(spp),
+        "expand": lambda i, spp: calls[i % R].expand(spp),
+    }
     with torch.cuda.stream(stream):
+        for i in range(2):              # warm up before any capture
+            step(i, sp)
+    torch.cuda.synchronize()
+    runners = {}
+    for name, fn in phases.items():
         if args.eager:
-            def run_steps(n):
-                for i in range(n):
-                    step(i, sp)
-
-            def run_apply(n):
-                for i in range(n):
-                    calls[i % R](sp)
-            graphs_needed = False
-        else:
-            graphs_needed = True
-
-    if graphs_needed:
-        # capture one pass over the replicas, twice: full steps and apply only
-        g_step = torch.cuda.CUDAGraph()
-        g_apply = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            for i in range(2):          # warm the allocator before capture
-                step(i, sp)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g_step, stream=stream):
+            runners[name] = (lambda fn: (lambda n: [fn(i, sp) for i in range(n)]))(fn)
+            continue
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
             cs = int(torch.cuda.current_stream().cuda_stream)
             for i in range(S):
-                step(i, cs)
-        with torch.cuda.graph(g_apply, stream=stream):
-            cs = int(torch.cuda.current_stream().cuda_stream)
-            for i in range(S):
-                calls[i % R](cs)
-        torch.cuda.synchronize()
-
-        def run_steps(n):
-            for _ in range(max(1, n // S)):
-                g_step.replay()
-
-        def run_apply(n):
-            for _ in range(max(1, n // S)):
-                g_apply.replay()
+                fn(i, cs)
+        runners[name] = (lambda g: (lambda n: [g.replay() for _ in range(max(1, n // S))]))(g)
+    torch.cuda.synchronize()
 
     K = args.steps if args.eager else max(S, (args.steps // S) * S)
     Wu = args.warmup if args.eager else max(S, (args.warmup // S) * S)
     print(f"[bench] warmup {Wu} steps", file=sys.stderr, flush=True)
-    timed(run_steps, Wu)
+    timed(runners["step"], Wu)
     print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
-    t_steps = timed(run_steps, K)
-    print(f"[bench] timing {K} applies (dominant kernels, no mapping stage)", file=sys.stderr,
-          flush=True)
-    t_apply = timed(run_apply, K)
-    # a plan-only pass for the record
+    t_steps = timed(runners["step"], K)
+    per = {}
+    for name in ("plan", "shrink", "expand"):
+        print(f"[bench] timing {K} launches of the {name} kernel alone", file=sys.stderr,
+              flush=True)
+        per[name] = timed(runners[name], K) / K
+    kb = kernel_bytes(wl)
+    dom = max(("shrink", "expand"), key=lambda n: per[n])
+    achieved = kb[dom] / per[dom] / 1e9
     ms_step = 1e3 * t_steps / K
-    apply_s = t_apply / K
-    achieved = B_alg / apply_s / 1e9
+    kernel_names = {"shrink": "shrink_mfma" if wl.dtype == W.BF16 else "shrink_valu",
+                    "expand": "expand_kernel", "plan": "plan_kernel"}
+    traffic = stored_traffic(wl.name, kernel_names[dom])
     out = {
         "metric": METRIC,
         "value": T * K / t_steps,
@@ -249,14 +340,27 @@ def main():
             "accumulate": "f32", "replicas": R, "graph": not args.eager,
             "alg_bytes_per_step": B_alg, "alg_flops_per_step": F_alg,
             "hbm_gbs_per_step": B_alg / (t_steps / K) / 1e9,
-            "apply_us": apply_s * 1e6, "step_us": ms_step * 1e3,
+            "hbm_frac_per_step": B_alg / (t_steps / K) / 1e9 / HBM_PEAK_GBS,
+            "step_us": ms_step * 1e3,
+            "kernel_us": {n: per[n] * 1e6 for n in per},
+            "kernel_alg_bytes": kb,
+            "kernel_gbs": {n: kb[n] / per[n] / 1e9 for n in per},
         },
         "roofline": {
-            "bound": "hbm", "kernel": "tcl_fused_apply (shrink + expand)",
+            "bound": "hbm", "kernel": kernel_names[dom],
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
         },
     }
+    if args.calibrate_copy:
+        # a plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+        # counters of the same profiling run
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -230,6 +230,23 @@ int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
                     void *const *y, const int64_t *ldy, tcl_dtype yd, void *ws,
                     size_t ws_bytes, void *stream);
 
+/*
+ * The two halves of tcl_fused_apply, for callers that schedule them apart
+ * (e.g. to overlap the expand with other work) and for per-kernel timing:
+ * tcl_fused_shrink launches the multi-module shrink and leaves z in `ws`
+ * (tcl_workspace_bytes); tcl_fused_expand reads z from `ws` and updates y.
+ * Called back to back on one stream with the same plan, modules and
+ * workspace they compute exactly what tcl_fused_apply computes.  Each is one
+ * kernel launch for up to 8 modules.  Same arguments and errors as
+ * tcl_fused_apply.
+ */
+int tcl_fused_shrink(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
+                     const void *const *x, const int64_t *ldx, tcl_dtype xd, void *ws,
+                     size_t ws_bytes, void *stream);
+int tcl_fused_expand(const tcl_plan *p, const tcl_module *mods, int32_t n_mods, void *ws,
+                     size_t ws_bytes, void *const *y, const int64_t *ldy, tcl_dtype yd,
+                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

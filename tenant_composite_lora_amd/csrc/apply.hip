@@ -1016,20 +1016,20 @@ int tcl_expand(const tcl_plan *p, const tcl_module *m, const float *z, void *y, 
   return launch_expand(p, m, 1, &zz, &zld, &y, &ldy, yd, static_cast<hipStream_t>(stream));
 }
 
-int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
-                    const void *const *x, const int64_t *ldx, tcl_dtype xd, void *const *y,
-                    const int64_t *ldy, tcl_dtype yd, void *ws, size_t ws_bytes,
-                    void *stream) {
+// Checks shared by the fused entry points; returns the workspace bytes needed.
+static int check_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
+                       const void *const *x, const int64_t *ldx, tcl_dtype xd, void *const *y,
+                       const int64_t *ldy, tcl_dtype yd, void *ws, size_t ws_bytes) {
   if (!p) return fail(TCL_EINVAL, "plan is NULL");
-  if (n_mods < 1 || !mods || !x || !ldx || !y || !ldy)
-    return fail(TCL_EINVAL, "module, x and y lists are required");
+  if (n_mods < 1 || !mods) return fail(TCL_EINVAL, "module list is required");
+  if ((x && !ldx) || (y && !ldy)) return fail(TCL_EINVAL, "leading dimensions are required");
   size_t need = 256;
   for (int i = 0; i < n_mods; ++i) {
     int rc = check_plan_module(p, &mods[i]);
     if (rc) return rc;
-    if ((rc = check_dtypes(&mods[i], xd, yd, true))) return rc;
-    if ((rc = check_io(x[i], ldx[i], mods[i].d_in, "x"))) return rc;
-    if ((rc = check_io(y[i], ldy[i], mods[i].d_out, "y"))) return rc;
+    if ((rc = check_dtypes(&mods[i], x ? xd : mods[i].wdtype, yd, y != nullptr))) return rc;
+    if (x && (rc = check_io(x[i], ldx[i], mods[i].d_in, "x"))) return rc;
+    if (y && (rc = check_io(y[i], ldy[i], mods[i].d_out, "y"))) return rc;
     if (mods[i].wdtype != mods[0].wdtype)
       return fail(TCL_EUNSUPPORTED, "modules of one call must share a weight dtype");
     need += z_bytes(p, &mods[i]);
@@ -1038,23 +1038,71 @@ int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
   if (reinterpret_cast<uintptr_t>(ws) & 255)
     return fail(TCL_EALIGN, "workspace must be 256-byte aligned");
   if (ws_bytes < need) return fail(TCL_ENOSPC, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return TCL_OK;
+}
+
+// z of module i lives in the workspace after the z of modules 0..i-1
+static void z_slices(const tcl_plan *p, const tcl_module *mods, int i0, int n, void *ws,
+                     float **z, int *zld) {
   char *wp = static_cast<char *>(ws);
+  for (int i = 0; i < i0; ++i) wp += z_bytes(p, &mods[i]);
+  for (int i = 0; i < n; ++i) {
+    z[i] = reinterpret_cast<float *>(wp);
+    zld[i] = z_ld(&mods[i0 + i]);
+    wp += z_bytes(p, &mods[i0 + i]);
+  }
+}
+
+static int run_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
+                     const void *const *x, const int64_t *ldx, void *const *y,
+                     const int64_t *ldy, tcl_dtype yd, void *ws, hipStream_t s) {
   for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
     const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
     float *z[kMaxMods];
     int zld[kMaxMods];
-    for (int i = 0; i < n; ++i) {
-      z[i] = reinterpret_cast<float *>(wp);
-      zld[i] = z_ld(&mods[i0 + i]);
-      wp += z_bytes(p, &mods[i0 + i]);
+    z_slices(p, mods, i0, n, ws, z, zld);
+    if (x) {
+      int rc = launch_shrink(p, mods + i0, n, x + i0, ldx + i0, z, zld, 0, s);
+      if (rc) return rc;
     }
-    int rc = launch_shrink(p, mods + i0, n, x + i0, ldx + i0, z, zld, 0, s);
-    if (rc) return rc;
-    rc = launch_expand(p, mods + i0, n, z, zld, y + i0, ldy + i0, yd, s);
-    if (rc) return rc;
+    if (y) {
+      int rc = launch_expand(p, mods + i0, n, z, zld, y + i0, ldy + i0, yd, s);
+      if (rc) return rc;
+    }
   }
   return TCL_OK;
+}
+
+int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
+                    const void *const *x, const int64_t *ldx, tcl_dtype xd, void *const *y,
+                    const int64_t *ldy, tcl_dtype yd, void *ws, size_t ws_bytes,
+                    void *stream) {
+  if (!x || !y) return fail(TCL_EINVAL, "x and y lists are required");
+  int rc = check_fused(p, mods, n_mods, x, ldx, xd, y, ldy, yd, ws, ws_bytes);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // shrink and expand alternate per batch of up to kMaxMods modules
+  return run_fused(p, mods, n_mods, x, ldx, y, ldy, yd, ws, s);
+}
+
+int tcl_fused_shrink(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
+                     const void *const *x, const int64_t *ldx, tcl_dtype xd, void *ws,
+                     size_t ws_bytes, void *stream) {
+  if (!x) return fail(TCL_EINVAL, "x list is required");
+  int rc = check_fused(p, mods, n_mods, x, ldx, xd, nullptr, nullptr, TCL_F32, ws, ws_bytes);
+  if (rc) return rc;
+  return run_fused(p, mods, n_mods, x, ldx, nullptr, nullptr, TCL_F32, ws,
+                   static_cast<hipStream_t>(stream));
+}
+
+int tcl_fused_expand(const tcl_plan *p, const tcl_module *mods, int32_t n_mods, void *ws,
+                     size_t ws_bytes, void *const *y, const int64_t *ldy, tcl_dtype yd,
+                     void *stream) {
+  if (!y) return fail(TCL_EINVAL, "y list is required");
+  int rc = check_fused(p, mods, n_mods, nullptr, nullptr, TCL_BF16, y, ldy, yd, ws, ws_bytes);
+  if (rc) return rc;
+  return run_fused(p, mods, n_mods, nullptr, nullptr, y, ldy, yd, ws,
+                   static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

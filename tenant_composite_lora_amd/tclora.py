@@ -27,7 +27,8 @@ _NAMES = {OK: "OK", EINVAL: "EINVAL", EALIGN: "EALIGN", ENOSPC: "ENOSPC",
 
 EXPORTS = ["tcl_last_error", "tcl_version", "tcl_plan_bytes", "tcl_plan_map", "tcl_plan_remap",
            "tcl_plan_status", "tcl_plan_copy_out", "tcl_plan_free", "tcl_module_load_ranks",
-           "tcl_workspace_bytes", "tcl_shrink", "tcl_expand", "tcl_fused_apply"]
+           "tcl_workspace_bytes", "tcl_shrink", "tcl_expand", "tcl_fused_apply",
+           "tcl_fused_shrink", "tcl_fused_expand"]
 
 
 class TclError(RuntimeError):
@@ -80,6 +81,10 @@ def lib(path: Optional[str] = None):
     L.tcl_fused_apply.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, ctypes.POINTER(vp),
                                   ctypes.POINTER(i64), i32, ctypes.POINTER(vp),
                                   ctypes.POINTER(i64), i32, vp, sz, vp]
+    L.tcl_fused_shrink.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, ctypes.POINTER(vp),
+                                   ctypes.POINTER(i64), i32, vp, sz, vp]
+    L.tcl_fused_expand.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, vp, sz,
+                                   ctypes.POINTER(vp), ctypes.POINTER(i64), i32, vp]
     if path is None:
         _lib = L
     return L
@@ -303,6 +308,18 @@ class FusedCall:
         check(lib().tcl_fused_apply(self.plan.handle, self.descs, self.n, self.xp, self.ldx,
                                     self.xd, self.yp, self.ldy, self.yd, self.ws.data_ptr(),
                                     self.ws.numel(), _stream(self.xs[0].device, stream)))
+
+    def shrink(self, stream=None):
+        """First half only: z of every module into the workspace."""
+        check(lib().tcl_fused_shrink(self.plan.handle, self.descs, self.n, self.xp, self.ldx,
+                                     self.xd, self.ws.data_ptr(), self.ws.numel(),
+                                     _stream(self.xs[0].device, stream)))
+
+    def expand(self, stream=None):
+        """Second half only: y += aggregated alpha * B z from the workspace."""
+        check(lib().tcl_fused_expand(self.plan.handle, self.descs, self.n, self.ws.data_ptr(),
+                                     self.ws.numel(), self.yp, self.ldy, self.yd,
+                                     _stream(self.xs[0].device, stream)))
 
 
 def fused_apply(plan: Plan, mods: Sequence[Module], xs: Sequence[torch.Tensor],

@@ -382,6 +382,21 @@ def test_alpha_zero_and_rank_zero_are_noops():
     assert np.array_equal(ys[0], wl.y_base[0].astype(np.float64))
 
 
+def test_fused_halves_equal_fused_apply():
+    """tcl_fused_shrink then tcl_fused_expand computes exactly tcl_fused_apply."""
+    wl = cfg(3)
+    banner("fused halves vs fused apply, config3")
+    a, plan, mods = run_fused(wl)
+    xs = [to_dev(x) for x in wl.x]
+    ys = [to_dev(y) for y in wl.y_base]
+    call = tclora.FusedCall(plan, mods, xs, ys)
+    call.shrink()
+    call.expand()
+    torch.cuda.synchronize()
+    for u, v in zip(a, ys):
+        assert np.array_equal(u, v.double().cpu().numpy())
+
+
 def test_retained_rank_equals_padded():
     """k_m on a zero-padded pool equals k = r_max on the same pool, bitwise."""
     wl = W.random_case(120, T=64, N=16, d_in=1024, d_out=768, r_max=32, max_pairs=4,
