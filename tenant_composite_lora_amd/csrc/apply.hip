@@ -105,8 +105,11 @@ struct ModArgs {
   int32_t zld;            // row stride of z (r_max, or r_max rounded up to 4)
   int32_t d;              // shrink: d_in, expand: d_out
   int32_t r_max;
-  int32_t first;          // shrink: first rank group, expand: first job
-  int32_t n_ct;           // expand: column tiles of 512 outputs
+  int32_t first;          // shrink: first unit, expand: first job
+  int32_t n_ct;           // expand: column tiles
+  int32_t nkc;            // K chunks the shrink splits d_in into (z partial planes)
+  int32_t kchunk;         // elements of d_in per K chunk (multiple of 32)
+  int32_t zstride;        // floats per tuple row of z: nkc partial rows of zld
 };
 
 struct ShrinkArgs {
@@ -234,12 +237,16 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
     for (int i = 1; i < kMaxMods; ++i)
       if (i < s.n_mods && rgg >= s.m[i].first) mi = i;
     const int first = s.m[mi].first, dd = s.m[mi].d, r_max = s.m[mi].r_max, zld = s.m[mi].zld;
+    const int nkc = s.m[mi].nkc, kchunk = s.m[mi].kchunk;
     const int64_t ld = s.m[mi].ld;
     const int32_t *k_dev = s.m[mi].k_dev;
-    float *Z = s.m[mi].z;
     const bf16_t *Aw = static_cast<const bf16_t *>(s.m[mi].W);
     const bf16_t *Xw = static_cast<const bf16_t *>(s.m[mi].io);
-    const int j0 = (rgg - first) * 16;
+    const int unit = rgg - first;
+    const int rt = unit / nkc, kc = unit - rt * nkc;  // rank tile, K chunk
+    const int zstride = s.m[mi].zstride;
+    float *Z = s.m[mi].z + kc * zld;  // this chunk's partial row inside each tuple row
+    const int j0 = rt * 16;
     const int a = head.x, p0 = head.y, ntok = head.z;
     const int k = eff_rank(k_dev, a, r_max);
     if (j0 >= k) {
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
       if (s.zero_tail && w == 0) {
         const int j = j0 + row;
         for (int tt = kg; tt < ntok; tt += 4)
-          if (j < r_max) Z[int64_t(p0 + tt) * zld + j] = 0.f;
+          if (j < r_max) Z[int64_t(p0 + tt) * zstride + j] = 0.f;
       }
       continue;
     }
@@ -255,9 +262,10 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
     const int jr = j0 + row;  // rank row this lane feeds
     const bf16_t *Xr = tok >= 0 ? Xw + int64_t(tok) * ld + kg * 8 : nullptr;
     const bf16_t *Ar = jr < k ? Aw + (int64_t(a) * r_max + jr) * dd + kg * 8 : nullptr;
-    const int nsteps = (dd + 31) / 32;
-    const int per = (nsteps + kShrinkWaves - 1) / kShrinkWaves;
-    const int s0 = w * per, s1 = min(nsteps, s0 + per);
+    // K steps of this chunk, split over the waves
+    const int c0 = kc * (kchunk / 32), c1 = min((dd + 31) / 32, c0 + kchunk / 32);
+    const int per = (c1 - c0 + kShrinkWaves - 1) / kShrinkWaves;
+    const int s0 = c0 + w * per, s1 = min(c1, s0 + per);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int st = s0; st < s1; st += kShrinkSteps) {
       bf16x8_t xv[kShrinkSteps], av[kShrinkSteps];
@@ -294,8 +302,8 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
         for (int i = 0; i < 4; ++i) {
           const int tt = 4 * kg + i;
           if (tt < ntok) {
-            if (j < k) Z[int64_t(p0 + tt) * zld + j] = sum[i];
-            else if (s.zero_tail) Z[int64_t(p0 + tt) * zld + j] = 0.f;
+            if (j < k) Z[int64_t(p0 + tt) * zstride + j] = sum[i];
+            else if (s.zero_tail) Z[int64_t(p0 + tt) * zstride + j] = 0.f;
           }
         }
       }
@@ -314,91 +322,107 @@ struct ExpandArgs {
   ModArgs m[kMaxMods];
 };
 
-// 8 consecutive weights of one B row
-template <typename TW>
-struct Row8;
+// C consecutive weights of one B row (C = 2, 4 or 8)
+template <typename TW, int C>
+struct RowN;
 
-template <>
-struct Row8<bf16_t> {
-  uint4 v;
-  __device__ inline void load(const bf16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
-  __device__ inline void zero() { v = make_uint4(0, 0, 0, 0); }
-  __device__ inline void fma_into(float w, float (&acc)[8]) const {
-    acc[0] = fmaf(w, bf16_lo(v.x), acc[0]);
-    acc[1] = fmaf(w, bf16_hi(v.x), acc[1]);
-    acc[2] = fmaf(w, bf16_lo(v.y), acc[2]);
-    acc[3] = fmaf(w, bf16_hi(v.y), acc[3]);
-    acc[4] = fmaf(w, bf16_lo(v.z), acc[4]);
-    acc[5] = fmaf(w, bf16_hi(v.z), acc[5]);
-    acc[6] = fmaf(w, bf16_lo(v.w), acc[6]);
-    acc[7] = fmaf(w, bf16_hi(v.w), acc[7]);
+template <int C>
+struct RowN<bf16_t, C> {
+  uint32_t w[C / 2];
+  __device__ inline void load(const bf16_t *p) {
+    if constexpr (C == 8) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(p);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (C == 4) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(p);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t *>(p);
+    }
   }
-};
-
-template <>
-struct Row8<float> {
-  float4 u, v;
-  __device__ inline void load(const float *p) {
-    u = reinterpret_cast<const float4 *>(p)[0];
-    v = reinterpret_cast<const float4 *>(p)[1];
-  }
-  __device__ inline void zero() { u = v = make_float4(0.f, 0.f, 0.f, 0.f); }
-  __device__ inline void fma_into(float w, float (&acc)[8]) const {
-    acc[0] = fmaf(w, u.x, acc[0]);
-    acc[1] = fmaf(w, u.y, acc[1]);
-    acc[2] = fmaf(w, u.z, acc[2]);
-    acc[3] = fmaf(w, u.w, acc[3]);
-    acc[4] = fmaf(w, v.x, acc[4]);
-    acc[5] = fmaf(w, v.y, acc[5]);
-    acc[6] = fmaf(w, v.z, acc[6]);
-    acc[7] = fmaf(w, v.w, acc[7]);
-  }
-};
-
-// 8 consecutive outputs
-template <typename TY>
-struct Out8;
-
-template <>
-struct Out8<float> {
-  float4 u, v;
-  __device__ inline void load(const float *p) {
-    u = reinterpret_cast<const float4 *>(p)[0];
-    v = reinterpret_cast<const float4 *>(p)[1];
-  }
-  __device__ inline void add_store(float *p, const float (&acc)[8]) {
-    u.x += acc[0]; u.y += acc[1]; u.z += acc[2]; u.w += acc[3];
-    v.x += acc[4]; v.y += acc[5]; v.z += acc[6]; v.w += acc[7];
-    reinterpret_cast<float4 *>(p)[0] = u;
-    reinterpret_cast<float4 *>(p)[1] = v;
-  }
-};
-
-template <>
-struct Out8<bf16_t> {
-  uint4 v;
-  __device__ inline void load(const bf16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
-  __device__ inline void add_store(bf16_t *p, const float (&acc)[8]) {
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  __device__ inline void zero() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < C / 2; ++i) w[i] = 0;
+  }
+  __device__ inline void fma_into(float x, float (&acc)[C]) const {
+#pragma unroll
+    for (int i = 0; i < C / 2; ++i) {
+      acc[2 * i] = fmaf(x, bf16_lo(w[i]), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(x, bf16_hi(w[i]), acc[2 * i + 1]);
+    }
+  }
+};
+
+template <int C>
+struct RowN<float, C> {
+  float f[C];
+  __device__ inline void load(const float *p) {
+#pragma unroll
+    for (int i = 0; i < C; i += 2) {
+      const float2 v = reinterpret_cast<const float2 *>(p)[i / 2];
+      f[i] = v.x;
+      f[i + 1] = v.y;
+    }
+  }
+  __device__ inline void zero() {
+#pragma unroll
+    for (int i = 0; i < C; ++i) f[i] = 0.f;
+  }
+  __device__ inline void fma_into(float x, float (&acc)[C]) const {
+#pragma unroll
+    for (int i = 0; i < C; ++i) acc[i] = fmaf(x, f[i], acc[i]);
+  }
+};
+
+// C consecutive outputs
+template <typename TY, int C>
+struct OutN;
+
+template <int C>
+struct OutN<float, C> {
+  float f[C];
+  __device__ inline void load(const float *p) {
+#pragma unroll
+    for (int i = 0; i < C; i += 2) {
+      const float2 v = reinterpret_cast<const float2 *>(p)[i / 2];
+      f[i] = v.x;
+      f[i + 1] = v.y;
+    }
+  }
+  __device__ inline void add_store(float *p, const float (&acc)[C]) {
+#pragma unroll
+    for (int i = 0; i < C; i += 2)
+      reinterpret_cast<float2 *>(p)[i / 2] = make_float2(f[i] + acc[i], f[i + 1] + acc[i + 1]);
+  }
+};
+
+template <int C>
+struct OutN<bf16_t, C> {
+  uint32_t w[C / 2];
+  __device__ inline void load(const bf16_t *p) {
+#pragma unroll
+    for (int i = 0; i < C / 2; ++i) w[i] = reinterpret_cast<const uint32_t *>(p)[i];
+  }
+  __device__ inline void add_store(bf16_t *p, const float (&acc)[C]) {
+#pragma unroll
+    for (int i = 0; i < C / 2; ++i) {
       const uint16_t lo = f32_to_bf16(bf16_lo(w[i]) + acc[2 * i]);
       const uint16_t hi = f32_to_bf16(bf16_hi(w[i]) + acc[2 * i + 1]);
-      w[i] = uint32_t(lo) | (uint32_t(hi) << 16);
+      reinterpret_cast<uint32_t *>(p)[i] = uint32_t(lo) | (uint32_t(hi) << 16);
     }
-    *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
 
-// One wave = 512 consecutive outputs (8 per lane) of one token of one module.
-// Block ids are spread so that every XCD owns a contiguous range of
+// One wave = 64 * CPL consecutive outputs (CPL per lane) of one token of one
+// module.  Block ids are spread so that every XCD owns a contiguous range of
 // (module, column tile) and all tokens of it: the B rows of a column tile are
 // fetched into one XCD's L2 once and reused by every token that needs them.
 // The token's slot records (padded table, one per lane), its slot count and
 // its y values are loaded together at the start; then the B rows of up to 32
-// (slot, rank) pairs are loaded before any of them is used.  Accumulation is
-// fp32 in slot order, rank order within a slot; y is added once at the end.
-template <int R, typename TW, typename TY>
+// (slot, rank) pairs are loaded before any of them is used.  z is the sum of
+// the shrink's K-chunk partials, added in chunk order.  Accumulation is fp32
+// in slot order, rank order within a slot; y is added once at the end.
+template <int R, int CPL, bool SPLIT, typename TW, typename TY>
 __global__ __launch_bounds__(64) void expand_kernel(ExpandArgs e) {
   constexpr int RB = R < 32 ? R : 32;  // ranks per batch
   constexpr int SB = 32 / RB;          // slots per batch
@@ -412,6 +436,7 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandArgs e) {
     if (i < e.n_mods && job >= e.m[i].first) mi = i;
   // uniform copies of the selected module's fields (kept in SGPRs, loaded once)
   const int first = e.m[mi].first, d = e.m[mi].d, r_max = e.m[mi].r_max, zld = e.m[mi].zld;
+  const int nkc = e.m[mi].nkc, zstride = e.m[mi].zstride;
   const int64_t ld = e.m[mi].ld;
   const int32_t *k_dev = e.m[mi].k_dev;
   const float *Z = e.m[mi].z;
@@ -419,18 +444,18 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandArgs e) {
   TY *Y = static_cast<TY *>(e.m[mi].io);
   const int local = job - first;
   const int ct = local / e.T, t = local - ct * e.T;
-  const int n0 = (ct * 64 + lane) * 8;
+  const int n0 = (ct * 64 + lane) * CPL;
   const bool active = n0 < d;
   TY *Yp = Y + int64_t(t) * ld + n0;
-  Out8<TY> yv;
+  OutN<TY, CPL> yv;
   if (active) yv.load(Yp);
   const int ns = e.tok_n[t];
   const int4 rec = e.tok_rec[int64_t(t) * kSlotPad + lane];
   if (ns <= 0) return;
 
-  float acc[8];
+  float acc[CPL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
   for (int sb = 0; sb < ns; sb += SB) {
     int pp[SB], aa[SB], kk[SB];
     float al[SB];
@@ -451,35 +476,54 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandArgs e) {
     }
 #pragma unroll
     for (int jb = 0; jb < R; jb += RB) {
-      Row8<TW> bv[SB][RB];
+      RowN<TW, CPL> bv[SB][RB];
       float zv[SB][RB];
-      // all loads of the batch first: z rows as whole vectors (entries at or
-      // beyond the effective rank are loaded but never used), B rows of the
-      // retained ranks only
+      // all loads of the batch first: B rows of the retained ranks and z
+      // (entries at or beyond the effective rank are never used).  A split
+      // shrink leaves nkc partial rows per tuple, added here in chunk order.
 #pragma unroll
       for (int b = 0; b < SB; ++b) {
-        const float *zrow = Z + int64_t(pp[b]) * zld + jb;
-        if ((zld & 3) == 0) {
-          // padded rows: whole float4s stay inside the row
-          const float4 *zr = reinterpret_cast<const float4 *>(zrow);
-#pragma unroll
-          for (int jj = 0; jj < RB; jj += 4) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (jb + jj < kk[b]) v = zr[jj / 4];
-            zv[b][jj] = v.x;
-            zv[b][jj + 1] = v.y;
-            zv[b][jj + 2] = v.z;
-            zv[b][jj + 3] = v.w;
-          }
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < RB; ++jj) zv[b][jj] = jb + jj < kk[b] ? zrow[jj] : 0.f;
-        }
 #pragma unroll
         for (int jj = 0; jj < RB; ++jj) {
           const int j = jb + jj;
           if (j < kk[b] && active) bv[b][jj].load(B + (int64_t(aa[b]) * r_max + j) * d + n0);
           else bv[b][jj].zero();
+        }
+        if constexpr (!SPLIT) {
+          // one z row per tuple, read as whole vectors
+          const float *zrow = Z + int64_t(pp[b]) * zld + jb;
+          if ((zld & 3) == 0) {
+            const float4 *zr = reinterpret_cast<const float4 *>(zrow);
+#pragma unroll
+            for (int jj = 0; jj < RB; jj += 4) {
+              float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+              if (jb + jj < kk[b]) v = zr[jj / 4];
+              zv[b][jj] = v.x;
+              zv[b][jj + 1] = v.y;
+              zv[b][jj + 2] = v.z;
+              zv[b][jj + 3] = v.w;
+            }
+          } else {
+#pragma unroll
+            for (int jj = 0; jj < RB; ++jj) zv[b][jj] = jb + jj < kk[b] ? zrow[jj] : 0.f;
+          }
+        } else {
+          // nkc partial rows per tuple (zld is a multiple of 4 here)
+#pragma unroll
+          for (int jj = 0; jj < RB; ++jj) zv[b][jj] = 0.f;
+          for (int c = 0; c < nkc; ++c) {
+            const float4 *zr = reinterpret_cast<const float4 *>(Z + int64_t(pp[b]) * zstride + c * zld + jb);
+#pragma unroll
+            for (int jj = 0; jj < RB; jj += 4) {
+              if (jb + jj < kk[b]) {
+                const float4 v = zr[jj / 4];
+                zv[b][jj] += v.x;
+                zv[b][jj + 1] += v.y;
+                zv[b][jj + 2] += v.z;
+                zv[b][jj + 3] += v.w;
+              }
+            }
+          }
         }
       }
 #pragma unroll
@@ -567,6 +611,7 @@ __global__ __launch_bounds__(256) void expand_mfma(ExpandMfmaArgs e) {
   for (int i = 1; i < kMaxMods; ++i)
     if (i < e.n_mods && job >= e.m[i].first) mi = i;
   const int first = e.m[mi].first, d = e.m[mi].d, r_max = e.m[mi].r_max, zld = e.m[mi].zld;
+  const int nkc = e.m[mi].nkc, zstride = e.m[mi].zstride;
   const int64_t ld = e.m[mi].ld;
   const int32_t *k_dev = e.m[mi].k_dev;
   const float *Z = e.m[mi].z;
@@ -626,21 +671,27 @@ __global__ __launch_bounds__(256) void expand_mfma(ExpandMfmaArgs e) {
         const float al = e.tup_alpha[p];
         const int j0 = (h - u_h0[i]) * kXHalf;
         const int kk = u_k[i];
-        const float *zr = Z + int64_t(p) * zld + j0;
         float zv[kXHalf];
-        if ((zld & 3) == 0) {
 #pragma unroll
-          for (int q = 0; q < kXHalf / 4; ++q) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j0 + 4 * q < kk) v = reinterpret_cast<const float4 *>(zr)[q];
-            zv[4 * q] = v.x;
-            zv[4 * q + 1] = v.y;
-            zv[4 * q + 2] = v.z;
-            zv[4 * q + 3] = v.w;
+        for (int q = 0; q < kXHalf; ++q) zv[q] = 0.f;
+        for (int c = 0; c < nkc; ++c) {
+          const float *zr = Z + int64_t(p) * zstride + c * zld + j0;
+          if ((zld & 3) == 0) {
+#pragma unroll
+            for (int q = 0; q < kXHalf / 4; ++q) {
+              if (j0 + 4 * q < kk) {
+                const float4 v = reinterpret_cast<const float4 *>(zr)[q];
+                zv[4 * q] += v.x;
+                zv[4 * q + 1] += v.y;
+                zv[4 * q + 2] += v.z;
+                zv[4 * q + 3] += v.w;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < kXHalf; ++q)
+              if (j0 + q < kk) zv[q] += zr[q];
           }
-        } else {
-#pragma unroll
-          for (int q = 0; q < kXHalf; ++q) zv[q] = j0 + q < kk ? zr[q] : 0.f;
         }
         uint32_t pk[kXHalf / 2];
 #pragma unroll
@@ -795,10 +846,53 @@ static int check_dtypes(const tcl_module *m, tcl_dtype xd, tcl_dtype yd, bool ne
   return TCL_OK;
 }
 
-// Shrink of n (<= kMaxMods) modules in one launch; z[i] is module i's output.
+// K-chunk width of the fused shrink: d_in is cut into chunks so that the
+// batch yields enough (item, rank tile, chunk) workgroups to keep every CU
+// issuing loads (a decode batch has only as many items as touched adapters).
+// Partial z planes are added by the expand in chunk order.  The public
+// single-module shrink writes final z (one chunk).
+static int env_int(const char *name, int dflt) {
+  const char *s = std::getenv(name);
+  return (s && *s) ? std::atoi(s) : dflt;
+}
+
+static int shrink_kchunk(const tcl_plan *p, const tcl_module *mods, int n) {
+  if (mods[0].wdtype != TCL_BF16) return 1 << 30;
+  int kchunk;
+  // TCL_KCHUNK=<elements> fixes the chunk width (tuning knob; 0 = policy)
+  const int forced = env_int("TCL_KCHUNK", 0);
+  if (forced > 0) {
+    kchunk = (forced + 31) / 32 * 32;
+  } else {
+    // measured on decode batches: tiny batches (fewer workgroups than CUs)
+    // gain most from 2048-element chunks, larger decode batches from
+    // 4096-element chunks, prefill-sized batches lose from any split
+    int64_t est_items = (p->L.cap < p->L.N ? p->L.cap : p->L.N) + p->L.cap / kTile;
+    int64_t units = 0;
+    for (int i = 0; i < n; ++i) units += (mods[i].r_max + 15) / 16;
+    const int64_t wgs = est_items * units;
+    kchunk = wgs < 256 ? 2048 : (wgs < 4096 ? 4096 : (1 << 30));
+  }
+  // keep a tuple's z row (all partial rows) within 128 floats
+  for (int i = 0; i < n; ++i) {
+    const int zl = (mods[i].r_max + 3) / 4 * 4;
+    const int max_chunks = 128 / zl;
+    if (max_chunks < 1) return 1 << 30;
+    const int min_kchunk = (mods[i].d_in + max_chunks - 1) / max_chunks;
+    if (kchunk < min_kchunk) kchunk = (min_kchunk + 31) / 32 * 32;
+  }
+  return kchunk;
+}
+
+static int n_kchunks(const tcl_module *m, int kchunk) {
+  return (m->d_in + kchunk - 1) / kchunk;
+}
+
+// Shrink of n (<= kMaxMods) modules in one launch; z[i] is module i's output
+// ([nkc][cap][zld] partial planes when kchunk < d_in).
 static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
                          const void *const *x, const int64_t *ldx, float *const *z,
-                         const int *zld, int zero_tail, hipStream_t s) {
+                         const int *zld, int kchunk, int zero_tail, hipStream_t s) {
   const bool bf = mods[0].wdtype == TCL_BF16;
   const int rows = bf ? 16 : 4;  // rank rows per workgroup job
   ShrinkArgs a{};
@@ -807,7 +901,7 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
   a.n_mods = n;
   a.items_cap = p->L.items_cap;
   a.zero_tail = zero_tail;
-  int rg = 0;
+  int units = 0;
   for (int i = 0; i < n; ++i) {
     ModArgs &M = a.m[i];
     M.W = mods[i].A_t;
@@ -818,16 +912,19 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
     M.ld = ldx[i];
     M.d = mods[i].d_in;
     M.r_max = mods[i].r_max;
-    M.first = rg;
+    M.first = units;
     M.n_ct = 0;
-    rg += (mods[i].r_max + rows - 1) / rows;
+    M.nkc = bf ? n_kchunks(&mods[i], kchunk) : 1;
+    M.kchunk = bf ? kchunk : (mods[i].d_in + 31) / 32 * 32;
+    M.zstride = M.nkc * zld[i];
+    units += (mods[i].r_max + rows - 1) / rows * M.nkc;
   }
-  a.rg_total = rg;
-  int64_t grid = int64_t(p->L.items_cap) * rg;
+  a.rg_total = units;
+  int64_t grid = int64_t(p->L.items_cap) * units;
   if (grid > 32768) grid = 32768;
   if (grid < 1) grid = 1;
-  logf("shrink(%s): modules=%d rank tiles=%d grid=%lld", bf ? "mfma" : "valu", n, rg,
-       (long long)grid);
+  logf("shrink(%s): modules=%d units/item=%d kchunk=%d grid=%lld", bf ? "mfma" : "valu", n,
+       units, kchunk, (long long)grid);
   if (bf)
     hipLaunchKernelGGL(shrink_mfma, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
   else
@@ -836,9 +933,13 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
   return TCL_OK;
 }
 
-template <int R, typename TW, typename TY>
-static void launch_expand_t(const ExpandArgs &e, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((expand_kernel<R, TW, TY>), dim3(grid), dim3(64), 0, s, e);
+template <int R, bool SPLIT, typename TW, typename TY>
+static void launch_expand_t(const ExpandArgs &e, int cpl, int grid, hipStream_t s) {
+  if (cpl == 8)
+    hipLaunchKernelGGL((expand_kernel<R, 8, SPLIT, TW, TY>), dim3(grid), dim3(64), 0, s, e);
+  else if (cpl == 4)
+    hipLaunchKernelGGL((expand_kernel<R, 4, SPLIT, TW, TY>), dim3(grid), dim3(64), 0, s, e);
+  else hipLaunchKernelGGL((expand_kernel<R, 2, SPLIT, TW, TY>), dim3(grid), dim3(64), 0, s, e);
 }
 
 // Which expand runs: the per-token VALU kernel by default; the matrix-core
@@ -865,8 +966,9 @@ static void launch_expand_mfma_t(const ExpandMfmaArgs &e, int grid, hipStream_t 
 
 // Expand of n (<= kMaxMods) modules in one launch.
 static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
-                         float *const *z, const int *zld, void *const *y, const int64_t *ldy,
-                         tcl_dtype yd, hipStream_t s) {
+                         float *const *z, const int *zld, int kchunk, void *const *y,
+                         const int64_t *ldy, tcl_dtype yd, hipStream_t s) {
+  const bool bfw = mods[0].wdtype == TCL_BF16;
   if (p->L.T == 0) return TCL_OK;
   if (use_mfma_expand(p, mods)) {
     ExpandMfmaArgs e{};
@@ -892,6 +994,8 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
       M.d = mods[i].d_out;
       M.r_max = mods[i].r_max;
       M.n_ct = (mods[i].d_out + kXCols - 1) / kXCols;
+      M.nkc = bfw ? n_kchunks(&mods[i], kchunk) : 1;
+      M.zstride = M.nkc * zld[i];
       M.first = int32_t(jobs);
       jobs += int64_t(M.n_ct) * p->L.tiles;
     }
@@ -910,8 +1014,15 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
   e.tok_rec = p->d.tok_rec;
   e.T = p->L.T;
   e.n_mods = n;
+  // outputs per lane: 8 unless the batch would then give too few waves
+  int64_t jobs8 = 0;
+  for (int i = 0; i < n; ++i) jobs8 += int64_t((mods[i].d_out + 511) / 512) * p->L.T;
+  int cpl = jobs8 >= 1024 ? 8 : (jobs8 >= 512 ? 4 : 2);
+  const int forced_cpl = env_int("TCL_CPL", 0);  // tuning knob: 2, 4 or 8
+  if (forced_cpl == 2 || forced_cpl == 4 || forced_cpl == 8) cpl = forced_cpl;
   int64_t jobs = 0;
   int rmax = 1;
+  bool split = false;
   for (int i = 0; i < n; ++i) {
     ModArgs &M = e.m[i];
     M.W = mods[i].B_t;
@@ -922,7 +1033,10 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
     M.ld = ldy[i];
     M.d = mods[i].d_out;
     M.r_max = mods[i].r_max;
-    M.n_ct = (mods[i].d_out + 511) / 512;
+    M.n_ct = (mods[i].d_out + 64 * cpl - 1) / (64 * cpl);
+    M.nkc = bfw ? n_kchunks(&mods[i], kchunk) : 1;
+    M.zstride = M.nkc * zld[i];
+    if (M.nkc > 1) split = true;
     M.first = int32_t(jobs);
     jobs += int64_t(M.n_ct) * p->L.T;
     if (mods[i].r_max > rmax) rmax = mods[i].r_max;
@@ -932,14 +1046,16 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
   e.jobs_per_xcd = int32_t((jobs + 7) / 8);
   const int grid = 8 * e.jobs_per_xcd;
   const int R = rank_bucket(rmax);
-  logf("expand(valu): modules=%d R=%d jobs=%lld grid=%d", n, R, (long long)jobs, grid);
+  logf("expand(valu): modules=%d R=%d cpl=%d jobs=%lld grid=%d", n, R, cpl, (long long)jobs, grid);
   const bool bf = mods[0].wdtype == TCL_BF16;
   const bool ybf = yd == TCL_BF16;
 #define TCL_EXPAND_CASE(RR)                                                \
   case RR:                                                                 \
-    if (bf && ybf) launch_expand_t<RR, bf16_t, bf16_t>(e, grid, s);        \
-    else if (bf) launch_expand_t<RR, bf16_t, float>(e, grid, s);           \
-    else launch_expand_t<RR, float, float>(e, grid, s);                    \
+    if (bf && ybf && split) launch_expand_t<RR, true, bf16_t, bf16_t>(e, cpl, grid, s);  \
+    else if (bf && ybf) launch_expand_t<RR, false, bf16_t, bf16_t>(e, cpl, grid, s);     \
+    else if (bf && split) launch_expand_t<RR, true, bf16_t, float>(e, cpl, grid, s);     \
+    else if (bf) launch_expand_t<RR, false, bf16_t, float>(e, cpl, grid, s);             \
+    else launch_expand_t<RR, false, float, float>(e, cpl, grid, s);                      \
     break;
   switch (R) {
     TCL_EXPAND_CASE(8)
@@ -954,8 +1070,9 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
 
 static int z_ld(const tcl_module *m) { return (m->r_max + 3) / 4 * 4; }
 
-static size_t z_bytes(const tcl_plan *p, const tcl_module *m) {
-  return (size_t(p->L.cap) * size_t(z_ld(m)) * 4 + 255) & ~size_t(255);
+static size_t z_bytes(const tcl_plan *p, const tcl_module *m, int kchunk) {
+  const size_t planes = m->wdtype == TCL_BF16 ? size_t(n_kchunks(m, kchunk)) : 1;
+  return (planes * size_t(p->L.cap) * size_t(z_ld(m)) * 4 + 255) & ~size_t(255);
 }
 
 }  // namespace tcl
@@ -986,7 +1103,11 @@ int tcl_workspace_bytes(const tcl_plan *p, const tcl_module *mods, int32_t n_mod
   for (int i = 0; i < n_mods; ++i) {
     int rc = check_plan_module(p, &mods[i]);
     if (rc) return rc;
-    need += z_bytes(p, &mods[i]);
+  }
+  for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
+    const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
+    const int kchunk = shrink_kchunk(p, mods + i0, n);
+    for (int i = 0; i < n; ++i) need += z_bytes(p, &mods[i0 + i], kchunk);
   }
   *bytes = need;
   return TCL_OK;
@@ -1001,7 +1122,7 @@ int tcl_shrink(const tcl_plan *p, const tcl_module *m, const void *x, int64_t ld
   if (!z) return fail(TCL_EINVAL, "z is NULL");
   if (reinterpret_cast<uintptr_t>(z) & 15) return fail(TCL_EALIGN, "z must be 16-byte aligned");
   const int zld = m->r_max;
-  return launch_shrink(p, m, 1, &x, &ldx, &z, &zld, 1, static_cast<hipStream_t>(stream));
+  return launch_shrink(p, m, 1, &x, &ldx, &z, &zld, 1 << 30, 1, static_cast<hipStream_t>(stream));
 }
 
 int tcl_expand(const tcl_plan *p, const tcl_module *m, const float *z, void *y, int64_t ldy,
@@ -1013,7 +1134,8 @@ int tcl_expand(const tcl_plan *p, const tcl_module *m, const float *z, void *y, 
   if (!z) return fail(TCL_EINVAL, "z is NULL");
   float *zz = const_cast<float *>(z);
   const int zld = m->r_max;
-  return launch_expand(p, m, 1, &zz, &zld, &y, &ldy, yd, static_cast<hipStream_t>(stream));
+  return launch_expand(p, m, 1, &zz, &zld, 1 << 30, &y, &ldy, yd,
+                       static_cast<hipStream_t>(stream));
 }
 
 // Checks shared by the fused entry points; returns the workspace bytes needed.
@@ -1032,7 +1154,11 @@ static int check_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods
     if (y && (rc = check_io(y[i], ldy[i], mods[i].d_out, "y"))) return rc;
     if (mods[i].wdtype != mods[0].wdtype)
       return fail(TCL_EUNSUPPORTED, "modules of one call must share a weight dtype");
-    need += z_bytes(p, &mods[i]);
+  }
+  for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
+    const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
+    const int kchunk = shrink_kchunk(p, mods + i0, n);
+    for (int i = 0; i < n; ++i) need += z_bytes(p, &mods[i0 + i], kchunk);
   }
   if (!ws) return fail(TCL_EINVAL, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) & 255)
@@ -1043,14 +1169,20 @@ static int check_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods
 
 // z of module i lives in the workspace after the z of modules 0..i-1
 static void z_slices(const tcl_plan *p, const tcl_module *mods, int i0, int n, void *ws,
-                     float **z, int *zld) {
+                     float **z, int *zld, int *kchunk_out) {
   char *wp = static_cast<char *>(ws);
-  for (int i = 0; i < i0; ++i) wp += z_bytes(p, &mods[i]);
+  for (int b = 0; b < i0; b += kMaxMods) {
+    const int nb = i0 - b < kMaxMods ? i0 - b : kMaxMods;
+    const int kc = shrink_kchunk(p, mods + b, nb);
+    for (int i = 0; i < nb; ++i) wp += z_bytes(p, &mods[b + i], kc);
+  }
+  const int kchunk = shrink_kchunk(p, mods + i0, n);
   for (int i = 0; i < n; ++i) {
     z[i] = reinterpret_cast<float *>(wp);
     zld[i] = z_ld(&mods[i0 + i]);
-    wp += z_bytes(p, &mods[i0 + i]);
+    wp += z_bytes(p, &mods[i0 + i], kchunk);
   }
+  *kchunk_out = kchunk;
 }
 
 static int run_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
@@ -1059,14 +1191,14 @@ static int run_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
   for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
     const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
     float *z[kMaxMods];
-    int zld[kMaxMods];
-    z_slices(p, mods, i0, n, ws, z, zld);
+    int zld[kMaxMods], kchunk;
+    z_slices(p, mods, i0, n, ws, z, zld, &kchunk);
     if (x) {
-      int rc = launch_shrink(p, mods + i0, n, x + i0, ldx + i0, z, zld, 0, s);
+      int rc = launch_shrink(p, mods + i0, n, x + i0, ldx + i0, z, zld, kchunk, 0, s);
       if (rc) return rc;
     }
     if (y) {
-      int rc = launch_expand(p, mods + i0, n, z, zld, y + i0, ldy + i0, yd, s);
+      int rc = launch_expand(p, mods + i0, n, z, zld, kchunk, y + i0, ldy + i0, yd, s);
       if (rc) return rc;
     }
   }
