@@ -140,6 +140,7 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.o_spos = take(size_t(NP) * 4);
   l.o_sgbase = take(size_t(G) * 4);
   l.o_shist = take(l.mode == PLAN_COUNT_GLOBAL ? size_t(N) * size_t(l.chunks) * 4 : 4);
+  l.o_sseg = take(l.mode == PLAN_DIRECT ? 4 : size_t(N) * 4);
   l.tiles = T >= kMfmaMinTokens ? (T + kXTok - 1) / kXTok : 0;
   l.o_ranges = take(size_t(l.tiles) * size_t(N) * 8);
   l.total = o;
@@ -523,6 +524,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
         if (end > beg) {
           A.d.seg_adapter[u] = a;
           A.d.seg_begin[u] = beg;
+          A.d.s_seg[a] = u;
           for (int p0 = beg; p0 < end; p0 += kTile)
             A.d.items[it++].head = make_int4(a, p0, min(end, p0 + kTile) - p0, u);
           ++u;
@@ -557,6 +559,9 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
     const int t0 = gtp[g], tl = gtp[g + 1] - t0, pl = gpp[g + 1] - gpp[g];
     const int a = pa[q], s = slot[q], base = pos[q], gb = gbase[g];
     const float w = pw[q];
+    int sg;  // segment of the adapter (its index in the segment table)
+    if constexpr (direct) sg = su[a];
+    else sg = A.d.s_seg[a];
     for (int i = 0; i < tl; ++i) {
       const int p = base + i;
       A.d.tup_token[p] = t0 + i;
@@ -564,7 +569,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
       A.d.tup_alpha[p] = w;
       A.d.tup_slot[p] = s;
       A.d.tok_tuple[gb + i * pl + s] = p;
-      A.d.tok_rec[int64_t(t0 + i) * kSlotPad + s] = make_int4(p, a, __float_as_int(w), s);
+      A.d.tok_rec[int64_t(t0 + i) * kSlotPad + s] = make_int4(p, a, __float_as_int(w), sg);
       if constexpr (direct) {
         const int local = p - sst[a];
         A.d.items[sib[a] + local / kTile].tok[local % kTile] = t0 + i;
@@ -632,6 +637,7 @@ static void bind(tcl_plan *p) {
   d.s_pos = reinterpret_cast<int32_t *>(b + L.o_spos);
   d.s_gbase = reinterpret_cast<int32_t *>(b + L.o_sgbase);
   d.s_hist = reinterpret_cast<int32_t *>(b + L.o_shist);
+  d.s_seg = reinterpret_cast<int32_t *>(b + L.o_sseg);
   d.ranges = reinterpret_cast<int2 *>(b + L.o_ranges);
 }
 

@@ -64,7 +64,8 @@ struct PlanLayout {
   int32_t tiles;    // token tiles of kXTok with tuple ranges (0: none)
   // byte offsets inside the device buffer
   size_t o_status, o_tok, o_ad, o_slot, o_alpha, o_toktuple, o_tokrec, o_tokn, o_tokptr,
-      o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_ranges, total;
+      o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_sseg, o_ranges,
+      total;
 };
 
 // Mapping-stage algorithms: small tables count positions directly (every pair
@@ -86,11 +87,12 @@ struct PlanDev {
   int32_t *tup_token, *tup_adapter, *tup_slot;
   float *tup_alpha;
   int32_t *tok_tuple, *tok_ptr;
-  int4 *tok_rec;   // [T][kSlotPad]: {tuple index, adapter, alpha bits, slot}
+  int4 *tok_rec;   // [T][kSlotPad]: {tuple index, adapter, alpha bits, segment index}
   int32_t *tok_n;  // [T] slots per token
   int32_t *seg_adapter, *seg_begin;
   Item *items;
   int32_t *s_slot, *s_group, *s_pos, *s_gbase, *s_hist;
+  int32_t *s_seg;  // counting path: segment index of every touched adapter [N]
   int2 *ranges;  // [tiles][N]: tuples of segment u whose token lies in tile
 };
 
