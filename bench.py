@@ -77,22 +77,26 @@ def kernel_bytes(wl) -> dict:
     return out
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources; a stored counter summary is only valid for the
-    kernels it was measured on."""
+# HIP sources each kernel is built from: a stored counter summary is only
+# valid while these are unchanged
+KERNEL_SOURCES = {"plan_kernel": ("plan.hip", "tcl_internal.hpp"),
+                  "tile_ranges_kernel": ("plan.hip", "tcl_internal.hpp")}
+APPLY_SOURCES = ("apply.hip", "tcl_internal.hpp")
+
+
+def kernel_source_hash(kernel: str) -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tenant_composite_lora_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in KERNEL_SOURCES.get(kernel, APPLY_SOURCES):
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (profiles/pmc_traffic.txt), or None when there is none for this
-    workload or the kernels changed since it was taken."""
+    workload or the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -101,17 +105,18 @@ def stored_traffic(workload: str, kernel: str):
     except ValueError:
         return None
     ent = rec.get("entries", {}).get(f"{workload}:{kernel}")
-    if not ent or rec.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("hbm_bytes_per_launch")
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None) -> dict:
     """HBM traffic per launch of each library kernel from two rocprofv3 --pmc
     runs of the same bench command (FETCH_SIZE, then WRITE_SIZE, KiB per
     dispatch).  Each counter is scaled by what it reads for the 256 MiB
     calibration copy of that run (the largest __amd_rocclr_copyBuffer
-    dispatch): factor = 256 MiB / measured."""
+    dispatch): factor = 256 MiB / measured.  Entries are merged into the
+    summary `into` when it exists."""
     import csv
     import collections
     calib = 256 << 20
@@ -124,23 +129,26 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
             name = r["Kernel_Name"]
             if name.startswith("__amd_rocclr_copyBuffer"):
                 biggest_copy = max(biggest_copy, v)
-            for short in ("shrink_mfma", "shrink_valu", "expand_kernel", "expand_mfma",
-                          "plan_kernel", "tile_ranges_kernel"):
+            for short in ("shrink_mfma", "shrink_valu", "expand_kernel", "expand_staged",
+                          "expand_mfma", "plan_kernel", "tile_ranges_kernel"):
                 if short in name:
                     per[short].append(v)
         return per, calib / biggest_copy
 
     f, ff = load(fetch_csv)
     w, fw = load(write_csv)
-    out = {"source_hash": kernel_source_hash(),
-           "calibration": {"copy_bytes": calib, "fetch_factor": ff, "write_factor": fw},
+    out = {"units": "bytes per kernel launch; FETCH_SIZE and WRITE_SIZE (KiB per dispatch) "
+                    "scaled by the 256 MiB copy calibration of the same run",
            "entries": {}}
+    if into and os.path.exists(into):
+        out = json.load(open(into))
     for k in sorted(set(f) | set(w)):
         fb = sum(f[k]) / len(f[k]) * ff if f.get(k) else 0.0
         wb = sum(w[k]) / len(w[k]) * fw if w.get(k) else 0.0
         out["entries"][f"{workload}:{k}"] = {
             "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-            "hbm_bytes_per_launch": fb + wb, "launches": len(f.get(k, []))}
+            "hbm_bytes_per_launch": fb + wb, "launches": len(f.get(k, [])),
+            "fetch_factor": ff, "write_factor": fw, "source_hash": kernel_source_hash(k)}
     return out
 
 
@@ -192,13 +200,16 @@ def main():
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the counter summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--pmc-into", metavar="JSON",
+                    help="with --pmc-summary: merge into this existing summary")
     args = ap.parse_args()
     if args.pmc_summary:
         names = {1: "tiny_f32_256", 2: "distinct_decode_q4096_n64_r8_t32",
                  3: "skewed_decode_llama3_8b_7proj_n128_r8_t64",
                  4: "sparse_prefill_gated_8x256_n128_r16",
                  5: "retained_rank_mixed_n256_r32_t4224"}
-        print(json.dumps(pmc_summary(*args.pmc_summary, names[args.config]), indent=1))
+        print(json.dumps(pmc_summary(*args.pmc_summary, names[args.config], args.pmc_into),
+                         indent=1))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -317,8 +328,11 @@ def main():
     dom = max(("shrink", "expand"), key=lambda n: per[n])
     achieved = kb[dom] / per[dom] / 1e9
     ms_step = 1e3 * t_steps / K
+    disp = os.environ.get("TCL_DISPATCH", "")
     kernel_names = {"shrink": "shrink_mfma" if wl.dtype == W.BF16 else "shrink_valu",
-                    "expand": "expand_kernel", "plan": "plan_kernel"}
+                    "expand": {"staged": "expand_staged", "mfma": "expand_mfma"}.get(
+                        disp, "expand_kernel") if wl.dtype == W.BF16 else "expand_kernel",
+                    "plan": "plan_kernel"}
     traffic = stored_traffic(wl.name, kernel_names[dom])
     out = {
         "metric": METRIC,
