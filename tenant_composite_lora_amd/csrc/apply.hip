@@ -1453,6 +1453,8 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
   const bool bfw = mods[0].wdtype == TCL_BF16;
   if (p->L.T == 0) return TCL_OK;
   if (use_mfma_expand(p, mods)) {
+    int rc = plan_prepare_ranges(p, s);
+    if (rc) return rc;
     ExpandMfmaArgs e{};
     e.status = p->d.status;
     e.seg_adapter = p->d.seg_adapter;

@@ -83,10 +83,11 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.cap = cap;
   l.items_cap = (cap < N ? cap : N) + cap / kTile + 1;
 
-  // Direct path: gtp, gpp (G+1 each), adapter, alpha, slot, group, pos,
-  // tokens-per-pair, head count (NP each) and group tuple base (G) in LDS.
-  const int64_t np16 = (int64_t(NP) + 15) / 16 * 16;
-  const int64_t direct_ints = 3 * int64_t(G) + 2 + 3 * np16 + 3 * int64_t(NP) + 4 * int64_t(N) + 16;
+  // Direct path in LDS: gtp, gpp (G+1 each), group tuple base (G); adapter,
+  // alpha, slot, group, tokens, ticket, bucket pair and bucket tokens (NP
+  // each); tuple count, pair count, segment start, item base, segment index
+  // and bucket start (N each).
+  const int64_t direct_ints = 3 * int64_t(G) + 2 + 8 * int64_t(NP) + 6 * int64_t(N) + 16;
   // Counting path in LDS: the same without the last two pair arrays, plus
   // the (adapter, chunk) histogram.
   const int64_t fixed = 3 * int64_t(G) + 2 + 5 * int64_t(NP);
@@ -151,58 +152,90 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
 // ---------------------------------------------------------------------------
 // block-wide helpers (NT threads = NT/64 waves of 64)
 // ---------------------------------------------------------------------------
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps of
+// 1, 2, 4 and 8 lanes inside each row of 16 (DPP row shifts, lanes without a
+// source add 0), then the last lane of row 0 is added to row 1 and 3 and the
+// last lane of row 1 to rows 2 and 3 (DPP row broadcasts).  No LDS traffic.
 __device__ inline int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
+// Every block-wide operation below gets its own scratch slot of kSlotInts
+// ints, so no trailing barrier is needed before the slot could be reused.
+constexpr int kScanMax = 4;
+constexpr int kSlotInts = kScanMax * (kPlanThreads / 64);
+
+// OR of small bit sets (EB_* bits) over the block: one ballot per bit.
 template <int NT>
-__device__ inline int block_or(int v, int *tmp) {
+__device__ inline int block_or(int v, int *slot) {
   constexpr int kWaves = NT / 64;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off, 64);
-  if (kWaves == 1) return v;
-  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
-  __syncthreads();
   int r = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) r |= tmp[i];
+  for (int b = 0; b < 3; ++b)
+    if (__ballot((v >> b) & 1)) r |= 1 << b;
+  if (kWaves == 1) return r;
+  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = r;
   __syncthreads();
+  r = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) r |= slot[i];
   return r;
+}
+
+// Exclusive prefix of K values over thread order (one barrier): v[i] is
+// replaced by its exclusive prefix and tot[i] receives the block total.
+template <int NT, int K>
+__device__ inline void block_excl_scan_n(int (&v)[K], int *slot, int (&tot)[K]) {
+  static_assert(K <= kScanMax, "scan width");
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) inc[i] = wave_incl_scan(v[i]);
+  if (kWaves == 1) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      tot[i] = __builtin_amdgcn_readlane(inc[i], 63);
+      v[i] = inc[i] - v[i];
+    }
+    return;
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) slot[i * kWaves + w] = inc[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    int before = 0, t = 0;
+#pragma unroll
+    for (int j = 0; j < kWaves; ++j) {
+      const int x = slot[i * kWaves + j];
+      before += j < w ? x : 0;
+      t += x;
+    }
+    tot[i] = t;
+    v[i] = before + inc[i] - v[i];
+  }
 }
 
 // Exclusive prefix of v over thread order; *total receives the block sum.
 template <int NT>
-__device__ inline int block_excl_scan(int v, int *tmp, int *total) {
-  constexpr int kWaves = NT / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(v);
-  if (kWaves == 1) {
-    *total = __shfl(incl, 63, 64);
-    return incl - v;
-  }
-  if (lane == 63) tmp[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    const int x = lane < kWaves ? tmp[lane] : 0;
-    const int xi = wave_incl_scan(x);
-    if (lane < kWaves) tmp[lane] = xi - x;
-    if (lane == kWaves - 1) tmp[kWaves] = xi;
-  }
-  __syncthreads();
-  const int r = tmp[w] + incl - v;
-  *total = tmp[kWaves];
-  __syncthreads();
-  return r;
+__device__ inline int block_excl_scan(int v, int *slot, int *total) {
+  int x[1] = {v}, t[1];
+  block_excl_scan_n<NT, 1>(x, slot, t);
+  *total = t[0];
+  return x[0];
 }
 
 struct PlanArgs {
-  int32_t T, G, NP, N, cap, C, mode;
+  int32_t T, G, NP, N, cap, C, mode, items_cap;
   const int32_t *gtp, *gpp, *pa;
   const float *pw;
   PlanDev d;
@@ -229,6 +262,8 @@ struct PlanView {
   const float *pw;
   int32_t *slot, *grp, *pos, *gbase, *hist, *ptl, *hcnt, *ssm, *sib;
   int32_t *cnt, *sst, *su;  // direct path: per-adapter count, segment start, segment index
+  int32_t *pcnt, *sbk;      // direct path: per-adapter pair count and pair-bucket start
+  int32_t *tkt, *bkt, *bkw; // direct path: pair ticket; bucket entries (pair, tokens)
 };
 
 template <int NT, int MODE>
@@ -250,26 +285,28 @@ __device__ inline PlanView plan_view(const PlanArgs &A, int *lds) {
     v.ssm = nullptr;
     v.sib = nullptr;
     v.cnt = v.sst = v.su = nullptr;
+    v.pcnt = v.sbk = v.tkt = v.bkt = v.bkw = nullptr;
   } else if constexpr (MODE == PLAN_DIRECT) {
-    // Per-pair arrays first, each padded to a multiple of 16 entries so the
-    // O(P^2) scan can read them 4 at a time; padding holds adapter INT_MAX and
-    // zero tokens so it never counts.
-    const int np16 = (NP + 15) / 16 * 16;
     const int N = A.N;
     int *p = lds;
-    int *l_pa = p; p += np16;
-    v.ptl = p; p += np16;
-    v.pos = p; p += np16;  // first the same-adapter rank, then the position
+    int *l_pa = p; p += NP;
+    v.ptl = p; p += NP;
+    v.pos = nullptr;
     float *l_pw = reinterpret_cast<float *>(p); p += NP;
     v.slot = p; p += NP;
     v.grp = p; p += NP;
+    v.tkt = p; p += NP;
+    v.bkt = p; p += NP;
+    v.bkw = p; p += NP;
     int *l_gtp = p; p += G + 1;
     int *l_gpp = p; p += G + 1;
     v.gbase = p; p += G;
     v.cnt = p; p += N;
+    v.pcnt = p; p += N;
     v.sst = p; p += N;
     v.sib = p; p += N;
     v.su = p; p += N;
+    v.sbk = p; p += N;
     v.hist = nullptr;
     v.hcnt = nullptr;
     v.ssm = nullptr;
@@ -277,13 +314,14 @@ __device__ inline PlanView plan_view(const PlanArgs &A, int *lds) {
       l_gtp[i] = A.gtp[i];
       l_gpp[i] = A.gpp[i];
     }
-    for (int i = threadIdx.x; i < np16; i += NT) {
-      l_pa[i] = i < NP ? A.pa[i] : 0x7fffffff;
-      v.ptl[i] = 0;
-      v.pos[i] = 0;
-      if (i < NP) l_pw[i] = A.pw[i];
+    for (int i = threadIdx.x; i < NP; i += NT) {
+      l_pa[i] = A.pa[i];
+      l_pw[i] = A.pw[i];
     }
-    for (int i = threadIdx.x; i < N; i += NT) v.cnt[i] = 0;
+    for (int i = threadIdx.x; i < N; i += NT) {
+      v.cnt[i] = 0;
+      v.pcnt[i] = 0;
+    }
     __syncthreads();
     v.gtp = l_gtp;
     v.gpp = l_gpp;
@@ -306,6 +344,7 @@ __device__ inline PlanView plan_view(const PlanArgs &A, int *lds) {
     v.sib = nullptr;
     v.cnt = v.sst = v.su = nullptr;
     v.hist = p;
+    v.pcnt = v.sbk = v.tkt = v.bkt = v.bkw = nullptr;
     for (int i = threadIdx.x; i <= G; i += NT) {
       l_gtp[i] = A.gtp[i];
       l_gpp[i] = A.gpp[i];
@@ -325,10 +364,9 @@ __device__ inline PlanView plan_view(const PlanArgs &A, int *lds) {
 
 template <int NT, int MODE>
 __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
-  constexpr int kWaves = NT / 64;
   constexpr bool direct = MODE == PLAN_DIRECT;
   __shared__ __align__(16) int lds[MODE == PLAN_COUNT_GLOBAL ? 4 : kPlanLdsInts];
-  __shared__ int tmp[kWaves + 1];
+  __shared__ int tmp[6 * kSlotInts];
   const int tid = threadIdx.x;
   const int T = A.T, G = A.G, NP = A.NP, N = A.N, C = A.C;
 
@@ -336,147 +374,139 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
   const int32_t *gtp = V.gtp, *gpp = V.gpp, *pa = V.pa;
   const float *pw = V.pw;
   int32_t *slot = V.slot, *grp = V.grp, *pos = V.pos, *gbase = V.gbase, *hist = V.hist,
-          *ptl = V.ptl, *cnt = V.cnt, *sst = V.sst, *sib = V.sib, *su = V.su;
+          *ptl = V.ptl, *cnt = V.cnt, *sst = V.sst, *sib = V.sib, *su = V.su, *pcnt = V.pcnt,
+          *sbk = V.sbk, *tkt = V.tkt, *bkt = V.bkt, *bkw = V.bkw;
 
-  // ---- validation and canonical slots ------------------------------------
+  // ---- groups: structure, tuples per group, group bases, token index -----
+  // One thread per contiguous range of groups.  Structural errors stop the
+  // mapping here; the per-pair checks below need a sound group table.
   int err = 0;
   if (tid == 0 && (gtp[0] != 0 || gtp[G] != T || gpp[0] != 0 || gpp[G] != NP)) err |= EB_INVAL;
-  for (int g = tid; g < G; g += NT) {
+  const int gper = (G + NT - 1) / NT;
+  const int g0 = min(G, tid * gper), g1 = min(G, g0 + gper);
+  int local = 0;
+  for (int g = g0; g < g1; ++g) {
     const int t0 = gtp[g], t1 = gtp[g + 1], q0 = gpp[g], q1 = gpp[g + 1];
     if (!(0 <= t0 && t0 <= t1 && t1 <= T && 0 <= q0 && q0 <= q1 && q1 <= NP)) {
       err |= EB_INVAL;
       continue;
     }
+    for (int q = q0; q < q1; ++q) {
+      grp[q] = g;
+      if constexpr (direct) ptl[q] = t1 - t0;
+    }
     if (q1 - q0 > TCL_MAX_PAIRS_PER_GROUP) {
       err |= EB_UNSUP;
       continue;
     }
-    for (int q = q0; q < q1; ++q) {
-      const int aq = pa[q];
-      int s = 0, dup = 0;
-      for (int q2 = q0; q2 < q1; ++q2) {
-        const int a2 = pa[q2];
-        s += (a2 < aq);
-        dup |= (a2 == aq) & (q2 != q);
+    local += (t1 - t0) * (q1 - q0);
+  }
+  int P = 0;
+  {
+    // group tuple bases; the token index itself is written at the very end,
+    // so that no barrier below waits for those stores
+    int run = block_excl_scan<NT>(local, tmp + 0 * kSlotInts, &P);
+    if (!err) {
+      for (int g = g0; g < g1; ++g) {
+        gbase[g] = run;
+        run += (gtp[g + 1] - gtp[g]) * (gpp[g + 1] - gpp[g]);
       }
-      if (dup) err |= EB_INVAL;
-      slot[q] = s;
-      grp[q] = g;
-      if constexpr (direct) ptl[q] = t1 - t0;
     }
   }
-  for (int q = tid; q < NP; q += NT) {
-    const int aq = pa[q];
-    if (aq < 0 || aq >= N) err |= EB_INVAL;
-    const uint32_t bits = __float_as_uint(pw[q]);
-    if ((bits & 0x7f800000u) == 0x7f800000u) err |= EB_INVAL;
-  }
-  err = block_or<NT>(err, tmp);
-  if (err) {
-    plan_fail<NT>(A, (err & EB_INVAL) ? TCL_EINVAL : TCL_EUNSUPPORTED, 0);
+  const int err_groups = block_or<NT>(err, tmp + 1 * kSlotInts);
+  if (err_groups & EB_INVAL) {
+    plan_fail<NT>(A, TCL_EINVAL, 0);
     return;
   }
 
-  // ---- tuples per group -> group base, token index -------------------------
-  int P = 0;
-  {
-    const int per = (G + NT - 1) / NT;
-    const int g0 = min(G, tid * per), g1 = min(G, g0 + per);
-    int local = 0;
-    for (int g = g0; g < g1; ++g) local += (gtp[g + 1] - gtp[g]) * (gpp[g + 1] - gpp[g]);
-    int run = block_excl_scan<NT>(local, tmp, &P);
-    if (P <= A.cap) {
-      for (int g = g0; g < g1; ++g) {
-        const int t0 = gtp[g], t1 = gtp[g + 1], pl = gpp[g + 1] - gpp[g];
-        gbase[g] = run;
-        for (int t = t0; t < t1; ++t) {
-          A.d.tok_ptr[t] = run + (t - t0) * pl;
-          A.d.tok_n[t] = pl;
-        }
-        run += (t1 - t0) * pl;
+  // ---- pairs: ids, weights, canonical slots, duplicates --------------------
+  // One thread per pair.  The slot is the number of the group's pairs with a
+  // smaller adapter id.  Groups beyond the pair limit are already rejected
+  // (EUNSUPPORTED) and are not searched for duplicates.  The direct path also
+  // adds the pair's tuples to its adapter's count here.
+  err = 0;
+  for (int q = tid; q < NP; q += NT) {
+    const int aq = pa[q];
+    const bool a_ok = aq >= 0 && aq < N;
+    if (!a_ok) err |= EB_INVAL;
+    const uint32_t bits = __float_as_uint(pw[q]);
+    if ((bits & 0x7f800000u) == 0x7f800000u) err |= EB_INVAL;
+    const int g = grp[q];
+    const int q0 = gpp[g], q1 = gpp[g + 1];
+    if (q1 - q0 > TCL_MAX_PAIRS_PER_GROUP) continue;
+    int s = 0, dup = 0;
+    for (int q2 = q0; q2 < q1; q2 += 8) {
+      int av[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) av[u] = q2 + u < q1 ? pa[q2 + u] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = q2 + u < q1;
+        s += (in && av[u] < aq) ? 1 : 0;
+        dup |= (in && av[u] == aq && q2 + u != q) ? 1 : 0;
       }
-      if (tid == 0) A.d.tok_ptr[T] = P;
     }
+    if (dup) err |= EB_INVAL;
+    slot[q] = s;
+    if constexpr (direct) {
+      if (a_ok) {
+        atomicAdd(&cnt[aq], ptl[q]);
+        tkt[q] = atomicAdd(&pcnt[aq], 1);  // the pair's place in its adapter's bucket
+      }
+    }
+  }
+  err = block_or<NT>(err, tmp + 2 * kSlotInts) | err_groups;
+  if (err) {
+    plan_fail<NT>(A, (err & EB_INVAL) ? TCL_EINVAL : TCL_EUNSUPPORTED, 0);
+    return;
   }
   if (P > A.cap) {
     plan_fail<NT>(A, TCL_ENOSPC, P);
     return;
   }
 
-  int n_items = 0;
+  int n_items = 0, n_segs = 0;
   if constexpr (direct) {
-    // ---- direct count.  position = (tuples of smaller adapters) + (tuples
-    //      of the same adapter in earlier pairs; earlier pairs hold earlier
-    //      tokens).  The first term and the segment/item tables come from
-    //      per-adapter counts and scans over adapters; only the second term
-    //      is a pairwise count, split into (pair, 64-pair chunk) units over
-    //      all threads.  Integer LDS additions make it order-independent.
-    for (int q = tid; q < NP; q += NT) atomicAdd(&cnt[pa[q]], ptl[q]);
-    __syncthreads();
+    // ---- direct: position = (tuples of smaller adapters) + (tokens of the
+    //      same adapter's earlier pairs; earlier pairs hold earlier tokens).
+    //      One four-value scan over per-adapter counts gives segment starts,
+    //      segment indices, item bases and pair-bucket starts.  Every pair
+    //      then enters its adapter's bucket at its ticket; the order inside a
+    //      bucket is arbitrary, and the rank below sums over the bucket's
+    //      pairs with a smaller index, which does not depend on that order.
+    const int per = (N + NT - 1) / NT;
+    const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
+    int sv[4] = {0, 0, 0, 0}, st[4];
+    for (int a = a0; a < a1; ++a) {
+      const int c = cnt[a];
+      sv[0] += c;
+      sv[1] += c > 0;
+      sv[2] += (c + kTile - 1) / kTile;
+      sv[3] += pcnt[a];
+    }
+    block_excl_scan_n<NT, 4>(sv, tmp + 3 * kSlotInts, st);
     {
-      const int per = (N + NT - 1) / NT;
-      const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
-      int c_loc = 0, n_loc = 0, i_loc = 0;
-      for (int a = a0; a < a1; ++a) {
-        const int c = cnt[a];
-        c_loc += c;
-        n_loc += c > 0;
-        i_loc += (c + kTile - 1) / kTile;
-      }
-      int tot, U, NI;
-      int ec = block_excl_scan<NT>(c_loc, tmp, &tot);
-      int en = block_excl_scan<NT>(n_loc, tmp, &U);
-      int ei = block_excl_scan<NT>(i_loc, tmp, &NI);
+      int ec = sv[0], en = sv[1], ei = sv[2], eb = sv[3];
       for (int a = a0; a < a1; ++a) {
         const int c = cnt[a];
         sst[a] = ec;
         sib[a] = ei;
         su[a] = en;
-        if (c > 0) {
-          A.d.seg_adapter[en] = a;
-          A.d.seg_begin[en] = ec;
-          for (int p0 = ec, i = ei; p0 < ec + c; p0 += kTile, ++i)
-            A.d.items[i].head = make_int4(a, p0, min(ec + c, p0 + kTile) - p0, en);
-          ++en;
-          ei += (c + kTile - 1) / kTile;
-        }
+        sbk[a] = eb;
+        en += c > 0;
+        ei += (c + kTile - 1) / kTile;
+        eb += pcnt[a];
         ec += c;
       }
-      n_items = NI;
-      if (tid == 0) {
-        A.d.seg_begin[U] = P;
-        A.d.status[ST_TUPLES] = P;
-        A.d.status[ST_SEGMENTS] = U;
-        A.d.status[ST_ITEMS] = NI;
-      }
     }
-    {
-      const int nch = (NP + 63) / 64;
-      const int4 *pa4 = reinterpret_cast<const int4 *>(pa);
-      const int4 *tl4 = reinterpret_cast<const int4 *>(ptl);
-      for (int u = tid; u < NP * nch; u += NT) {
-        const int q = u / nch, c = u - q * nch;
-        const int lo = c * 64;
-        if (lo >= q) continue;
-        const int a = pa[q];
-        const int hi = min(q, lo + 64);
-        int part = 0;
-        for (int q2 = lo; q2 < hi; q2 += 16) {
-          int av[16], tv[16];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int4 x = pa4[q2 / 4 + v], y = tl4[q2 / 4 + v];
-            av[4 * v] = x.x; av[4 * v + 1] = x.y; av[4 * v + 2] = x.z; av[4 * v + 3] = x.w;
-            tv[4 * v] = y.x; tv[4 * v + 1] = y.y; tv[4 * v + 2] = y.z; tv[4 * v + 3] = y.w;
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) part += (av[v] == a && q2 + v < hi) ? tv[v] : 0;
-        }
-        if (part) atomicAdd(&pos[q], part);
-      }
-    }
+    n_items = st[2];
+    n_segs = st[1];
     __syncthreads();
-    for (int q = tid; q < NP; q += NT) pos[q] += sst[pa[q]];
+    for (int q = tid; q < NP; q += NT) {
+      const int e = sbk[pa[q]] + tkt[q];
+      bkt[e] = q;
+      bkw[e] = ptl[q];
+    }
   } else {
     // ---- counting sort: per-chunk counts per adapter ----------------------
     const int M = N * C;
@@ -497,7 +527,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
       int local = 0;
       for (int i = i0; i < i1; ++i) local += hist[i];
       int tot;
-      int run = block_excl_scan<NT>(local, tmp, &tot);
+      int run = block_excl_scan<NT>(local, tmp + 4 * kSlotInts, &tot);
       for (int i = i0; i < i1; ++i) {
         const int v = hist[i];
         hist[i] = run;
@@ -516,17 +546,18 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
         nseg += cnt > 0;
         nitem += (cnt + kTile - 1) / kTile;
       }
-      int U, NI;
-      int u = block_excl_scan<NT>(nseg, tmp, &U);
-      int it = block_excl_scan<NT>(nitem, tmp, &NI);
+      int sv[2] = {nseg, nitem}, st[2];
+      block_excl_scan_n<NT, 2>(sv, tmp + 5 * kSlotInts, st);
+      int u = sv[0], it = sv[1];
+      const int U = st[0], NI = st[1];
       for (int a = a0; a < a1; ++a) {
         const int beg = hist[a * C], end = (a + 1 < N) ? hist[(a + 1) * C] : P;
         if (end > beg) {
           A.d.seg_adapter[u] = a;
           A.d.seg_begin[u] = beg;
           A.d.s_seg[a] = u;
-          for (int p0 = beg; p0 < end; p0 += kTile)
-            A.d.items[it++].head = make_int4(a, p0, min(end, p0 + kTile) - p0, u);
+          for (int p0 = beg; p0 < end; p0 += kTile, ++it)
+            if (it < A.items_cap) A.d.items[it].head = make_int4(a, p0, min(end, p0 + kTile) - p0, u);
           ++u;
         }
       }
@@ -557,13 +588,34 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
   for (int q = tid; q < NP; q += NT) {
     const int g = grp[q];
     const int t0 = gtp[g], tl = gtp[g + 1] - t0, pl = gpp[g + 1] - gpp[g];
-    const int a = pa[q], s = slot[q], base = pos[q], gb = gbase[g];
+    const int a = pa[q], s = slot[q], gb = gbase[g];
+    int base;
+    if constexpr (direct) {
+      const int b0 = sbk[a], b1 = b0 + pcnt[a];
+      int r = 0;
+      for (int e = b0; e < b1; e += 8) {
+        int qq[8], ww[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          qq[u] = e + u < b1 ? bkt[e + u] : NP;
+          ww[u] = e + u < b1 ? bkw[e + u] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r += qq[u] < q ? ww[u] : 0;
+      }
+      base = sst[a] + r;
+    } else {
+      base = pos[q];
+    }
     const float w = pw[q];
     int sg;  // segment of the adapter (its index in the segment table)
     if constexpr (direct) sg = su[a];
     else sg = A.d.s_seg[a];
     for (int i = 0; i < tl; ++i) {
       const int p = base + i;
+      // positions are < P <= cap by construction; the guards keep a logic
+      // error from writing outside the plan buffer
+      if (p >= A.cap || gb + i * pl + s >= A.cap || s >= kSlotPad) continue;
       A.d.tup_token[p] = t0 + i;
       A.d.tup_adapter[p] = a;
       A.d.tup_alpha[p] = w;
@@ -572,12 +624,40 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
       A.d.tok_rec[int64_t(t0 + i) * kSlotPad + s] = make_int4(p, a, __float_as_int(w), sg);
       if constexpr (direct) {
         const int local = p - sst[a];
-        A.d.items[sib[a] + local / kTile].tok[local % kTile] = t0 + i;
+        const int it = sib[a] + local / kTile;
+        if (it < A.items_cap) A.d.items[it].tok[local % kTile] = t0 + i;
       }
     }
   }
+  // ---- token index (deferred so that no barrier above waited for it) ------
+  for (int g = g0; g < g1; ++g) {
+    const int t0 = gtp[g], t1 = gtp[g + 1], pl = gpp[g + 1] - gpp[g], run = gbase[g];
+    for (int t = t0; t < t1; ++t) {
+      A.d.tok_ptr[t] = run + (t - t0) * pl;
+      A.d.tok_n[t] = pl;
+    }
+  }
+  if (tid == 0) A.d.tok_ptr[T] = P;
   if constexpr (direct) {
-    if (tid == 0) A.d.status[ST_CODE] = TCL_OK;
+    // segment table, work-item heads and status words, also deferred
+    const int per = (N + NT - 1) / NT;
+    const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
+    for (int a = a0; a < a1; ++a) {
+      const int c = cnt[a];
+      if (c == 0) continue;
+      const int ec = sst[a], en = su[a];
+      A.d.seg_adapter[en] = a;
+      A.d.seg_begin[en] = ec;
+      for (int p0 = ec, i = sib[a]; p0 < ec + c; p0 += kTile, ++i)
+        if (i < A.items_cap) A.d.items[i].head = make_int4(a, p0, min(ec + c, p0 + kTile) - p0, en);
+    }
+    if (tid == 0) {
+      A.d.seg_begin[n_segs] = P;
+      A.d.status[ST_TUPLES] = P;
+      A.d.status[ST_SEGMENTS] = n_segs;
+      A.d.status[ST_ITEMS] = n_items;
+      A.d.status[ST_CODE] = TCL_OK;
+    }
     return;
   }
   __syncthreads();
@@ -659,6 +739,7 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
   A.cap = p->L.cap;
   A.C = p->L.chunks;
   A.mode = p->L.mode;
+  A.items_cap = p->L.items_cap;
   A.gtp = c->group_tok_ptr;
   A.gpp = c->group_pair_ptr;
   A.pa = c->pair_adapter;
@@ -677,12 +758,17 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
     hipLaunchKernelGGL((plan_kernel<kPlanThreads, PLAN_COUNT_GLOBAL>), dim3(1),
                        dim3(kPlanThreads), 0, s, A);
   TCL_HIP(hipGetLastError());
-  if (p->L.tiles > 0) {
-    const int64_t n = int64_t(p->L.tiles) * p->L.N;
-    hipLaunchKernelGGL(tile_ranges_kernel, dim3(int((n + 255) / 256)), dim3(256), 0, s, p->d,
-                       p->L.N, p->L.tiles);
-  }
+  p->ranges_ready = false;
+  return TCL_OK;
+}
+
+int plan_prepare_ranges(const tcl_plan *p, hipStream_t s) {
+  if (p->ranges_ready || p->L.tiles == 0) return TCL_OK;
+  const int64_t n = int64_t(p->L.tiles) * p->L.N;
+  hipLaunchKernelGGL(tile_ranges_kernel, dim3(int((n + 255) / 256)), dim3(256), 0, s, p->d,
+                     p->L.N, p->L.tiles);
   TCL_HIP(hipGetLastError());
+  p->ranges_ready = true;
   return TCL_OK;
 }
 
