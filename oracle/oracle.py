@@ -69,8 +69,9 @@ def validate(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
 
     EINVAL: CSR pointers that do not start at 0, end at the token / pair
     count, or decrease; an adapter id outside [0, n_adapters); a non-finite
-    alpha; the same adapter twice in one composite.  EUNSUPPORTED: a group
-    with more than ``max_pairs_per_group`` pairs.  ENOSPC: more tuples than
+    alpha; the same adapter twice in one composite (composites within the
+    pair limit).  EUNSUPPORTED: a group with more than
+    ``max_pairs_per_group`` pairs.  ENOSPC: more tuples than
     ``max_tuples``.  EINVAL outranks EUNSUPPORTED, which outranks ENOSPC."""
     gt = [int(v) for v in group_tok_ptr]
     gp = [int(v) for v in group_pair_ptr]
@@ -93,7 +94,9 @@ def validate(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
             return EINVAL
     for g in range(len(gt) - 1):
         ids = ad[gp[g]:gp[g + 1]]
-        if len(set(ids)) != len(ids):
+        # a group beyond the pair limit is unsupported whatever it holds, so
+        # it is not searched for duplicates
+        if len(ids) <= max_pairs_per_group and len(set(ids)) != len(ids):
             return EINVAL
     for g in range(len(gt) - 1):
         if gp[g + 1] - gp[g] > max_pairs_per_group:

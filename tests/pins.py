@@ -383,6 +383,14 @@ def pin_validation(O):
     assert v(*good, max_tuples=4) == O.OK
     assert v([0, 1, 3], [0, 2, 3], [1, 1, 3], [.5, .5, 1.], max_tuples=0) == O.EINVAL
     assert v([0], [0], [], [], T=0) == O.OK                                    # empty batch
+    # a group beyond the pair limit is EUNSUPPORTED even when it repeats an
+    # adapter; an EINVAL elsewhere in the table still outranks it
+    assert v([0, 1, 3], [0, 2, 3], [1, 1, 3], [.5, .5, 1.], max_pairs_per_group=1) \
+        == O.EUNSUPPORTED
+    assert v([0, 1, 3], [0, 2, 3], [1, 1, 3], [.5, np.nan, 1.], max_pairs_per_group=1) \
+        == O.EINVAL
+    assert v([0, 1, 3], [0, 2, 3], [1, 2, 3], [.5, .5, 1.], max_pairs_per_group=1) \
+        == O.EUNSUPPORTED
 
 
 ALL_PINS = [pin_x1_elora_example, pin_x2_dense_premerge, pin_x3_textbook_lora,

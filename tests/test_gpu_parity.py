@@ -170,13 +170,17 @@ def _bad_tables():
         "over_capacity": good + (3, 3),
         "fits_capacity": good + (3, 4),
         "too_many_pairs": ([0, 1], [0, 65], list(range(65)), [1.0] * 65, 1, None),
+        "too_many_pairs_with_dup": ([0, 1], [0, 65], list(range(64)) + [5], [1.0] * 65, 1,
+                                    None),
+        "too_many_pairs_and_bad_id": ([0, 1, 2], [0, 65, 66], list(range(65)) + [90],
+                                      [1.0] * 66, 2, None),
     }
 
 
 @pytest.mark.parametrize("name", sorted(_bad_tables()))
 def test_plan_device_validation(name):
     tp, pp, ad, al, T, cap = _bad_tables()[name]
-    N = 4 if name != "too_many_pairs" else 80
+    N = 80 if name.startswith("too_many_pairs") else 4
     want = O.validate(np.array(tp), np.array(pp), np.array(ad, np.int32),
                       np.array(al, np.float32), T, N, max_tuples=cap)
     banner(f"validation {name}: expect {want}")

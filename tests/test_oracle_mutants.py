@@ -24,7 +24,8 @@ MUTANTS = {
     "dropped_base": ("return widen(y_base) + delta, delta", "return delta, delta"),
     "bf16_truncated": ("return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)",
                        "return (a.astype(np.uint32) << 8).view(np.float32).astype(np.float64)"),
-    "dup_allowed": ("if len(set(ids)) != len(ids):", "if False:"),
+    "dup_allowed": ("if len(ids) <= max_pairs_per_group and len(set(ids)) != len(ids):",
+                    "if False:"),
     "adapter_fraction_one_side": ("return (d_in + d_out) * r / (d_in * d_out)",
                                   "return d_in * r / (d_in * d_out)"),
 }
