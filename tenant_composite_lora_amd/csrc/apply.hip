@@ -213,22 +213,24 @@ constexpr int kShrinkSteps = 16;  // 32-element K steps each lane has in flight
 // and never read.  The 8 waves split the K steps of d_in, each keeping
 // kShrinkSteps steps of loads in flight, and their partial tiles are summed
 // through LDS in wave order.  z is written final.
-__global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
-  __shared__ f32x4_t red[kShrinkWaves][64];
+// Jobs job0, job0 + stride, ... of one workgroup (8 waves).
+__device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int stride,
+                                        f32x4_t (*red)[64]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   // The item record of the first job is fetched together with the item count
-  // (the grid never exceeds items_cap * rg_total, so the read is in bounds),
-  // which saves one dependent memory round trip.
-  int job = blockIdx.x;
-  int4 head = s.items[job / s.rg_total].head;
-  int tokl = s.items[job / s.rg_total].tok[row];
+  // (clamped to the item table, which a padded grid may pass), which saves
+  // one dependent memory round trip.
+  int job = job0;
+  const int item0 = min(job / s.rg_total, s.items_cap - 1);
+  int4 head = s.items[item0].head;
+  int tokl = s.items[item0].tok[row];
   const int n_items = s.status[ST_ITEMS];
   const int total = n_items * s.rg_total;
 
-  for (; job < total; job += gridDim.x) {
+  for (; job < total; job += stride) {
     const int item = job / s.rg_total, rgg = job - item * s.rg_total;
-    if (job != int(blockIdx.x)) {
+    if (job != job0 || item != item0) {
       head = s.items[item].head;
       tokl = s.items[item].tok[row];
     }
@@ -310,6 +312,11 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
+  __shared__ f32x4_t red[kShrinkWaves][64];
+  shrink_mfma_jobs(s, blockIdx.x, gridDim.x, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -489,13 +496,12 @@ struct OutN<bf16_t, C> {
 // (slot, rank) pairs are loaded before any of them is used.  z is the sum of
 // the shrink's K-chunk partials, added in chunk order.  Accumulation is fp32
 // in slot order, rank order within a slot; y is added once at the end.
+// One expand job (token, 64 * CPL outputs of one module) for the calling wave.
 template <int R, int CPL, bool SPLIT, typename TW, typename TY>
-__global__ __launch_bounds__(64) void expand_kernel(ExpandArgs e) {
+__device__ inline void expand_job(const ExpandArgs &e, int job) {
   constexpr int RB = R < 32 ? R : 32;  // ranks per batch
   constexpr int SB = 32 / RB;          // slots per batch
-  const int lane = threadIdx.x;
-  // XCD-aware job index: workgroups are dealt to the 8 XCDs round-robin
-  const int job = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
+  const int lane = threadIdx.x & 63;
   if (job >= e.jobs) return;
   int mi = 0;
 #pragma unroll
@@ -603,6 +609,16 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandArgs e) {
   if (active) yv.add_store(Yp, acc);
 }
 
+// W waves (jobs) per workgroup.  XCD-aware job index: workgroups are dealt
+// to the 8 XCDs round-robin, and each XCD owns a contiguous range of jobs.
+template <int R, int CPL, bool SPLIT, typename TW, typename TY, int W>
+__global__ __launch_bounds__(64 * W) void expand_kernel(ExpandArgs e) {
+  const int blk = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
+  // the job is uniform across the wave: say so, so that everything derived
+  // from it stays in scalar registers
+  const int job = __builtin_amdgcn_readfirstlane(blk * W + int(threadIdx.x >> 6));
+  expand_job<R, CPL, SPLIT, TW, TY>(e, job);
+}
 
 // ---------------------------------------------------------------------------
 // staged expand: a token tile's B rows are read from HBM once per column slice
@@ -1347,12 +1363,13 @@ static int n_kchunks(const tcl_module *m, int kchunk) {
 
 // Shrink of n (<= kMaxMods) modules in one launch; z[i] is module i's output
 // ([nkc][cap][zld] partial planes when kchunk < d_in).
-static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
-                         const void *const *x, const int64_t *ldx, float *const *z,
-                         const int *zld, int kchunk, int zero_tail, hipStream_t s) {
+// Launch table and grid of the shrink of n (<= kMaxMods) modules.
+static int64_t shrink_args(const tcl_plan *p, const tcl_module *mods, int n,
+                           const void *const *x, const int64_t *ldx, float *const *z,
+                           const int *zld, int kchunk, int zero_tail, ShrinkArgs &a) {
   const bool bf = mods[0].wdtype == TCL_BF16;
   const int rows = bf ? 16 : 4;  // rank rows per workgroup job
-  ShrinkArgs a{};
+  a = ShrinkArgs{};
   a.status = p->d.status;
   a.items = p->d.items;
   a.n_mods = n;
@@ -1380,8 +1397,18 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
   int64_t grid = int64_t(p->L.items_cap) * units;
   if (grid > 32768) grid = 32768;
   if (grid < 1) grid = 1;
+  return grid;
+}
+
+// Shrink of n (<= kMaxMods) modules in one launch; z[i] is module i's output.
+static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
+                         const void *const *x, const int64_t *ldx, float *const *z,
+                         const int *zld, int kchunk, int zero_tail, hipStream_t s) {
+  const bool bf = mods[0].wdtype == TCL_BF16;
+  ShrinkArgs a;
+  const int64_t grid = shrink_args(p, mods, n, x, ldx, z, zld, kchunk, zero_tail, a);
   logf("shrink(%s): modules=%d units/item=%d kchunk=%d grid=%lld", bf ? "mfma" : "valu", n,
-       units, kchunk, (long long)grid);
+       a.rg_total, kchunk, (long long)grid);
   if (bf)
     hipLaunchKernelGGL(shrink_mfma, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
   else
@@ -1390,13 +1417,23 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
   return TCL_OK;
 }
 
+template <int R, int CPL, bool SPLIT, typename TW, typename TY>
+static void launch_expand_w(ExpandArgs e, int waves, hipStream_t s) {
+  // e.jobs_per_xcd counts workgroups per XCD here
+  const int64_t blocks = (int64_t(e.jobs) + waves - 1) / waves;
+  e.jobs_per_xcd = int32_t((blocks + 7) / 8);
+  const int grid = 8 * e.jobs_per_xcd;
+  if (waves == 4)
+    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 4>), dim3(grid), dim3(256), 0, s, e);
+  else
+    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 1>), dim3(grid), dim3(64), 0, s, e);
+}
+
 template <int R, bool SPLIT, typename TW, typename TY>
-static void launch_expand_t(const ExpandArgs &e, int cpl, int grid, hipStream_t s) {
-  if (cpl == 8)
-    hipLaunchKernelGGL((expand_kernel<R, 8, SPLIT, TW, TY>), dim3(grid), dim3(64), 0, s, e);
-  else if (cpl == 4)
-    hipLaunchKernelGGL((expand_kernel<R, 4, SPLIT, TW, TY>), dim3(grid), dim3(64), 0, s, e);
-  else hipLaunchKernelGGL((expand_kernel<R, 2, SPLIT, TW, TY>), dim3(grid), dim3(64), 0, s, e);
+static void launch_expand_t(const ExpandArgs &e, int cpl, int waves, hipStream_t s) {
+  if (cpl == 8) launch_expand_w<R, 8, SPLIT, TW, TY>(e, waves, s);
+  else if (cpl == 4) launch_expand_w<R, 4, SPLIT, TW, TY>(e, waves, s);
+  else launch_expand_w<R, 2, SPLIT, TW, TY>(e, waves, s);
 }
 
 // Which expand runs: the per-token VALU kernel by default; the matrix-core
@@ -1447,6 +1484,10 @@ static void launch_expand_mfma_t(const ExpandMfmaArgs &e, int grid, hipStream_t 
 }
 
 // Expand of n (<= kMaxMods) modules in one launch.
+static int expand_args(const tcl_plan *p, const tcl_module *mods, int n, float *const *z,
+                       const int *zld, int kchunk, void *const *y, const int64_t *ldy,
+                       ExpandArgs &e, int &cpl, int &R, bool &split, int cpl_min = 2);
+
 static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
                          float *const *z, const int *zld, int kchunk, void *const *y,
                          const int64_t *ldy, tcl_dtype yd, hipStream_t s) {
@@ -1559,7 +1600,45 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
     TCL_HIP(hipGetLastError());
     return TCL_OK;
   }
-  ExpandArgs e{};
+  ExpandArgs e;
+  int cpl, R;
+  bool split;
+  int rc = expand_args(p, mods, n, z, zld, kchunk, y, ldy, e, cpl, R, split);
+  if (rc) return rc;
+  // jobs per workgroup: four for prefill-sized launches (fewer, larger
+  // workgroups measured faster there), one otherwise; TCL_EWAVES=1/4 forces
+  const int ew = env_int("TCL_EWAVES", 0);
+  const int waves = ew == 1 || ew == 4 ? ew : (e.jobs >= 32768 ? 4 : 1);
+  logf("expand(valu): modules=%d R=%d cpl=%d jobs=%d waves/workgroup=%d", n, R, cpl, e.jobs,
+       waves);
+  const bool bf = mods[0].wdtype == TCL_BF16;
+  const bool ybf = yd == TCL_BF16;
+#define TCL_EXPAND_CASE(RR)                                                                    \
+  case RR:                                                                                     \
+    if (bf && ybf && split) launch_expand_t<RR, true, bf16_t, bf16_t>(e, cpl, waves, s);       \
+    else if (bf && ybf) launch_expand_t<RR, false, bf16_t, bf16_t>(e, cpl, waves, s);          \
+    else if (bf && split) launch_expand_t<RR, true, bf16_t, float>(e, cpl, waves, s);          \
+    else if (bf) launch_expand_t<RR, false, bf16_t, float>(e, cpl, waves, s);                  \
+    else launch_expand_t<RR, false, float, float>(e, cpl, waves, s);                           \
+    break;
+  switch (R) {
+    TCL_EXPAND_CASE(8)
+    TCL_EXPAND_CASE(16)
+    TCL_EXPAND_CASE(32)
+    TCL_EXPAND_CASE(64)
+  }
+#undef TCL_EXPAND_CASE
+  TCL_HIP(hipGetLastError());
+  return TCL_OK;
+}
+
+// Launch table of the per-token expand of n (<= kMaxMods) modules: outputs
+// per lane, rank bucket and whether z holds split-K partial rows.
+static int expand_args(const tcl_plan *p, const tcl_module *mods, int n, float *const *z,
+                       const int *zld, int kchunk, void *const *y, const int64_t *ldy,
+                       ExpandArgs &e, int &cpl, int &R, bool &split, int cpl_min) {
+  const bool bfw = mods[0].wdtype == TCL_BF16;
+  e = ExpandArgs{};
   e.tok_n = p->d.tok_n;
   e.tok_rec = p->d.tok_rec;
   e.T = p->L.T;
@@ -1567,12 +1646,13 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
   // outputs per lane: 8 unless the batch would then give too few waves
   int64_t jobs8 = 0;
   for (int i = 0; i < n; ++i) jobs8 += int64_t((mods[i].d_out + 511) / 512) * p->L.T;
-  int cpl = jobs8 >= 1024 ? 8 : (jobs8 >= 512 ? 4 : 2);
+  cpl = jobs8 >= 1024 ? 8 : (jobs8 >= 512 ? 4 : 2);
+  if (cpl < cpl_min) cpl = cpl_min;
   const int forced_cpl = env_int("TCL_CPL", 0);  // tuning knob: 2, 4 or 8
   if (forced_cpl == 2 || forced_cpl == 4 || forced_cpl == 8) cpl = forced_cpl;
   int64_t jobs = 0;
   int rmax = 1;
-  bool split = false;
+  split = false;
   for (int i = 0; i < n; ++i) {
     ModArgs &M = e.m[i];
     M.W = mods[i].B_t;
@@ -1594,27 +1674,7 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
   if (jobs > (int64_t(1) << 30)) return fail(TCL_EUNSUPPORTED, "expand grid too large");
   e.jobs = int32_t(jobs);
   e.jobs_per_xcd = int32_t((jobs + 7) / 8);
-  const int grid = 8 * e.jobs_per_xcd;
-  const int R = rank_bucket(rmax);
-  logf("expand(valu): modules=%d R=%d cpl=%d jobs=%lld grid=%d", n, R, cpl, (long long)jobs, grid);
-  const bool bf = mods[0].wdtype == TCL_BF16;
-  const bool ybf = yd == TCL_BF16;
-#define TCL_EXPAND_CASE(RR)                                                \
-  case RR:                                                                 \
-    if (bf && ybf && split) launch_expand_t<RR, true, bf16_t, bf16_t>(e, cpl, grid, s);  \
-    else if (bf && ybf) launch_expand_t<RR, false, bf16_t, bf16_t>(e, cpl, grid, s);     \
-    else if (bf && split) launch_expand_t<RR, true, bf16_t, float>(e, cpl, grid, s);     \
-    else if (bf) launch_expand_t<RR, false, bf16_t, float>(e, cpl, grid, s);             \
-    else launch_expand_t<RR, false, float, float>(e, cpl, grid, s);                      \
-    break;
-  switch (R) {
-    TCL_EXPAND_CASE(8)
-    TCL_EXPAND_CASE(16)
-    TCL_EXPAND_CASE(32)
-    TCL_EXPAND_CASE(64)
-  }
-#undef TCL_EXPAND_CASE
-  TCL_HIP(hipGetLastError());
+  R = rank_bucket(rmax);
   return TCL_OK;
 }
 
