@@ -202,7 +202,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 constexpr int kShrinkWaves = 8;   // waves per workgroup, splitting d_in
-constexpr int kShrinkSteps = 16;  // 32-element K steps each lane has in flight
+constexpr int kShrinkSteps = 8;   // 32-element K steps each lane has in flight
 
 // z[tokens x ranks] = X[tokens x d_in] . A_a^T[d_in x ranks] for one work item
 // (up to 16 tuples of one adapter) and one tile of 16 rank rows, with
@@ -213,7 +213,9 @@ constexpr int kShrinkSteps = 16;  // 32-element K steps each lane has in flight
 // and never read.  The 8 waves split the K steps of d_in, each keeping
 // kShrinkSteps steps of loads in flight, and their partial tiles are summed
 // through LDS in wave order.  z is written final.
-// Jobs job0, job0 + stride, ... of one workgroup (8 waves).
+// Jobs job0, job0 + stride, ... of one workgroup (8 waves); each lane keeps
+// STEPS K steps of loads in flight.
+template <int STEPS>
 __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int stride,
                                         f32x4_t (*red)[64]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -269,10 +271,10 @@ __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int strid
     const int per = (c1 - c0 + kShrinkWaves - 1) / kShrinkWaves;
     const int s0 = c0 + w * per, s1 = min(c1, s0 + per);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int st = s0; st < s1; st += kShrinkSteps) {
-      bf16x8_t xv[kShrinkSteps], av[kShrinkSteps];
+    for (int st = s0; st < s1; st += STEPS) {
+      bf16x8_t xv[STEPS], av[STEPS];
 #pragma unroll
-      for (int u = 0; u < kShrinkSteps; ++u) {
+      for (int u = 0; u < STEPS; ++u) {
         const int e0 = (st + u) * 32 + kg * 8;  // first element of this lane's granule
         const bool in = st + u < s1 && e0 < dd;
         uint4 xb = make_uint4(0, 0, 0, 0), ab = make_uint4(0, 0, 0, 0);
@@ -282,7 +284,7 @@ __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int strid
         av[u] = __builtin_bit_cast(bf16x8_t, ab);
       }
 #pragma unroll
-      for (int u = 0; u < kShrinkSteps; ++u)
+      for (int u = 0; u < STEPS; ++u)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[u], av[u], acc, 0, 0, 0);
     }
     red[w][lane] = acc;
@@ -314,9 +316,10 @@ __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int strid
   }
 }
 
+template <int STEPS>
 __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
   __shared__ f32x4_t red[kShrinkWaves][64];
-  shrink_mfma_jobs(s, blockIdx.x, gridDim.x, red);
+  shrink_mfma_jobs<STEPS>(s, blockIdx.x, gridDim.x, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -496,11 +499,12 @@ struct OutN<bf16_t, C> {
 // (slot, rank) pairs are loaded before any of them is used.  z is the sum of
 // the shrink's K-chunk partials, added in chunk order.  Accumulation is fp32
 // in slot order, rank order within a slot; y is added once at the end.
-// One expand job (token, 64 * CPL outputs of one module) for the calling wave.
-template <int R, int CPL, bool SPLIT, typename TW, typename TY>
+// One expand job (token, 64 * CPL outputs of one module) for the calling wave;
+// BR (slot, rank) rows of B are loaded per batch.
+template <int R, int CPL, bool SPLIT, typename TW, typename TY, int BR>
 __device__ inline void expand_job(const ExpandArgs &e, int job) {
-  constexpr int RB = R < 32 ? R : 32;  // ranks per batch
-  constexpr int SB = 32 / RB;          // slots per batch
+  constexpr int RB = R < BR ? R : BR;  // ranks per batch
+  constexpr int SB = BR / RB;          // slots per batch
   const int lane = threadIdx.x & 63;
   if (job >= e.jobs) return;
   int mi = 0;
@@ -611,13 +615,13 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
 
 // W waves (jobs) per workgroup.  XCD-aware job index: workgroups are dealt
 // to the 8 XCDs round-robin, and each XCD owns a contiguous range of jobs.
-template <int R, int CPL, bool SPLIT, typename TW, typename TY, int W>
+template <int R, int CPL, bool SPLIT, typename TW, typename TY, int W, int BR>
 __global__ __launch_bounds__(64 * W) void expand_kernel(ExpandArgs e) {
   const int blk = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
   // the job is uniform across the wave: say so, so that everything derived
   // from it stays in scalar registers
   const int job = __builtin_amdgcn_readfirstlane(blk * W + int(threadIdx.x >> 6));
-  expand_job<R, CPL, SPLIT, TW, TY>(e, job);
+  expand_job<R, CPL, SPLIT, TW, TY, BR>(e, job);
 }
 
 // ---------------------------------------------------------------------------
@@ -1409,8 +1413,13 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
   const int64_t grid = shrink_args(p, mods, n, x, ldx, z, zld, kchunk, zero_tail, a);
   logf("shrink(%s): modules=%d units/item=%d kchunk=%d grid=%lld", bf ? "mfma" : "valu", n,
        a.rg_total, kchunk, (long long)grid);
-  if (bf)
-    hipLaunchKernelGGL(shrink_mfma, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
+  // K steps in flight per lane: 8 (95 VGPRs, two workgroups per CU) measured
+  // faster than 16 (161 VGPRs, one per CU); TCL_SSTEPS=16 forces the deeper one
+  const int steps = env_int("TCL_SSTEPS", kShrinkSteps) == 16 ? 16 : 8;
+  if (bf && steps == 8)
+    hipLaunchKernelGGL(shrink_mfma<8>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
+  else if (bf)
+    hipLaunchKernelGGL(shrink_mfma<16>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
   else
     hipLaunchKernelGGL((shrink_valu<float>), dim3(int(grid)), dim3(256), 0, s, a);
   TCL_HIP(hipGetLastError());
@@ -1423,10 +1432,18 @@ static void launch_expand_w(ExpandArgs e, int waves, hipStream_t s) {
   const int64_t blocks = (int64_t(e.jobs) + waves - 1) / waves;
   e.jobs_per_xcd = int32_t((blocks + 7) / 8);
   const int grid = 8 * e.jobs_per_xcd;
-  if (waves == 4)
-    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 4>), dim3(grid), dim3(256), 0, s, e);
+  // rows of B per load batch: 16 when a lane holds 8 outputs (fewer VGPRs,
+  // more waves per SIMD), else 32; TCL_EBATCH=16/32 forces
+  const int ebf = env_int("TCL_EBATCH", 0);
+  const int br = ebf == 16 || ebf == 32 ? ebf : (CPL == 8 ? 16 : 32);
+  if (waves == 4 && br == 16)
+    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 4, 16>), dim3(grid), dim3(256), 0, s, e);
+  else if (waves == 4)
+    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 4, 32>), dim3(grid), dim3(256), 0, s, e);
+  else if (br == 16)
+    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 1, 16>), dim3(grid), dim3(64), 0, s, e);
   else
-    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 1>), dim3(grid), dim3(64), 0, s, e);
+    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 1, 32>), dim3(grid), dim3(64), 0, s, e);
 }
 
 template <int R, bool SPLIT, typename TW, typename TY>
