@@ -1622,10 +1622,12 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
   bool split;
   int rc = expand_args(p, mods, n, z, zld, kchunk, y, ldy, e, cpl, R, split);
   if (rc) return rc;
-  // jobs per workgroup: four for prefill-sized launches (fewer, larger
-  // workgroups measured faster there), one otherwise; TCL_EWAVES=1/4 forces
+  // jobs per workgroup: four for prefill-sized launches of ranks up to 16
+  // (measured faster there: sparse prefill 148 -> 141 us), one otherwise (four
+  // measured slower for rank 32: retained-rank batch 870 -> 1001 us);
+  // TCL_EWAVES=1/4 forces
   const int ew = env_int("TCL_EWAVES", 0);
-  const int waves = ew == 1 || ew == 4 ? ew : (e.jobs >= 32768 ? 4 : 1);
+  const int waves = ew == 1 || ew == 4 ? ew : (e.jobs >= 32768 && R <= 16 ? 4 : 1);
   logf("expand(valu): modules=%d R=%d cpl=%d jobs=%d waves/workgroup=%d", n, R, cpl, e.jobs,
        waves);
   const bool bf = mods[0].wdtype == TCL_BF16;
