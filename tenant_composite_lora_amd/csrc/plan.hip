@@ -67,6 +67,16 @@ int hip_fail(hipError_t e, const char *what) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// multi-workgroup mapping: groups per workgroup, pair capacity per workgroup
+// (a valid table has at most TCL_MAX_PAIRS_PER_GROUP pairs per group), and
+// the limits within which it is used
+constexpr int kMgGroups = 64;
+constexpr int kMgPairs = kMgGroups * TCL_MAX_PAIRS_PER_GROUP;
+constexpr int kMgThreads = 256;
+constexpr int kMultiMaxN = 4096;
+constexpr int kMultiMaxBlocks = 128;
+
+
 int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLayout *L) {
   const int64_t kLim = int64_t(1) << 24;
   if (T < 0 || G < 0 || NP < 0 || cap < 0)
@@ -91,10 +101,16 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   // Counting path in LDS: the same without the last two pair arrays, plus
   // the (adapter, chunk) histogram.
   const int64_t fixed = 3 * int64_t(G) + 2 + 5 * int64_t(NP);
+  const int64_t mblocks = (int64_t(G) + kMgGroups - 1) / kMgGroups;
   if (NP <= kDirectMaxPairs && direct_ints <= kPlanLdsInts) {
     l.mode = PLAN_DIRECT;
     l.threads = NP <= 256 ? 256 : kPlanThreads;
     l.chunks = 1;
+  } else if (N <= kMultiMaxN && mblocks <= kMultiMaxBlocks) {
+    l.mode = PLAN_MULTI;
+    l.threads = kMgThreads;
+    l.chunks = 1;
+    l.blocks = int32_t(mblocks < 1 ? 1 : mblocks);
   } else {
     l.threads = kPlanThreads;
     int64_t c = (NP + 7) / 8;
@@ -142,6 +158,11 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.o_sgbase = take(size_t(G) * 4);
   l.o_shist = take(l.mode == PLAN_COUNT_GLOBAL ? size_t(N) * size_t(l.chunks) * 4 : 4);
   l.o_sseg = take(l.mode == PLAN_DIRECT ? 4 : size_t(N) * 4);
+  const bool multi = l.mode == PLAN_MULTI;
+  l.o_mhist = take(multi ? size_t(N) * size_t(l.blocks) * 4 : 4);
+  l.o_mblk = take(multi ? size_t(l.blocks) * 16 : 4);
+  l.o_msst = take(multi ? size_t(N) * 4 : 4);
+  l.o_msib = take(multi ? size_t(N) * 4 : 4);
   l.tiles = T >= kMfmaMinTokens ? (T + kXTok - 1) / kXTok : 0;
   l.o_ranges = take(size_t(l.tiles) * size_t(N) * 8);
   l.total = o;
@@ -696,6 +717,375 @@ __global__ __launch_bounds__(256) void tile_ranges_kernel(PlanDev d, int32_t N, 
   d.ranges[idx] = make_int2(lo, lo2);
 }
 
+// ---------------------------------------------------------------------------
+// mapping of larger tables over many workgroups (PLAN_MULTI)
+// ---------------------------------------------------------------------------
+// Workgroup b owns the kMgGroups consecutive groups starting at b*kMgGroups,
+// so earlier workgroups hold earlier tokens and the (adapter, token, slot)
+// order of the result is that of the single-workgroup paths.
+//   plan_m_local   checks its groups and pairs, computes slots, counts tuples
+//                  per adapter, and ranks every pair among the earlier pairs
+//                  of the same adapter in the workgroup (tickets into
+//                  per-adapter buckets, as in the direct path);
+//   plan_m_scan    (one workgroup) combines the workgroups' error bits and
+//                  tuple totals, turns the per-(adapter, workgroup) counts
+//                  into prefixes, and builds the segment table, the work
+//                  items and the status words;
+//   plan_m_scatter writes the tuples and the token index.  A pair's first
+//                  tuple goes to (segment start of its adapter) + (tuples of
+//                  that adapter in earlier workgroups) + (its rank).
+struct MArgs {
+  int32_t T, G, NP, N, cap, items_cap, NB;
+  const int32_t *gtp, *gpp, *pa;
+  const float *pw;
+  PlanDev d;
+};
+
+// LDS of plan_m_local: six pair arrays of kMgPairs ints and two adapter arrays
+static size_t m_local_lds_bytes(int N) {
+  return (size_t(6) * kMgPairs + 2 * size_t(N) + 2 + 2 * (kMgGroups + 1) + 4 * kSlotInts) * 4;
+}
+static size_t lds_max_bytes() { return m_local_lds_bytes(kMultiMaxN); }
+
+__global__ __launch_bounds__(kMgThreads) void plan_m_local(MArgs A) {
+  extern __shared__ __align__(16) int m_lds[];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int T = A.T, G = A.G, NP = A.NP, N = A.N, NB = A.NB;
+  int *l_pa = m_lds, *l_ptl = l_pa + kMgPairs, *l_grp = l_ptl + kMgPairs;
+  int *l_tkt = l_grp + kMgPairs, *l_bkt = l_tkt + kMgPairs, *l_bkw = l_bkt + kMgPairs;
+  int *l_cnt = l_bkw + kMgPairs;  // tuples per adapter
+  int *l_pst = l_cnt + N;         // pairs per adapter, then bucket starts [N + 1]
+  int *l_gtp = l_pst + N + 1, *l_gpp = l_gtp + kMgGroups + 1;
+  int *tmp = l_gpp + kMgGroups + 1;
+
+  const int g0 = min(G, b * kMgGroups), g1 = min(G, g0 + kMgGroups), ng = g1 - g0;
+  if (tid <= ng) {
+    l_gtp[tid] = A.gtp[g0 + tid];
+    l_gpp[tid] = A.gpp[g0 + tid];
+  }
+  for (int a = tid; a < N; a += kMgThreads) {
+    l_cnt[a] = 0;
+    l_pst[a] = 0;
+  }
+  __syncthreads();
+
+  // ---- groups
+  int err = 0;
+  if (b == 0 && tid == 0 &&
+      (A.gtp[0] != 0 || A.gtp[G] != T || A.gpp[0] != 0 || A.gpp[G] != NP))
+    err |= EB_INVAL;
+  int gtup = 0;
+  if (tid < ng) {
+    const int t0 = l_gtp[tid], t1 = l_gtp[tid + 1], q0 = l_gpp[tid], q1 = l_gpp[tid + 1];
+    if (!(0 <= t0 && t0 <= t1 && t1 <= T && 0 <= q0 && q0 <= q1 && q1 <= NP)) err |= EB_INVAL;
+    else if (q1 - q0 > TCL_MAX_PAIRS_PER_GROUP) err |= EB_UNSUP;
+    else gtup = (t1 - t0) * (q1 - q0);
+  }
+  int P_b;
+  block_excl_scan<kMgThreads>(gtup, tmp + 0 * kSlotInts, &P_b);
+  const int err_g = block_or<kMgThreads>(err, tmp + 1 * kSlotInts);
+  const int qb0 = l_gpp[0];
+  const int span = (err_g & EB_INVAL) ? 0 : l_gpp[ng] - qb0;
+  if ((err_g & EB_INVAL) || span > kMgPairs || (err_g & EB_UNSUP)) {
+    // the table is rejected: only look for invalid ids and weights (an
+    // EINVAL outranks the other codes)
+    err = err_g;
+    if (!(err_g & EB_INVAL)) {
+      for (int q = qb0 + tid; q < qb0 + span; q += kMgThreads) {
+        const int aq = A.pa[q];
+        if (aq < 0 || aq >= N) err |= EB_INVAL;
+        if ((__float_as_uint(A.pw[q]) & 0x7f800000u) == 0x7f800000u) err |= EB_INVAL;
+      }
+      // duplicates in the groups within the pair limit
+      if (tid < ng) {
+        const int q0 = l_gpp[tid], q1 = l_gpp[tid + 1];
+        if (q1 - q0 <= TCL_MAX_PAIRS_PER_GROUP)
+          for (int q = q0; q < q1; ++q)
+            for (int q2 = q + 1; q2 < q1; ++q2)
+              if (A.pa[q] == A.pa[q2]) err |= EB_INVAL;
+      }
+    }
+    err = block_or<kMgThreads>(err, tmp + 2 * kSlotInts);
+    if (tid == 0) {
+      A.d.m_blk[4 * b] = 0;
+      A.d.m_blk[4 * b + 1] = err;
+    }
+    return;
+  }
+
+  // ---- pairs: stage, group index, checks, slots, counts and tickets
+  for (int i = tid; i < span; i += kMgThreads) l_pa[i] = A.pa[qb0 + i];
+  if (tid < ng) {
+    const int q0 = l_gpp[tid] - qb0, q1 = l_gpp[tid + 1] - qb0;
+    const int tl = l_gtp[tid + 1] - l_gtp[tid];
+    for (int q = q0; q < q1; ++q) {
+      l_grp[q] = tid;
+      l_ptl[q] = tl;
+    }
+  }
+  __syncthreads();
+  err = 0;
+  for (int i = tid; i < span; i += kMgThreads) {
+    const int aq = l_pa[i];
+    const bool a_ok = aq >= 0 && aq < N;
+    if (!a_ok) err |= EB_INVAL;
+    if ((__float_as_uint(A.pw[qb0 + i]) & 0x7f800000u) == 0x7f800000u) err |= EB_INVAL;
+    const int g = l_grp[i];
+    const int q0 = l_gpp[g] - qb0, q1 = l_gpp[g + 1] - qb0;
+    int sl = 0, dup = 0;
+    for (int q2 = q0; q2 < q1; q2 += 8) {
+      int av[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) av[u] = q2 + u < q1 ? l_pa[q2 + u] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = q2 + u < q1;
+        sl += (in && av[u] < aq) ? 1 : 0;
+        dup |= (in && av[u] == aq && q2 + u != i) ? 1 : 0;
+      }
+    }
+    if (dup) err |= EB_INVAL;
+    A.d.s_slot[qb0 + i] = sl;
+    if (a_ok) {
+      atomicAdd(&l_cnt[aq], l_ptl[i]);
+      l_tkt[i] = atomicAdd(&l_pst[aq], 1);
+    }
+  }
+  err = block_or<kMgThreads>(err, tmp + 2 * kSlotInts);
+  if (err) {
+    if (tid == 0) {
+      A.d.m_blk[4 * b] = 0;
+      A.d.m_blk[4 * b + 1] = err;
+    }
+    return;
+  }
+
+  // ---- bucket starts (exclusive scan of the pair counts, in place)
+  {
+    const int per = (N + kMgThreads - 1) / kMgThreads;
+    const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
+    int sum = 0;
+    for (int a = a0; a < a1; ++a) sum += l_pst[a];
+    int tot;
+    int run = block_excl_scan<kMgThreads>(sum, tmp + 3 * kSlotInts, &tot);
+    for (int a = a0; a < a1; ++a) {
+      const int c = l_pst[a];
+      l_pst[a] = run;
+      run += c;
+    }
+    if (tid == 0) l_pst[N] = tot;
+  }
+  __syncthreads();
+  for (int i = tid; i < span; i += kMgThreads) {
+    const int e = l_pst[l_pa[i]] + l_tkt[i];
+    l_bkt[e] = i;
+    l_bkw[e] = l_ptl[i];
+  }
+  __syncthreads();
+  // ---- rank: tuples of the same adapter's earlier pairs in this workgroup
+  for (int i = tid; i < span; i += kMgThreads) {
+    const int a = l_pa[i];
+    const int b0 = l_pst[a], b1 = l_pst[a + 1];
+    int r = 0;
+    for (int e = b0; e < b1; e += 8) {
+      int qq[8], ww[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        qq[u] = e + u < b1 ? l_bkt[e + u] : kMgPairs;
+        ww[u] = e + u < b1 ? l_bkw[e + u] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += qq[u] < i ? ww[u] : 0;
+    }
+    A.d.s_pos[qb0 + i] = r;
+  }
+  for (int a = tid; a < N; a += kMgThreads) A.d.m_hist[int64_t(a) * NB + b] = l_cnt[a];
+  if (tid == 0) {
+    A.d.m_blk[4 * b] = P_b;
+    A.d.m_blk[4 * b + 1] = 0;
+  }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_m_scan(MArgs A) {
+  constexpr int NT = kPlanThreads;
+  __shared__ int tmp[6 * kSlotInts];
+  __shared__ int s_tot[kMultiMaxN];
+  const int tid = threadIdx.x, NB = A.NB, N = A.N;
+  // ---- workgroup totals and error bits (NB <= kMultiMaxBlocks <= NT)
+  int pb = 0, err = 0;
+  if (tid < NB) {
+    pb = A.d.m_blk[4 * tid];
+    err = A.d.m_blk[4 * tid + 1];
+  }
+  int P;
+  const int base = block_excl_scan<NT>(pb, tmp + 0 * kSlotInts, &P);
+  if (tid < NB) A.d.m_blk[4 * tid + 2] = base;
+  err = block_or<NT>(err, tmp + 1 * kSlotInts);
+  const int code = (err & EB_INVAL) ? TCL_EINVAL
+                 : (err & EB_UNSUP) ? TCL_EUNSUPPORTED
+                 : (P > A.cap) ? TCL_ENOSPC : TCL_OK;
+  if (code != TCL_OK) {
+    if (tid == 0) {
+      A.d.status[ST_CODE] = code;
+      A.d.status[ST_TUPLES] = code == TCL_ENOSPC ? P : 0;
+      A.d.status[ST_SEGMENTS] = 0;
+      A.d.status[ST_ITEMS] = 0;
+    }
+    return;
+  }
+  // ---- per adapter: prefix over workgroups (in place) and total; a column
+  //      is NB <= kMultiMaxBlocks ints, read 32 at a time
+  for (int a = tid; a < N; a += NT) {
+    int32_t *h = A.d.m_hist + int64_t(a) * NB;
+    int run = 0;
+    for (int b0 = 0; b0 < NB; b0 += 32) {
+      int v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) v[u] = b0 + u < NB ? h[b0 + u] : 0;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        if (b0 + u < NB) h[b0 + u] = run;
+        run += v[u];
+      }
+    }
+    s_tot[a] = run;
+  }
+  __syncthreads();
+  // ---- segments and work items: one scan over adapters
+  const int per = (N + NT - 1) / NT;
+  const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
+  int sv[3] = {0, 0, 0}, st[3];
+  for (int a = a0; a < a1; ++a) {
+    const int c = s_tot[a];
+    sv[0] += c;
+    sv[1] += c > 0;
+    sv[2] += (c + kTile - 1) / kTile;
+  }
+  block_excl_scan_n<NT, 3>(sv, tmp + 2 * kSlotInts, st);
+  int ec = sv[0], en = sv[1], ei = sv[2];
+  for (int a = a0; a < a1; ++a) {
+    const int c = s_tot[a];
+    A.d.m_sst[a] = ec;
+    A.d.m_sib[a] = ei;
+    A.d.s_seg[a] = en;
+    if (c > 0) {
+      A.d.seg_adapter[en] = a;
+      A.d.seg_begin[en] = ec;
+      for (int p0 = ec, i = ei; p0 < ec + c; p0 += kTile, ++i)
+        if (i < A.items_cap) A.d.items[i].head = make_int4(a, p0, min(ec + c, p0 + kTile) - p0, en);
+      ++en;
+      ei += (c + kTile - 1) / kTile;
+    }
+    ec += c;
+  }
+  if (tid == 0) {
+    A.d.seg_begin[st[1]] = P;
+    A.d.status[ST_TUPLES] = P;
+    A.d.status[ST_SEGMENTS] = st[1];
+    A.d.status[ST_ITEMS] = st[2];
+    A.d.status[ST_CODE] = TCL_OK;
+  }
+}
+
+__global__ __launch_bounds__(kMgThreads) void plan_m_scatter(MArgs A) {
+  __shared__ int l_gtp[kMgGroups + 1], l_gpp[kMgGroups + 1], l_gbase[kMgGroups];
+  __shared__ int l_grp[kMgPairs];
+  __shared__ int tmp[kSlotInts];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int T = A.T, G = A.G, NB = A.NB;
+  if (A.d.status[ST_CODE] != TCL_OK) {
+    // rejected: an empty token index, so that every later kernel is a no-op
+    const int tper = (T + NB - 1) / NB;
+    const int t0 = min(T, b * tper), t1 = min(T, t0 + tper);
+    for (int t = t0 + tid; t < t1; t += kMgThreads) {
+      A.d.tok_ptr[t] = 0;
+      A.d.tok_n[t] = 0;
+    }
+    if (b == 0 && tid == 0) A.d.tok_ptr[T] = 0;
+    return;
+  }
+  const int g0 = min(G, b * kMgGroups), g1 = min(G, g0 + kMgGroups), ng = g1 - g0;
+  if (tid <= ng) {
+    l_gtp[tid] = A.gtp[g0 + tid];
+    l_gpp[tid] = A.gpp[g0 + tid];
+  }
+  __syncthreads();
+  // group tuple bases and the token index
+  const int gtup =
+      tid < ng ? (l_gtp[tid + 1] - l_gtp[tid]) * (l_gpp[tid + 1] - l_gpp[tid]) : 0;
+  int unused;
+  const int gb = block_excl_scan<kMgThreads>(gtup, tmp, &unused) + A.d.m_blk[4 * b + 2];
+  const int qb0 = l_gpp[0];
+  if (tid < ng) {
+    const int t0 = l_gtp[tid], t1 = l_gtp[tid + 1], q0 = l_gpp[tid], q1 = l_gpp[tid + 1];
+    const int pl = q1 - q0;
+    l_gbase[tid] = gb;
+    for (int q = q0; q < q1; ++q) l_grp[q - qb0] = tid;
+    for (int t = t0; t < t1; ++t) {
+      A.d.tok_ptr[t] = gb + (t - t0) * pl;
+      A.d.tok_n[t] = pl;
+    }
+  }
+  if (b == NB - 1 && tid == 0) A.d.tok_ptr[T] = A.d.status[ST_TUPLES];
+  __syncthreads();
+  const int span = l_gpp[ng] - qb0;
+  for (int i = tid; i < span; i += kMgThreads) {
+    const int q = qb0 + i;
+    const int g = l_grp[i];
+    const int t0 = l_gtp[g], tl = l_gtp[g + 1] - t0, pl = l_gpp[g + 1] - l_gpp[g];
+    const int a = A.pa[q], s = A.d.s_slot[q], gbase = l_gbase[g];
+    const float w = A.pw[q];
+    const int sst = A.d.m_sst[a];
+    const int base = sst + A.d.m_hist[int64_t(a) * NB + b] + A.d.s_pos[q];
+    const int sg = A.d.s_seg[a], sib = A.d.m_sib[a];
+    for (int k = 0; k < tl; ++k) {
+      const int p = base + k;
+      // positions are < P <= cap by construction; the guards keep a logic
+      // error from writing outside the plan buffer
+      if (p >= A.cap || gbase + k * pl + s >= A.cap || s >= kSlotPad) continue;
+      A.d.tup_token[p] = t0 + k;
+      A.d.tup_adapter[p] = a;
+      A.d.tup_alpha[p] = w;
+      A.d.tup_slot[p] = s;
+      A.d.tok_tuple[gbase + k * pl + s] = p;
+      A.d.tok_rec[int64_t(t0 + k) * kSlotPad + s] = make_int4(p, a, __float_as_int(w), sg);
+      const int local = p - sst;
+      const int it = sib + local / kTile;
+      if (it < A.items_cap) A.d.items[it].tok[local % kTile] = t0 + k;
+    }
+  }
+}
+
+static int launch_plan_multi(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
+  MArgs A;
+  A.T = p->L.T;
+  A.G = p->L.G;
+  A.NP = p->L.NP;
+  A.N = p->L.N;
+  A.cap = p->L.cap;
+  A.items_cap = p->L.items_cap;
+  A.NB = p->L.blocks;
+  A.gtp = c->group_tok_ptr;
+  A.gpp = c->group_pair_ptr;
+  A.pa = c->pair_adapter;
+  A.pw = c->pair_alpha;
+  A.d = p->d;
+  const size_t lds = m_local_lds_bytes(A.N);
+  static bool attr_set = false;
+  if (!attr_set) {
+    TCL_HIP(hipFuncSetAttribute(reinterpret_cast<const void *>(plan_m_local),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_max_bytes())));
+    attr_set = true;
+  }
+  logf("plan(multi): T=%d G=%d pairs=%d N=%d workgroups=%d lds=%zu", A.T, A.G, A.NP, A.N, A.NB,
+       lds);
+  hipLaunchKernelGGL(plan_m_local, dim3(A.NB), dim3(kMgThreads), lds, s, A);
+  hipLaunchKernelGGL(plan_m_scan, dim3(1), dim3(kPlanThreads), 0, s, A);
+  hipLaunchKernelGGL(plan_m_scatter, dim3(A.NB), dim3(kMgThreads), 0, s, A);
+  TCL_HIP(hipGetLastError());
+  return TCL_OK;
+}
+
 static void bind(tcl_plan *p) {
   char *b = static_cast<char *>(p->buf);
   const PlanLayout &L = p->L;
@@ -718,6 +1108,10 @@ static void bind(tcl_plan *p) {
   d.s_gbase = reinterpret_cast<int32_t *>(b + L.o_sgbase);
   d.s_hist = reinterpret_cast<int32_t *>(b + L.o_shist);
   d.s_seg = reinterpret_cast<int32_t *>(b + L.o_sseg);
+  d.m_hist = reinterpret_cast<int32_t *>(b + L.o_mhist);
+  d.m_blk = reinterpret_cast<int32_t *>(b + L.o_mblk);
+  d.m_sst = reinterpret_cast<int32_t *>(b + L.o_msst);
+  d.m_sib = reinterpret_cast<int32_t *>(b + L.o_msib);
   d.ranges = reinterpret_cast<int2 *>(b + L.o_ranges);
 }
 
@@ -745,6 +1139,11 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
   A.pa = c->pair_adapter;
   A.pw = c->pair_alpha;
   A.d = p->d;
+  if (A.mode == PLAN_MULTI) {
+    int rc = launch_plan_multi(p, c, s);
+    p->ranges_ready = false;
+    return rc;
+  }
   logf("plan: T=%d G=%d pairs=%d N=%d cap=%d chunks=%d mode=%d threads=%d", A.T, A.G, A.NP, A.N,
        A.cap, A.C, A.mode, p->L.threads);
   if (A.mode == PLAN_DIRECT && p->L.threads == 64)

@@ -59,19 +59,22 @@ struct PlanLayout {
   // sizes
   int32_t T, G, NP, N, cap, items_cap;
   int32_t chunks;   // counting path: groups are split into this many chunks
-  int32_t mode;     // PLAN_DIRECT, PLAN_COUNT_LDS or PLAN_COUNT_GLOBAL
+  int32_t mode;     // PLAN_DIRECT, PLAN_MULTI, PLAN_COUNT_LDS or PLAN_COUNT_GLOBAL
+  int32_t blocks;   // PLAN_MULTI: workgroups of the local and scatter kernels
   int32_t threads;  // workgroup size of the mapping kernel (64, 256 or 1024)
   int32_t tiles;    // token tiles of kXTok with tuple ranges (0: none)
   // byte offsets inside the device buffer
   size_t o_status, o_tok, o_ad, o_slot, o_alpha, o_toktuple, o_tokrec, o_tokn, o_tokptr,
       o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_sseg, o_ranges,
-      total;
+      o_mhist, o_mblk, o_msst, o_msib, total;
 };
 
-// Mapping-stage algorithms: small tables count positions directly (every pair
-// scans all pairs, O(P^2) on LDS, no scans); larger ones run the chunked
-// counting sort with its scratch in LDS or, beyond LDS, in the plan buffer.
-enum { PLAN_DIRECT = 0, PLAN_COUNT_LDS = 1, PLAN_COUNT_GLOBAL = 2 };
+// Mapping-stage algorithms: small tables run in one workgroup with the table
+// in LDS (direct); larger ones over many workgroups of consecutive groups
+// (multi: local counts and ranks, one scan, scatter); tables beyond the
+// multi path's limits run the chunked counting sort in one workgroup, with
+// its scratch in LDS or, beyond LDS, in the plan buffer.
+enum { PLAN_DIRECT = 0, PLAN_COUNT_LDS = 1, PLAN_COUNT_GLOBAL = 2, PLAN_MULTI = 3 };
 
 int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLayout *L);
 
@@ -92,7 +95,11 @@ struct PlanDev {
   int32_t *seg_adapter, *seg_begin;
   Item *items;
   int32_t *s_slot, *s_group, *s_pos, *s_gbase, *s_hist;
-  int32_t *s_seg;  // counting path: segment index of every touched adapter [N]
+  int32_t *s_seg;  // counting / multi path: segment index of every touched adapter [N]
+  // multi-workgroup path: per-(adapter, workgroup) tuple counts then bases
+  // [N][blocks], per-workgroup {tuples, error bits, tuple base, -} [blocks][4],
+  // per-adapter segment start and first work item [N]
+  int32_t *m_hist, *m_blk, *m_sst, *m_sib;
   int2 *ranges;  // [tiles][N]: tuples of segment u whose token lies in tile
 };
 

@@ -73,6 +73,14 @@ EDGE_CASES = {
                         tokens_per_group=37),
     "mfma_many_adapters": dict(seed=133, T=256, N=600, d_in=64, d_out=264, r_max=8,
                                max_pairs=8),
+    # mapping-stage modes: more pairs than the one-workgroup direct path holds
+    # (multi-workgroup), more adapters or more groups than the multi path
+    # takes (one-workgroup counting sort)
+    "multi_ragged": dict(seed=134, T=700, N=90, d_in=64, d_out=72, r_max=8, max_pairs=5,
+                         empty_frac=0.05),
+    "count_5000_adapters": dict(seed=135, T=600, N=5000, d_in=64, d_out=64, r_max=4,
+                                max_pairs=3),
+    "count_9000_groups": dict(seed=136, T=9000, N=64, d_in=32, d_out=32, r_max=4, max_pairs=2),
 }
 
 
@@ -175,6 +183,75 @@ def _bad_tables():
         "too_many_pairs_and_bad_id": ([0, 1, 2], [0, 65, 66], list(range(65)) + [90],
                                       [1.0] * 66, 2, None),
     }
+
+
+def _bad_large_tables():
+    """Tables of a few hundred groups (the multi-workgroup mapping path) with
+    one defect each; (group_tok_ptr, group_pair_ptr, adapters, alphas, T, N,
+    max_tuples)."""
+    base = W.random_case(150, T=400, N=50, d_in=16, d_out=16, r_max=4, max_pairs=4).composites
+    gt, gp = base.group_tok_ptr.astype(np.int64), base.group_pair_ptr.astype(np.int64)
+    ad, al = base.pair_adapter.astype(np.int64), base.pair_alpha.astype(np.float32)
+    T, N, NP = base.n_tokens, base.n_adapters, base.n_pairs
+    mid = NP // 2
+    out = {}
+    out["ok"] = (gt, gp, ad, al, T, N, None)
+    a2 = ad.copy(); a2[mid] = N
+    out["bad_id"] = (gt, gp, a2, al, T, N, None)
+    w2 = al.copy(); w2[NP - 1] = np.nan
+    out["nan_alpha"] = (gt, gp, ad, w2, T, N, None)
+    g = int(np.searchsorted(gp, mid, side="right")) - 1
+    while gp[g + 1] - gp[g] < 2:
+        g += 1
+    a3 = ad.copy(); a3[gp[g] + 1] = a3[gp[g]]
+    out["duplicate"] = (gt, gp, a3, al, T, N, None)
+    # one group of 70 pairs (beyond the limit) right before a group with a
+    # repeated adapter: EINVAL outranks EUNSUPPORTED
+    big = list(range(70))
+    gp4 = np.concatenate([[0, 70], 70 + gp[1:]]).astype(np.int64)
+    gt4 = np.concatenate([[0, 1], 1 + gt[1:]]).astype(np.int64)
+    a4 = np.concatenate([big, a3]).astype(np.int64)
+    w4 = np.concatenate([np.ones(70, np.float32), al]).astype(np.float32)
+    out["oversized_then_dup"] = (gt4, gp4, a4, w4, T + 1, 80, None)
+    out["oversized_only"] = (gt4, gp4, np.concatenate([big, ad]).astype(np.int64), w4, T + 1,
+                             80, None)
+    # the repeated adapter in the group right after the oversized one (the
+    # same workgroup of the multi path)
+    g1 = 0
+    while gp[g1 + 1] - gp[g1] < 2:
+        g1 += 1
+    a6 = ad.copy(); a6[gp[g1] + 1] = a6[gp[g1]]
+    out["oversized_dup_same_block"] = (gt4, gp4, np.concatenate([big, a6]).astype(np.int64), w4,
+                                       T + 1, 80, None)
+    out["over_capacity"] = (gt, gp, ad, al, T, N, base.n_tuples() - 1)
+    gt5 = gt.copy(); gt5[200], gt5[201] = gt5[201], gt5[200]
+    out["decreasing_tokens"] = (gt5, gp, ad, al, T, N, None)
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(_bad_large_tables()))
+def test_plan_multi_validation(name):
+    tp, pp, ad, al, T, N, cap = _bad_large_tables()[name]
+    want = O.validate(tp, pp, ad.astype(np.int32), al, T, N, max_tuples=cap)
+    banner(f"multi-workgroup validation {name}: pairs={len(ad)} expect {want}")
+    c = W.Composites(T, N, tp.astype(np.int32), pp.astype(np.int32), ad.astype(np.int32),
+                     al.astype(np.float32))
+    n_tup = int(np.sum(np.diff(tp).clip(0) * np.diff(pp).clip(0)))
+    plan = make_plan(c, max_tuples=cap if cap is not None else max(n_tup, 1))
+    rc, _, _ = plan.status()
+    assert rc == want
+    if rc == 0:
+        assert_plan_equal(plan.copy_out(), oracle_plan(c))
+    else:
+        # a rejected plan turns the apply into a no-op
+        m = W.random_case(2, T=T, N=N, d_in=16, d_out=16, r_max=4, max_pairs=1).modules[0]
+        mod = make_module(m)
+        x = torch.randn(T, 16, device="cuda:0").to(torch.bfloat16)
+        y = torch.randn(T, 16, device="cuda:0")
+        y0 = y.clone()
+        tclora.fused_apply(plan, [mod], [x], [y])
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0)
 
 
 @pytest.mark.parametrize("name", sorted(_bad_tables()))
