@@ -79,8 +79,9 @@ def kernel_bytes(wl) -> dict:
 
 # HIP sources each kernel is built from: a stored counter summary is only
 # valid while these are unchanged
-KERNEL_SOURCES = {"plan_kernel": ("plan.hip", "tcl_internal.hpp"),
-                  "tile_ranges_kernel": ("plan.hip", "tcl_internal.hpp")}
+KERNEL_SOURCES = {k: ("plan.hip", "tcl_internal.hpp")
+                  for k in ("plan_kernel", "tile_ranges_kernel", "plan_m_local", "plan_m_scan",
+                            "plan_m_scatter")}
 APPLY_SOURCES = ("apply.hip", "tcl_internal.hpp")
 
 
@@ -130,7 +131,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None)
             if name.startswith("__amd_rocclr_copyBuffer"):
                 biggest_copy = max(biggest_copy, v)
             for short in ("shrink_mfma", "shrink_valu", "expand_kernel", "expand_staged",
-                          "expand_mfma", "plan_kernel", "tile_ranges_kernel"):
+                          "expand_mfma", "plan_kernel", "tile_ranges_kernel", "plan_m_local",
+                          "plan_m_scan", "plan_m_scatter"):
                 if short in name:
                     per[short].append(v)
         return per, calib / biggest_copy
