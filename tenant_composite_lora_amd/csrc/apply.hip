@@ -19,6 +19,8 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
+#include <vector>
 
 #include "tcl_internal.hpp"
 
@@ -92,9 +94,8 @@ __device__ inline int eff_rank(const int32_t *k_dev, int a, int r_max) {
 // ---------------------------------------------------------------------------
 // multi-module launch tables
 // ---------------------------------------------------------------------------
-// One launch covers up to kMaxMods modules that share the plan (e.g. the
-// seven projections of a transformer layer).
-constexpr int kMaxMods = 8;
+// One launch covers up to kMaxMods modules (tcl_internal.hpp) that share the
+// plan.
 
 struct ModArgs {
   const void *W;          // shrink: A_t, expand: B_t
@@ -328,9 +329,18 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
 struct ExpandArgs {
   const int32_t *tok_n;
   const int4 *tok_rec;  // [T][kSlotPad]
-  int32_t T, n_mods, jobs, jobs_per_xcd;
+  // split launch: per-tile {tuples, segments} (the tiles that the
+  // matrix-core expand takes are skipped here), else NULL
+  const int2 *tcount;
+  int32_t T, n_mods, jobs, jobs_per_xcd, tiles, min_tok;
   ModArgs m[kMaxMods];
 };
+
+// A token tile goes to the matrix cores when the segments that touch it
+// carry at least min_tok of its tuples each on average (the matrix cores
+// work on every token of the tile for every touched adapter's rank rows).
+__device__ inline bool dense_tile(int2 c, int min_tok) { return c.y == 0 || c.x >= min_tok * c.y; }
+
 
 // C consecutive weights of one B row (C = 2, 4 or 8)
 template <typename TW, int C>
@@ -501,12 +511,19 @@ struct OutN<bf16_t, C> {
 // in slot order, rank order within a slot; y is added once at the end.
 // One expand job (token, 64 * CPL outputs of one module) for the calling wave;
 // BR (slot, rank) rows of B are loaded per batch.
-template <int R, int CPL, bool SPLIT, typename TW, typename TY, int BR>
+//
+// TILED: a split launch.  The tile's counts are read with the slot table and
+// the job ends there if the matrix-core expand owns the tile; y is loaded
+// after that check (it is needed only at the end, so the check adds no
+// latency to the jobs that run).
+template <int R, int CPL, bool SPLIT, typename TW, typename TY, int BR, bool TILED = false>
 __device__ inline void expand_job(const ExpandArgs &e, int job) {
   constexpr int RB = R < BR ? R : BR;  // ranks per batch
   constexpr int SB = BR / RB;          // slots per batch
   const int lane = threadIdx.x & 63;
   if (job >= e.jobs) return;
+  int2 tc{0, 0};
+  if constexpr (TILED) tc = e.tcount[(job % e.T) / kXTok];  // module jobs start at multiples of T
   int mi = 0;
 #pragma unroll
   for (int i = 1; i < kMaxMods; ++i)
@@ -525,9 +542,15 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
   const bool active = n0 < d;
   TY *Yp = Y + int64_t(t) * ld + n0;
   OutN<TY, CPL> yv;
-  if (active) yv.load(Yp);
+  if constexpr (!TILED) {
+    if (active) yv.load(Yp);
+  }
   const int ns = e.tok_n[t];
   const int4 rec = e.tok_rec[int64_t(t) * kSlotPad + lane];
+  if constexpr (TILED) {
+    if (dense_tile(tc, e.min_tok)) return;
+    if (active) yv.load(Yp);
+  }
   if (ns <= 0) return;
 
   float acc[CPL];
@@ -614,7 +637,8 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
 }
 
 // W waves (jobs) per workgroup.  XCD-aware job index: workgroups are dealt
-// to the 8 XCDs round-robin, and each XCD owns a contiguous range of jobs.
+// to the 8 XCDs round-robin, and each XCD owns a contiguous range of
+// jobs_per_xcd workgroups' jobs.
 template <int R, int CPL, bool SPLIT, typename TW, typename TY, int W, int BR>
 __global__ __launch_bounds__(64 * W) void expand_kernel(ExpandArgs e) {
   const int blk = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
@@ -622,6 +646,16 @@ __global__ __launch_bounds__(64 * W) void expand_kernel(ExpandArgs e) {
   // from it stays in scalar registers
   const int job = __builtin_amdgcn_readfirstlane(blk * W + int(threadIdx.x >> 6));
   expand_job<R, CPL, SPLIT, TW, TY, BR>(e, job);
+}
+
+// The same jobs in a split launch (e.tcount set: the matrix-core expand has
+// done the dense tiles; bf16 pools): each job is skipped when its token's
+// tile is dense.
+template <int R, int CPL, bool SPLIT, typename TY, int W, int BR>
+__global__ __launch_bounds__(64 * W) void expand_kernel_split(ExpandArgs e) {
+  const int blk = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
+  const int job = __builtin_amdgcn_readfirstlane(blk * W + int(threadIdx.x >> 6));
+  expand_job<R, CPL, SPLIT, bf16_t, TY, BR, true>(e, job);
 }
 
 // ---------------------------------------------------------------------------
@@ -1018,71 +1052,145 @@ __global__ __launch_bounds__(kStThreads) void expand_staged(StagedArgs e) {
 // prefill expand on the matrix cores
 // ---------------------------------------------------------------------------
 // One workgroup owns kXTok tokens x kXCols output columns of one module.  The
-// adapters its tokens use (the union) are concatenated along K, each adapter
-// contributing its retained rank rows in half-steps of 16:
+// adapters that its tokens hold (the tile's union) are concatenated along K,
+// each contributing its retained rank rows in octets of 8:
 //     Y[tokens x cols] += W[tokens x K] . Bcat[K x cols]
-// with W[t][(a, j)] = bf16(alpha_{t,a} z_{t,a}[j]) when token t holds
-// adapter a and 0 otherwise, and Bcat[(a, j)][n] = B_t[a][j][n].  W is built
-// in LDS from the sorted tuples; Bcat is staged through LDS transposed (the
-// MFMA operand wants 8 consecutive K per lane while B_t rows run along n):
-// each thread loads an 8 x 8 block with 16-byte row loads, transposes it in
-// registers with byte permutes and writes 16-byte column vectors, the K octet
-// XOR-swizzled by the column's octet to spread LDS banks.  Stages of 64 K rows
-// are double-buffered and prefetched one stage ahead.  Unions are taken over
-// at most kXSeg segments at a time, in ascending adapter order.
-constexpr int kXCols = 256;   // output columns per tile (16 MFMA column blocks)
-constexpr int kXHalf = 16;    // rank rows per half K-step
-constexpr int kXChunk = 16;   // half K-steps per W chunk (256 K values)
-constexpr int kXSeg = 256;    // segments examined per union pass
-constexpr int kWPad = kXChunk * kXHalf + 8;  // W row stride (bf16)
-constexpr int kBPad = 64 + 8;                // transposed B row stride (bf16)
+// with W[t][(a, j)] = bf16(alpha_{t,a} z_{t,a}[j]) when token t holds adapter
+// a (else 0) and Bcat[(a, j)][n] = B_t[a][j][n].  The matrix cores compute the
+// transposed product D[n][t] = sum_k Bcat[k][n] W[t][k], so each lane of a
+// 16 x 16 output block holds four consecutive columns of one token: y moves
+// as 16-byte vectors, is loaded into the accumulators while the union and the
+// coefficients are set up, and is stored once at the end.
+//
+// Wave w owns columns [64w, 64w + 64) of the tile for all kXTok tokens.  It
+// stages the B rows of exactly those columns, so its staging area in LDS is
+// private and needs no workgroup barrier; only the coefficients W are shared.
+// B rows run along n while the operand wants 8 consecutive K per lane, so a
+// lane loads an 8 x 8 block (8 rank rows x 8 columns, 16-byte loads),
+// transposes it with byte permutes and writes one K octet per column.  Octets
+// are XOR-swizzled by column (B) and by token (W) so that the 16-byte operand
+// reads of 16 consecutive columns or tokens hit distinct banks.  The next
+// stage's rows are loaded into registers while the current stage multiplies.
+//
+// Rank rows at or beyond an adapter's retained rank are never read (zeros go
+// to LDS instead).  A token's coefficient for an adapter it does not hold is
+// an exact zero, so the pools must be finite, as everywhere on this path.
+constexpr int kXCols = 256;     // output columns per tile (4 waves x 64)
+constexpr int kXOct = 8;        // rank rows per K octet
+constexpr int kXStageOct = 8;   // K octets per stage (64 K values)
+constexpr int kXChunkOct = 16;  // K octets of W per chunk (128 K values)
+constexpr int kXSeg = 128;      // segments examined per union window
 
 struct ExpandMfmaArgs {
   const int32_t *status, *seg_adapter, *tup_token, *tok_n;
   const float *tup_alpha;
   const int2 *ranges;  // [tiles][N]
+  const int2 *tcount;  // [tiles]: {tuples, segments with tuples}
   int32_t T, N, tiles, n_mods, jobs, jobs_per_xcd;
+  int32_t min_tok;     // density threshold of dense_tile (0: every tile is taken)
   ModArgs m[kMaxMods];  // first = first job; n_ct = column tiles of kXCols
 };
 
-__device__ inline int block_scan256(int v, int *tmp, int *total) {
+// Exclusive prefix sums of two values over the 256 threads, and their totals.
+__device__ inline void block_scan2(int v0, int v1, int *tmp, int &x0, int &x1, int &s0,
+                                   int &s1) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
+  int i0 = v0, i1 = v1;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += t;
+    const int a0 = __shfl_up(i0, off, 64), a1 = __shfl_up(i1, off, 64);
+    if (lane >= off) {
+      i0 += a0;
+      i1 += a1;
+    }
   }
-  if (lane == 63) tmp[w] = incl;
+  if (lane == 63) {
+    tmp[w] = i0;
+    tmp[4 + w] = i1;
+  }
   __syncthreads();
-  const int t0 = tmp[0], t1 = tmp[1], t2 = tmp[2], t3 = tmp[3];
-  const int before = (w > 0 ? t0 : 0) + (w > 1 ? t1 : 0) + (w > 2 ? t2 : 0);
-  *total = t0 + t1 + t2 + t3;
+  int b0 = 0, b1 = 0;
+  s0 = 0;
+  s1 = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c0 = tmp[j], c1 = tmp[4 + j];
+    if (j < w) {
+      b0 += c0;
+      b1 += c1;
+    }
+    s0 += c0;
+    s1 += c1;
+  }
   __syncthreads();
-  return before + incl - v;
+  x0 = b0 + i0 - v0;
+  x1 = b1 + i1 - v1;
 }
 
-// union entry that owns half-step h: the last i with h0[i] <= h
-__device__ inline int owner_of(const int *h0, int n, int h) {
-  int lo = 0, hi = n - 1;
+// The last i in [lo, hi) with a[i] <= v (a ascending, a[lo] <= v).
+__device__ inline int last_le(const int *a, int lo, int hi, int v) {
+  --hi;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (h0[mid] <= h) lo = mid;
+    if (a[mid] <= v) lo = mid;
     else hi = mid - 1;
   }
   return lo;
 }
 
+// LDS offsets (bf16 elements) of the swizzled operand layouts.
+__device__ inline int bsw_off(int c, int oct) {  // wave's B stage: [64 columns][8 octets]
+  return c * 64 + ((oct ^ ((c ^ (c >> 3)) & 7)) << 3);
+}
+__device__ inline int wsw_off(int t, int oct) {  // coefficients: [kXTok tokens][16 octets]
+  return t * (kXChunkOct * 8) + ((oct ^ (t & 15)) << 3);
+}
+
+// Orders this wave's LDS writes before its later reads (and reads before
+// later writes): a wave's LDS operations execute in program order, so only
+// the compiler has to be kept from moving them.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Four consecutive y values.  Plain (not non-temporal) accesses: measured
+// faster here than the streaming hint.
+template <typename TY>
+__device__ inline f32x4_t load_y4(const TY *p) {
+  if constexpr (sizeof(TY) == 4) {
+    const nt_f4 v = *reinterpret_cast<const nt_f4 *>(p);
+    return f32x4_t{v.x, v.y, v.z, v.w};
+  } else {
+    const nt_u2 v = *reinterpret_cast<const nt_u2 *>(p);
+    return f32x4_t{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+  }
+}
+
+template <typename TY>
+__device__ inline void store_y4(TY *p, f32x4_t v) {
+  if constexpr (sizeof(TY) == 4) {
+    *reinterpret_cast<nt_f4 *>(p) = nt_f4{v[0], v[1], v[2], v[3]};
+  } else {
+    *reinterpret_cast<nt_u2 *>(p) =
+        nt_u2{uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16),
+              uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16)};
+  }
+}
+
 template <typename TY>
 __global__ __launch_bounds__(256) void expand_mfma(ExpandMfmaArgs e) {
-  __shared__ __align__(16) uint16_t Wl[kXTok * kWPad];
-  __shared__ __align__(16) uint16_t Bl[2][kXCols * kBPad];
-  __shared__ int u_a[kXSeg], u_lo[kXSeg], u_hi[kXSeg], u_k[kXSeg], u_h0[kXSeg + 1];
-  __shared__ int tmp[4];
+  __shared__ __align__(16) uint16_t Bl[4][64 * 64];                 // per wave, one stage
+  __shared__ __align__(16) uint16_t Wl[kXTok * kXChunkOct * 8];     // one chunk of W
+  __shared__ int u_a[kXSeg], u_lo[kXSeg], u_k[kXSeg], u_h0[kXSeg + 1], u_q0[kXSeg + 1];
+  __shared__ int o_a[kXChunkOct], o_j0[kXChunkOct], o_k[kXChunkOct];
+  __shared__ int tmp[8];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
-  // XCD-aware job index, as in the decode expand
+  // XCD-aware job index, as in the per-token expand
   const int job = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
-  if (job >= e.jobs) return;
+  if (job >= e.jobs || e.status[ST_CODE] != TCL_OK) return;
+  const int U = e.status[ST_SEGMENTS];
   int mi = 0;
 #pragma unroll
   for (int i = 1; i < kMaxMods; ++i)
@@ -1096,177 +1204,213 @@ __global__ __launch_bounds__(256) void expand_mfma(ExpandMfmaArgs e) {
   TY *Y = static_cast<TY *>(e.m[mi].io);
   const int local = job - first;
   const int ct = local / e.tiles, tile = local - ct * e.tiles;
-  const int t0 = tile * kXTok, n0 = ct * kXCols;
-  const int U = e.status[ST_SEGMENTS];
+  const int t0 = tile * kXTok, cw = ct * kXCols + 64 * w;  // first column of this wave
+  uint16_t *bw = Bl[w];
+  // B stage block of this lane: K octet kb, column octet cb of the wave's 64
+  const int kb = lane & 7, cb = lane >> 3;
 
-  f32x4_t acc[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // B stage block of this thread: K octet kb (8 of 64 rows), column octet cb
-  const int kb = tid & 7, cb = tid >> 3;
-
-  for (int ub = 0; ub < U; ub += kXSeg) {
-    // ---- union of this tile over segments [ub, ub + kXSeg)
-    const int u = ub + tid;
-    int lo = 0, hi = 0, a = 0, k = 0, hs = 0;
-    if (u < U) {
-      const int2 rg = e.ranges[int64_t(tile) * e.N + u];
-      lo = rg.x;
-      hi = rg.y;
-      a = e.seg_adapter[u];
-      k = eff_rank(k_dev, a, r_max);
-      if (hi > lo && k > 0) hs = (k + kXHalf - 1) / kXHalf;
+  // segment ub + tid of a union window: its tuples in the tile and rank
+  int lo = 0, nt = 0, a = 0, k = 0;
+  auto load_seg = [&](int ub) {
+    lo = nt = a = k = 0;
+    if (tid < kXSeg && ub + tid < U) {
+      const int2 rg = e.ranges[int64_t(tile) * e.N + ub + tid];
+      a = e.seg_adapter[ub + tid];
+      if (rg.y > rg.x) {
+        k = eff_rank(k_dev, a, r_max);
+        lo = rg.x;
+        nt = k > 0 ? rg.y - rg.x : 0;
+      }
     }
-    int n_union, H;
-    const int pos = block_scan256(hs > 0 ? 1 : 0, tmp, &n_union);
-    const int h0 = block_scan256(hs, tmp, &H);
-    if (hs > 0) {
-      u_a[pos] = a;
-      u_lo[pos] = lo;
-      u_hi[pos] = hi;
-      u_k[pos] = k;
-      u_h0[pos] = h0;
-    }
-    __syncthreads();
+  };
 
-    for (int hc0 = 0; hc0 < H; hc0 += kXChunk) {
-      const int nh = min(kXChunk, H - hc0);
-      // ---- W chunk: zero, then alpha * z of every tuple of the chunk
-      {
-        uint4 *W4 = reinterpret_cast<uint4 *>(Wl);
-        for (int i = tid; i < kXTok * kWPad / 8; i += 256) W4[i] = make_uint4(0, 0, 0, 0);
-      }
-      __syncthreads();
-      for (int it = tid; it < nh * kXTok; it += 256) {
-        const int hc = it / kXTok, slot = it - hc * kXTok;
-        const int h = hc0 + hc;
-        const int i = owner_of(u_h0, n_union, h);
-        const int p = u_lo[i] + slot;
-        if (p >= u_hi[i]) continue;
-        const int trow = e.tup_token[p] - t0;
-        const float al = e.tup_alpha[p];
-        const int j0 = (h - u_h0[i]) * kXHalf;
-        const int kk = u_k[i];
-        float zv[kXHalf];
-#pragma unroll
-        for (int q = 0; q < kXHalf; ++q) zv[q] = 0.f;
-        for (int c = 0; c < nkc; ++c) {
-          const float *zr = Z + int64_t(p) * zstride + c * zld + j0;
-          if ((zld & 3) == 0) {
-#pragma unroll
-            for (int q = 0; q < kXHalf / 4; ++q) {
-              if (j0 + 4 * q < kk) {
-                const float4 v = reinterpret_cast<const float4 *>(zr)[q];
-                zv[4 * q] += v.x;
-                zv[4 * q + 1] += v.y;
-                zv[4 * q + 2] += v.z;
-                zv[4 * q + 3] += v.w;
-              }
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < kXHalf; ++q)
-              if (j0 + q < kk) zv[q] += zr[q];
-          }
-        }
-        uint32_t pk[kXHalf / 2];
-#pragma unroll
-        for (int q = 0; q < kXHalf / 2; ++q) {
-          const float v0 = j0 + 2 * q < kk ? al * zv[2 * q] : 0.f;
-          const float v1 = j0 + 2 * q + 1 < kk ? al * zv[2 * q + 1] : 0.f;
-          pk[q] = uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16);
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(Wl + trow * kWPad + hc * kXHalf);
-        dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-      }
-      __syncthreads();
+  {
+    // sparse tiles are the per-token expand's; empty ones need nothing
+    const int2 tc = e.tcount[tile];
+    if (!dense_tile(tc, e.min_tok) || tc.y == 0 || U <= 0) return;
+  }
 
-      // ---- K loop: stages of 64 K rows (4 half-steps), double-buffered
-      const int nst = (nh + 3) / 4;
-      uint4 pre[8];
-      auto load_stage = [&](int st) {
-        const int hc = 4 * st + (kb >> 1);
-        int jr = -1, aa = 0, kk = 0;
-        if (hc < nh) {
-          const int h = hc0 + hc;
-          const int i = owner_of(u_h0, n_union, h);
-          jr = (h - u_h0[i]) * kXHalf + (kb & 1) * 8;
-          aa = u_a[i];
-          kk = u_k[i];
-        }
-        const int n = n0 + cb * 8;
-        const bool col_ok = n < d;
+  // y -> accumulators: token t0 + 16 tb + r16, columns cw + 16 nb + 4 kg .. + 4
+  f32x4_t acc[4][4];  // [column block][token block]
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          pre[r] = make_uint4(0, 0, 0, 0);
-          if (col_ok && jr >= 0 && jr + r < kk)
-            pre[r] = *reinterpret_cast<const uint4 *>(Bw + (int64_t(aa) * r_max + jr + r) * d + n);
-        }
-      };
-      auto store_stage = [&](int buf) {
-        // 8 x 8 transpose: column c of the block gets K rows 0..7
-        const uint32_t *rw = reinterpret_cast<const uint32_t *>(pre);  // rw[4*r + dword]
-        uint16_t *bt = Bl[buf];
-        const int slotk = (kb ^ (cb & 7)) * 8;
+  for (int tb = 0; tb < 4; ++tb) {
+    const int t = t0 + 16 * tb + r16;
 #pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-          uint32_t lo[4], hi[4];
-#pragma unroll
-          for (int rp = 0; rp < 4; ++rp) {
-            const uint32_t x = rw[4 * (2 * rp) + dw], y = rw[4 * (2 * rp + 1) + dw];
-            lo[rp] = __builtin_amdgcn_perm(y, x, 0x05040100u);  // rows 2rp, 2rp+1 of column 2dw
-            hi[rp] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // rows 2rp, 2rp+1 of column 2dw+1
-          }
-          const int c0 = cb * 8 + 2 * dw;
-          *reinterpret_cast<uint4 *>(bt + c0 * kBPad + slotk) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-          *reinterpret_cast<uint4 *>(bt + (c0 + 1) * kBPad + slotk) =
-              make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        }
-      };
-      load_stage(0);
-      for (int st = 0; st < nst; ++st) {
-        store_stage(st & 1);
-        __syncthreads();
-        if (st + 1 < nst) load_stage(st + 1);
-        const uint16_t *bt = Bl[st & 1];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(
-              Wl + (16 * w + r16) * kWPad + 64 * st + 32 * ks + 8 * kg);
-          const int oct = ks * 4 + kg;
-#pragma unroll
-          for (int cbk = 0; cbk < 16; ++cbk) {
-            const int c = cbk * 16 + r16;
-            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(
-                bt + c * kBPad + ((oct ^ ((c >> 3) & 7)) * 8));
-            acc[cbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[cbk], 0, 0, 0);
-          }
-        }
-      }
-      __syncthreads();
+    for (int nb = 0; nb < 4; ++nb) {
+      const int col = cw + 16 * nb + 4 * kg;
+      acc[nb][tb] = (t < e.T && col < d) ? load_y4(Y + int64_t(t) * ld + col)
+                                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
 
-  // ---- y += acc for tokens that hold at least one pair
+  for (int ub = 0; ub < U; ub += kXSeg) {
+    // ---- union of the tile over segments [ub, ub + kXSeg)
+    load_seg(ub);
+    const int oc = (k + kXOct - 1) / kXOct;
+    int pos, q0, tot, Q;
+    block_scan2(oc > 0 ? 1 + (oc << 16) : 0, nt, tmp, pos, q0, tot, Q);
+    const int n_union = tot & 0xffff, H = tot >> 16;
+    if (oc > 0) {
+      const int i = pos & 0xffff;
+      u_a[i] = a;
+      u_lo[i] = lo;
+      u_k[i] = k;
+      u_h0[i] = pos >> 16;
+      u_q0[i] = q0;
+    }
+    if (tid == 0) {
+      u_h0[n_union] = H;
+      u_q0[n_union] = Q;
+    }
+    __syncthreads();
+
+    for (int c0 = 0; c0 < H; c0 += kXChunkOct) {
+      const int nh = min(kXChunkOct, H - c0);
+      // ---- octet table of the chunk; W cleared
+      if (tid < nh) {
+        const int h = c0 + tid;
+        const int i = last_le(u_h0, 0, n_union, h);
+        o_a[tid] = u_a[i];
+        o_j0[tid] = (h - u_h0[i]) * kXOct;
+        o_k[tid] = u_k[i];
+      }
+      {
+        uint4 *W4 = reinterpret_cast<uint4 *>(Wl);
+        for (int i = tid; i < kXTok * kXChunkOct; i += 256) W4[i] = make_uint4(0, 0, 0, 0);
+      }
+      __syncthreads();
+
+      // ---- B rows of a stage (8 octets x the wave's 64 columns) into registers
+      uint4 pre[8];
+      auto load_stage = [&](int st) {
+        const int oi = st * kXStageOct + kb;
+        int j0 = 0, kk = 0, aa = 0;
+        if (oi < nh) {
+          aa = o_a[oi];
+          j0 = o_j0[oi];
+          kk = o_k[oi];
+        }
+        const int n = cw + 8 * cb;
+        if (n >= d) kk = 0;
+        const uint16_t *src = Bw + (int64_t(aa) * r_max + j0) * d + n;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + 16 * w + 4 * kg + i;
-    if (t >= e.T || e.tok_n[t] <= 0) continue;
-    TY *yr = Y + int64_t(t) * ld;
+        for (int r = 0; r < 8; ++r)
+          pre[r] = j0 + r < kk ? *reinterpret_cast<const uint4 *>(src + int64_t(r) * d)
+                               : make_uint4(0, 0, 0, 0);
+      };
+      load_stage(0);
+
+      // ---- coefficients: alpha * z of every tuple of the entries that own
+      // octets of this chunk, in bf16, at (token row, octet)
+      {
+        const int c1 = c0 + nh;
+        const int i_lo = last_le(u_h0, 0, n_union, c0);
+        const int i_hi = last_le(u_h0, 0, n_union, c1 - 1) + 1;
+        const int q_end = u_q0[i_hi];
+        for (int q = u_q0[i_lo] + tid; q < q_end; q += 256) {
+          const int i = last_le(u_q0, i_lo, i_hi, q);
+          const int p = u_lo[i] + (q - u_q0[i]);
+          const int trow = e.tup_token[p] - t0;
+          const float al = e.tup_alpha[p];
+          const int kk = u_k[i], h0 = u_h0[i];
+          const int ob = max(h0, c0), oe = min(u_h0[i + 1], c1);
+          for (int o = ob; o < oe; ++o) {
+            const int j0 = (o - h0) * kXOct;
+            float zv[8];
 #pragma unroll
-    for (int cbk = 0; cbk < 16; ++cbk) {
-      const int n = n0 + cbk * 16 + r16;
-      if (n < d) {
-        if constexpr (sizeof(TY) == 4) {
-          reinterpret_cast<float *>(yr)[n] += acc[cbk][i];
-        } else {
-          uint16_t *yb = reinterpret_cast<uint16_t *>(yr);
-          const float v = __uint_as_float(uint32_t(yb[n]) << 16) + acc[cbk][i];
-          yb[n] = f32_to_bf16(v);
+            for (int q2 = 0; q2 < 8; ++q2) zv[q2] = 0.f;
+            for (int c = 0; c < nkc; ++c) {
+              const float *zr = Z + int64_t(p) * zstride + c * zld + j0;
+              if ((zld & 3) == 0) {
+                // j0 < kk always; the second vector lies inside the row when used
+                const float4 v0 = *reinterpret_cast<const float4 *>(zr);
+                zv[0] += v0.x;
+                zv[1] += v0.y;
+                zv[2] += v0.z;
+                zv[3] += v0.w;
+                if (j0 + 4 < kk) {
+                  const float4 v1 = *reinterpret_cast<const float4 *>(zr + 4);
+                  zv[4] += v1.x;
+                  zv[5] += v1.y;
+                  zv[6] += v1.z;
+                  zv[7] += v1.w;
+                }
+              } else {
+#pragma unroll
+                for (int q2 = 0; q2 < 8; ++q2)
+                  if (j0 + q2 < kk) zv[q2] += zr[q2];
+              }
+            }
+            uint32_t pk[4];
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+              const float v0 = j0 + 2 * q2 < kk ? al * zv[2 * q2] : 0.f;
+              const float v1 = j0 + 2 * q2 + 1 < kk ? al * zv[2 * q2 + 1] : 0.f;
+              pk[q2] = uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16);
+            }
+            *reinterpret_cast<uint4 *>(Wl + wsw_off(trow, o - c0)) =
+                make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          }
         }
       }
+      __syncthreads();
+
+      // ---- stages of 64 K: transpose into the wave's LDS area, multiply
+      const int nst = (nh + kXStageOct - 1) / kXStageOct;
+      for (int st = 0; st < nst; ++st) {
+        {
+          // 8 x 8 transpose: column cc of the block gets rank rows 0..7
+          const uint32_t *rw = reinterpret_cast<const uint32_t *>(pre);  // rw[4 * row + dword]
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+            uint32_t lo4[4], hi4[4];
+#pragma unroll
+            for (int rp = 0; rp < 4; ++rp) {
+              const uint32_t x = rw[4 * (2 * rp) + dw], y = rw[4 * (2 * rp + 1) + dw];
+              lo4[rp] = __builtin_amdgcn_perm(y, x, 0x05040100u);  // column 2 dw
+              hi4[rp] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // column 2 dw + 1
+            }
+            const int c = 8 * cb + 2 * dw;
+            *reinterpret_cast<uint4 *>(bw + bsw_off(c, kb)) = make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]);
+            *reinterpret_cast<uint4 *>(bw + bsw_off(c + 1, kb)) =
+                make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]);
+          }
+        }
+        wave_lds_sync();
+        if (st + 1 < nst) load_stage(st + 1);
+        const int left = nh - st * kXStageOct;  // octets of this stage that exist (> 0)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks == 1 && left <= 4) break;
+          bf16x8_t av[4], bv[4];
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            av[nb] = *reinterpret_cast<const bf16x8_t *>(bw + bsw_off(16 * nb + r16, 4 * ks + kg));
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+            bv[tb] = *reinterpret_cast<const bf16x8_t *>(
+                Wl + wsw_off(16 * tb + r16, st * kXStageOct + 4 * ks + kg));
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+              acc[nb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nb], bv[tb], acc[nb][tb], 0, 0, 0);
+        }
+        wave_lds_sync();
+      }
+      __syncthreads();  // W and the octet table are rewritten by the next chunk
+    }
+  }
+
+  // ---- y = accumulators, for tokens that hold at least one pair
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int t = t0 + 16 * tb + r16;
+    if (t >= e.T || e.tok_n[t] <= 0) continue;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int col = cw + 16 * nb + 4 * kg;
+      if (col < d) store_y4(Y + int64_t(t) * ld + col, acc[nb][tb]);
     }
   }
 }
@@ -1426,24 +1570,34 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
   return TCL_OK;
 }
 
-template <int R, int CPL, bool SPLIT, typename TW, typename TY>
-static void launch_expand_w(ExpandArgs e, int waves, hipStream_t s) {
-  // e.jobs_per_xcd counts workgroups per XCD here
-  const int64_t blocks = (int64_t(e.jobs) + waves - 1) / waves;
+// Launch of kernel k with W waves per workgroup; e.jobs_per_xcd becomes the
+// number of workgroups per XCD.
+template <int W, typename K>
+static void launch_expand_k(K k, ExpandArgs e, hipStream_t s) {
+  const int64_t blocks = (int64_t(e.jobs) + W - 1) / W;
   e.jobs_per_xcd = int32_t((blocks + 7) / 8);
-  const int grid = 8 * e.jobs_per_xcd;
+  hipLaunchKernelGGL(k, dim3(8 * e.jobs_per_xcd), dim3(64 * W), 0, s, e);
+}
+
+template <int R, int CPL, bool SPLIT, typename TW, typename TY>
+static void launch_expand_w(const ExpandArgs &e, int waves, hipStream_t s) {
   // rows of B per load batch: 16 when a lane holds 8 outputs (fewer VGPRs,
   // more waves per SIMD), else 32; TCL_EBATCH=16/32 forces
   const int ebf = env_int("TCL_EBATCH", 0);
   const int br = ebf == 16 || ebf == 32 ? ebf : (CPL == 8 ? 16 : 32);
-  if (waves == 4 && br == 16)
-    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 4, 16>), dim3(grid), dim3(256), 0, s, e);
-  else if (waves == 4)
-    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 4, 32>), dim3(grid), dim3(256), 0, s, e);
-  else if (br == 16)
-    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 1, 16>), dim3(grid), dim3(64), 0, s, e);
-  else
-    hipLaunchKernelGGL((expand_kernel<R, CPL, SPLIT, TW, TY, 1, 32>), dim3(grid), dim3(64), 0, s, e);
+  if constexpr (std::is_same<TW, bf16_t>::value) {
+    if (e.tcount) {  // split launch: B batches follow CPL only
+      if (waves == 4 && CPL == 8) launch_expand_k<4>(expand_kernel_split<R, CPL, SPLIT, TY, 4, 16>, e, s);
+      else if (waves == 4) launch_expand_k<4>(expand_kernel_split<R, CPL, SPLIT, TY, 4, 32>, e, s);
+      else if (CPL == 8) launch_expand_k<1>(expand_kernel_split<R, CPL, SPLIT, TY, 1, 16>, e, s);
+      else launch_expand_k<1>(expand_kernel_split<R, CPL, SPLIT, TY, 1, 32>, e, s);
+      return;
+    }
+  }
+  if (waves == 4 && br == 16) launch_expand_k<4>(expand_kernel<R, CPL, SPLIT, TW, TY, 4, 16>, e, s);
+  else if (waves == 4) launch_expand_k<4>(expand_kernel<R, CPL, SPLIT, TW, TY, 4, 32>, e, s);
+  else if (br == 16) launch_expand_k<1>(expand_kernel<R, CPL, SPLIT, TW, TY, 1, 16>, e, s);
+  else launch_expand_k<1>(expand_kernel<R, CPL, SPLIT, TW, TY, 1, 32>, e, s);
 }
 
 template <int R, bool SPLIT, typename TW, typename TY>
@@ -1453,10 +1607,16 @@ static void launch_expand_t(const ExpandArgs &e, int cpl, int waves, hipStream_t
   else launch_expand_w<R, 2, SPLIT, TW, TY>(e, waves, s);
 }
 
-// Which expand runs: the per-token VALU kernel by default; the matrix-core
-// tile kernel when TCL_DISPATCH=mfma and the batch is prefill-sized bf16 (the
-// plan prepared tile ranges).  The tile kernel is correct but not yet faster
-// on the measured prefill batches, so it is opt-in.
+// Which expand runs.  Batches of bf16 pools with token tiles (prefill-sized;
+// the plan prepares tile ranges and per-tile counts) go to the matrix-core
+// kernel first.  It takes the dense tiles: those whose touched segments hold
+// at least kMfmaMinTok of the tile's tuples each on average (TCL_MFMA_MIN_TOK
+// overrides).  The per-token kernel then runs as a split launch over the
+// other tiles.  Other batches run the per-token kernel alone.
+// TCL_DISPATCH=valu forces the per-token kernel, =mfma the matrix-core kernel
+// for every tile, =staged the staged kernel.
+constexpr int kMfmaMinTok = 8;
+
 static int dispatch_override() {
   const char *s = std::getenv("TCL_DISPATCH");
   if (!s) return 0;
@@ -1492,7 +1652,8 @@ static void launch_staged_r(const StagedArgs &e, int cpl, int grid, size_t lds, 
 
 static bool use_mfma_expand(const tcl_plan *p, const tcl_module *mods) {
   if (mods[0].wdtype != TCL_BF16 || p->L.tiles == 0) return false;
-  return dispatch_override() == 2;
+  const int o = dispatch_override();
+  return o == 0 || o == 2;
 }
 
 template <typename TY>
@@ -1505,6 +1666,123 @@ static int expand_args(const tcl_plan *p, const tcl_module *mods, int n, float *
                        const int *zld, int kchunk, void *const *y, const int64_t *ldy,
                        ExpandArgs &e, int &cpl, int &R, bool &split, int cpl_min = 2);
 
+// The matrix-core expand over the tiles that dense_tile() gives it
+// (min_tok 0: every tile).
+static int launch_expand_mfma(const tcl_plan *p, const tcl_module *mods, int n,
+                              float *const *z, const int *zld, int kchunk, void *const *y,
+                              const int64_t *ldy, tcl_dtype yd, int min_tok, hipStream_t s) {
+  const bool bfw = mods[0].wdtype == TCL_BF16;
+  ExpandMfmaArgs e{};
+  e.status = p->d.status;
+  e.seg_adapter = p->d.seg_adapter;
+  e.tup_token = p->d.tup_token;
+  e.tok_n = p->d.tok_n;
+  e.tup_alpha = p->d.tup_alpha;
+  e.ranges = p->d.ranges;
+  e.tcount = p->d.tcount;
+  e.min_tok = min_tok;
+  e.T = p->L.T;
+  e.N = p->L.N;
+  e.tiles = p->L.tiles;
+  e.n_mods = n;
+  int64_t jobs = 0;
+  for (int i = 0; i < n; ++i) {
+    ModArgs &M = e.m[i];
+    M.W = mods[i].B_t;
+    M.io = y[i];
+    M.k_dev = mods[i].k_dev;
+    M.z = z[i];
+    M.zld = zld[i];
+    M.ld = ldy[i];
+    M.d = mods[i].d_out;
+    M.r_max = mods[i].r_max;
+    M.n_ct = (mods[i].d_out + kXCols - 1) / kXCols;
+    M.nkc = bfw ? n_kchunks(&mods[i], kchunk) : 1;
+    M.zstride = M.nkc * zld[i];
+    M.first = int32_t(jobs);
+    jobs += int64_t(M.n_ct) * p->L.tiles;
+  }
+  if (jobs > (int64_t(1) << 30)) return fail(TCL_EUNSUPPORTED, "expand grid too large");
+  e.jobs = int32_t(jobs);
+  e.jobs_per_xcd = int32_t((jobs + 7) / 8);
+  const int grid = 8 * e.jobs_per_xcd;
+  logf("expand(mfma): modules=%d tiles=%d jobs=%lld min_tok=%d", n, p->L.tiles,
+       (long long)jobs, e.min_tok);
+  if (yd == TCL_BF16) launch_expand_mfma_t<bf16_t>(e, grid, s);
+  else launch_expand_mfma_t<float>(e, grid, s);
+  TCL_HIP(hipGetLastError());
+  return TCL_OK;
+}
+
+// The per-token expand: every token, or (tcount set) those of the tiles
+// that dense_tile() leaves to it.
+static int launch_expand_valu(const tcl_plan *p, const tcl_module *mods, int n,
+                              float *const *z, const int *zld, int kchunk, void *const *y,
+                              const int64_t *ldy, tcl_dtype yd, const int2 *tcount,
+                              int min_tok, hipStream_t s) {
+  ExpandArgs e;
+  int cpl, R;
+  bool split;
+  int rc = expand_args(p, mods, n, z, zld, kchunk, y, ldy, e, cpl, R, split);
+  if (rc) return rc;
+  e.tcount = tcount;
+  e.tiles = p->L.tiles;
+  e.min_tok = min_tok;
+  // jobs per workgroup: four for prefill-sized launches of ranks up to 16
+  // (measured faster there: sparse prefill 148 -> 141 us), one otherwise (four
+  // measured slower for rank 32: retained-rank batch 870 -> 1001 us);
+  // TCL_EWAVES=1/4 forces
+  const int ew = env_int("TCL_EWAVES", 0);
+  const int waves = ew == 1 || ew == 4 ? ew : (e.jobs >= 32768 && R <= 16 ? 4 : 1);
+  logf("expand(valu): modules=%d R=%d cpl=%d jobs=%d waves/workgroup=%d", n, R, cpl, e.jobs,
+       waves);
+  const bool bf = mods[0].wdtype == TCL_BF16;
+  const bool ybf = yd == TCL_BF16;
+#define TCL_EXPAND_CASE(RR)                                                                    \
+  case RR:                                                                                     \
+    if (bf && ybf && split) launch_expand_t<RR, true, bf16_t, bf16_t>(e, cpl, waves, s);       \
+    else if (bf && ybf) launch_expand_t<RR, false, bf16_t, bf16_t>(e, cpl, waves, s);          \
+    else if (bf && split) launch_expand_t<RR, true, bf16_t, float>(e, cpl, waves, s);          \
+    else if (bf) launch_expand_t<RR, false, bf16_t, float>(e, cpl, waves, s);                  \
+    else launch_expand_t<RR, false, float, float>(e, cpl, waves, s);                           \
+    break;
+  switch (R) {
+    TCL_EXPAND_CASE(8)
+    TCL_EXPAND_CASE(16)
+    TCL_EXPAND_CASE(32)
+    TCL_EXPAND_CASE(64)
+  }
+#undef TCL_EXPAND_CASE
+  TCL_HIP(hipGetLastError());
+  return TCL_OK;
+}
+
+// A second stream per (host thread, device).  The two halves of a split
+// expand run on the caller's stream and on this one at the same time (the
+// per-token half's early exits on dense tiles then cost nothing); it forks
+// from and joins the caller's stream through events, so work queued on the
+// caller's stream later still runs after both, and a graph captured from the
+// caller's stream holds both.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+static int side_stream(SideStream *&out) {
+  thread_local std::vector<SideStream> tab;
+  int dev = 0;
+  TCL_HIP(hipGetDevice(&dev));
+  if (int(tab.size()) <= dev) tab.resize(size_t(dev) + 1);
+  SideStream &ss = tab[size_t(dev)];
+  if (!ss.s) {
+    TCL_HIP(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
+    TCL_HIP(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
+    TCL_HIP(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
+  }
+  out = &ss;
+  return TCL_OK;
+}
+
 static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
                          float *const *z, const int *zld, int kchunk, void *const *y,
                          const int64_t *ldy, tcl_dtype yd, hipStream_t s) {
@@ -1513,43 +1791,20 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
   if (use_mfma_expand(p, mods)) {
     int rc = plan_prepare_ranges(p, s);
     if (rc) return rc;
-    ExpandMfmaArgs e{};
-    e.status = p->d.status;
-    e.seg_adapter = p->d.seg_adapter;
-    e.tup_token = p->d.tup_token;
-    e.tok_n = p->d.tok_n;
-    e.tup_alpha = p->d.tup_alpha;
-    e.ranges = p->d.ranges;
-    e.T = p->L.T;
-    e.N = p->L.N;
-    e.tiles = p->L.tiles;
-    e.n_mods = n;
-    int64_t jobs = 0;
-    for (int i = 0; i < n; ++i) {
-      ModArgs &M = e.m[i];
-      M.W = mods[i].B_t;
-      M.io = y[i];
-      M.k_dev = mods[i].k_dev;
-      M.z = z[i];
-      M.zld = zld[i];
-      M.ld = ldy[i];
-      M.d = mods[i].d_out;
-      M.r_max = mods[i].r_max;
-      M.n_ct = (mods[i].d_out + kXCols - 1) / kXCols;
-      M.nkc = bfw ? n_kchunks(&mods[i], kchunk) : 1;
-      M.zstride = M.nkc * zld[i];
-      M.first = int32_t(jobs);
-      jobs += int64_t(M.n_ct) * p->L.tiles;
-    }
-    if (jobs > (int64_t(1) << 30)) return fail(TCL_EUNSUPPORTED, "expand grid too large");
-    e.jobs = int32_t(jobs);
-    e.jobs_per_xcd = int32_t((jobs + 7) / 8);
-    const int grid = 8 * e.jobs_per_xcd;
-    logf("expand(mfma): modules=%d tiles=%d jobs=%lld", n, p->L.tiles, (long long)jobs);
-    if (yd == TCL_BF16) launch_expand_mfma_t<bf16_t>(e, grid, s);
-    else launch_expand_mfma_t<float>(e, grid, s);
-    TCL_HIP(hipGetLastError());
-    return TCL_OK;
+    if (dispatch_override() == 2)
+      return launch_expand_mfma(p, mods, n, z, zld, kchunk, y, ldy, yd, 0, s);
+    const int min_tok = env_int("TCL_MFMA_MIN_TOK", kMfmaMinTok);
+    SideStream *ss = nullptr;
+    rc = side_stream(ss);
+    if (rc) return rc;
+    TCL_HIP(hipEventRecord(ss->fork, s));
+    TCL_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
+    const int rc1 = launch_expand_mfma(p, mods, n, z, zld, kchunk, y, ldy, yd, min_tok, s);
+    const int rc2 =
+        launch_expand_valu(p, mods, n, z, zld, kchunk, y, ldy, yd, p->d.tcount, min_tok, ss->s);
+    TCL_HIP(hipEventRecord(ss->join, ss->s));
+    TCL_HIP(hipStreamWaitEvent(s, ss->join, 0));
+    return rc1 ? rc1 : rc2;
   }
   if (use_staged_expand(p, mods)) {
     StagedArgs e{};
@@ -1617,38 +1872,7 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
     TCL_HIP(hipGetLastError());
     return TCL_OK;
   }
-  ExpandArgs e;
-  int cpl, R;
-  bool split;
-  int rc = expand_args(p, mods, n, z, zld, kchunk, y, ldy, e, cpl, R, split);
-  if (rc) return rc;
-  // jobs per workgroup: four for prefill-sized launches of ranks up to 16
-  // (measured faster there: sparse prefill 148 -> 141 us), one otherwise (four
-  // measured slower for rank 32: retained-rank batch 870 -> 1001 us);
-  // TCL_EWAVES=1/4 forces
-  const int ew = env_int("TCL_EWAVES", 0);
-  const int waves = ew == 1 || ew == 4 ? ew : (e.jobs >= 32768 && R <= 16 ? 4 : 1);
-  logf("expand(valu): modules=%d R=%d cpl=%d jobs=%d waves/workgroup=%d", n, R, cpl, e.jobs,
-       waves);
-  const bool bf = mods[0].wdtype == TCL_BF16;
-  const bool ybf = yd == TCL_BF16;
-#define TCL_EXPAND_CASE(RR)                                                                    \
-  case RR:                                                                                     \
-    if (bf && ybf && split) launch_expand_t<RR, true, bf16_t, bf16_t>(e, cpl, waves, s);       \
-    else if (bf && ybf) launch_expand_t<RR, false, bf16_t, bf16_t>(e, cpl, waves, s);          \
-    else if (bf && split) launch_expand_t<RR, true, bf16_t, float>(e, cpl, waves, s);          \
-    else if (bf) launch_expand_t<RR, false, bf16_t, float>(e, cpl, waves, s);                  \
-    else launch_expand_t<RR, false, float, float>(e, cpl, waves, s);                           \
-    break;
-  switch (R) {
-    TCL_EXPAND_CASE(8)
-    TCL_EXPAND_CASE(16)
-    TCL_EXPAND_CASE(32)
-    TCL_EXPAND_CASE(64)
-  }
-#undef TCL_EXPAND_CASE
-  TCL_HIP(hipGetLastError());
-  return TCL_OK;
+  return launch_expand_valu(p, mods, n, z, zld, kchunk, y, ldy, yd, nullptr, 0, s);
 }
 
 // Launch table of the per-token expand of n (<= kMaxMods) modules: outputs

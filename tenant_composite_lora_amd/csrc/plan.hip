@@ -165,6 +165,7 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.o_msib = take(multi ? size_t(N) * 4 : 4);
   l.tiles = T >= kMfmaMinTokens ? (T + kXTok - 1) / kXTok : 0;
   l.o_ranges = take(size_t(l.tiles) * size_t(N) * 8);
+  l.o_tcount = take(size_t(l.tiles) * 8);
   l.total = o;
   *L = l;
   return TCL_OK;
@@ -692,29 +693,51 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs A) {
   if (tid == 0) A.d.status[ST_CODE] = TCL_OK;
 }
 
-// For every (token tile of kXTok tokens, segment): the run of the segment's
-// tuples whose token falls in the tile.  Tuples of a segment are in token
-// order, so two binary searches find it.  Used by the prefill expand.
-__global__ __launch_bounds__(256) void tile_ranges_kernel(PlanDev d, int32_t N, int32_t tiles) {
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= int64_t(tiles) * N) return;
-  const int tile = int(idx / N), u = int(idx - int64_t(tile) * N);
-  if (d.status[ST_CODE] != TCL_OK || u >= d.status[ST_SEGMENTS]) return;
-  const int beg = d.seg_begin[u], end = d.seg_begin[u + 1];
-  const int t0 = tile * kXTok, t1 = t0 + kXTok;
-  int lo = beg, hi = end;
-  while (lo < hi) {  // first tuple with token >= t0
-    const int mid = (lo + hi) >> 1;
-    if (d.tup_token[mid] < t0) lo = mid + 1;
-    else hi = mid;
+// One workgroup per token tile of kXTok tokens: for every segment, the run
+// of its tuples whose token falls in the tile (tuples of a segment are in
+// token order, so two binary searches find it), and the tile's totals
+// {tuples, segments with tuples}.  Used by the prefill expand: the totals
+// decide whether the tile goes to the matrix cores.
+__global__ __launch_bounds__(256) void tile_ranges_kernel(PlanDev d, int32_t N) {
+  __shared__ int red[8];
+  const int tile = blockIdx.x, tid = threadIdx.x;
+  int tup = 0, nseg = 0;
+  if (d.status[ST_CODE] == TCL_OK) {
+    const int U = d.status[ST_SEGMENTS];
+    const int t0 = tile * kXTok, t1 = t0 + kXTok;
+    for (int u = tid; u < U; u += 256) {
+      const int beg = d.seg_begin[u], end = d.seg_begin[u + 1];
+      int lo = beg, hi = end;
+      while (lo < hi) {  // first tuple with token >= t0
+        const int mid = (lo + hi) >> 1;
+        if (d.tup_token[mid] < t0) lo = mid + 1;
+        else hi = mid;
+      }
+      int lo2 = lo, hi2 = end;
+      while (lo2 < hi2) {  // first tuple with token >= t1
+        const int mid = (lo2 + hi2) >> 1;
+        if (d.tup_token[mid] < t1) lo2 = mid + 1;
+        else hi2 = mid;
+      }
+      d.ranges[int64_t(tile) * N + u] = make_int2(lo, lo2);
+      if (lo2 > lo) {
+        tup += lo2 - lo;
+        ++nseg;
+      }
+    }
   }
-  int lo2 = lo, hi2 = end;
-  while (lo2 < hi2) {  // first tuple with token >= t1
-    const int mid = (lo2 + hi2) >> 1;
-    if (d.tup_token[mid] < t1) lo2 = mid + 1;
-    else hi2 = mid;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    tup += __shfl_xor(tup, off, 64);
+    nseg += __shfl_xor(nseg, off, 64);
   }
-  d.ranges[idx] = make_int2(lo, lo2);
+  if ((tid & 63) == 0) {
+    red[tid >> 6] = tup;
+    red[4 + (tid >> 6)] = nseg;
+  }
+  __syncthreads();
+  if (tid == 0)
+    d.tcount[tile] = make_int2(red[0] + red[1] + red[2] + red[3], red[4] + red[5] + red[6] + red[7]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1113,6 +1136,7 @@ static void bind(tcl_plan *p) {
   d.m_sst = reinterpret_cast<int32_t *>(b + L.o_msst);
   d.m_sib = reinterpret_cast<int32_t *>(b + L.o_msib);
   d.ranges = reinterpret_cast<int2 *>(b + L.o_ranges);
+  d.tcount = reinterpret_cast<int2 *>(b + L.o_tcount);
 }
 
 static int check_composites(const tcl_composites *c) {
@@ -1163,9 +1187,7 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
 
 int plan_prepare_ranges(const tcl_plan *p, hipStream_t s) {
   if (p->ranges_ready || p->L.tiles == 0) return TCL_OK;
-  const int64_t n = int64_t(p->L.tiles) * p->L.N;
-  hipLaunchKernelGGL(tile_ranges_kernel, dim3(int((n + 255) / 256)), dim3(256), 0, s, p->d,
-                     p->L.N, p->L.tiles);
+  hipLaunchKernelGGL(tile_ranges_kernel, dim3(p->L.tiles), dim3(256), 0, s, p->d, p->L.N);
   TCL_HIP(hipGetLastError());
   p->ranges_ready = true;
   return TCL_OK;

@@ -49,6 +49,10 @@ constexpr int kPlanLdsInts = 32768;
 constexpr int kXTok = 64;
 constexpr int kMfmaMinTokens = 256;
 
+// One apply launch covers up to kMaxMods modules that share the plan (e.g.
+// the seven projections of a transformer layer).
+constexpr int kMaxMods = 8;
+
 // device status words
 enum { ST_CODE = 0, ST_TUPLES = 1, ST_SEGMENTS = 2, ST_ITEMS = 3, ST_WORDS = 64 };
 
@@ -66,7 +70,7 @@ struct PlanLayout {
   // byte offsets inside the device buffer
   size_t o_status, o_tok, o_ad, o_slot, o_alpha, o_toktuple, o_tokrec, o_tokn, o_tokptr,
       o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_sseg, o_ranges,
-      o_mhist, o_mblk, o_msst, o_msib, total;
+      o_tcount, o_mhist, o_mblk, o_msst, o_msib, total;
 };
 
 // Mapping-stage algorithms: small tables run in one workgroup with the table
@@ -101,6 +105,7 @@ struct PlanDev {
   // per-adapter segment start and first work item [N]
   int32_t *m_hist, *m_blk, *m_sst, *m_sib;
   int2 *ranges;  // [tiles][N]: tuples of segment u whose token lies in tile
+  int2 *tcount;  // [tiles]: {tuples, segments with tuples} of the tile
 };
 
 }  // namespace tcl

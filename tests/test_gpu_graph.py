@@ -1,0 +1,79 @@
+"""A whole step (mapping stage + fused apply) captured in a HIP graph and
+replayed: every replay gives the eager result bit for bit.
+
+The prefill cases run the split expand, whose two halves run on the
+caller's stream and on the library's second stream joined by events; the
+graph must hold both.  Between replays the outputs are overwritten with NaN
+and an unrelated eager apply runs, so a replay that skipped or reused work
+would show.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import composites_to_dev, make_module, to_dev
+from tenant_composite_lora_amd import tclora
+from tenant_composite_lora_amd import workloads as W
+from test_gpu_mfma import MFMA_CASES
+from test_gpu_parity import CASES, banner
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name):
+    return MFMA_CASES[name]() if name in MFMA_CASES else CASES[name]()
+
+
+@pytest.mark.parametrize("name", ["config2", "config3", "config4", "mx_mixed",
+                                  "mfma_many_adapters"])
+def test_graph_replays_match_eager(name, monkeypatch):
+    monkeypatch.delenv("TCL_DISPATCH", raising=False)
+    monkeypatch.delenv("TCL_KCHUNK", raising=False)
+    wl = _case(name)
+    c = wl.composites
+    banner(f"graph replay {name}: T={wl.n_tokens} P={c.n_tuples()}")
+    gtp, gpp, pa, pw = composites_to_dev(c)
+    plan = tclora.Plan(gtp, gpp, pa, pw, c.n_adapters, n_tokens=c.n_tokens,
+                       max_tuples=c.n_tuples())
+    mods = [make_module(m) for m in wl.modules]
+    xs = [to_dev(x) for x in wl.x]
+    ybs = [to_dev(y) for y in wl.y_base]
+    ys = [y.clone() for y in ybs]
+    call = tclora.FusedCall(plan, mods, xs, ys)
+    # an unrelated batch run eagerly between replays
+    other = W.random_case(7, T=24, N=c.n_adapters, d_in=wl.modules[0].d_in,
+                          d_out=wl.modules[0].d_out, r_max=wl.modules[0].r_max, max_pairs=3)
+    o_gtp, o_gpp, o_pa, o_pw = composites_to_dev(other.composites)
+    o_plan = tclora.Plan(o_gtp, o_gpp, o_pa, o_pw, c.n_adapters, n_tokens=24,
+                         max_tuples=other.composites.n_tuples())
+    o_y = torch.zeros(24, wl.modules[0].d_out, device="cuda:0")
+    o_x = to_dev(other.x[0])
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for y, yb in zip(ys, ybs):
+            y.copy_(yb)
+        plan.remap(gtp, gpp, pa, pw, c.n_tokens, stream=s)
+        call(s)
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        cs = torch.cuda.current_stream()
+        for y, yb in zip(ys, ybs):
+            y.copy_(yb)
+        plan.remap(gtp, gpp, pa, pw, c.n_tokens, stream=cs)
+        call(cs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        tclora.fused_apply(o_plan, [mods[0]], [o_x], [o_y])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for mi, (y, r) in enumerate(zip(ys, ref)):
+            bad = torch.nonzero(y != r)
+            assert bad.numel() == 0, (rep, mi, bad[:5].tolist())
+    assert np.all(np.isfinite(o_y.cpu().numpy()))

@@ -371,9 +371,10 @@ def test_prefill_paths_agree(name, monkeypatch):
         assert ea <= TOL[wl.dtype] and eb <= TOL[wl.dtype]
 
 
-def test_mfma_bf16_output():
+def test_mfma_bf16_output(monkeypatch):
     wl = edge("mfma_ragged")
     banner("mfma expand with bf16 y")
+    monkeypatch.setenv("TCL_DISPATCH", "mfma")
     yb16 = W.f32_to_bf16_bits(wl.y_base[0])
     wl2 = W.Workload(wl.name, wl.dtype, wl.n_adapters, wl.composites, wl.modules, wl.x,
                      [W.bf16_bits_to_f32(yb16)])
