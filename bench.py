@@ -130,11 +130,12 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None)
             name = r["Kernel_Name"]
             if name.startswith("__amd_rocclr_copyBuffer"):
                 biggest_copy = max(biggest_copy, v)
-            for short in ("shrink_mfma", "shrink_valu", "expand_kernel", "expand_staged",
-                          "expand_mfma", "plan_kernel", "tile_ranges_kernel", "plan_m_local",
-                          "plan_m_scan", "plan_m_scatter"):
+            for short in ("shrink_mfma", "shrink_valu", "expand_kernel_split", "expand_kernel",
+                          "expand_staged", "expand_mfma", "plan_kernel", "tile_ranges_kernel",
+                          "plan_m_local", "plan_m_scan", "plan_m_scatter"):
                 if short in name:
                     per[short].append(v)
+                    break
         return per, calib / biggest_copy
 
     f, ff = load(fetch_csv)
@@ -331,10 +332,16 @@ def main():
     achieved = kb[dom] / per[dom] / 1e9
     ms_step = 1e3 * t_steps / K
     disp = os.environ.get("TCL_DISPATCH", "")
+    if wl.dtype != W.BF16:
+        expand_name = "expand_kernel"
+    else:
+        # prefill-sized batches: the matrix-core expand takes the dense tiles
+        # (the per-token kernel runs beside it for the others) unless forced
+        expand_name = {"staged": "expand_staged", "mfma": "expand_mfma",
+                       "valu": "expand_kernel"}.get(disp, "expand_mfma" if T >= 256
+                                                    else "expand_kernel")
     kernel_names = {"shrink": "shrink_mfma" if wl.dtype == W.BF16 else "shrink_valu",
-                    "expand": {"staged": "expand_staged", "mfma": "expand_mfma"}.get(
-                        disp, "expand_kernel") if wl.dtype == W.BF16 else "expand_kernel",
-                    "plan": "plan_kernel"}
+                    "expand": expand_name, "plan": "plan_kernel"}
     traffic = stored_traffic(wl.name, kernel_names[dom])
     out = {
         "metric": METRIC,
