@@ -79,10 +79,10 @@ def kernel_bytes(wl) -> dict:
 
 # HIP sources each kernel is built from: a stored counter summary is only
 # valid while these are unchanged
-KERNEL_SOURCES = {k: ("plan.hip", "tcl_internal.hpp")
+KERNEL_SOURCES = {k: ("plan.hip", "plan_core.hpp", "tcl_internal.hpp")
                   for k in ("plan_kernel", "tile_ranges_kernel", "plan_m_local", "plan_m_scan",
                             "plan_m_scatter")}
-APPLY_SOURCES = ("apply.hip", "tcl_internal.hpp")
+APPLY_SOURCES = ("apply.hip", "plan_core.hpp", "tcl_internal.hpp")
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -130,7 +130,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None)
             name = r["Kernel_Name"]
             if name.startswith("__amd_rocclr_copyBuffer"):
                 biggest_copy = max(biggest_copy, v)
-            for short in ("shrink_mfma", "shrink_valu", "expand_kernel_split", "expand_kernel",
+            for short in ("plan_shrink", "shrink_mfma", "shrink_valu", "expand_kernel_split",
+                          "expand_kernel",
                           "expand_staged", "expand_mfma", "plan_kernel", "tile_ranges_kernel",
                           "plan_m_local", "plan_m_scan", "plan_m_scatter"):
                 if short in name:
@@ -270,8 +271,26 @@ def main():
     import ctypes
 
     def step(i, stream_ptr):
-        tclora.check(L.tcl_plan_remap(plan.handle, ctypes.byref(comp_c), stream_ptr))
-        calls[i % R](stream_ptr)
+        # one step = tcl_remap_apply: mapping stage, shrink, expand
+        cl = calls[i % R]
+        tclora.check(L.tcl_remap_apply(plan.handle, ctypes.byref(comp_c), cl.descs, cl.n, cl.xp,
+                                       cl.ldx, cl.xd, cl.yp, cl.ldy, cl.yd, cl.ws.data_ptr(),
+                                       cl.ws.numel(), stream_ptr))
+
+    # decode tables (the one-workgroup mapping mode) of bf16 pools run the
+    # mapping stage inside the shrink launch; the shrink timing below then
+    # times that launch (tcl_remap_shrink), as the step runs it
+    fused = (wl.dtype == W.BF16 and c.n_pairs <= 512
+             and os.environ.get("TCL_FUSED_MAPPING") != "0")
+
+    def shrink_only(i, spp):
+        cl = calls[i % R]
+        if fused:
+            tclora.check(L.tcl_remap_shrink(plan.handle, ctypes.byref(comp_c), cl.descs, cl.n,
+                                            cl.xp, cl.ldx, cl.xd, cl.ws.data_ptr(),
+                                            cl.ws.numel(), spp))
+        else:
+            cl.shrink(spp)
 
     stream = torch.cuda.Stream(device=dev)
     sp = int(stream.cuda_stream)
@@ -296,7 +315,7 @@ def main():
     phases = {
         "step": step,
         "plan": plan_only,
-        "shrink": lambda i, spp: calls[i % R].shrink(spp),
+        "shrink": shrink_only,
         "expand": lambda i, spp: calls[i % R].expand(spp),
     }
     with torch.cuda.stream(stream):
@@ -340,8 +359,9 @@ def main():
         expand_name = {"staged": "expand_staged", "mfma": "expand_mfma",
                        "valu": "expand_kernel"}.get(disp, "expand_mfma" if T >= 256
                                                     else "expand_kernel")
-    kernel_names = {"shrink": "shrink_mfma" if wl.dtype == W.BF16 else "shrink_valu",
-                    "expand": expand_name, "plan": "plan_kernel"}
+    shrink_name = ("plan_shrink" if fused else "shrink_mfma") if wl.dtype == W.BF16 \
+        else "shrink_valu"
+    kernel_names = {"shrink": shrink_name, "expand": expand_name, "plan": "plan_kernel"}
     traffic = stored_traffic(wl.name, kernel_names[dom])
     out = {
         "metric": METRIC,

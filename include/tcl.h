@@ -247,6 +247,33 @@ int tcl_fused_expand(const tcl_plan *p, const tcl_module *mods, int32_t n_mods, 
                      size_t ws_bytes, void *const *y, const int64_t *ldy, tcl_dtype yd,
                      void *stream);
 
+/*
+ * One step: tcl_plan_remap(p, c) followed by tcl_fused_apply on the new plan,
+ * with the same arguments, results and errors as those two calls (the
+ * DyMerge-LoRA pipeline: the mapping stage, then the fused shrink and the
+ * aggregation).  Every host check of both runs before anything is queued.
+ * For tables of the one-workgroup mapping mode (every decode batch) and bf16
+ * pools, the mapping stage runs inside the shrink launch: each shrink
+ * workgroup maps the table in its own LDS and keeps its work items there,
+ * the first one also writes the plan out, so the step is two launches
+ * (TCL_FUSED_MAPPING=0 in the environment turns that off).  Results are bit
+ * for bit those of the separate calls.
+ */
+int tcl_remap_apply(tcl_plan *p, const tcl_composites *c, const tcl_module *mods,
+                    int32_t n_mods, const void *const *x, const int64_t *ldx, tcl_dtype xd,
+                    void *const *y, const int64_t *ldy, tcl_dtype yd, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/*
+ * The first half of tcl_remap_apply: tcl_plan_remap(p, c) and
+ * tcl_fused_shrink, in one launch where tcl_remap_apply would use one.
+ * tcl_fused_expand with the same plan, modules and workspace completes the
+ * step.  Same arguments and errors as those calls.
+ */
+int tcl_remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *mods,
+                     int32_t n_mods, const void *const *x, const int64_t *ldx, tcl_dtype xd,
+                     void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "plan_core.hpp"
 #include "tcl_internal.hpp"
 
 namespace tcl {
@@ -218,24 +219,29 @@ constexpr int kShrinkSteps = 8;   // 32-element K steps each lane has in flight
 // STEPS K steps of loads in flight.
 template <int STEPS>
 __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int stride,
-                                        f32x4_t (*red)[64]) {
+                                        f32x4_t (*red)[64], const Item *litems = nullptr,
+                                        int n_litems = 0) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   // The item record of the first job is fetched together with the item count
   // (clamped to the item table, which a padded grid may pass), which saves
   // one dependent memory round trip.
+  // litems: the work items in LDS (a mapping stage run by this workgroup),
+  // else the plan's item table
+  const Item *items = litems ? litems : s.items;
+  const int cap = litems ? max(n_litems, 1) : s.items_cap;
   int job = job0;
-  const int item0 = min(job / s.rg_total, s.items_cap - 1);
-  int4 head = s.items[item0].head;
-  int tokl = s.items[item0].tok[row];
-  const int n_items = s.status[ST_ITEMS];
+  const int item0 = min(job / s.rg_total, cap - 1);
+  int4 head = items[item0].head;
+  int tokl = items[item0].tok[row];
+  const int n_items = litems ? n_litems : s.status[ST_ITEMS];
   const int total = n_items * s.rg_total;
 
   for (; job < total; job += stride) {
     const int item = job / s.rg_total, rgg = job - item * s.rg_total;
     if (job != job0 || item != item0) {
-      head = s.items[item].head;
-      tokl = s.items[item].tok[row];
+      head = items[item].head;
+      tokl = items[item].tok[row];
     }
     int mi = 0;
 #pragma unroll
@@ -321,6 +327,36 @@ template <int STEPS>
 __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
   __shared__ f32x4_t red[kShrinkWaves][64];
   shrink_mfma_jobs<STEPS>(s, blockIdx.x, gridDim.x, red);
+}
+
+// ---------------------------------------------------------------------------
+// decode step: the mapping stage inside the shrink launch
+// ---------------------------------------------------------------------------
+// For tables of the direct mapping mode (every decode batch) every workgroup
+// of the shrink launch first runs the whole mapping stage on its own LDS copy
+// of the table (a few KiB: LDS work, no extra dependent memory round trip),
+// keeps the work items it produced in LDS and then runs its shrink jobs on
+// them; workgroup 0 also writes the plan out for the expand and the host.
+// The work items come out the same in every workgroup (the mapping stage is
+// deterministic), so the jobs split exactly as in shrink_mfma.  A table the
+// mapping stage rejects is left at that: workgroup 0 writes the verdict and
+// no workgroup runs a shrink job.  This takes one launch and the plan's
+// write-then-read round trip off a decode step.
+constexpr int kFusedLdsInts = 12288;  // direct-mode mapping scratch (48 KiB)
+constexpr int kFusedItems = 192;      // work items held in LDS (15 KiB)
+
+template <int STEPS>
+__global__ __launch_bounds__(64 * kShrinkWaves) void plan_shrink(PlanArgs A, ShrinkArgs s) {
+  __shared__ __align__(16) int lds[kFusedLdsInts];
+  __shared__ int tmp[6 * kSlotInts];
+  __shared__ Item li[kFusedItems];
+  __shared__ f32x4_t red[kShrinkWaves][64];
+  int n_items;
+  const int rc = plan_run<64 * kShrinkWaves, PLAN_DIRECT>(A, lds, tmp, blockIdx.x == 0, li,
+                                                          kFusedItems, &n_items);
+  if (rc != TCL_OK) return;
+  __syncthreads();  // the items in LDS are complete
+  shrink_mfma_jobs<STEPS>(s, blockIdx.x, gridDim.x, red, li, n_items);
 }
 
 // ---------------------------------------------------------------------------
@@ -2068,6 +2104,96 @@ int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
   hipStream_t s = static_cast<hipStream_t>(stream);
   // shrink and expand alternate per batch of up to kMaxMods modules
   return run_fused(p, mods, n_mods, x, ldx, y, ldy, yd, ws, s);
+}
+
+// Compute units of the current device (256 when the query fails).
+static int cus() {
+  static const int n = [] {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+      c = 256;
+    return c;
+  }();
+  return n;
+}
+
+// The decode step's shrink with the mapping stage inside (plan_shrink):
+// direct-mode tables whose LDS view and work items fit the kernel's budget,
+// bf16 pools, one launch's worth of modules.  TCL_FUSED_MAPPING=0 turns it
+// off (the mapping kernel then runs on its own before the shrink).
+static bool fused_mapping(const tcl_plan *p, const tcl_module *mods, int n_mods) {
+  if (p->L.mode != PLAN_DIRECT || mods[0].wdtype != TCL_BF16 || n_mods > kMaxMods) return false;
+  if (plan_direct_lds_ints(p) > kFusedLdsInts || p->L.items_cap > kFusedItems) return false;
+  const char *e = std::getenv("TCL_FUSED_MAPPING");
+  return !(e && !std::strcmp(e, "0"));
+}
+
+// Mapping stage of p (just laid out for c) and the shrink of every module.
+static int remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *mods,
+                        int32_t n_mods, const void *const *x, const int64_t *ldx, void *ws,
+                        hipStream_t s) {
+  if (!fused_mapping(p, mods, n_mods)) {
+    int rc = plan_launch(p, c, s);
+    if (rc) return rc;
+    return run_fused(p, mods, n_mods, x, ldx, nullptr, nullptr, TCL_F32, ws, s);
+  }
+  float *z[kMaxMods];
+  int zld[kMaxMods], kchunk;
+  z_slices(p, mods, 0, n_mods, ws, z, zld, &kchunk);
+  PlanArgs A;
+  plan_fill_args(p, c, &A);
+  ShrinkArgs a;
+  int64_t grid = shrink_args(p, mods, n_mods, x, ldx, z, zld, kchunk, 0, a);
+  // every workgroup maps the table once: at most two per CU (what the LDS
+  // allows at once), each looping over its share of the shrink jobs
+  const int cap = env_int("TCL_FUSED_GRID", 2 * cus());
+  if (grid > cap) grid = cap;
+  logf("plan+shrink: T=%d pairs=%d N=%d modules=%d units/item=%d kchunk=%d grid=%lld", p->L.T,
+       p->L.NP, p->L.N, n_mods, a.rg_total, kchunk, (long long)grid);
+  if (env_int("TCL_SSTEPS", kShrinkSteps) == 16)
+    hipLaunchKernelGGL(plan_shrink<16>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, A, a);
+  else
+    hipLaunchKernelGGL(plan_shrink<8>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, A, a);
+  TCL_HIP(hipGetLastError());
+  p->ranges_ready = false;
+  return TCL_OK;
+}
+
+int tcl_remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *mods,
+                     int32_t n_mods, const void *const *x, const int64_t *ldx, tcl_dtype xd,
+                     void *ws, size_t ws_bytes, void *stream) {
+  if (!x) return fail(TCL_EINVAL, "x list is required");
+  tcl_plan next;
+  int rc = plan_remap_prepare(p, c, &next);
+  if (rc) return rc;
+  rc = check_fused(&next, mods, n_mods, x, ldx, xd, nullptr, nullptr, TCL_F32, ws, ws_bytes);
+  if (rc) return rc;
+  *p = next;
+  return remap_shrink(p, c, mods, n_mods, x, ldx, ws, static_cast<hipStream_t>(stream));
+}
+
+int tcl_remap_apply(tcl_plan *p, const tcl_composites *c, const tcl_module *mods,
+                    int32_t n_mods, const void *const *x, const int64_t *ldx, tcl_dtype xd,
+                    void *const *y, const int64_t *ldy, tcl_dtype yd, void *ws,
+                    size_t ws_bytes, void *stream) {
+  if (!x || !y) return fail(TCL_EINVAL, "x and y lists are required");
+  tcl_plan next;
+  int rc = plan_remap_prepare(p, c, &next);
+  if (rc) return rc;
+  rc = check_fused(&next, mods, n_mods, x, ldx, xd, y, ldy, yd, ws, ws_bytes);
+  if (rc) return rc;
+  *p = next;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!fused_mapping(p, mods, n_mods)) {
+    // mapping kernel(s), then shrink and expand alternating per module batch
+    rc = plan_launch(p, c, s);
+    if (rc) return rc;
+    return run_fused(p, mods, n_mods, x, ldx, y, ldy, yd, ws, s);
+  }
+  rc = remap_shrink(p, c, mods, n_mods, x, ldx, ws, s);
+  if (rc) return rc;
+  return run_fused(p, mods, n_mods, nullptr, nullptr, y, ldy, yd, ws, s);
 }
 
 int tcl_fused_shrink(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,

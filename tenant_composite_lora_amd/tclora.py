@@ -28,7 +28,7 @@ _NAMES = {OK: "OK", EINVAL: "EINVAL", EALIGN: "EALIGN", ENOSPC: "ENOSPC",
 EXPORTS = ["tcl_last_error", "tcl_version", "tcl_plan_bytes", "tcl_plan_map", "tcl_plan_remap",
            "tcl_plan_status", "tcl_plan_copy_out", "tcl_plan_free", "tcl_module_load_ranks",
            "tcl_workspace_bytes", "tcl_shrink", "tcl_expand", "tcl_fused_apply",
-           "tcl_fused_shrink", "tcl_fused_expand"]
+           "tcl_fused_shrink", "tcl_fused_expand", "tcl_remap_apply", "tcl_remap_shrink"]
 
 
 class TclError(RuntimeError):
@@ -85,6 +85,11 @@ def lib(path: Optional[str] = None):
                                    ctypes.POINTER(i64), i32, vp, sz, vp]
     L.tcl_fused_expand.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, vp, sz,
                                    ctypes.POINTER(vp), ctypes.POINTER(i64), i32, vp]
+    L.tcl_remap_apply.argtypes = [vp, ctypes.POINTER(Composites), ctypes.POINTER(ModuleDesc),
+                                  i32, ctypes.POINTER(vp), ctypes.POINTER(i64), i32,
+                                  ctypes.POINTER(vp), ctypes.POINTER(i64), i32, vp, sz, vp]
+    L.tcl_remap_shrink.argtypes = [vp, ctypes.POINTER(Composites), ctypes.POINTER(ModuleDesc),
+                                   i32, ctypes.POINTER(vp), ctypes.POINTER(i64), i32, vp, sz, vp]
     if path is None:
         _lib = L
     return L
@@ -320,6 +325,40 @@ class FusedCall:
         check(lib().tcl_fused_expand(self.plan.handle, self.descs, self.n, self.ws.data_ptr(),
                                      self.ws.numel(), self.yp, self.ldy, self.yd,
                                      _stream(self.xs[0].device, stream)))
+
+    def _remap_table(self, group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha, n_tokens):
+        plan = self.plan
+        G = int(group_tok_ptr.shape[0]) - 1
+        NP = int(pair_adapter.shape[0])
+        plan._inputs = (group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha)
+        plan._c = Composites(int(n_tokens), G, NP, plan.n_adapters, plan.max_tuples,
+                             _ptr(group_tok_ptr), _ptr(group_pair_ptr), _ptr(pair_adapter),
+                             _ptr(pair_alpha))
+        return G, NP
+
+    def remap_apply(self, group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+                    n_tokens: int, stream=None):
+        """One step (tcl_remap_apply): re-map the plan with this composite
+        table, then shrink and expand every module."""
+        plan = self.plan
+        G, NP = self._remap_table(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+                                  n_tokens)
+        check(lib().tcl_remap_apply(plan.handle, ctypes.byref(plan._c), self.descs, self.n,
+                                    self.xp, self.ldx, self.xd, self.yp, self.ldy, self.yd,
+                                    self.ws.data_ptr(), self.ws.numel(),
+                                    _stream(self.xs[0].device, stream)))
+        plan.n_tokens, plan.n_groups, plan.n_pairs = int(n_tokens), G, NP
+
+    def remap_shrink(self, group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+                     n_tokens: int, stream=None):
+        """First half of a step (tcl_remap_shrink); expand() completes it."""
+        plan = self.plan
+        G, NP = self._remap_table(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+                                  n_tokens)
+        check(lib().tcl_remap_shrink(plan.handle, ctypes.byref(plan._c), self.descs, self.n,
+                                     self.xp, self.ldx, self.xd, self.ws.data_ptr(),
+                                     self.ws.numel(), _stream(self.xs[0].device, stream)))
+        plan.n_tokens, plan.n_groups, plan.n_pairs = int(n_tokens), G, NP
 
 
 def fused_apply(plan: Plan, mods: Sequence[Module], xs: Sequence[torch.Tensor],

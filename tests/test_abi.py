@@ -104,6 +104,13 @@ def test_null_plan_rejected(L):
     assert L.tcl_shrink(None, ctypes.byref(m), 0x1000, 16, 0, 0x1000, None) == tclora.EINVAL
     assert L.tcl_expand(None, ctypes.byref(m), 0x1000, 0x1000, 16, 1, None) == tclora.EINVAL
     assert L.tcl_plan_status(None, None, None, None) == tclora.EINVAL
+    c = tclora.Composites(4, 4, 4, 4, 4, 0x1000, 0x2000, 0x3000, 0x4000)
+    ptrs = (ctypes.c_void_p * 1)(0x1000)
+    lds = (ctypes.c_int64 * 1)(16)
+    assert L.tcl_remap_apply(None, ctypes.byref(c), ctypes.byref(m), 1, ptrs, lds, 0, ptrs,
+                             lds, 1, 0x1000, 1 << 20, None) == tclora.EINVAL
+    assert L.tcl_remap_shrink(None, ctypes.byref(c), ctypes.byref(m), 1, ptrs, lds, 0, 0x1000,
+                              1 << 20, None) == tclora.EINVAL
     assert L.tcl_plan_copy_out(None, *([None] * 9)) == tclora.EINVAL
     L.tcl_plan_free(None)
 

@@ -26,12 +26,15 @@ def _case(name):
 
 @pytest.mark.parametrize("name", ["config2", "config3", "config4", "mx_mixed",
                                   "mfma_many_adapters"])
-def test_graph_replays_match_eager(name, monkeypatch):
+@pytest.mark.parametrize("one_call", [False, True])
+def test_graph_replays_match_eager(name, one_call, monkeypatch):
     monkeypatch.delenv("TCL_DISPATCH", raising=False)
     monkeypatch.delenv("TCL_KCHUNK", raising=False)
+    monkeypatch.delenv("TCL_FUSED_MAPPING", raising=False)
     wl = _case(name)
     c = wl.composites
-    banner(f"graph replay {name}: T={wl.n_tokens} P={c.n_tuples()}")
+    banner(f"graph replay {name} ({'tcl_remap_apply' if one_call else 'remap + apply'}): "
+           f"T={wl.n_tokens} P={c.n_tuples()}")
     gtp, gpp, pa, pw = composites_to_dev(c)
     plan = tclora.Plan(gtp, gpp, pa, pw, c.n_adapters, n_tokens=c.n_tokens,
                        max_tuples=c.n_tuples())
@@ -49,12 +52,18 @@ def test_graph_replays_match_eager(name, monkeypatch):
     o_y = torch.zeros(24, wl.modules[0].d_out, device="cuda:0")
     o_x = to_dev(other.x[0])
 
+    def step(st):
+        if one_call:
+            call.remap_apply(gtp, gpp, pa, pw, c.n_tokens, stream=st)
+        else:
+            plan.remap(gtp, gpp, pa, pw, c.n_tokens, stream=st)
+            call(st)
+
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         for y, yb in zip(ys, ybs):
             y.copy_(yb)
-        plan.remap(gtp, gpp, pa, pw, c.n_tokens, stream=s)
-        call(s)
+        step(s)
     torch.cuda.synchronize()
     ref = [y.clone() for y in ys]
 
@@ -63,8 +72,7 @@ def test_graph_replays_match_eager(name, monkeypatch):
         cs = torch.cuda.current_stream()
         for y, yb in zip(ys, ybs):
             y.copy_(yb)
-        plan.remap(gtp, gpp, pa, pw, c.n_tokens, stream=cs)
-        call(cs)
+        step(cs)
     torch.cuda.synchronize()
     for rep in range(3):
         for y in ys:
