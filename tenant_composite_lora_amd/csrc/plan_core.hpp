@@ -220,6 +220,244 @@ __device__ inline PlanView plan_view(const PlanArgs &A, int *lds) {
   return v;
 }
 
+// The direct mode for tables of at most NT groups and NT pairs (every
+// decode-sized table): thread i owns group i and pair i.  Their table
+// entries go from global memory straight into registers, and each phase
+// below reads from LDS only what another thread produced, in one round trip
+// where the general path below takes several.  The stage's time is the
+// length of its dependent chain (LDS round trips, barriers and the
+// instructions between them), not bandwidth.  The outputs, error codes and
+// their precedence are those of the general path:
+//   A  groups: bounds, tuple counts, pair -> group records; one scan gives
+//      the group tuple bases and the structural verdict;
+//   B  pairs: ids, weights, canonical slot (pairs of the group with a
+//      smaller adapter id), duplicates, per-adapter tuple and pair counts;
+//   C  adapters: one four-value scan gives segment starts, item bases,
+//      segment indices and pair-bucket starts; segment table and work-item
+//      heads are written here;
+//   D  each pair enters its adapter's bucket at the ticket its count gave;
+//   E  a pair's first tuple position is its segment start plus the tuples of
+//      the bucket's pairs with a smaller pair index (earlier pairs hold
+//      earlier tokens), which does not depend on the order inside a bucket;
+//      tuples, token records and inlined work-item tokens are written.
+// lds must hold 8 NP + G + 6 N ints (16-byte aligned); tmp 3 kSlotInts.
+template <int NT>
+__device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool out, Item *li,
+                                     int li_cap, int *n_items_out) {
+  const int tid = threadIdx.x;
+  const int T = A.T, G = A.G, NP = A.NP, N = A.N;
+  *n_items_out = 0;
+  int4 *ainfo = reinterpret_cast<int4 *>(lds);   // [N] {seg start, item base, seg index, bucket}
+  int4 *pinfo = ainfo + N;                       // [NP] {group's first pair, pairs, first token, tokens}
+  int *l_pa = reinterpret_cast<int *>(pinfo + NP);  // [NP] adapter of every pair
+  int *pg = l_pa + NP;                           // [NP] group of every pair
+  int *bkt = pg + NP, *bkw = bkt + NP;           // [NP] bucket entries: pair, its tokens
+  int *gbase = bkw + NP;                         // [G] first token-index entry of every group
+  int *cnt = gbase + G, *pcnt = cnt + N;         // [N] tuples and pairs of every adapter
+
+  // the table, straight into registers.  Every thread loads (indices
+  // clamped into the arrays) so that the loads share one round trip: loads
+  // under per-thread conditions made the compiler wait for each group of
+  // them before issuing the next.  With no pairs, pa and pw may be empty;
+  // then the group array stands in for them.
+  const int gi = min(tid, G), gj = min(tid + 1, G);
+  const int pj = NP > 0 ? min(tid, NP - 1) : 0;
+  const int32_t *pap = NP > 0 ? A.pa : A.gtp;
+  const float *pwp = NP > 0 ? A.pw : reinterpret_cast<const float *>(A.gtp);
+  const int t0 = A.gtp[gi], t1 = A.gtp[gj], q0 = A.gpp[gi], q1 = A.gpp[gj];
+  const int aq = pap[pj];
+  const float w = pwp[pj];
+  for (int i = tid; i < N; i += NT) {
+    cnt[i] = 0;
+    pcnt[i] = 0;
+  }
+
+  // ---- A: groups ----------------------------------------------------------
+  int err = 0, local = 0;
+  // table ends: gtp[0] and gpp[0] are thread 0's first entries, gtp[G] and
+  // gpp[G] the second ones of thread max(G - 1, 0)
+  if (tid == 0 && (t0 != 0 || q0 != 0)) err |= EB_INVAL;
+  if (tid == max(G - 1, 0) && (t1 != T || q1 != NP)) err |= EB_INVAL;
+  if (tid < G) {
+    if (!(0 <= t0 && t0 <= t1 && t1 <= T && 0 <= q0 && q0 <= q1 && q1 <= NP)) {
+      err |= EB_INVAL;
+    } else {
+      const int4 rec = make_int4(q0, q1 - q0, t0, t1 - t0);
+      for (int q = q0; q < q1; ++q) {
+        pinfo[q] = rec;
+        pg[q] = tid;
+      }
+      if (q1 - q0 > TCL_MAX_PAIRS_PER_GROUP) err |= EB_UNSUP;
+      else local = (t1 - t0) * (q1 - q0);
+    }
+  }
+  if (tid < NP) l_pa[tid] = aq;
+  int P = 0, err_groups = 0, gb = 0;
+  {
+    int sv[3] = {local, err & EB_INVAL, (err & EB_UNSUP) >> 1}, st[3];
+    block_excl_scan_n<NT, 3>(sv, tmp + 0 * kSlotInts, st);
+    P = st[0];
+    gb = sv[0];
+    err_groups = (st[1] ? EB_INVAL : 0) | (st[2] ? EB_UNSUP : 0);
+  }
+  if (err_groups & EB_INVAL) {
+    if (out) plan_fail<NT>(A, TCL_EINVAL, 0);
+    return TCL_EINVAL;
+  }
+  if (tid < G) gbase[tid] = gb;
+
+  // ---- B: pairs (the group table is sound from here on) -------------------
+  err = 0;
+  int s = 0, tkt = 0, g = 0;
+  int4 pi = make_int4(0, 0, 0, 0);
+  bool live = false;
+  if (tid < NP) {
+    pi = pinfo[tid];
+    g = pg[tid];
+    const bool a_ok = aq >= 0 && aq < N;
+    if (!a_ok) err |= EB_INVAL;
+    if ((__float_as_uint(w) & 0x7f800000u) == 0x7f800000u) err |= EB_INVAL;
+    if (pi.y <= TCL_MAX_PAIRS_PER_GROUP) {
+      // counts first: the ticket's round trip then overlaps the slot search
+      if (a_ok) {
+        atomicAdd(&cnt[aq], pi.w);
+        tkt = atomicAdd(&pcnt[aq], 1);
+        live = true;
+      }
+      int dup = 0;
+      for (int q2 = pi.x; q2 < pi.x + pi.y; q2 += 8) {
+        int av[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) av[u] = q2 + u < pi.x + pi.y ? l_pa[q2 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool in = q2 + u < pi.x + pi.y;
+          s += (in && av[u] < aq) ? 1 : 0;
+          dup |= (in && av[u] == aq && q2 + u != tid) ? 1 : 0;
+        }
+      }
+      if (dup) err |= EB_INVAL;
+    }
+  }
+  err = block_or<NT>(err, tmp + 1 * kSlotInts) | err_groups;
+  if (err) {
+    const int code = (err & EB_INVAL) ? TCL_EINVAL : TCL_EUNSUPPORTED;
+    if (out) plan_fail<NT>(A, code, 0);
+    return code;
+  }
+  if (P > A.cap) {
+    if (out) plan_fail<NT>(A, TCL_ENOSPC, P);
+    return TCL_ENOSPC;
+  }
+
+  // ---- C: adapters ----------------------------------------------------------
+  int n_items = 0, n_segs = 0;
+  {
+    const int per = (N + NT - 1) / NT;
+    const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
+    int sv[4] = {0, 0, 0, 0}, st[4];
+    int c1 = 0, pc1 = 0;  // the counts of adapter a0 (the only one when N <= NT)
+    for (int a = a0; a < a1; ++a) {
+      const int c = cnt[a], pc = pcnt[a];
+      if (a == a0) {
+        c1 = c;
+        pc1 = pc;
+      }
+      sv[0] += c;
+      sv[1] += c > 0;
+      sv[2] += (c + kTile - 1) / kTile;
+      sv[3] += pc;
+    }
+    block_excl_scan_n<NT, 4>(sv, tmp + 2 * kSlotInts, st);
+    n_items = st[2];
+    n_segs = st[1];
+    int ec = sv[0], en = sv[1], ei = sv[2], eb = sv[3];
+    for (int a = a0; a < a1; ++a) {
+      const int c = a == a0 ? c1 : cnt[a], pc = a == a0 ? pc1 : pcnt[a];
+      ainfo[a] = make_int4(ec, ei, en, (eb << 16) | pc);
+      if (c > 0) {
+        if (out) {
+          A.d.seg_adapter[en] = a;
+          A.d.seg_begin[en] = ec;
+        }
+        for (int p0 = ec, i = ei; p0 < ec + c; p0 += kTile, ++i) {
+          const int4 h = make_int4(a, p0, min(ec + c, p0 + kTile) - p0, en);
+          if (out && i < A.items_cap) A.d.items[i].head = h;
+          if (li && i < li_cap) li[i].head = h;
+        }
+        en += 1;
+      }
+      ei += (c + kTile - 1) / kTile;
+      eb += pc;
+      ec += c;
+    }
+  }
+  __syncthreads();
+
+  // ---- D: buckets -----------------------------------------------------------
+  int4 ai = make_int4(0, 0, 0, 0);
+  if (live) {
+    ai = ainfo[aq];
+    const int e = (ai.w >> 16) + tkt;
+    bkt[e] = tid;
+    bkw[e] = pi.w;
+  }
+  __syncthreads();
+
+  // ---- E: tuple positions and records ---------------------------------------
+  if (live) {
+    const int b0 = ai.w >> 16, b1 = b0 + (ai.w & 0xffff);
+    int r = 0;
+    for (int e = b0; e < b1; e += 8) {
+      int qq[8], ww[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        qq[u] = e + u < b1 ? bkt[e + u] : NP;
+        ww[u] = e + u < b1 ? bkw[e + u] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += qq[u] < tid ? ww[u] : 0;
+    }
+    const int base = ai.x + r, gbq = gbase[g], pl = pi.y, tq0 = pi.z;
+    for (int i = 0; i < pi.w; ++i) {
+      const int p = base + i;
+      // positions are < P <= cap by construction; the guards keep a logic
+      // error from writing outside the plan buffer
+      if (p >= A.cap || gbq + i * pl + s >= A.cap || s >= kSlotPad) continue;
+      if (out) {
+        A.d.tup_token[p] = tq0 + i;
+        A.d.tup_adapter[p] = aq;
+        A.d.tup_alpha[p] = w;
+        A.d.tup_slot[p] = s;
+        A.d.tok_tuple[gbq + i * pl + s] = p;
+        A.d.tok_rec[int64_t(tq0 + i) * kSlotPad + s] = make_int4(p, aq, __float_as_int(w), ai.z);
+      }
+      const int lp = p - ai.x;
+      const int it = ai.y + lp / kTile;
+      if (out && it < A.items_cap) A.d.items[it].tok[lp % kTile] = tq0 + i;
+      if (li && it < li_cap) li[it].tok[lp % kTile] = tq0 + i;
+    }
+  }
+  if (out) {
+    if (tid < G) {
+      for (int t = t0; t < t1; ++t) {
+        A.d.tok_ptr[t] = gb + (t - t0) * (q1 - q0);
+        A.d.tok_n[t] = q1 - q0;
+      }
+    }
+    if (tid == 0) {
+      A.d.tok_ptr[T] = P;
+      A.d.seg_begin[n_segs] = P;
+      A.d.status[ST_TUPLES] = P;
+      A.d.status[ST_SEGMENTS] = n_segs;
+      A.d.status[ST_ITEMS] = n_items;
+      A.d.status[ST_CODE] = TCL_OK;
+    }
+  }
+  *n_items_out = n_items;
+  return TCL_OK;
+}
+
 // The mapping stage in the calling workgroup of NT threads.  lds: the LDS
 // block of the mode (kPlanLdsInts ints, 4 for PLAN_COUNT_GLOBAL); tmp:
 // 6 * kSlotInts ints of LDS.  out: write the plan (status words, tuples,
@@ -232,6 +470,10 @@ template <int NT, int MODE>
 __device__ inline int plan_run(const PlanArgs &A, int *lds, int *tmp, bool out, Item *li,
                                int li_cap, int *n_items_out) {
   constexpr bool direct = MODE == PLAN_DIRECT;
+  if constexpr (direct) {
+    if (A.G <= NT && A.NP <= NT)
+      return plan_run_small<NT>(A, lds, tmp, out, li, li_cap, n_items_out);
+  }
   const int tid = threadIdx.x;
   *n_items_out = 0;
   const int T = A.T, G = A.G, NP = A.NP, N = A.N, C = A.C;

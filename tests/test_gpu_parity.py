@@ -81,6 +81,13 @@ EDGE_CASES = {
     "count_5000_adapters": dict(seed=135, T=600, N=5000, d_in=64, d_out=64, r_max=4,
                                 max_pairs=3),
     "count_9000_groups": dict(seed=136, T=9000, N=64, d_in=32, d_out=32, r_max=4, max_pairs=2),
+    # direct-mode tables with more groups than the mapping workgroup has
+    # threads (mostly empty tokens): the general direct path, not the
+    # one-thread-per-group one
+    "direct_400_groups": dict(seed=137, T=400, N=20, d_in=64, d_out=72, r_max=4, max_pairs=2,
+                              empty_frac=0.75),
+    "direct_1500_groups": dict(seed=138, T=1500, N=30, d_in=64, d_out=72, r_max=4,
+                               max_pairs=2, empty_frac=0.8),
 }
 
 
@@ -254,9 +261,18 @@ def test_plan_multi_validation(name):
         assert torch.equal(y, y0)
 
 
+def _pad_groups(tp, pp, n):
+    """The same table with n empty groups (no tokens, no pairs) appended:
+    more groups than the direct mapping workgroup has threads."""
+    return list(tp) + [tp[-1]] * n, list(pp) + [pp[-1]] * n
+
+
+@pytest.mark.parametrize("padded", [False, True])
 @pytest.mark.parametrize("name", sorted(_bad_tables()))
-def test_plan_device_validation(name):
+def test_plan_device_validation(name, padded):
     tp, pp, ad, al, T, cap = _bad_tables()[name]
+    if padded:
+        tp, pp = _pad_groups(tp, pp, 1100)
     N = 80 if name.startswith("too_many_pairs") else 4
     want = O.validate(np.array(tp), np.array(pp), np.array(ad, np.int32),
                       np.array(al, np.float32), T, N, max_tuples=cap)

@@ -13,13 +13,14 @@ import oracle as O
 from gpu_util import composites_to_dev, make_module, rel_err, to_dev
 from tenant_composite_lora_amd import tclora
 from tenant_composite_lora_amd import workloads as W
-from test_gpu_parity import CASES, TOL, _bad_tables, banner, oracle_apply
+from test_gpu_parity import CASES, TOL, _bad_tables, _pad_groups, banner, oracle_apply
 
 pytestmark = pytest.mark.gpu
 
 STEP_CASES = ["config1", "config2", "config3", "ragged_tiles", "static_groups", "empty_tokens",
               "ranks_with_zero", "rank_40", "rank_5", "single_token", "all_adapters",
-              "64_pairs_per_token", "rank_64_f32", "mfma_ragged"]
+              "64_pairs_per_token", "rank_64_f32", "mfma_ragged", "direct_400_groups",
+              "direct_1500_groups"]
 
 
 def _step(wl, y_dtype=torch.float32, plan_wl=None):
@@ -66,7 +67,8 @@ def test_step_vs_oracle(name, monkeypatch):
 
 
 @pytest.mark.parametrize("name", ["config2", "config3", "static_groups", "64_pairs_per_token",
-                                  "empty_tokens", "ranks_with_zero", "all_adapters"])
+                                  "empty_tokens", "ranks_with_zero", "all_adapters",
+                                  "direct_400_groups", "direct_1500_groups"])
 def test_step_paths_agree(name, monkeypatch):
     """The mapping stage inside the shrink launch and the separate mapping
     kernel give the same plan and the same y, bit for bit."""
@@ -133,10 +135,13 @@ def test_consecutive_steps_on_one_plan(monkeypatch):
         _check(wl, [y.double().cpu().numpy()])
 
 
+@pytest.mark.parametrize("padded", [False, True])
 @pytest.mark.parametrize("name", sorted(_bad_tables()))
-def test_step_rejected_table_is_noop(name, monkeypatch):
+def test_step_rejected_table_is_noop(name, padded, monkeypatch):
     monkeypatch.delenv("TCL_FUSED_MAPPING", raising=False)
     tp, pp, ad, al, T, cap = _bad_tables()[name]
+    if padded:
+        tp, pp = _pad_groups(tp, pp, 1100)
     N = 80 if name.startswith("too_many_pairs") else 4
     want = O.validate(np.array(tp), np.array(pp), np.array(ad, np.int32),
                       np.array(al, np.float32), T, N, max_tuples=cap)
