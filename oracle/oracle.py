@@ -126,6 +126,49 @@ def group_of_token(group_tok_ptr) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# token-level gate: the composite of each token from its gate logits
+# (DyMerge-LoRA, section 3.1 dynamic composition; section 5.1 Sparse
+# workload: a request references 5-8 adapters and two are active per token)
+# ---------------------------------------------------------------------------
+
+def gate_topk(logits, candidates, k: int):
+    """Composite table of a token-level gate.
+
+    Token t has candidate adapters ``candidates[t, c]`` (entries < 0 are
+    padding) with gate logits ``logits[t, c]``.  Its weights are the softmax
+    of the logits over the valid candidates; the k largest weights are kept,
+    not renormalised, ties going to the earlier candidate (the softmax is
+    increasing in the logit, so this is the order of the logits).  The
+    pairs of a token are listed in that order.  A token with fewer than k
+    valid candidates lists adapter -1 with weight 0 for each missing pair,
+    and a token with a non-finite valid logit lists adapter -1 with weight 0
+    for all k pairs (tables the mapping stage rejects).
+
+    Returns (group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha) with one
+    group per token; pair_alpha is float64 here."""
+    lg = np.asarray(logits, dtype=np.float64)
+    cd = np.asarray(candidates, dtype=np.int64)
+    T = lg.shape[0]
+    gtp = np.arange(T + 1, dtype=np.int64)
+    gpp = np.arange(T + 1, dtype=np.int64) * k
+    pa = np.full(T * k, -1, dtype=np.int64)
+    pw = np.zeros(T * k, dtype=np.float64)
+    for t in range(T):
+        valid = [c for c in range(cd.shape[1]) if cd[t, c] >= 0]
+        if not valid or not all(math.isfinite(lg[t, c]) for c in valid):
+            continue
+        top = max(lg[t, c] for c in valid)
+        e = {c: math.exp(lg[t, c] - top) for c in valid}
+        total = sum(e[c] for c in valid)
+        # largest logit first; equal logits keep the candidate order
+        order = sorted(valid, key=lambda c: (-lg[t, c], c))
+        for i, c in enumerate(order[:k]):
+            pa[t * k + i] = cd[t, c]
+            pw[t * k + i] = e[c] / total
+    return gtp, gpp, pa, pw
+
+
+# ---------------------------------------------------------------------------
 # mapping stage: tuples reordered by adapter id (DyMerge-LoRA, section 4.3)
 # ---------------------------------------------------------------------------
 

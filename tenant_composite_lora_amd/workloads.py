@@ -273,10 +273,17 @@ def config4(seed: int = 0) -> Workload:
         n = int(rng.integers(5, 9))
         refs.append(rng.choice(N, n, replace=False).tolist())
     ads, als = [], []
+    # the gate's inputs as a device gate takes them: per token, the request's
+    # referenced adapters padded with -1 to 8 candidates, and the logits
+    cand = np.full((T, 8), -1, dtype=np.int32)
+    logits = np.zeros((T, 8), dtype=np.float64)
     for q in range(R):
         ref = refs[q]
-        for _ in range(L):
+        for i in range(L):
             lg = rng.standard_normal(len(ref))
+            t = q * L + i
+            cand[t, :len(ref)] = ref
+            logits[t, :len(ref)] = lg
             e = np.exp(lg - lg.max())
             pr = e / e.sum()
             order = np.argsort(-pr, kind="stable")[:2]
@@ -286,7 +293,8 @@ def config4(seed: int = 0) -> Workload:
     x = [_x(rng, T, m.d_in, BF16) for m in mods]
     yb = [_ybase(rng, T, m.d_out) for m in mods]
     return Workload("sparse_prefill_gated_8x256_n128_r16", BF16, N, comp, mods, x, yb,
-                    n_prefill=T, meta={"refs": refs})
+                    n_prefill=T, meta={"refs": refs, "gate_candidates": cand,
+                                       "gate_logits": logits, "gate_k": 2})
 
 
 def config5(seed: int = 0, scale_tokens: float = 1.0) -> Workload:

@@ -393,7 +393,62 @@ def pin_validation(O):
         == O.EUNSUPPORTED
 
 
+def pin_gate(O):
+    """The token-level gate (DyMerge-LoRA, section 3.1 dynamic composition,
+    section 5.1 Sparse workload): top-k of the softmax of the gate logits over
+    a token's valid candidates, not renormalised, ties to the earlier
+    candidate."""
+    rng = np.random.default_rng(71)
+    T, C, k = 40, 8, 2
+    lg = rng.standard_normal((T, C))
+    cand = np.stack([rng.permutation(100)[:C] for _ in range(T)]).astype(np.int64)
+    gtp, gpp, pa, pw = O.gate_topk(lg, cand, k)
+    assert np.array_equal(gtp, np.arange(T + 1)) and np.array_equal(gpp, np.arange(T + 1) * k)
+    # library routines: torch.topk picks the indices, torch.softmax the weights
+    lt = torch.tensor(lg, dtype=torch.float64)
+    idx = torch.topk(lt, k, dim=1).indices.numpy()
+    sm = torch.softmax(lt, dim=1).numpy()
+    for t in range(T):
+        assert pa[t * k:(t + 1) * k].tolist() == cand[t, idx[t]].tolist(), t
+        assert np.allclose(pw[t * k:(t + 1) * k], sm[t, idx[t]], rtol=1e-13, atol=0), t
+    # keeping every candidate: the weights are the whole softmax, in
+    # descending order, summing to 1
+    _, _, pa2, pw2 = O.gate_topk(lg, cand, C)
+    w2 = pw2.reshape(T, C)
+    assert np.allclose(w2.sum(1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(np.diff(w2, axis=1) <= 0)
+    # a common shift of the logits changes nothing
+    _, _, pa3, pw3 = O.gate_topk(lg + 3.75, cand, k)
+    assert np.array_equal(pa3, pa) and np.allclose(pw3, pw, rtol=1e-13, atol=0)
+    # ties go to the earlier candidate; equal logits give equal weights
+    _, _, pa4, pw4 = O.gate_topk([[1.0, 1.0, 1.0, 0.0]], [[10, 11, 12, 13]], 2)
+    e = np.e
+    assert pa4.tolist() == [10, 11]
+    assert np.allclose(pw4, [e / (3 * e + 1)] * 2, rtol=1e-15, atol=0)
+    # padding (-1) is not a candidate: the same as the compacted list
+    _, _, pa5, pw5 = O.gate_topk([[0.3, 9.0, -0.2, 0.7]], [[4, -1, 6, 8]], 2)
+    _, _, pa6, pw6 = O.gate_topk([[0.3, -0.2, 0.7]], [[4, 6, 8]], 2)
+    assert np.array_equal(pa5, pa6) and np.allclose(pw5, pw6, rtol=1e-15, atol=0)
+    # fewer valid candidates than k, or a non-finite logit: adapter -1
+    _, _, pa7, pw7 = O.gate_topk([[0.5, 0.0, 0.0]], [[5, -1, -1]], 2)
+    assert pa7.tolist() == [5, -1] and pw7.tolist() == [1.0, 0.0]
+    _, _, pa8, pw8 = O.gate_topk([[float("nan"), 0.0]], [[5, 6]], 2)
+    assert pa8.tolist() == [-1, -1] and pw8.tolist() == [0.0, 0.0]
+    # brute force on small cases: the kept set has the largest total weight
+    # of all k-subsets
+    from itertools import combinations
+    for trial in range(20):
+        n = int(rng.integers(3, 7))
+        kk = int(rng.integers(1, n + 1))
+        l1 = rng.standard_normal((1, n))
+        c1 = np.arange(n)[None, :]
+        _, _, a1, w1 = O.gate_topk(l1, c1, kk)
+        p1 = np.exp(l1[0] - l1[0].max()) / np.exp(l1[0] - l1[0].max()).sum()
+        best = max(combinations(range(n), kk), key=lambda S: sum(p1[i] for i in S))
+        assert sorted(a1.tolist()) == sorted(best), trial
+
+
 ALL_PINS = [pin_x1_elora_example, pin_x2_dense_premerge, pin_x3_textbook_lora,
             pin_x4_linearity, pin_x5_noop, pin_x6_truncation, pin_x7_rank_bound,
             pin_x8_mapping, pin_x9_adapter_fraction, pin_x10_permutation,
-            pin_split_and_rows, pin_validation]
+            pin_split_and_rows, pin_validation, pin_gate]

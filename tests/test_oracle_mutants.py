@@ -28,6 +28,14 @@ MUTANTS = {
                     "if False:"),
     "adapter_fraction_one_side": ("return (d_in + d_out) * r / (d_in * d_out)",
                                   "return d_in * r / (d_in * d_out)"),
+    "gate_renormalised": ("pw[t * k + i] = e[c] / total",
+                          "pw[t * k + i] = e[c] / sum(e[o] for o in order[:k])"),
+    "gate_ties_to_later": ("order = sorted(valid, key=lambda c: (-lg[t, c], c))",
+                           "order = sorted(valid, key=lambda c: (-lg[t, c], -c))"),
+    "gate_smallest": ("order = sorted(valid, key=lambda c: (-lg[t, c], c))",
+                      "order = sorted(valid, key=lambda c: (lg[t, c], c))"),
+    "gate_padding_kept": ("valid = [c for c in range(cd.shape[1]) if cd[t, c] >= 0]",
+                          "valid = [c for c in range(cd.shape[1])]"),
 }
 
 
