@@ -274,6 +274,40 @@ int tcl_remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *mod
                      int32_t n_mods, const void *const *x, const int64_t *ldx, tcl_dtype xd,
                      void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Token-level gate: the composite table of dynamic composition from gate
+ * logits, on the GPU (DyMerge-LoRA, section 3.1: under dynamic composition
+ * alpha is computed per token; section 5.1, Sparse workload: a request
+ * references 5-8 adapters and two are active per token; the one-minute
+ * summary names padding and masking for the gate's vectorised form).
+ *
+ * Token t has n_candidates candidate adapters candidates[t * ld_candidates
+ * + c] (an id < 0 is padding, not a candidate) with gate logits
+ * logits[t * ld_logits + c], fp32, c in [0, n_candidates).  Its weights are
+ * the softmax of the logits over the valid candidates, computed in fp32; the
+ * k largest are kept, not renormalised, ties going to the smaller c (the
+ * order of the logits, since the softmax is increasing).  Output, one group
+ * per token, device arrays of the caller:
+ *   group_tok_ptr[t] = t        (n_tokens + 1 entries)
+ *   group_pair_ptr[t] = t * k   (n_tokens + 1 entries)
+ *   pair_adapter[t * k + i], pair_alpha[t * k + i], i in [0, k): the kept
+ *     pairs, largest weight first   (n_tokens * k entries each)
+ * A token with fewer than k valid candidates gets adapter -1 (weight 0) for
+ * each missing pair, and a token with a non-finite valid logit gets adapter
+ * -1 (weight 0) for all k: the mapping stage rejects such a table with
+ * TCL_EINVAL.  Candidate ids are not range-checked here; the mapping stage
+ * does that too.  The table is ready for tcl_plan_map, tcl_plan_remap or
+ * tcl_remap_apply without a trip through host memory.
+ * Host checks: 1 <= n_candidates <= 64, 1 <= k <= n_candidates, k <=
+ * TCL_MAX_PAIRS_PER_GROUP, leading dimensions >= n_candidates, n_tokens >= 0,
+ * n_tokens * k < 2^31, every pointer 4-byte aligned and non-NULL (logits
+ * and candidates may be NULL when n_tokens is 0).
+ */
+int tcl_gate_topk(const float *logits, int64_t ld_logits, const int32_t *candidates,
+                  int64_t ld_candidates, int32_t n_tokens, int32_t n_candidates, int32_t k,
+                  int32_t *group_tok_ptr, int32_t *group_pair_ptr, int32_t *pair_adapter,
+                  float *pair_alpha, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

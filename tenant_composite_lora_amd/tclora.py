@@ -28,7 +28,8 @@ _NAMES = {OK: "OK", EINVAL: "EINVAL", EALIGN: "EALIGN", ENOSPC: "ENOSPC",
 EXPORTS = ["tcl_last_error", "tcl_version", "tcl_plan_bytes", "tcl_plan_map", "tcl_plan_remap",
            "tcl_plan_status", "tcl_plan_copy_out", "tcl_plan_free", "tcl_module_load_ranks",
            "tcl_workspace_bytes", "tcl_shrink", "tcl_expand", "tcl_fused_apply",
-           "tcl_fused_shrink", "tcl_fused_expand", "tcl_remap_apply", "tcl_remap_shrink"]
+           "tcl_fused_shrink", "tcl_fused_expand", "tcl_remap_apply", "tcl_remap_shrink",
+           "tcl_gate_topk"]
 
 
 class TclError(RuntimeError):
@@ -90,6 +91,7 @@ def lib(path: Optional[str] = None):
                                   ctypes.POINTER(vp), ctypes.POINTER(i64), i32, vp, sz, vp]
     L.tcl_remap_shrink.argtypes = [vp, ctypes.POINTER(Composites), ctypes.POINTER(ModuleDesc),
                                    i32, ctypes.POINTER(vp), ctypes.POINTER(i64), i32, vp, sz, vp]
+    L.tcl_gate_topk.argtypes = [vp, i64, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp]
     if path is None:
         _lib = L
     return L
@@ -366,3 +368,27 @@ def fused_apply(plan: Plan, mods: Sequence[Module], xs: Sequence[torch.Tensor],
                 stream=None) -> List[torch.Tensor]:
     FusedCall(plan, mods, xs, ys, ws)(stream)
     return list(ys)
+
+
+def gate_topk(logits: torch.Tensor, candidates: torch.Tensor, k: int, stream=None):
+    """tcl_gate_topk: the composite table of a token-level gate on the GPU.
+    logits: fp32 [T, C]; candidates: int32 [T, C] adapter ids (< 0 = padding).
+    Returns (group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha), device
+    tensors ready for Plan / Plan.remap / FusedCall.remap_apply."""
+    if logits.dim() != 2 or candidates.shape != logits.shape:
+        raise ValueError("logits and candidates must both be [T, C]")
+    if logits.dtype != torch.float32 or candidates.dtype != torch.int32:
+        raise ValueError("logits must be float32 and candidates int32")
+    T, C = logits.shape
+    if T > 0 and (logits.stride(1) != 1 or candidates.stride(1) != 1):
+        raise ValueError("logits and candidates must have contiguous rows")
+    ldl, ldc = (logits.stride(0), candidates.stride(0)) if T > 0 else (C, C)
+    dev = logits.device
+    gtp = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    gpp = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    pa = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    pw = torch.empty(max(T * k, 1), dtype=torch.float32, device=dev)
+    check(lib().tcl_gate_topk(logits.data_ptr(), ldl, candidates.data_ptr(),
+                              ldc, T, C, k, gtp.data_ptr(), gpp.data_ptr(),
+                              pa.data_ptr(), pw.data_ptr(), _stream(dev, stream)))
+    return gtp, gpp, pa[:T * k], pw[:T * k]

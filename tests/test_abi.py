@@ -126,3 +126,25 @@ def test_load_ranks_host_errors(L):
                                  None)
     assert rc == tclora.EINVAL
     assert L.tcl_module_load_ranks(ctypes.byref(m), None, 0x3000, None) == tclora.EINVAL
+
+
+def test_gate_host_errors(L):
+    """tcl_gate_topk rejects bad sizes and pointers on the host (no GPU)."""
+    P = 0x1000
+
+    def call(T=4, C=8, k=2, ldl=8, ldc=8, lg=P, cd=P, out=P):
+        return L.tcl_gate_topk(lg, ldl, cd, ldc, T, C, k, out, out, out, out, None)
+
+    assert call(T=-1) == tclora.EINVAL
+    assert call(C=0) == tclora.EINVAL
+    assert call(C=65, ldl=65, ldc=65) == tclora.EINVAL
+    assert call(k=0) == tclora.EINVAL
+    assert call(k=9) == tclora.EINVAL              # k > n_candidates
+    assert call(ldl=7) == tclora.EINVAL
+    assert call(ldc=7) == tclora.EINVAL
+    assert call(lg=None) == tclora.EINVAL
+    assert call(cd=None) == tclora.EINVAL
+    assert call(out=None) == tclora.EINVAL
+    assert call(T=1 << 30, k=4, C=8) == tclora.EINVAL  # T * k beyond 32-bit indexing
+    assert call(lg=P + 2) == tclora.EALIGN
+    assert b"gate" in L.tcl_last_error()
