@@ -294,7 +294,9 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)
     sp = int(stream.cuda_stream)
-    S = R  # steps per graph: one pass over the replicas
+    # steps per graph: whole passes over the replicas, at least 64 steps, so
+    # that a replay's own launch cost is spread thin
+    S = R * max(1, -(-64 // R))
     print(f"[bench] {wl.name}: T={T} P={P_dev} U={U_dev} replicas={R} "
           f"alg bytes={B_alg} flops={F_alg}", file=sys.stderr, flush=True)
 
@@ -346,6 +348,42 @@ def main():
         print(f"[bench] timing {K} launches of the {name} kernel alone", file=sys.stderr,
               flush=True)
         per[name] = timed(runners[name], K) / K
+    gate = None
+    if "gate_logits" in wl.meta:
+        # the token-level gate that produces this workload's table from its
+        # logits (tcl_gate_topk), timed alone the same way
+        lg = torch.from_numpy(np.ascontiguousarray(wl.meta["gate_logits"], np.float32)).to(dev)
+        cd = torch.from_numpy(np.ascontiguousarray(wl.meta["gate_candidates"], np.int32)).to(dev)
+        gk, C = int(wl.meta["gate_k"]), lg.shape[1]
+        g_out = [torch.empty(T + 1, dtype=torch.int32, device=dev),
+                 torch.empty(T + 1, dtype=torch.int32, device=dev),
+                 torch.empty(T * gk, dtype=torch.int32, device=dev),
+                 torch.empty(T * gk, dtype=torch.float32, device=dev)]
+
+        def gate_call(spp):
+            tclora.check(L.tcl_gate_topk(lg.data_ptr(), C, cd.data_ptr(), C, T, C, gk,
+                                         *[o.data_ptr() for o in g_out], spp))
+
+        # 64 launches per graph: the replicas do not matter here (the gate's
+        # inputs are a few hundred KiB), and a short graph would time its
+        # own launch instead of the kernel
+        GS = 64
+        gK = max(GS, (K // GS) * GS)
+        if args.eager:
+            g_run = lambda n: [gate_call(sp) for _ in range(n)]
+        else:
+            gg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gg, stream=stream):
+                cs = int(torch.cuda.current_stream().cuda_stream)
+                for _ in range(GS):
+                    gate_call(cs)
+            g_run = (lambda g: (lambda n: [g.replay() for _ in range(max(1, n // GS))]))(gg)
+        print(f"[bench] timing {gK} launches of the gate kernel alone", file=sys.stderr, flush=True)
+        g_run(GS)
+        g_us = timed(g_run, gK) / gK * 1e6
+        g_bytes = T * C * 8 + (T + 1) * 8 + T * gk * 8
+        gate = {"kernel": "gate_topk_kernel", "us": g_us, "alg_bytes": g_bytes,
+                "gbs": g_bytes / g_us / 1e3, "k": gk, "candidates": C}
     kb = kernel_bytes(wl)
     dom = max(("shrink", "expand"), key=lambda n: per[n])
     achieved = kb[dom] / per[dom] / 1e9
@@ -388,6 +426,7 @@ def main():
             "kernel_us": {n: per[n] * 1e6 for n in per},
             "kernel_alg_bytes": kb,
             "kernel_gbs": {n: kb[n] / per[n] / 1e9 for n in per},
+            **({"gate": gate} if gate else {}),
         },
         "roofline": {
             "bound": "hbm", "kernel": kernel_names[dom],

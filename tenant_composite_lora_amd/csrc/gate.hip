@@ -3,6 +3,8 @@
 // workload).  One wave per token, one lane per candidate: the softmax over
 // the valid candidates, then k rounds of a wave-wide maximum pick the kept
 // pairs.  The table goes straight to the mapping stage in device memory.
+// The work per token is a few dozen instructions; the time is the launch
+// and one load round trip.
 #include <cmath>
 
 #include "tcl_internal.hpp"
@@ -21,19 +23,37 @@ struct GateArgs {
   float *pw;
 };
 
-// Butterfly reductions over the 64 lanes.  Every lane ends with the same
-// value: each step adds (or compares) two partial results that two lanes
-// hold in swapped order, and both operations are commutative.
+// Reductions over the 64 lanes with DPP moves (no LDS traffic): steps of
+// 1, 2, 4 and 8 lanes inside each row of 16, then the row broadcasts carry
+// rows 0 and 1 into rows 1 and 3 and rows 2 and 3, so lane 63 ends with the
+// whole wave's result, which is then read as a uniform value.  Lanes without
+// a source take the operation's identity.  The order of the operations is
+// fixed, so the result is the same on every run.
+template <int CTRL, int ROW_MASK, typename Op>
+__device__ inline float dpp_step(float v, int identity, Op op) {
+  const float o = __int_as_float(
+      __builtin_amdgcn_update_dpp(identity, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+  return op(v, o);
+}
+
+template <typename Op>
+__device__ inline float wave_reduce(float v, float identity, Op op) {
+  const int id = __float_as_int(identity);
+  v = dpp_step<0x111, 0xf>(v, id, op);  // row_shr:1
+  v = dpp_step<0x112, 0xf>(v, id, op);  // row_shr:2
+  v = dpp_step<0x114, 0xf>(v, id, op);  // row_shr:4
+  v = dpp_step<0x118, 0xf>(v, id, op);  // row_shr:8
+  v = dpp_step<0x142, 0xa>(v, id, op);  // row_bcast:15
+  v = dpp_step<0x143, 0xc>(v, id, op);  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  return wave_reduce(v, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  return wave_reduce(v, 0.f, [](float a, float b) { return a + b; });
 }
 
 __global__ __launch_bounds__(64 * kGateWaves) void gate_topk_kernel(GateArgs g) {
@@ -48,10 +68,12 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_topk_kernel(GateArgs g) 
     }
     return;
   }
+  // both loads at once (the logit does not wait for the id)
   const bool in = lane < g.C;
   const int id = in ? g.cand[int64_t(t) * g.ldc + lane] : -1;
+  const float lin = in ? g.logits[int64_t(t) * g.ldl + lane] : 0.f;
   const bool valid = id >= 0;
-  const float l = valid ? g.logits[int64_t(t) * g.ldl + lane] : 0.f;
+  const float l = valid ? lin : 0.f;
   const bool bad = __ballot(valid && !isfinite(l)) != 0;
   const float m = wave_max(valid ? l : -INFINITY);
   const float e = valid ? expf(l - m) : 0.f;
@@ -68,8 +90,8 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_topk_kernel(GateArgs g) 
     const uint64_t win = __ballot(cand_here && l == mx);
     if (win == 0) break;  // fewer valid candidates than k
     const int wl = __builtin_ctzll(win);
-    const int a = __shfl(id, wl, 64);
-    const float pv = __shfl(p, wl, 64);
+    const int a = __builtin_amdgcn_readlane(id, wl);
+    const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), wl));
     if (lane == i) {
       my_a = a;
       my_p = pv;
