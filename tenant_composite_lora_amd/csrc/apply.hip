@@ -351,12 +351,30 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void plan_shrink(PlanArgs A, Shr
   __shared__ int tmp[6 * kSlotInts];
   __shared__ Item li[kFusedItems];
   __shared__ f32x4_t red[kShrinkWaves][64];
+  constexpr int NT = 64 * kShrinkWaves;
+  // Workgroup 0 runs the whole mapping stage and writes the plan; it has no
+  // shrink job.  The others need only the work items of their own jobs: on
+  // small tables they stop the mapping stage at the item heads and fill the
+  // token lists of just those items.
+  const bool lead = blockIdx.x == 0, small = A.G <= NT && A.NP <= NT;
   int n_items;
-  const int rc = plan_run<64 * kShrinkWaves, PLAN_DIRECT>(A, lds, tmp, blockIdx.x == 0, li,
-                                                          kFusedItems, &n_items);
-  if (rc != TCL_OK) return;
+  const int rc = plan_run<NT, PLAN_DIRECT>(A, lds, tmp, lead, li, kFusedItems, &n_items,
+                                           small && !lead);
+  if (rc != TCL_OK || lead) return;
+  const int job0 = blockIdx.x - 1, stride = gridDim.x - 1;
+  if (small) {
+    const int total = n_items * s.rg_total;
+    int last = -1, calls = 0;
+    for (int job = job0; job < total; job += stride) {
+      const int item = job / s.rg_total;
+      if (item == last) continue;
+      plan_small_item_tokens<NT>(A, lds, tmp + (3 + (calls & 1)) * kSlotInts, li, item);
+      last = item;
+      ++calls;
+    }
+  }
   __syncthreads();  // the items in LDS are complete
-  shrink_mfma_jobs<STEPS>(s, blockIdx.x, gridDim.x, red, li, n_items);
+  shrink_mfma_jobs<STEPS>(s, job0, stride, red, li, n_items);
 }
 
 // ---------------------------------------------------------------------------
@@ -2147,8 +2165,10 @@ static int remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *
   int64_t grid = shrink_args(p, mods, n_mods, x, ldx, z, zld, kchunk, 0, a);
   // every workgroup maps the table once: at most two per CU (what the LDS
   // allows at once), each looping over its share of the shrink jobs
-  const int cap = env_int("TCL_FUSED_GRID", 2 * cus());
+  // (plus workgroup 0, which writes the plan and has no shrink job)
+  const int cap = env_int("TCL_FUSED_GRID", 2 * cus() - 1);
   if (grid > cap) grid = cap;
+  grid += 1;
   logf("plan+shrink: T=%d pairs=%d N=%d modules=%d units/item=%d kchunk=%d grid=%lld", p->L.T,
        p->L.NP, p->L.N, n_mods, a.rg_total, kchunk, (long long)grid);
   if (env_int("TCL_SSTEPS", kShrinkSteps) == 16)

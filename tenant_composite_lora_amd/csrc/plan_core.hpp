@@ -243,7 +243,7 @@ __device__ inline PlanView plan_view(const PlanArgs &A, int *lds) {
 // lds must hold 8 NP + G + 6 N ints (16-byte aligned); tmp 3 kSlotInts.
 template <int NT>
 __device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool out, Item *li,
-                                     int li_cap, int *n_items_out) {
+                                     int li_cap, int *n_items_out, bool heads_only = false) {
   const int tid = threadIdx.x;
   const int T = A.T, G = A.G, NP = A.NP, N = A.N;
   *n_items_out = 0;
@@ -393,6 +393,12 @@ __device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool
     }
   }
   __syncthreads();
+  if (heads_only) {
+    // work-item heads only (no plan output): plan_small_item_tokens fills
+    // the token lists of the items a caller needs
+    *n_items_out = n_items;
+    return TCL_OK;
+  }
 
   // ---- D: buckets -----------------------------------------------------------
   int4 ai = make_int4(0, 0, 0, 0);
@@ -458,6 +464,33 @@ __device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool
   return TCL_OK;
 }
 
+// The token ids of work item `item` (its head in li), after plan_run_small
+// ran with heads_only on the same lds: the pairs of the item's adapter, in
+// pair order, each expanded to its group's tokens, are the adapter's tuples
+// in (token, slot) order (a group holds an adapter at most once, and groups
+// are in token order), so a pair's first tuple position is the segment
+// start plus the token counts of the adapter's earlier pairs: one block
+// scan.  Every thread of the workgroup calls it; calls in a row must
+// alternate between two tmp slots (kSlotInts ints each).  The caller
+// synchronises before the token lists are read.
+template <int NT>
+__device__ inline void plan_small_item_tokens(const PlanArgs &A, const int *lds, int *tmp,
+                                              Item *li, int item) {
+  const int tid = threadIdx.x, N = A.N, NP = A.NP;
+  const int4 *ainfo = reinterpret_cast<const int4 *>(lds);
+  const int4 *pinfo = ainfo + N;
+  const int *l_pa = reinterpret_cast<const int *>(pinfo + NP);
+  const int4 h = li[item].head;  // adapter, first tuple, tuples, segment
+  int4 pi = make_int4(0, 0, 0, 0);
+  if (tid < NP && l_pa[tid] == h.x) pi = pinfo[tid];
+  int total;
+  const int off = ainfo[h.x].x + block_excl_scan<NT>(pi.w, tmp, &total);
+  for (int i = 0; i < pi.w; ++i) {
+    const int pos = off + i;
+    if (pos >= h.y && pos < h.y + h.z) li[item].tok[pos - h.y] = pi.z + i;
+  }
+}
+
 // The mapping stage in the calling workgroup of NT threads.  lds: the LDS
 // block of the mode (kPlanLdsInts ints, 4 for PLAN_COUNT_GLOBAL); tmp:
 // 6 * kSlotInts ints of LDS.  out: write the plan (status words, tuples,
@@ -468,11 +501,11 @@ __device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool
 // of work items.  Without out the counting modes compute nothing usable.
 template <int NT, int MODE>
 __device__ inline int plan_run(const PlanArgs &A, int *lds, int *tmp, bool out, Item *li,
-                               int li_cap, int *n_items_out) {
+                               int li_cap, int *n_items_out, bool heads_only = false) {
   constexpr bool direct = MODE == PLAN_DIRECT;
   if constexpr (direct) {
     if (A.G <= NT && A.NP <= NT)
-      return plan_run_small<NT>(A, lds, tmp, out, li, li_cap, n_items_out);
+      return plan_run_small<NT>(A, lds, tmp, out, li, li_cap, n_items_out, heads_only);
   }
   const int tid = threadIdx.x;
   *n_items_out = 0;
