@@ -596,9 +596,6 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
   const bool active = n0 < d;
   TY *Yp = Y + int64_t(t) * ld + n0;
   OutN<TY, CPL> yv;
-  if constexpr (!TILED) {
-    if (active) yv.load(Yp);
-  }
   const int ns = e.tok_n[t];
   const int4 rec = e.tok_rec[int64_t(t) * kSlotPad + lane];
   if constexpr (TILED) {
@@ -642,6 +639,13 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
           const int j = jb + jj;
           if (j < kk[b] && active) bv[b][jj].load(B + (int64_t(aa[b]) * r_max + j) * d + n0);
           else bv[b][jj].zero();
+        }
+        if constexpr (!TILED) {
+          // y right after the first batch's B rows: its latency then
+          // overlaps theirs instead of the slot records' (the memory
+          // counter is in order, so a load issued before the slot records
+          // would be waited for together with them)
+          if (sb == 0 && jb == 0 && b == 0 && active) yv.load(Yp);
         }
         if constexpr (!SPLIT) {
           // one z row per tuple, read as whole vectors
