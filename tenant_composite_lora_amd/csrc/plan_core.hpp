@@ -325,7 +325,9 @@ __device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool
         live = true;
       }
       int dup = 0;
-      for (int q2 = pi.x; q2 < pi.x + pi.y; q2 += 8) {
+      // heads only: no slots, and the table's verdict is the plan writer's
+      // (a table with duplicates or bad weights still yields in-range items)
+      for (int q2 = pi.x; !heads_only && q2 < pi.x + pi.y; q2 += 8) {
         int av[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) av[u] = q2 + u < pi.x + pi.y ? l_pa[q2 + u] : 0;
@@ -339,7 +341,12 @@ __device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool
       if (dup) err |= EB_INVAL;
     }
   }
-  err = block_or<NT>(err, tmp + 1 * kSlotInts) | err_groups;
+  if (heads_only) {
+    __syncthreads();  // the counts are complete
+    err = err_groups;
+  } else {
+    err = block_or<NT>(err, tmp + 1 * kSlotInts) | err_groups;
+  }
   if (err) {
     const int code = (err & EB_INVAL) ? TCL_EINVAL : TCL_EUNSUPPORTED;
     if (out) plan_fail<NT>(A, code, 0);
