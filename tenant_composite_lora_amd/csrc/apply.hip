@@ -332,15 +332,17 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
 // ---------------------------------------------------------------------------
 // decode step: the mapping stage inside the shrink launch
 // ---------------------------------------------------------------------------
-// For tables of the direct mapping mode (every decode batch) every workgroup
-// of the shrink launch first runs the whole mapping stage on its own LDS copy
-// of the table (a few KiB: LDS work, no extra dependent memory round trip),
-// keeps the work items it produced in LDS and then runs its shrink jobs on
-// them; workgroup 0 also writes the plan out for the expand and the host.
-// The work items come out the same in every workgroup (the mapping stage is
-// deterministic), so the jobs split exactly as in shrink_mfma.  A table the
-// mapping stage rejects is left at that: workgroup 0 writes the verdict and
-// no workgroup runs a shrink job.  This takes one launch and the plan's
+// For tables of the direct mapping mode (every decode batch) the mapping
+// stage runs inside the shrink launch, on each workgroup's own LDS copy of
+// the table (a few KiB: LDS work, no extra dependent memory round trip).
+// Workgroup 0 runs all of it and writes the plan out for the expand and the
+// host; it takes no shrink job.  Every other workgroup keeps the work items
+// in LDS and runs its shrink jobs on them: on small tables it stops the
+// mapping stage at the item heads and fills the token lists of its own items
+// only.  The mapping stage is deterministic, so every workgroup derives the
+// same items and the jobs split exactly as in shrink_mfma.  The verdict on
+// the table is workgroup 0's: a rejected table leaves an empty token index,
+// so the expand does nothing.  This takes one launch and the plan's
 // write-then-read round trip off a decode step.
 constexpr int kFusedLdsInts = 12288;  // direct-mode mapping scratch (48 KiB)
 constexpr int kFusedItems = 192;      // work items held in LDS (15 KiB)
@@ -2168,8 +2170,8 @@ static int remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *
   ShrinkArgs a;
   int64_t grid = shrink_args(p, mods, n_mods, x, ldx, z, zld, kchunk, 0, a);
   // every workgroup maps the table once: at most two per CU (what the LDS
-  // allows at once), each looping over its share of the shrink jobs
-  // (plus workgroup 0, which writes the plan and has no shrink job)
+  // allows at once), each looping over its share of the shrink jobs, plus
+  // workgroup 0, which writes the plan and has no shrink job
   const int cap = env_int("TCL_FUSED_GRID", 2 * cus() - 1);
   if (grid > cap) grid = cap;
   grid += 1;

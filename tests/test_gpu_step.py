@@ -1,8 +1,8 @@
 """tcl_remap_apply and tcl_remap_shrink (one step: mapping stage + fused
 apply) against the fp64 oracle.  Decode-sized bf16 batches run the mapping
-stage inside the shrink launch (every workgroup maps the table in LDS, the
-first one also writes the plan); the others run the plain remap + fused
-apply.  The step must match the oracle to the stated tolerance, match the
+stage inside the shrink launch (workgroup 0 maps the table in LDS and
+writes the plan, the others map it up to their work items); the others run
+the plain remap + fused apply.  The step must match the oracle to the stated tolerance, match the
 separate calls bit for bit, leave y untouched for a table the mapping stage
 rejects, and handle consecutive steps with different tables on one plan."""
 import numpy as np
