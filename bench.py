@@ -82,6 +82,7 @@ def kernel_bytes(wl) -> dict:
 KERNEL_SOURCES = {k: ("plan.hip", "plan_core.hpp", "tcl_internal.hpp")
                   for k in ("plan_kernel", "tile_ranges_kernel", "plan_m_local", "plan_m_scan",
                             "plan_m_scatter")}
+KERNEL_SOURCES["gate_topk_kernel"] = ("gate.hip", "tcl_internal.hpp")
 APPLY_SOURCES = ("apply.hip", "plan_core.hpp", "tcl_internal.hpp")
 
 
@@ -133,7 +134,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None)
             for short in ("plan_shrink", "shrink_mfma", "shrink_valu", "expand_kernel_split",
                           "expand_kernel",
                           "expand_staged", "expand_mfma", "plan_kernel", "tile_ranges_kernel",
-                          "plan_m_local", "plan_m_scan", "plan_m_scatter"):
+                          "plan_m_local", "plan_m_scan", "plan_m_scatter", "gate_topk_kernel"):
                 if short in name:
                     per[short].append(v)
                     break

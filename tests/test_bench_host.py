@@ -1,0 +1,81 @@
+"""bench.py's host-side logic without a GPU: the one-GPU rule, the
+algorithmic byte counts and the counter summary."""
+import csv
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+from tenant_composite_lora_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_tiny(bench):
+    """The tiny fp32 workload: 4 adapters of rank 8 on 256 -> 256, 16 tokens:
+    adapters 4 * 8 * (256 + 256) * 4 B, x 16 * 256 * 4 B, y read and written
+    2 * 16 * 256 * 4 B, plus 16 B per tuple."""
+    wl = W.make(1)
+    P = wl.composites.n_tuples()
+    assert bench.algorithmic_bytes(wl) == 65536 + 16384 + 32768 + 16 * P
+    kb = bench.kernel_bytes(wl)
+    assert kb["shrink"] + kb["expand"] + kb["plan"] == bench.algorithmic_bytes(wl)
+
+
+def test_algorithmic_bytes_retained_rank(bench):
+    """Only the retained rows of touched adapters count."""
+    wl = W.random_case(3, T=20, N=6, d_in=64, d_out=32, r_max=8, max_pairs=2, with_k=True)
+    c, m = wl.composites, wl.modules[0]
+    used = np.unique(c.pair_adapter)
+    want = int(m.k[used].sum()) * (64 + 32) * 2 + 20 * 64 * 2 + 2 * 20 * 32 * 4 + 16 * c.n_tuples()
+    assert bench.algorithmic_bytes(wl) == want
+
+
+def _csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerows(rows)
+
+
+def test_pmc_summary_scales_by_the_copy(bench, tmp_path):
+    """Counters are KiB per dispatch, scaled so that the 256 MiB calibration
+    copy reads 256 MiB."""
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    copy_kib = (256 << 20) / 1024
+    _csv(fetch, [["__amd_rocclr_copyBuffer", "FETCH_SIZE", copy_kib / 2],
+                 ["void tcl::plan_shrink<8>(tcl::PlanArgs, tcl::ShrinkArgs)", "FETCH_SIZE", 100.0],
+                 ["void tcl::plan_shrink<8>(tcl::PlanArgs, tcl::ShrinkArgs)", "FETCH_SIZE", 300.0],
+                 ["void tcl::expand_kernel<8, 2, true>(tcl::ExpandArgs)", "FETCH_SIZE", 50.0]])
+    _csv(write, [["__amd_rocclr_copyBuffer", "WRITE_SIZE", copy_kib],
+                 ["void tcl::expand_kernel<8, 2, true>(tcl::ExpandArgs)", "WRITE_SIZE", 10.0]])
+    out = bench.pmc_summary(str(fetch), str(write), "wl")
+    e = out["entries"]["wl:plan_shrink"]
+    assert e["fetch_factor"] == 2.0 and e["launches"] == 2
+    assert e["fetch_bytes_per_launch"] == 200.0 * 1024 * 2
+    x = out["entries"]["wl:expand_kernel"]
+    assert x["write_bytes_per_launch"] == 10.0 * 1024 and x["hbm_bytes_per_launch"] == (50 * 2 + 10) * 1024
+    assert x["source_hash"] == bench.kernel_source_hash("expand_kernel")
+
+
+def test_stored_traffic_unknown_workload(bench):
+    assert bench.stored_traffic("no_such_workload", "plan_shrink") is None
