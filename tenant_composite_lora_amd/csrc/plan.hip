@@ -252,7 +252,7 @@ static size_t lds_max_bytes() { return m_local_lds_bytes(kMultiMaxN); }
 __global__ __launch_bounds__(kMgThreads) void plan_m_local(MArgs A) {
   extern __shared__ __align__(16) int m_lds[];
   const int tid = threadIdx.x, b = blockIdx.x;
-  const int T = A.T, G = A.G, NP = A.NP, N = A.N, NB = A.NB;
+  const int T = A.T, G = A.G, NP = A.NP, N = A.N;
   int *l_pa = m_lds, *l_ptl = l_pa + kMgPairs, *l_grp = l_ptl + kMgPairs;
   int *l_tkt = l_grp + kMgPairs, *l_bkt = l_tkt + kMgPairs, *l_bkw = l_bkt + kMgPairs;
   int *l_cnt = l_bkw + kMgPairs;  // tuples per adapter
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kMgThreads) void plan_m_local(MArgs A) {
     }
     A.d.s_pos[qb0 + i] = r;
   }
-  for (int a = tid; a < N; a += kMgThreads) A.d.m_hist[int64_t(a) * NB + b] = l_cnt[a];
+  for (int a = tid; a < N; a += kMgThreads) A.d.m_hist[int64_t(b) * N + a] = l_cnt[a];
   if (tid == 0) {
     A.d.m_blk[4 * b] = P_b;
     A.d.m_blk[4 * b + 1] = 0;
@@ -435,18 +435,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_m_scan(MArgs A) {
     }
     return;
   }
-  // ---- per adapter: prefix over workgroups (in place) and total; a column
-  //      is NB <= kMultiMaxBlocks ints, read 32 at a time
+  // ---- per adapter: prefix over workgroups (in place) and total.  The
+  //      counts are stored workgroup-major ([NB][N]), so for each workgroup
+  //      the threads read consecutive adapters: 32 coalesced rows at a time
   for (int a = tid; a < N; a += NT) {
-    int32_t *h = A.d.m_hist + int64_t(a) * NB;
+    int32_t *h = A.d.m_hist + a;
     int run = 0;
     for (int b0 = 0; b0 < NB; b0 += 32) {
       int v[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) v[u] = b0 + u < NB ? h[b0 + u] : 0;
+      for (int u = 0; u < 32; ++u) v[u] = b0 + u < NB ? h[int64_t(b0 + u) * N] : 0;
 #pragma unroll
       for (int u = 0; u < 32; ++u) {
-        if (b0 + u < NB) h[b0 + u] = run;
+        if (b0 + u < NB) h[int64_t(b0 + u) * N] = run;
         run += v[u];
       }
     }
@@ -538,7 +539,7 @@ __global__ __launch_bounds__(kMgThreads) void plan_m_scatter(MArgs A) {
     const int a = A.pa[q], s = A.d.s_slot[q], gbase = l_gbase[g];
     const float w = A.pw[q];
     const int sst = A.d.m_sst[a];
-    const int base = sst + A.d.m_hist[int64_t(a) * NB + b] + A.d.s_pos[q];
+    const int base = sst + A.d.m_hist[int64_t(b) * A.N + a] + A.d.s_pos[q];
     const int sg = A.d.s_seg[a], sib = A.d.m_sib[a];
     for (int k = 0; k < tl; ++k) {
       const int p = base + k;

@@ -101,7 +101,8 @@ struct PlanDev {
   int32_t *s_slot, *s_group, *s_pos, *s_gbase, *s_hist;
   int32_t *s_seg;  // counting / multi path: segment index of every touched adapter [N]
   // multi-workgroup path: per-(adapter, workgroup) tuple counts then bases
-  // [N][blocks], per-workgroup {tuples, error bits, tuple base, -} [blocks][4],
+  // [blocks][N] (workgroup-major), per-workgroup {tuples, error bits, tuple
+  // base, -} [blocks][4],
   // per-adapter segment start and first work item [N]
   int32_t *m_hist, *m_blk, *m_sst, *m_sib;
   int2 *ranges;  // [tiles][N]: tuples of segment u whose token lies in tile
