@@ -326,3 +326,90 @@ def adapter_fraction(d_in: int, d_out: int, r: int) -> float:
     """Values of one rank-r adapter (A: d_in x r, B: d_out x r) as a fraction
     of the d_out x d_in base weight it modifies."""
     return (d_in + d_out) * r / (d_in * d_out)
+
+
+# ---------------------------------------------------------------------------
+# retained-rank producer (LoRAForge, approach (2) rank allocation and
+# approach (3) factor construction)
+# ---------------------------------------------------------------------------
+
+def factor_balanced(B_t, A_t):
+    """Balanced factors of one module's update, spectrum first.
+
+    The update is Delta W = B A^T = X Y with X = B (d_out x r, the tall-skinny
+    factor; ``B_t`` holds its columns as rows) and Y = A^T (r x d_in, the rows
+    of ``A_t``).  Following LoRAForge approach (3): a thin QR of X gives R,
+    then H = R Y, and the eigendecomposition of H H^T = U diag(lambda) U^T
+    gives the spectrum, sigma_j = sqrt(lambda_j), largest first.  The balanced
+    factors are F = Q U diag(sigma)^(1/2) and T = diag(sigma)^(-1/2) U^T H, so
+    F T = X Y, F^T F = T T^T = diag(sigma), and the first k columns of F with
+    the first k rows of T are the rank-k truncated SVD of Delta W.
+
+    Directions whose eigenvalue is at most r * 2^-52 times the largest (the
+    rounding level of the r x r eigenproblem) are taken as exactly zero:
+    sigma 0, a zero column of F and a zero row of T.
+
+    Returns (F_t, T, sigma): F_t = F^T (r x d_out, the new B_t rows), T (r x
+    d_in, the new A_t rows), sigma (r,), all float64."""
+    X = widen(B_t).T
+    Y = widen(A_t)
+    r = X.shape[1]
+    # with fewer rows than r (d_out < r) the thin QR has min(d_out, r) rows
+    # of R and the remaining directions are zero
+    Q, R = np.linalg.qr(X, mode="reduced")
+    H = R @ Y
+    lam, U = np.linalg.eigh(H @ H.T)
+    order = np.argsort(-lam, kind="stable")
+    lam, U = lam[order], U[:, order]
+    kq = len(lam)
+    live = lam > r * 2.0 ** -52 * max(lam[0], 0.0)
+    sigma = np.zeros(r)
+    sigma[:kq] = np.where(live, np.sqrt(np.where(live, lam, 1.0)), 0.0)
+    F = np.zeros((X.shape[0], r))
+    T = np.zeros((r, Y.shape[1]))
+    for j in range(kq):
+        if live[j]:
+            F[:, j] = (Q @ U[:, j]) * math.sqrt(sigma[j])
+            T[j, :] = (U[:, j] @ H) / math.sqrt(sigma[j])
+    return F.T.copy(), T, sigma
+
+
+def uniform_ranks(ranks, denominator: int):
+    """LoRAForge-U (LoRAForge, approach (2)): module m keeps
+    u_m = max(1, floor(r_m / d)) of its r_m directions."""
+    return np.array([max(1, int(r) // int(denominator)) for r in ranks], dtype=np.int64)
+
+
+def uniform_budget(ranks, costs, denominator: int) -> int:
+    """The parameter budget P_U of LoRAForge-U: sum over modules of
+    u_m * (d_in + d_out), the values its retained prefixes hold."""
+    u = uniform_ranks(ranks, denominator)
+    return int(sum(int(a) * int(c) for a, c in zip(u, costs)))
+
+
+def spectral_ranks(sigmas, costs, budget: int, floors):
+    """LoRAForge-S (LoRAForge, approach (2)): spend the budget on the
+    directions with the most spectral energy per parameter.
+
+    Module m has singular values sigma_{m,0} >= sigma_{m,1} >= ... and each
+    retained direction costs c_m = d_in + d_out values.  Every module first
+    keeps its floor of l_m directions (capped at its rank).  The remaining
+    directions are then visited by decreasing eta_{m,j} = sigma_{m,j}^2 / c_m
+    (equal ratios: lower module index, then lower j), and a direction is kept
+    when its cost still fits in what is left of the budget.  Since sigma is
+    non-increasing within a module, the kept directions of each module are a
+    prefix.  Returns k_m for every module (int64)."""
+    M = len(sigmas)
+    k = np.array([min(int(floors[m]), len(sigmas[m])) for m in range(M)], dtype=np.int64)
+    left = int(budget) - sum(int(k[m]) * int(costs[m]) for m in range(M))
+    items = []
+    for m in range(M):
+        s = np.asarray(sigmas[m], dtype=np.float64)
+        for j in range(int(k[m]), len(s)):
+            items.append((-(s[j] * s[j]) / float(costs[m]), m, j))
+    items.sort()
+    for _, m, j in items:
+        if j == k[m] and int(costs[m]) <= left:
+            k[m] += 1
+            left -= int(costs[m])
+    return k

@@ -341,6 +341,49 @@ def config5(seed: int = 0, scale_tokens: float = 1.0) -> Workload:
                     n_prefill=n_pre)
 
 
+# --------------------------------------------------------------------------
+# retained-rank producer inputs (LoRAForge, approach (3); the Llama fleet of
+# its Figure 1: 35 adapters, 7840 LoRA matrices = 35 x 32 layers x 7
+# projections)
+# --------------------------------------------------------------------------
+
+# (name, d_in, d_out) of the Llama-3.1-8B projections
+LLAMA31_8B_PROJ = [("q_proj", 4096, 4096), ("k_proj", 4096, 1024), ("v_proj", 4096, 1024),
+                   ("o_proj", 4096, 4096), ("gate_proj", 4096, 14336),
+                   ("up_proj", 4096, 14336), ("down_proj", 14336, 4096)]
+FLEET_ADAPTERS, FLEET_LAYERS, FLEET_RANK = 35, 32, 16
+
+
+def factor_batch(seed: int, M: int, r: int, d_out: int, d_in: int, decay: float = 0.85,
+                 repeated_rows=()):
+    """Synthetic LoRA factors for the producer, bf16 bits: B_t [M, r, d_out]
+    and A_t [M, r, d_in].  A_t rows are N(0, 1/d_in) (the usual
+    initialisation scale of A); B_t row j is N(0, 0.02^2) * decay^j, so the
+    update's spectrum falls off with the direction like a trained adapter's.
+    repeated_rows: B_t rows j that copy row 0, leaving B without full rank."""
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, r, d_in), dtype=np.float32) * np.float32(1.0 / np.sqrt(d_in))
+    B = rng.standard_normal((M, r, d_out), dtype=np.float32) * np.float32(0.02)
+    B *= (np.float32(decay) ** np.arange(r, dtype=np.float32))[None, :, None]
+    for j in repeated_rows:
+        B[:, j] = B[:, 0]
+    return f32_to_bf16_bits(B), f32_to_bf16_bits(A)
+
+
+
+def factor_batch_torch(seed: int, M: int, r: int, d_out: int, d_in: int, device,
+                       decay: float = 0.85):
+    """The recipe of factor_batch drawn with torch's generator on `device`
+    (fleet-sized batches, too large to draw and copy from the host): bf16
+    tensors B_t [M, r, d_out] and A_t [M, r, d_in]."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    A = torch.randn((M, r, d_in), generator=g, device=device) * (1.0 / float(np.sqrt(d_in)))
+    B = torch.randn((M, r, d_out), generator=g, device=device) * 0.02
+    B *= (decay ** torch.arange(r, device=device, dtype=torch.float32))[None, :, None]
+    return B.to(torch.bfloat16), A.to(torch.bfloat16)
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 

@@ -448,7 +448,128 @@ def pin_gate(O):
         assert sorted(a1.tolist()) == sorted(best), trial
 
 
+def pin_factor(O):
+    """Balanced factor construction (LoRAForge, approach (3)) against the
+    library SVD of the explicit product: same singular values, the first k
+    directions give the Eckart-Young truncation for every k, F T = X Y, and
+    F^T F = T T^T = diag(sigma)."""
+    rng = np.random.default_rng(81)
+    for trial, (r, d_out, d_in) in enumerate([(4, 40, 24), (8, 96, 64), (16, 130, 70), (1, 9, 5)]):
+        scale = 0.8 ** np.arange(r)
+        Bt = rng.standard_normal((r, d_out)) * scale[:, None]
+        At = rng.standard_normal((r, d_in))
+        F_t, T, sigma = O.factor_balanced(Bt, At)
+        D = Bt.T @ At
+        U, S, Vt = np.linalg.svd(D)
+        assert np.allclose(sigma, S[:r], rtol=1e-10, atol=0), trial
+        assert np.all(np.diff(sigma) <= 0)
+        assert np.allclose(F_t.T @ T, D, rtol=0, atol=1e-12 * S[0]), trial
+        assert np.allclose(F_t @ F_t.T, np.diag(sigma), rtol=0, atol=1e-12 * S[0]), trial
+        assert np.allclose(T @ T.T, np.diag(sigma), rtol=0, atol=1e-12 * S[0]), trial
+        for k in range(1, r + 1):
+            trunc = (U[:, :k] * S[:k]) @ Vt[:k]
+            assert np.allclose(F_t[:k].T @ T[:k], trunc, rtol=0, atol=1e-11 * S[0]), (trial, k)
+    # closed form: B with orthogonal columns of norms 3, 2 and A with
+    # orthonormal columns give sigma = (3, 2) and balanced factors
+    # sqrt(3) e_0 (x) a_0 and sqrt(2) e_1 (x) a_1, up to the sign of each
+    Bt = np.zeros((2, 5))
+    Bt[0, 0], Bt[1, 1] = 2.0, 3.0
+    At = np.zeros((2, 4))
+    At[0, 2], At[1, 3] = 1.0, 1.0
+    F_t, T, sigma = O.factor_balanced(Bt, At)
+    assert np.allclose(sigma, [3.0, 2.0], rtol=1e-15, atol=0)
+    s0 = np.sign(F_t[0, 1])
+    assert np.allclose(F_t[0] * s0, [0, np.sqrt(3), 0, 0, 0], atol=1e-15)
+    assert np.allclose(T[0] * s0, [0, 0, 0, np.sqrt(3)], atol=1e-15)
+    s1 = np.sign(F_t[1, 0])
+    assert np.allclose(F_t[1] * s1, [np.sqrt(2), 0, 0, 0, 0], atol=1e-15)
+    assert np.allclose(T[1] * s1, [0, 0, np.sqrt(2), 0], atol=1e-15)
+    # rank-deficient B (a repeated column): the dead direction is exactly
+    # zero and the live ones still reproduce the product
+    Bt = rng.standard_normal((4, 30))
+    Bt[3] = Bt[1]
+    At = rng.standard_normal((4, 20))
+    F_t, T, sigma = O.factor_balanced(Bt, At)
+    S = np.linalg.svd(Bt.T @ At, compute_uv=False)
+    assert sigma[3] == 0.0 and not F_t[3].any() and not T[3].any()
+    assert np.allclose(sigma[:3], S[:3], rtol=1e-10, atol=0)
+    assert np.allclose(F_t.T @ T, Bt.T @ At, rtol=0, atol=1e-12 * S[0])
+    # fewer output rows than the rank: the spectrum is the product's, padded
+    # with zeros, and the factors still reproduce it
+    Bt = rng.standard_normal((6, 3))
+    At = rng.standard_normal((6, 10))
+    F_t, T, sigma = O.factor_balanced(Bt, At)
+    S = np.linalg.svd(Bt.T @ At, compute_uv=False)
+    assert F_t.shape == (6, 3) and T.shape == (6, 10)
+    assert np.allclose(sigma[:3], S[:3], rtol=1e-10, atol=0) and not sigma[3:].any()
+    assert np.allclose(F_t.T @ T, Bt.T @ At, rtol=0, atol=1e-12 * S[0])
+    # bf16 bit patterns are widened exactly first
+    bits = (np.arange(12, dtype=np.uint32).reshape(2, 6) * 613 + 0x3f00).astype(np.uint16)
+    a_bits = (np.arange(8, dtype=np.uint32).reshape(2, 4) * 977 + 0x3e80).astype(np.uint16)
+    f1 = O.factor_balanced(bits, a_bits)
+    f2 = O.factor_balanced(O.widen(bits), O.widen(a_bits))
+    assert all(np.array_equal(u, v) for u, v in zip(f1, f2))
+
+
+def pin_rank_allocation(O):
+    """LoRAForge-U and LoRAForge-S (LoRAForge, approach (2)).  U: a worked
+    example.  S: with equal costs the kept directions are the budget's worth
+    of largest sigma^2, which brute force over every prefix choice confirms
+    is the least discarded energy; with unequal costs, a hand-worked
+    example."""
+    assert O.uniform_ranks([16, 8, 12, 4, 24], 12).tolist() == [1, 1, 1, 1, 2]
+    assert O.uniform_ranks([64, 32], 8).tolist() == [8, 4]
+    assert O.uniform_budget([16, 24], [10, 7], 12) == 1 * 10 + 2 * 7
+    from itertools import product
+    rng = np.random.default_rng(83)
+    for trial in range(30):
+        M = int(rng.integers(2, 4))
+        r = [int(rng.integers(1, 5)) for _ in range(M)]
+        sig = [np.sort(rng.random(rm))[::-1] for rm in r]
+        c = 3
+        floors = [int(rng.integers(0, 2)) for _ in range(M)]
+        budget = c * int(rng.integers(sum(floors), sum(r) + 2))
+        k = O.spectral_ranks(sig, [c] * M, budget, floors)
+        best, best_k = None, None
+        for ks in product(*[range(rm + 1) for rm in r]):
+            if any(ks[m] < floors[m] for m in range(M)) or c * sum(ks) > budget:
+                continue
+            lost = sum(float(np.sum(sig[m][ks[m]:] ** 2)) for m in range(M))
+            if best is None or lost < best - 1e-15:
+                best, best_k = lost, ks
+        assert tuple(k.tolist()) == best_k, (trial, k, best_k)
+    # unequal costs by hand: module 0 costs 10 with sigma (4, 3, 1), eta
+    # 1.6, 0.9, 0.1; module 1 costs 4 with sigma (3, 2, 2), eta 2.25, 1.0,
+    # 1.0.  Floors (1, 0), so 10 of the budget is spent first; then the
+    # visiting order is (1,0) (1,1) (1,2) (0,1) (0,2).
+    sg, cs = [[4.0, 3.0, 1.0], [3.0, 2.0, 2.0]], [10, 4]
+    # budget 30: 20 left -> 16, 12, 8; (0,1) needs 10: skipped; (0,2) would
+    # leave a gap
+    assert O.spectral_ranks(sg, cs, 30, [1, 0]).tolist() == [1, 3]
+    # budget 32: 22 left -> 18, 14, 10, (0,1) fits exactly -> 0
+    assert O.spectral_ranks(sg, cs, 32, [1, 0]).tolist() == [2, 3]
+    # budget 41: 31 -> 27, 23, 19, 9; (0,2) needs 10.  Budget 42: all kept
+    assert O.spectral_ranks(sg, cs, 41, [1, 0]).tolist() == [2, 3]
+    assert O.spectral_ranks(sg, cs, 42, [1, 0]).tolist() == [3, 3]
+    # budget 21: 11 -> 7, 3; (1,2) needs 4: skipped
+    assert O.spectral_ranks(sg, cs, 21, [1, 0]).tolist() == [1, 2]
+    # a skipped expensive direction does not stop cheaper ones: with sigma
+    # (4, 3.5) module 0's second direction (eta 1.225) comes before module
+    # 1's (1.0).  Budget 23: 13 left -> (1,0) 9; (0,1) needs 10: skipped;
+    # (1,1) 5; (1,2) 1.  Budget 24: 14 -> 10; (0,1) fits -> 0.
+    sg2 = [[4.0, 3.5], [3.0, 2.0, 2.0]]
+    assert O.spectral_ranks(sg2, cs, 23, [1, 0]).tolist() == [1, 3]
+    assert O.spectral_ranks(sg2, cs, 24, [1, 0]).tolist() == [2, 1]
+    # floors above the budget are kept, and nothing else is
+    k = O.spectral_ranks([[4.0, 3.0], [3.0, 2.0]], [10, 4], 5, [1, 1])
+    assert k.tolist() == [1, 1]
+    # a floor beyond a module's rank keeps all of it
+    k = O.spectral_ranks([[4.0], [3.0, 2.0]], [10, 4], 100, [3, 0])
+    assert k.tolist() == [1, 2]
+
+
 ALL_PINS = [pin_x1_elora_example, pin_x2_dense_premerge, pin_x3_textbook_lora,
             pin_x4_linearity, pin_x5_noop, pin_x6_truncation, pin_x7_rank_bound,
             pin_x8_mapping, pin_x9_adapter_fraction, pin_x10_permutation,
-            pin_split_and_rows, pin_validation, pin_gate]
+            pin_split_and_rows, pin_validation, pin_gate,
+            pin_factor, pin_rank_allocation]

@@ -36,6 +36,22 @@ MUTANTS = {
                       "order = sorted(valid, key=lambda c: (lg[t, c], c))"),
     "gate_padding_kept": ("valid = [c for c in range(cd.shape[1]) if cd[t, c] >= 0]",
                           "valid = [c for c in range(cd.shape[1])]"),
+    "factor_ascending": ('order = np.argsort(-lam, kind="stable")', 'order = np.argsort(lam, kind="stable")'),
+    "factor_unbalanced": ("F[:, j] = (Q @ U[:, j]) * math.sqrt(sigma[j])", "F[:, j] = (Q @ U[:, j]) * sigma[j]"),
+    "factor_h_transposed": ("H = R @ Y", "H = R.T @ Y"),
+    "factor_no_sqrt": ("sigma[:kq] = np.where(live, np.sqrt(np.where(live, lam, 1.0)), 0.0)",
+                       "sigma[:kq] = np.where(live, np.where(live, lam, 1.0), 0.0)"),
+    "factor_tail_not_zero": ("    sigma = np.zeros(r)\n", "    sigma = np.ones(r)\n"),
+    "uniform_ceil": ("max(1, int(r) // int(denominator))", "max(1, -(-int(r) // int(denominator)))"),
+    "uniform_no_min": ("max(1, int(r) // int(denominator))", "max(0, int(r) // int(denominator))"),
+    "spectral_sigma_not_squared": ("items.append((-(s[j] * s[j]) / float(costs[m]), m, j))",
+                                   "items.append((-s[j] / float(costs[m]), m, j))"),
+    "spectral_cost_ignored": ("items.append((-(s[j] * s[j]) / float(costs[m]), m, j))",
+                              "items.append((-(s[j] * s[j]), m, j))"),
+    "spectral_stop_at_first_misfit": ("        if j == k[m] and int(costs[m]) <= left:\n            k[m] += 1\n            left -= int(costs[m])",
+                                      "        if j == k[m] and int(costs[m]) <= left:\n            k[m] += 1\n            left -= int(costs[m])\n        else:\n            break"),
+    "spectral_no_floor": ("k = np.array([min(int(floors[m]), len(sigmas[m])) for m in range(M)], dtype=np.int64)",
+                          "k = np.array([0 for m in range(M)], dtype=np.int64)"),
 }
 
 
