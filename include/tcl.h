@@ -308,6 +308,69 @@ int tcl_gate_topk(const float *logits, int64_t ld_logits, const int32_t *candida
                   int32_t *group_tok_ptr, int32_t *group_pair_ptr, int32_t *pair_adapter,
                   float *pair_alpha, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Retained-rank producer (LoRAForge, approach (2) rank allocation and
+ * approach (3) factor construction; Figure 3 for the batched QR schedule).
+ * ------------------------------------------------------------------------ */
+
+/* Workspace (device bytes) that tcl_factor_balanced needs for a batch of
+ * n_modules modules of shape (d_out, d_in) and rank `rank`.
+ * Errors: TCL_EINVAL (NULL bytes, n_modules outside 0..65535, d_out < 2,
+ * d_in < 8), TCL_EALIGN (d_out odd or d_in not a multiple of 8),
+ * TCL_EUNSUPPORTED (rank outside 1..32). */
+int tcl_factor_workspace_bytes(int32_t n_modules, int32_t d_out, int32_t d_in, int32_t rank,
+                               size_t *bytes);
+
+/* Balanced factors of a batch of LoRA modules, on the GPU.  Module m's
+ * update is Delta W_m = B_m A_m^T with B_t[m] (rank x d_out, row j = column j
+ * of B_m) and A_t[m] (rank x d_in, row j = column j of A_m), bf16, row-major
+ * and contiguous: B_t[(m * rank + j) * d_out + i], A_t[(m * rank + j) * d_in
+ * + i].  Following LoRAForge approach (3): a thin QR of B_m gives R, H = R
+ * A_m^T, the eigendecomposition of H H^T gives the spectrum, and the
+ * balanced factors F = Q U S^(1/2), T = S^(-1/2) U^T H are written in the
+ * same layout as the inputs (device arrays of the caller, bf16):
+ *   F_t[m] (rank x d_out): row j = column j of F, the new B_t rows;
+ *   T[m]   (rank x d_in):  row j of T, the new A_t rows;
+ *   sigma[m * rank + j] (fp32): singular values, largest first.
+ * F T = Delta W, and the first k rows of F_t and T are the rank-k truncated
+ * SVD of Delta W: the ordered prefix that the retained-rank contract of
+ * approach (1) consumes.  Directions whose eigenvalue is at most 2^-23 of
+ * the largest are returned as zero (sigma 0, zero rows).  The QR and the
+ * Gram Y Y^T run in fp32 (bf16 products), the r x r eigenproblem in fp64.
+ * ws: device workspace of at least tcl_factor_workspace_bytes bytes,
+ * 16-byte aligned; its contents need no initialisation.  Asynchronous on
+ * `stream`; n_modules == 0 is a no-op.
+ * Errors: those of tcl_factor_workspace_bytes; TCL_EINVAL (a NULL pointer),
+ * TCL_EALIGN (A_t or ws not 16-byte aligned, B_t, F_t, T or sigma not 4-byte
+ * aligned), TCL_ENOSPC (ws_bytes too small), TCL_EHIP. */
+int tcl_factor_balanced(const void *B_t, const void *A_t, int32_t n_modules, int32_t d_out,
+                        int32_t d_in, int32_t rank, void *F_t, void *T, float *sigma, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/* LoRAForge-U (LoRAForge, approach (2)), on the host: module m keeps
+ * u_out[m] = max(1, floor(ranks[m] / denominator)) directions, and the
+ * parameter budget is *budget_out = sum_m u_out[m] * costs[m], costs[m] =
+ * d_in + d_out of the module.  Host arrays of n_modules entries.
+ * Errors: TCL_EINVAL (NULL pointer, n_modules < 0, denominator < 1, a rank
+ * < 0 or a cost < 1). */
+int tcl_rank_uniform(const int32_t *ranks, const int64_t *costs, int32_t n_modules,
+                     int32_t denominator, int32_t *u_out, int64_t *budget_out);
+
+/* LoRAForge-S (LoRAForge, approach (2)), on the host: spend `budget`
+ * parameters on the directions with the most spectral energy per parameter.
+ * Module m has ranks[m] singular values sigma[m * ld_sigma + j], largest
+ * first, and each kept direction costs costs[m] (= d_in + d_out).  Every
+ * module first keeps min(floors[m], ranks[m]) directions; the remaining ones
+ * are visited by decreasing eta = sigma^2 / cost (computed in fp64; equal
+ * values in the order of module, then direction) and kept when the module's
+ * previous direction is kept and the cost fits in what is left of the
+ * budget.  k_out[m] receives the kept count (a prefix).  Host arrays.
+ * Errors: TCL_EINVAL (NULL pointer, n_modules < 0, a rank < 0 or > ld_sigma,
+ * a cost < 1, a floor < 0, a sigma that is negative or not finite). */
+int tcl_rank_spectral(const double *sigma, int64_t ld_sigma, const int32_t *ranks,
+                      const int64_t *costs, const int32_t *floors, int32_t n_modules,
+                      int64_t budget, int32_t *k_out);
+
 #ifdef __cplusplus
 }
 #endif

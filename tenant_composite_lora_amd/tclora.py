@@ -29,7 +29,8 @@ EXPORTS = ["tcl_last_error", "tcl_version", "tcl_plan_bytes", "tcl_plan_map", "t
            "tcl_plan_status", "tcl_plan_copy_out", "tcl_plan_free", "tcl_module_load_ranks",
            "tcl_workspace_bytes", "tcl_shrink", "tcl_expand", "tcl_fused_apply",
            "tcl_fused_shrink", "tcl_fused_expand", "tcl_remap_apply", "tcl_remap_shrink",
-           "tcl_gate_topk"]
+           "tcl_gate_topk", "tcl_factor_workspace_bytes",
+           "tcl_factor_balanced", "tcl_rank_uniform", "tcl_rank_spectral"]
 
 
 class TclError(RuntimeError):
@@ -92,6 +93,10 @@ def lib(path: Optional[str] = None):
     L.tcl_remap_shrink.argtypes = [vp, ctypes.POINTER(Composites), ctypes.POINTER(ModuleDesc),
                                    i32, ctypes.POINTER(vp), ctypes.POINTER(i64), i32, vp, sz, vp]
     L.tcl_gate_topk.argtypes = [vp, i64, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.tcl_factor_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.tcl_factor_balanced.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.tcl_rank_uniform.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(i64)]
+    L.tcl_rank_spectral.argtypes = [vp, i64, vp, vp, vp, i32, i64, vp]
     if path is None:
         _lib = L
     return L
@@ -392,3 +397,59 @@ def gate_topk(logits: torch.Tensor, candidates: torch.Tensor, k: int, stream=Non
                               ldc, T, C, k, gtp.data_ptr(), gpp.data_ptr(),
                               pa.data_ptr(), pw.data_ptr(), _stream(dev, stream)))
     return gtp, gpp, pa[:T * k], pw[:T * k]
+
+
+def factor_balanced(B_t: torch.Tensor, A_t: torch.Tensor, stream=None):
+    """tcl_factor_balanced: balanced factors of a batch of modules of one
+    shape (LoRAForge, approach (3)).  B_t: bf16 [M, r, d_out] and A_t: bf16
+    [M, r, d_in], contiguous, on one device.  Returns (F_t, T, sigma): the
+    new B_t and A_t rows (bf16, same shapes), directions largest first, and
+    the singular values (fp32 [M, r])."""
+    if B_t.dtype != torch.bfloat16 or A_t.dtype != torch.bfloat16:
+        raise TypeError("factor_balanced: B_t and A_t must be bfloat16")
+    if B_t.dim() != 3 or A_t.dim() != 3 or B_t.shape[:2] != A_t.shape[:2]:
+        raise ValueError("factor_balanced: B_t [M, r, d_out] and A_t [M, r, d_in] expected")
+    if not (B_t.is_contiguous() and A_t.is_contiguous()):
+        raise ValueError("factor_balanced: contiguous tensors expected")
+    M, r, d_out = B_t.shape
+    d_in = A_t.shape[2]
+    L = lib()
+    nb = ctypes.c_size_t()
+    check(L.tcl_factor_workspace_bytes(M, d_out, d_in, r, ctypes.byref(nb)))
+    dev = B_t.device
+    F_t = torch.empty_like(B_t)
+    T = torch.empty_like(A_t)
+    sigma = torch.empty(M, r, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(nb.value, 1), dtype=torch.uint8, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    check(L.tcl_factor_balanced(B_t.data_ptr(), A_t.data_ptr(), M, d_out, d_in, r,
+                                F_t.data_ptr(), T.data_ptr(), sigma.data_ptr(), ws.data_ptr(),
+                                nb.value, int(st.cuda_stream)))
+    return F_t, T, sigma
+
+
+def rank_uniform(ranks, costs, denominator: int):
+    """tcl_rank_uniform (host): LoRAForge-U's kept ranks and budget P_U."""
+    import numpy as np
+    rk = np.ascontiguousarray(ranks, dtype=np.int32)
+    cs = np.ascontiguousarray(costs, dtype=np.int64)
+    u = np.empty(len(rk), dtype=np.int32)
+    b = ctypes.c_int64()
+    check(lib().tcl_rank_uniform(rk.ctypes.data, cs.ctypes.data, len(rk), int(denominator),
+                                 u.ctypes.data, ctypes.byref(b)))
+    return u, int(b.value)
+
+
+def rank_spectral(sigma, ranks, costs, floors, budget: int):
+    """tcl_rank_spectral (host): LoRAForge-S's kept ranks.  sigma: float64
+    [M, ld] (row m's first ranks[m] entries are module m's spectrum)."""
+    import numpy as np
+    sg = np.ascontiguousarray(sigma, dtype=np.float64)
+    rk = np.ascontiguousarray(ranks, dtype=np.int32)
+    cs = np.ascontiguousarray(costs, dtype=np.int64)
+    fl = np.ascontiguousarray(floors, dtype=np.int32)
+    k = np.empty(len(rk), dtype=np.int32)
+    ld = sg.shape[1] if sg.ndim == 2 else 0
+    check(lib().tcl_rank_spectral(sg.ctypes.data, ld, rk.ctypes.data, cs.ctypes.data,
+                                  fl.ctypes.data, len(rk), int(budget), k.ctypes.data))
+    return k
