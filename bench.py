@@ -15,6 +15,12 @@ rank-8 bf16 adapters.
 
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--eager]
+
+``--producer`` times the retained-rank producer instead (LoRAForge, approach
+(2) and (3)): balanced factors of a whole Llama-3.1-8B fleet of 35 adapters x
+32 layers x 7 projections (its Figure 1: 7840 LoRA matrices), rank 16, then
+LoRAForge-S ranks for the LoRAForge-U budget at d = 4 with floor 1 (at
+rank 16, d = 12 keeps one direction per module and the floors spend it all).
 """
 from __future__ import annotations
 
@@ -192,11 +198,158 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
                       f"repeated {reps}x, {t_used:.1f} s, fp64 numpy, 1 BLAS thread"}
 
 
+PRODUCER_METRIC = "retained-rank fleet factor construction, LoRA matrices/s"
+
+
+def producer_alg(classes, r):
+    """Algorithmic bytes and flops of one fleet: every factor read once and
+    every output written once (bf16), sigma written; QR 2 d_out r^2, Gram
+    2 d_in r^2, outputs 2 r^2 (d_out + d_in) flops per module."""
+    b = f = 0
+    for M, d_out, d_in in classes:
+        b += M * (2 * r * (d_out + d_in) * 2 + 4 * r)
+        f += M * (2 * d_out * r * r + 2 * d_in * r * r + 2 * r * r * (d_out + d_in))
+    return b, f
+
+
+def producer_cpu_baseline(classes, r, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle's factor construction on this host, one module of each
+    shape class in turn (fresh inputs from the same recipe), until
+    ``budget_s`` seconds of work; scaled to modules per second."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from tenant_composite_lora_amd import workloads as W
+    ins = [W.factor_batch(90 + i, 1, r, d_out, d_in) for i, (_, d_out, d_in) in enumerate(classes)]
+    n, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_used < budget_s and n < 100000:
+            Bt, At = ins[n % len(ins)]
+            t0 = time.perf_counter()
+            O.factor_balanced(Bt[0], At[0])
+            t_used += time.perf_counter() - t0
+            n += 1
+    return {"value": n / t_used, "unit": "LoRA matrices/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} modules cycling through the {len(classes)} projection shapes "
+                      f"(equal counts; the fleet has 2:2:2:1), {t_used:.1f} s, fp64 numpy, "
+                      f"1 BLAS thread"}
+
+
+def producer_main(args):
+    import torch
+
+    from tenant_composite_lora_amd import tclora
+    from tenant_composite_lora_amd import workloads as W
+    import ctypes
+
+    dev = torch.device("cuda:0")
+    r, nA, nL = W.FLEET_RANK, W.FLEET_ADAPTERS, W.FLEET_LAYERS
+    shapes = {}
+    for name, d_in, d_out in W.LLAMA31_8B_PROJ:
+        shapes.setdefault((d_out, d_in), []).append(name)
+    classes = [(nA * nL * len(v), d_out, d_in) for (d_out, d_in), v in shapes.items()]
+    print(f"[bench] generating the fleet: {classes}", file=sys.stderr, flush=True)
+    L = tclora.lib()
+    st = torch.cuda.Stream(device=dev)
+    bufs = []
+    for i, (M, d_out, d_in) in enumerate(classes):
+        Bt, At = W.factor_batch_torch(100 + i, M, r, d_out, d_in, dev)
+        nb = ctypes.c_size_t()
+        tclora.check(L.tcl_factor_workspace_bytes(M, d_out, d_in, r, ctypes.byref(nb)))
+        bufs.append(dict(M=M, d_out=d_out, d_in=d_in, Bt=Bt, At=At, Ft=torch.empty_like(Bt),
+                         T=torch.empty_like(At),
+                         sg=torch.empty(M, r, dtype=torch.float32, device=dev),
+                         ws=torch.empty(nb.value, dtype=torch.uint8, device=dev), nb=nb.value))
+    torch.cuda.synchronize()
+    sp = int(st.cuda_stream)
+
+    def factor_fleet():
+        for b in bufs:
+            tclora.check(L.tcl_factor_balanced(b["Bt"].data_ptr(), b["At"].data_ptr(), b["M"],
+                                               b["d_out"], b["d_in"], r, b["Ft"].data_ptr(),
+                                               b["T"].data_ptr(), b["sg"].data_ptr(),
+                                               b["ws"].data_ptr(), b["nb"], sp))
+
+    costs = np.concatenate([np.full(b["M"], b["d_out"] + b["d_in"], np.int64) for b in bufs])
+    ranks = np.full(len(costs), r, np.int32)
+    floors = np.ones(len(costs), np.int32)
+    _, budget = tclora.rank_uniform(ranks, costs, 4)
+    sig_host = torch.empty(len(costs), r, dtype=torch.float32, pin_memory=True)
+
+    def allocate():
+        off = 0
+        for b in bufs:
+            sig_host[off:off + b["M"]].copy_(b["sg"], non_blocking=True)
+            off += b["M"]
+        st.synchronize()
+        return tclora.rank_spectral(sig_host.numpy().astype(np.float64), ranks, costs, floors,
+                                    budget)
+
+    K, Wu = max(1, args.steps), max(0, args.warmup)
+    with torch.cuda.stream(st):
+        for _ in range(Wu):
+            factor_fleet()
+            allocate()
+        st.synchronize()
+        # GPU part alone, events on the stream the kernels run on
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(K):
+            factor_fleet()
+        e1.record(st)
+        e1.synchronize()
+        gpu_ms = e0.elapsed_time(e1) / K
+        # the allocation on the host (sigma copied out, LoRAForge-S), alone
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            k = allocate()
+        alloc_ms = (time.perf_counter() - t0) / K * 1e3
+    step_s = gpu_ms * 1e-3
+    n_mod = int(sum(b["M"] for b in bufs))
+    B_alg, F_alg = producer_alg(classes, r)
+    achieved = B_alg / (gpu_ms * 1e-3) / 1e9
+    out = {
+        "metric": PRODUCER_METRIC,
+        "value": n_mod / step_s,
+        "unit": "LoRA matrices/s",
+        "n_gpus": 1, "steps": K, "warmup": Wu,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": f"llama31_8b_fleet_{nA}x{nL}x7_r{r}",
+            "modules": n_mod, "rank": r,
+            "classes": [{"modules": M, "d_out": d_out, "d_in": d_in} for M, d_out, d_in in classes],
+            "factor_gpu_ms": gpu_ms,
+            "allocation_host_ms": alloc_ms,
+            "allocation": "LoRAForge-S on the host (native, fp64), LoRAForge-U budget at d = 4, "
+                          "floor 1; sigma copied out first; not in value",
+            "alg_bytes_per_step": B_alg, "alg_flops_per_step": F_alg,
+            "budget_params": budget, "kept_params": int((k.astype(np.int64) * costs).sum()),
+            "mean_kept_rank": float(k.mean()),
+            "compute": "QR and Gram fp32 (bf16 products), r x r eigenproblem fp64, factors bf16",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "tcl_factor_balanced (tsqr_leaf, gram_kernel, "
+                                      "factor_core, factor_out; timed together)",
+            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = producer_cpu_baseline(classes, r)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2048)
-    ap.add_argument("--warmup", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 2048; 10 with --producer)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default 256; 2 with --producer)")
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--eager", action="store_true", help="no HIP graph capture")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -205,6 +358,8 @@ def main():
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the counter summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--producer", action="store_true",
+                    help="time the retained-rank producer on the Llama fleet instead")
     ap.add_argument("--pmc-into", metavar="JSON",
                     help="with --pmc-summary: merge into this existing summary")
     args = ap.parse_args()
@@ -221,6 +376,13 @@ def main():
               "(one GPU holds one data-parallel shard of the batch)",
               file=sys.stderr)
         sys.exit(2)
+    if args.producer:
+        args.steps = 10 if args.steps is None else args.steps
+        args.warmup = 2 if args.warmup is None else args.warmup
+        producer_main(args)
+        return
+    args.steps = 2048 if args.steps is None else args.steps
+    args.warmup = 256 if args.warmup is None else args.warmup
 
     import torch
 

@@ -6,13 +6,14 @@
 // The balanced factors come from four launches over a batch of modules of
 // one shape:
 //   1. tsqr_leaf    one wave per (module, row tile of X): Householder QR of
-//                   the tile, 128 - RT new rows at a time stacked under the
-//                   running R, in registers (lane i holds rows i and 64 + i).
+//                   the tile, 512 - RT (rank <= 16) or 256 - RT new rows at a
+//                   time stacked under the running R, in registers (lane i
+//                   holds rows i, 64 + i, ...).
 //                   Writes the tile's R.
 //   2. gram_kernel  one wave per (module, column slice of Y): the slice's
 //                   share of G = Y Y^T on the matrix cores (bf16 in, fp32
 //                   accumulation).
-//   3. factor_core  one workgroup per module: merges the tiles' R factors
+//   3. factor_core  one wave per module: merges the tiles' R factors
 //                   (the same Householder pass over two stacked R), then, in
 //                   fp64, H H^T = R G R^T (H = R Y is never formed), a
 //                   parallel cyclic Jacobi eigensolver, the spectrum sorted
@@ -54,8 +55,6 @@ struct FacArgs {
   int M, d_out, d_in, r, P, S, rows_per_leaf, cols_per_split;
 };
 
-__device__ inline float bf16_bits(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
-
 __device__ inline uint16_t to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7f800000u) == 0x7f800000u) return uint16_t((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
@@ -85,38 +84,50 @@ __device__ inline float lane_value(float v, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }
 
-// Householder QR of the 128 rows one wave holds (row `lane` in x0, row
-// 64 + lane in x1; RT columns).  Afterwards rows 0..RT-1 hold the upper
-// triangular R of the rows' span (up to row signs) and every row below is
-// zero.  Column j's reflector is v = x_j - beta e_j over rows >= j with
-// beta = -sign(alpha) |x_j|; v^T x_c is read off the Gram row
+// Householder QR of the 64 * RPL rows one wave holds (row 64 s + lane in
+// x[s]; RT columns).  Afterwards rows 0..RT-1 (x[0] of lanes 0..RT-1) hold
+// the upper triangular R of the rows' span (up to row signs) and every row
+// below is zero.  Column j's reflector is v = x_j - beta e_j over rows >= j
+// with beta = -sign(alpha) |x_j|; v^T x_c is read off the Gram row
 // g_c = sum_{rows >= j} x_j x_c as g_c - beta x[j][c], so each column costs
-// one batch of wave sums.
-template <int RT>
-__device__ inline void hh_pass(float (&x0)[RT], float (&x1)[RT], int lane) {
+// one batch of wave sums whatever the number of rows.
+template <int RT, int RPL>
+__device__ inline void hh_pass(float (&x)[RPL][RT], int lane) {
 #pragma unroll
   for (int j = 0; j < RT; ++j) {
     float g[RT];
 #pragma unroll
-    for (int c = j; c < RT; ++c) g[c] = wave_total((lane >= j ? x0[j] * x0[c] : 0.f) + x1[j] * x1[c]);
+    for (int c = j; c < RT; ++c) {
+      float p = lane >= j ? x[0][j] * x[0][c] : 0.f;
+#pragma unroll
+      for (int sl = 1; sl < RPL; ++sl) p += x[sl][j] * x[sl][c];
+      g[c] = wave_total(p);
+    }
     const float nrm2 = g[j];
     if (nrm2 > 1e-30f) {  // below this the column is zero to fp32 precision
-      const float alpha = lane_value(x0[j], j);
+      const float alpha = lane_value(x[0][j], j);
       const float beta = alpha >= 0.f ? -sqrtf(nrm2) : sqrtf(nrm2);
       const float f = 1.f / (beta * (beta - alpha));
-      const float v0 = lane > j ? x0[j] : (lane == j ? alpha - beta : 0.f);
-      const float v1 = x1[j];
+      float v[RPL];
+      v[0] = lane > j ? x[0][j] : (lane == j ? alpha - beta : 0.f);
+#pragma unroll
+      for (int sl = 1; sl < RPL; ++sl) v[sl] = x[sl][j];
 #pragma unroll
       for (int c = j + 1; c < RT; ++c) {
-        const float w = f * (g[c] - beta * lane_value(x0[c], j));
-        x0[c] -= v0 * w;
-        x1[c] -= v1 * w;
+        const float w = f * (g[c] - beta * lane_value(x[0][c], j));
+#pragma unroll
+        for (int sl = 0; sl < RPL; ++sl) x[sl][c] -= v[sl] * w;
       }
-      x0[j] = lane == j ? beta : (lane > j ? 0.f : x0[j]);
-      x1[j] = 0.f;
+      x[0][j] = lane == j ? beta : (lane > j ? 0.f : x[0][j]);
+#pragma unroll
+      for (int sl = 1; sl < RPL; ++sl) x[sl][j] = 0.f;
     }
   }
 }
+
+// Rows per lane of the leaf pass: 512 rows per wave at rank 16, 256 at 32.
+template <int RT>
+constexpr int leaf_rpl() { return RT <= 16 ? 8 : 4; }
 
 template <int RT>
 __global__ __launch_bounds__(64 * kFacWaves) void tsqr_leaf(FacArgs a) {
@@ -126,28 +137,52 @@ __global__ __launch_bounds__(64 * kFacWaves) void tsqr_leaf(FacArgs a) {
   const int m = job / a.P, l = job - m * a.P;
   const int row0 = l * a.rows_per_leaf, row1 = min(a.d_out, row0 + a.rows_per_leaf);
   const uint16_t *X = a.Bt + int64_t(m) * a.r * a.d_out;  // X[row][c] = X[c * d_out + row]
-  constexpr int kNew = 128 - RT;                          // new rows per pass
-  float x0[RT], x1[RT];
+  constexpr int RPL = leaf_rpl<RT>();
+  constexpr int kNew = 64 * RPL - RT;  // new rows per pass
+  float x[RPL][RT];
 #pragma unroll
-  for (int c = 0; c < RT; ++c) x0[c] = x1[c] = 0.f;
+  for (int sl = 0; sl < RPL; ++sl)
+#pragma unroll
+    for (int c = 0; c < RT; ++c) x[sl][c] = 0.f;
   for (int base = row0; base < row1; base += kNew) {
-    // new row q: q < 64 - RT in x0 of lane RT + q, else in x1 of lane q - (64 - RT)
-    const int g0 = base + lane - RT, g1 = base + lane + 64 - RT;
-    const bool ok0 = lane >= RT && g0 < row1, ok1 = g1 < row1;
+    // new row q: q < 64 - RT in slot 0 of lane RT + q, else in slot
+    // 1 + (q - 64 + RT) / 64 of lane (q - 64 + RT) % 64
+    // every load is issued (indices clamped into the module) and the
+    // invalid ones are replaced afterwards, so the pass waits once for all
+    // of them instead of once per guarded load
+    // (slots 1.. hold only rows the previous pass zeroed, so they take the
+    // loads directly; slot 0 keeps R in lanes < RT and loads into t)
+    uint32_t t[RT];
 #pragma unroll
-    for (int c = 0; c < RT; ++c) {
-      const bool cc = c < a.r;
-      const float v0 = cc && ok0 ? bf16_bits(X[int64_t(c) * a.d_out + g0]) : 0.f;
-      const float v1 = cc && ok1 ? bf16_bits(X[int64_t(c) * a.d_out + g1]) : 0.f;
-      if (lane >= RT) x0[c] = v0;
-      x1[c] = v1;
+    for (int sl = 0; sl < RPL; ++sl) {
+      const int gc = min(max(base + 64 * sl + lane - RT, 0), a.d_out - 1);
+#pragma unroll
+      for (int c = 0; c < RT; ++c) {
+        const uint32_t h = X[int64_t(min(c, a.r - 1)) * a.d_out + gc];
+        if (sl == 0)
+          t[c] = h;
+        else
+          x[sl][c] = __uint_as_float(h << 16);
+      }
     }
-    hh_pass<RT>(x0, x1, lane);
+#pragma unroll
+    for (int sl = 0; sl < RPL; ++sl) {
+      const int g = base + 64 * sl + lane - RT;
+      const bool ok = (sl > 0 || lane >= RT) && g < row1;
+#pragma unroll
+      for (int c = 0; c < RT; ++c) {
+        if (sl == 0)
+          x[0][c] = lane >= RT ? (c < a.r && ok ? __uint_as_float(t[c] << 16) : 0.f) : x[0][c];
+        else
+          x[sl][c] = c < a.r && ok ? x[sl][c] : 0.f;
+      }
+    }
+    hh_pass<RT, RPL>(x, lane);
   }
   if (lane < RT) {
     float *dst = a.leafR + (int64_t(m) * a.P + l) * RT * RT + lane * RT;
 #pragma unroll
-    for (int c = 0; c < RT; ++c) dst[c] = x0[c];
+    for (int c = 0; c < RT; ++c) dst[c] = x[0][c];
   }
 }
 
@@ -174,13 +209,12 @@ __global__ __launch_bounds__(64 * kFacWaves) void gram_kernel(FacArgs a) {
     fbf16x8_t y[NB];
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib) {
+      // clamped, unconditional load (c1 - 8 >= c0 is a valid octet), then zero
       const int row = 16 * ib + r16;
-      if (row < a.r && col < c1) {
-        y[ib] = *reinterpret_cast<const fbf16x8_t *>(Y + int64_t(row) * a.d_in + col);
-      } else {
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        y[ib] = *reinterpret_cast<const fbf16x8_t *>(&z);
-      }
+      uint4 w = *reinterpret_cast<const uint4 *>(Y + int64_t(min(row, a.r - 1)) * a.d_in +
+                                                 min(col, c1 - 8));
+      if (!(row < a.r && col < c1)) w = make_uint4(0, 0, 0, 0);
+      y[ib] = *reinterpret_cast<const fbf16x8_t *>(&w);
     }
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
@@ -211,8 +245,10 @@ __device__ inline void jacobi_pair(int t, int i, int &p, int &q) {
   }
 }
 
+constexpr int kCoreThreads = 64;  // one wave per module: barriers are cheap
+
 template <int RT>
-__global__ __launch_bounds__(256) void factor_core(FacArgs a) {
+__global__ __launch_bounds__(kCoreThreads) void factor_core(FacArgs a) {
   __shared__ double sR[RT][RT + 1], sG[RT][RT + 1], sP[RT][RT + 1], sA[RT][RT + 1], sV[RT][RT + 1];
   __shared__ double rot_c[RT / 2], rot_s[RT / 2], lam[RT];
   __shared__ int perm[RT];
@@ -220,43 +256,43 @@ __global__ __launch_bounds__(256) void factor_core(FacArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int m = blockIdx.x;
 
-  if (tid < 64) {
+  {
     // merge the row tiles' R factors: the running R in rows 0..RT-1, the
-    // next tile's R in rows RT..2RT-1
+    // next tile's R in rows RT..2RT-1 (loads clamped, then selected)
     const float *L = a.leafR + int64_t(m) * a.P * RT * RT;
-    float x0[RT], x1[RT];
+    float x[1][RT];
 #pragma unroll
     for (int c = 0; c < RT; ++c) {
-      x0[c] = lane < RT ? L[lane * RT + c] : 0.f;
-      x1[c] = 0.f;
+      const float v = L[min(lane, RT - 1) * RT + c];
+      x[0][c] = lane < RT ? v : 0.f;
     }
+    const int li = min(max(lane - RT, 0), RT - 1);
     for (int p = 1; p < a.P; ++p) {
 #pragma unroll
       for (int c = 0; c < RT; ++c) {
-        const float v = lane >= RT && lane < 2 * RT ? L[(p * RT + lane - RT) * RT + c] : 0.f;
-        if (lane >= RT) x0[c] = v;
+        const float v = L[(p * RT + li) * RT + c];
+        x[0][c] = lane < RT ? x[0][c] : (lane < 2 * RT ? v : 0.f);
       }
-      hh_pass<RT>(x0, x1, lane);
+      hh_pass<RT, 1>(x, lane);
     }
     if (lane < RT)
 #pragma unroll
-      for (int c = 0; c < RT; ++c) sR[lane][c] = x0[c];
-  } else {
-    for (int e = tid - 64; e < RT * RT; e += 192) {
+      for (int c = 0; c < RT; ++c) sR[lane][c] = x[0][c];
+    for (int e = tid; e < RT * RT; e += kCoreThreads) {
       double g = 0.0;
       for (int s = 0; s < a.S; ++s) g += a.gpart[(int64_t(m) * a.S + s) * RT * RT + e];
       sG[e / RT][e % RT] = g;
     }
   }
   __syncthreads();
-  for (int e = tid; e < RT * RT; e += 256) {  // P = R G
+  for (int e = tid; e < RT * RT; e += kCoreThreads) {  // P = R G
     const int i = e / RT, c = e % RT;
     double v = 0.0;
     for (int k = 0; k < RT; ++k) v += sR[i][k] * sG[k][c];
     sP[i][c] = v;
   }
   __syncthreads();
-  for (int e = tid; e < RT * RT; e += 256) {  // H H^T = P R^T; V = I
+  for (int e = tid; e < RT * RT; e += kCoreThreads) {  // H H^T = P R^T; V = I
     const int i = e / RT, k = e % RT;
     double v = 0.0;
     for (int c = 0; c < RT; ++c) v += sP[i][c] * sR[k][c];
@@ -264,7 +300,7 @@ __global__ __launch_bounds__(256) void factor_core(FacArgs a) {
     sV[i][k] = i == k ? 1.0 : 0.0;
   }
   __syncthreads();
-  for (int e = tid; e < RT * RT; e += 256) {  // exact symmetry
+  for (int e = tid; e < RT * RT; e += kCoreThreads) {  // exact symmetry
     const int i = e / RT, k = e % RT;
     if (i < k) {
       const double v = 0.5 * (sA[i][k] + sA[k][i]);
@@ -284,7 +320,7 @@ __global__ __launch_bounds__(256) void factor_core(FacArgs a) {
         jacobi_pair<RT>(t, tid, p, q);
         const double apq = sA[p][q], app = sA[p][p], aqq = sA[q][q];
         double c = 1.0, s = 0.0;
-        if (apq != 0.0 && fabs(apq) > 1e-17 * sqrt(fabs(app * aqq))) {
+        if (fabs(apq) > 0x1p-52 * sqrt(fabs(app * aqq))) {
           const double tau = (aqq - app) / (2.0 * apq);
           const double tt = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
           c = 1.0 / sqrt(1.0 + tt * tt);
@@ -295,26 +331,31 @@ __global__ __launch_bounds__(256) void factor_core(FacArgs a) {
         rot_s[tid] = s;
       }
       __syncthreads();
-      for (int e = tid; e < RT / 2 * RT; e += 256) {  // rows p and q
-        const int i = e / RT, col = e % RT;
-        int p, q;
-        jacobi_pair<RT>(t, i, p, q);
-        const double c = rot_c[i], s = rot_s[i], ap = sA[p][col], aq = sA[q][col];
-        sA[p][col] = c * ap - s * aq;
-        sA[q][col] = s * ap + c * aq;
+      // J^T A J by 2 x 2 blocks: block (i, k) holds rows (p_i, q_i) and
+      // columns (p_k, q_k); rotating its rows by pair i, then its columns
+      // by pair k, touches no other block.  The rotated pair's own (p, q)
+      // entries are stored as exact zeros.  V <- V J in the same pass.
+      for (int e = tid; e < RT / 2 * RT / 2; e += kCoreThreads) {
+        const int i = e / (RT / 2), k = e % (RT / 2);
+        int pi, qi, pk, qk;
+        jacobi_pair<RT>(t, i, pi, qi);
+        jacobi_pair<RT>(t, k, pk, qk);
+        const double ci = rot_c[i], si = rot_s[i], ck = rot_c[k], sk = rot_s[k];
+        const double a0 = sA[pi][pk], b0 = sA[pi][qk], c0 = sA[qi][pk], d0 = sA[qi][qk];
+        const double a1 = ci * a0 - si * c0, b1 = ci * b0 - si * d0;
+        const double c1 = si * a0 + ci * c0, d1 = si * b0 + ci * d0;
+        sA[pi][pk] = ck * a1 - sk * b1;
+        sA[pi][qk] = i == k ? 0.0 : sk * a1 + ck * b1;
+        sA[qi][pk] = i == k ? 0.0 : ck * c1 - sk * d1;
+        sA[qi][qk] = sk * c1 + ck * d1;
       }
-      __syncthreads();
-      for (int e = tid; e < RT / 2 * RT; e += 256) {  // columns p and q
-        const int i = e / RT, row = e % RT;
-        int p, q;
-        jacobi_pair<RT>(t, i, p, q);
-        const double c = rot_c[i], s = rot_s[i];
-        const double ap = sA[row][p], aq = sA[row][q];
-        sA[row][p] = c * ap - s * aq;
-        sA[row][q] = s * ap + c * aq;
-        const double vp = sV[row][p], vq = sV[row][q];
-        sV[row][p] = c * vp - s * vq;
-        sV[row][q] = s * vp + c * vq;
+      for (int e = tid; e < RT * RT / 2; e += kCoreThreads) {
+        const int row = e / (RT / 2), k = e % (RT / 2);
+        int pk, qk;
+        jacobi_pair<RT>(t, k, pk, qk);
+        const double ck = rot_c[k], sk = rot_s[k], vp = sV[row][pk], vq = sV[row][qk];
+        sV[row][pk] = ck * vp - sk * vq;
+        sV[row][qk] = sk * vp + ck * vq;
       }
       __syncthreads();
     }
@@ -335,7 +376,7 @@ __global__ __launch_bounds__(256) void factor_core(FacArgs a) {
   double lmax = 0.0;
   for (int i = 0; i < RT; ++i) lmax = fmax(lmax, lam[i]);
   float *Mf = a.mats + int64_t(m) * 2 * RT * RT, *Mt = Mf + RT * RT;
-  for (int e = tid; e < RT * RT; e += 256) {
+  for (int e = tid; e < RT * RT; e += kCoreThreads) {
     const int pos = e / RT, c = e % RT, j = perm[pos];
     const double l = lam[j];
     const bool live = lmax > 0.0 && l > 0x1p-23 * lmax;
@@ -373,8 +414,8 @@ __global__ __launch_bounds__(256) void factor_out(FacArgs a) {
   float in0[RT], in1[RT];
 #pragma unroll
   for (int c = 0; c < RT; ++c) {
-    uint32_t w = 0;
-    if (c < a.r) w = *reinterpret_cast<const uint32_t *>(In + int64_t(c) * D + n);
+    uint32_t w = *reinterpret_cast<const uint32_t *>(In + int64_t(min(c, a.r - 1)) * D + n);
+    if (c >= a.r) w = 0;
     in0[c] = __uint_as_float(w << 16);
     in1[c] = __uint_as_float(w & 0xffff0000u);
   }
@@ -408,7 +449,7 @@ int factor_geometry(int32_t M, int32_t d_out, int32_t d_in, int32_t r, FacGeom &
   if (d_out % 2 || d_in % 8)
     return fail(TCL_EALIGN, "factor: d_out must be even and d_in a multiple of 8 (%d, %d)", d_out, d_in);
   g.RT = r <= 16 ? 16 : 32;
-  const int kNew = 128 - g.RT;
+  const int kNew = 64 * (g.RT == 16 ? leaf_rpl<16>() : leaf_rpl<32>()) - g.RT;  // leaf rows per pass
   const int Mm = std::max(M, 1);
   int P = std::max(1, std::min((kLeafWaveTarget + Mm - 1) / Mm, kMaxLeaves));
   P = std::min(P, (d_out + kNew - 1) / kNew);
@@ -435,7 +476,7 @@ void launch_factor(const FacArgs &a, hipStream_t st) {
                      dim3(64 * kFacWaves), 0, st, a);
   hipLaunchKernelGGL(gram_kernel<RT>, dim3(unsigned((gram_waves + kFacWaves - 1) / kFacWaves)),
                      dim3(64 * kFacWaves), 0, st, a);
-  hipLaunchKernelGGL(factor_core<RT>, dim3(a.M), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(factor_core<RT>, dim3(a.M), dim3(kCoreThreads), 0, st, a);
   const int D = std::max(a.d_out, a.d_in);
   hipLaunchKernelGGL(factor_out<RT>, dim3((D / 2 + 255) / 256, a.M, 2), dim3(256), 0, st, a);
 }

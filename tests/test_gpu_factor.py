@@ -11,8 +11,9 @@ may mix, so factors are not compared entry by entry.  Instead:
   perturbation moves every eigenvalue by at most its norm;
 * the rank-k products F_k^T T_k against the oracle's, for k = r and for
   every k in {1, 2, r/2} whose eigenvalue gap is at least 1e-2 lambda_0:
-  relative Frobenius error <= 1e-2.  The factors are stored in bf16 (2^-9
-  relative rounding per entry, about 3e-3 on a product of two), and a gap
+  relative Frobenius error <= 1e-2.  The factors are stored in bf16 (2^-8
+  relative rounding per entry at most, about 3e-3 RMS on a product of two),
+  and a gap
   of 1e-2 lambda_0 keeps the rotation of the truncated subspace near 1e-3;
 * balance: F_t F_t^T and T T^T against diag(sigma), within 1e-2 sigma_0;
 * directions the oracle finds exactly zero are zero (sigma 0, zero rows).
@@ -159,9 +160,15 @@ def test_factor_fleet_shape_sampled():
     # elementwise products and sums only (no batched matrix products)
     lhs = (Ft.double() * (T.double() * v).sum(2)[:, :, None]).sum(1)
     rhs = (Bt.double() * (At.double() * v).sum(2)[:, :, None]).sum(1)
-    rel = (lhs - rhs).norm(dim=1) / rhs.norm(dim=1)
-    print(f"  probe rel max {rel.max().item():.3e}", flush=True)
-    assert rel.max().item() <= 1e-2
+    # each stored factor entry is within 2^-8 (relative; bf16 keeps 8
+    # significant bits) of its fp32 value, so |F^T T v - B A^T v| <= 2^-7
+    # |F|^T (|T| |v|) per entry to first order; twice that leaves room for
+    # the fp32 arithmetic before the rounding
+    bound = (Ft.double().abs() * (T.double().abs() * v.abs()).sum(2)[:, :, None]).sum(1)
+    ratio = ((lhs - rhs).abs() / (2.0 ** -6 * bound + 1e-30)).max().item()
+    rel = ((lhs - rhs).norm(dim=1) / rhs.norm(dim=1)).max().item()
+    print(f"  probe rel max {rel:.3e}, error / bound max {ratio:.3f}", flush=True)
+    assert ratio <= 1.0
     for m in (0, 1117, M - 1):
         _check_module(_bits(Bt[m]), _bits(At[m]), _bits(Ft[m]), _bits(T[m]),
                       sg[m].cpu().numpy(), ("fleet", m))

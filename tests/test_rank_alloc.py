@@ -77,6 +77,7 @@ def test_rank_host_errors():
     s2[1, 2] = -1.0
     with pytest.raises(RuntimeError):
         tclora.rank_spectral(s2, **ok)
+
     with pytest.raises(RuntimeError):
         tclora.rank_uniform([4], [1], 0)
     with pytest.raises(RuntimeError):
