@@ -89,6 +89,10 @@ KERNEL_SOURCES = {k: ("plan.hip", "plan_core.hpp", "tcl_internal.hpp")
                   for k in ("plan_kernel", "tile_ranges_kernel", "plan_m_local", "plan_m_scan",
                             "plan_m_scatter")}
 KERNEL_SOURCES["gate_topk_kernel"] = ("gate.hip", "tcl_internal.hpp")
+# the producer's four kernels are summarised per fleet under the entry point's name
+KERNEL_SOURCES["tcl_factor_balanced"] = ("factor.hip", "tcl_internal.hpp")
+FACTOR_KERNELS = ("tsqr_leaf", "gram_kernel", "factor_core", "factor_out")
+PRODUCER_WORKLOAD = "llama31_8b_fleet_35x32x7_r16"
 APPLY_SOURCES = ("apply.hip", "plan_core.hpp", "tcl_internal.hpp")
 
 
@@ -137,6 +141,9 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None)
             name = r["Kernel_Name"]
             if name.startswith("__amd_rocclr_copyBuffer"):
                 biggest_copy = max(biggest_copy, v)
+            if any(k in name for k in FACTOR_KERNELS):
+                per["tcl_factor_balanced"].append(v)
+                continue
             for short in ("plan_shrink", "shrink_mfma", "shrink_valu", "expand_kernel_split",
                           "expand_kernel",
                           "expand_staged", "expand_mfma", "plan_kernel", "tile_ranges_kernel",
@@ -154,11 +161,13 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None)
     if into and os.path.exists(into):
         out = json.load(open(into))
     for k in sorted(set(f) | set(w)):
-        fb = sum(f[k]) / len(f[k]) * ff if f.get(k) else 0.0
-        wb = sum(w[k]) / len(w[k]) * fw if w.get(k) else 0.0
+        # the producer: one "launch" is one fleet, 4 shapes x 4 kernels
+        per_launch = 16 if k == "tcl_factor_balanced" else 1
+        fb = sum(f[k]) / len(f[k]) * per_launch * ff if f.get(k) else 0.0
+        wb = sum(w[k]) / len(w[k]) * per_launch * fw if w.get(k) else 0.0
         out["entries"][f"{workload}:{k}"] = {
             "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-            "hbm_bytes_per_launch": fb + wb, "launches": len(f.get(k, [])),
+            "hbm_bytes_per_launch": fb + wb, "launches": len(f.get(k, [])) // per_launch,
             "fetch_factor": ff, "write_factor": fw, "source_hash": kernel_source_hash(k)}
     return out
 
@@ -318,7 +327,7 @@ def producer_main(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {
-            "workload": f"llama31_8b_fleet_{nA}x{nL}x7_r{r}",
+            "workload": PRODUCER_WORKLOAD,
             "modules": n_mod, "rank": r,
             "classes": [{"modules": M, "d_out": d_out, "d_in": d_in} for M, d_out, d_in in classes],
             "factor_gpu_ms": gpu_ms,
@@ -334,9 +343,17 @@ def producer_main(args):
             "bound": "hbm", "kernel": "tcl_factor_balanced (tsqr_leaf, gram_kernel, "
                                       "factor_core, factor_out; timed together)",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": stored_traffic(PRODUCER_WORKLOAD, "tcl_factor_balanced"),
         },
     }
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = producer_cpu_baseline(classes, r)
@@ -368,8 +385,8 @@ def main():
                  3: "skewed_decode_llama3_8b_7proj_n128_r8_t64",
                  4: "sparse_prefill_gated_8x256_n128_r16",
                  5: "retained_rank_mixed_n256_r32_t4224"}
-        print(json.dumps(pmc_summary(*args.pmc_summary, names[args.config], args.pmc_into),
-                         indent=1))
+        wname = PRODUCER_WORKLOAD if args.producer else names[args.config]
+        print(json.dumps(pmc_summary(*args.pmc_summary, wname, args.pmc_into), indent=1))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
