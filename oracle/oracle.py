@@ -413,3 +413,117 @@ def spectral_ranks(sigmas, costs, budget: int, floors):
             k[m] += 1
             left -= int(costs[m])
     return k
+
+
+# ---------------------------------------------------------------------------
+# adapter residency and batch choice (DyMerge-LoRA, section 4: BAM and the
+# LAG scheduler)
+# ---------------------------------------------------------------------------
+
+def bam_run(n_slots: int, batches):
+    """Replay batches through BAM, the slot pool that keeps raw adapter
+    factors on the GPU (DyMerge-LoRA, section 4: adapters the running batch
+    uses are pinned, the others leave least recently used first).
+
+    Each batch is a list of adapter ids.  Batch number t (time t):
+      1. its adapters already in a slot are hits: pinned, last use = t;
+      2. each missing adapter, in the batch's order (a repeat counts once),
+         takes the lowest-numbered empty slot, else the slot whose adapter
+         was used longest ago among the slots this batch has not pinned
+         (equal times: the lower slot); it is loaded there, pinned, last
+         use = t;
+      3. if some adapter finds no slot the batch is rejected (status
+         ENOSPC) and the pool is left as it was before the batch.
+    Pins last for the batch only.
+
+    Returns one record per batch: (status, {adapter: slot}, [(slot, loaded
+    adapter, evicted adapter or -1), ...]) and the final slot contents."""
+    slot_ad = [-1] * n_slots
+    last = [-1] * n_slots
+    out = []
+    for t, batch in enumerate(batches):
+        ad_list = []
+        for a in batch:
+            if a not in ad_list:
+                ad_list.append(int(a))
+        s_ad, s_last = list(slot_ad), list(last)
+        pinned = set()
+        where = {}
+        for a in ad_list:
+            if a in s_ad:
+                s = s_ad.index(a)
+                pinned.add(s)
+                s_last[s] = t
+                where[a] = s
+        loads = []
+        ok = True
+        for a in ad_list:
+            if a in where:
+                continue
+            empty = [s for s in range(n_slots) if s_ad[s] == -1]
+            if empty:
+                s = empty[0]
+            else:
+                cand = [s for s in range(n_slots) if s not in pinned]
+                if not cand:
+                    ok = False
+                    break
+                s = min(cand, key=lambda q: (s_last[q], q))
+            loads.append((s, a, s_ad[s]))
+            s_ad[s] = a
+            s_last[s] = t
+            pinned.add(s)
+            where[a] = s
+        if ok:
+            slot_ad, last = s_ad, s_last
+            out.append((OK, where, loads))
+        else:
+            out.append((ENOSPC, {}, []))
+    return out, slot_ad
+
+
+def lag_select(now: float, theta: float, arrival, adapters, resident, max_batch: int,
+               n_slots: int):
+    """The next batch, chosen the LAG way (DyMerge-LoRA, section 4: batch
+    the requests that need the fewest adapters not already resident, and
+    serve requests that have waited longer than theta first, in arrival
+    order).
+
+    Request i arrived at arrival[i] and uses the adapters adapters[i].  A
+    batch holds at most max_batch requests, and the distinct adapters of its
+    requests must fit in n_slots slots.  First the waiting-too-long requests
+    (now - arrival > theta), by arrival (equal: lower index), each taken if
+    it still fits.  Then, while the batch has room, the remaining request
+    with the fewest new loads |L(r) minus (resident + adapters already in the
+    batch)| among those that fit, ties by arrival then index.  Returns the
+    chosen request indices in the order taken."""
+    n = len(arrival)
+    res = set(int(a) for a in resident)
+    chosen = []
+    in_batch = set()
+
+    def fits(i):
+        return len(in_batch | set(int(a) for a in adapters[i])) <= n_slots
+
+    def take(i):
+        chosen.append(i)
+        in_batch.update(int(a) for a in adapters[i])
+
+    old = sorted((i for i in range(n) if now - arrival[i] > theta),
+                 key=lambda i: (arrival[i], i))
+    for i in old:
+        if len(chosen) < max_batch and fits(i):
+            take(i)
+    while len(chosen) < max_batch:
+        best = None
+        for i in range(n):
+            if i in chosen or not fits(i):
+                continue
+            new = len(set(int(a) for a in adapters[i]) - res - in_batch)
+            key = (new, arrival[i], i)
+            if best is None or key < best[0]:
+                best = (key, i)
+        if best is None:
+            break
+        take(best[1])
+    return chosen

@@ -568,8 +568,119 @@ def pin_rank_allocation(O):
     assert k.tolist() == [1, 2]
 
 
+def pin_bam(O):
+    """BAM (DyMerge-LoRA, section 4): a hand-worked replay; residency
+    invariants on a random stream; single-adapter batches reduce to a
+    textbook LRU cache (collections.OrderedDict); enough slots means no
+    evictions."""
+    from collections import OrderedDict
+    # two slots.  t0 [1, 2]: empty slots 0, 1.  t1 [3]: both last used at 0,
+    # the lower slot goes (adapter 1 out).  t2 [1, 4]: 1 takes slot 1 (used
+    # at 0, older than slot 0's 1), then 4 takes slot 0 (3 out).  t3 [5, 6,
+    # 7]: three adapters, two slots: rejected, nothing changes.  t4 [2]:
+    # slots used at 2 and 2: slot 0 (adapter 4) goes.
+    recs, final = O.bam_run(2, [[1, 2], [3], [1, 4], [5, 6, 7], [2]])
+    assert [r[0] for r in recs] == [O.OK, O.OK, O.OK, O.ENOSPC, O.OK]
+    assert recs[0][2] == [(0, 1, -1), (1, 2, -1)]
+    assert recs[1][2] == [(0, 3, 1)]
+    assert recs[2][1] == {1: 1, 4: 0} and recs[2][2] == [(1, 1, 2), (0, 4, 3)]
+    assert recs[3][1] == {} and recs[4][2] == [(0, 2, 4)] and final == [2, 1]
+    # a hit is pinned before any load: [1, 9] with 1 resident never evicts 1
+    recs, _ = O.bam_run(2, [[1], [2], [9, 1]])
+    assert recs[2][1] == {1: 0, 9: 1} and recs[2][2] == [(1, 9, 2)]
+    rng = np.random.default_rng(91)
+    for trial in range(20):
+        S, A = int(rng.integers(1, 6)), int(rng.integers(2, 12))
+        batches = [list(rng.integers(0, A, int(rng.integers(1, 5)))) for _ in range(40)]
+        recs, final = O.bam_run(S, batches)
+        # replay the records to rebuild the pool and check every step
+        pool = [-1] * S
+        for b, (st, where, loads) in zip(batches, recs):
+            distinct = set(int(a) for a in b)
+            before = set(a for a in pool if a >= 0)
+            if st != O.OK:
+                assert len(distinct) > S and where == {} and loads == []
+                continue
+            assert set(where) == distinct
+            assert [ld[1] for ld in loads] == [a for a in dict.fromkeys(int(x) for x in b)
+                                               if a not in before]
+            empty_before = pool.count(-1)
+            for sl, a, ev in loads:
+                assert pool[sl] == ev and ev not in distinct
+                pool[sl] = a
+            assert sum(1 for ld in loads if ld[2] >= 0) == max(0, len(loads) - empty_before)
+            assert all(pool[where[a]] == a for a in distinct)
+            assert len(set(a for a in pool if a >= 0)) == S - pool.count(-1)
+        assert pool == final
+        # single-adapter batches: the textbook LRU cache of S entries
+        seq = [int(x) for x in rng.integers(0, A, 60)]
+        recs, final = O.bam_run(S, [[a] for a in seq])
+        lru = OrderedDict()
+        for a, (st, where, loads) in zip(seq, recs):
+            hit = a in lru
+            evicted = -1
+            if hit:
+                lru.move_to_end(a)
+            else:
+                if len(lru) == S:
+                    evicted = lru.popitem(last=False)[0]
+                lru[a] = True
+            assert st == O.OK
+            assert loads == [] if hit else [ld[1:] for ld in loads] == [(a, evicted)]
+        assert set(a for a in final if a >= 0) == set(lru)
+        # slots for every adapter: nothing is ever evicted
+        recs, _ = O.bam_run(A, batches[:10])
+        assert all(ev == -1 for st, _, loads in recs for _, _, ev in loads)
+
+
+def pin_lag(O):
+    """LAG (DyMerge-LoRA, section 4): hand-worked batches; with every
+    request waiting too long it is FIFO under the slot limit; with every
+    adapter resident it is arrival order; without starvation the first pick
+    has the fewest new loads of all requests (brute force)."""
+    # now 10, theta 5: request 0 (arrived at 0) has waited too long and goes
+    # first; then request 3 needs nothing new (5 is resident), request 2
+    # needs 4, request 1 needs 2 and 3
+    assert O.lag_select(10.0, 5.0, [0, 8, 9, 9.5], [[1], [2, 3], [1, 4], [5]], [1, 5], 2, 4) == [0, 3]
+    assert O.lag_select(10.0, 5.0, [0, 8, 9, 9.5], [[1], [2, 3], [1, 4], [5]], [1, 5], 3, 4) == [0, 3, 2]
+    # an adapter brought in by the batch is free for later picks: after
+    # request 1 loads 2 and 3, request 4 (adapter 3) needs nothing
+    got = O.lag_select(0.0, 9.0, [0, 1, 2, 3, 4], [[7, 8], [2, 3], [6], [5, 4], [3]], [], 3, 8)
+    # fewest new loads: 2 (one), 4 (one; arrival 4 > 2) -> 2 first; then 4
+    # (one: adapter 3), then 1 (one: adapter 2, since 3 is now in the batch)
+    assert got == [2, 4, 1], got
+    # slots limit: a request whose adapters would overflow is skipped
+    assert O.lag_select(0.0, 9.0, [0, 1, 2], [[1, 2, 3], [4], [5]], [], 3, 2) == [1, 2]
+    rng = np.random.default_rng(93)
+    for trial in range(30):
+        n, A = int(rng.integers(1, 9)), int(rng.integers(2, 10))
+        arr = list(np.round(rng.random(n) * 10, 1))
+        ads = [list(set(int(a) for a in rng.integers(0, A, int(rng.integers(1, 4))))) for _ in range(n)]
+        B, S = int(rng.integers(1, 5)), int(rng.integers(1, 6))
+        res = list(set(int(a) for a in rng.integers(0, A, 3)))
+        # every request waiting too long: FIFO, each taken if it fits
+        got = O.lag_select(100.0, -1.0, arr, ads, res, B, S)
+        fifo, inb = [], set()
+        for i in sorted(range(n), key=lambda i: (arr[i], i)):
+            if len(fifo) < B and len(inb | set(ads[i])) <= S:
+                fifo.append(i)
+                inb |= set(ads[i])
+        assert got == fifo, (trial, got, fifo)
+        # every adapter resident and slots for all: arrival order
+        got = O.lag_select(0.0, 1e9, arr, ads, list(range(A)), B, A)
+        assert got == sorted(range(n), key=lambda i: (arr[i], i))[:B]
+        # no starvation: the first pick has the fewest new loads (brute force)
+        got = O.lag_select(0.0, 1e9, arr, ads, res, B, S)
+        feas = [i for i in range(n) if len(ads[i]) <= S]
+        if feas:
+            best = min(len(set(ads[i]) - set(res)) for i in feas)
+            assert len(set(ads[got[0]]) - set(res)) == best
+        assert len(got) <= B and len(set(got)) == len(got)
+        assert len(set(a for i in got for a in ads[i])) <= S
+
+
 ALL_PINS = [pin_x1_elora_example, pin_x2_dense_premerge, pin_x3_textbook_lora,
             pin_x4_linearity, pin_x5_noop, pin_x6_truncation, pin_x7_rank_bound,
             pin_x8_mapping, pin_x9_adapter_fraction, pin_x10_permutation,
             pin_split_and_rows, pin_validation, pin_gate,
-            pin_factor, pin_rank_allocation]
+            pin_factor, pin_rank_allocation, pin_bam, pin_lag]

@@ -52,6 +52,21 @@ MUTANTS = {
                                       "        if j == k[m] and int(costs[m]) <= left:\n            k[m] += 1\n            left -= int(costs[m])\n        else:\n            break"),
     "spectral_no_floor": ("k = np.array([min(int(floors[m]), len(sigmas[m])) for m in range(M)], dtype=np.int64)",
                           "k = np.array([0 for m in range(M)], dtype=np.int64)"),
+    "bam_most_recent": ("s = min(cand, key=lambda q: (s_last[q], q))", "s = max(cand, key=lambda q: (s_last[q], -q))"),
+    "bam_ties_high_slot": ("s = min(cand, key=lambda q: (s_last[q], q))", "s = min(cand, key=lambda q: (s_last[q], -q))"),
+    "bam_no_pins": ("cand = [s for s in range(n_slots) if s not in pinned]", "cand = [s for s in range(n_slots)]"),
+    "bam_hits_not_touched": ("                pinned.add(s)\n                s_last[s] = t\n                where[a] = s",
+                             "                pinned.add(s)\n                where[a] = s"),
+    "bam_no_rollback": ("            out.append((ENOSPC, {}, []))", "            slot_ad, last = s_ad, s_last\n            out.append((ENOSPC, {}, []))"),
+    "lag_ignores_residency": ("new = len(set(int(a) for a in adapters[i]) - res - in_batch)",
+                              "new = len(set(int(a) for a in adapters[i]) - in_batch)"),
+    "lag_ignores_batch": ("new = len(set(int(a) for a in adapters[i]) - res - in_batch)",
+                          "new = len(set(int(a) for a in adapters[i]) - res)"),
+    "lag_starving_by_index": ("key=lambda i: (arrival[i], i))\n    for i in old:", "key=lambda i: i)\n    for i in old:"),
+    "lag_ties_latest": ("key = (new, arrival[i], i)", "key = (new, -arrival[i], i)"),
+    "lag_no_slot_limit": ("        return len(in_batch | set(int(a) for a in adapters[i])) <= n_slots",
+                          "        return True"),
+
 }
 
 
