@@ -371,6 +371,56 @@ int tcl_rank_spectral(const double *sigma, int64_t ld_sigma, const int32_t *rank
                       const int64_t *costs, const int32_t *floors, int32_t n_modules,
                       int64_t budget, int32_t *k_out);
 
+/* ------------------------------------------------------------------------
+ * Adapter residency and batch choice, on the host (DyMerge-LoRA, section 4:
+ * BAM and the LAG scheduler).
+ * ------------------------------------------------------------------------ */
+
+typedef struct tcl_bam tcl_bam;
+
+/* A pool of n_slots adapter slots (BAM), all empty.  The caller owns the
+ * GPU memory of the slots (for instance a [n_slots][r][d] pool per module)
+ * and copies an adapter's factors into its slot when told to load it.
+ * Errors: TCL_EINVAL (out NULL, n_slots < 1). */
+int tcl_bam_create(int32_t n_slots, tcl_bam **out);
+void tcl_bam_free(tcl_bam *bam);
+
+/* Makes the adapters of one batch resident.  adapters[0..n) (ids >= 0,
+ * repeats allowed) are the batch's adapters.  Its adapters already in a slot
+ * are pinned for this call and their last use becomes now (one tick per
+ * call); each missing adapter, in order of first appearance, takes the
+ * lowest-numbered empty slot, else the slot used longest ago among those
+ * not pinned by this batch (equal: the lower slot), and is pinned there.
+ * Output: slot_of[i] = the slot of adapters[i]; load_slot / load_adapter /
+ * load_evicted[0..*n_loads) = the loads the caller must perform, in order
+ * (load_evicted -1 for an empty slot).  Host arrays of n entries each.
+ * Errors: TCL_EINVAL (NULL pointer, n < 0, an id < 0), TCL_ENOSPC (more
+ * distinct adapters than slots: nothing changes, *n_loads = 0; the tick
+ * still advances). */
+int tcl_bam_acquire(tcl_bam *bam, const int32_t *adapters, int32_t n, int32_t *slot_of,
+                    int32_t *load_slot, int32_t *load_adapter, int32_t *load_evicted,
+                    int32_t *n_loads);
+
+/* The adapter in every slot (-1 when empty): n_slots entries. */
+int tcl_bam_slots(const tcl_bam *bam, int32_t *slot_adapter);
+
+/* The next batch, chosen the LAG way.  Request i (of n_requests) arrived at
+ * arrival[i] and uses the adapters req_adapters[req_ptr[i] .. req_ptr[i +
+ * 1]) (ids >= 0, repeats count once).  resident[0..n_resident) are the
+ * adapters now in slots.  A batch holds at most max_batch requests, and the
+ * distinct adapters of its requests must fit in n_slots.  First the requests
+ * with now - arrival > theta, by arrival (equal: lower index), each taken if
+ * it still fits; then, while there is room, the request with the fewest
+ * adapters neither resident nor already in the batch, among those that fit,
+ * ties by arrival then index.  chosen[0..*n_chosen) receives the request
+ * indices in the order taken (room for min(max_batch, n_requests)).
+ * Errors: TCL_EINVAL (NULL pointer, negative sizes, req_ptr not starting at
+ * 0 or decreasing, an id < 0, a NaN time). */
+int tcl_lag_select(const double *arrival, const int32_t *req_ptr, const int32_t *req_adapters,
+                   int32_t n_requests, const int32_t *resident, int32_t n_resident, double now,
+                   double theta, int32_t max_batch, int32_t n_slots, int32_t *chosen,
+                   int32_t *n_chosen);
+
 #ifdef __cplusplus
 }
 #endif

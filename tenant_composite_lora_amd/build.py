@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtclora.so")
-SOURCES = ["plan.hip", "apply.hip", "gate.hip", "factor.hip"]
+SOURCES = ["plan.hip", "apply.hip", "gate.hip", "factor.hip", "sched.cpp"]
 ARCH = os.environ.get("TCL_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU forms are switched off for the device code: the compiler
@@ -39,7 +39,7 @@ def build(verbose: bool = True, jobs: int = 4) -> str:
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmd = [cc, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:

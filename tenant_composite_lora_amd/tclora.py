@@ -30,7 +30,8 @@ EXPORTS = ["tcl_last_error", "tcl_version", "tcl_plan_bytes", "tcl_plan_map", "t
            "tcl_workspace_bytes", "tcl_shrink", "tcl_expand", "tcl_fused_apply",
            "tcl_fused_shrink", "tcl_fused_expand", "tcl_remap_apply", "tcl_remap_shrink",
            "tcl_gate_topk", "tcl_factor_workspace_bytes",
-           "tcl_factor_balanced", "tcl_rank_uniform", "tcl_rank_spectral"]
+           "tcl_factor_balanced", "tcl_rank_uniform", "tcl_rank_spectral",
+           "tcl_bam_create", "tcl_bam_free", "tcl_bam_acquire", "tcl_bam_slots", "tcl_lag_select"]
 
 
 class TclError(RuntimeError):
@@ -97,6 +98,13 @@ def lib(path: Optional[str] = None):
     L.tcl_factor_balanced.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.tcl_rank_uniform.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(i64)]
     L.tcl_rank_spectral.argtypes = [vp, i64, vp, vp, vp, i32, i64, vp]
+    L.tcl_bam_create.argtypes = [i32, ctypes.POINTER(vp)]
+    L.tcl_bam_free.argtypes = [vp]
+    L.tcl_bam_free.restype = None
+    L.tcl_bam_acquire.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
+    L.tcl_bam_slots.argtypes = [vp, vp]
+    L.tcl_lag_select.argtypes = [vp, vp, vp, i32, vp, i32, ctypes.c_double, ctypes.c_double,
+                                 i32, i32, vp, vp]
     if path is None:
         _lib = L
     return L
@@ -453,3 +461,57 @@ def rank_spectral(sigma, ranks, costs, floors, budget: int):
     check(lib().tcl_rank_spectral(sg.ctypes.data, ld, rk.ctypes.data, cs.ctypes.data,
                                   fl.ctypes.data, len(rk), int(budget), k.ctypes.data))
     return k
+
+
+class Bam:
+    """tcl_bam_*: the adapter slot pool (host bookkeeping; the caller copies
+    each loaded adapter into its slot)."""
+
+    def __init__(self, n_slots: int):
+        self.n_slots = int(n_slots)
+        h = ctypes.c_void_p()
+        check(lib().tcl_bam_create(self.n_slots, ctypes.byref(h)))
+        self._h = h
+
+    def acquire(self, adapters):
+        """Returns (slot of each entry, [(slot, loaded adapter, evicted or -1)])."""
+        import numpy as np
+        a = np.ascontiguousarray(adapters, dtype=np.int32)
+        n = len(a)
+        so, ls, la, le = (np.empty(max(n, 1), np.int32) for _ in range(4))
+        nl = ctypes.c_int32()
+        check(lib().tcl_bam_acquire(self._h, a.ctypes.data, n, so.ctypes.data, ls.ctypes.data,
+                                    la.ctypes.data, le.ctypes.data, ctypes.byref(nl)))
+        k = nl.value
+        return so[:n].copy(), list(zip(ls[:k].tolist(), la[:k].tolist(), le[:k].tolist()))
+
+    def slots(self):
+        import numpy as np
+        out = np.empty(self.n_slots, np.int32)
+        check(lib().tcl_bam_slots(self._h, out.ctypes.data))
+        return out
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.tcl_bam_free(h)
+            self._h = None
+
+
+def lag_select(now: float, theta: float, arrival, adapters, resident, max_batch: int,
+               n_slots: int):
+    """tcl_lag_select (host): the chosen request indices, in order."""
+    import numpy as np
+    arr = np.ascontiguousarray(arrival, dtype=np.float64)
+    n = len(arr)
+    ptr = np.zeros(n + 1, np.int32)
+    ptr[1:] = np.cumsum([len(a) for a in adapters]) if n else []
+    flat = np.ascontiguousarray(np.concatenate([np.asarray(a, np.int32) for a in adapters])
+                                if n and ptr[-1] else np.zeros(1, np.int32), dtype=np.int32)
+    res = np.ascontiguousarray(resident, dtype=np.int32) if len(resident) else np.zeros(1, np.int32)
+    out = np.empty(max(1, min(int(max_batch), n)), np.int32)
+    nc = ctypes.c_int32()
+    check(lib().tcl_lag_select(arr.ctypes.data if n else None, ptr.ctypes.data, flat.ctypes.data,
+                               n, res.ctypes.data, len(resident), float(now), float(theta),
+                               int(max_batch), int(n_slots), out.ctypes.data, ctypes.byref(nc)))
+    return out[:nc.value].tolist()
