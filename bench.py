@@ -16,6 +16,9 @@ rank-8 bf16 adapters.
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--eager]
 
+``--scheduler`` times the host-side LAG batch choice and BAM slot assignment
+on a synthetic request stream (no GPU).
+
 ``--producer`` times the retained-rank producer instead (LoRAForge, approach
 (2) and (3)): balanced factors of a whole Llama-3.1-8B fleet of 35 adapters x
 32 layers x 7 projections (its Figure 1: 7840 LoRA matrices), rank 16, then
@@ -360,6 +363,99 @@ def producer_main(args):
     print(json.dumps(out), flush=True)
 
 
+SCHED_METRIC = "LAG batch choice + BAM slot assignment, decisions/s (host)"
+
+
+def sched_stream(seed, steps, A=128, per_step=32, burst=256):
+    """Synthetic request stream standing in for the pages' ShareGPT traces: a
+    burst of `burst` requests, then per_step arrivals per step (as many as a
+    batch holds, so a backlog of about `burst` stays waiting), each a
+    composite of 2-5 distinct adapters drawn Zipf(1.2) over A adapters."""
+    rng = np.random.default_rng(seed)
+    p = 1.0 / np.arange(1, A + 1) ** 1.2
+    p /= p.sum()
+
+    def req():
+        return list(int(a) for a in rng.choice(A, int(rng.integers(2, 6)), replace=False, p=p))
+    return [[req() for _ in range(per_step + (burst if t == 0 else 0))] for t in range(steps)]
+
+
+def sched_replay(stream, select, make_pool, theta, B, S):
+    """Runs the stream: each step adds its arrivals, picks a batch, makes its
+    adapters resident.  Returns (loads per batch, seconds in select+acquire)."""
+    pool = make_pool(S)
+    arr, ads, loads, t_used = [], [], 0, 0.0
+    for step, new in enumerate(stream):
+        for a in new:
+            arr.append(float(step))
+            ads.append(a)
+        t0 = time.perf_counter()
+        res = pool.resident()
+        ch = select(float(step), theta, arr, ads, res, B, S)
+        loads += pool.acquire([a for i in ch for a in ads[i]])
+        t_used += time.perf_counter() - t0
+        chs = set(ch)
+        keep = [i for i in range(len(arr)) if i not in chs]
+        arr, ads = [arr[i] for i in keep], [ads[i] for i in keep]
+    return loads / len(stream), t_used
+
+
+def sched_main(args):
+    from tenant_composite_lora_amd import tclora
+
+    class LibPool:
+        def __init__(self, S):
+            self.b = tclora.Bam(S)
+
+        def resident(self):
+            return [a for a in self.b.slots().tolist() if a >= 0]
+
+        def acquire(self, batch):
+            return len(self.b.acquire(batch)[1])
+
+    steps = args.steps
+    stream = sched_stream(11, steps + args.warmup)
+    B, S, theta = 32, 64, 16.0
+    lag_loads, t = sched_replay(stream, tclora.lag_select, LibPool, theta, B, S)
+    fifo_loads, _ = sched_replay(stream, tclora.lag_select, LibPool, float("-inf"), B, S)
+    n_dec = len(stream)
+    out = {
+        "metric": SCHED_METRIC, "value": n_dec / t, "unit": "decisions/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": t / n_dec * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": "zipf1.2_a128_slots64_batch32_backlog256_theta16",
+                   "adapters": 128, "slots": S, "max_batch": B, "theta_steps": theta,
+                   "arrivals_per_step": 32, "initial_burst": 256,
+                   "composite": "2-5 adapters, Zipf(1.2)",
+                   "loads_per_batch_lag": lag_loads, "loads_per_batch_fifo": fifo_loads,
+                   "timed": "lag_select + bam acquire per step, binding included"},
+        "roofline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+
+        class OraclePool:
+            def __init__(self, S):
+                self.S, self.batches = S, []
+
+            def resident(self):
+                return [a for a in O.bam_run(self.S, self.batches)[1] if a >= 0]
+
+            def acquire(self, batch):
+                self.batches.append(batch)
+                return len(O.bam_run(self.S, self.batches)[0][-1][2])
+
+        sample = stream[:64]
+        o_loads, o_t = sched_replay(sample, O.lag_select, OraclePool, theta, B, S)
+        out["cpu_baseline"] = {"value": len(sample) / o_t, "unit": "decisions/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the first {len(sample)} steps of the same stream "
+                                         f"(the oracle's pool replays its history each step), "
+                                         f"{o_t:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -377,6 +473,8 @@ def main():
                     help="print the counter summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--producer", action="store_true",
                     help="time the retained-rank producer on the Llama fleet instead")
+    ap.add_argument("--scheduler", action="store_true",
+                    help="time the host-side LAG/BAM decisions on a synthetic request stream")
     ap.add_argument("--pmc-into", metavar="JSON",
                     help="with --pmc-summary: merge into this existing summary")
     args = ap.parse_args()
@@ -393,6 +491,11 @@ def main():
               "(one GPU holds one data-parallel shard of the batch)",
               file=sys.stderr)
         sys.exit(2)
+    if args.scheduler:
+        args.steps = 2000 if args.steps is None else args.steps
+        args.warmup = 0 if args.warmup is None else args.warmup
+        sched_main(args)
+        return
     if args.producer:
         args.steps = 10 if args.steps is None else args.steps
         args.warmup = 2 if args.warmup is None else args.warmup
