@@ -274,13 +274,27 @@ def producer_main(args):
                          ws=torch.empty(nb.value, dtype=torch.uint8, device=dev), nb=nb.value))
     torch.cuda.synchronize()
     sp = int(st.cuda_stream)
+    # the four shape batches are independent: each runs on a stream of its
+    # own (default priority), forked from and joined to `st` by events, so a
+    # latency-bound kernel of one batch overlaps the others' streaming ones
+    side = [torch.cuda.Stream(device=dev) for _ in bufs] if not args.one_stream else []
+    fork, joins = torch.cuda.Event(), [torch.cuda.Event() for _ in bufs]
 
     def factor_fleet():
-        for b in bufs:
+        if side:
+            fork.record(st)
+        for i, b in enumerate(bufs):
+            if side:
+                side[i].wait_event(fork)
             tclora.check(L.tcl_factor_balanced(b["Bt"].data_ptr(), b["At"].data_ptr(), b["M"],
                                                b["d_out"], b["d_in"], r, b["Ft"].data_ptr(),
                                                b["T"].data_ptr(), b["sg"].data_ptr(),
-                                               b["ws"].data_ptr(), b["nb"], sp))
+                                               b["ws"].data_ptr(), b["nb"],
+                                               int(side[i].cuda_stream) if side else sp))
+            if side:
+                joins[i].record(side[i])
+        for e in joins if side else []:
+            st.wait_event(e)
 
     costs = np.concatenate([np.full(b["M"], b["d_out"] + b["d_in"], np.int64) for b in bufs])
     ranks = np.full(len(costs), r, np.int32)
@@ -341,6 +355,7 @@ def producer_main(args):
             "budget_params": budget, "kept_params": int((k.astype(np.int64) * costs).sum()),
             "mean_kept_rank": float(k.mean()),
             "compute": "QR and Gram fp32 (bf16 products), r x r eigenproblem fp64, factors bf16",
+            "streams": 1 if args.one_stream else len(bufs),
         },
         "roofline": {
             "bound": "hbm", "kernel": "tcl_factor_balanced (tsqr_leaf, gram_kernel, "
@@ -473,6 +488,8 @@ def main():
                     help="print the counter summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--producer", action="store_true",
                     help="time the retained-rank producer on the Llama fleet instead")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="with --producer: the four shape batches in sequence on one stream")
     ap.add_argument("--scheduler", action="store_true",
                     help="time the host-side LAG/BAM decisions on a synthetic request stream")
     ap.add_argument("--pmc-into", metavar="JSON",
