@@ -79,3 +79,53 @@ def test_pmc_summary_scales_by_the_copy(bench, tmp_path):
 
 def test_stored_traffic_unknown_workload(bench):
     assert bench.stored_traffic("no_such_workload", "plan_shrink") is None
+
+
+def test_producer_algorithmic_bytes():
+    """Every factor read once and every output written once, bf16, plus
+    sigma: for the Llama fleet at rank 16, 2 * 2.94 GB."""
+    import bench
+    classes = [(2240, 4096, 4096), (2240, 1024, 4096), (2240, 14336, 4096), (1120, 4096, 14336)]
+    b, f = bench.producer_alg(classes, 16)
+    per_adapter_layer = sum(d_in + d_out for _, d_in, d_out in
+                            [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024),
+                             ("o", 4096, 4096), ("g", 4096, 14336), ("u", 4096, 14336),
+                             ("d", 14336, 4096)])
+    n = 35 * 32
+    assert b == n * per_adapter_layer * 16 * 2 * 2 + 7840 * 16 * 4
+    assert f == sum(M * 4 * 16 * 16 * (d_out + d_in) for M, d_out, d_in in classes)
+
+
+def test_scheduler_replay_library_matches_oracle():
+    """The scheduler leg's replay gives the same loads through the library
+    and through the oracle on a short stream."""
+    import bench
+    import oracle as O
+    from tenant_composite_lora_amd import tclora
+
+    class LibPool:
+        def __init__(self, S):
+            self.b = tclora.Bam(S)
+
+        def resident(self):
+            return [a for a in self.b.slots().tolist() if a >= 0]
+
+        def acquire(self, batch):
+            return len(self.b.acquire(batch)[1])
+
+    class OraclePool:
+        def __init__(self, S):
+            self.S, self.batches = S, []
+
+        def resident(self):
+            return [a for a in O.bam_run(self.S, self.batches)[1] if a >= 0]
+
+        def acquire(self, batch):
+            self.batches.append(batch)
+            return len(O.bam_run(self.S, self.batches)[0][-1][2])
+
+    stream = bench.sched_stream(3, 12, A=40, per_step=8, burst=30)
+    for theta in (4.0, float("-inf")):
+        lib_loads, _ = bench.sched_replay(stream, tclora.lag_select, LibPool, theta, 8, 16)
+        ora_loads, _ = bench.sched_replay(stream, O.lag_select, OraclePool, theta, 8, 16)
+        assert lib_loads == ora_loads
