@@ -329,6 +329,132 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
   shrink_mfma_jobs<STEPS>(s, blockIdx.x, gridDim.x, red);
 }
 
+// Item pairs: one job takes work items 2q and 2q + 1 of one (rank tile, K
+// chunk, module) unit.  When both belong to the same adapter (consecutive
+// items of one segment) they share every A-row load and run two matrix-core
+// accumulators, one per item; otherwise the items run one after the other.
+// Each accumulator sees the same K steps in the same order as in
+// shrink_mfma_jobs, and the wave partials are summed in the same wave order,
+// so z is bit for bit that of shrink_mfma.  Half as many jobs, and half the A
+// rows moved into the compute units, for prefill batches whose segments span
+// several items.
+template <int STEPS>
+__device__ inline void shrink_pair_body(const ShrinkArgs &s, int rgg, int4 h0, int tok0,
+                                        bool two, int4 h1, int tok1, f32x4_t (*red)[64]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  int mi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMods; ++i)
+    if (i < s.n_mods && rgg >= s.m[i].first) mi = i;
+  const int first = s.m[mi].first, dd = s.m[mi].d, r_max = s.m[mi].r_max, zld = s.m[mi].zld;
+  const int nkc = s.m[mi].nkc, kchunk = s.m[mi].kchunk;
+  const int64_t ld = s.m[mi].ld;
+  const bf16_t *Aw = static_cast<const bf16_t *>(s.m[mi].W);
+  const bf16_t *Xw = static_cast<const bf16_t *>(s.m[mi].io);
+  const int unit = rgg - first;
+  const int rt = unit / nkc, kc = unit - rt * nkc;
+  const int zstride = s.m[mi].zstride;
+  float *Z = s.m[mi].z + kc * zld;
+  const int j0 = rt * 16;
+  const int a = h0.x;
+  const int k = eff_rank(s.m[mi].k_dev, a, r_max);
+  const int n0 = h0.z, n1 = two ? h1.z : 0;
+  if (j0 >= k) {
+    if (s.zero_tail && w == 0) {
+      const int j = j0 + row;
+      if (j < r_max) {
+        for (int tt = kg; tt < n0; tt += 4) Z[int64_t(h0.y + tt) * zstride + j] = 0.f;
+        for (int tt = kg; tt < n1; tt += 4) Z[int64_t(h1.y + tt) * zstride + j] = 0.f;
+      }
+    }
+    return;
+  }
+  const int jr = j0 + row;
+  const bf16_t *X0 = row < n0 ? Xw + int64_t(tok0) * ld + kg * 8 : nullptr;
+  const bf16_t *X1 = row < n1 ? Xw + int64_t(tok1) * ld + kg * 8 : nullptr;
+  const bf16_t *Ar = jr < k ? Aw + (int64_t(a) * r_max + jr) * dd + kg * 8 : nullptr;
+  const int c0 = kc * (kchunk / 32), c1 = min((dd + 31) / 32, c0 + kchunk / 32);
+  const int per = (c1 - c0 + kShrinkWaves - 1) / kShrinkWaves;
+  const int s0 = c0 + w * per, s1 = min(c1, s0 + per);
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int st = s0; st < s1; st += STEPS) {
+    bf16x8_t xv0[STEPS], xv1[STEPS], av[STEPS];
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      const int e0 = (st + u) * 32 + kg * 8;
+      const bool in = st + u < s1 && e0 < dd;
+      uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0), ab = make_uint4(0, 0, 0, 0);
+      if (in && Ar) ab = *reinterpret_cast<const uint4 *>(Ar + (st + u) * 32);
+      if (in && X0) x0 = *reinterpret_cast<const uint4 *>(X0 + (st + u) * 32);
+      if (in && X1) x1 = *reinterpret_cast<const uint4 *>(X1 + (st + u) * 32);
+      xv0[u] = __builtin_bit_cast(bf16x8_t, x0);
+      xv1[u] = __builtin_bit_cast(bf16x8_t, x1);
+      av[u] = __builtin_bit_cast(bf16x8_t, ab);
+    }
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv0[u], av[u], acc0, 0, 0, 0);
+      if (two) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv1[u], av[u], acc1, 0, 0, 0);
+    }
+  }
+  red[w][lane] = acc0;
+  red[kShrinkWaves + w][lane] = acc1;
+  __syncthreads();
+  // wave 0 finishes the first item, wave 1 the second
+  if (w < (two ? 2 : 1)) {
+    const int base = w * kShrinkWaves, p0 = w ? h1.y : h0.y, nt = w ? n1 : n0;
+    f32x4_t sum = red[base][lane];
+#pragma unroll
+    for (int v = 1; v < kShrinkWaves; ++v) {
+      const f32x4_t o = red[base + v][lane];
+      sum[0] += o[0];
+      sum[1] += o[1];
+      sum[2] += o[2];
+      sum[3] += o[3];
+    }
+    const int j = j0 + row;
+    if (j < r_max) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = 4 * kg + i;
+        if (tt < nt) {
+          if (j < k) Z[int64_t(p0 + tt) * zstride + j] = sum[i];
+          else if (s.zero_tail) Z[int64_t(p0 + tt) * zstride + j] = 0.f;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int STEPS>
+__global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma_pair(ShrinkArgs s) {
+  __shared__ f32x4_t red[2 * kShrinkWaves][64];
+  const int row = threadIdx.x & 15;
+  const int n_items = min(s.status[ST_ITEMS], s.items_cap);
+  const int total = (n_items + 1) / 2 * s.rg_total;
+  for (int job = blockIdx.x; job < total; job += gridDim.x) {
+    const int q = job / s.rg_total, rgg = job - q * s.rg_total;
+    const int i0 = 2 * q, i1 = 2 * q + 1;
+    const int4 h0 = s.items[i0].head;
+    const int t0 = s.items[i0].tok[row];
+    const bool has1 = i1 < n_items;
+    int4 h1 = h0;
+    int t1 = t0;
+    if (has1) {
+      h1 = s.items[i1].head;
+      t1 = s.items[i1].tok[row];
+    }
+    if (has1 && h1.x == h0.x) {
+      shrink_pair_body<STEPS>(s, rgg, h0, t0, true, h1, t1, red);
+    } else {
+      shrink_pair_body<STEPS>(s, rgg, h0, t0, false, h0, t0, red);
+      if (has1) shrink_pair_body<STEPS>(s, rgg, h1, t1, false, h1, t1, red);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // decode step: the mapping stage inside the shrink launch
 // ---------------------------------------------------------------------------
@@ -1537,6 +1663,18 @@ static int env_int(const char *name, int dflt) {
   return (s && *s) ? std::atoi(s) : dflt;
 }
 
+// Compute units of the current device (256 when the query fails).
+static int cus() {
+  static const int n = [] {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+      c = 256;
+    return c;
+  }();
+  return n;
+}
+
 static int shrink_kchunk(const tcl_plan *p, const tcl_module *mods, int n) {
   if (mods[0].wdtype != TCL_BF16) return 1 << 30;
   int kchunk;
@@ -1620,7 +1758,23 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
   // K steps in flight per lane: 8 (95 VGPRs, two workgroups per CU) measured
   // faster than 16 (161 VGPRs, one per CU); TCL_SSTEPS=16 forces the deeper one
   const int steps = env_int("TCL_SSTEPS", kShrinkSteps) == 16 ? 16 : 8;
-  if (bf && steps == 8)
+  // Item pairs when the paired launch still has at least two rounds of
+  // resident workgroups (1024 jobs: 2 per CU, twice over): measured on the
+  // retained-rank batch 156.9 -> 142.6 us; with fewer jobs the CUs run short
+  // of work (sparse prefill, 386 pair jobs: 26.2 -> 29.3 us).
+  // TCL_SHRINK_PAIR=0/1 forces; TCL_PSTEPS=8 puts 8 K steps in flight, not 4
+  // (slower on both).
+  int64_t pg = (int64_t(p->L.items_cap) + 1) / 2 * a.rg_total;
+  const int pair_env = env_int("TCL_SHRINK_PAIR", -1);
+  const bool pair = pair_env == 1 || (pair_env != 0 && pg >= 4 * int64_t(cus()));
+  if (bf && pair) {
+    if (pg > 32768) pg = 32768;
+    if (pg < 1) pg = 1;
+    if (env_int("TCL_PSTEPS", 4) == 8)
+      hipLaunchKernelGGL(shrink_mfma_pair<8>, dim3(int(pg)), dim3(64 * kShrinkWaves), 0, s, a);
+    else
+      hipLaunchKernelGGL(shrink_mfma_pair<4>, dim3(int(pg)), dim3(64 * kShrinkWaves), 0, s, a);
+  } else if (bf && steps == 8)
     hipLaunchKernelGGL(shrink_mfma<8>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
   else if (bf)
     hipLaunchKernelGGL(shrink_mfma<16>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
@@ -2130,17 +2284,6 @@ int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
   return run_fused(p, mods, n_mods, x, ldx, y, ldy, yd, ws, s);
 }
 
-// Compute units of the current device (256 when the query fails).
-static int cus() {
-  static const int n = [] {
-    int dev = 0, c = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
-      c = 256;
-    return c;
-  }();
-  return n;
-}
 
 // The decode step's shrink with the mapping stage inside (plan_shrink):
 // direct-mode tables whose LDS view and work items fit the kernel's budget,
