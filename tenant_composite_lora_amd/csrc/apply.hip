@@ -1942,12 +1942,13 @@ static int launch_expand_valu(const tcl_plan *p, const tcl_module *mods, int n,
   e.tcount = tcount;
   e.tiles = p->L.tiles;
   e.min_tok = min_tok;
-  // jobs per workgroup: four for prefill-sized launches of ranks up to 16
-  // (measured faster there: sparse prefill 148 -> 141 us), one otherwise (four
-  // measured slower for rank 32: retained-rank batch 870 -> 1001 us);
-  // TCL_EWAVES=1/4 forces
+  // jobs per workgroup: four for launches of at least 4096 jobs of ranks up
+  // to 16 (measured faster: sparse prefill 148 -> 141 us, 7-projection decode
+  // step 38.6 -> 37.5 us), one otherwise (four measured slower for rank 32:
+  // retained-rank batch 1037 -> 1206 us; and on the 1024-job decode batch,
+  // 14.99 -> 15.05 us); TCL_EWAVES=1/4 forces
   const int ew = env_int("TCL_EWAVES", 0);
-  const int waves = ew == 1 || ew == 4 ? ew : (e.jobs >= 32768 && R <= 16 ? 4 : 1);
+  const int waves = ew == 1 || ew == 4 ? ew : (e.jobs >= 4096 && R <= 16 ? 4 : 1);
   logf("expand(valu): modules=%d R=%d cpl=%d jobs=%d waves/workgroup=%d", n, R, cpl, e.jobs,
        waves);
   const bool bf = mods[0].wdtype == TCL_BF16;
