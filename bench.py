@@ -89,8 +89,8 @@ def kernel_bytes(wl) -> dict:
 # HIP sources each kernel is built from: a stored counter summary is only
 # valid while these are unchanged
 KERNEL_SOURCES = {k: ("plan.hip", "plan_core.hpp", "tcl_internal.hpp")
-                  for k in ("plan_kernel", "tile_ranges_kernel", "plan_m_local", "plan_m_scan",
-                            "plan_m_scatter")}
+                  for k in ("plan_kernel", "tile_ranges_kernel", "tile_ranges_tok_kernel",
+                            "plan_m_local", "plan_m_scan", "plan_m_scatter")}
 KERNEL_SOURCES["gate_topk_kernel"] = ("gate.hip", "tcl_internal.hpp")
 # the producer's four kernels are summarised per fleet under the entry point's name
 KERNEL_SOURCES["tcl_factor_balanced"] = ("factor.hip", "tcl_internal.hpp")
@@ -150,6 +150,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None)
             for short in ("plan_shrink", "shrink_mfma", "shrink_valu", "expand_kernel_split",
                           "expand_kernel",
                           "expand_staged", "expand_mfma", "plan_kernel", "tile_ranges_kernel",
+                          "tile_ranges_tok_kernel",
                           "plan_m_local", "plan_m_scan", "plan_m_scatter", "gate_topk_kernel"):
                 if short in name:
                     per[short].append(v)

@@ -219,6 +219,64 @@ __global__ __launch_bounds__(256) void tile_ranges_kernel(PlanDev d, int32_t N) 
     d.tcount[tile] = make_int2(red[0] + red[1] + red[2] + red[3], red[4] + red[5] + red[6] + red[7]);
 }
 
+// The same ranges and totals from the token index, for pools of at most
+// kRangesLdsN adapters.  The tuples of a tile are the slot records of its
+// tokens, and each record names its tuple and its segment; a segment's tuples
+// are in token order, so those that fall in the tile are consecutive and
+// their run is [least tuple, greatest tuple + 1).  Four threads per token
+// take its records (two dependent loads: the slot count, then the records)
+// and fold the tuple indices into per-segment minima and maxima in LDS;
+// integer minima and maxima do not depend on the order of the updates.  A
+// segment without tuples in the tile gets the empty run (0, 0), which every
+// reader treats like any other empty run.
+constexpr int kRangesLdsN = 4096;
+static_assert(kXTok * 4 == 256, "four threads per token of a tile");
+
+__global__ __launch_bounds__(256) void tile_ranges_tok_kernel(PlanDev d, int32_t N, int32_t T) {
+  __shared__ int lo_s[kRangesLdsN], hi_s[kRangesLdsN];
+  __shared__ int red[8];
+  const int tile = blockIdx.x, tid = threadIdx.x;
+  const bool ok = d.status[ST_CODE] == TCL_OK;
+  const int U = ok ? min(d.status[ST_SEGMENTS], min(N, kRangesLdsN)) : 0;
+  for (int u = tid; u < U; u += 256) {
+    lo_s[u] = 0x7fffffff;
+    hi_s[u] = -1;
+  }
+  __syncthreads();
+  int tup = 0;
+  const int t = tile * kXTok + (tid >> 2);
+  if (ok && t < T) {
+    const int ns = min(d.tok_n[t], kSlotPad);
+    for (int sl = tid & 3; sl < ns; sl += 4) {
+      const int4 r = d.tok_rec[int64_t(t) * kSlotPad + sl];
+      if (r.w >= 0 && r.w < U) {
+        atomicMin(&lo_s[r.w], r.x);
+        atomicMax(&hi_s[r.w], r.x);
+        ++tup;
+      }
+    }
+  }
+  __syncthreads();
+  int nseg = 0;
+  for (int u = tid; u < U; u += 256) {
+    const int lo = lo_s[u], hi = hi_s[u];
+    d.ranges[int64_t(tile) * N + u] = hi >= 0 ? make_int2(lo, hi + 1) : make_int2(0, 0);
+    nseg += hi >= 0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    tup += __shfl_xor(tup, off, 64);
+    nseg += __shfl_xor(nseg, off, 64);
+  }
+  if ((tid & 63) == 0) {
+    red[tid >> 6] = tup;
+    red[4 + (tid >> 6)] = nseg;
+  }
+  __syncthreads();
+  if (tid == 0)
+    d.tcount[tile] = make_int2(red[0] + red[1] + red[2] + red[3], red[4] + red[5] + red[6] + red[7]);
+}
+
 // ---------------------------------------------------------------------------
 // mapping of larger tables over many workgroups (PLAN_MULTI)
 // ---------------------------------------------------------------------------
@@ -706,7 +764,14 @@ int plan_launch(tcl_plan *p, const tcl_composites *c, hipStream_t s) { return la
 
 int plan_prepare_ranges(const tcl_plan *p, hipStream_t s) {
   if (p->ranges_ready || p->L.tiles == 0) return TCL_OK;
-  hipLaunchKernelGGL(tile_ranges_kernel, dim3(p->L.tiles), dim3(256), 0, s, p->d, p->L.N);
+  // from the token index where the pool fits the LDS tables
+  // (TCL_RANGES_TOK=0 keeps the binary searches)
+  const char *e = std::getenv("TCL_RANGES_TOK");
+  if (p->L.N <= kRangesLdsN && !(e && !std::strcmp(e, "0")))
+    hipLaunchKernelGGL(tile_ranges_tok_kernel, dim3(p->L.tiles), dim3(256), 0, s, p->d, p->L.N,
+                       p->L.T);
+  else
+    hipLaunchKernelGGL(tile_ranges_kernel, dim3(p->L.tiles), dim3(256), 0, s, p->d, p->L.N);
   TCL_HIP(hipGetLastError());
   p->ranges_ready = true;
   return TCL_OK;

@@ -200,3 +200,28 @@ def test_mfma_rejected_plan_is_noop(monkeypatch):
     tclora.fused_apply(plan, [mod], [x], [y])
     torch.cuda.synchronize()
     assert torch.equal(y, y0)
+
+
+@pytest.mark.parametrize("name", ["config4", "mx_windows", "mx_mixed", "mx_empty",
+                                  "mfma_many_adapters", "mx_requests"])
+@pytest.mark.parametrize("dispatch", [None, "mfma"])
+def test_tile_ranges_from_token_index(name, dispatch, monkeypatch):
+    """Per-tile tuple ranges and totals from the token index (the default for
+    pools of up to 4096 adapters) against the binary searches over each
+    segment (TCL_RANGES_TOK=0): y bit for bit, under the automatic dispatch
+    (which splits tiles by the totals) and with every tile on the matrix
+    cores."""
+    wl = _case(name)
+    banner(f"tile ranges from the token index {name}, dispatch {dispatch}")
+    monkeypatch.delenv("TCL_KCHUNK", raising=False)
+    if dispatch is None:
+        monkeypatch.delenv("TCL_DISPATCH", raising=False)
+    else:
+        monkeypatch.setenv("TCL_DISPATCH", dispatch)
+    monkeypatch.setenv("TCL_RANGES_TOK", "0")
+    ys0, _, _ = run_fused(wl)
+    monkeypatch.delenv("TCL_RANGES_TOK", raising=False)
+    ys1, _, _ = run_fused(wl)
+    for a, b in zip(ys0, ys1):
+        assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+    _check(wl, ys1, "ranges")
