@@ -109,7 +109,7 @@ def test_pair_rejected_plan_is_noop(monkeypatch):
     assert torch.equal(y, y0)
 
 
-def test_pair_config5_full_size_bitwise(monkeypatch):
+def test_pair_retained_rank_full_size_bitwise(monkeypatch):
     """The full retained-rank batch, where the default dispatch takes item
     pairs: the step's y equals that of the one-item shrink bit for bit."""
     from test_gpu_parity import cfg
