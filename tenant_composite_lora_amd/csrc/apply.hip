@@ -1,17 +1,19 @@
 // Shrink, expand and the fused apply of the composite multi-LoRA path.
 //
-//   shrink  (LoRAForge approach (4), segmented shrink): for one adapter's run
-//           of tuples, z_p = A_a[:, :k]^T x_{t_p}.  A wave owns one rank row j
-//           of one work item (an adapter and up to kTile consecutive tuples
-//           of its segment) and streams that row of A_a^T with coalesced
-//           16-byte loads, reusing it across the item's tokens; each lane
-//           keeps fp32 partial dot products that a 64-lane butterfly folds in
-//           a fixed order.  z is written final (no split-K partials).
+//   shrink  (LoRAForge approach (4), segmented shrink): z_p = A_a[:, :k]^T
+//           x_{t_p} for one work item (an adapter and up to kTile consecutive
+//           tuples of its segment) and one tile of 16 rank rows, on the
+//           matrix cores in bf16 (shrink_mfma, shrink_mfma_pair, plan_shrink)
+//           or with fp32 dot products and a wave butterfly (shrink_valu).
+//           Decode batches split d_in into K chunks whose partial z rows the
+//           expand adds in chunk order.
 //   expand  (LoRAForge approach (4), RowExpand; DyMerge-LoRA aggregation
-//           stage): one wave owns 512 consecutive outputs of one token and
-//           adds alpha_s * B_a[n, :k] z_s for the token's slots in order, in
-//           fp32, then adds the total to y once.  Each output element has
-//           exactly one owner; there are no atomics.
+//           stage): one wave owns 64 * CPL consecutive outputs of one token
+//           and adds alpha_s * B_a[n, :k] z_s for the token's slots in order,
+//           in fp32, then adds the total to y once (expand_kernel).  Dense
+//           64-token tiles of prefill batches run on the matrix cores instead
+//           (expand_mfma).  Each output element has exactly one owner; there
+//           are no atomics.
 //
 // A plan whose composite table was rejected has an empty token index and no
 // work items, so every kernel below finds nothing to do.
@@ -845,396 +847,6 @@ __global__ __launch_bounds__(64 * W) void expand_kernel_split(ExpandArgs e) {
 }
 
 // ---------------------------------------------------------------------------
-// staged expand: a token tile's B rows are read from HBM once per column slice
-// ---------------------------------------------------------------------------
-// One workgroup (256 threads) owns kStTok consecutive tokens and CW = 64 * CPL
-// consecutive outputs of one module.  The per-token kernel above re-reads the
-// B rows of every (token, slot) from L2; here the rows of the adapters the
-// tile touches are copied into LDS once and every token of the tile reads
-// them from there.  Thread (token ti, group g) owns the outputs of token ti
-// in the 16-byte column chunks g, g + 4, g + 8, ... of the slice, so the 64
-// tokens of a tile advance in parallel, one per four lanes.
-//
-//   1. coefficients: alpha_p * z_p[j] of every tuple of the tile's tokens,
-//      in token-major slot order, together with each tuple's segment (the
-//      adapter's position in the plan's segment table).  Tiles with more
-//      tuples than fit are handled in passes over consecutive tokens.
-//   2. windows of kStWin segments (one per thread): the segments the pass
-//      uses are marked, their rank rows counted and prefix-summed, and every
-//      tuple of the pass gets the first row of its segment in the window.
-//      Rows are staged in chunks that fit the LDS budget.
-//   3. for each chunk every thread walks its token's slots from its cursor
-//      while the slot's rows lie in the chunk.  The arithmetic and its order
-//      per output are those of the per-token kernel: alpha * z (z summed over
-//      K-chunk partials in chunk order), one fma per rank in rank order,
-//      slots in slot order, y added once at the end.
-constexpr int kStTok = 64;
-constexpr int kStThreads = 256;
-constexpr int kStWin = 256;
-constexpr int kStBBytes = 32768;  // staged B rows per chunk
-constexpr int kStCoefFloats = 4096;
-constexpr int kStFar = 0x3fffffff;  // row of a tuple whose segment lies beyond the window
-
-struct StagedArgs {
-  const int32_t *status;
-  const int32_t *seg_adapter;
-  const int32_t *tok_ptr;
-  const int32_t *tok_n;
-  const int4 *tok_rec;
-  int32_t T, N, ntiles, jobs, jobs_per_xcd, n_mods;
-  int32_t b_rows;  // staged rank rows per chunk (>= 64)
-  int32_t q_cap;   // tuples per pass (>= 64)
-  ModArgs m[kMaxMods];
-};
-
-// staged row stride in bf16: CW outputs plus 8 (16 bytes) against bank conflicts
-__host__ __device__ constexpr int st_row_stride(int cpl) { return 64 * cpl + 8; }
-
-// LDS bytes of one staged workgroup
-static inline size_t staged_lds_bytes(int R, int cpl, int b_rows, int q_cap) {
-  size_t b = 0;
-  b += size_t(kStTok) * 4;          // s_ns
-  b += size_t(kStTok + 1) * 4;      // s_qoff
-  b += 16 * 4;                      // s_red
-  b += size_t(kStWin) * 4 * 4;      // s_flag, s_boff, s_bk, s_bad
-  b += size_t(b_rows) * 4;          // s_rowmap
-  b += size_t(q_cap) * 4 * 3;       // s_qseg, s_qrow, s_qk
-  b = (b + 15) & ~size_t(15);
-  b += size_t(q_cap) * R * 4;       // s_coef
-  b += size_t(b_rows) * st_row_stride(cpl) * 2;  // s_B
-  return b;
-}
-
-// inclusive scan over the 256 threads of the workgroup; returns the total
-__device__ inline int st_block_scan(int v, int *red, int &total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
-  if (lane == 63) red[w] = v;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int i = 0; i < kStThreads / 64; ++i) {
-    const int r = red[i];
-    if (i < w) before += r;
-    total += r;
-  }
-  __syncthreads();
-  return v + before;
-}
-
-// maximum of two values over the workgroup
-__device__ inline void st_block_max2(int &a, int &b, int *red) {
-  constexpr int kW = kStThreads / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    a = max(a, __shfl_xor(a, off, 64));
-    b = max(b, __shfl_xor(b, off, 64));
-  }
-  if (lane == 0) {
-    red[w] = a;
-    red[kW + w] = b;
-  }
-  __syncthreads();
-  a = red[0];
-  b = red[kW];
-#pragma unroll
-  for (int i = 1; i < kW; ++i) {
-    a = max(a, red[i]);
-    b = max(b, red[kW + i]);
-  }
-  __syncthreads();
-}
-
-template <typename TY>
-struct Out8;  // eight consecutive outputs
-
-template <>
-struct Out8<float> {
-  nt_f4 u, v;
-  __device__ inline void load(const float *p) {
-    u = __builtin_nontemporal_load(reinterpret_cast<const nt_f4 *>(p));
-    v = __builtin_nontemporal_load(reinterpret_cast<const nt_f4 *>(p) + 1);
-  }
-  __device__ inline void add_store(float *p, const float *acc) {
-    nt_f4 a = u, b = v;
-    a.x += acc[0]; a.y += acc[1]; a.z += acc[2]; a.w += acc[3];
-    b.x += acc[4]; b.y += acc[5]; b.z += acc[6]; b.w += acc[7];
-    __builtin_nontemporal_store(a, reinterpret_cast<nt_f4 *>(p));
-    __builtin_nontemporal_store(b, reinterpret_cast<nt_f4 *>(p) + 1);
-  }
-};
-
-template <>
-struct Out8<bf16_t> {
-  nt_u4 v;
-  __device__ inline void load(const bf16_t *p) {
-    v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4 *>(p));
-  }
-  __device__ inline void add_store(bf16_t *p, const float *acc) {
-    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t lo = f32_to_bf16(bf16_lo(in[i]) + acc[2 * i]);
-      const uint16_t hi = f32_to_bf16(bf16_hi(in[i]) + acc[2 * i + 1]);
-      o[i] = uint32_t(lo) | (uint32_t(hi) << 16);
-    }
-    nt_u4 r;
-    r.x = o[0]; r.y = o[1]; r.z = o[2]; r.w = o[3];
-    __builtin_nontemporal_store(r, reinterpret_cast<nt_u4 *>(p));
-  }
-};
-
-template <int R, int CPL, bool SPLIT, typename TY>
-__global__ __launch_bounds__(kStThreads) void expand_staged(StagedArgs e) {
-  extern __shared__ __align__(16) unsigned char st_smem[];
-  constexpr int CW = 64 * CPL;     // outputs of the slice
-  constexpr int NCH = CW / 32;     // 8-output chunks per thread (chunk g + 4 i)
-  constexpr int RS = st_row_stride(CPL);
-  const int tid = threadIdx.x;
-  const int ti = tid >> 2, g = tid & 3;  // this thread's token and column group
-  const int job = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
-  if (job >= e.jobs) return;
-  int mi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxMods; ++i)
-    if (i < e.n_mods && job >= e.m[i].first) mi = i;
-  const int first = e.m[mi].first, d = e.m[mi].d, r_max = e.m[mi].r_max, zld = e.m[mi].zld;
-  const int nkc = e.m[mi].nkc, zstride = e.m[mi].zstride;
-  const int64_t ld = e.m[mi].ld;
-  const int32_t *k_dev = e.m[mi].k_dev;
-  const float *Z = e.m[mi].z;
-  const uint16_t *B = static_cast<const uint16_t *>(e.m[mi].W);
-  TY *Y = static_cast<TY *>(e.m[mi].io);
-  const int local = job - first;
-  const int cs = local / e.ntiles, tile = local - cs * e.ntiles;
-  const int t0 = tile * kStTok;
-  const int nt = min(kStTok, e.T - t0);
-  const int c0 = cs * CW;  // first output of the slice
-  const int b_rows = e.b_rows, q_cap = e.q_cap;
-
-  int *s_ns = reinterpret_cast<int *>(st_smem);
-  int *s_qoff = s_ns + kStTok;
-  int *s_red = s_qoff + kStTok + 1;
-  int *s_flag = s_red + 16;
-  int *s_boff = s_flag + kStWin;
-  int *s_bk = s_boff + kStWin;
-  int *s_bad = s_bk + kStWin;
-  int *s_rowmap = s_bad + kStWin;
-  int *s_qseg = s_rowmap + b_rows;
-  int *s_qrow = s_qseg + q_cap;
-  int *s_qk = s_qrow + q_cap;
-  const size_t off =
-      (reinterpret_cast<unsigned char *>(s_qk + q_cap) - st_smem + 15) & ~size_t(15);
-  float *s_coef = reinterpret_cast<float *>(st_smem + off);
-  uint16_t *s_B = reinterpret_cast<uint16_t *>(s_coef + size_t(q_cap) * R);
-
-  // y of this thread's outputs, loaded first (only added to at the end)
-  const bool tok_ok = ti < nt;
-  Out8<TY> yv[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int col = c0 + (g + 4 * i) * 8;
-    if (tok_ok && col < d) yv[i].load(Y + int64_t(t0 + ti) * ld + col);
-  }
-  const int U = e.status[ST_CODE] == TCL_OK ? e.status[ST_SEGMENTS] : 0;
-  if (tid < nt) s_ns[tid] = e.tok_n[t0 + tid];
-  if (tid <= nt) s_qoff[tid] = e.tok_ptr[t0 + tid];
-  __syncthreads();
-  const int my_ns = tok_ok ? s_ns[ti] : 0;
-
-  float acc[NCH * 8];
-#pragma unroll
-  for (int i = 0; i < NCH * 8; ++i) acc[i] = 0.f;
-  int cur = 0;  // next slot of this thread's token
-
-  for (int ia = 0; ia < nt;) {
-    // ---- pass over tokens [ia, ib): the most whose tuples fit q_cap ------
-    int ib = ia + 1;
-    while (ib < nt && s_qoff[ib + 1] - s_qoff[ia] <= q_cap) ++ib;
-    const int qa = s_qoff[ia];
-    const int nq = s_qoff[ib] - qa;
-    // 1. coefficients: the four threads of a token take its slots in turn
-    if (ti >= ia && ti < ib) {
-      const int qb = s_qoff[ti] - qa;
-      for (int sb = g; sb < my_ns; sb += 16) {
-        int4 rec[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (sb + 4 * u < my_ns) rec[u] = e.tok_rec[int64_t(t0 + ti) * kSlotPad + sb + 4 * u];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int sl = sb + 4 * u;
-          if (sl < my_ns) {
-            const float al = __int_as_float(rec[u].z);
-            const int q = qb + sl;
-            s_qseg[q] = rec[u].w;
-            const float *zr = Z + int64_t(rec[u].x) * zstride;
-            float *cf = s_coef + size_t(q) * R;
-#pragma unroll
-            for (int j = 0; j < R; j += 4) {
-              if (j < zld) {
-                float4 v;
-                if constexpr (SPLIT) {
-                  v = make_float4(0.f, 0.f, 0.f, 0.f);
-                  for (int c = 0; c < nkc; ++c) {
-                    const float4 t = *reinterpret_cast<const float4 *>(zr + c * zld + j);
-                    v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
-                  }
-                } else if ((zld & 3) == 0) {
-                  v = *reinterpret_cast<const float4 *>(zr + j);
-                } else {
-                  v.x = zr[j];
-                  v.y = j + 1 < zld ? zr[j + 1] : 0.f;
-                  v.z = j + 2 < zld ? zr[j + 2] : 0.f;
-                  v.w = j + 3 < zld ? zr[j + 3] : 0.f;
-                }
-                *reinterpret_cast<float4 *>(cf + j) =
-                    make_float4(al * v.x, al * v.y, al * v.z, al * v.w);
-              }
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-    const bool in_pass = ti >= ia && ti < ib;
-    const int my_qb = in_pass ? s_qoff[ti] - qa : 0;
-
-    // 2./3. windows of segments, staged in chunks
-    for (int lo = 0; lo < U; lo += kStWin) {
-      const int hi = min(U, lo + kStWin);
-      s_flag[tid] = 0;
-      __syncthreads();
-      for (int q = tid; q < nq; q += kStThreads) {
-        const int sg = s_qseg[q];
-        if (sg >= lo && sg < hi) s_flag[sg - lo] = 1;
-      }
-      __syncthreads();
-      const int sg = lo + tid;
-      const bool used = sg < hi && s_flag[tid];
-      int a = 0, k = 0;
-      if (used) {
-        a = e.seg_adapter[sg];
-        k = eff_rank(k_dev, a, r_max);
-      }
-      const int rows = used ? k : 0;
-      int total;
-      const int incl = st_block_scan(rows, s_red, total);
-      const int excl = incl - rows;
-      int any_used = used ? 1 : 0, dummy = 0;
-      st_block_max2(any_used, dummy, s_red);
-      if (!any_used) continue;
-      if (used) {
-        s_boff[tid] = excl;
-        s_bk[tid] = k;
-        s_bad[tid] = a;
-      }
-      __syncthreads();
-      // first window row and rank of every tuple of the pass
-      for (int q = tid; q < nq; q += kStThreads) {
-        const int sq = s_qseg[q];
-        int row = -1, kk = 0;
-        if (sq >= hi) {
-          row = kStFar;
-        } else if (sq >= lo) {
-          row = s_boff[sq - lo];
-          kk = s_bk[sq - lo];
-        }
-        s_qrow[q] = row;
-        s_qk[q] = kk;
-      }
-      int cstart = 0;
-      do {
-        // segments whose rows lie in [cstart, cstart + b_rows)
-        const bool in = used && excl >= cstart && incl <= cstart + b_rows;
-        if (in)
-          for (int j = 0; j < rows; ++j) s_rowmap[excl - cstart + j] = tid | (j << 16);
-        int cend = in ? incl : 0, dummy2 = 0;
-        st_block_max2(cend, dummy2, s_red);  // its barrier also publishes the row map
-        const int nrows = cend - cstart;
-        // stage the chunk's rows: 16-byte pieces, all loads before any store
-        constexpr int kPieces = CW / 8;
-        for (int pb = 0; pb < nrows * kPieces; pb += 4 * kStThreads) {
-          uint4 v[4];
-          int dst[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int pc = pb + u * kStThreads + tid;
-            v[u] = make_uint4(0u, 0u, 0u, 0u);
-            dst[u] = -1;
-            if (pc < nrows * kPieces) {
-              const int r = pc / kPieces, gp = pc - r * kPieces;
-              const int map = s_rowmap[r];
-              const int ws = map & 0xffff, j = map >> 16;
-              const int col0 = c0 + gp * 8;
-              if (col0 < d) {
-                v[u] = *reinterpret_cast<const uint4 *>(B + (int64_t(s_bad[ws]) * r_max + j) * d +
-                                                        col0);
-                dst[u] = r * RS + gp * 8;
-              }
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (dst[u] >= 0) *reinterpret_cast<uint4 *>(s_B + dst[u]) = v[u];
-        }
-        __syncthreads();
-        // accumulate the chunk's slots of this thread's token
-        const int cend_eff = cend == total ? kStFar - 1 : cend;  // last chunk takes the rest
-        if (in_pass) {
-          int c = cur;
-          while (c < my_ns) {
-            const int q = my_qb + c;
-            const int row = s_qrow[q];
-            if (row >= cend_eff) break;
-            ++c;
-            if (row < 0) continue;  // segment of an earlier window (rank 0)
-            const int kk = s_qk[q];
-            const float *cf = s_coef + size_t(q) * R;
-            const uint16_t *br = s_B + (row - cstart) * RS + g * 8;
-            for (int j = 0; j < kk; ++j) {
-              const float cj = cf[j];
-#pragma unroll
-              for (int i = 0; i < NCH; ++i) {
-                const uint4 b = *reinterpret_cast<const uint4 *>(br + j * RS + 32 * i);
-                float *ac = acc + 8 * i;
-                ac[0] = fmaf(cj, bf16_lo(b.x), ac[0]);
-                ac[1] = fmaf(cj, bf16_hi(b.x), ac[1]);
-                ac[2] = fmaf(cj, bf16_lo(b.y), ac[2]);
-                ac[3] = fmaf(cj, bf16_hi(b.y), ac[3]);
-                ac[4] = fmaf(cj, bf16_lo(b.z), ac[4]);
-                ac[5] = fmaf(cj, bf16_hi(b.z), ac[5]);
-                ac[6] = fmaf(cj, bf16_lo(b.w), ac[6]);
-                ac[7] = fmaf(cj, bf16_hi(b.w), ac[7]);
-              }
-            }
-          }
-          cur = c;
-        }
-        __syncthreads();
-        cstart = cend;
-      } while (cstart < total);
-    }
-    ia = ib;
-  }
-  // y += accumulated delta, tokens with at least one slot
-  if (tok_ok && my_ns > 0) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int col = c0 + (g + 4 * i) * 8;
-      if (col < d) yv[i].add_store(Y + int64_t(t0 + ti) * ld + col, acc + 8 * i);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // prefill expand on the matrix cores
 // ---------------------------------------------------------------------------
 // One workgroup owns kXTok tokens x kXCols output columns of one module.  The
@@ -1828,7 +1440,7 @@ static void launch_expand_t(const ExpandArgs &e, int cpl, int waves, hipStream_t
 // overrides).  The per-token kernel then runs as a split launch over the
 // other tiles.  Other batches run the per-token kernel alone.
 // TCL_DISPATCH=valu forces the per-token kernel, =mfma the matrix-core kernel
-// for every tile, =staged the staged kernel.
+// for every tile.
 constexpr int kMfmaMinTok = 8;
 
 static int dispatch_override() {
@@ -1836,32 +1448,7 @@ static int dispatch_override() {
   if (!s) return 0;
   if (!std::strcmp(s, "valu")) return 1;
   if (!std::strcmp(s, "mfma")) return 2;
-  if (!std::strcmp(s, "staged")) return 3;
   return 0;
-}
-
-// The staged expand pays off when a column slice's B rows serve several
-// tokens: batches of at least kStagedMinTokens tokens (bf16 weights).
-constexpr int kStagedMinTokens = 1 << 30;  // opt-in until it beats the per-token kernel
-
-static bool use_staged_expand(const tcl_plan *p, const tcl_module *mods) {
-  if (mods[0].wdtype != TCL_BF16) return false;
-  const int o = dispatch_override();
-  if (o == 3) return true;
-  if (o != 0) return false;
-  return p->L.T >= env_int("TCL_STAGED_MIN_T", kStagedMinTokens);
-}
-
-template <int R, int CPL, bool SPLIT, typename TY>
-static void launch_staged_t(const StagedArgs &e, int grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((expand_staged<R, CPL, SPLIT, TY>), dim3(grid), dim3(kStThreads), lds, s,
-                     e);
-}
-
-template <int R, bool SPLIT, typename TY>
-static void launch_staged_r(const StagedArgs &e, int cpl, int grid, size_t lds, hipStream_t s) {
-  if (cpl == 2) launch_staged_t<R, 2, SPLIT, TY>(e, grid, lds, s);
-  else launch_staged_t<R, 1, SPLIT, TY>(e, grid, lds, s);
 }
 
 static bool use_mfma_expand(const tcl_plan *p, const tcl_module *mods) {
@@ -2001,11 +1588,9 @@ static int side_stream(SideStream *&out) {
 static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
                          float *const *z, const int *zld, int kchunk, void *const *y,
                          const int64_t *ldy, tcl_dtype yd, hipStream_t s) {
-  const bool bfw = mods[0].wdtype == TCL_BF16;
   if (p->L.T == 0) return TCL_OK;
   if (use_mfma_expand(p, mods)) {
-    int rc = plan_prepare_ranges(p, s);
-    if (rc) return rc;
+    int rc;
     if (dispatch_override() == 2)
       return launch_expand_mfma(p, mods, n, z, zld, kchunk, y, ldy, yd, 0, s);
     const int min_tok = env_int("TCL_MFMA_MIN_TOK", kMfmaMinTok);
@@ -2020,72 +1605,6 @@ static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
     TCL_HIP(hipEventRecord(ss->join, ss->s));
     TCL_HIP(hipStreamWaitEvent(s, ss->join, 0));
     return rc1 ? rc1 : rc2;
-  }
-  if (use_staged_expand(p, mods)) {
-    StagedArgs e{};
-    e.status = p->d.status;
-    e.seg_adapter = p->d.seg_adapter;
-    e.tok_ptr = p->d.tok_ptr;
-    e.tok_n = p->d.tok_n;
-    e.tok_rec = p->d.tok_rec;
-    e.T = p->L.T;
-    e.N = p->L.N;
-    e.ntiles = (p->L.T + kStTok - 1) / kStTok;
-    e.n_mods = n;
-    // two outputs per lane unless that leaves too few workgroups
-    int64_t jobs2 = 0;
-    for (int i = 0; i < n; ++i) jobs2 += int64_t((mods[i].d_out + 127) / 128) * e.ntiles;
-    int cpl = jobs2 >= 512 ? 2 : 1;
-    const int forced = env_int("TCL_SCPL", 0);
-    if (forced == 1 || forced == 2) cpl = forced;
-    int64_t jobs = 0;
-    int rmax = 1;
-    bool split = false;
-    for (int i = 0; i < n; ++i) {
-      ModArgs &M = e.m[i];
-      M.W = mods[i].B_t;
-      M.io = y[i];
-      M.k_dev = mods[i].k_dev;
-      M.z = z[i];
-      M.zld = zld[i];
-      M.ld = ldy[i];
-      M.d = mods[i].d_out;
-      M.r_max = mods[i].r_max;
-      M.n_ct = (mods[i].d_out + 64 * cpl - 1) / (64 * cpl);
-      M.nkc = bfw ? n_kchunks(&mods[i], kchunk) : 1;
-      M.zstride = M.nkc * zld[i];
-      if (M.nkc > 1) split = true;
-      M.first = int32_t(jobs);
-      jobs += int64_t(M.n_ct) * e.ntiles;
-      if (mods[i].r_max > rmax) rmax = mods[i].r_max;
-    }
-    if (jobs > (int64_t(1) << 30)) return fail(TCL_EUNSUPPORTED, "expand grid too large");
-    const int R = rank_bucket(rmax);
-    e.jobs = int32_t(jobs);
-    e.jobs_per_xcd = int32_t((jobs + 7) / 8);
-    e.b_rows = kStBBytes / (64 * cpl * 2);
-    e.q_cap = kStCoefFloats / R;
-    const int grid = 8 * e.jobs_per_xcd;
-    const size_t lds = staged_lds_bytes(R, cpl, e.b_rows, e.q_cap);
-    logf("expand(staged): modules=%d R=%d cpl=%d tiles=%d jobs=%lld lds=%zu", n, R, cpl,
-         e.ntiles, (long long)jobs, lds);
-    const bool ybf = yd == TCL_BF16;
-#define TCL_STAGED_CASE(RR)                                                   \
-  case RR:                                                                    \
-    if (ybf && split) launch_staged_r<RR, true, bf16_t>(e, cpl, grid, lds, s);  \
-    else if (ybf) launch_staged_r<RR, false, bf16_t>(e, cpl, grid, lds, s);     \
-    else if (split) launch_staged_r<RR, true, float>(e, cpl, grid, lds, s);     \
-    else launch_staged_r<RR, false, float>(e, cpl, grid, lds, s);               \
-    break;
-    switch (R) {
-      TCL_STAGED_CASE(8)
-      TCL_STAGED_CASE(16)
-      TCL_STAGED_CASE(32)
-      TCL_STAGED_CASE(64)
-    }
-#undef TCL_STAGED_CASE
-    TCL_HIP(hipGetLastError());
-    return TCL_OK;
   }
   return launch_expand_valu(p, mods, n, z, zld, kchunk, y, ldy, yd, nullptr, 0, s);
 }
@@ -2326,8 +1845,7 @@ static int remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *
   else
     hipLaunchKernelGGL(plan_shrink<8>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, A, a);
   TCL_HIP(hipGetLastError());
-  p->ranges_ready = false;
-  return TCL_OK;
+  return plan_launch_ranges(p, s);
 }
 
 int tcl_remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *mods,

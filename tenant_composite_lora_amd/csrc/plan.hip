@@ -3,22 +3,29 @@
 // mapping step of the MAF-MVM kernel; the reorder by LoRA id is what lets one
 // workgroup stream one adapter's factors over a contiguous token run).
 //
-// One workgroup does the whole stage: validation, canonical slots, a stable
-// counting sort keyed by adapter id, the segment table, the per-token tuple
-// index (also as packed records for the expand) and the shrink work list.  The sort is deterministic
-// and uses no atomics: groups are split into C contiguous chunks, every chunk
-// counts its tuples per adapter, one exclusive scan over the (adapter, chunk)
-// matrix in adapter-major order gives every (adapter, chunk) its first output
-// position, and each chunk then walks its pairs in order handing out
-// consecutive positions.  Within an adapter, tuples therefore follow token
-// order, which is the (adapter, token, slot) order because a token holds an
-// adapter at most once.
-//
-// When the composite table is small (every decode batch) it is copied to LDS
-// first with coalesced loads, and positions are counted directly: every pair
-// scans all pairs and adds up the tuples of smaller adapters and of earlier
-// pairs of its own adapter.  That is O(P^2) work on LDS but needs no scans and
-// no serial chunk walks, which is what a latency-bound decode batch wants.
+// The stage validates the composite table, fixes each pair's slot (its
+// position in its composite ordered by adapter id), expands the groups into
+// (token, adapter, alpha, slot) tuples and sorts them stably by adapter id,
+// then writes the segment table, the per-token tuple index (also as packed
+// slot records for the expand), the shrink work items and, for batches with
+// token tiles, the per-(tile, segment) tuple ranges.  Three algorithms give
+// the same output bit for bit:
+//   - direct (tables of at most 512 pairs, one workgroup, table in LDS):
+//     every pair takes a ticket in its adapter's bucket through an LDS
+//     atomic, and its rank within the adapter is then counted from the
+//     bucket (the tokens of the bucket's pairs with a smaller pair index), so
+//     the order of the tickets does not reach the output;
+//   - multi-workgroup (larger tables): each workgroup counts and ranks the
+//     pairs of 64 consecutive groups the same way, one scan over the
+//     (adapter, workgroup) counts gives every workgroup its first position
+//     per adapter, and a scatter writes the tuples;
+//   - chunked counting sort (tables beyond the multi path's limits, one
+//     workgroup): per-(adapter, chunk) histograms, one exclusive scan in
+//     adapter-major order, then each chunk walks its pairs in order.
+// Within an adapter, tuples therefore follow token order, which is the
+// (adapter, token, slot) order because a token holds an adapter at most
+// once.  The LDS atomics only hand out counts and tickets; no output depends
+// on the order in which they land.
 
 #include <cstdarg>
 #include <cstdio>
@@ -724,8 +731,8 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
   A.d = p->d;
   if (A.mode == PLAN_MULTI) {
     int rc = launch_plan_multi(p, c, s);
-    p->ranges_ready = false;
-    return rc;
+    if (rc) return rc;
+    return plan_launch_ranges(p, s);
   }
   logf("plan: T=%d G=%d pairs=%d N=%d cap=%d chunks=%d mode=%d threads=%d", A.T, A.G, A.NP, A.N,
        A.cap, A.C, A.mode, p->L.threads);
@@ -740,8 +747,7 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
     hipLaunchKernelGGL((plan_kernel<kPlanThreads, PLAN_COUNT_GLOBAL>), dim3(1),
                        dim3(kPlanThreads), 0, s, A);
   TCL_HIP(hipGetLastError());
-  p->ranges_ready = false;
-  return TCL_OK;
+  return plan_launch_ranges(p, s);
 }
 
 int plan_remap_prepare(const tcl_plan *p, const tcl_composites *c, tcl_plan *next) {
@@ -756,14 +762,13 @@ int plan_remap_prepare(const tcl_plan *p, const tcl_composites *c, tcl_plan *nex
   *next = *p;
   next->L = L;
   bind(next);
-  next->ranges_ready = false;
   return TCL_OK;
 }
 
 int plan_launch(tcl_plan *p, const tcl_composites *c, hipStream_t s) { return launch_plan(p, c, s); }
 
-int plan_prepare_ranges(const tcl_plan *p, hipStream_t s) {
-  if (p->ranges_ready || p->L.tiles == 0) return TCL_OK;
+int plan_launch_ranges(const tcl_plan *p, hipStream_t s) {
+  if (p->L.tiles == 0) return TCL_OK;
   // from the token index where the pool fits the LDS tables
   // (TCL_RANGES_TOK=0 keeps the binary searches)
   const char *e = std::getenv("TCL_RANGES_TOK");
@@ -773,7 +778,6 @@ int plan_prepare_ranges(const tcl_plan *p, hipStream_t s) {
   else
     hipLaunchKernelGGL(tile_ranges_kernel, dim3(p->L.tiles), dim3(256), 0, s, p->d, p->L.N);
   TCL_HIP(hipGetLastError());
-  p->ranges_ready = true;
   return TCL_OK;
 }
 

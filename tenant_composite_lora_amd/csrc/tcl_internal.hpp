@@ -116,12 +116,12 @@ struct tcl_plan {
   tcl::PlanDev d;
   void *buf;
   size_t buf_bytes;
-  // per-(token tile, segment) tuple ranges are computed on first use (only
-  // the matrix-core expand reads them); a new mapping invalidates them
-  mutable bool ranges_ready;
 };
 
 namespace tcl {
-// queue the tile-range computation of p on stream s unless already done
-int plan_prepare_ranges(const tcl_plan *p, hipStream_t s);
+// Queue the per-(token tile, segment) tuple ranges and the per-tile totals of
+// p on stream s, behind the mapping kernel(s) that wrote the plan (no-op for
+// batches without token tiles).  Every mapping launch ends with it, so the
+// ranges always belong to the plan the stream last wrote.
+int plan_launch_ranges(const tcl_plan *p, hipStream_t s);
 }

@@ -129,3 +129,25 @@ def test_scheduler_replay_library_matches_oracle():
         lib_loads, _ = bench.sched_replay(stream, tclora.lag_select, LibPool, theta, 8, 16)
         ora_loads, _ = bench.sched_replay(stream, O.lag_select, OraclePool, theta, 8, 16)
         assert lib_loads == ora_loads
+
+
+def test_cpu_baseline_uses_the_cores_it_names():
+    """The oracle baseline splits the batch over worker processes and
+    reports their count; every token is covered once per repetition."""
+    import bench
+    wl = W.random_case(5, T=40, N=6, d_in=64, d_out=32, r_max=8, max_pairs=3)
+    out = bench.cpu_baseline(wl, budget_s=0.2, cores=3)
+    assert out["cores"] == 3 and out["kind"] == "oracle" and out["value"] > 0
+    assert "3 contiguous token ranges" in out["sample"]
+
+
+def test_dense_tiles_rule(bench):
+    """Tiles of 64 tokens: dense when the adapters a tile's tokens hold carry
+    at least 8 of its tuples each on average."""
+    T = 256
+    ads = [[0, 1]] * 64 + [[t % 50, 50 + t % 13] for t in range(64)] + [[]] * 64 + [[3]] * 64
+    als = [[0.5] * len(a) for a in ads]
+    wl = W.random_case(1, T=T, N=64, d_in=32, d_out=32, r_max=4, max_pairs=1)
+    wl.composites = W.csr_from_token_lists(ads, als, 64)
+    assert bench.dense_tiles(wl) == (2, 3, 4)
+    assert bench.kernel_names(wl, False)["expand"].startswith("expand_mfma + expand_kernel_split")

@@ -85,3 +85,97 @@ def test_graph_replays_match_eager(name, one_call, monkeypatch):
             bad = torch.nonzero(y != r)
             assert bad.numel() == 0, (rep, mi, bad[:5].tolist())
     assert np.all(np.isfinite(o_y.cpu().numpy()))
+
+
+def _permuted_table(c, seed):
+    """The same group structure with every adapter id sent through one
+    permutation of the pool: a table of the same sizes whose segments (and so
+    its per-tile tuple ranges) differ."""
+    perm = np.random.default_rng(seed).permutation(c.n_adapters).astype(np.int32)
+    return W.Composites(c.n_tokens, c.n_adapters, c.group_tok_ptr.copy(),
+                        c.group_pair_ptr.copy(), perm[c.pair_adapter], c.pair_alpha.copy())
+
+
+def _oracle_check(wl, c, ys, label):
+    import oracle as O
+    from gpu_util import rel_err
+    for mi, m in enumerate(wl.modules):
+        _, delta = O.apply(c.group_tok_ptr, c.group_pair_ptr, c.pair_adapter, c.pair_alpha,
+                           m.A_t, m.B_t, m.k, wl.x[mi], wl.y_base[mi])
+        got = ys[mi].double().cpu().numpy() - wl.y_base[mi]
+        rel = rel_err(got, delta)
+        assert rel <= 1e-2, (label, mi, rel)
+
+
+@pytest.mark.parametrize("name", ["mx_mixed", "mfma_many_adapters"])
+def test_apply_graph_sees_later_remap(name, monkeypatch):
+    """An apply-only graph captured after an eager apply, replayed after an
+    eager remap to a different table of the same sizes, applies the new table:
+    the per-tile tuple ranges the matrix-core expand reads are written by
+    every mapping launch, not once per plan."""
+    monkeypatch.delenv("TCL_DISPATCH", raising=False)
+    monkeypatch.delenv("TCL_FUSED_MAPPING", raising=False)
+    wl = _case(name)
+    c0 = wl.composites
+    c1 = _permuted_table(c0, 5)
+    banner(f"apply-only graph after a remap {name}: T={wl.n_tokens} P={c0.n_tuples()}")
+    t0 = composites_to_dev(c0)
+    t1 = composites_to_dev(c1)
+    plan = tclora.Plan(*t0, c0.n_adapters, n_tokens=c0.n_tokens, max_tuples=c0.n_tuples())
+    mods = [make_module(m) for m in wl.modules]
+    xs = [to_dev(x) for x in wl.x]
+    ybs = [to_dev(y) for y in wl.y_base]
+    ys = [y.clone() for y in ybs]
+    call = tclora.FusedCall(plan, mods, xs, ys)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call(s)                      # eager apply of table 0
+    torch.cuda.synchronize()
+    _oracle_check(wl, c0, ys, "eager table 0")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        cs = torch.cuda.current_stream()
+        for y, yb in zip(ys, ybs):
+            y.copy_(yb)
+        call(cs)
+    torch.cuda.synchronize()
+    for rep, (tab, c) in enumerate([(t1, c1), (t0, c0), (t1, c1)]):
+        with torch.cuda.stream(s):
+            plan.remap(*tab, c.n_tokens, stream=s)   # eager remap, then replay
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _oracle_check(wl, c, ys, f"replay {rep}")
+
+
+def test_eager_apply_before_first_replay(monkeypatch):
+    """A graph captured on a fresh plan, then an eager apply before any
+    replay: the eager apply reads tile ranges the mapping launch wrote."""
+    monkeypatch.delenv("TCL_DISPATCH", raising=False)
+    wl = _case("mx_mixed")
+    c = wl.composites
+    banner(f"eager apply before the first replay: T={wl.n_tokens}")
+    tab = composites_to_dev(c)
+    plan = tclora.Plan(*tab, c.n_adapters, n_tokens=c.n_tokens, max_tuples=c.n_tuples())
+    mods = [make_module(m) for m in wl.modules]
+    xs = [to_dev(x) for x in wl.x]
+    ybs = [to_dev(y) for y in wl.y_base]
+    ys = [y.clone() for y in ybs]
+    call = tclora.FusedCall(plan, mods, xs, ys)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        cs = torch.cuda.current_stream()
+        for y, yb in zip(ys, ybs):
+            y.copy_(yb)
+        call(cs)
+    torch.cuda.synchronize()
+    for y, yb in zip(ys, ybs):
+        y.copy_(yb)
+    with torch.cuda.stream(s):
+        call(s)
+    torch.cuda.synchronize()
+    _oracle_check(wl, c, ys, "eager")
+    g.replay()
+    torch.cuda.synchronize()
+    _oracle_check(wl, c, ys, "replay")
