@@ -256,32 +256,6 @@ def cpu_baseline(wl, budget_s: float = 12.0, cores: int = 0) -> dict:
                       f"{reps}x, {wall:.1f} s wall, fp64 numpy, {n} processes x 1 BLAS thread"}
 
 
-def dense_tiles(wl, min_tok: int = 8, tile: int = 64) -> tuple:
-    """(dense, with tuples, all) token tiles of a prefill-sized batch under the
-    expand's dispatch rule: a tile goes to the matrix cores when the adapters
-    its tokens hold carry at least ``min_tok`` of its tuples each on average.
-    Used only to name the expand kernel that does the work."""
-    c = wl.composites
-    T = c.n_tokens
-    if T < 256:
-        return 0, 0, 0
-    owner = np.repeat(np.arange(c.n_groups), np.diff(c.group_tok_ptr))
-    dense = busy = 0
-    n_tiles = (T + tile - 1) // tile
-    for ti in range(n_tiles):
-        toks = owner[ti * tile:(ti + 1) * tile]
-        tup, ads = 0, set()
-        for g in toks:
-            pr = c.pair_adapter[c.group_pair_ptr[g]:c.group_pair_ptr[g + 1]]
-            tup += len(pr)
-            ads.update(int(a) for a in pr)
-        if tup:
-            busy += 1
-            if tup >= min_tok * len(ads):
-                dense += 1
-    return dense, busy, n_tiles
-
-
 PRODUCER_METRIC = "retained-rank fleet factor construction, LoRA matrices/s"
 
 
@@ -884,26 +858,28 @@ STREAM_PEAK_GBS = 6400.0
 
 def kernel_names(wl, fused: bool) -> dict:
     """The kernels each timed phase launches, by the library's dispatch rules:
-    the decode step's shrink carries the mapping stage (plan_shrink); on
-    prefill-sized bf16 batches the matrix-core expand takes the dense tiles
-    and the per-token kernel the others (the one that does the work is named
-    first)."""
+    the decode step's shrink carries the mapping stage (plan_shrink); a
+    prefill-sized shrink pairs its work items when that still leaves at least
+    1024 jobs (two rounds of two workgroups on each of the 256 compute
+    units); prefill-sized bf16 batches expand over token tiles on the matrix
+    cores (tile_prep writes each tile's coefficients, expand_tile does the
+    work), other batches on the per-token kernel."""
     from tenant_composite_lora_amd import workloads as W
+    c = wl.composites
     bf = wl.dtype == W.BF16
-    shrink = ("plan_shrink" if fused else "shrink_mfma") if bf else "shrink_valu"
-    disp = os.environ.get("TCL_DISPATCH", "")
-    if not bf or wl.composites.n_tokens < 256 or disp == "valu":
-        expand = "expand_kernel"
-    elif disp == "mfma":
-        expand = "expand_mfma"
+    if not bf:
+        shrink = "shrink_valu"
+    elif fused:
+        shrink = "plan_shrink"
     else:
-        dense, busy, _ = dense_tiles(wl)
-        if dense == 0:
-            expand = "expand_kernel_split (expand_mfma has no dense tile)"
-        elif dense == busy:
-            expand = "expand_mfma (expand_kernel_split has no sparse tile)"
-        else:
-            expand = f"expand_mfma + expand_kernel_split ({dense} of {busy} tiles dense)"
+        P = c.n_tuples()
+        items_cap = min(P, wl.n_adapters) + P // 16 + 1
+        units = sum(-(-m.r_max // 16) for m in wl.modules)
+        shrink = "shrink_mfma_pair" if -(-items_cap // 2) * units >= 4 * 256 else "shrink_mfma"
+    if not bf or c.n_tokens < 256 or os.environ.get("TCL_DISPATCH") == "valu":
+        expand = "expand_kernel"
+    else:
+        expand = "expand_tile (after tile_prep)"
     return {"plan": "plan_kernel", "shrink": shrink, "expand": expand}
 
 

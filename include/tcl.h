@@ -42,7 +42,9 @@
  *     8 elements.  Host pointers are only read during the call.
  *   - Every GPU call is asynchronous on the caller's stream (a hipStream_t
  *     passed as void*, NULL = the default stream).  Only tcl_plan_copy_out and
- *     tcl_plan_status synchronise (they read plan data back to the host).
+ *     tcl_plan_status (they read plan data back to the host) and
+ *     tcl_module_init / tcl_module_load_ranks (their host ranks may be freed
+ *     on return) synchronise.
  *   - Every function returns a status code (TCL_OK = 0 or a negative TCL_E*).
  *     Host-side checks run before any HIP call, so they need no GPU.  The
  *     message of the last failure on the calling thread is tcl_last_error().
@@ -78,8 +80,10 @@ typedef enum { TCL_BF16 = 0, TCL_F32 = 1 } tcl_dtype;
  * Composite table (DyMerge-LoRA section 3.1: static composition fixes alpha per
  * request, dynamic composition per token).  A group is a run of consecutive
  * tokens sharing one list of (adapter, alpha) pairs; one group per token is
- * token-level (dynamic) composition.  All arrays are DEVICE memory so that a
- * gate running on the GPU can feed the plan directly.
+ * token-level (dynamic) composition.  For tcl_plan_map, tcl_plan_remap and
+ * the step calls every array is DEVICE memory, so that a gate running on the
+ * GPU can feed the plan directly; tcl_plan_map_host and tcl_plan_remap_host
+ * take the same struct with HOST arrays.
  *
  *   group_tok_ptr [n_groups+1]: group g covers tokens [ptr[g], ptr[g+1]);
  *                               ptr[0] = 0, non-decreasing, ptr[G] = n_tokens.
@@ -90,9 +94,12 @@ typedef enum { TCL_BF16 = 0, TCL_F32 = 1 } tcl_dtype;
  *   pair_alpha   [n_pairs]    : finite fp32 weight (copied bit for bit).
  *   max_tuples                : capacity for P = sum_g tokens_g * pairs_g.
  *
- * The table's contents are validated on the device by tcl_plan_map; a bad table
- * leaves an error in the plan's device status (see tcl_plan_status) and every
- * later call on that plan does nothing.
+ * A device-resident table is validated on the device by the mapping stage;
+ * a bad table leaves an error in the plan's device status (read it with
+ * tcl_plan_status, which synchronises, or tcl_plan_status_async, which does
+ * not) and every later apply call on that plan changes nothing.  A
+ * host-resident table is validated on the host, before any HIP call, and a
+ * bad one is refused with its code.
  */
 typedef struct {
   int32_t n_tokens;
@@ -110,7 +117,14 @@ typedef struct {
  * One projection's adapter pool (the loader output of the LoRAForge
  * retained-rank contract).  k_dev is DEVICE int32 [n_adapters] of effective
  * ranks in [0, r_max], or NULL for "every adapter uses r_max"; fill it with
- * tcl_module_load_ranks.
+ * tcl_module_init (or tcl_module_load_ranks).
+ *
+ * B_k is an optional DEVICE rank-contiguous copy of B for the prefill expand
+ * on the matrix cores: B_k[a][n][j] = row j of B_a^T at column n for j < k_a,
+ * zero for k_a <= j < r_pad, r_pad = r_max rounded up to a multiple of 8
+ * ([n_adapters][d_out][r_pad] bf16).  Fill it with tcl_module_pack after the
+ * ranks are loaded (and again whenever B_t or the ranks change).  NULL: the
+ * prefill expand runs on the per-token kernel over B_t.
  */
 typedef struct {
   int32_t n_adapters;
@@ -121,6 +135,7 @@ typedef struct {
   const void *A_t;     /* device [n_adapters][r_max][d_in]  */
   const void *B_t;     /* device [n_adapters][r_max][d_out] */
   const int32_t *k_dev;
+  const void *B_k;     /* device [n_adapters][d_out][r_pad] or NULL */
 } tcl_module;
 
 typedef struct tcl_plan tcl_plan; /* opaque host handle; device arrays live in
@@ -185,6 +200,54 @@ int tcl_plan_copy_out(const tcl_plan *p, int32_t *tup_token, int32_t *tup_adapte
 void tcl_plan_free(tcl_plan *p);
 
 /*
+ * Host-resident composite tables.  The same tcl_composites, with every
+ * array in HOST memory.  The table is validated on the host before any HIP
+ * call, by the rules the mapping stage applies on the device and with the
+ * same codes and precedence: TCL_EINVAL (CSR pointers that do not start at
+ * 0, end at n_tokens / n_pairs or decrease; an adapter id outside
+ * [0, n_adapters); a non-finite alpha; an adapter twice in one composite of
+ * at most TCL_MAX_PAIRS_PER_GROUP pairs) before TCL_EUNSUPPORTED (a larger
+ * composite) before TCL_ENOSPC (more tuples than max_tuples).
+ *
+ * tcl_composites_validate: that check alone (host only, no GPU); on success
+ * *n_tuples = the tuple count P and *n_segments = the adapters that own at
+ * least one tuple (either pointer may be NULL).
+ *
+ * tcl_plan_map_host / tcl_plan_remap_host: the check, then the table is
+ * copied into the plan buffer (tcl_plan_bytes includes room for it) through
+ * a pinned staging buffer the plan owns, and the mapping stage runs on the
+ * device copy exactly as tcl_plan_map / tcl_plan_remap do.  The caller's
+ * arrays may be freed or reused as soon as the call returns.  A rejected
+ * table returns its code and queues nothing (the plan of a failed remap is
+ * unchanged).  The copy reads the table when called, so these calls must not
+ * be captured into a graph (TCL_EUNSUPPORTED on a capturing stream); a later
+ * host remap waits for the previous one's copy to finish before reusing the
+ * staging buffer.
+ */
+int tcl_composites_validate(const tcl_composites *c, int32_t *n_tuples, int32_t *n_segments);
+int tcl_plan_map_host(const tcl_composites *c, void *dev_buf, size_t dev_bytes, void *stream,
+                      tcl_plan **out);
+int tcl_plan_remap_host(tcl_plan *p, const tcl_composites *c, void *stream);
+
+/*
+ * Tuple and segment counts of a plan whose last table was host-resident
+ * (known on the host from the validation; no GPU call).  TCL_EUNSUPPORTED
+ * for a plan mapped from a device-resident table: its counts live on the
+ * device (tcl_plan_status, tcl_plan_status_async).
+ */
+int tcl_plan_info(const tcl_plan *p, int32_t *n_tuples, int32_t *n_segments);
+
+/*
+ * The plan's device verdict without a host synchronisation: queues on
+ * `stream` a copy of {status code, tuples, segments, work items} into the
+ * caller's device array dev_status[4] (int32, 4-byte aligned).  Queued after
+ * a mapping call (or a step, which maps first) on the same stream it reads
+ * that mapping's verdict: TCL_OK, or the code listed under tcl_plan_map for a
+ * rejected table, whose apply calls change nothing.  Graph-capturable.
+ */
+int tcl_plan_status_async(const tcl_plan *p, int32_t *dev_status, void *stream);
+
+/*
  * Loader step of the retained-rank contract (LoRAForge approach (1)): checks
  * host ranks k_host[n_adapters] in [0, r_max] and copies them to the device
  * array k_dev (caller-owned, n_adapters int32), then sets m->k_dev = k_dev.
@@ -192,6 +255,32 @@ void tcl_plan_free(tcl_plan *p);
  */
 int tcl_module_load_ranks(tcl_module *m, const int32_t *k_host, int32_t *k_dev,
                           void *stream);
+
+/*
+ * Module set-up: validates the whole module (sizes, r_max in
+ * 1..TCL_MAX_RANK, weight dtype, d_in and d_out multiples of 8, 16-byte
+ * aligned A_t and B_t) and, when k_host is given, its ranks as
+ * tcl_module_load_ranks does (k_host[n_adapters] in [0, r_max], copied to
+ * the caller's device array k_dev, then m->k_dev = k_dev; synchronises the
+ * stream so that k_host may be freed on return).  k_host NULL sets
+ * m->k_dev = NULL (every adapter at r_max).  All checks run before any HIP
+ * call.  Errors: TCL_EINVAL, TCL_EALIGN, TCL_EUNSUPPORTED, TCL_EHIP.
+ */
+int tcl_module_init(tcl_module *m, const int32_t *k_host, int32_t *k_dev, void *stream);
+
+/*
+ * The rank-contiguous copy B_k of a bf16 module's B_t (see tcl_module),
+ * written on `stream` from B_t and the module's ranks (m->k_dev, or r_max for
+ * every adapter when NULL); then m->B_k = B_k.  Rows of B_t at or beyond an
+ * adapter's rank are not read.  B_k: caller-owned device memory of at least
+ * tcl_module_pack_bytes bytes, 16-byte aligned.  The pack reads the ranks
+ * queued before it on the stream; re-pack after new ranks or new factors.
+ * Errors: those of tcl_module_init's module checks; TCL_EUNSUPPORTED (fp32
+ * pool), TCL_EINVAL (B_k NULL), TCL_EALIGN, TCL_ENOSPC (bytes too small),
+ * TCL_EHIP.
+ */
+int tcl_module_pack_bytes(const tcl_module *m, size_t *bytes);
+int tcl_module_pack(tcl_module *m, void *B_k, size_t bytes, void *stream);
 
 /* Device workspace tcl_fused_apply needs for these modules (host only). */
 int tcl_workspace_bytes(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,

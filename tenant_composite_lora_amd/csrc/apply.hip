@@ -10,10 +10,10 @@
 //   expand  (LoRAForge approach (4), RowExpand; DyMerge-LoRA aggregation
 //           stage): one wave owns 64 * CPL consecutive outputs of one token
 //           and adds alpha_s * B_a[n, :k] z_s for the token's slots in order,
-//           in fp32, then adds the total to y once (expand_kernel).  Dense
-//           64-token tiles of prefill batches run on the matrix cores instead
-//           (expand_mfma).  Each output element has exactly one owner; there
-//           are no atomics.
+//           in fp32, then adds the total to y once (expand_kernel).  Prefill
+//           batches run over 64-token tiles on the matrix cores instead
+//           (tile_prep + expand_tile).  Each output element has exactly one
+//           owner; there are no atomics.
 //
 // A plan whose composite table was rejected has an empty token index and no
 // work items, so every kernel below finds nothing to do.
@@ -513,17 +513,9 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void plan_shrink(PlanArgs A, Shr
 struct ExpandArgs {
   const int32_t *tok_n;
   const int4 *tok_rec;  // [T][kSlotPad]
-  // split launch: per-tile {tuples, segments} (the tiles that the
-  // matrix-core expand takes are skipped here), else NULL
-  const int2 *tcount;
-  int32_t T, n_mods, jobs, jobs_per_xcd, tiles, min_tok;
+  int32_t T, n_mods, jobs, jobs_per_xcd;
   ModArgs m[kMaxMods];
 };
-
-// A token tile goes to the matrix cores when the segments that touch it
-// carry at least min_tok of its tuples each on average (the matrix cores
-// work on every token of the tile for every touched adapter's rank rows).
-__device__ inline bool dense_tile(int2 c, int min_tok) { return c.y == 0 || c.x >= min_tok * c.y; }
 
 
 // C consecutive weights of one B row (C = 2, 4 or 8)
@@ -695,19 +687,12 @@ struct OutN<bf16_t, C> {
 // in slot order, rank order within a slot; y is added once at the end.
 // One expand job (token, 64 * CPL outputs of one module) for the calling wave;
 // BR (slot, rank) rows of B are loaded per batch.
-//
-// TILED: a split launch.  The tile's counts are read with the slot table and
-// the job ends there if the matrix-core expand owns the tile; y is loaded
-// after that check (it is needed only at the end, so the check adds no
-// latency to the jobs that run).
-template <int R, int CPL, bool SPLIT, typename TW, typename TY, int BR, bool TILED = false>
+template <int R, int CPL, bool SPLIT, typename TW, typename TY, int BR>
 __device__ inline void expand_job(const ExpandArgs &e, int job) {
   constexpr int RB = R < BR ? R : BR;  // ranks per batch
   constexpr int SB = BR / RB;          // slots per batch
   const int lane = threadIdx.x & 63;
   if (job >= e.jobs) return;
-  int2 tc{0, 0};
-  if constexpr (TILED) tc = e.tcount[(job % e.T) / kXTok];  // module jobs start at multiples of T
   int mi = 0;
 #pragma unroll
   for (int i = 1; i < kMaxMods; ++i)
@@ -728,10 +713,6 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
   OutN<TY, CPL> yv;
   const int ns = e.tok_n[t];
   const int4 rec = e.tok_rec[int64_t(t) * kSlotPad + lane];
-  if constexpr (TILED) {
-    if (dense_tile(tc, e.min_tok)) return;
-    if (active) yv.load(Yp);
-  }
   if (ns <= 0) return;
 
   float acc[CPL];
@@ -770,13 +751,11 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
           if (j < kk[b] && active) bv[b][jj].load(B + (int64_t(aa[b]) * r_max + j) * d + n0);
           else bv[b][jj].zero();
         }
-        if constexpr (!TILED) {
-          // y right after the first batch's B rows: its latency then
-          // overlaps theirs instead of the slot records' (the memory
-          // counter is in order, so a load issued before the slot records
-          // would be waited for together with them)
-          if (sb == 0 && jb == 0 && b == 0 && active) yv.load(Yp);
-        }
+        // y right after the first batch's B rows: its latency then overlaps
+        // theirs instead of the slot records' (the memory counter is in
+        // order, so a load issued before the slot records would be waited
+        // for together with them)
+        if (sb == 0 && jb == 0 && b == 0 && active) yv.load(Yp);
         if constexpr (!SPLIT) {
           // one z row per tuple, read as whole vectors
           const float *zrow = Z + int64_t(pp[b]) * zld + jb;
@@ -836,58 +815,10 @@ __global__ __launch_bounds__(64 * W) void expand_kernel(ExpandArgs e) {
   expand_job<R, CPL, SPLIT, TW, TY, BR>(e, job);
 }
 
-// The same jobs in a split launch (e.tcount set: the matrix-core expand has
-// done the dense tiles; bf16 pools): each job is skipped when its token's
-// tile is dense.
-template <int R, int CPL, bool SPLIT, typename TY, int W, int BR>
-__global__ __launch_bounds__(64 * W) void expand_kernel_split(ExpandArgs e) {
-  const int blk = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
-  const int job = __builtin_amdgcn_readfirstlane(blk * W + int(threadIdx.x >> 6));
-  expand_job<R, CPL, SPLIT, bf16_t, TY, BR, true>(e, job);
-}
-
 // ---------------------------------------------------------------------------
-// prefill expand on the matrix cores
+// helpers of the prefill expand
 // ---------------------------------------------------------------------------
-// One workgroup owns kXTok tokens x kXCols output columns of one module.  The
-// adapters that its tokens hold (the tile's union) are concatenated along K,
-// each contributing its retained rank rows in octets of 8:
-//     Y[tokens x cols] += W[tokens x K] . Bcat[K x cols]
-// with W[t][(a, j)] = bf16(alpha_{t,a} z_{t,a}[j]) when token t holds adapter
-// a (else 0) and Bcat[(a, j)][n] = B_t[a][j][n].  The matrix cores compute the
-// transposed product D[n][t] = sum_k Bcat[k][n] W[t][k], so each lane of a
-// 16 x 16 output block holds four consecutive columns of one token: y moves
-// as 16-byte vectors, is loaded into the accumulators while the union and the
-// coefficients are set up, and is stored once at the end.
-//
-// Wave w owns columns [64w, 64w + 64) of the tile for all kXTok tokens.  It
-// stages the B rows of exactly those columns, so its staging area in LDS is
-// private and needs no workgroup barrier; only the coefficients W are shared.
-// B rows run along n while the operand wants 8 consecutive K per lane, so a
-// lane loads an 8 x 8 block (8 rank rows x 8 columns, 16-byte loads),
-// transposes it with byte permutes and writes one K octet per column.  Octets
-// are XOR-swizzled by column (B) and by token (W) so that the 16-byte operand
-// reads of 16 consecutive columns or tokens hit distinct banks.  The next
-// stage's rows are loaded into registers while the current stage multiplies.
-//
-// Rank rows at or beyond an adapter's retained rank are never read (zeros go
-// to LDS instead).  A token's coefficient for an adapter it does not hold is
-// an exact zero, so the pools must be finite, as everywhere on this path.
-constexpr int kXCols = 256;     // output columns per tile (4 waves x 64)
-constexpr int kXOct = 8;        // rank rows per K octet
-constexpr int kXStageOct = 8;   // K octets per stage (64 K values)
-constexpr int kXChunkOct = 16;  // K octets of W per chunk (128 K values)
-constexpr int kXSeg = 128;      // segments examined per union window
-
-struct ExpandMfmaArgs {
-  const int32_t *status, *seg_adapter, *tup_token, *tok_n;
-  const float *tup_alpha;
-  const int2 *ranges;  // [tiles][N]
-  const int2 *tcount;  // [tiles]: {tuples, segments with tuples}
-  int32_t T, N, tiles, n_mods, jobs, jobs_per_xcd;
-  int32_t min_tok;     // density threshold of dense_tile (0: every tile is taken)
-  ModArgs m[kMaxMods];  // first = first job; n_ct = column tiles of kXCols
-};
+constexpr int kXCols = 256;  // output columns per tile job (4 waves x 64)
 
 // Exclusive prefix sums of two values over the 256 threads, and their totals.
 __device__ inline void block_scan2(int v0, int v1, int *tmp, int &x0, int &x1, int &s0,
@@ -936,23 +867,6 @@ __device__ inline int last_le(const int *a, int lo, int hi, int v) {
   return lo;
 }
 
-// LDS offsets (bf16 elements) of the swizzled operand layouts.
-__device__ inline int bsw_off(int c, int oct) {  // wave's B stage: [64 columns][8 octets]
-  return c * 64 + ((oct ^ ((c ^ (c >> 3)) & 7)) << 3);
-}
-__device__ inline int wsw_off(int t, int oct) {  // coefficients: [kXTok tokens][16 octets]
-  return t * (kXChunkOct * 8) + ((oct ^ (t & 15)) << 3);
-}
-
-// Orders this wave's LDS writes before its later reads (and reads before
-// later writes): a wave's LDS operations execute in program order, so only
-// the compiler has to be kept from moving them.
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Four consecutive y values.  Plain (not non-temporal) accesses: measured
 // faster here than the streaming hint.
 template <typename TY>
@@ -977,239 +891,497 @@ __device__ inline void store_y4(TY *p, f32x4_t v) {
   }
 }
 
-template <typename TY>
-__global__ __launch_bounds__(256) void expand_mfma(ExpandMfmaArgs e) {
-  __shared__ __align__(16) uint16_t Bl[4][64 * 64];                 // per wave, one stage
-  __shared__ __align__(16) uint16_t Wl[kXTok * kXChunkOct * 8];     // one chunk of W
-  __shared__ int u_a[kXSeg], u_lo[kXSeg], u_k[kXSeg], u_h0[kXSeg + 1], u_q0[kXSeg + 1];
-  __shared__ int o_a[kXChunkOct], o_j0[kXChunkOct], o_k[kXChunkOct];
+// ---------------------------------------------------------------------------
+// prefill expand over token tiles on the matrix cores
+// ---------------------------------------------------------------------------
+// The expand of a prefill-sized batch is, per 64-token tile and block of 256
+// output columns, a product Y[tokens x cols] += W[tokens x K] . Bcat[K x cols]
+// over the tile's union: the adapters its tokens hold, in the plan's segment
+// order (ascending id), each contributing its retained ranks in octets of 8
+// (ceil(k / 8) octets).  W[t][(a, j)] = bf16(alpha_{t,a} z_{t,a}[j]) when
+// token t holds adapter a, else 0 (LoRAForge approach (4), RowExpand: an
+// adapter's B rows serve every token of the tile that holds it; DyMerge-LoRA
+// section 4.3: one kernel aggregates every (token, adapter) pair).
+//
+// The matrix cores want both operands with 8 consecutive K values per lane.
+// K is the rank here, so the expand reads a packed, rank-contiguous copy of
+// the pool (tcl_module_pack, made once when the adapters are loaded: per
+// adapter and column its ceil(k / 8) rank octets); its octets load straight
+// from memory into the operand registers, with no LDS staging and no
+// transposes.  The tiles follow the plan's tile order, which groups tokens
+// that share a rare adapter.
+//
+// tile_prep (one workgroup per (module, tile)) writes the tile's record: its
+// tokens (the plan's tile order) and their slot counts; the octet table (for
+// octet h of the concatenated K: the octet's first 16-byte unit in the
+// packed pool, the union entry, the octet's index inside the adapter and the
+// adapter's octet count); the coefficient octets bf16(alpha * z[j]) of every
+// tuple of the tile (z summed over the shrink's K-chunk partials in chunk
+// order; ranks at or beyond k zero); and, per (token, union entry), the first
+// coefficient octet of that pair or -1.  Tiles beyond the record's limits
+// (kRMaxQ tuples, kRMaxU union entries, kRHcap octets, kRMaxCoef coefficient
+// octets) are marked instead; their jobs run a per-token fp32 loop with the
+// arithmetic of expand_kernel.
+//
+// expand_tile (one workgroup of 4 waves per (module, tile, 256 columns); wave
+// w owns 64 columns of all 64 tokens) copies the record into LDS and loads
+// its y rows into the accumulators, then walks K four octets (32 ranks) per
+// step: each lane loads, three steps ahead, the packed-pool octet of its
+// column for each of the four 16-column blocks, and reads from LDS the
+// coefficient octet of its token for each of the four 16-token blocks (zero
+// where the token does not hold the octet's adapter).
+constexpr int kRMaxQ = 1024;     // tuples per tile
+constexpr int kRMaxU = 128;      // union entries
+constexpr int kRHcap = 256;      // K octets (2048 ranks) per tile
+constexpr int kRMaxCoef = 1024;  // coefficient octets per tile
+constexpr int kRMaxWords = 128;  // adapter bitmap words: pools of at most 4096 adapters
+// record layout (int32 words): header {Q, H, fast, C, U, idx offset, coef
+// offset, -}, the tile's tokens, their slot counts, octet table A (first
+// 16-byte unit of the octet in the packed pool), octet table B (union entry |
+// octet in adapter << 9 | adapter's octets << 12), then at the offsets the
+// header gives: idx [64][U] int16 and the coefficient octets [C].
+constexpr int kRTok = 8;
+constexpr int kRTokN = kRTok + kXTok;
+constexpr int kROctA = kRTokN + kXTok;
+constexpr int kRWords = kROctA + 2 * kRHcap + kXTok * kRMaxU / 2 + 4 + 4 * kRMaxCoef;
+static_assert(kROctA % 4 == 0 && kRWords % 4 == 0, "record regions of whole 16-byte units");
+static_assert(kXTok * 4 == 256, "four threads per token of a tile");
+
+struct TileArgs {
+  const int32_t *status;
+  const int32_t *tok_n;
+  const int4 *tok_rec;     // [T][kSlotPad]
+  const int32_t *tile_tok;  // token order of the tiles (status[ST_BUSY] entries)
+  int32_t *rec;            // [n_mods][tiles][kRWords]
+  int32_t T, N, tiles, n_mods, jobs, jobs_per_xcd;
+  // packed pools (tcl_module_pack): per adapter its first 16-byte unit, and
+  // the data, [d_out][ceil(k / 8)] octets per adapter
+  const int32_t *bk_off[kMaxMods];
+  const uint4 *bk_data[kMaxMods];
+  ModArgs m[kMaxMods];  // first = first job; n_ct = column tiles of kXCols
+};
+
+// In-place exclusive prefix sum of a[0..n), n <= 1024, over the 256 threads
+// (a complete before the call); returns the total.
+__device__ inline int lds_scan(int *a, int n, int *tmp) {
+  const int tid = threadIdx.x;
+  int v[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = 4 * tid + i;
+    v[i] = idx < n ? a[idx] : 0;
+    s += v[i];
+  }
+  int x0, x1, s0, s1;
+  block_scan2(s, 0, tmp, x0, x1, s0, s1);
+  int run = x0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = 4 * tid + i;
+    if (idx < n) a[idx] = run;
+    run += v[i];
+  }
+  __syncthreads();
+  return s0;
+}
+
+__global__ __launch_bounds__(256) void tile_prep(TileArgs e) {
+  __shared__ int s_n[kXTok], s_t[kXTok], s_off[kXTok + 1];
+  __shared__ unsigned s_bm[kRMaxWords];
+  __shared__ int s_wp[kRMaxWords];
+  __shared__ int s_p[kRMaxQ], s_a[kRMaxQ], s_u[kRMaxQ], s_k[kRMaxQ], s_c[kRMaxQ];
+  __shared__ float s_al[kRMaxQ];
+  __shared__ int u_h0[kRMaxU + 1], u_a[kRMaxU], u_k[kRMaxU];
   __shared__ int tmp[8];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
-  // XCD-aware job index, as in the per-token expand
-  const int job = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
-  if (job >= e.jobs || e.status[ST_CODE] != TCL_OK) return;
-  const int U = e.status[ST_SEGMENTS];
-  int mi = 0;
+  __shared__ int s_info[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int mi = blockIdx.x / e.tiles, tile = blockIdx.x - mi * e.tiles;
+  int sel = 0;
 #pragma unroll
   for (int i = 1; i < kMaxMods; ++i)
-    if (i < e.n_mods && job >= e.m[i].first) mi = i;
-  const int first = e.m[mi].first, d = e.m[mi].d, r_max = e.m[mi].r_max, zld = e.m[mi].zld;
-  const int nkc = e.m[mi].nkc, zstride = e.m[mi].zstride;
-  const int64_t ld = e.m[mi].ld;
-  const int32_t *k_dev = e.m[mi].k_dev;
-  const float *Z = e.m[mi].z;
-  const uint16_t *Bw = static_cast<const uint16_t *>(e.m[mi].W);
-  TY *Y = static_cast<TY *>(e.m[mi].io);
-  const int local = job - first;
-  const int ct = local / e.tiles, tile = local - ct * e.tiles;
-  const int t0 = tile * kXTok, cw = ct * kXCols + 64 * w;  // first column of this wave
-  uint16_t *bw = Bl[w];
-  // B stage block of this lane: K octet kb, column octet cb of the wave's 64
-  const int kb = lane & 7, cb = lane >> 3;
-
-  // segment ub + tid of a union window: its tuples in the tile and rank
-  int lo = 0, nt = 0, a = 0, k = 0;
-  auto load_seg = [&](int ub) {
-    lo = nt = a = k = 0;
-    if (tid < kXSeg && ub + tid < U) {
-      const int2 rg = e.ranges[int64_t(tile) * e.N + ub + tid];
-      a = e.seg_adapter[ub + tid];
-      if (rg.y > rg.x) {
-        k = eff_rank(k_dev, a, r_max);
-        lo = rg.x;
-        nt = k > 0 ? rg.y - rg.x : 0;
-      }
+    if (i < e.n_mods && mi >= i) sel = i;
+  const int r_max = e.m[sel].r_max, zld = e.m[sel].zld, nkc = e.m[sel].nkc;
+  const int zstride = e.m[sel].zstride;
+  const int32_t *k_dev = e.m[sel].k_dev;
+  const float *Z = e.m[sel].z;
+  const int32_t *bk_off = e.bk_off[sel];
+  int32_t *rec = e.rec + int64_t(blockIdx.x) * kRWords;
+  const bool ok = e.status[ST_CODE] == TCL_OK;
+  const int busy = ok ? e.status[ST_BUSY] : 0;
+  if (tid < kXTok) {
+    // row tid of the tile: the plan's tile order
+    const int i = tile * kXTok + tid;
+    const int t = i < busy ? e.tile_tok[i] : -1;
+    int n = t >= 0 ? e.tok_n[t] : 0;
+    n = n < 0 ? 0 : (n > kSlotPad ? kSlotPad : n);
+    s_n[tid] = n;
+    s_t[tid] = t;
+    rec[kRTok + tid] = t;
+    rec[kRTokN + tid] = n;
+  }
+  if (tid < kRMaxWords) s_bm[tid] = 0u;
+  __syncthreads();
+  if (tid < 64) {  // prefix of the slot counts
+    const int n = s_n[lane];
+    int inc = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += v;
+    }
+    s_off[lane] = inc - n;
+    if (lane == 63) {
+      s_off[kXTok] = inc;
+      s_info[0] = inc;
+    }
+  }
+  __syncthreads();
+  const int Q = s_info[0];
+  auto header = [&](int q, int h, int fast, int c, int u, int oidx, int ocoef) {
+    if (tid == 0) {
+      rec[0] = q;
+      rec[1] = h;
+      rec[2] = fast;
+      rec[3] = c;
+      rec[4] = u;
+      rec[5] = oidx;
+      rec[6] = ocoef;
+      rec[7] = 0;
     }
   };
-
-  {
-    // sparse tiles are the per-token expand's; empty ones need nothing
-    const int2 tc = e.tcount[tile];
-    if (!dense_tile(tc, e.min_tok) || tc.y == 0 || U <= 0) return;
+  if (Q == 0) return header(0, 0, 1, 0, 0, 0, 0);
+  if (Q > kRMaxQ || e.N > 32 * kRMaxWords) return header(Q, 0, 0, 0, 0, 0, 0);
+  // the tile's tuples: thread (token r, sub) takes slots sub, sub + 4, ...
+  const int r = tid >> 2, sub = tid & 3;
+  const int nr = s_n[r], offr = s_off[r];
+  const int tr = s_t[r];
+  for (int s = sub; s < nr; s += 4) {
+    const int4 rc = e.tok_rec[int64_t(tr) * kSlotPad + s];
+    const int q = offr + s;
+    const int u = min(max(rc.w, 0), 32 * kRMaxWords - 1);
+    s_p[q] = rc.x;
+    s_a[q] = rc.y;
+    s_al[q] = __int_as_float(rc.z);
+    s_u[q] = u;
+    atomicOr(&s_bm[u >> 5], 1u << (u & 31));
+    s_k[q] = eff_rank(k_dev, rc.y, r_max);
   }
+  __syncthreads();
+  if (tid < 64) {  // prefix of the bitmap words' bit counts, two words per lane
+    const int c0 = __popc(s_bm[2 * lane]), c1 = __popc(s_bm[2 * lane + 1]);
+    int inc = c0 + c1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += v;
+    }
+    s_wp[2 * lane] = inc - c0 - c1;
+    s_wp[2 * lane + 1] = inc - c1;
+    if (lane == 63) s_info[2] = inc;
+  }
+  __syncthreads();
+  const int nU = s_info[2];
+  if (nU > kRMaxU) return header(Q, 0, 0, 0, nU, 0, 0);
+  // union entry of each tuple (segments ascending = adapters ascending); per
+  // entry its adapter, rank and octet count (every tuple of an entry writes
+  // the same values)
+  for (int s = sub; s < nr; s += 4) {
+    const int q = offr + s, u = s_u[q];
+    const int ui = s_wp[u >> 5] + __popc(s_bm[u >> 5] & ((1u << (u & 31)) - 1u));
+    const int oc = (s_k[q] + 7) >> 3;
+    s_u[q] = ui;
+    u_a[ui] = s_a[q];
+    u_k[ui] = s_k[q];
+    u_h0[ui] = oc;
+    s_c[q] = oc;
+  }
+  __syncthreads();
+  const int H = lds_scan(u_h0, nU, tmp);  // first octet of each entry
+  const int C = lds_scan(s_c, Q, tmp);    // first coefficient octet of each tuple
+  if (H > kRHcap || C > kRMaxCoef) return header(Q, H, 0, C, nU, 0, 0);
+  const int oidx = kROctA + 2 * H;                   // int16 [64][nU]
+  const int ocoef = (oidx + (kXTok * nU + 1) / 2 + 3) & ~3;  // 16-byte aligned
+  if (tid == 0) u_h0[nU] = H;
+  __syncthreads();
+  for (int h = tid; h < H; h += 256) {
+    const int i = last_le(u_h0, 0, nU, h);  // entries without octets (k = 0) are passed over
+    const int oi = h - u_h0[i], octs = (u_k[i] + 7) >> 3;
+    rec[kROctA + h] = bk_off[u_a[i]] + oi;
+    rec[kROctA + H + h] = i | (oi << 9) | (octs << 12);
+  }
+  // per (token, union entry): first coefficient octet, or -1
+  int16_t *idx = reinterpret_cast<int16_t *>(rec + oidx);
+  for (int i = tid; i < kXTok * nU; i += 256) idx[i] = -1;
+  __syncthreads();
+  for (int s = sub; s < nr; s += 4) {
+    const int q = offr + s;
+    idx[r * nU + s_u[q]] = int16_t(s_c[q]);
+  }
+  // coefficient octets bf16(alpha * z) of every tuple
+  uint4 *coef = reinterpret_cast<uint4 *>(rec + ocoef);
+  for (int f = tid; f < C; f += 256) {
+    const int q = last_le(s_c, 0, Q, f);
+    const int o = f - s_c[q], j0 = 8 * o, k = s_k[q];
+    const float al = s_al[q];
+    float zv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zv[i] = 0.f;
+    for (int c = 0; c < nkc; ++c) {
+      const float *zr = Z + int64_t(s_p[q]) * zstride + c * zld + j0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (j0 + i < k) zv[i] += zr[i];
+    }
+    uint32_t pk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v0 = j0 + 2 * i < k ? al * zv[2 * i] : 0.f;
+      const float v1 = j0 + 2 * i + 1 < k ? al * zv[2 * i + 1] : 0.f;
+      pk[i] = uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16);
+    }
+    coef[f] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+  header(Q, H, 1, C, nU, oidx, ocoef);
+}
 
-  // y -> accumulators: token t0 + 16 tb + r16, columns cw + 16 nb + 4 kg .. + 4
+// Orders LDS accesses of the workgroup around a barrier without waiting for
+// outstanding global loads (a plain __syncthreads() waits for those too).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// A tile beyond the record's limits: per token, per slot in order, per rank in
+// order, acc = fma(alpha * z_j, B[j][n], acc), then y += acc, as in
+// expand_kernel; lane = one column of the wave's 64.
+template <typename TY>
+__device__ void tile_fallback(const TileArgs &e, int sel, const int *tok, int cw) {
+  const int lane = threadIdx.x & 63;
+  const int d = e.m[sel].d, r_max = e.m[sel].r_max, zld = e.m[sel].zld;
+  const int nkc = e.m[sel].nkc, zstride = e.m[sel].zstride;
+  const int64_t ld = e.m[sel].ld;
+  const int32_t *k_dev = e.m[sel].k_dev;
+  const float *Z = e.m[sel].z;
+  const bf16_t *B = static_cast<const bf16_t *>(e.m[sel].W);
+  TY *Y = static_cast<TY *>(e.m[sel].io);
+  const int col = cw + lane;
+  for (int rr = 0; rr < kXTok; ++rr) {
+    const int t = tok[rr];
+    if (t < 0) break;
+    const int n = min(e.tok_n[t], kSlotPad);
+    if (n <= 0) continue;
+    float acc = 0.f;
+    for (int s = 0; s < n; ++s) {
+      const int4 rc = e.tok_rec[int64_t(t) * kSlotPad + s];
+      const int k = eff_rank(k_dev, rc.y, r_max);
+      const float al = __int_as_float(rc.z);
+      for (int j = 0; j < k; ++j) {
+        float zj = 0.f;
+        if (nkc == 1) {
+          zj = Z[int64_t(rc.x) * zstride + j];
+        } else {
+          for (int c = 0; c < nkc; ++c) zj += Z[int64_t(rc.x) * zstride + c * zld + j];
+        }
+        if (col < d) {
+          const float b = __uint_as_float(uint32_t(B[(int64_t(rc.y) * r_max + j) * d + col].bits) << 16);
+          acc = fmaf(al * zj, b, acc);
+        }
+      }
+    }
+    if (col < d) {
+      TY *yp = Y + int64_t(t) * ld + col;
+      if constexpr (sizeof(TY) == 4) {
+        *reinterpret_cast<float *>(yp) = *reinterpret_cast<const float *>(yp) + acc;
+      } else {
+        const float yv = __uint_as_float(uint32_t(reinterpret_cast<const bf16_t *>(yp)->bits) << 16);
+        reinterpret_cast<bf16_t *>(yp)->bits = f32_to_bf16(yv + acc);
+      }
+    }
+  }
+}
+
+template <typename TY>
+__global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
+  __shared__ __align__(16) int rl[kRWords];  // the tile's record
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
+  // XCD-aware job index: each XCD takes a contiguous range of jobs, which
+  // run the tiles of one column block in turn (its packed B columns stay in
+  // that XCD's L2)
+  const int job = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
+  if (job >= e.jobs) return;
+  int sel = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMods; ++i)
+    if (i < e.n_mods && job >= e.m[i].first) sel = i;
+  const int first = e.m[sel].first, d = e.m[sel].d;
+  const int64_t ld = e.m[sel].ld;
+  const uint4 *Bk = e.bk_data[sel];
+  TY *Y = static_cast<TY *>(e.m[sel].io);
+  const int local = job - first;
+  const int ct = local / e.tiles, tile = local - ct * e.tiles;
+  const int cw = ct * kXCols + 64 * w;
+  const int32_t *rg = e.rec + (int64_t(sel) * e.tiles + tile) * kRWords;
+  // header, tokens and slot counts, then the rest of the record that is in use
+  if (tid < kROctA / 4)
+    reinterpret_cast<uint4 *>(rl)[tid] = reinterpret_cast<const uint4 *>(rg)[tid];
+  __syncthreads();
+  const int Q = rl[0], H = rl[1], fast = rl[2], C = rl[3], U = rl[4];
+  const int oidx = rl[5], ocoef = rl[6];
+  if (Q == 0) return;
+  if (!fast) {
+    tile_fallback<TY>(e, sel, rl + kRTok, cw);
+    return;
+  }
+  const int used = ocoef + 4 * C;  // words, a multiple of 4
+  for (int i = kROctA / 4 + tid; i < used / 4; i += 256)
+    reinterpret_cast<uint4 *>(rl)[i] = reinterpret_cast<const uint4 *>(rg)[i];
+  // y of the tile's tokens into the accumulators (issued after the record's
+  // loads, so that waiting for the record does not wait for y)
   f32x4_t acc[4][4];  // [column block][token block]
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const int t = t0 + 16 * tb + r16;
+    const int t = rl[kRTok + 16 * tb + r16];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int col = cw + 16 * nb + 4 * kg;
-      acc[nb][tb] = (t < e.T && col < d) ? load_y4(Y + int64_t(t) * ld + col)
-                                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc[nb][tb] = (t >= 0 && col < d) ? load_y4(Y + int64_t(t) * ld + col)
+                                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
-
-  for (int ub = 0; ub < U; ub += kXSeg) {
-    // ---- union of the tile over segments [ub, ub + kXSeg)
-    load_seg(ub);
-    const int oc = (k + kXOct - 1) / kXOct;
-    int pos, q0, tot, Q;
-    block_scan2(oc > 0 ? 1 + (oc << 16) : 0, nt, tmp, pos, q0, tot, Q);
-    const int n_union = tot & 0xffff, H = tot >> 16;
-    if (oc > 0) {
-      const int i = pos & 0xffff;
-      u_a[i] = a;
-      u_lo[i] = lo;
-      u_k[i] = k;
-      u_h0[i] = pos >> 16;
-      u_q0[i] = q0;
+  lds_barrier();
+  const int *octA = rl + kROctA, *octB = rl + kROctA + H;
+  const int16_t *idx = reinterpret_cast<const int16_t *>(rl + oidx);
+  const uint4 *coef = reinterpret_cast<const uint4 *>(rl + ocoef);
+  const int nsteps = (H + 3) >> 2;
+  // packed-pool octets of this lane's column in the four 16-column blocks
+  auto load = [&](uint4 (&a)[4], int st) {
+    const int h = 4 * st + kg;
+    int base = 0, stride = 0;
+    const bool in = h < H;
+    if (in) {
+      base = octA[h];
+      stride = (octB[h] >> 12) & 0xf;
     }
-    if (tid == 0) {
-      u_h0[n_union] = H;
-      u_q0[n_union] = Q;
+    const uint4 *src = Bk + int64_t(base) + int64_t(cw + r16) * stride;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      a[nb] = in && cw + 16 * nb + r16 < d ? src[int64_t(16 * nb) * stride]
+                                           : make_uint4(0, 0, 0, 0);
+  };
+  // coefficient octets of this lane's token in the four 16-token blocks, then
+  // the step on the matrix cores
+  auto mult = [&](const uint4 (&a)[4], int st) {
+    const int h = 4 * st + kg;
+    int ui = 0, oi = 0;
+    const bool in = h < H;
+    if (in) {
+      const int pk = octB[h];
+      ui = pk & 0x1ff;
+      oi = (pk >> 9) & 7;
     }
-    __syncthreads();
-
-    for (int c0 = 0; c0 < H; c0 += kXChunkOct) {
-      const int nh = min(kXChunkOct, H - c0);
-      // ---- octet table of the chunk; W cleared
-      if (tid < nh) {
-        const int h = c0 + tid;
-        const int i = last_le(u_h0, 0, n_union, h);
-        o_a[tid] = u_a[i];
-        o_j0[tid] = (h - u_h0[i]) * kXOct;
-        o_k[tid] = u_k[i];
-      }
-      {
-        uint4 *W4 = reinterpret_cast<uint4 *>(Wl);
-        for (int i = tid; i < kXTok * kXChunkOct; i += 256) W4[i] = make_uint4(0, 0, 0, 0);
-      }
-      __syncthreads();
-
-      // ---- B rows of a stage (8 octets x the wave's 64 columns) into registers
-      uint4 pre[8];
-      auto load_stage = [&](int st) {
-        const int oi = st * kXStageOct + kb;
-        int j0 = 0, kk = 0, aa = 0;
-        if (oi < nh) {
-          aa = o_a[oi];
-          j0 = o_j0[oi];
-          kk = o_k[oi];
-        }
-        const int n = cw + 8 * cb;
-        if (n >= d) kk = 0;
-        const uint16_t *src = Bw + (int64_t(aa) * r_max + j0) * d + n;
+    uint4 b[4];
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-          pre[r] = j0 + r < kk ? *reinterpret_cast<const uint4 *>(src + int64_t(r) * d)
-                               : make_uint4(0, 0, 0, 0);
-      };
-      load_stage(0);
-
-      // ---- coefficients: alpha * z of every tuple of the entries that own
-      // octets of this chunk, in bf16, at (token row, octet)
-      {
-        const int c1 = c0 + nh;
-        const int i_lo = last_le(u_h0, 0, n_union, c0);
-        const int i_hi = last_le(u_h0, 0, n_union, c1 - 1) + 1;
-        const int q_end = u_q0[i_hi];
-        for (int q = u_q0[i_lo] + tid; q < q_end; q += 256) {
-          const int i = last_le(u_q0, i_lo, i_hi, q);
-          const int p = u_lo[i] + (q - u_q0[i]);
-          const int trow = e.tup_token[p] - t0;
-          const float al = e.tup_alpha[p];
-          const int kk = u_k[i], h0 = u_h0[i];
-          const int ob = max(h0, c0), oe = min(u_h0[i + 1], c1);
-          for (int o = ob; o < oe; ++o) {
-            const int j0 = (o - h0) * kXOct;
-            float zv[8];
+    for (int tb = 0; tb < 4; ++tb) {
+      const int c = in ? idx[(16 * tb + r16) * U + ui] : -1;
+      b[tb] = c >= 0 ? coef[c + oi] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-            for (int q2 = 0; q2 < 8; ++q2) zv[q2] = 0.f;
-            for (int c = 0; c < nkc; ++c) {
-              const float *zr = Z + int64_t(p) * zstride + c * zld + j0;
-              if ((zld & 3) == 0) {
-                // j0 < kk always; the second vector lies inside the row when used
-                const float4 v0 = *reinterpret_cast<const float4 *>(zr);
-                zv[0] += v0.x;
-                zv[1] += v0.y;
-                zv[2] += v0.z;
-                zv[3] += v0.w;
-                if (j0 + 4 < kk) {
-                  const float4 v1 = *reinterpret_cast<const float4 *>(zr + 4);
-                  zv[4] += v1.x;
-                  zv[5] += v1.y;
-                  zv[6] += v1.z;
-                  zv[7] += v1.w;
-                }
-              } else {
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                for (int q2 = 0; q2 < 8; ++q2)
-                  if (j0 + q2 < kk) zv[q2] += zr[q2];
-              }
-            }
-            uint32_t pk[4];
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) {
-              const float v0 = j0 + 2 * q2 < kk ? al * zv[2 * q2] : 0.f;
-              const float v1 = j0 + 2 * q2 + 1 < kk ? al * zv[2 * q2 + 1] : 0.f;
-              pk[q2] = uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16);
-            }
-            *reinterpret_cast<uint4 *>(Wl + wsw_off(trow, o - c0)) =
-                make_uint4(pk[0], pk[1], pk[2], pk[3]);
-          }
-        }
-      }
-      __syncthreads();
-
-      // ---- stages of 64 K: transpose into the wave's LDS area, multiply
-      const int nst = (nh + kXStageOct - 1) / kXStageOct;
-      for (int st = 0; st < nst; ++st) {
-        {
-          // 8 x 8 transpose: column cc of the block gets rank rows 0..7
-          const uint32_t *rw = reinterpret_cast<const uint32_t *>(pre);  // rw[4 * row + dword]
-#pragma unroll
-          for (int dw = 0; dw < 4; ++dw) {
-            uint32_t lo4[4], hi4[4];
-#pragma unroll
-            for (int rp = 0; rp < 4; ++rp) {
-              const uint32_t x = rw[4 * (2 * rp) + dw], y = rw[4 * (2 * rp + 1) + dw];
-              lo4[rp] = __builtin_amdgcn_perm(y, x, 0x05040100u);  // column 2 dw
-              hi4[rp] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // column 2 dw + 1
-            }
-            const int c = 8 * cb + 2 * dw;
-            *reinterpret_cast<uint4 *>(bw + bsw_off(c, kb)) = make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]);
-            *reinterpret_cast<uint4 *>(bw + bsw_off(c + 1, kb)) =
-                make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]);
-          }
-        }
-        wave_lds_sync();
-        if (st + 1 < nst) load_stage(st + 1);
-        const int left = nh - st * kXStageOct;  // octets of this stage that exist (> 0)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (ks == 1 && left <= 4) break;
-          bf16x8_t av[4], bv[4];
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            av[nb] = *reinterpret_cast<const bf16x8_t *>(bw + bsw_off(16 * nb + r16, 4 * ks + kg));
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb)
-            bv[tb] = *reinterpret_cast<const bf16x8_t *>(
-                Wl + wsw_off(16 * tb + r16, st * kXStageOct + 4 * ks + kg));
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-              acc[nb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nb], bv[tb], acc[nb][tb], 0, 0, 0);
-        }
-        wave_lds_sync();
-      }
-      __syncthreads();  // W and the octet table are rewritten by the next chunk
+      for (int tb = 0; tb < 4; ++tb)
+        acc[nb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, a[nb]), __builtin_bit_cast(bf16x8_t, b[tb]),
+            acc[nb][tb], 0, 0, 0);
+  };
+  uint4 a0[4], a1[4], a2[4];
+  load(a0, 0);
+  load(a1, 1);
+  load(a2, 2);
+  for (int st = 0; st < nsteps; st += 3) {
+    mult(a0, st);
+    load(a0, st + 3);
+    if (st + 1 < nsteps) {
+      mult(a1, st + 1);
+      load(a1, st + 4);
+    }
+    if (st + 2 < nsteps) {
+      mult(a2, st + 2);
+      load(a2, st + 5);
     }
   }
-
-  // ---- y = accumulators, for tokens that hold at least one pair
+  // y = accumulators, for tokens that hold at least one pair
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const int t = t0 + 16 * tb + r16;
-    if (t >= e.T || e.tok_n[t] <= 0) continue;
+    const int rrow = 16 * tb + r16, t = rl[kRTok + rrow];
+    if (t < 0 || rl[kRTokN + rrow] <= 0) continue;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int col = cw + 16 * nb + 4 * kg;
       if (col < d) store_y4(Y + int64_t(t) * ld + col, acc[nb][tb]);
     }
+  }
+}
+
+// Packed, rank-contiguous copy of a pool's B for the prefill expand: adapter
+// a keeps ceil(k_a / 8) octets per output column, B_k[n][o] = ranks 8o ..
+// 8o + 7 of column n (zero at and beyond k_a), starting at its first 16-byte
+// unit off[a] (a prefix over the adapters of d_out * ceil(k / 8)).  A column's
+// retained ranks are then 16-byte loads in the matrix cores' operand order,
+// and an adapter takes only the room its rank needs (the tiles' working set
+// in L2 scales with the retained ranks, not with r_max).
+constexpr int kPackThreads = 1024;
+
+__global__ __launch_bounds__(kPackThreads) void pack_offsets_kernel(const int32_t *k_dev,
+                                                                    int32_t N, int32_t r_max,
+                                                                    int32_t d, int32_t *off) {
+  __shared__ int tmp[kPackThreads / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int base = 0;
+  for (int a0 = 0; a0 < N; a0 += kPackThreads) {
+    const int a = a0 + threadIdx.x;
+    const int v = a < N ? ((eff_rank(k_dev, a, r_max) + 7) >> 3) * d : 0;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    if (lane == 63) tmp[w] = inc;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int j = 0; j < kPackThreads / 64; ++j) {
+      if (j < w) before += tmp[j];
+      total += tmp[j];
+    }
+    __syncthreads();
+    if (a < N) off[a] = base + before + inc - v;
+    base += total;
+  }
+}
+
+// One thread per (adapter, column): k loads along the rank (each coalesced
+// across the threads of a workgroup), ceil(k / 8) 16-byte stores.
+__global__ __launch_bounds__(256) void pack_b_kernel(const uint16_t *Bt, const int32_t *k_dev,
+                                                     int32_t N, int32_t r_max, int32_t d,
+                                                     const int32_t *off, uint4 *Bk) {
+  const int blocks = (d + 255) / 256;
+  const int a = blockIdx.x / blocks, n = (blockIdx.x - a * blocks) * 256 + threadIdx.x;
+  if (a >= N || n >= d) return;
+  const int k = eff_rank(k_dev, a, r_max), octs = (k + 7) >> 3;
+  const uint16_t *src = Bt + int64_t(a) * r_max * d + n;
+  uint4 *dst = Bk + int64_t(off[a]) + int64_t(n) * octs;
+  for (int o = 0; o < octs; ++o) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j0 = 8 * o + 2 * i;
+      const uint32_t lo = j0 < k ? src[int64_t(j0) * d] : 0u;
+      const uint32_t hi = j0 + 1 < k ? src[int64_t(j0 + 1) * d] : 0u;
+      w[i] = lo | (hi << 16);
+    }
+    dst[o] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -1411,15 +1583,6 @@ static void launch_expand_w(const ExpandArgs &e, int waves, hipStream_t s) {
   // more waves per SIMD), else 32; TCL_EBATCH=16/32 forces
   const int ebf = env_int("TCL_EBATCH", 0);
   const int br = ebf == 16 || ebf == 32 ? ebf : (CPL == 8 ? 16 : 32);
-  if constexpr (std::is_same<TW, bf16_t>::value) {
-    if (e.tcount) {  // split launch: B batches follow CPL only
-      if (waves == 4 && CPL == 8) launch_expand_k<4>(expand_kernel_split<R, CPL, SPLIT, TY, 4, 16>, e, s);
-      else if (waves == 4) launch_expand_k<4>(expand_kernel_split<R, CPL, SPLIT, TY, 4, 32>, e, s);
-      else if (CPL == 8) launch_expand_k<1>(expand_kernel_split<R, CPL, SPLIT, TY, 1, 16>, e, s);
-      else launch_expand_k<1>(expand_kernel_split<R, CPL, SPLIT, TY, 1, 32>, e, s);
-      return;
-    }
-  }
   if (waves == 4 && br == 16) launch_expand_k<4>(expand_kernel<R, CPL, SPLIT, TW, TY, 4, 16>, e, s);
   else if (waves == 4) launch_expand_k<4>(expand_kernel<R, CPL, SPLIT, TW, TY, 4, 32>, e, s);
   else if (br == 16) launch_expand_k<1>(expand_kernel<R, CPL, SPLIT, TW, TY, 1, 16>, e, s);
@@ -1433,58 +1596,57 @@ static void launch_expand_t(const ExpandArgs &e, int cpl, int waves, hipStream_t
   else launch_expand_w<R, 2, SPLIT, TW, TY>(e, waves, s);
 }
 
-// Which expand runs.  Batches of bf16 pools with token tiles (prefill-sized;
-// the plan prepares tile ranges and per-tile counts) go to the matrix-core
-// kernel first.  It takes the dense tiles: those whose touched segments hold
-// at least kMfmaMinTok of the tile's tuples each on average (TCL_MFMA_MIN_TOK
-// overrides).  The per-token kernel then runs as a split launch over the
-// other tiles.  Other batches run the per-token kernel alone.
-// TCL_DISPATCH=valu forces the per-token kernel, =mfma the matrix-core kernel
-// for every tile.
-constexpr int kMfmaMinTok = 8;
-
+// Which expand runs.  Batches with token tiles (prefill-sized: at least
+// kMfmaMinTokens tokens) of bf16 pools whose modules carry the packed copy of
+// B run the token-tile expand on the matrix cores (tile_prep + expand_tile);
+// every other batch runs the per-token kernel.  TCL_DISPATCH=valu forces the
+// per-token kernel.
 static int dispatch_override() {
   const char *s = std::getenv("TCL_DISPATCH");
   if (!s) return 0;
   if (!std::strcmp(s, "valu")) return 1;
-  if (!std::strcmp(s, "mfma")) return 2;
   return 0;
 }
 
-static bool use_mfma_expand(const tcl_plan *p, const tcl_module *mods) {
-  if (mods[0].wdtype != TCL_BF16 || p->L.tiles == 0) return false;
-  const int o = dispatch_override();
-  return o == 0 || o == 2;
+// The prefill expand over token tiles (tile_prep + expand_tile): bf16 pools,
+// batches with token tiles, pools within the record's adapter bitmap.
+// TCL_DISPATCH=valu forces the per-token kernel.
+static bool use_tile_expand(const tcl_plan *p, const tcl_module *mods, int n) {
+  if (mods[0].wdtype != TCL_BF16 || p->L.T < kMfmaMinTokens || p->L.N > 32 * kRMaxWords)
+    return false;
+  for (int i = 0; i < n; ++i)
+    if (!mods[i].B_k) return false;
+  return dispatch_override() == 0;
 }
 
-template <typename TY>
-static void launch_expand_mfma_t(const ExpandMfmaArgs &e, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((expand_mfma<TY>), dim3(grid), dim3(256), 0, s, e);
+static int r_pad(const tcl_module *m) { return (m->r_max + 7) / 8 * 8; }
+
+// bytes before the packed data: the adapters' first 16-byte units
+static size_t pack_head_bytes(const tcl_module *m) {
+  return (size_t(m->n_adapters) * 4 + 255) & ~size_t(255);
 }
 
-// Expand of n (<= kMaxMods) modules in one launch.
-static int expand_args(const tcl_plan *p, const tcl_module *mods, int n, float *const *z,
-                       const int *zld, int kchunk, void *const *y, const int64_t *ldy,
-                       ExpandArgs &e, int &cpl, int &R, bool &split, int cpl_min = 2);
+static int n_tiles(const tcl_plan *p) { return (p->L.T + kXTok - 1) / kXTok; }
 
-// The matrix-core expand over the tiles that dense_tile() gives it
-// (min_tok 0: every tile).
-static int launch_expand_mfma(const tcl_plan *p, const tcl_module *mods, int n,
+// workspace bytes of the per-tile records of one launch of n modules
+static size_t tile_rec_bytes(const tcl_plan *p, const tcl_module *mods, int n) {
+  if (!use_tile_expand(p, mods, n)) return 0;
+  return size_t(n) * size_t(n_tiles(p)) * kRWords * 4;
+}
+
+// tile_prep then expand_tile for n (<= kMaxMods) modules; rec: the records'
+// workspace (tile_rec_bytes)
+static int launch_expand_tile(const tcl_plan *p, const tcl_module *mods, int n,
                               float *const *z, const int *zld, int kchunk, void *const *y,
-                              const int64_t *ldy, tcl_dtype yd, int min_tok, hipStream_t s) {
-  const bool bfw = mods[0].wdtype == TCL_BF16;
-  ExpandMfmaArgs e{};
+                              const int64_t *ldy, tcl_dtype yd, int32_t *rec, hipStream_t s) {
+  TileArgs e{};
   e.status = p->d.status;
-  e.seg_adapter = p->d.seg_adapter;
-  e.tup_token = p->d.tup_token;
   e.tok_n = p->d.tok_n;
-  e.tup_alpha = p->d.tup_alpha;
-  e.ranges = p->d.ranges;
-  e.tcount = p->d.tcount;
-  e.min_tok = min_tok;
+  e.tok_rec = p->d.tok_rec;
+  e.rec = rec;
   e.T = p->L.T;
   e.N = p->L.N;
-  e.tiles = p->L.tiles;
+  e.tiles = n_tiles(p);
   e.n_mods = n;
   int64_t jobs = 0;
   for (int i = 0; i < n; ++i) {
@@ -1498,37 +1660,42 @@ static int launch_expand_mfma(const tcl_plan *p, const tcl_module *mods, int n,
     M.d = mods[i].d_out;
     M.r_max = mods[i].r_max;
     M.n_ct = (mods[i].d_out + kXCols - 1) / kXCols;
-    M.nkc = bfw ? n_kchunks(&mods[i], kchunk) : 1;
+    M.nkc = n_kchunks(&mods[i], kchunk);
     M.zstride = M.nkc * zld[i];
     M.first = int32_t(jobs);
-    jobs += int64_t(M.n_ct) * p->L.tiles;
+    jobs += int64_t(M.n_ct) * e.tiles;
+    e.bk_off[i] = static_cast<const int32_t *>(mods[i].B_k);
+    e.bk_data[i] = reinterpret_cast<const uint4 *>(static_cast<const char *>(mods[i].B_k) +
+                                                   pack_head_bytes(&mods[i]));
   }
   if (jobs > (int64_t(1) << 30)) return fail(TCL_EUNSUPPORTED, "expand grid too large");
   e.jobs = int32_t(jobs);
   e.jobs_per_xcd = int32_t((jobs + 7) / 8);
-  const int grid = 8 * e.jobs_per_xcd;
-  logf("expand(mfma): modules=%d tiles=%d jobs=%lld min_tok=%d", n, p->L.tiles,
-       (long long)jobs, e.min_tok);
-  if (yd == TCL_BF16) launch_expand_mfma_t<bf16_t>(e, grid, s);
-  else launch_expand_mfma_t<float>(e, grid, s);
+  e.tile_tok = p->d.tile_tok;
+  logf("expand(tile): modules=%d tiles=%d jobs=%lld", n, e.tiles, (long long)jobs);
+  hipLaunchKernelGGL(tile_prep, dim3(n * e.tiles), dim3(256), 0, s, e);
+  if (yd == TCL_BF16)
+    hipLaunchKernelGGL((expand_tile<bf16_t>), dim3(8 * e.jobs_per_xcd), dim3(256), 0, s, e);
+  else
+    hipLaunchKernelGGL((expand_tile<float>), dim3(8 * e.jobs_per_xcd), dim3(256), 0, s, e);
   TCL_HIP(hipGetLastError());
   return TCL_OK;
 }
 
-// The per-token expand: every token, or (tcount set) those of the tiles
-// that dense_tile() leaves to it.
+// Expand of n (<= kMaxMods) modules in one launch.
+static int expand_args(const tcl_plan *p, const tcl_module *mods, int n, float *const *z,
+                       const int *zld, int kchunk, void *const *y, const int64_t *ldy,
+                       ExpandArgs &e, int &cpl, int &R, bool &split, int cpl_min = 2);
+
+// The per-token expand of every token.
 static int launch_expand_valu(const tcl_plan *p, const tcl_module *mods, int n,
                               float *const *z, const int *zld, int kchunk, void *const *y,
-                              const int64_t *ldy, tcl_dtype yd, const int2 *tcount,
-                              int min_tok, hipStream_t s) {
+                              const int64_t *ldy, tcl_dtype yd, hipStream_t s) {
   ExpandArgs e;
   int cpl, R;
   bool split;
   int rc = expand_args(p, mods, n, z, zld, kchunk, y, ldy, e, cpl, R, split);
   if (rc) return rc;
-  e.tcount = tcount;
-  e.tiles = p->L.tiles;
-  e.min_tok = min_tok;
   // jobs per workgroup: four for launches of at least 4096 jobs of ranks up
   // to 16 (measured faster: sparse prefill 148 -> 141 us, 7-projection decode
   // step 38.6 -> 37.5 us), one otherwise (four measured slower for rank 32:
@@ -1559,54 +1726,13 @@ static int launch_expand_valu(const tcl_plan *p, const tcl_module *mods, int n,
   return TCL_OK;
 }
 
-// A second stream per (host thread, device).  The two halves of a split
-// expand run on the caller's stream and on this one at the same time (the
-// per-token half's early exits on dense tiles then cost nothing); it forks
-// from and joins the caller's stream through events, so work queued on the
-// caller's stream later still runs after both, and a graph captured from the
-// caller's stream holds both.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-
-static int side_stream(SideStream *&out) {
-  thread_local std::vector<SideStream> tab;
-  int dev = 0;
-  TCL_HIP(hipGetDevice(&dev));
-  if (int(tab.size()) <= dev) tab.resize(size_t(dev) + 1);
-  SideStream &ss = tab[size_t(dev)];
-  if (!ss.s) {
-    TCL_HIP(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
-    TCL_HIP(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
-    TCL_HIP(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
-  }
-  out = &ss;
-  return TCL_OK;
-}
-
 static int launch_expand(const tcl_plan *p, const tcl_module *mods, int n,
                          float *const *z, const int *zld, int kchunk, void *const *y,
-                         const int64_t *ldy, tcl_dtype yd, hipStream_t s) {
+                         const int64_t *ldy, tcl_dtype yd, int32_t *rec, hipStream_t s) {
   if (p->L.T == 0) return TCL_OK;
-  if (use_mfma_expand(p, mods)) {
-    int rc;
-    if (dispatch_override() == 2)
-      return launch_expand_mfma(p, mods, n, z, zld, kchunk, y, ldy, yd, 0, s);
-    const int min_tok = env_int("TCL_MFMA_MIN_TOK", kMfmaMinTok);
-    SideStream *ss = nullptr;
-    rc = side_stream(ss);
-    if (rc) return rc;
-    TCL_HIP(hipEventRecord(ss->fork, s));
-    TCL_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
-    const int rc1 = launch_expand_mfma(p, mods, n, z, zld, kchunk, y, ldy, yd, min_tok, s);
-    const int rc2 =
-        launch_expand_valu(p, mods, n, z, zld, kchunk, y, ldy, yd, p->d.tcount, min_tok, ss->s);
-    TCL_HIP(hipEventRecord(ss->join, ss->s));
-    TCL_HIP(hipStreamWaitEvent(s, ss->join, 0));
-    return rc1 ? rc1 : rc2;
-  }
-  return launch_expand_valu(p, mods, n, z, zld, kchunk, y, ldy, yd, nullptr, 0, s);
+  if (rec && use_tile_expand(p, mods, n))
+    return launch_expand_tile(p, mods, n, z, zld, kchunk, y, ldy, yd, rec, s);
+  return launch_expand_valu(p, mods, n, z, zld, kchunk, y, ldy, yd, s);
 }
 
 // Launch table of the per-token expand of n (<= kMaxMods) modules: outputs
@@ -1662,6 +1788,29 @@ static size_t z_bytes(const tcl_plan *p, const tcl_module *m, int kchunk) {
   return (planes * size_t(p->L.cap) * size_t(z_ld(m)) * 4 + 255) & ~size_t(255);
 }
 
+// Workspace layout: z of every module (batches of up to kMaxMods modules in
+// order), then the per-tile records of the prefill expand, one region shared
+// by the batches (they run in stream order).
+static size_t ws_z_bytes(const tcl_plan *p, const tcl_module *mods, int n_mods) {
+  size_t z = 0;
+  for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
+    const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
+    const int kchunk = shrink_kchunk(p, mods + i0, n);
+    for (int i = 0; i < n; ++i) z += z_bytes(p, &mods[i0 + i], kchunk);
+  }
+  return z;
+}
+
+static size_t ws_need(const tcl_plan *p, const tcl_module *mods, int n_mods) {
+  size_t rec = 0;
+  for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
+    const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
+    const size_t b = tile_rec_bytes(p, mods + i0, n);
+    if (b > rec) rec = b;
+  }
+  return 256 + ws_z_bytes(p, mods, n_mods) + ((rec + 255) & ~size_t(255));
+}
+
 }  // namespace tcl
 
 using namespace tcl;
@@ -1681,22 +1830,61 @@ int tcl_module_load_ranks(tcl_module *m, const int32_t *k_host, int32_t *k_dev, 
   return TCL_OK;
 }
 
+int tcl_module_init(tcl_module *m, const int32_t *k_host, int32_t *k_dev, void *stream) {
+  int rc = check_module(m);
+  if (rc) return rc;
+  if (!k_host) {
+    m->k_dev = nullptr;
+    return TCL_OK;
+  }
+  return tcl_module_load_ranks(m, k_host, k_dev, stream);
+}
+
+int tcl_module_pack_bytes(const tcl_module *m, size_t *bytes) {
+  if (!bytes) return fail(TCL_EINVAL, "bytes is NULL");
+  int rc = check_module(m);
+  if (rc) return rc;
+  *bytes = pack_head_bytes(m) + size_t(m->n_adapters) * size_t(m->d_out) * size_t(r_pad(m)) * 2;
+  return TCL_OK;
+}
+
+int tcl_module_pack(tcl_module *m, void *B_k, size_t bytes, void *stream) {
+  size_t need = 0;
+  int rc = tcl_module_pack_bytes(m, &need);
+  if (rc) return rc;
+  if (m->wdtype != TCL_BF16) return fail(TCL_EUNSUPPORTED, "the packed copy is for bf16 pools");
+  if (!B_k) return fail(TCL_EINVAL, "B_k is NULL");
+  if (reinterpret_cast<uintptr_t>(B_k) & 255)
+    return fail(TCL_EALIGN, "B_k must be 256-byte aligned");
+  if (bytes < need) return fail(TCL_ENOSPC, "B_k holds %zu bytes, needs %zu", bytes, need);
+  const int blocks = (m->d_out + 255) / 256;
+  const int64_t grid = int64_t(m->n_adapters) * blocks;
+  const int64_t units = int64_t(m->n_adapters) * m->d_out * (r_pad(m) / 8);
+  if (grid > (int64_t(1) << 31) - 1 || units > (int64_t(1) << 31) - 1)
+    return fail(TCL_EUNSUPPORTED, "pool too large to pack");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t *off = static_cast<int32_t *>(B_k);
+  hipLaunchKernelGGL(pack_offsets_kernel, dim3(1), dim3(kPackThreads), 0, s, m->k_dev,
+                     m->n_adapters, m->r_max, m->d_out, off);
+  hipLaunchKernelGGL(pack_b_kernel, dim3(unsigned(grid)), dim3(256), 0, s,
+                     static_cast<const uint16_t *>(m->B_t), m->k_dev, m->n_adapters, m->r_max,
+                     m->d_out, off,
+                     reinterpret_cast<uint4 *>(static_cast<char *>(B_k) + pack_head_bytes(m)));
+  TCL_HIP(hipGetLastError());
+  m->B_k = B_k;
+  return TCL_OK;
+}
+
 int tcl_workspace_bytes(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
                         size_t *bytes) {
   if (!bytes) return fail(TCL_EINVAL, "bytes is NULL");
   if (!p) return fail(TCL_EINVAL, "plan is NULL");
   if (n_mods < 0 || (n_mods > 0 && !mods)) return fail(TCL_EINVAL, "bad module list");
-  size_t need = 256;
   for (int i = 0; i < n_mods; ++i) {
     int rc = check_plan_module(p, &mods[i]);
     if (rc) return rc;
   }
-  for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
-    const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
-    const int kchunk = shrink_kchunk(p, mods + i0, n);
-    for (int i = 0; i < n; ++i) need += z_bytes(p, &mods[i0 + i], kchunk);
-  }
-  *bytes = need;
+  *bytes = ws_need(p, mods, n_mods);
   return TCL_OK;
 }
 
@@ -1721,7 +1909,7 @@ int tcl_expand(const tcl_plan *p, const tcl_module *m, const float *z, void *y, 
   if (!z) return fail(TCL_EINVAL, "z is NULL");
   float *zz = const_cast<float *>(z);
   const int zld = m->r_max;
-  return launch_expand(p, m, 1, &zz, &zld, 1 << 30, &y, &ldy, yd,
+  return launch_expand(p, m, 1, &zz, &zld, 1 << 30, &y, &ldy, yd, nullptr,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -1732,7 +1920,6 @@ static int check_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods
   if (!p) return fail(TCL_EINVAL, "plan is NULL");
   if (n_mods < 1 || !mods) return fail(TCL_EINVAL, "module list is required");
   if ((x && !ldx) || (y && !ldy)) return fail(TCL_EINVAL, "leading dimensions are required");
-  size_t need = 256;
   for (int i = 0; i < n_mods; ++i) {
     int rc = check_plan_module(p, &mods[i]);
     if (rc) return rc;
@@ -1742,11 +1929,7 @@ static int check_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods
     if (mods[i].wdtype != mods[0].wdtype)
       return fail(TCL_EUNSUPPORTED, "modules of one call must share a weight dtype");
   }
-  for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
-    const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
-    const int kchunk = shrink_kchunk(p, mods + i0, n);
-    for (int i = 0; i < n; ++i) need += z_bytes(p, &mods[i0 + i], kchunk);
-  }
+  const size_t need = ws_need(p, mods, n_mods);
   if (!ws) return fail(TCL_EINVAL, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) & 255)
     return fail(TCL_EALIGN, "workspace must be 256-byte aligned");
@@ -1775,6 +1958,7 @@ static void z_slices(const tcl_plan *p, const tcl_module *mods, int i0, int n, v
 static int run_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
                      const void *const *x, const int64_t *ldx, void *const *y,
                      const int64_t *ldy, tcl_dtype yd, void *ws, hipStream_t s) {
+  int32_t *rec = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + ws_z_bytes(p, mods, n_mods));
   for (int i0 = 0; i0 < n_mods; i0 += kMaxMods) {
     const int n = n_mods - i0 < kMaxMods ? n_mods - i0 : kMaxMods;
     float *z[kMaxMods];
@@ -1785,7 +1969,7 @@ static int run_fused(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
       if (rc) return rc;
     }
     if (y) {
-      int rc = launch_expand(p, mods + i0, n, z, zld, kchunk, y + i0, ldy + i0, yd, s);
+      int rc = launch_expand(p, mods + i0, n, z, zld, kchunk, y + i0, ldy + i0, yd, rec, s);
       if (rc) return rc;
     }
   }
@@ -1845,7 +2029,7 @@ static int remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *
   else
     hipLaunchKernelGGL(plan_shrink<8>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, A, a);
   TCL_HIP(hipGetLastError());
-  return plan_launch_ranges(p, s);
+  return plan_launch_tile_order(p, s);
 }
 
 int tcl_remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *mods,

@@ -8,8 +8,8 @@
 // (token, adapter, alpha, slot) tuples and sorts them stably by adapter id,
 // then writes the segment table, the per-token tuple index (also as packed
 // slot records for the expand), the shrink work items and, for batches with
-// token tiles, the per-(tile, segment) tuple ranges.  Three algorithms give
-// the same output bit for bit:
+// token tiles, the token order of the prefill expand's tiles.  Three
+// algorithms give the same output bit for bit:
 //   - direct (tables of at most 512 pairs, one workgroup, table in LDS):
 //     every pair takes a ticket in its adapter's bucket through an LDS
 //     atomic, and its rank within the adapter is then counted from the
@@ -27,11 +27,13 @@
 // once.  The LDS atomics only hand out counts and tickets; no output depends
 // on the order in which they land.
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "plan_core.hpp"
 #include "tcl_internal.hpp"
@@ -172,116 +174,111 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.o_msst = take(multi ? size_t(N) * 4 : 4);
   l.o_msib = take(multi ? size_t(N) * 4 : 4);
   l.tiles = T >= kMfmaMinTokens ? (T + kXTok - 1) / kXTok : 0;
-  l.o_ranges = take(size_t(l.tiles) * size_t(N) * 8);
-  l.o_tcount = take(size_t(l.tiles) * 8);
+  l.o_ttok = take(l.tiles ? size_t(T) * 4 : 4);
+  // per-workgroup counts of the tile order's two launches
+  l.o_ocnt = take(l.tiles ? (size_t(T + 255) / 256 + size_t(cap + 255) / 256) * 4 : 4);
+  // device copy of a host-resident composite table: group_tok_ptr,
+  // group_pair_ptr (G + 1 each), pair_adapter, pair_alpha (NP each)
+  l.o_tab = take((2 * size_t(G) + 2 + 2 * size_t(NP)) * 4);
   l.total = o;
   *L = l;
   return TCL_OK;
 }
 
-// One workgroup per token tile of kXTok tokens: for every segment, the run
-// of its tuples whose token falls in the tile (tuples of a segment are in
-// token order, so two binary searches find it), and the tile's totals
-// {tuples, segments with tuples}.  Used by the prefill expand: the totals
-// decide whether the tile goes to the matrix cores.
-__global__ __launch_bounds__(256) void tile_ranges_kernel(PlanDev d, int32_t N) {
-  __shared__ int red[8];
-  const int tile = blockIdx.x, tid = threadIdx.x;
-  int tup = 0, nseg = 0;
-  if (d.status[ST_CODE] == TCL_OK) {
-    const int U = d.status[ST_SEGMENTS];
-    const int t0 = tile * kXTok, t1 = t0 + kXTok;
-    for (int u = tid; u < U; u += 256) {
-      const int beg = d.seg_begin[u], end = d.seg_begin[u + 1];
-      int lo = beg, hi = end;
-      while (lo < hi) {  // first tuple with token >= t0
-        const int mid = (lo + hi) >> 1;
-        if (d.tup_token[mid] < t0) lo = mid + 1;
-        else hi = mid;
-      }
-      int lo2 = lo, hi2 = end;
-      while (lo2 < hi2) {  // first tuple with token >= t1
-        const int mid = (lo2 + hi2) >> 1;
-        if (d.tup_token[mid] < t1) lo2 = mid + 1;
-        else hi2 = mid;
-      }
-      d.ranges[int64_t(tile) * N + u] = make_int2(lo, lo2);
-      if (lo2 > lo) {
-        tup += lo2 - lo;
-        ++nseg;
-      }
-    }
+// Token order of the prefill expand's 64-token tiles (tile_tok, ST_BUSY of
+// them): the tokens that hold at least one pair, first those whose rarest
+// adapter (the last of their slots, adapters ascending) is common -- its
+// segment holds at least T / kXTok tuples, about one per tile -- in token
+// order, then the others grouped by that adapter (ascending), in token order
+// within an adapter.  Tokens that share a rare adapter then share a tile,
+// which shrinks the tiles' unions (the adapters whose B rows a tile reads);
+// a common adapter is in most tiles whatever the order, and keeping those
+// tokens in order keeps the locality a batch of requests already has.  The
+// rare ones, in (adapter, token) order, are the tuples of the sorted plan
+// that are their token's last slot and belong to a rare segment.
+// Two launches over all tokens (the common ones) and all tuples (the rare
+// ones), one item per thread: the first flags the items and counts them per
+// workgroup, the second adds the counts of the earlier workgroups and writes
+// each flagged item at its place.  Workgroups [0, bt) take tokens, [bt, bt +
+// bp) tuples, so the common tokens come first.
+constexpr int kOrdThreads = 256;
+
+__device__ inline bool ord_flag(const PlanDev &d, int wg, int bt, int T, int P, int thr, int *item) {
+  const int i = (wg < bt ? wg : wg - bt) * kOrdThreads + threadIdx.x;
+  if (wg < bt) {  // token i, common
+    if (i >= T) return false;
+    const int n = min(d.tok_n[i], kSlotPad);
+    *item = i;
+    if (n <= 0) return false;
+    const int u = d.tok_rec[int64_t(i) * kSlotPad + n - 1].w;
+    return d.seg_begin[u + 1] - d.seg_begin[u] >= thr;
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    tup += __shfl_xor(tup, off, 64);
-    nseg += __shfl_xor(nseg, off, 64);
-  }
-  if ((tid & 63) == 0) {
-    red[tid >> 6] = tup;
-    red[4 + (tid >> 6)] = nseg;
-  }
-  __syncthreads();
-  if (tid == 0)
-    d.tcount[tile] = make_int2(red[0] + red[1] + red[2] + red[3], red[4] + red[5] + red[6] + red[7]);
+  if (i >= P) return false;  // tuple i: the last slot of its token, rare
+  const int t = d.tup_token[i], sl = d.tup_slot[i];
+  *item = t;
+  if (sl < 0 || sl >= kSlotPad || sl != d.tok_n[t] - 1) return false;
+  const int u = d.tok_rec[int64_t(t) * kSlotPad + sl].w;
+  return d.seg_begin[u + 1] - d.seg_begin[u] < thr;
 }
 
-// The same ranges and totals from the token index, for pools of at most
-// kRangesLdsN adapters.  The tuples of a tile are the slot records of its
-// tokens, and each record names its tuple and its segment; a segment's tuples
-// are in token order, so those that fall in the tile are consecutive and
-// their run is [least tuple, greatest tuple + 1).  Four threads per token
-// take its records (two dependent loads: the slot count, then the records)
-// and fold the tuple indices into per-segment minima and maxima in LDS;
-// integer minima and maxima do not depend on the order of the updates.  A
-// segment without tuples in the tile gets the empty run (0, 0), which every
-// reader treats like any other empty run.
-constexpr int kRangesLdsN = 4096;
-static_assert(kXTok * 4 == 256, "four threads per token of a tile");
-
-__global__ __launch_bounds__(256) void tile_ranges_tok_kernel(PlanDev d, int32_t N, int32_t T) {
-  __shared__ int lo_s[kRangesLdsN], hi_s[kRangesLdsN];
-  __shared__ int red[8];
-  const int tile = blockIdx.x, tid = threadIdx.x;
+__global__ __launch_bounds__(kOrdThreads) void tile_order_count(PlanDev d, int32_t T, int32_t bt) {
+  __shared__ int tmp[kOrdThreads / 64];
   const bool ok = d.status[ST_CODE] == TCL_OK;
-  const int U = ok ? min(d.status[ST_SEGMENTS], min(N, kRangesLdsN)) : 0;
-  for (int u = tid; u < U; u += 256) {
-    lo_s[u] = 0x7fffffff;
-    hi_s[u] = -1;
-  }
+  const int P = ok ? d.status[ST_TUPLES] : 0;
+  int item = 0;
+  const bool f = ok && ord_flag(d, blockIdx.x, bt, T, P, max(T / kXTok, 1), &item);
+  const uint64_t m = __ballot(f);
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = __popcll(m);
   __syncthreads();
-  int tup = 0;
-  const int t = tile * kXTok + (tid >> 2);
-  if (ok && t < T) {
-    const int ns = min(d.tok_n[t], kSlotPad);
-    for (int sl = tid & 3; sl < ns; sl += 4) {
-      const int4 r = d.tok_rec[int64_t(t) * kSlotPad + sl];
-      if (r.w >= 0 && r.w < U) {
-        atomicMin(&lo_s[r.w], r.x);
-        atomicMax(&hi_s[r.w], r.x);
-        ++tup;
-      }
-    }
+  if (threadIdx.x == 0) {
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < kOrdThreads / 64; ++j) c += tmp[j];
+    d.ord_cnt[blockIdx.x] = c;
   }
-  __syncthreads();
-  int nseg = 0;
-  for (int u = tid; u < U; u += 256) {
-    const int lo = lo_s[u], hi = hi_s[u];
-    d.ranges[int64_t(tile) * N + u] = hi >= 0 ? make_int2(lo, hi + 1) : make_int2(0, 0);
-    nseg += hi >= 0;
+}
+
+__global__ __launch_bounds__(kOrdThreads) void tile_order_place(PlanDev d, int32_t T, int32_t bt) {
+  __shared__ int tmp[kOrdThreads / 64];
+  __shared__ int wsum[kOrdThreads / 64];
+  const bool ok = d.status[ST_CODE] == TCL_OK;
+  const int P = ok ? d.status[ST_TUPLES] : 0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // items of the earlier workgroups, and of all of them
+  int before = 0, all = 0;
+  for (int j = threadIdx.x; j < int(gridDim.x); j += kOrdThreads) {
+    const int c = d.ord_cnt[j];
+    if (j < int(blockIdx.x)) before += c;
+    all += c;
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    tup += __shfl_xor(tup, off, 64);
-    nseg += __shfl_xor(nseg, off, 64);
+  for (int o = 32; o > 0; o >>= 1) {
+    before += __shfl_xor(before, o, 64);
+    all += __shfl_xor(all, o, 64);
   }
-  if ((tid & 63) == 0) {
-    red[tid >> 6] = tup;
-    red[4 + (tid >> 6)] = nseg;
+  if (lane == 0) {
+    tmp[w] = before;
+    wsum[w] = all;
   }
   __syncthreads();
-  if (tid == 0)
-    d.tcount[tile] = make_int2(red[0] + red[1] + red[2] + red[3], red[4] + red[5] + red[6] + red[7]);
+  int base = 0, total = 0;
+#pragma unroll
+  for (int j = 0; j < kOrdThreads / 64; ++j) {
+    base += tmp[j];
+    total += wsum[j];
+  }
+  __syncthreads();
+  int item = 0;
+  const bool f = ok && ord_flag(d, blockIdx.x, bt, T, P, max(T / kXTok, 1), &item);
+  const uint64_t m = __ballot(f);
+  if (lane == 0) tmp[w] = __popcll(m);
+  __syncthreads();
+  int wb = 0;
+#pragma unroll
+  for (int j = 0; j < kOrdThreads / 64; ++j)
+    if (j < w) wb += tmp[j];
+  if (f) d.tile_tok[base + wb + __popcll(m & ((uint64_t(1) << lane) - 1))] = item;
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) d.status[ST_BUSY] = ok ? total : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -680,8 +677,8 @@ static void bind(tcl_plan *p) {
   d.m_blk = reinterpret_cast<int32_t *>(b + L.o_mblk);
   d.m_sst = reinterpret_cast<int32_t *>(b + L.o_msst);
   d.m_sib = reinterpret_cast<int32_t *>(b + L.o_msib);
-  d.ranges = reinterpret_cast<int2 *>(b + L.o_ranges);
-  d.tcount = reinterpret_cast<int2 *>(b + L.o_tcount);
+  d.tile_tok = reinterpret_cast<int32_t *>(b + L.o_ttok);
+  d.ord_cnt = reinterpret_cast<int32_t *>(b + L.o_ocnt);
 }
 
 static int check_composites(const tcl_composites *c) {
@@ -732,7 +729,7 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
   if (A.mode == PLAN_MULTI) {
     int rc = launch_plan_multi(p, c, s);
     if (rc) return rc;
-    return plan_launch_ranges(p, s);
+    return plan_launch_tile_order(p, s);
   }
   logf("plan: T=%d G=%d pairs=%d N=%d cap=%d chunks=%d mode=%d threads=%d", A.T, A.G, A.NP, A.N,
        A.cap, A.C, A.mode, p->L.threads);
@@ -747,7 +744,7 @@ static int launch_plan(tcl_plan *p, const tcl_composites *c, hipStream_t s) {
     hipLaunchKernelGGL((plan_kernel<kPlanThreads, PLAN_COUNT_GLOBAL>), dim3(1),
                        dim3(kPlanThreads), 0, s, A);
   TCL_HIP(hipGetLastError());
-  return plan_launch_ranges(p, s);
+  return plan_launch_tile_order(p, s);
 }
 
 int plan_remap_prepare(const tcl_plan *p, const tcl_composites *c, tcl_plan *next) {
@@ -761,23 +758,134 @@ int plan_remap_prepare(const tcl_plan *p, const tcl_composites *c, tcl_plan *nex
     return fail(TCL_ENOSPC, "plan buffer holds %zu bytes, needs %zu", p->buf_bytes, L.total);
   *next = *p;
   next->L = L;
+  next->host_tuples = next->host_segments = -1;
   bind(next);
   return TCL_OK;
 }
 
 int plan_launch(tcl_plan *p, const tcl_composites *c, hipStream_t s) { return launch_plan(p, c, s); }
 
-int plan_launch_ranges(const tcl_plan *p, hipStream_t s) {
+int plan_launch_tile_order(const tcl_plan *p, hipStream_t s) {
   if (p->L.tiles == 0) return TCL_OK;
-  // from the token index where the pool fits the LDS tables
-  // (TCL_RANGES_TOK=0 keeps the binary searches)
-  const char *e = std::getenv("TCL_RANGES_TOK");
-  if (p->L.N <= kRangesLdsN && !(e && !std::strcmp(e, "0")))
-    hipLaunchKernelGGL(tile_ranges_tok_kernel, dim3(p->L.tiles), dim3(256), 0, s, p->d, p->L.N,
-                       p->L.T);
-  else
-    hipLaunchKernelGGL(tile_ranges_kernel, dim3(p->L.tiles), dim3(256), 0, s, p->d, p->L.N);
+  const int bt = (p->L.T + kOrdThreads - 1) / kOrdThreads;
+  const int bp = (p->L.cap + kOrdThreads - 1) / kOrdThreads;
+  hipLaunchKernelGGL(tile_order_count, dim3(bt + bp), dim3(kOrdThreads), 0, s, p->d, p->L.T, bt);
+  hipLaunchKernelGGL(tile_order_place, dim3(bt + bp), dim3(kOrdThreads), 0, s, p->d, p->L.T, bt);
   TCL_HIP(hipGetLastError());
+  return TCL_OK;
+}
+
+// The plan's status words {code, tuples, segments, work items} into a
+// caller's device array, in stream order.
+__global__ void status_copy_kernel(const int32_t *status, int32_t *out) {
+  if (threadIdx.x < 4) out[threadIdx.x] = status[threadIdx.x];
+}
+
+// A host-resident composite table, checked on the host by the rules of the
+// mapping stage (DyMerge-LoRA section 4.3: the tuples are built from the
+// composites; the table's rules are the library's), with its codes and their
+// precedence: TCL_EINVAL (CSR pointers that do not start at 0, end at the
+// token and pair counts or decrease; an adapter id outside [0, N); a
+// non-finite alpha; an adapter twice in a composite of at most
+// TCL_MAX_PAIRS_PER_GROUP pairs) before TCL_EUNSUPPORTED (a larger
+// composite) before TCL_ENOSPC (more tuples than max_tuples).  Counts the
+// tuples and the adapters that own at least one tuple.  No GPU is touched.
+static int validate_host(const tcl_composites *c, int64_t *P_out, int32_t *U_out) {
+  const int32_t G = c->n_groups, NP = c->n_pairs, T = c->n_tokens, N = c->n_adapters;
+  if (G < 0 || NP < 0 || T < 0 || c->max_tuples < 0)
+    return fail(TCL_EINVAL, "negative size (tokens %d, groups %d, pairs %d, max_tuples %d)", T,
+                G, NP, c->max_tuples);
+  if (N < 1) return fail(TCL_EINVAL, "n_adapters must be >= 1 (got %d)", N);
+  const int32_t *gt = c->group_tok_ptr, *gp = c->group_pair_ptr, *pa = c->pair_adapter;
+  const float *pw = c->pair_alpha;
+  if (gt[0] != 0 || gt[G] != T)
+    return fail(TCL_EINVAL, "group_tok_ptr must run from 0 to n_tokens (%d .. %d, want 0 .. %d)",
+                gt[0], gt[G], T);
+  if (gp[0] != 0 || gp[G] != NP)
+    return fail(TCL_EINVAL, "group_pair_ptr must run from 0 to n_pairs (%d .. %d, want 0 .. %d)",
+                gp[0], gp[G], NP);
+  for (int32_t g = 0; g < G; ++g)
+    if (gt[g + 1] < gt[g] || gp[g + 1] < gp[g])
+      return fail(TCL_EINVAL, "group pointers decrease at group %d", g);
+  for (int32_t q = 0; q < NP; ++q) {
+    if (pa[q] < 0 || pa[q] >= N)
+      return fail(TCL_EINVAL, "pair %d: adapter id %d outside [0, %d)", q, pa[q], N);
+    if (!std::isfinite(pw[q])) return fail(TCL_EINVAL, "pair %d: alpha is not finite", q);
+  }
+  std::vector<int32_t> last(size_t(N), -1);
+  for (int32_t g = 0; g < G; ++g) {
+    if (gp[g + 1] - gp[g] > TCL_MAX_PAIRS_PER_GROUP) continue;  // not searched (too large)
+    for (int32_t q = gp[g]; q < gp[g + 1]; ++q) {
+      if (last[size_t(pa[q])] == g)
+        return fail(TCL_EINVAL, "group %d holds adapter %d twice", g, pa[q]);
+      last[size_t(pa[q])] = g;
+    }
+  }
+  for (int32_t g = 0; g < G; ++g)
+    if (gp[g + 1] - gp[g] > TCL_MAX_PAIRS_PER_GROUP)
+      return fail(TCL_EUNSUPPORTED, "group %d holds %d pairs (at most %d)", g, gp[g + 1] - gp[g],
+                  TCL_MAX_PAIRS_PER_GROUP);
+  int64_t P = 0;
+  std::vector<char> used(size_t(N), 0);
+  int32_t U = 0;
+  for (int32_t g = 0; g < G; ++g) {
+    const int64_t nt = gt[g + 1] - gt[g];
+    P += nt * (gp[g + 1] - gp[g]);
+    if (nt > 0)
+      for (int32_t q = gp[g]; q < gp[g + 1]; ++q)
+        if (!used[size_t(pa[q])]) {
+          used[size_t(pa[q])] = 1;
+          ++U;
+        }
+  }
+  if (P > c->max_tuples)
+    return fail(TCL_ENOSPC, "the table expands to %lld tuples, max_tuples is %d", (long long)P,
+                c->max_tuples);
+  *P_out = P;
+  *U_out = U;
+  return TCL_OK;
+}
+
+// Copies the validated host table c into the plan buffer's table region
+// through the plan's pinned staging buffer and points *dc at the device copy.
+// The staging buffer is reused by the next host table once the previous copy
+// has finished (its event).
+static int stage_table(tcl_plan *p, const tcl_composites *c, hipStream_t s, tcl_composites *dc) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  TCL_HIP(hipStreamIsCapturing(s, &cs));
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(TCL_EUNSUPPORTED, "host-resident tables are copied when called; they cannot "
+                                  "be captured into a graph (use a device-resident table)");
+  const size_t G = size_t(c->n_groups), NP = size_t(c->n_pairs);
+  const size_t bytes = (2 * G + 2 + 2 * NP) * 4;
+  if (p->stage_pending) {
+    TCL_HIP(hipEventSynchronize(p->stage_ev));
+    p->stage_pending = false;
+  }
+  if (!p->stage_ev) TCL_HIP(hipEventCreateWithFlags(&p->stage_ev, hipEventDisableTiming));
+  if (p->stage_bytes < bytes) {
+    if (p->stage) TCL_HIP(hipHostFree(p->stage));
+    p->stage = nullptr;
+    p->stage_bytes = 0;
+    TCL_HIP(hipHostMalloc(&p->stage, bytes, hipHostMallocDefault));
+    p->stage_bytes = bytes;
+  }
+  int32_t *h = static_cast<int32_t *>(p->stage);
+  std::memcpy(h, c->group_tok_ptr, (G + 1) * 4);
+  std::memcpy(h + G + 1, c->group_pair_ptr, (G + 1) * 4);
+  if (NP) {
+    std::memcpy(h + 2 * G + 2, c->pair_adapter, NP * 4);
+    std::memcpy(h + 2 * G + 2 + NP, c->pair_alpha, NP * 4);
+  }
+  int32_t *d = reinterpret_cast<int32_t *>(static_cast<char *>(p->buf) + p->L.o_tab);
+  TCL_HIP(hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, s));
+  TCL_HIP(hipEventRecord(p->stage_ev, s));
+  p->stage_pending = true;
+  *dc = *c;
+  dc->group_tok_ptr = d;
+  dc->group_pair_ptr = d + G + 1;
+  dc->pair_adapter = d + 2 * G + 2;
+  dc->pair_alpha = reinterpret_cast<const float *>(d + 2 * G + 2 + NP);
   return TCL_OK;
 }
 
@@ -788,6 +896,94 @@ using namespace tcl;
 extern "C" {
 
 const char *tcl_last_error(void) { return g_err.c_str(); }
+
+int tcl_composites_validate(const tcl_composites *c, int32_t *n_tuples, int32_t *n_segments) {
+  int rc = check_composites(c);
+  if (rc) return rc;
+  int64_t P = 0;
+  int32_t U = 0;
+  if ((rc = validate_host(c, &P, &U))) return rc;
+  if (n_tuples) *n_tuples = int32_t(P);
+  if (n_segments) *n_segments = U;
+  return TCL_OK;
+}
+
+int tcl_plan_map_host(const tcl_composites *c, void *dev_buf, size_t dev_bytes, void *stream,
+                      tcl_plan **out) {
+  if (!out) return fail(TCL_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_composites(c);
+  if (rc) return rc;
+  int64_t P = 0;
+  int32_t U = 0;
+  if ((rc = validate_host(c, &P, &U))) return rc;
+  PlanLayout L;
+  rc = plan_layout(c->n_tokens, c->n_groups, c->n_pairs, c->n_adapters, c->max_tuples, &L);
+  if (rc) return rc;
+  if (!dev_buf) return fail(TCL_EINVAL, "plan buffer is NULL");
+  if (reinterpret_cast<uintptr_t>(dev_buf) & 255)
+    return fail(TCL_EALIGN, "plan buffer must be 256-byte aligned");
+  if (dev_bytes < L.total)
+    return fail(TCL_ENOSPC, "plan buffer holds %zu bytes, needs %zu", dev_bytes, L.total);
+  tcl_plan *p = new (std::nothrow) tcl_plan;
+  if (!p) return fail(TCL_EINVAL, "out of host memory");
+  p->L = L;
+  p->buf = dev_buf;
+  p->buf_bytes = dev_bytes;
+  bind(p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  tcl_composites dc;
+  rc = stage_table(p, c, s, &dc);
+  if (!rc) rc = launch_plan(p, &dc, s);
+  if (rc) {
+    tcl_plan_free(p);
+    return rc;
+  }
+  p->host_tuples = int32_t(P);
+  p->host_segments = U;
+  *out = p;
+  return TCL_OK;
+}
+
+int tcl_plan_remap_host(tcl_plan *p, const tcl_composites *c, void *stream) {
+  int rc = check_composites(c);
+  if (rc) return rc;
+  int64_t P = 0;
+  int32_t U = 0;
+  if ((rc = validate_host(c, &P, &U))) return rc;
+  tcl_plan next;
+  if ((rc = plan_remap_prepare(p, c, &next))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  *p = next;
+  tcl_composites dc;
+  p->host_tuples = p->host_segments = -1;
+  if ((rc = stage_table(p, c, s, &dc))) return rc;
+  if ((rc = launch_plan(p, &dc, s))) return rc;
+  p->host_tuples = int32_t(P);
+  p->host_segments = U;
+  return TCL_OK;
+}
+
+int tcl_plan_info(const tcl_plan *p, int32_t *n_tuples, int32_t *n_segments) {
+  if (!p) return fail(TCL_EINVAL, "plan is NULL");
+  if (p->host_tuples < 0)
+    return fail(TCL_EUNSUPPORTED, "the plan was mapped from a device-resident table: its "
+                                  "counts are on the device (tcl_plan_status, "
+                                  "tcl_plan_status_async)");
+  if (n_tuples) *n_tuples = p->host_tuples;
+  if (n_segments) *n_segments = p->host_segments;
+  return TCL_OK;
+}
+
+int tcl_plan_status_async(const tcl_plan *p, int32_t *dev_status, void *stream) {
+  if (!p || !dev_status) return fail(TCL_EINVAL, "plan and dev_status are required");
+  if (reinterpret_cast<uintptr_t>(dev_status) & 3)
+    return fail(TCL_EALIGN, "dev_status must be 4-byte aligned");
+  hipLaunchKernelGGL(status_copy_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     p->d.status, dev_status);
+  TCL_HIP(hipGetLastError());
+  return TCL_OK;
+}
 
 const char *tcl_version(void) { return "tclora 0.1 gfx950"; }
 
@@ -874,6 +1070,12 @@ int tcl_plan_copy_out(const tcl_plan *p, int32_t *tup_token, int32_t *tup_adapte
   return TCL_OK;
 }
 
-void tcl_plan_free(tcl_plan *p) { delete p; }
+void tcl_plan_free(tcl_plan *p) {
+  if (!p) return;
+  if (p->stage_pending) (void)hipEventSynchronize(p->stage_ev);
+  if (p->stage) (void)hipHostFree(p->stage);
+  if (p->stage_ev) (void)hipEventDestroy(p->stage_ev);
+  delete p;
+}
 
 }  // extern "C"

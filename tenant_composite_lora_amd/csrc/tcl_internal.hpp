@@ -45,7 +45,7 @@ constexpr int kSlotPad = TCL_MAX_PAIRS_PER_GROUP;
 constexpr int kPlanLdsInts = 32768;
 
 // Prefill expand on the matrix cores: tokens per tile, and the smallest token
-// count for which a plan prepares per-(token tile, segment) tuple ranges.
+// count for which a plan orders its tokens into such tiles.
 constexpr int kXTok = 64;
 constexpr int kMfmaMinTokens = 256;
 
@@ -54,7 +54,7 @@ constexpr int kMfmaMinTokens = 256;
 constexpr int kMaxMods = 8;
 
 // device status words
-enum { ST_CODE = 0, ST_TUPLES = 1, ST_SEGMENTS = 2, ST_ITEMS = 3, ST_WORDS = 64 };
+enum { ST_CODE = 0, ST_TUPLES = 1, ST_SEGMENTS = 2, ST_ITEMS = 3, ST_BUSY = 4, ST_WORDS = 64 };
 
 // error bits raised by the mapping kernel
 enum { EB_INVAL = 1, EB_UNSUP = 2, EB_NOSPC = 4 };
@@ -66,11 +66,11 @@ struct PlanLayout {
   int32_t mode;     // PLAN_DIRECT, PLAN_MULTI, PLAN_COUNT_LDS or PLAN_COUNT_GLOBAL
   int32_t blocks;   // PLAN_MULTI: workgroups of the local and scatter kernels
   int32_t threads;  // workgroup size of the mapping kernel (64, 256 or 1024)
-  int32_t tiles;    // token tiles of kXTok with tuple ranges (0: none)
+  int32_t tiles;    // token tiles of kXTok of the prefill expand (0: none)
   // byte offsets inside the device buffer
   size_t o_status, o_tok, o_ad, o_slot, o_alpha, o_toktuple, o_tokrec, o_tokn, o_tokptr,
-      o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_sseg, o_ranges,
-      o_tcount, o_mhist, o_mblk, o_msst, o_msib, total;
+      o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_sseg, o_ttok, o_ocnt,
+      o_mhist, o_mblk, o_msst, o_msib, o_tab, total;
 };
 
 // Mapping-stage algorithms: small tables run in one workgroup with the table
@@ -105,8 +105,8 @@ struct PlanDev {
   // base, -} [blocks][4],
   // per-adapter segment start and first work item [N]
   int32_t *m_hist, *m_blk, *m_sst, *m_sib;
-  int2 *ranges;  // [tiles][N]: tuples of segment u whose token lies in tile
-  int2 *tcount;  // [tiles]: {tuples, segments with tuples} of the tile
+  int32_t *tile_tok;  // [T]: token order of the prefill expand's tiles (ST_BUSY entries)
+  int32_t *ord_cnt;   // per-workgroup counts of the tile order launches
 };
 
 }  // namespace tcl
@@ -116,12 +116,21 @@ struct tcl_plan {
   tcl::PlanDev d;
   void *buf;
   size_t buf_bytes;
+  // host-resident tables (tcl_plan_map_host, tcl_plan_remap_host): a pinned
+  // staging copy the H2D copy reads from, and the event after that copy
+  void *stage = nullptr;
+  size_t stage_bytes = 0;
+  hipEvent_t stage_ev = nullptr;
+  bool stage_pending = false;
+  // tuple and segment counts known on the host (the last table was a host
+  // table, validated and counted there); -1 otherwise
+  int32_t host_tuples = -1, host_segments = -1;
 };
 
 namespace tcl {
-// Queue the per-(token tile, segment) tuple ranges and the per-tile totals of
-// p on stream s, behind the mapping kernel(s) that wrote the plan (no-op for
-// batches without token tiles).  Every mapping launch ends with it, so the
-// ranges always belong to the plan the stream last wrote.
-int plan_launch_ranges(const tcl_plan *p, hipStream_t s);
+// Queue the token order of the prefill expand's tiles of p on stream s,
+// behind the mapping kernel(s) that wrote the plan (no-op for batches without
+// token tiles).  Every mapping launch ends with it, so the order always
+// belongs to the plan the stream last wrote.
+int plan_launch_tile_order(const tcl_plan *p, hipStream_t s);
 }

@@ -31,7 +31,10 @@ EXPORTS = ["tcl_last_error", "tcl_version", "tcl_plan_bytes", "tcl_plan_map", "t
            "tcl_fused_shrink", "tcl_fused_expand", "tcl_remap_apply", "tcl_remap_shrink",
            "tcl_gate_topk", "tcl_factor_workspace_bytes",
            "tcl_factor_balanced", "tcl_rank_uniform", "tcl_rank_spectral",
-           "tcl_bam_create", "tcl_bam_free", "tcl_bam_acquire", "tcl_bam_slots", "tcl_lag_select"]
+           "tcl_bam_create", "tcl_bam_free", "tcl_bam_acquire", "tcl_bam_slots", "tcl_lag_select",
+           "tcl_module_init", "tcl_composites_validate", "tcl_plan_map_host",
+           "tcl_plan_remap_host", "tcl_plan_info", "tcl_plan_status_async",
+           "tcl_module_pack_bytes", "tcl_module_pack"]
 
 
 class TclError(RuntimeError):
@@ -52,7 +55,8 @@ class ModuleDesc(ctypes.Structure):
     _fields_ = [("n_adapters", ctypes.c_int32), ("d_in", ctypes.c_int32),
                 ("d_out", ctypes.c_int32), ("r_max", ctypes.c_int32),
                 ("wdtype", ctypes.c_int32), ("A_t", ctypes.c_void_p),
-                ("B_t", ctypes.c_void_p), ("k_dev", ctypes.c_void_p)]
+                ("B_t", ctypes.c_void_p), ("k_dev", ctypes.c_void_p),
+                ("B_k", ctypes.c_void_p)]
 
 
 _lib = None
@@ -78,6 +82,15 @@ def lib(path: Optional[str] = None):
     L.tcl_plan_free.argtypes = [vp]
     L.tcl_plan_free.restype = None
     L.tcl_module_load_ranks.argtypes = [ctypes.POINTER(ModuleDesc), vp, vp, vp]
+    L.tcl_module_init.argtypes = [ctypes.POINTER(ModuleDesc), vp, vp, vp]
+    L.tcl_composites_validate.argtypes = [ctypes.POINTER(Composites), ctypes.POINTER(i32),
+                                          ctypes.POINTER(i32)]
+    L.tcl_plan_map_host.argtypes = [ctypes.POINTER(Composites), vp, sz, vp, ctypes.POINTER(vp)]
+    L.tcl_plan_remap_host.argtypes = [vp, ctypes.POINTER(Composites), vp]
+    L.tcl_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.tcl_plan_status_async.argtypes = [vp, vp, vp]
+    L.tcl_module_pack_bytes.argtypes = [ctypes.POINTER(ModuleDesc), ctypes.POINTER(sz)]
+    L.tcl_module_pack.argtypes = [ctypes.POINTER(ModuleDesc), vp, sz, vp]
     L.tcl_workspace_bytes.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, ctypes.POINTER(sz)]
     L.tcl_shrink.argtypes = [vp, ctypes.POINTER(ModuleDesc), vp, i64, i32, vp, vp]
     L.tcl_expand.argtypes = [vp, ctypes.POINTER(ModuleDesc), vp, vp, i64, i32, vp]
@@ -141,6 +154,35 @@ def plan_bytes(n_tokens: int, n_groups: int, n_pairs: int, n_adapters: int,
     return out.value
 
 
+def _host_table(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha):
+    import numpy as np
+    return (np.ascontiguousarray(group_tok_ptr, dtype=np.int32),
+            np.ascontiguousarray(group_pair_ptr, dtype=np.int32),
+            np.ascontiguousarray(pair_adapter, dtype=np.int32),
+            np.ascontiguousarray(pair_alpha, dtype=np.float32))
+
+
+def _host_composites(arrs, n_tokens: int, n_adapters: int, max_tuples: int) -> Composites:
+    gtp, gpp, pa, pw = arrs
+    ptr = lambda a: a.ctypes.data if a.size else None  # noqa: E731
+    return Composites(int(n_tokens), gtp.shape[0] - 1, pa.shape[0], int(n_adapters),
+                      int(max_tuples), ptr(gtp), ptr(gpp), ptr(pa), ptr(pw))
+
+
+def validate_composites(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+                        n_adapters: int, n_tokens: Optional[int] = None,
+                        max_tuples: Optional[int] = None):
+    """Host-side check of a HOST-resident table (tcl_composites_validate, no
+    GPU): returns (status code, tuples, segments)."""
+    arrs = _host_table(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha)
+    T = int(arrs[0][-1]) if n_tokens is None and arrs[0].size else int(n_tokens or 0)
+    cap = (1 << 31) - 1 if max_tuples is None else int(max_tuples)
+    c = _host_composites(arrs, T, n_adapters, cap)
+    P, U = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = lib().tcl_composites_validate(ctypes.byref(c), ctypes.byref(P), ctypes.byref(U))
+    return rc, P.value, U.value
+
+
 class Plan:
     """A mapped batch: tuples reordered by adapter id plus the token index.
 
@@ -195,6 +237,62 @@ class Plan:
         check(lib().tcl_plan_remap(self.handle, ctypes.byref(self._c), _stream(self.device, stream)))
         self.n_tokens, self.n_groups, self.n_pairs = int(n_tokens), G, NP
 
+    @classmethod
+    def from_host(cls, group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+                  n_adapters: int, device, n_tokens: Optional[int] = None,
+                  max_tuples: Optional[int] = None, buf: Optional[torch.Tensor] = None,
+                  stream=None) -> "Plan":
+        """A plan from a HOST-resident table (numpy arrays): validated on the
+        host (tcl_plan_map_host), then copied and mapped on the device."""
+        import numpy as np
+        arrs = _host_table(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha)
+        gtp, gpp, pa, pw = arrs
+        G, NP = gtp.shape[0] - 1, pa.shape[0]
+        T = int(gtp[-1]) if n_tokens is None else int(n_tokens)
+        if max_tuples is None:
+            max_tuples = int((np.diff(gtp.astype(np.int64)) * np.diff(gpp.astype(np.int64))).sum())
+        self = cls.__new__(cls)
+        self.device = torch.device(device)
+        self.n_tokens, self.n_groups, self.n_pairs = T, G, NP
+        self.n_adapters, self.max_tuples = int(n_adapters), int(max_tuples)
+        nbytes = plan_bytes(T, G, NP, self.n_adapters, self.max_tuples)
+        if buf is None:
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        self.buf = buf
+        self._inputs = None
+        self._c = _host_composites(arrs, T, self.n_adapters, self.max_tuples)
+        h = ctypes.c_void_p(0)
+        check(lib().tcl_plan_map_host(ctypes.byref(self._c), buf.data_ptr(), buf.numel(),
+                                      _stream(self.device, stream), ctypes.byref(h)))
+        self.handle = h
+        return self
+
+    def remap_host(self, group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
+                   n_tokens: Optional[int] = None, stream=None) -> None:
+        """Re-map with a HOST-resident table (tcl_plan_remap_host)."""
+        arrs = _host_table(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha)
+        T = int(arrs[0][-1]) if n_tokens is None else int(n_tokens)
+        c = _host_composites(arrs, T, self.n_adapters, self.max_tuples)
+        check(lib().tcl_plan_remap_host(self.handle, ctypes.byref(c),
+                                        _stream(self.device, stream)))
+        self._inputs = None
+        self.n_tokens, self.n_groups, self.n_pairs = T, arrs[0].shape[0] - 1, arrs[2].shape[0]
+
+    def info(self):
+        """(rc, tuples, segments) known on the host (tcl_plan_info)."""
+        P, U = ctypes.c_int32(0), ctypes.c_int32(0)
+        rc = lib().tcl_plan_info(self.handle, ctypes.byref(P), ctypes.byref(U))
+        return rc, P.value, U.value
+
+    def status_async(self, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """Queues a copy of {code, tuples, segments, items} into a device int32
+        tensor of 4 entries (tcl_plan_status_async); no synchronisation."""
+        if out is None:
+            out = torch.empty(4, dtype=torch.int32, device=self.device)
+        check(lib().tcl_plan_status_async(self.handle, out.data_ptr(),
+                                          _stream(self.device, stream)))
+        return out
+
     def status(self, stream=None):
         P, U = ctypes.c_int32(0), ctypes.c_int32(0)
         rc = lib().tcl_plan_status(self.handle, _stream(self.device, stream), ctypes.byref(P),
@@ -237,9 +335,12 @@ class Plan:
 class Module:
     """One projection's adapter pool: A_t [N, r_max, d_in], B_t [N, r_max,
     d_out] (rank-major, bf16 or fp32, on the GPU) and optional effective
-    ranks k (host ints, loaded to the device once)."""
+    ranks k (host ints, loaded to the device once).  bf16 pools also get the
+    rank-contiguous copy of B the prefill expand reads (tcl_module_pack)
+    unless ``pack`` is False."""
 
-    def __init__(self, A_t: torch.Tensor, B_t: torch.Tensor, k=None, stream=None):
+    def __init__(self, A_t: torch.Tensor, B_t: torch.Tensor, k=None, stream=None,
+                 pack: bool = True):
         if A_t.dim() != 3 or B_t.dim() != 3 or A_t.shape[:2] != B_t.shape[:2]:
             raise ValueError("A_t and B_t must be [N, r_max, d] with equal N and r_max")
         if A_t.dtype != B_t.dtype:
@@ -257,10 +358,20 @@ class Module:
             if kh.shape != (N,):
                 raise ValueError("k must have one entry per adapter")
             self.k_dev = torch.empty(N, dtype=torch.int32, device=A_t.device)
-            check(lib().tcl_module_load_ranks(ctypes.byref(self.desc),
-                                              kh.ctypes.data_as(ctypes.c_void_p),
-                                              self.k_dev.data_ptr(),
-                                              _stream(A_t.device, stream)))
+            check(lib().tcl_module_init(ctypes.byref(self.desc),
+                                        kh.ctypes.data_as(ctypes.c_void_p),
+                                        self.k_dev.data_ptr(), _stream(A_t.device, stream)))
+        else:
+            check(lib().tcl_module_init(ctypes.byref(self.desc), None, None,
+                                        _stream(A_t.device, stream)))
+        self.B_k = None
+        if pack and self.desc.wdtype == BF16:
+            nb = ctypes.c_size_t(0)
+            check(lib().tcl_module_pack_bytes(ctypes.byref(self.desc), ctypes.byref(nb)))
+            self.B_k = torch.empty(max(nb.value // 2, 8), dtype=torch.bfloat16,
+                                   device=A_t.device)
+            check(lib().tcl_module_pack(ctypes.byref(self.desc), self.B_k.data_ptr(), nb.value,
+                                        _stream(A_t.device, stream)))
 
     @property
     def n_adapters(self):

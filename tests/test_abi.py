@@ -148,3 +148,154 @@ def test_gate_host_errors(L):
     assert call(T=1 << 30, k=4, C=8) == tclora.EINVAL  # T * k beyond 32-bit indexing
     assert call(lg=P + 2) == tclora.EALIGN
     assert b"gate" in L.tcl_last_error()
+
+
+# ---------------------------------------------------------------------------
+# host-resident composite tables: validated on the host, before any HIP call
+# ---------------------------------------------------------------------------
+
+def _mutations(seed, n):
+    """Random tables with random defects (or none): every error class of the
+    validation, alone and together, over a few hundred groups."""
+    from tenant_composite_lora_amd import workloads as W
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        T = int(rng.integers(0, 60))
+        base = W.random_case(int(rng.integers(1 << 30)), T=max(T, 1), N=12, d_in=8, d_out=8,
+                             r_max=2, max_pairs=6, empty_frac=0.2,
+                             tokens_per_group=int(rng.integers(1, 4))).composites
+        gt = base.group_tok_ptr.astype(np.int64).copy()
+        gp = base.group_pair_ptr.astype(np.int64).copy()
+        ad = base.pair_adapter.astype(np.int64).copy()
+        al = base.pair_alpha.astype(np.float32).copy()
+        N, Tn = base.n_adapters, base.n_tokens
+        cap = None
+        kinds = rng.choice(9, size=int(rng.integers(0, 3)), replace=False)
+        for k in kinds:
+            G, NP = len(gt) - 1, len(ad)
+            if k == 0 and NP:
+                ad[rng.integers(NP)] = rng.choice([-1, N, N + 7])
+            elif k == 1 and NP:
+                al[rng.integers(NP)] = rng.choice([np.nan, np.inf, -np.inf])
+            elif k == 2 and G > 1:
+                g = int(rng.integers(1, G))
+                gt[g] = gt[g - 1] - 1 if gt[g - 1] > 0 else gt[g + 1] + 1
+            elif k == 3 and G > 1:
+                g = int(rng.integers(1, G))
+                gp[g] = gp[g + 1] + 1
+            elif k == 4:
+                Tn += 1
+            elif k == 5:
+                for g in range(G):
+                    if gp[g + 1] - gp[g] >= 2:
+                        ad[gp[g] + 1] = ad[gp[g]]
+                        break
+            elif k == 6:
+                # a group of 70 pairs appended (beyond the limit)
+                ad = np.concatenate([ad, np.arange(70) % N + 0]).astype(np.int64)
+                ad[-70:] = np.arange(70)
+                N = max(N, 70)
+                al = np.concatenate([al, np.ones(70, np.float32)])
+                gp = np.concatenate([gp, [gp[-1] + 70]])
+                gt = np.concatenate([gt, [gt[-1] + 1]])
+                Tn += 1
+            elif k == 7:
+                P = int(np.sum(np.diff(gt).clip(0) * np.diff(gp).clip(0)))
+                cap = max(P - 1, 0)
+            elif k == 8:
+                gp[-1] += 1
+        yield i, gt, gp, ad, al, Tn, N, cap
+
+
+def _validate_both(gt, gp, ad, al, T, N, cap):
+    import oracle as O
+    want = O.validate(gt, gp, ad.astype(np.int32), al, T, N, max_tuples=cap)
+    rc, P, U = tclora.validate_composites(gt, gp, ad, al, N, n_tokens=T, max_tuples=cap)
+    return want, rc, P, U
+
+
+def test_host_validation_matches_oracle_on_hand_tables():
+    """Every hand-made defect (and the defect-free tables) gets the oracle's
+    code, including the precedence of EINVAL over EUNSUPPORTED over
+    ENOSPC."""
+    from test_gpu_parity import _bad_large_tables, _bad_tables, _pad_groups
+    for name, (tp, pp, ad, al, T, cap) in _bad_tables().items():
+        N = 80 if name.startswith("too_many_pairs") else 4
+        for padded in (False, True):
+            tq, pq = _pad_groups(tp, pp, 1100) if padded else (tp, pp)
+            want, rc, _, _ = _validate_both(np.array(tq), np.array(pq), np.array(ad),
+                                            np.array(al, np.float32), T, N, cap)
+            assert rc == want, (name, padded, rc, want)
+    for name, (tp, pp, ad, al, T, N, cap) in _bad_large_tables().items():
+        want, rc, _, _ = _validate_both(tp, pp, ad, al, T, N, cap)
+        assert rc == want, (name, rc, want)
+
+
+def test_host_validation_matches_oracle_on_random_defects():
+    import oracle as O
+    seen = set()
+    for i, gt, gp, ad, al, T, N, cap in _mutations(5, 400):
+        want, rc, P, U = _validate_both(gt, gp, ad, al, T, N, cap)
+        assert rc == want, (i, rc, want)
+        seen.add(want)
+        if rc == 0:
+            pl = O.plan(gt, gp, ad.astype(np.int32), al)
+            assert P == len(pl["tup_token"]) and U == len(pl["seg_adapter"])
+    assert seen == {O.OK, O.EINVAL, O.EUNSUPPORTED, O.ENOSPC}
+
+
+def test_host_plan_map_rejects_before_any_hip_call(L):
+    """A bad host table is refused with its code before the library touches
+    the GPU (this container has none: a HIP call would fail with EHIP)."""
+    from test_gpu_parity import _bad_tables
+    h = ctypes.c_void_p(0)
+    for name, (tp, pp, ad, al, T, cap) in _bad_tables().items():
+        if name == "fits_capacity":
+            continue
+        N = 80 if name.startswith("too_many_pairs") else 4
+        arrs = tclora._host_table(tp, pp, ad, al)
+        c = tclora._host_composites(arrs, T, N, cap if cap is not None else 16)
+        import oracle as O
+        want = O.validate(np.array(tp), np.array(pp), np.array(ad, np.int32),
+                          np.array(al, np.float32), T, N, max_tuples=cap)
+        assert want != 0
+        rc = L.tcl_plan_map_host(ctypes.byref(c), 0x10000, 1 << 30, None, ctypes.byref(h))
+        assert rc == want, (name, rc, want)
+        assert h.value is None
+        assert len(L.tcl_last_error()) > 0
+
+
+def test_plan_info_and_status_async_host_errors(L):
+    P, U = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert L.tcl_plan_info(None, ctypes.byref(P), ctypes.byref(U)) == tclora.EINVAL
+    assert L.tcl_plan_status_async(None, 0x1000, None) == tclora.EINVAL
+    assert L.tcl_plan_remap_host(None, None, None) == tclora.EINVAL
+
+
+def test_module_init_host_errors(L):
+    ok = dict(n=4, d_in=16, d_out=16, r=8, dt=tclora.BF16, A=0x1000, B=0x2000)
+
+    def m(**kw):
+        a = {**ok, **kw}
+        return tclora.ModuleDesc(a["n"], a["d_in"], a["d_out"], a["r"], a["dt"], a["A"], a["B"],
+                                 None)
+
+    k = np.array([0, 8, 3, 1], np.int32)
+    kp = k.ctypes.data_as(ctypes.c_void_p)
+    assert L.tcl_module_init(None, kp, 0x3000, None) == tclora.EINVAL
+    assert L.tcl_module_init(ctypes.byref(m(A=0)), kp, 0x3000, None) == tclora.EINVAL
+    assert L.tcl_module_init(ctypes.byref(m(n=0)), kp, 0x3000, None) == tclora.EINVAL
+    assert L.tcl_module_init(ctypes.byref(m(r=65)), kp, 0x3000, None) == tclora.EUNSUPPORTED
+    assert L.tcl_module_init(ctypes.byref(m(r=0)), kp, 0x3000, None) == tclora.EUNSUPPORTED
+    assert L.tcl_module_init(ctypes.byref(m(d_in=12)), kp, 0x3000, None) == tclora.EALIGN
+    assert L.tcl_module_init(ctypes.byref(m(A=0x1008)), kp, 0x3000, None) == tclora.EALIGN
+    assert L.tcl_module_init(ctypes.byref(m(dt=7)), kp, 0x3000, None) == tclora.EINVAL
+    bad = np.array([0, 9, 3, 1], np.int32)
+    assert L.tcl_module_init(ctypes.byref(m()), bad.ctypes.data_as(ctypes.c_void_p), 0x3000,
+                             None) == tclora.EINVAL
+    assert L.tcl_module_init(ctypes.byref(m()), kp, None, None) == tclora.EINVAL
+    # no ranks: every adapter at r_max, no GPU call
+    d = m()
+    d.k_dev = 0x5000
+    assert L.tcl_module_init(ctypes.byref(d), None, None, None) == tclora.OK
+    assert d.k_dev is None

@@ -141,13 +141,12 @@ def test_cpu_baseline_uses_the_cores_it_names():
     assert "3 contiguous token ranges" in out["sample"]
 
 
-def test_dense_tiles_rule(bench):
-    """Tiles of 64 tokens: dense when the adapters a tile's tokens hold carry
-    at least 8 of its tuples each on average."""
-    T = 256
-    ads = [[0, 1]] * 64 + [[t % 50, 50 + t % 13] for t in range(64)] + [[]] * 64 + [[3]] * 64
-    als = [[0.5] * len(a) for a in ads]
-    wl = W.random_case(1, T=T, N=64, d_in=32, d_out=32, r_max=4, max_pairs=1)
-    wl.composites = W.csr_from_token_lists(ads, als, 64)
-    assert bench.dense_tiles(wl) == (2, 3, 4)
-    assert bench.kernel_names(wl, False)["expand"].startswith("expand_mfma + expand_kernel_split")
+def test_kernel_names_follow_dispatch(bench):
+    """The bench names the kernels the library's dispatch picks: the paired
+    prefill shrink from 1024 pair jobs on, the token-tile expand for
+    prefill-sized bf16 batches."""
+    k5 = bench.kernel_names(W.make(4), False)
+    assert k5["shrink"] == "shrink_mfma" and k5["expand"].startswith("expand_tile")
+    small = W.random_case(1, T=40, N=8, d_in=32, d_out=32, r_max=8, max_pairs=2)
+    k = bench.kernel_names(small, True)
+    assert k["shrink"] == "plan_shrink" and k["expand"] == "expand_kernel"

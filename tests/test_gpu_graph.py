@@ -14,7 +14,7 @@ import torch
 from gpu_util import composites_to_dev, make_module, to_dev
 from tenant_composite_lora_amd import tclora
 from tenant_composite_lora_amd import workloads as W
-from test_gpu_mfma import MFMA_CASES
+from test_gpu_tile import MFMA_CASES
 from test_gpu_parity import CASES, banner
 
 pytestmark = pytest.mark.gpu

@@ -371,26 +371,26 @@ def test_bf16_output():
 
 @pytest.mark.parametrize("name", ["config4", "mfma_ragged", "mfma_ranks24", "mfma_static"])
 def test_prefill_paths_agree(name, monkeypatch):
-    """The matrix-core expand and the per-token VALU expand on the same batch:
-    both within tolerance of the oracle, and of each other."""
+    """The token-tile expand on the matrix cores and the per-token VALU expand
+    on the same batch: both within tolerance of the oracle."""
     wl = CASES[name]()
-    banner(f"valu vs mfma expand {name}")
+    banner(f"valu vs tile expand {name}")
     monkeypatch.setenv("TCL_DISPATCH", "valu")
     a, _, _ = run_fused(wl)
-    monkeypatch.setenv("TCL_DISPATCH", "mfma")
+    monkeypatch.delenv("TCL_DISPATCH", raising=False)
     b, _, _ = run_fused(wl)
     for mi in range(len(wl.modules)):
         _, d_ora = oracle_apply(wl, mi)
         base = wl.y_base[mi].astype(np.float64)
         ea, eb = rel_err(a[mi] - base, d_ora), rel_err(b[mi] - base, d_ora)
-        print(f"  module {mi}: valu rel {ea:.3e}, mfma rel {eb:.3e}", flush=True)
+        print(f"  module {mi}: valu rel {ea:.3e}, tile rel {eb:.3e}", flush=True)
         assert ea <= TOL[wl.dtype] and eb <= TOL[wl.dtype]
 
 
-def test_mfma_bf16_output(monkeypatch):
+def test_tile_bf16_output(monkeypatch):
     wl = edge("mfma_ragged")
-    banner("mfma expand with bf16 y")
-    monkeypatch.setenv("TCL_DISPATCH", "mfma")
+    banner("tile expand with bf16 y")
+    monkeypatch.delenv("TCL_DISPATCH", raising=False)
     yb16 = W.f32_to_bf16_bits(wl.y_base[0])
     wl2 = W.Workload(wl.name, wl.dtype, wl.n_adapters, wl.composites, wl.modules, wl.x,
                      [W.bf16_bits_to_f32(yb16)])

@@ -17,7 +17,7 @@ import torch
 from gpu_util import make_module, make_plan, run_fused, run_split
 from tenant_composite_lora_amd import tclora
 from tenant_composite_lora_amd import workloads as W
-from test_gpu_mfma import BF16_NAN, MFMA_CASES, _check
+from test_gpu_tile import BF16_NAN, MFMA_CASES, _check
 from test_gpu_parity import CASES, banner
 
 pytestmark = pytest.mark.gpu
