@@ -939,11 +939,12 @@ constexpr int kRMaxWords = 128;  // adapter bitmap words: pools of at most 4096 
 // offset, -}, the tile's tokens, their slot counts, octet table A (first
 // 16-byte unit of the octet in the packed pool), octet table B (union entry |
 // octet in adapter << 9 | adapter's octets << 12), then at the offsets the
-// header gives: idx [64][U] int16 and the coefficient octets [C].
+// header gives: idx [64][U] int16 and the coefficient octets [C + 8] (the
+// last eight zero).
 constexpr int kRTok = 8;
 constexpr int kRTokN = kRTok + kXTok;
 constexpr int kROctA = kRTokN + kXTok;
-constexpr int kRWords = kROctA + 2 * kRHcap + kXTok * kRMaxU / 2 + 4 + 4 * kRMaxCoef;
+constexpr int kRWords = kROctA + 2 * kRHcap + kXTok * kRMaxU / 2 + 4 + 4 * (kRMaxCoef + 8);
 static_assert(kROctA % 4 == 0 && kRWords % 4 == 0, "record regions of whole 16-byte units");
 static_assert(kXTok * 4 == 256, "four threads per token of a tile");
 
@@ -958,6 +959,7 @@ struct TileArgs {
   // the data, [d_out][ceil(k / 8)] octets per adapter
   const int32_t *bk_off[kMaxMods];
   const uint4 *bk_data[kMaxMods];
+  const uint4 *bk_zero[kMaxMods];  // a zero 16-byte unit of each packed pool
   ModArgs m[kMaxMods];  // first = first job; n_ct = column tiles of kXCols
 };
 
@@ -1101,6 +1103,8 @@ __global__ __launch_bounds__(256) void tile_prep(TileArgs e) {
   if (H > kRHcap || C > kRMaxCoef) return header(Q, H, 0, C, nU, 0, 0);
   const int oidx = kROctA + 2 * H;                   // int16 [64][nU]
   const int ocoef = (oidx + (kXTok * nU + 1) / 2 + 3) & ~3;  // 16-byte aligned
+  // the coefficient octets are followed by eight zero octets, the entry of
+  // every (token, union entry) pair the tile does not hold
   if (tid == 0) u_h0[nU] = H;
   __syncthreads();
   for (int h = tid; h < H; h += 256) {
@@ -1109,9 +1113,9 @@ __global__ __launch_bounds__(256) void tile_prep(TileArgs e) {
     rec[kROctA + h] = bk_off[u_a[i]] + oi;
     rec[kROctA + H + h] = i | (oi << 9) | (octs << 12);
   }
-  // per (token, union entry): first coefficient octet, or -1
+  // per (token, union entry): first coefficient octet, or the zero octets
   int16_t *idx = reinterpret_cast<int16_t *>(rec + oidx);
-  for (int i = tid; i < kXTok * nU; i += 256) idx[i] = -1;
+  for (int i = tid; i < kXTok * nU; i += 256) idx[i] = int16_t(C);
   __syncthreads();
   for (int s = sub; s < nr; s += 4) {
     const int q = offr + s;
@@ -1141,6 +1145,7 @@ __global__ __launch_bounds__(256) void tile_prep(TileArgs e) {
     }
     coef[f] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   }
+  if (tid < 8) coef[C + tid] = make_uint4(0, 0, 0, 0);
   header(Q, H, 1, C, nU, oidx, ocoef);
 }
 
@@ -1203,7 +1208,7 @@ __device__ void tile_fallback(const TileArgs &e, int sel, const int *tok, int cw
 
 template <typename TY>
 __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
-  __shared__ __align__(16) int rl[kRWords];  // the tile's record
+  __shared__ __align__(16) int rl[kRWords + 256];  // the tile's record (+ a chunk)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
   // XCD-aware job index: each XCD takes a contiguous range of jobs, which
   // run the tiles of one column block in turn (its packed B columns stay in
@@ -1233,11 +1238,25 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
     tile_fallback<TY>(e, sel, rl + kRTok, cw);
     return;
   }
-  const int used = ocoef + 4 * C;  // words, a multiple of 4
-  for (int i = kROctA / 4 + tid; i < used / 4; i += 256)
-    reinterpret_cast<uint4 *>(rl)[i] = reinterpret_cast<const uint4 *>(rg)[i];
-  // y of the tile's tokens into the accumulators (issued after the record's
-  // loads, so that waiting for the record does not wait for y)
+  // the rest of the record in use, copied straight into LDS (no registers):
+  // wave w takes 1 KiB chunks w, w + 4, ... (past the used part the lanes
+  // repeat its last 16 bytes; rl has room for a whole last chunk)
+  const int used4 = (ocoef + 4 * (C + 8)) / 4;
+  {
+    const int nchunk = (used4 - kROctA / 4 + 63) / 64;
+    const uint4 *src = reinterpret_cast<const uint4 *>(rg);
+    uint4 *dst = reinterpret_cast<uint4 *>(rl);
+    for (int c = w; c < nchunk; c += 4) {
+      const int j = kROctA / 4 + c * 64;
+      __builtin_amdgcn_global_load_lds(src + min(j + lane, used4 - 1), dst + j, 16, 0, 0);
+    }
+  }
+  lds_barrier();  // (the compiler waits for the copies before it)
+  // y of the tile's tokens into the accumulators.  Every load of this
+  // kernel is issued whatever its lane's condition (at a clamped address,
+  // masked afterwards where it matters): loads under per-lane branches keep
+  // the compiler from counting them, and it then waits for all of them at
+  // once.
   f32x4_t acc[4][4];  // [column block][token block]
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
@@ -1245,47 +1264,42 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int col = cw + 16 * nb + 4 * kg;
-      acc[nb][tb] = (t >= 0 && col < d) ? load_y4(Y + int64_t(t) * ld + col)
-                                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc[nb][tb] = load_y4(Y + int64_t(max(t, 0)) * ld + min(col, d - 4));
     }
   }
-  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   const int *octA = rl + kROctA, *octB = rl + kROctA + H;
   const int16_t *idx = reinterpret_cast<const int16_t *>(rl + oidx);
   const uint4 *coef = reinterpret_cast<const uint4 *>(rl + ocoef);
   const int nsteps = (H + 3) >> 2;
   // packed-pool octets of this lane's column in the four 16-column blocks
+  // (lanes past the union or past d_out read the pool's zero unit, so no
+  // loaded value needs masking: a mask would wait for the load at once)
+  const uint4 *Bz = e.bk_zero[sel];
   auto load = [&](uint4 (&a)[4], int st) {
     const int h = 4 * st + kg;
-    int base = 0, stride = 0;
     const bool in = h < H;
-    if (in) {
-      base = octA[h];
-      stride = (octB[h] >> 12) & 0xf;
-    }
-    const uint4 *src = Bk + int64_t(base) + int64_t(cw + r16) * stride;
+    const int hc = in ? h : 0;
+    const int base = octA[hc], stride = (octB[hc] >> 12) & 0xf;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      a[nb] = in && cw + 16 * nb + r16 < d ? src[int64_t(16 * nb) * stride]
-                                           : make_uint4(0, 0, 0, 0);
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = cw + 16 * nb + r16;
+      const uint4 *src = in && n < d ? Bk + (int64_t(base) + int64_t(n) * stride) : Bz;
+      a[nb] = *src;
+    }
   };
-  // coefficient octets of this lane's token in the four 16-token blocks, then
-  // the step on the matrix cores
-  auto mult = [&](const uint4 (&a)[4], int st) {
+  // coefficient octets of this lane's token in the four 16-token blocks
+  // (zero where the token does not hold the octet's adapter)
+  // (a token without the octet's adapter reads the record's zero octets;
+  // past the union the pool octets are zero, so any finite value serves)
+  auto coefs = [&](uint4 (&b)[4], int st) {
     const int h = 4 * st + kg;
-    int ui = 0, oi = 0;
-    const bool in = h < H;
-    if (in) {
-      const int pk = octB[h];
-      ui = pk & 0x1ff;
-      oi = (pk >> 9) & 7;
-    }
-    uint4 b[4];
+    const int pk = octB[h < H ? h : 0];
+    const int ui = pk & 0x1ff, oi = (pk >> 9) & 7;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int c = in ? idx[(16 * tb + r16) * U + ui] : -1;
-      b[tb] = c >= 0 ? coef[c + oi] : make_uint4(0, 0, 0, 0);
-    }
+    for (int tb = 0; tb < 4; ++tb) b[tb] = coef[idx[(16 * tb + r16) * U + ui] + oi];
+  };
+  auto mult = [&](const uint4 (&a)[4], const uint4 (&b)[4]) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -1294,21 +1308,37 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
             __builtin_bit_cast(bf16x8_t, a[nb]), __builtin_bit_cast(bf16x8_t, b[tb]),
             acc[nb][tb], 0, 0, 0);
   };
-  uint4 a0[4], a1[4], a2[4];
+  // B three steps ahead of the matrix cores, the coefficients one step
+  // ahead.  Scheduling barriers keep the loads in program order, so that
+  // each step waits only for its own operands (the memory counter is in
+  // order) and the later steps' loads stay in flight.
+  uint4 a0[4], a1[4], a2[4], b0[4], b1[4];
   load(a0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   load(a1, 1);
+  __builtin_amdgcn_sched_barrier(0);
   load(a2, 2);
-  for (int st = 0; st < nsteps; st += 3) {
-    mult(a0, st);
-    load(a0, st + 3);
-    if (st + 1 < nsteps) {
-      mult(a1, st + 1);
-      load(a1, st + 4);
-    }
-    if (st + 2 < nsteps) {
-      mult(a2, st + 2);
-      load(a2, st + 5);
-    }
+  __builtin_amdgcn_sched_barrier(0);
+  coefs(b0, 0);
+  auto step = [&](uint4 (&a)[4], const uint4 (&b)[4], uint4 (&bn)[4], int st) {
+    coefs(bn, st + 1);
+    mult(a, b);
+    __builtin_amdgcn_sched_barrier(0);
+    load(a, st + 3);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int st = 0; st < nsteps; st += 6) {
+    step(a0, b0, b1, st);
+    if (st + 1 >= nsteps) break;
+    step(a1, b1, b0, st + 1);
+    if (st + 2 >= nsteps) break;
+    step(a2, b0, b1, st + 2);
+    if (st + 3 >= nsteps) break;
+    step(a0, b1, b0, st + 3);
+    if (st + 4 >= nsteps) break;
+    step(a1, b0, b1, st + 4);
+    if (st + 5 >= nsteps) break;
+    step(a2, b1, b0, st + 5);
   }
   // y = accumulators, for tokens that hold at least one pair
 #pragma unroll
@@ -1334,9 +1364,11 @@ constexpr int kPackThreads = 1024;
 
 __global__ __launch_bounds__(kPackThreads) void pack_offsets_kernel(const int32_t *k_dev,
                                                                     int32_t N, int32_t r_max,
-                                                                    int32_t d, int32_t *off) {
+                                                                    int32_t d, int32_t *off,
+                                                                    uint4 *zero) {
   __shared__ int tmp[kPackThreads / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) *zero = make_uint4(0, 0, 0, 0);
   int base = 0;
   for (int a0 = 0; a0 < N; a0 += kPackThreads) {
     const int a = a0 + threadIdx.x;
@@ -1621,9 +1653,10 @@ static bool use_tile_expand(const tcl_plan *p, const tcl_module *mods, int n) {
 
 static int r_pad(const tcl_module *m) { return (m->r_max + 7) / 8 * 8; }
 
-// bytes before the packed data: the adapters' first 16-byte units
+// bytes before the packed data: the adapters' first 16-byte units, then a
+// zero 16-byte unit right before the data
 static size_t pack_head_bytes(const tcl_module *m) {
-  return (size_t(m->n_adapters) * 4 + 255) & ~size_t(255);
+  return (size_t(m->n_adapters) * 4 + 16 + 255) & ~size_t(255);
 }
 
 static int n_tiles(const tcl_plan *p) { return (p->L.T + kXTok - 1) / kXTok; }
@@ -1667,6 +1700,7 @@ static int launch_expand_tile(const tcl_plan *p, const tcl_module *mods, int n,
     e.bk_off[i] = static_cast<const int32_t *>(mods[i].B_k);
     e.bk_data[i] = reinterpret_cast<const uint4 *>(static_cast<const char *>(mods[i].B_k) +
                                                    pack_head_bytes(&mods[i]));
+    e.bk_zero[i] = e.bk_data[i] - 1;
   }
   if (jobs > (int64_t(1) << 30)) return fail(TCL_EUNSUPPORTED, "expand grid too large");
   e.jobs = int32_t(jobs);
@@ -1865,7 +1899,8 @@ int tcl_module_pack(tcl_module *m, void *B_k, size_t bytes, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t *off = static_cast<int32_t *>(B_k);
   hipLaunchKernelGGL(pack_offsets_kernel, dim3(1), dim3(kPackThreads), 0, s, m->k_dev,
-                     m->n_adapters, m->r_max, m->d_out, off);
+                     m->n_adapters, m->r_max, m->d_out, off,
+                     reinterpret_cast<uint4 *>(static_cast<char *>(B_k) + pack_head_bytes(m)) - 1);
   hipLaunchKernelGGL(pack_b_kernel, dim3(unsigned(grid)), dim3(256), 0, s,
                      static_cast<const uint16_t *>(m->B_t), m->k_dev, m->n_adapters, m->r_max,
                      m->d_out, off,
