@@ -97,14 +97,23 @@ def kernel_bytes(wl) -> dict:
 # HIP sources each kernel is built from: a stored counter summary is only
 # valid while these are unchanged
 KERNEL_SOURCES = {k: ("plan.hip", "plan_core.hpp", "tcl_internal.hpp")
-                  for k in ("plan_kernel", "tile_ranges_kernel", "tile_ranges_tok_kernel",
+                  for k in ("plan_kernel", "tile_order_count", "tile_order_place",
                             "plan_m_local", "plan_m_scan", "plan_m_scatter")}
+KERNEL_SOURCES.update({k: ("tile.hip", "kern_common.hpp", "tcl_internal.hpp")
+                       for k in ("tile_prep", "expand_tile", "pack_offsets_kernel",
+                                 "pack_b_kernel")})
 KERNEL_SOURCES["gate_topk_kernel"] = ("gate.hip", "tcl_internal.hpp")
 # the producer's four kernels are summarised per fleet under the entry point's name
 KERNEL_SOURCES["tcl_factor_balanced"] = ("factor.hip", "tcl_internal.hpp")
 FACTOR_KERNELS = ("tsqr_leaf", "gram_kernel", "factor_core", "factor_out")
 PRODUCER_WORKLOAD = "llama31_8b_fleet_35x32x7_r16"
-APPLY_SOURCES = ("apply.hip", "plan_core.hpp", "tcl_internal.hpp")
+APPLY_SOURCES = ("apply.hip", "kern_common.hpp", "plan_core.hpp", "tcl_internal.hpp")
+# library kernels the counter summary keeps apart (whole identifiers of the
+# demangled names)
+PMC_KERNELS = ("plan_shrink", "shrink_mfma", "shrink_mfma_pair", "shrink_valu", "expand_kernel",
+               "tile_prep", "expand_tile", "tile_order_count", "tile_order_place",
+               "pack_offsets_kernel", "pack_b_kernel", "plan_kernel", "plan_m_local",
+               "plan_m_scan", "plan_m_scatter", "gate_topk_kernel")
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -117,9 +126,10 @@ def kernel_source_hash(kernel: str) -> str:
 
 
 def stored_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (profiles/pmc_traffic.txt), or None when there is none for this
-    workload or the kernel's sources changed since it was taken."""
+    """HBM bytes per launch of `kernel` ("a+b": the sum over kernels launched
+    back to back) from the committed rocprofv3 counter summary
+    (profiles/pmc_traffic.txt), or None when any part has no entry for this
+    workload or its sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -127,10 +137,13 @@ def stored_traffic(workload: str, kernel: str):
         rec = json.load(open(path))
     except ValueError:
         return None
-    ent = rec.get("entries", {}).get(f"{workload}:{kernel}")
-    if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
-        return None
-    return ent.get("hbm_bytes_per_launch")
+    total = 0.0
+    for k in kernel.split("+"):
+        ent = rec.get("entries", {}).get(f"{workload}:{k}")
+        if not ent or ent.get("source_hash") != kernel_source_hash(k):
+            return None
+        total += ent.get("hbm_bytes_per_launch")
+    return total
 
 
 def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None) -> dict:
@@ -142,6 +155,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None)
     summary `into` when it exists."""
     import csv
     import collections
+    import re
     calib = 256 << 20
 
     def load(path):
@@ -155,12 +169,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, into: str = None)
             if any(k in name for k in FACTOR_KERNELS):
                 per["tcl_factor_balanced"].append(v)
                 continue
-            for short in ("plan_shrink", "shrink_mfma", "shrink_valu", "expand_kernel_split",
-                          "expand_kernel",
-                          "expand_staged", "expand_mfma", "plan_kernel", "tile_ranges_kernel",
-                          "tile_ranges_tok_kernel",
-                          "plan_m_local", "plan_m_scan", "plan_m_scatter", "gate_topk_kernel"):
-                if short in name:
+            for short in PMC_KERNELS:
+                if re.search(r"(?<![A-Za-z0-9_])" + short + r"(?![A-Za-z0-9_])", name):
                     per[short].append(v)
                     break
         return per, calib / biggest_copy
@@ -843,7 +853,7 @@ def measure(wl, dev, stream, steps, warmup, eager, replicas, latency=False) -> d
             "bound": "hbm", "kernel": names[dom],
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": stored_traffic(wl.name, names[dom].split(" ")[0]),
+            "traffic": stored_traffic(wl.name, names[dom]),
         },
         "_t_steps": t_steps,
     }
@@ -879,7 +889,7 @@ def kernel_names(wl, fused: bool) -> dict:
     if not bf or c.n_tokens < 256 or os.environ.get("TCL_DISPATCH") == "valu":
         expand = "expand_kernel"
     else:
-        expand = "expand_tile (after tile_prep)"
+        expand = "tile_prep+expand_tile"
     return {"plan": "plan_kernel", "shrink": shrink, "expand": expand}
 
 

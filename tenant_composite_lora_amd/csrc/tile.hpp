@@ -1,0 +1,33 @@
+// Host side of the prefill expand over token tiles (tile.hip), as the apply
+// dispatch calls it.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "tcl_internal.hpp"
+
+namespace tcl {
+
+// Adapters a tile record's adapter bitmap covers: larger pools run the
+// per-token expand.
+constexpr int kTileMaxAdapters = 4096;
+
+// Workspace bytes of the per-tile records of one launch over n_mods modules.
+size_t tile_records_bytes(const tcl_plan *p, int n_mods);
+
+// Bytes of a module's packed rank-contiguous copy of B (tcl_module_pack).
+size_t tile_pack_bytes(const tcl_module *m);
+
+// Enqueue the two kernels that write the packed copy of m->B_t into B_k
+// (tile_pack_bytes(m) bytes, 256-byte aligned; checked by the caller).
+int launch_module_pack(const tcl_module *m, void *B_k, hipStream_t s);
+
+// tile_prep then expand_tile for n (<= kMaxMods) modules.  z[i]: module i's
+// shrink output with zld[i] floats a row and nkc[i] K-chunk partial planes;
+// rec: tile_records_bytes(p, n) bytes of workspace.
+int launch_expand_tile(const tcl_plan *p, const tcl_module *mods, int n, float *const *z,
+                       const int *zld, const int *nkc, void *const *y, const int64_t *ldy,
+                       tcl_dtype yd, int32_t *rec, hipStream_t s);
+
+}  // namespace tcl

@@ -77,6 +77,25 @@ def test_pmc_summary_scales_by_the_copy(bench, tmp_path):
     assert x["source_hash"] == bench.kernel_source_hash("expand_kernel")
 
 
+def test_pmc_summary_keeps_kernels_apart(bench, tmp_path):
+    """Kernel names are matched as whole identifiers: the paired shrink is
+    not counted as the plain one, and the two kernels of the token-tile
+    expand keep their own entries, which the traffic lookup sums."""
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    copy_kib = (256 << 20) / 1024
+    _csv(fetch, [["__amd_rocclr_copyBuffer", "FETCH_SIZE", copy_kib],
+                 ["void tcl::shrink_mfma<8>(tcl::ShrinkArgs)", "FETCH_SIZE", 1.0],
+                 ["void tcl::shrink_mfma_pair<8>(tcl::ShrinkArgs)", "FETCH_SIZE", 4.0],
+                 ["tcl::tile_prep(tcl::TileArgs)", "FETCH_SIZE", 2.0],
+                 ["void tcl::expand_tile<tcl::bf16_t>(tcl::TileArgs)", "FETCH_SIZE", 8.0]])
+    _csv(write, [["__amd_rocclr_copyBuffer", "WRITE_SIZE", copy_kib]])
+    e = bench.pmc_summary(str(fetch), str(write), "wl")["entries"]
+    assert e["wl:shrink_mfma"]["fetch_bytes_per_launch"] == 1024.0
+    assert e["wl:shrink_mfma_pair"]["fetch_bytes_per_launch"] == 4096.0
+    assert e["wl:tile_prep"]["source_hash"] == bench.kernel_source_hash("tile_prep")
+    assert e["wl:expand_tile"]["fetch_bytes_per_launch"] == 8192.0
+
+
 def test_stored_traffic_unknown_workload(bench):
     assert bench.stored_traffic("no_such_workload", "plan_shrink") is None
 
@@ -145,8 +164,8 @@ def test_kernel_names_follow_dispatch(bench):
     """The bench names the kernels the library's dispatch picks: the paired
     prefill shrink from 1024 pair jobs on, the token-tile expand for
     prefill-sized bf16 batches."""
-    k5 = bench.kernel_names(W.make(4), False)
-    assert k5["shrink"] == "shrink_mfma" and k5["expand"].startswith("expand_tile")
+    k4 = bench.kernel_names(W.make(4), False)
+    assert k4["shrink"] == "shrink_mfma" and k4["expand"] == "tile_prep+expand_tile"
     small = W.random_case(1, T=40, N=8, d_in=32, d_out=32, r_max=8, max_pairs=2)
     k = bench.kernel_names(small, True)
     assert k["shrink"] == "plan_shrink" and k["expand"] == "expand_kernel"
