@@ -320,6 +320,24 @@ int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
                     size_t ws_bytes, void *stream);
 
 /*
+ * Allocation-free tcl_fused_apply, for callers that cannot allocate device
+ * memory (code under stream or graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, arithmetic and errors as
+ * tcl_fused_apply, without ws / ws_bytes: the workspace is a static device
+ * array of TCL_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; its device address is looked up on the first call
+ * on a device, with that device current.  No call allocates or frees.
+ * Batches whose workspace (tcl_workspace_bytes) exceeds TCL_SCRATCH_BYTES
+ * return TCL_ENOSPC before any launch.  Every call on one GPU shares that
+ * GPU's array: calls that may overlap on one GPU (different streams, or
+ * graphs replayed concurrently) race and must be ordered by the caller.
+ */
+#define TCL_SCRATCH_BYTES (32u << 20)
+int tcl_fused_apply_noalloc(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
+                            const void *const *x, const int64_t *ldx, tcl_dtype xd,
+                            void *const *y, const int64_t *ldy, tcl_dtype yd, void *stream);
+
+/*
  * The two halves of tcl_fused_apply, for callers that schedule them apart
  * (e.g. to overlap the expand with other work) and for per-kernel timing:
  * tcl_fused_shrink launches the multi-module shrink and leaves z in `ws`

@@ -21,6 +21,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -1260,6 +1261,70 @@ int tcl_fused_apply(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
   return run_fused(p, mods, n_mods, x, ldx, y, ldy, yd, ws, s);
 }
 
+
+}  // extern "C"
+
+namespace tcl {
+
+// Workspace of tcl_fused_apply_noalloc: a file-scope device array (each GPU
+// holds its own copy at its own address from module load to process end).
+// Host code never passes the array's name to a kernel or a copy (on the host
+// it is a stand-in, not a device address): it looks the device address up
+// once per device and uses that.
+static __device__ __align__(256) unsigned char scratch[TCL_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+static void *g_scratch_dev[kScratchDevices];
+static std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device with the device current.
+static int scratch_address(void **out) {
+  int dev = 0;
+  TCL_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(TCL_EUNSUPPORTED, "device %d beyond the %d the scratch table covers", dev,
+                kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *ptr = nullptr;
+    TCL_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(TCL_EHIP, "no device address for the scratch array");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return TCL_OK;
+}
+
+}  // namespace tcl
+
+extern "C" {
+
+int tcl_fused_apply_noalloc(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
+                            const void *const *x, const int64_t *ldx, tcl_dtype xd,
+                            void *const *y, const int64_t *ldy, tcl_dtype yd, void *stream) {
+  if (!x || !y) return fail(TCL_EINVAL, "x and y lists are required");
+  if (!p) return fail(TCL_EINVAL, "plan is NULL");
+  if (n_mods < 1 || !mods) return fail(TCL_EINVAL, "module list is required");
+  for (int i = 0; i < n_mods; ++i) {
+    int rc = check_plan_module(p, &mods[i]);
+    if (rc) return rc;
+  }
+  const size_t need = ws_need(p, mods, n_mods);
+  if (need > TCL_SCRATCH_BYTES)
+    return fail(TCL_ENOSPC,
+                "batch needs %zu bytes of workspace, the allocation-free apply holds %zu; "
+                "use tcl_fused_apply with a caller workspace",
+                need, size_t(TCL_SCRATCH_BYTES));
+  void *ws = nullptr;
+  int rc = scratch_address(&ws);
+  if (rc) return rc;
+  rc = check_fused(p, mods, n_mods, x, ldx, xd, y, ldy, yd, ws, TCL_SCRATCH_BYTES);
+  if (rc) return rc;
+  // every workspace byte the kernels read was written earlier in the same
+  // call (z by the shrink, the tile records by tile_prep): nothing to clear
+  return run_fused(p, mods, n_mods, x, ldx, y, ldy, yd, ws, static_cast<hipStream_t>(stream));
+}
 
 // The decode step's shrink with the mapping stage inside (plan_shrink):
 // direct-mode tables whose LDS view and work items fit the kernel's budget,

@@ -34,7 +34,10 @@ EXPORTS = ["tcl_last_error", "tcl_version", "tcl_plan_bytes", "tcl_plan_map", "t
            "tcl_bam_create", "tcl_bam_free", "tcl_bam_acquire", "tcl_bam_slots", "tcl_lag_select",
            "tcl_module_init", "tcl_composites_validate", "tcl_plan_map_host",
            "tcl_plan_remap_host", "tcl_plan_info", "tcl_plan_status_async",
-           "tcl_module_pack_bytes", "tcl_module_pack"]
+           "tcl_module_pack_bytes", "tcl_module_pack", "tcl_fused_apply_noalloc"]
+
+# bytes of the static device workspace of tcl_fused_apply_noalloc
+SCRATCH_BYTES = 32 << 20
 
 
 class TclError(RuntimeError):
@@ -97,6 +100,9 @@ def lib(path: Optional[str] = None):
     L.tcl_fused_apply.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, ctypes.POINTER(vp),
                                   ctypes.POINTER(i64), i32, ctypes.POINTER(vp),
                                   ctypes.POINTER(i64), i32, vp, sz, vp]
+    L.tcl_fused_apply_noalloc.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32,
+                                          ctypes.POINTER(vp), ctypes.POINTER(i64), i32,
+                                          ctypes.POINTER(vp), ctypes.POINTER(i64), i32, vp]
     L.tcl_fused_shrink.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, ctypes.POINTER(vp),
                                    ctypes.POINTER(i64), i32, vp, sz, vp]
     L.tcl_fused_expand.argtypes = [vp, ctypes.POINTER(ModuleDesc), i32, vp, sz,
@@ -439,6 +445,13 @@ class FusedCall:
         check(lib().tcl_fused_apply(self.plan.handle, self.descs, self.n, self.xp, self.ldx,
                                     self.xd, self.yp, self.ldy, self.yd, self.ws.data_ptr(),
                                     self.ws.numel(), _stream(self.xs[0].device, stream)))
+
+    def noalloc(self, stream=None):
+        """The same apply through tcl_fused_apply_noalloc: the library's static
+        device workspace instead of self.ws."""
+        check(lib().tcl_fused_apply_noalloc(self.plan.handle, self.descs, self.n, self.xp,
+                                            self.ldx, self.xd, self.yp, self.ldy, self.yd,
+                                            _stream(self.xs[0].device, stream)))
 
     def shrink(self, stream=None):
         """First half only: z of every module into the workspace."""

@@ -47,6 +47,8 @@ def test_header_constants_match_binding():
     assert int(consts["TCL_EHIP"]) == tclora.EHIP
     assert f"TCL_MAX_RANK {tclora.MAX_RANK}" in text
     assert f"TCL_MAX_PAIRS_PER_GROUP {tclora.MAX_PAIRS_PER_GROUP}" in text
+    m = re.search(r"#define TCL_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == tclora.SCRATCH_BYTES
 
 
 def test_status_codes_match_oracle():
