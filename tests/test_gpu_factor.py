@@ -156,7 +156,9 @@ def test_factor_fleet_shape_sampled():
     Ft, T, sg = tclora.factor_balanced(Bt, At)
     torch.cuda.synchronize()
     assert torch.isfinite(sg).all()
-    v = torch.randn(d_in, device="cuda:0", dtype=torch.float64)
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(11)
+    v = torch.randn(d_in, device="cuda:0", dtype=torch.float64, generator=gen)
     # elementwise products and sums only (no batched matrix products)
     lhs = (Ft.double() * (T.double() * v).sum(2)[:, :, None]).sum(1)
     rhs = (Bt.double() * (At.double() * v).sum(2)[:, :, None]).sum(1)
@@ -167,8 +169,13 @@ def test_factor_fleet_shape_sampled():
     bound = (Ft.double().abs() * (T.double().abs() * v.abs()).sum(2)[:, :, None]).sum(1)
     ratio = ((lhs - rhs).abs() / (2.0 ** -6 * bound + 1e-30)).max().item()
     rel = ((lhs - rhs).norm(dim=1) / rhs.norm(dim=1)).max().item()
-    print(f"  probe rel max {rel:.3e}, error / bound max {ratio:.3f}", flush=True)
+    cond = (bound.norm(dim=1) / rhs.norm(dim=1)).max().item()
+    print(f"  probe rel max {rel:.3e}, error / bound max {ratio:.3f}, "
+          f"|F|^T(|T||v|) / |F^T T v| max {cond:.3f}", flush=True)
     assert ratio <= 1.0
+    # normwise: the bf16 tolerance of the apply (both factors rounded to
+    # bf16; measured 7.5e-3 at the worst of the 2240 modules)
+    assert rel <= 1e-2
     for m in (0, 1117, M - 1):
         _check_module(_bits(Bt[m]), _bits(At[m]), _bits(Ft[m]), _bits(T[m]),
                       sg[m].cpu().numpy(), ("fleet", m))
