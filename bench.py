@@ -490,6 +490,11 @@ def sched_main(args):
     lag_loads, t = sched_replay(stream, tclora.lag_select, LibPool, theta, B, S)
     fifo_loads, _ = sched_replay(stream, tclora.lag_select, LibPool, float("-inf"), B, S)
     n_dec = len(stream)
+    # bytes one load moves host to device (tcl_bam_load copies A and B rows):
+    # a rank-16 bf16 adapter on the seven projections of each of the 32
+    # layers of Llama-3-8B (d_in + d_out summed over q, k, v, o, gate, up, down)
+    per_layer = (4096 + 4096) + 2 * (4096 + 1024) + (4096 + 4096) + 3 * (4096 + 14336)
+    adapter_bytes = per_layer * 16 * 2 * 32
     out = {
         "metric": SCHED_METRIC, "value": n_dec / t, "unit": "decisions/s",
         "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": t / n_dec * 1e3,
@@ -500,6 +505,9 @@ def sched_main(args):
                    "arrivals_per_step": 32, "initial_burst": 256,
                    "composite": "2-5 adapters, Zipf(1.2)",
                    "loads_per_batch_lag": lag_loads, "loads_per_batch_fifo": fifo_loads,
+                   "adapter_bytes": adapter_bytes,
+                   "h2d_bytes_per_batch_lag": lag_loads * adapter_bytes,
+                   "h2d_bytes_per_batch_fifo": fifo_loads * adapter_bytes,
                    "timed": "lag_select + bam acquire per step, binding included"},
         "roofline": None,
     }

@@ -511,6 +511,38 @@ int tcl_bam_acquire(tcl_bam *bam, const int32_t *adapters, int32_t n, int32_t *s
 /* The adapter in every slot (-1 when empty): n_slots entries. */
 int tcl_bam_slots(const tcl_bam *bam, int32_t *slot_adapter);
 
+/* The GPU half of the slot pool.  A slot pool is a tcl_module whose
+ * n_adapters entries are slots: A_t [n_slots][r_max][d_in] and B_t
+ * [n_slots][r_max][d_out] on the device, owned by the caller.
+ *
+ * tcl_bam_pool_init sets every slot empty (rank 0 in k_dev, caller-owned
+ * device int[n_slots]) and, with B_k (bf16 pools; tcl_module_pack_bytes
+ * bytes, 256-byte aligned), lays out the packed copy of B with a fixed
+ * region per slot, so that a load re-packs only its slot; then m->k_dev =
+ * k_dev and m->B_k = B_k.  Enqueued on `stream`.  Errors: those of
+ * tcl_module_init's module checks; TCL_EINVAL (k_dev NULL), TCL_EALIGN,
+ * TCL_EUNSUPPORTED (B_k with an fp32 pool), TCL_ENOSPC, TCL_EHIP.
+ *
+ * tcl_bam_load performs the loads tcl_bam_acquire returned (DyMerge-LoRA
+ * section 4: BAM keeps the raw factors of resident adapters on the GPU):
+ * for load i, rows j < k of adapter load_adapter[i] of the caller's host
+ * pools A_host [n_logical][r_max][d_in] and B_host [n_logical][r_max][d_out]
+ * (the module's dtype; pinned memory, e.g. hipHostMalloc, for the copies to
+ * be asynchronous) go to slot load_slot[i], whose rank becomes k =
+ * k_host[load_adapter[i]] (k_host NULL: r_max), and its packed columns are
+ * re-written.  Rows at or beyond k are neither copied nor read later.  All
+ * on `stream`: host-to-device copies, then one kernel per 64 loads.  The
+ * host pools must stay unchanged until the copies have run.  Apply over the
+ * pool with slot ids as adapter ids (tcl_bam_acquire's slot_of).  Checks,
+ * all before any HIP call: the module is a slot pool (k_dev set), slots in
+ * [0, n_slots) and distinct within the call, adapters in [0, n_logical),
+ * ranks in [0, r_max].  Errors: TCL_EINVAL, TCL_EALIGN, TCL_EUNSUPPORTED,
+ * TCL_EHIP. */
+int tcl_bam_pool_init(tcl_module *m, int32_t *k_dev, void *B_k, size_t bytes, void *stream);
+int tcl_bam_load(const tcl_module *m, const void *A_host, const void *B_host,
+                 const int32_t *k_host, int32_t n_logical, int32_t n_loads,
+                 const int32_t *load_slot, const int32_t *load_adapter, void *stream);
+
 /* The next batch, chosen the LAG way.  Request i (of n_requests) arrived at
  * arrival[i] and uses the adapters req_adapters[req_ptr[i] .. req_ptr[i +
  * 1]) (ids >= 0, repeats count once).  resident[0..n_resident) are the

@@ -1148,6 +1148,67 @@ int tcl_module_pack(tcl_module *m, void *B_k, size_t bytes, void *stream) {
   return TCL_OK;
 }
 
+int tcl_bam_pool_init(tcl_module *m, int32_t *k_dev, void *B_k, size_t bytes, void *stream) {
+  int rc = check_module(m);
+  if (rc) return rc;
+  if (!k_dev) return fail(TCL_EINVAL, "k_dev is NULL");
+  if (reinterpret_cast<uintptr_t>(k_dev) & 3) return fail(TCL_EALIGN, "k_dev must be 4-byte aligned");
+  if (B_k) {
+    if (m->wdtype != TCL_BF16) return fail(TCL_EUNSUPPORTED, "the packed copy is for bf16 pools");
+    if (reinterpret_cast<uintptr_t>(B_k) & 255)
+      return fail(TCL_EALIGN, "B_k must be 256-byte aligned");
+    if (bytes < tile_pack_bytes(m))
+      return fail(TCL_ENOSPC, "B_k holds %zu bytes, needs %zu", bytes, tile_pack_bytes(m));
+  }
+  rc = launch_slot_pool_init(m, k_dev, B_k, static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  m->k_dev = k_dev;
+  m->B_k = B_k;
+  return TCL_OK;
+}
+
+int tcl_bam_load(const tcl_module *m, const void *A_host, const void *B_host,
+                 const int32_t *k_host, int32_t n_logical, int32_t n_loads,
+                 const int32_t *load_slot, const int32_t *load_adapter, void *stream) {
+  int rc = check_module(m);
+  if (rc) return rc;
+  if (!m->k_dev) return fail(TCL_EINVAL, "module is not a slot pool (k_dev NULL): tcl_bam_pool_init");
+  if (n_loads < 0 || n_logical < 1) return fail(TCL_EINVAL, "n_loads < 0 or n_logical < 1");
+  if (n_loads == 0) return TCL_OK;
+  if (!A_host || !B_host || !load_slot || !load_adapter)
+    return fail(TCL_EINVAL, "host pools and load lists are required");
+  std::vector<int32_t> ranks(n_loads);
+  for (int i = 0; i < n_loads; ++i) {
+    const int sl = load_slot[i], a = load_adapter[i];
+    if (sl < 0 || sl >= m->n_adapters)
+      return fail(TCL_EINVAL, "load %d: slot %d outside [0, %d)", i, sl, m->n_adapters);
+    if (a < 0 || a >= n_logical)
+      return fail(TCL_EINVAL, "load %d: adapter %d outside [0, %d)", i, a, n_logical);
+    for (int j = 0; j < i; ++j)
+      if (load_slot[j] == sl) return fail(TCL_EINVAL, "slot %d loaded twice in one call", sl);
+    const int k = k_host ? k_host[a] : m->r_max;
+    if (k < 0 || k > m->r_max)
+      return fail(TCL_EINVAL, "adapter %d: rank %d outside [0, %d]", a, k, m->r_max);
+    ranks[i] = k;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t es = m->wdtype == TCL_BF16 ? 2 : 4;
+  const size_t rowA = size_t(m->d_in) * es, rowB = size_t(m->d_out) * es;
+  const size_t slotA = size_t(m->r_max) * rowA, slotB = size_t(m->r_max) * rowB;
+  for (int i = 0; i < n_loads; ++i) {
+    // rows at or beyond the retained rank are never read: copy rows < k only
+    const size_t sl = size_t(load_slot[i]), a = size_t(load_adapter[i]), k = size_t(ranks[i]);
+    if (k == 0) continue;
+    TCL_HIP(hipMemcpyAsync(static_cast<char *>(const_cast<void *>(m->A_t)) + sl * slotA,
+                           static_cast<const char *>(A_host) + a * slotA, k * rowA,
+                           hipMemcpyHostToDevice, s));
+    TCL_HIP(hipMemcpyAsync(static_cast<char *>(const_cast<void *>(m->B_t)) + sl * slotB,
+                           static_cast<const char *>(B_host) + a * slotB, k * rowB,
+                           hipMemcpyHostToDevice, s));
+  }
+  return launch_slot_update(m, load_slot, ranks.data(), n_loads, s);
+}
+
 int tcl_workspace_bytes(const tcl_plan *p, const tcl_module *mods, int32_t n_mods,
                         size_t *bytes) {
   if (!bytes) return fail(TCL_EINVAL, "bytes is NULL");

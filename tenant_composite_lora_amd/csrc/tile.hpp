@@ -23,6 +23,17 @@ size_t tile_pack_bytes(const tcl_module *m);
 // (tile_pack_bytes(m) bytes, 256-byte aligned; checked by the caller).
 int launch_module_pack(const tcl_module *m, void *B_k, hipStream_t s);
 
+// A new adapter slot pool: every slot's rank 0 in k_dev, and (B_k non-NULL)
+// the offsets of the packed copy fixed at s * d_out * ceil(r_max / 8) units
+// (tile_pack_bytes(m) bytes, 256-byte aligned; checked by the caller).
+int launch_slot_pool_init(const tcl_module *m, int32_t *k_dev, void *B_k, hipStream_t s);
+
+// n loads into a slot pool whose factors are already in place: slot
+// slots[i] gets rank ranks[i] in m->k_dev and, when m->B_k is set, its packed
+// columns re-written.  Kernel arguments carry the lists (no device copies).
+int launch_slot_update(const tcl_module *m, const int32_t *slots, const int32_t *ranks, int n,
+                       hipStream_t s);
+
 // tile_prep then expand_tile for n (<= kMaxMods) modules.  z[i]: module i's
 // shrink output with zld[i] floats a row and nkc[i] K-chunk partial planes;
 // rec: tile_records_bytes(p, n) bytes of workspace.

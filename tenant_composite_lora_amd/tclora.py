@@ -34,7 +34,8 @@ EXPORTS = ["tcl_last_error", "tcl_version", "tcl_plan_bytes", "tcl_plan_map", "t
            "tcl_bam_create", "tcl_bam_free", "tcl_bam_acquire", "tcl_bam_slots", "tcl_lag_select",
            "tcl_module_init", "tcl_composites_validate", "tcl_plan_map_host",
            "tcl_plan_remap_host", "tcl_plan_info", "tcl_plan_status_async",
-           "tcl_module_pack_bytes", "tcl_module_pack", "tcl_fused_apply_noalloc"]
+           "tcl_module_pack_bytes", "tcl_module_pack", "tcl_fused_apply_noalloc",
+           "tcl_bam_pool_init", "tcl_bam_load"]
 
 # bytes of the static device workspace of tcl_fused_apply_noalloc
 SCRATCH_BYTES = 32 << 20
@@ -122,6 +123,8 @@ def lib(path: Optional[str] = None):
     L.tcl_bam_free.restype = None
     L.tcl_bam_acquire.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
     L.tcl_bam_slots.argtypes = [vp, vp]
+    L.tcl_bam_pool_init.argtypes = [ctypes.POINTER(ModuleDesc), vp, vp, sz, vp]
+    L.tcl_bam_load.argtypes = [ctypes.POINTER(ModuleDesc), vp, vp, vp, i32, i32, vp, vp, vp]
     L.tcl_lag_select.argtypes = [vp, vp, vp, i32, vp, i32, ctypes.c_double, ctypes.c_double,
                                  i32, i32, vp, vp]
     if path is None:
@@ -620,6 +623,66 @@ class Bam:
         if h is not None and h.value and _lib is not None:
             _lib.tcl_bam_free(h)
             self._h = None
+
+
+class SlotPool:
+    """BAM on the GPU: n_slots device slots per module, filled from host pools.
+
+    ``host_pools``: one (A_t, B_t, k) per module, A_t [N, r_max, d_in] and
+    B_t [N, r_max, d_out] CPU tensors (bf16 or fp32; copied once into pinned
+    memory here) over the N logical adapters, k their retained ranks (ints,
+    or None for r_max).  ``modules`` are the device slot pools (tcl_module
+    descriptors whose adapter ids are slots); load() makes a batch's adapters
+    resident (tcl_bam_acquire, then tcl_bam_load for every module) and
+    returns the slot of each adapter."""
+
+    def __init__(self, n_slots: int, host_pools, device, stream=None):
+        import numpy as np
+        self.bam = Bam(n_slots)
+        self.device = torch.device(device)
+        self.n_logical = int(host_pools[0][0].shape[0])
+        self.modules, self._host, self.h2d_bytes = [], [], 0
+        for A_h, B_h, k in host_pools:
+            if A_h.shape[0] != self.n_logical or B_h.shape[0] != self.n_logical:
+                raise ValueError("every host pool holds the same logical adapters")
+            A_p, B_p = A_h.contiguous().pin_memory(), B_h.contiguous().pin_memory()
+            kh = None if k is None else np.ascontiguousarray(np.asarray(k, dtype=np.int32))
+            _, r, d_in = A_p.shape
+            d_out = B_p.shape[2]
+            A_t = torch.zeros(n_slots, r, d_in, dtype=A_p.dtype, device=self.device)
+            B_t = torch.zeros(n_slots, r, d_out, dtype=B_p.dtype, device=self.device)
+            mod = Module(A_t, B_t, pack=False)
+            mod.k_dev = torch.empty(n_slots, dtype=torch.int32, device=self.device)
+            if mod.desc.wdtype == BF16:
+                nb = ctypes.c_size_t(0)
+                check(lib().tcl_module_pack_bytes(ctypes.byref(mod.desc), ctypes.byref(nb)))
+                mod.B_k = torch.empty(max(nb.value // 2, 8), dtype=torch.bfloat16,
+                                      device=self.device)
+                bk, nbytes = mod.B_k.data_ptr(), nb.value
+            else:
+                bk, nbytes = None, 0
+            check(lib().tcl_bam_pool_init(ctypes.byref(mod.desc), mod.k_dev.data_ptr(), bk,
+                                          nbytes, _stream(self.device, stream)))
+            self.modules.append(mod)
+            self._host.append((A_p, B_p, kh))
+
+    def load(self, adapters, stream=None):
+        """Slots for the adapters of one batch (in the order given); the loads
+        are queued on the stream.  Returns (slot of each entry, loads)."""
+        import numpy as np
+        slot_of, loads = self.bam.acquire(adapters)
+        if loads:
+            ls = np.ascontiguousarray([l[0] for l in loads], dtype=np.int32)
+            la = np.ascontiguousarray([l[1] for l in loads], dtype=np.int32)
+            for mod, (A_p, B_p, kh) in zip(self.modules, self._host):
+                check(lib().tcl_bam_load(ctypes.byref(mod.desc), A_p.data_ptr(), B_p.data_ptr(),
+                                         None if kh is None else kh.ctypes.data,
+                                         self.n_logical, len(loads), ls.ctypes.data,
+                                         la.ctypes.data, _stream(self.device, stream)))
+                es = A_p.element_size()
+                ks = [mod.r_max if kh is None else int(kh[a]) for a in la.tolist()]
+                self.h2d_bytes += sum(ks) * (mod.d_in + mod.d_out) * es
+        return slot_of, loads
 
 
 def lag_select(now: float, theta: float, arrival, adapters, resident, max_batch: int,

@@ -301,3 +301,37 @@ def test_module_init_host_errors(L):
     d.k_dev = 0x5000
     assert L.tcl_module_init(ctypes.byref(d), None, None, None) == tclora.OK
     assert d.k_dev is None
+
+
+def test_bam_load_host_errors(L):
+    """tcl_bam_load and tcl_bam_pool_init check everything on the host before
+    any HIP call (the pointers here are never dereferenced)."""
+    pool = tclora.ModuleDesc(4, 16, 16, 8, tclora.BF16, 0x1000, 0x2000, 0x3000, None)
+    plain = tclora.ModuleDesc(4, 16, 16, 8, tclora.BF16, 0x1000, 0x2000, None, None)
+    k = np.array([8, 3, 9, 0, 2], np.int32)       # adapter 2 has rank 9 > r_max
+    kp = k.ctypes.data_as(ctypes.c_void_p)
+
+    def load(desc, slots, ads, n_logical=5, kk=kp):
+        s = np.ascontiguousarray(slots, np.int32)
+        a = np.ascontiguousarray(ads, np.int32)
+        return L.tcl_bam_load(ctypes.byref(desc), 0x4000, 0x5000, kk, n_logical, len(s),
+                              s.ctypes.data, a.ctypes.data, None)
+
+    assert load(plain, [0], [0]) == tclora.EINVAL               # not a slot pool
+    assert b"slot pool" in L.tcl_last_error()
+    assert load(pool, [4], [0]) == tclora.EINVAL                # slot out of range
+    assert load(pool, [-1], [0]) == tclora.EINVAL
+    assert load(pool, [0], [5]) == tclora.EINVAL                # adapter out of range
+    assert load(pool, [1, 1], [0, 1]) == tclora.EINVAL          # slot twice
+    assert load(pool, [0], [2]) == tclora.EINVAL                # rank beyond r_max
+    assert b"rank 9" in L.tcl_last_error()
+    assert load(pool, [0], [0], n_logical=0) == tclora.EINVAL
+    assert load(pool, [], []) == tclora.OK                      # nothing to do
+    assert L.tcl_bam_load(None, 0x4000, 0x5000, kp, 5, 0, None, None, None) == tclora.EINVAL
+    assert L.tcl_bam_pool_init(ctypes.byref(plain), None, None, 0, None) == tclora.EINVAL
+    assert L.tcl_bam_pool_init(ctypes.byref(plain), 0x3002, None, 0, None) == tclora.EALIGN
+    assert L.tcl_bam_pool_init(ctypes.byref(plain), 0x3000, 0x6010, 1 << 20, None) == tclora.EALIGN
+    assert L.tcl_bam_pool_init(ctypes.byref(plain), 0x3000, 0x6000, 16, None) == tclora.ENOSPC
+    f32 = tclora.ModuleDesc(4, 16, 16, 8, tclora.F32, 0x1000, 0x2000, None, None)
+    assert L.tcl_bam_pool_init(ctypes.byref(f32), 0x3000, 0x6000, 1 << 20, None) == \
+        tclora.EUNSUPPORTED
