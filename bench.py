@@ -100,8 +100,9 @@ KERNEL_SOURCES = {k: ("plan.hip", "plan_core.hpp", "tcl_internal.hpp")
                   for k in ("plan_kernel", "tile_order_count", "tile_order_place",
                             "plan_m_local", "plan_m_scan", "plan_m_scatter")}
 KERNEL_SOURCES.update({k: ("tile.hip", "kern_common.hpp", "tcl_internal.hpp")
-                       for k in ("tile_prep", "expand_tile", "pack_offsets_kernel",
-                                 "pack_b_kernel")})
+                       for k in ("tile_prep", "expand_tile")})
+KERNEL_SOURCES.update({k: ("pack.hip", "kern_common.hpp", "tcl_internal.hpp")
+                       for k in ("pack_offsets_kernel", "pack_b_kernel")})
 KERNEL_SOURCES["gate_topk_kernel"] = ("gate.hip", "tcl_internal.hpp")
 # the producer's four kernels are summarised per fleet under the entry point's name
 KERNEL_SOURCES["tcl_factor_balanced"] = ("factor.hip", "tcl_internal.hpp")

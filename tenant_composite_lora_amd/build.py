@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtclora.so")
-SOURCES = ["plan.hip", "apply.hip", "tile.hip", "gate.hip", "factor.hip", "sched.cpp"]
+SOURCES = ["plan.hip", "apply.hip", "tile.hip", "pack.hip", "gate.hip", "factor.hip", "sched.cpp", "host.cpp"]
 ARCH = os.environ.get("TCL_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU forms are switched off for the device code: the compiler

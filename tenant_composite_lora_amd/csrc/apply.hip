@@ -12,11 +12,14 @@
 //           and adds alpha_s * B_a[n, :k] z_s for the token's slots in order,
 //           in fp32, then adds the total to y once (expand_kernel).  Prefill
 //           batches run over 64-token tiles on the matrix cores instead
-//           (tile_prep + expand_tile).  Each output element has exactly one
-//           owner; there are no atomics.
+//           (tile_prep + expand_tile, in tile.hip).  Each output element has
+//           exactly one owner; there are no atomics.
 //
-// A plan whose composite table was rejected has an empty token index and no
-// work items, so every kernel below finds nothing to do.
+// Also here: the host side of every apply entry point (checks, workspace
+// layout, dispatch), the allocation-free apply over a static device
+// workspace, and the loads of an adapter slot pool (DyMerge-LoRA section 4,
+// BAM).  A plan whose composite table was rejected has an empty token index
+// and no work items, so every kernel below finds nothing to do.
 
 #include <cstdint>
 #include <cstdlib>

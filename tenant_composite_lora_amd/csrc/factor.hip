@@ -522,53 +522,3 @@ extern "C" int tcl_factor_balanced(const void *B_t, const void *A_t, int32_t n_m
   TCL_HIP(hipGetLastError());
   return TCL_OK;
 }
-
-extern "C" int tcl_rank_uniform(const int32_t *ranks, const int64_t *costs, int32_t n_modules,
-                                int32_t denominator, int32_t *u_out, int64_t *budget_out) {
-  if (n_modules < 0 || denominator < 1) return fail(TCL_EINVAL, "rank_uniform: bad sizes");
-  if (n_modules > 0 && (!ranks || !costs || !u_out)) return fail(TCL_EINVAL, "rank_uniform: NULL pointer");
-  if (!budget_out) return fail(TCL_EINVAL, "rank_uniform: budget_out is NULL");
-  int64_t budget = 0;
-  for (int m = 0; m < n_modules; ++m) {
-    if (ranks[m] < 0 || costs[m] < 1) return fail(TCL_EINVAL, "rank_uniform: module %d: rank < 0 or cost < 1", m);
-    u_out[m] = std::max(1, ranks[m] / denominator);
-    budget += int64_t(u_out[m]) * costs[m];
-  }
-  *budget_out = budget;
-  return TCL_OK;
-}
-
-extern "C" int tcl_rank_spectral(const double *sigma, int64_t ld_sigma, const int32_t *ranks,
-                                 const int64_t *costs, const int32_t *floors, int32_t n_modules,
-                                 int64_t budget, int32_t *k_out) {
-  if (n_modules < 0) return fail(TCL_EINVAL, "rank_spectral: n_modules < 0");
-  if (n_modules > 0 && (!sigma || !ranks || !costs || !floors || !k_out))
-    return fail(TCL_EINVAL, "rank_spectral: NULL pointer");
-  struct Item {
-    double eta;
-    int32_t m, j;
-  };
-  std::vector<Item> items;
-  int64_t left = budget;
-  for (int m = 0; m < n_modules; ++m) {
-    if (ranks[m] < 0 || ranks[m] > ld_sigma || costs[m] < 1 || floors[m] < 0)
-      return fail(TCL_EINVAL, "rank_spectral: module %d: bad rank, cost or floor", m);
-    k_out[m] = std::min(floors[m], ranks[m]);
-    left -= int64_t(k_out[m]) * costs[m];
-    for (int j = 0; j < ranks[m]; ++j) {
-      const double s = sigma[int64_t(m) * ld_sigma + j];
-      if (!(s >= 0.0) || !std::isfinite(s)) return fail(TCL_EINVAL, "rank_spectral: sigma[%d][%d] not finite and >= 0", m, j);
-      if (j >= k_out[m]) items.push_back({s * s / double(costs[m]), m, j});
-    }
-  }
-  std::sort(items.begin(), items.end(), [](const Item &x, const Item &y) {
-    if (x.eta != y.eta) return x.eta > y.eta;
-    return x.m != y.m ? x.m < y.m : x.j < y.j;
-  });
-  for (const Item &it : items)
-    if (it.j == k_out[it.m] && costs[it.m] <= left) {
-      ++k_out[it.m];
-      left -= costs[it.m];
-    }
-  return TCL_OK;
-}

@@ -40,37 +40,6 @@
 
 namespace tcl {
 
-static thread_local std::string g_err;
-
-bool log_enabled() {
-  static int on = [] {
-    const char *s = std::getenv("TCL_LOG");
-    return (s && *s && *s != '0') ? 1 : 0;
-  }();
-  return on != 0;
-}
-
-void logf(const char *fmt, ...) {
-  if (!log_enabled()) return;
-  va_list ap;
-  va_start(ap, fmt);
-  std::fprintf(stderr, "[tcl] ");
-  std::vfprintf(stderr, fmt, ap);
-  std::fprintf(stderr, "\n");
-  va_end(ap);
-}
-
-int fail(int code, const char *fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  std::vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_err = buf;
-  logf("error %d: %s", code, buf);
-  return code;
-}
-
 int hip_fail(hipError_t e, const char *what) {
   return fail(TCL_EHIP, "%s failed: %s", what, hipGetErrorString(e));
 }
@@ -681,15 +650,6 @@ static void bind(tcl_plan *p) {
   d.ord_cnt = reinterpret_cast<int32_t *>(b + L.o_ocnt);
 }
 
-static int check_composites(const tcl_composites *c) {
-  if (!c) return fail(TCL_EINVAL, "composites is NULL");
-  if (!c->group_tok_ptr || !c->group_pair_ptr)
-    return fail(TCL_EINVAL, "group pointer arrays must not be NULL");
-  if (c->n_pairs > 0 && (!c->pair_adapter || !c->pair_alpha))
-    return fail(TCL_EINVAL, "pair arrays must not be NULL when n_pairs > 0");
-  return TCL_OK;
-}
-
 void plan_fill_args(const tcl_plan *p, const tcl_composites *c, PlanArgs *out) {
   PlanArgs &A = *out;
   A.T = p->L.T;
@@ -781,71 +741,6 @@ __global__ void status_copy_kernel(const int32_t *status, int32_t *out) {
   if (threadIdx.x < 4) out[threadIdx.x] = status[threadIdx.x];
 }
 
-// A host-resident composite table, checked on the host by the rules of the
-// mapping stage (DyMerge-LoRA section 4.3: the tuples are built from the
-// composites; the table's rules are the library's), with its codes and their
-// precedence: TCL_EINVAL (CSR pointers that do not start at 0, end at the
-// token and pair counts or decrease; an adapter id outside [0, N); a
-// non-finite alpha; an adapter twice in a composite of at most
-// TCL_MAX_PAIRS_PER_GROUP pairs) before TCL_EUNSUPPORTED (a larger
-// composite) before TCL_ENOSPC (more tuples than max_tuples).  Counts the
-// tuples and the adapters that own at least one tuple.  No GPU is touched.
-static int validate_host(const tcl_composites *c, int64_t *P_out, int32_t *U_out) {
-  const int32_t G = c->n_groups, NP = c->n_pairs, T = c->n_tokens, N = c->n_adapters;
-  if (G < 0 || NP < 0 || T < 0 || c->max_tuples < 0)
-    return fail(TCL_EINVAL, "negative size (tokens %d, groups %d, pairs %d, max_tuples %d)", T,
-                G, NP, c->max_tuples);
-  if (N < 1) return fail(TCL_EINVAL, "n_adapters must be >= 1 (got %d)", N);
-  const int32_t *gt = c->group_tok_ptr, *gp = c->group_pair_ptr, *pa = c->pair_adapter;
-  const float *pw = c->pair_alpha;
-  if (gt[0] != 0 || gt[G] != T)
-    return fail(TCL_EINVAL, "group_tok_ptr must run from 0 to n_tokens (%d .. %d, want 0 .. %d)",
-                gt[0], gt[G], T);
-  if (gp[0] != 0 || gp[G] != NP)
-    return fail(TCL_EINVAL, "group_pair_ptr must run from 0 to n_pairs (%d .. %d, want 0 .. %d)",
-                gp[0], gp[G], NP);
-  for (int32_t g = 0; g < G; ++g)
-    if (gt[g + 1] < gt[g] || gp[g + 1] < gp[g])
-      return fail(TCL_EINVAL, "group pointers decrease at group %d", g);
-  for (int32_t q = 0; q < NP; ++q) {
-    if (pa[q] < 0 || pa[q] >= N)
-      return fail(TCL_EINVAL, "pair %d: adapter id %d outside [0, %d)", q, pa[q], N);
-    if (!std::isfinite(pw[q])) return fail(TCL_EINVAL, "pair %d: alpha is not finite", q);
-  }
-  std::vector<int32_t> last(size_t(N), -1);
-  for (int32_t g = 0; g < G; ++g) {
-    if (gp[g + 1] - gp[g] > TCL_MAX_PAIRS_PER_GROUP) continue;  // not searched (too large)
-    for (int32_t q = gp[g]; q < gp[g + 1]; ++q) {
-      if (last[size_t(pa[q])] == g)
-        return fail(TCL_EINVAL, "group %d holds adapter %d twice", g, pa[q]);
-      last[size_t(pa[q])] = g;
-    }
-  }
-  for (int32_t g = 0; g < G; ++g)
-    if (gp[g + 1] - gp[g] > TCL_MAX_PAIRS_PER_GROUP)
-      return fail(TCL_EUNSUPPORTED, "group %d holds %d pairs (at most %d)", g, gp[g + 1] - gp[g],
-                  TCL_MAX_PAIRS_PER_GROUP);
-  int64_t P = 0;
-  std::vector<char> used(size_t(N), 0);
-  int32_t U = 0;
-  for (int32_t g = 0; g < G; ++g) {
-    const int64_t nt = gt[g + 1] - gt[g];
-    P += nt * (gp[g + 1] - gp[g]);
-    if (nt > 0)
-      for (int32_t q = gp[g]; q < gp[g + 1]; ++q)
-        if (!used[size_t(pa[q])]) {
-          used[size_t(pa[q])] = 1;
-          ++U;
-        }
-  }
-  if (P > c->max_tuples)
-    return fail(TCL_ENOSPC, "the table expands to %lld tuples, max_tuples is %d", (long long)P,
-                c->max_tuples);
-  *P_out = P;
-  *U_out = U;
-  return TCL_OK;
-}
-
 // Copies the validated host table c into the plan buffer's table region
 // through the plan's pinned staging buffer and points *dc at the device copy.
 // The staging buffer is reused by the next host table once the previous copy
@@ -894,19 +789,6 @@ static int stage_table(tcl_plan *p, const tcl_composites *c, hipStream_t s, tcl_
 using namespace tcl;
 
 extern "C" {
-
-const char *tcl_last_error(void) { return g_err.c_str(); }
-
-int tcl_composites_validate(const tcl_composites *c, int32_t *n_tuples, int32_t *n_segments) {
-  int rc = check_composites(c);
-  if (rc) return rc;
-  int64_t P = 0;
-  int32_t U = 0;
-  if ((rc = validate_host(c, &P, &U))) return rc;
-  if (n_tuples) *n_tuples = int32_t(P);
-  if (n_segments) *n_segments = U;
-  return TCL_OK;
-}
 
 int tcl_plan_map_host(const tcl_composites *c, void *dev_buf, size_t dev_bytes, void *stream,
                       tcl_plan **out) {

@@ -82,6 +82,12 @@ enum { PLAN_DIRECT = 0, PLAN_COUNT_LDS = 1, PLAN_COUNT_GLOBAL = 2, PLAN_MULTI = 
 
 int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLayout *L);
 
+// host.cpp: NULL checks of a composite table's pointers, and the whole check
+// of a host-resident table (codes and their precedence those of the mapping
+// stage) with its tuple and touched-adapter counts
+int check_composites(const tcl_composites *c);
+int validate_host(const tcl_composites *c, int64_t *P_out, int32_t *U_out);
+
 // A shrink work item: up to kTile consecutive tuples of one adapter's
 // segment, with their token ids inlined so a wave needs one load to start.
 struct Item {

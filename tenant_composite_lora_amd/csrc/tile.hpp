@@ -1,5 +1,5 @@
-// Host side of the prefill expand over token tiles (tile.hip), as the apply
-// dispatch calls it.
+// Host side of the prefill expand over token tiles (tile.hip) and of the
+// packed copy of B it reads (pack.hip), as the apply entry points call them.
 #pragma once
 
 #include <cstddef>
@@ -15,6 +15,10 @@ constexpr int kTileMaxAdapters = 4096;
 
 // Workspace bytes of the per-tile records of one launch over n_mods modules.
 size_t tile_records_bytes(const tcl_plan *p, int n_mods);
+
+// Bytes before the packed data of a module's packed copy of B: the adapters'
+// first 16-byte units, then a zero 16-byte unit right before the data.
+size_t tile_pack_head_bytes(const tcl_module *m);
 
 // Bytes of a module's packed rank-contiguous copy of B (tcl_module_pack).
 size_t tile_pack_bytes(const tcl_module *m);
