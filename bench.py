@@ -545,6 +545,10 @@ def main():
                     help="untimed steps (default 5; 2 with --producer)")
     ap.add_argument("--config", type=int, default=5,
                     help="the workload of the headline line (default: 5, the largest)")
+    ap.add_argument("--full-rank", action="store_true",
+                    help="every adapter at r_max (retained ranks ignored; the zero rows "
+                         "beyond them are then read and multiplied): the padded-pool "
+                         "comparison for the retained-rank batch")
     ap.add_argument("--no-nested", action="store_true",
                     help="measure only --config (no nested decode/prefill configurations)")
     ap.add_argument("--eager", action="store_true", help="no HIP graph capture")
@@ -596,6 +600,10 @@ def main():
 
     print(f"[bench] generating config {args.config}", file=sys.stderr, flush=True)
     wl = W.make(args.config)
+    if args.full_rank:
+        for m in wl.modules:
+            m.k = None
+        wl.name += "_full_rank"
     cpu = None
     if not args.no_cpu_baseline:
         # before anything touches the GPU: the oracle's workers are forked

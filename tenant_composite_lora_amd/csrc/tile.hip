@@ -130,7 +130,7 @@ __device__ inline void store_y4(TY *p, f32x4_t v) {
 // where the token does not hold the octet's adapter).
 constexpr int kRMaxQ = 1024;     // tuples per tile
 constexpr int kRMaxU = 128;      // union entries
-constexpr int kRHcap = 256;      // K octets (2048 ranks) per tile
+constexpr int kRHcap = 512;      // K octets (4096 ranks) per tile
 constexpr int kRMaxCoef = 1024;  // coefficient octets per tile
 constexpr int kRMaxWords = 128;  // adapter bitmap words: pools of at most 4096 adapters
 // record layout (int32 words): header {Q, H, fast, C, U, idx offset, coef

@@ -39,6 +39,10 @@ MFMA_CASES = {
     # half the tokens without pairs, ragged last tile and column tile
     "mx_empty": lambda: W.random_case(152, T=290, N=16, d_in=96, d_out=136, r_max=16,
                                       max_pairs=3, empty_frac=0.5),
+    # rank-64 adapters at full rank, about 45 a tile: 330-400 K octets a tile
+    # (more than 256), within the record
+    "mx_octets": lambda: W.random_case(158, T=260, N=60, d_in=64, d_out=264, r_max=64,
+                                       max_pairs=2),
     # requests of 64 tokens sharing one composite (dense unions)
     "mx_requests": lambda: W.random_case(153, T=384, N=30, d_in=256, d_out=1032, r_max=16,
                                          max_pairs=6, tokens_per_group=64, with_k=True),
@@ -71,7 +75,7 @@ def _mixed_case():
 MFMA_CASES["mx_mixed"] = _mixed_case
 
 # limits of a tile record (the kernel's constants)
-MAX_Q, MAX_U, MAX_OCT, MAX_COEF = 1024, 128, 256, 1024
+MAX_Q, MAX_U, MAX_OCT, MAX_COEF = 1024, 128, 512, 1024
 
 FALLBACK_CASES = {
     # more than 1024 tuples in a tile (up to 40 pairs a token)
