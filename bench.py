@@ -735,7 +735,8 @@ def measure(wl, dev, stream, steps, warmup, eager, replicas, latency=False) -> d
     # mapping stage inside the shrink launch; the shrink timing below then
     # times that launch (tcl_remap_shrink), as the step runs it
     fused = (wl.dtype == W.BF16 and c.n_pairs <= 512
-             and os.environ.get("TCL_FUSED_MAPPING") != "0")
+             and os.environ.get("TCL_FUSED_MAPPING") != "0"
+             and os.environ.get("TCL_SHRINK") != "valu")
 
     def shrink_only(i, spp):
         cl = calls[i % R]
@@ -894,7 +895,7 @@ def kernel_names(wl, fused: bool) -> dict:
     from tenant_composite_lora_amd import workloads as W
     c = wl.composites
     bf = wl.dtype == W.BF16
-    if not bf:
+    if not bf or os.environ.get("TCL_SHRINK") == "valu":
         shrink = "shrink_valu"
     elif fused:
         shrink = "plan_shrink"

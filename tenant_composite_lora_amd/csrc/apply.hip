@@ -791,6 +791,15 @@ static int env_int(const char *name, int dflt) {
 }
 
 // Compute units of the current device (256 when the query fails).
+// Matrix-core shrink for bf16 pools.  TCL_SHRINK=valu runs the fp32 VALU
+// kernel on them instead (whole-d_in z rows, no fused mapping): the
+// measurement of the two decode shrinks against each other.
+static bool mfma_shrink(const tcl_module *mods) {
+  if (mods[0].wdtype != TCL_BF16) return false;
+  const char *e = std::getenv("TCL_SHRINK");
+  return !(e && !std::strcmp(e, "valu"));
+}
+
 static int cus() {
   static const int n = [] {
     int dev = 0, c = 0;
@@ -803,7 +812,7 @@ static int cus() {
 }
 
 static int shrink_kchunk(const tcl_plan *p, const tcl_module *mods, int n) {
-  if (mods[0].wdtype != TCL_BF16) return 1 << 30;
+  if (!mfma_shrink(mods)) return 1 << 30;
   int kchunk;
   // TCL_KCHUNK=<elements> fixes the chunk width (tuning knob; 0 = policy)
   const int forced = env_int("TCL_KCHUNK", 0);
@@ -840,7 +849,7 @@ static int n_kchunks(const tcl_module *m, int kchunk) {
 static int64_t shrink_args(const tcl_plan *p, const tcl_module *mods, int n,
                            const void *const *x, const int64_t *ldx, float *const *z,
                            const int *zld, int kchunk, int zero_tail, ShrinkArgs &a) {
-  const bool bf = mods[0].wdtype == TCL_BF16;
+  const bool bf = mfma_shrink(mods);
   const int rows = bf ? 16 : 4;  // rank rows per workgroup job
   a = ShrinkArgs{};
   a.status = p->d.status;
@@ -877,7 +886,7 @@ static int64_t shrink_args(const tcl_plan *p, const tcl_module *mods, int n,
 static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
                          const void *const *x, const int64_t *ldx, float *const *z,
                          const int *zld, int kchunk, int zero_tail, hipStream_t s) {
-  const bool bf = mods[0].wdtype == TCL_BF16;
+  const bool bf = mfma_shrink(mods);
   ShrinkArgs a;
   const int64_t grid = shrink_args(p, mods, n, x, ldx, z, zld, kchunk, zero_tail, a);
   logf("shrink(%s): modules=%d units/item=%d kchunk=%d grid=%lld", bf ? "mfma" : "valu", n,
@@ -905,6 +914,8 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
     hipLaunchKernelGGL(shrink_mfma<8>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
   else if (bf)
     hipLaunchKernelGGL(shrink_mfma<16>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
+  else if (mods[0].wdtype == TCL_BF16)
+    hipLaunchKernelGGL((shrink_valu<bf16_t>), dim3(int(grid)), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((shrink_valu<float>), dim3(int(grid)), dim3(256), 0, s, a);
   TCL_HIP(hipGetLastError());
@@ -1395,7 +1406,7 @@ int tcl_fused_apply_noalloc(const tcl_plan *p, const tcl_module *mods, int32_t n
 // bf16 pools, one launch's worth of modules.  TCL_FUSED_MAPPING=0 turns it
 // off (the mapping kernel then runs on its own before the shrink).
 static bool fused_mapping(const tcl_plan *p, const tcl_module *mods, int n_mods) {
-  if (p->L.mode != PLAN_DIRECT || mods[0].wdtype != TCL_BF16 || n_mods > kMaxMods) return false;
+  if (p->L.mode != PLAN_DIRECT || !mfma_shrink(mods) || n_mods > kMaxMods) return false;
   if (plan_direct_lds_ints(p) > kFusedLdsInts || p->L.items_cap > kFusedItems) return false;
   const char *e = std::getenv("TCL_FUSED_MAPPING");
   return !(e && !std::strcmp(e, "0"));

@@ -316,6 +316,22 @@ def test_fused_apply_parity(name):
         assert np.array_equal(ys[mi][empty], wl.y_base[mi][empty].astype(np.float64))
 
 
+@pytest.mark.parametrize("name", ["config2", "config3", "config4", "ranks_with_zero",
+                                  "static_groups"])
+def test_valu_shrink_on_bf16_pools(name, monkeypatch):
+    """TCL_SHRINK=valu: the fp32 VALU shrink on bf16 pools (whole-d_in z rows,
+    the mapping kernel apart from the shrink), against the oracle."""
+    monkeypatch.setenv("TCL_SHRINK", "valu")
+    wl = CASES[name]()
+    banner(f"valu shrink {name}: modules={len(wl.modules)} T={wl.n_tokens}")
+    ys, _, _ = run_fused(wl)
+    for mi in range(len(wl.modules)):
+        _, d_ora = oracle_apply(wl, mi)
+        err = rel_err(ys[mi] - wl.y_base[mi].astype(np.float64), d_ora)
+        print(f"  module {wl.modules[mi].name}: rel {err:.3e}", flush=True)
+        assert err <= TOL[wl.dtype], (wl.modules[mi].name, err)
+
+
 @pytest.mark.parametrize("name", ["config1", "config2", "ragged_tiles", "ranks_with_zero",
                                   "rank_64_f32", "static_groups"])
 def test_shrink_expand_parity(name):
