@@ -67,11 +67,17 @@ def validate(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
              max_tuples: Optional[int] = None) -> int:
     """Status of a composite table.
 
-    EINVAL: CSR pointers that do not start at 0, end at the token / pair
-    count, or decrease; an adapter id outside [0, n_adapters); a non-finite
-    alpha; the same adapter twice in one composite (composites within the
-    pair limit).  EUNSUPPORTED: a group with more than
-    ``max_pairs_per_group`` pairs.  ENOSPC: more tuples than
+    The pair arrays may be longer than the table: its pairs are those below
+    group_pair_ptr[G], and entries at or beyond it are unused capacity,
+    never read (a gate writing variable-length pair lists into fixed-size
+    arrays; DyMerge-LoRA one-minute summary, padding and masking of the
+    gate's vectorised form).
+
+    EINVAL: CSR pointers that do not start at 0, end at the token count (and
+    at most at the pair arrays' length), or decrease; an adapter id outside
+    [0, n_adapters); a non-finite alpha; the same adapter twice in one
+    composite (composites within the pair limit).  EUNSUPPORTED: a group
+    with more than ``max_pairs_per_group`` pairs.  ENOSPC: more tuples than
     ``max_tuples``.  EINVAL outranks EUNSUPPORTED, which outranks ENOSPC."""
     gt = [int(v) for v in group_tok_ptr]
     gp = [int(v) for v in group_pair_ptr]
@@ -79,17 +85,18 @@ def validate(group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha,
     al = [float(v) for v in np.asarray(pair_alpha, dtype=np.float32)]
     if n_tokens < 0 or n_adapters < 1 or len(gt) < 1 or len(gt) != len(gp):
         return EINVAL
-    if gt[0] != 0 or gt[-1] != n_tokens or gp[0] != 0 or gp[-1] != len(ad):
+    if gt[0] != 0 or gt[-1] != n_tokens or gp[0] != 0 or gp[-1] > len(ad):
         return EINVAL
     if len(al) != len(ad):
         return EINVAL
     for g in range(len(gt) - 1):
         if gt[g + 1] < gt[g] or gp[g + 1] < gp[g]:
             return EINVAL
-    for a in ad:
+    n_pairs = gp[-1]
+    for a in ad[:n_pairs]:
         if a < 0 or a >= n_adapters:
             return EINVAL
-    for w in al:
+    for w in al[:n_pairs]:
         if not math.isfinite(w):
             return EINVAL
     for g in range(len(gt) - 1):
@@ -138,11 +145,15 @@ def gate_topk(logits, candidates, k: int):
     padding) with gate logits ``logits[t, c]``.  Its weights are the softmax
     of the logits over the valid candidates; the k largest weights are kept,
     not renormalised, ties going to the earlier candidate (the softmax is
-    increasing in the logit, so this is the order of the logits).  The
-    pairs of a token are listed in that order.  A token with fewer than k
-    valid candidates lists adapter -1 with weight 0 for each missing pair,
-    and a token with a non-finite valid logit lists adapter -1 with weight 0
-    for all k pairs (tables the mapping stage rejects).
+    increasing in the logit, so this is the order of the logits), listed in
+    that order.  A token with fewer than k valid candidates keeps them all:
+    its pair list is shorter (no valid candidate: an empty composite, which
+    leaves the token unchanged).  A token with a non-finite valid logit lists
+    k pairs of adapter -1 and weight 0, a table the mapping stage rejects.
+
+    The pair lists follow one another; the pair arrays keep n_tokens * k
+    entries, and those at or beyond group_pair_ptr[T] are unused capacity
+    (adapter -1, weight 0).
 
     Returns (group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha) with one
     group per token; pair_alpha is float64 here."""
@@ -150,21 +161,27 @@ def gate_topk(logits, candidates, k: int):
     cd = np.asarray(candidates, dtype=np.int64)
     T = lg.shape[0]
     gtp = np.arange(T + 1, dtype=np.int64)
-    gpp = np.arange(T + 1, dtype=np.int64) * k
+    gpp = np.zeros(T + 1, dtype=np.int64)
     pa = np.full(T * k, -1, dtype=np.int64)
     pw = np.zeros(T * k, dtype=np.float64)
     for t in range(T):
         valid = [c for c in range(cd.shape[1]) if cd[t, c] >= 0]
-        if not valid or not all(math.isfinite(lg[t, c]) for c in valid):
+        if not all(math.isfinite(lg[t, c]) for c in valid):
+            gpp[t + 1] = gpp[t] + k          # k pairs of adapter -1: rejected
             continue
-        top = max(lg[t, c] for c in valid)
-        e = {c: math.exp(lg[t, c] - top) for c in valid}
-        total = sum(e[c] for c in valid)
-        # largest logit first; equal logits keep the candidate order
-        order = sorted(valid, key=lambda c: (-lg[t, c], c))
-        for i, c in enumerate(order[:k]):
-            pa[t * k + i] = cd[t, c]
-            pw[t * k + i] = e[c] / total
+        kept = []
+        if valid:
+            top = max(lg[t, c] for c in valid)
+            e = {c: math.exp(lg[t, c] - top) for c in valid}
+            total = sum(e[c] for c in valid)
+            # largest logit first; equal logits keep the candidate order
+            order = sorted(valid, key=lambda c: (-lg[t, c], c))
+            kept = [(int(cd[t, c]), e[c] / total) for c in order[:k]]
+        base = int(gpp[t])
+        for i, (a, w) in enumerate(kept):
+            pa[base + i] = a
+            pw[base + i] = w
+        gpp[t + 1] = base + len(kept)
     return gtp, gpp, pa, pw
 
 

@@ -372,7 +372,12 @@ def pin_validation(O):
     assert v(*good) == O.OK
     assert v([0, 1, 2], [0, 2, 3], [0, 1, 3], [.5, .5, 1.]) == O.EINVAL        # tokens != T
     assert v([0, 2, 1], [0, 2, 3], [0, 1, 3], [.5, .5, 1.]) == O.EINVAL        # decreasing
-    assert v([0, 1, 3], [0, 2, 2], [0, 1, 3], [.5, .5, 1.]) == O.EINVAL        # pairs != n
+    assert v([0, 1, 3], [0, 2, 4], [0, 1, 3], [.5, .5, 1.]) == O.EINVAL        # past the arrays
+    # entries at or beyond group_pair_ptr[G] are unused capacity, never read:
+    # bad ids, repeats and NaN there change nothing
+    assert v([0, 1, 3], [0, 2, 2], [0, 1, 3], [.5, .5, 1.]) == O.OK
+    assert v([0, 1, 3], [0, 1, 2], [0, 1, -1, 9, 1], [.5, .5, np.nan, 1., 2.]) == O.OK
+    assert v([0, 1, 3], [0, 1, 2], [0, -1, 2], [.5, .5, 1.]) == O.EINVAL       # inside: still checked
     assert v([0, 1, 3], [0, 2, 3], [0, 4, 3], [.5, .5, 1.]) == O.EINVAL        # id >= N
     assert v([0, 1, 3], [0, 2, 3], [0, -1, 3], [.5, .5, 1.]) == O.EINVAL       # id < 0
     assert v([0, 1, 3], [0, 2, 3], [1, 1, 3], [.5, .5, 1.]) == O.EINVAL        # duplicate
@@ -429,11 +434,34 @@ def pin_gate(O):
     _, _, pa5, pw5 = O.gate_topk([[0.3, 9.0, -0.2, 0.7]], [[4, -1, 6, 8]], 2)
     _, _, pa6, pw6 = O.gate_topk([[0.3, -0.2, 0.7]], [[4, 6, 8]], 2)
     assert np.array_equal(pa5, pa6) and np.allclose(pw5, pw6, rtol=1e-15, atol=0)
-    # fewer valid candidates than k, or a non-finite logit: adapter -1
-    _, _, pa7, pw7 = O.gate_topk([[0.5, 0.0, 0.0]], [[5, -1, -1]], 2)
-    assert pa7.tolist() == [5, -1] and pw7.tolist() == [1.0, 0.0]
-    _, _, pa8, pw8 = O.gate_topk([[float("nan"), 0.0]], [[5, 6]], 2)
-    assert pa8.tolist() == [-1, -1] and pw8.tolist() == [0.0, 0.0]
+    # fewer valid candidates than k: a shorter pair list (one valid
+    # candidate keeps weight 1); none: an empty composite; the arrays keep
+    # T * k entries, the unused tail adapter -1 and weight 0
+    g7, gp7, pa7, pw7 = O.gate_topk([[0.5, 0.0, 0.0]], [[5, -1, -1]], 2)
+    assert gp7.tolist() == [0, 1] and pa7.tolist() == [5, -1] and pw7.tolist() == [1.0, 0.0]
+    assert O.validate(g7, gp7, pa7, pw7, 1, 6) == O.OK
+    g9, gp9, pa9, pw9 = O.gate_topk([[0.1, 0.2], [0.3, 0.4], [1.0, 2.0]],
+                                    [[-1, -1], [7, -1], [3, 4]], 2)
+    assert gp9.tolist() == [0, 0, 1, 3] and pa9.tolist() == [7, 4, 3, -1, -1, -1]
+    e1 = 1.0 / (1.0 + np.exp(-1.0))
+    assert np.allclose(pw9[:3], [1.0, e1, 1.0 - e1], rtol=1e-15, atol=0)
+    assert O.validate(g9, gp9, pa9, pw9, 3, 8) == O.OK
+    # the unused tail is not part of the table: the plan equals that of the
+    # trimmed arrays, and the empty token is left as it was
+    trim = (g9, gp9, pa9[:3], pw9[:3])
+    full, cut = O.plan(g9, gp9, pa9, pw9), O.plan(*trim)
+    assert all(np.array_equal(full[key], cut[key]) for key in cut)
+    Ag = np.ones((8, 1, 2))
+    Bg = np.ones((8, 1, 2))
+    xg = np.ones((3, 2))
+    y0 = np.zeros((3, 2))
+    yg, _ = O.apply(g9, gp9, pa9, pw9, Ag, Bg, None, xg, y0)
+    assert np.array_equal(yg[0], [0.0, 0.0])
+    assert np.allclose(yg[1], [2.0, 2.0]) and np.allclose(yg[2], [2.0, 2.0])
+    # a non-finite logit: k pairs of adapter -1, a table the mapping rejects
+    g8, gp8, pa8, pw8 = O.gate_topk([[float("nan"), 0.0]], [[5, 6]], 2)
+    assert gp8.tolist() == [0, 2] and pa8.tolist() == [-1, -1] and pw8.tolist() == [0.0, 0.0]
+    assert O.validate(g8, gp8, pa8, pw8, 1, 7) == O.EINVAL
     # brute force on small cases: the kept set has the largest total weight
     # of all k-subsets
     from itertools import combinations

@@ -28,8 +28,11 @@ MUTANTS = {
                     "if False:"),
     "adapter_fraction_one_side": ("return (d_in + d_out) * r / (d_in * d_out)",
                                   "return d_in * r / (d_in * d_out)"),
-    "gate_renormalised": ("pw[t * k + i] = e[c] / total",
-                          "pw[t * k + i] = e[c] / sum(e[o] for o in order[:k])"),
+    "gate_renormalised": ("e[c] / total) for c in order[:k]]",
+                          "e[c] / sum(e[o] for o in order[:k])) for c in order[:k]]"),
+    "gate_short_padded": ("gpp[t + 1] = base + len(kept)", "gpp[t + 1] = base + k"),
+    "validate_full_arrays": ("gp[-1] > len(ad)", "gp[-1] != len(ad)"),
+    "validate_reads_tail": ("for a in ad[:n_pairs]:", "for a in ad:"),
     "gate_ties_to_later": ("order = sorted(valid, key=lambda c: (-lg[t, c], c))",
                            "order = sorted(valid, key=lambda c: (-lg[t, c], -c))"),
     "gate_smallest": ("order = sorted(valid, key=lambda c: (-lg[t, c], c))",
