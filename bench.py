@@ -103,7 +103,8 @@ KERNEL_SOURCES.update({k: ("tile.hip", "kern_common.hpp", "tcl_internal.hpp")
                        for k in ("tile_prep", "expand_tile")})
 KERNEL_SOURCES.update({k: ("pack.hip", "kern_common.hpp", "tcl_internal.hpp")
                        for k in ("pack_offsets_kernel", "pack_b_kernel")})
-KERNEL_SOURCES["gate_topk_kernel"] = ("gate.hip", "tcl_internal.hpp")
+KERNEL_SOURCES.update({k: ("gate.hip", "tcl_internal.hpp")
+                       for k in ("gate_count_kernel", "gate_scan_kernel", "gate_topk_kernel")})
 # the producer's four kernels are summarised per fleet under the entry point's name
 KERNEL_SOURCES["tcl_factor_balanced"] = ("factor.hip", "tcl_internal.hpp")
 FACTOR_KERNELS = ("tsqr_leaf", "gram_kernel", "factor_core", "factor_out")
@@ -114,7 +115,8 @@ APPLY_SOURCES = ("apply.hip", "kern_common.hpp", "plan_core.hpp", "tcl_internal.
 PMC_KERNELS = ("plan_shrink", "shrink_mfma", "shrink_mfma_pair", "shrink_valu", "expand_kernel",
                "tile_prep", "expand_tile", "tile_order_count", "tile_order_place",
                "pack_offsets_kernel", "pack_b_kernel", "plan_kernel", "plan_m_local",
-               "plan_m_scan", "plan_m_scatter", "gate_topk_kernel")
+               "plan_m_scan", "plan_m_scatter", "gate_count_kernel", "gate_scan_kernel",
+               "gate_topk_kernel")
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -838,7 +840,8 @@ def measure(wl, dev, stream, steps, warmup, eager, replicas, latency=False) -> d
         timed(rg)
         g_us = timed(rg) / GS * 1e6
         g_bytes = T * C * 8 + (T + 1) * 8 + T * gk * 8
-        gate = {"kernel": "gate_topk_kernel", "us": g_us, "alg_bytes": g_bytes,
+        gate = {"kernel": "gate_count_kernel+gate_scan_kernel+gate_topk_kernel", "us": g_us,
+                "alg_bytes": g_bytes,
                 "gbs": g_bytes / g_us / 1e3, "k": gk, "candidates": C}
     kb = kernel_bytes(wl)
     dom = max(("shrink", "expand"), key=lambda n: per[n])

@@ -88,10 +88,15 @@ typedef enum { TCL_BF16 = 0, TCL_F32 = 1 } tcl_dtype;
  *   group_tok_ptr [n_groups+1]: group g covers tokens [ptr[g], ptr[g+1]);
  *                               ptr[0] = 0, non-decreasing, ptr[G] = n_tokens.
  *   group_pair_ptr[n_groups+1]: group g owns pairs [ptr[g], ptr[g+1]);
- *                               ptr[0] = 0, non-decreasing, ptr[G] = n_pairs.
+ *                               ptr[0] = 0, non-decreasing, ptr[G] <= n_pairs.
  *   pair_adapter [n_pairs]    : adapter id in [0, n_adapters), no id twice in
  *                               one group.
  *   pair_alpha   [n_pairs]    : finite fp32 weight (copied bit for bit).
+ *   n_pairs is the length of the two pair arrays.  The table's pairs are
+ *   those below group_pair_ptr[G]; entries at or beyond it are unused
+ *   capacity and are never read (a gate on the GPU writes variable-length
+ *   pair lists into arrays sized for the largest; DyMerge-LoRA one-minute
+ *   summary, padding and masking).
  *   max_tuples                : capacity for P = sum_g tokens_g * pairs_g.
  *
  * A device-resident table is validated on the device by the mapping stage;
@@ -120,11 +125,14 @@ typedef struct {
  * tcl_module_init (or tcl_module_load_ranks).
  *
  * B_k is an optional DEVICE rank-contiguous copy of B for the prefill expand
- * on the matrix cores: B_k[a][n][j] = row j of B_a^T at column n for j < k_a,
- * zero for k_a <= j < r_pad, r_pad = r_max rounded up to a multiple of 8
- * ([n_adapters][d_out][r_pad] bf16).  Fill it with tcl_module_pack after the
- * ranks are loaded (and again whenever B_t or the ranks change).  NULL: the
- * prefill expand runs on the per-token kernel over B_t.
+ * on the matrix cores (tcl_module_pack_bytes bytes): a header of int32
+ * first-unit offsets per adapter and one zero 16-byte unit, padded to 256
+ * bytes, then per adapter a [d_out][ceil(k_a / 8)] array of 16-byte units,
+ * unit (n, o) holding ranks 8o .. 8o + 7 of column n of B_a^T as bf16 (zero
+ * at and beyond k_a).  Fill it with tcl_module_pack after the ranks are
+ * loaded (and again whenever B_t or the ranks change), or with
+ * tcl_bam_pool_init / tcl_bam_load for a slot pool.  NULL: the prefill
+ * expand runs on the per-token kernel over B_t.
  */
 typedef struct {
   int32_t n_adapters;
@@ -204,8 +212,9 @@ void tcl_plan_free(tcl_plan *p);
  * array in HOST memory.  The table is validated on the host before any HIP
  * call, by the rules the mapping stage applies on the device and with the
  * same codes and precedence: TCL_EINVAL (CSR pointers that do not start at
- * 0, end at n_tokens / n_pairs or decrease; an adapter id outside
- * [0, n_adapters); a non-finite alpha; an adapter twice in one composite of
+ * 0, do not end at n_tokens, end beyond n_pairs or decrease; among the
+ * table's pairs, an adapter id outside [0, n_adapters) or a non-finite
+ * alpha; an adapter twice in one composite of
  * at most TCL_MAX_PAIRS_PER_GROUP pairs) before TCL_EUNSUPPORTED (a larger
  * composite) before TCL_ENOSPC (more tuples than max_tuples).
  *
@@ -273,7 +282,7 @@ int tcl_module_init(tcl_module *m, const int32_t *k_host, int32_t *k_dev, void *
  * written on `stream` from B_t and the module's ranks (m->k_dev, or r_max for
  * every adapter when NULL); then m->B_k = B_k.  Rows of B_t at or beyond an
  * adapter's rank are not read.  B_k: caller-owned device memory of at least
- * tcl_module_pack_bytes bytes, 16-byte aligned.  The pack reads the ranks
+ * tcl_module_pack_bytes bytes, 256-byte aligned.  The pack reads the ranks
  * queued before it on the stream; re-pack after new ranks or new factors.
  * Errors: those of tcl_module_init's module checks; TCL_EUNSUPPORTED (fp32
  * pool), TCL_EINVAL (B_k NULL), TCL_EALIGN, TCL_ENOSPC (bytes too small),
@@ -393,17 +402,21 @@ int tcl_remap_shrink(tcl_plan *p, const tcl_composites *c, const tcl_module *mod
  * logits[t * ld_logits + c], fp32, c in [0, n_candidates).  Its weights are
  * the softmax of the logits over the valid candidates, computed in fp32; the
  * k largest are kept, not renormalised, ties going to the smaller c (the
- * order of the logits, since the softmax is increasing).  Output, one group
- * per token, device arrays of the caller:
- *   group_tok_ptr[t] = t        (n_tokens + 1 entries)
- *   group_pair_ptr[t] = t * k   (n_tokens + 1 entries)
- *   pair_adapter[t * k + i], pair_alpha[t * k + i], i in [0, k): the kept
- *     pairs, largest weight first   (n_tokens * k entries each)
- * A token with fewer than k valid candidates gets adapter -1 (weight 0) for
- * each missing pair, and a token with a non-finite valid logit gets adapter
- * -1 (weight 0) for all k: the mapping stage rejects such a table with
- * TCL_EINVAL.  Candidate ids are not range-checked here; the mapping stage
- * does that too.  The table is ready for tcl_plan_map, tcl_plan_remap or
+ * order of the logits, since the softmax is increasing).  A token keeps
+ * k pairs, or all its valid candidates when it has fewer than k (none: an
+ * empty composite, the token is left unchanged).  A token with a non-finite
+ * valid logit gets k pairs of adapter -1 (weight 0): the mapping stage
+ * rejects such a table with TCL_EINVAL.  Output, one group per token, device
+ * arrays of the caller:
+ *   group_tok_ptr[t] = t                       (n_tokens + 1 entries)
+ *   group_pair_ptr[t] = pairs of tokens < t    (n_tokens + 1 entries)
+ *   pair_adapter[group_pair_ptr[t] + i], pair_alpha[...], i below token t's
+ *     count: its pairs, largest weight first   (n_tokens * k entries each;
+ *     the entries at or beyond group_pair_ptr[n_tokens] are unused capacity,
+ *     written as adapter -1 and weight 0)
+ * Pass n_pairs = n_tokens * k to the mapping calls.  Three launches (counts,
+ * their scan in one workgroup, the pairs).  Candidate ids are not range-checked here; the
+ * mapping stage does that.  The table is ready for tcl_plan_map, tcl_plan_remap or
  * tcl_remap_apply without a trip through host memory.
  * Host checks: 1 <= n_candidates <= 64, 1 <= k <= n_candidates, k <=
  * TCL_MAX_PAIRS_PER_GROUP, leading dimensions >= n_candidates, n_tokens >= 0,

@@ -1,10 +1,22 @@
 // Token-level gate: the composite table of dynamic composition from gate
 // logits (DyMerge-LoRA, section 3.1 dynamic composition; section 5.1 Sparse
-// workload).  One wave per token, one lane per candidate: the softmax over
-// the valid candidates, then k rounds of a wave-wide maximum pick the kept
-// pairs.  The table goes straight to the mapping stage in device memory.
-// The work per token is a few dozen instructions; the time is the launch
-// and one load round trip.
+// workload; the one-minute summary's padding and masking of the gate's
+// vectorised form).  Three launches:
+//   gate_count_kernel  one wave per token: how many pairs the token keeps
+//                      (k, fewer when it has fewer valid candidates, k again
+//                      for a token with a non-finite logit, whose pairs name
+//                      adapter -1 so that the mapping stage rejects the
+//                      table), into group_pair_ptr[t + 1];
+//   gate_scan_kernel   one workgroup: those counts into the pair offsets;
+//   gate_topk_kernel   one wave per token, one lane per candidate: the
+//                      softmax over the valid candidates, then rounds of a
+//                      wave-wide maximum pick the kept pairs, written at the
+//                      token's offset; each token also writes its share of
+//                      the unused tail of the pair arrays (adapter -1,
+//                      weight 0), so every entry is defined.
+// The table goes straight to the mapping stage in device memory.  The work
+// per token is a few dozen instructions; the time is the launches and a load
+// round trip each.
 #include <cmath>
 
 #include "tcl_internal.hpp"
@@ -56,41 +68,98 @@ __device__ inline float wave_sum(float v) {
   return wave_reduce(v, 0.f, [](float a, float b) { return a + b; });
 }
 
-__global__ __launch_bounds__(64 * kGateWaves) void gate_topk_kernel(GateArgs g) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kGateWaves + (threadIdx.x >> 6);
-  if (t > g.T) return;
-  if (t == g.T) {
-    // the end entries of the two pointer arrays
-    if (lane == 0) {
-      g.gtp[t] = t;
-      g.gpp[t] = t * g.k;
-    }
-    return;
-  }
+// The candidate row of token t: one lane per candidate.
+struct GateRow {
+  int id;
+  float l;
+  bool valid;
+};
+
+__device__ inline GateRow gate_row(const GateArgs &g, int t, int lane) {
   // both loads at once (the logit does not wait for the id)
   const bool in = lane < g.C;
   const int id = in ? g.cand[int64_t(t) * g.ldc + lane] : -1;
   const float lin = in ? g.logits[int64_t(t) * g.ldl + lane] : 0.f;
   const bool valid = id >= 0;
-  const float l = valid ? lin : 0.f;
-  const bool bad = __ballot(valid && !isfinite(l)) != 0;
-  const float m = wave_max(valid ? l : -INFINITY);
-  const float e = valid ? expf(l - m) : 0.f;
+  return {id, valid ? lin : 0.f, valid};
+}
+
+// pairs token t keeps: min(k, valid candidates), or k when a valid logit is
+// not finite (those pairs name adapter -1)
+__device__ inline int gate_kept(const GateArgs &g, const GateRow &r) {
+  const bool bad = __ballot(r.valid && !isfinite(r.l)) != 0;
+  const int nv = __popcll(__ballot(r.valid));
+  return bad ? g.k : min(g.k, nv);
+}
+
+__global__ __launch_bounds__(64 * kGateWaves) void gate_count_kernel(GateArgs g) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kGateWaves + (threadIdx.x >> 6);
+  if (t >= g.T) return;
+  const GateRow r = gate_row(g, t, lane);
+  const int n = gate_kept(g, r);
+  if (lane == 0) g.gpp[t + 1] = n;
+}
+
+// In place: group_pair_ptr[t + 1] from the count of token t to the end of its
+// pairs.  Thread i owns a contiguous run of tokens.  (Counting inside this
+// one workgroup instead of in gate_count_kernel serialises a load round trip
+// per token a wave: 46 us for 2048 tokens against 7 us for the three
+// launches.)
+constexpr int kGateScanThreads = 1024;
+
+__global__ __launch_bounds__(kGateScanThreads) void gate_scan_kernel(int32_t *gpp, int32_t T) {
+  __shared__ int wsum[kGateScanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (T + kGateScanThreads - 1) / kGateScanThreads;
+  const int t0 = min(T, tid * per), t1 = min(T, t0 + per);
+  int own = 0;
+  for (int t = t0; t < t1; ++t) own += gpp[t + 1];
+  int inc = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int run = inc - own;
+  for (int j = 0; j < w; ++j) run += wsum[j];
+  for (int t = t0; t < t1; ++t) {
+    const int c = gpp[t + 1];
+    run += c;
+    gpp[t + 1] = run;
+  }
+  if (tid == 0) gpp[0] = 0;
+}
+
+__global__ __launch_bounds__(64 * kGateWaves) void gate_topk_kernel(GateArgs g) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kGateWaves + (threadIdx.x >> 6);
+  if (t > g.T) return;
+  if (t == g.T) {
+    if (lane == 0) g.gtp[t] = t;  // the end entry (group_pair_ptr's is the scan's)
+    return;
+  }
+  const GateRow r = gate_row(g, t, lane);
+  const int base = g.gpp[t], n = g.gpp[t + 1] - base, total = g.gpp[g.T];
+  const bool bad = __ballot(r.valid && !isfinite(r.l)) != 0;
+  const float m = wave_max(r.valid ? r.l : -INFINITY);
+  const float e = r.valid ? expf(r.l - m) : 0.f;
   const float p = e / wave_sum(e);
 
-  // k rounds: the remaining valid lane with the largest logit, the lowest
+  // n rounds: the remaining valid lane with the largest logit, the lowest
   // such lane on ties; lane i keeps round i's pick
-  uint64_t left = __ballot(valid);
+  uint64_t left = __ballot(r.valid);
   int my_a = -1;
   float my_p = 0.f;
-  for (int i = 0; i < g.k; ++i) {
+  for (int i = 0; i < n && !bad; ++i) {
     const bool cand_here = (left >> lane) & 1;
-    const float mx = wave_max(cand_here ? l : -INFINITY);
-    const uint64_t win = __ballot(cand_here && l == mx);
-    if (win == 0) break;  // fewer valid candidates than k
+    const float mx = wave_max(cand_here ? r.l : -INFINITY);
+    const uint64_t win = __ballot(cand_here && r.l == mx);
+    if (win == 0) break;
     const int wl = __builtin_ctzll(win);
-    const int a = __builtin_amdgcn_readlane(id, wl);
+    const int a = __builtin_amdgcn_readlane(r.id, wl);
     const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), wl));
     if (lane == i) {
       my_a = a;
@@ -98,18 +167,16 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_topk_kernel(GateArgs g) 
     }
     left &= ~(uint64_t(1) << wl);
   }
-  if (bad) {
-    my_a = -1;
-    my_p = 0.f;
-  }
+  // lanes [0, n): the kept pairs at the token's offset; lanes [n, k): the
+  // token's share of the unused tail, after the total (the tokens before it
+  // left t * k - base entries of the tail)
   if (lane < g.k) {
-    g.pa[int64_t(t) * g.k + lane] = my_a;
-    g.pw[int64_t(t) * g.k + lane] = my_p;
+    const int64_t at = lane < n ? int64_t(base) + lane
+                                : int64_t(total) + int64_t(t) * g.k - base + (lane - n);
+    g.pa[at] = lane < n ? my_a : -1;
+    g.pw[at] = lane < n ? my_p : 0.f;
   }
-  if (lane == 0) {
-    g.gtp[t] = t;
-    g.gpp[t] = t * g.k;
-  }
+  if (lane == 0) g.gtp[t] = t;
 }
 
 }  // namespace
@@ -143,11 +210,16 @@ extern "C" int tcl_gate_topk(const float *logits, int64_t ld_logits, const int32
   if (al & 3) return fail(TCL_EALIGN, "gate: pointers must be 4-byte aligned");
   GateArgs g{logits, candidates, ld_logits, ld_candidates, n_tokens, n_candidates, k,
              group_tok_ptr, group_pair_ptr, pair_adapter, pair_alpha};
-  // one wave per token plus one for the end entries of the pointer arrays
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int count_blocks = int((int64_t(n_tokens) + kGateWaves - 1) / kGateWaves);
+  if (count_blocks > 0)
+    hipLaunchKernelGGL(gate_count_kernel, dim3(count_blocks), dim3(64 * kGateWaves), 0, s, g);
+  hipLaunchKernelGGL(gate_scan_kernel, dim3(1), dim3(kGateScanThreads), 0, s, group_pair_ptr,
+                     n_tokens);
+  // one wave per token plus one for the end entry of group_tok_ptr
   const int64_t waves = int64_t(n_tokens) + 1;
   const int blocks = int((waves + kGateWaves - 1) / kGateWaves);
-  hipLaunchKernelGGL(gate_topk_kernel, dim3(blocks), dim3(64 * kGateWaves), 0,
-                     static_cast<hipStream_t>(stream), g);
+  hipLaunchKernelGGL(gate_topk_kernel, dim3(blocks), dim3(64 * kGateWaves), 0, s, g);
   TCL_HIP(hipGetLastError());
   return TCL_OK;
 }

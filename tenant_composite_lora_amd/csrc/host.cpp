@@ -58,7 +58,8 @@ int check_composites(const tcl_composites *c) {
 // mapping stage (DyMerge-LoRA section 4.3: the tuples are built from the
 // composites; the table's rules are the library's), with its codes and their
 // precedence: TCL_EINVAL (CSR pointers that do not start at 0, end at the
-// token and pair counts or decrease; an adapter id outside [0, N); a
+// token count, end beyond the pair arrays or decrease; an adapter id outside
+// [0, N) among the table's pairs; a
 // non-finite alpha; an adapter twice in a composite of at most
 // TCL_MAX_PAIRS_PER_GROUP pairs) before TCL_EUNSUPPORTED (a larger
 // composite) before TCL_ENOSPC (more tuples than max_tuples).  Counts the
@@ -74,13 +75,17 @@ int validate_host(const tcl_composites *c, int64_t *P_out, int32_t *U_out) {
   if (gt[0] != 0 || gt[G] != T)
     return fail(TCL_EINVAL, "group_tok_ptr must run from 0 to n_tokens (%d .. %d, want 0 .. %d)",
                 gt[0], gt[G], T);
-  if (gp[0] != 0 || gp[G] != NP)
-    return fail(TCL_EINVAL, "group_pair_ptr must run from 0 to n_pairs (%d .. %d, want 0 .. %d)",
+  // the pair arrays hold n_pairs entries; the table's pairs end at gp[G],
+  // and entries beyond it are unused capacity, never read
+  if (gp[0] != 0 || gp[G] > NP)
+    return fail(TCL_EINVAL,
+                "group_pair_ptr must run from 0 to at most n_pairs (%d .. %d, n_pairs %d)",
                 gp[0], gp[G], NP);
   for (int32_t g = 0; g < G; ++g)
     if (gt[g + 1] < gt[g] || gp[g + 1] < gp[g])
       return fail(TCL_EINVAL, "group pointers decrease at group %d", g);
-  for (int32_t q = 0; q < NP; ++q) {
+  const int32_t NPe = gp[G];
+  for (int32_t q = 0; q < NPe; ++q) {
     if (pa[q] < 0 || pa[q] >= N)
       return fail(TCL_EINVAL, "pair %d: adapter id %d outside [0, %d)", q, pa[q], N);
     if (!std::isfinite(pw[q])) return fail(TCL_EINVAL, "pair %d: alpha is not finite", q);

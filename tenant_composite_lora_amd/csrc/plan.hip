@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kMgThreads) void plan_m_local(MArgs A) {
   // ---- groups
   int err = 0;
   if (b == 0 && tid == 0 &&
-      (A.gtp[0] != 0 || A.gtp[G] != T || A.gpp[0] != 0 || A.gpp[G] != NP))
+      (A.gtp[0] != 0 || A.gtp[G] != T || A.gpp[0] != 0 || A.gpp[G] > NP))
     err |= EB_INVAL;
   int gtup = 0;
   if (tid < ng) {

@@ -277,7 +277,8 @@ __device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool
   // table ends: gtp[0] and gpp[0] are thread 0's first entries, gtp[G] and
   // gpp[G] the second ones of thread max(G - 1, 0)
   if (tid == 0 && (t0 != 0 || q0 != 0)) err |= EB_INVAL;
-  if (tid == max(G - 1, 0) && (t1 != T || q1 != NP)) err |= EB_INVAL;
+  // (pairs at or beyond gpp[G] are unused capacity of the arrays)
+  if (tid == max(G - 1, 0) && (t1 != T || q1 > NP)) err |= EB_INVAL;
   if (tid < G) {
     if (!(0 <= t0 && t0 <= t1 && t1 <= T && 0 <= q0 && q0 <= q1 && q1 <= NP)) {
       err |= EB_INVAL;
@@ -291,19 +292,24 @@ __device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool
       else local = (t1 - t0) * (q1 - q0);
     }
   }
-  if (tid < NP) l_pa[tid] = aq;
-  int P = 0, err_groups = 0, gb = 0;
+  int P = 0, err_groups = 0, gb = 0, NPe = 0;
   {
-    int sv[3] = {local, err & EB_INVAL, (err & EB_UNSUP) >> 1}, st[3];
-    block_excl_scan_n<NT, 3>(sv, tmp + 0 * kSlotInts, st);
+    // the table's pair count gpp[G] (the end of the last group's pairs)
+    // travels with the scan
+    const int end = tid == max(G - 1, 0) ? q1 : 0;
+    int sv[4] = {local, err & EB_INVAL, (err & EB_UNSUP) >> 1, end}, st[4];
+    block_excl_scan_n<NT, 4>(sv, tmp + 0 * kSlotInts, st);
     P = st[0];
     gb = sv[0];
     err_groups = (st[1] ? EB_INVAL : 0) | (st[2] ? EB_UNSUP : 0);
+    NPe = st[3];
   }
   if (err_groups & EB_INVAL) {
     if (out) plan_fail<NT>(A, TCL_EINVAL, 0);
     return TCL_EINVAL;
   }
+  // pairs of the table, and -1 for the unused capacity (never an adapter id)
+  if (tid < NP) l_pa[tid] = tid < NPe ? aq : -1;
   if (tid < G) gbase[tid] = gb;
 
   // ---- B: pairs (the group table is sound from here on) -------------------
@@ -311,7 +317,7 @@ __device__ inline int plan_run_small(const PlanArgs &A, int *lds, int *tmp, bool
   int s = 0, tkt = 0, g = 0;
   int4 pi = make_int4(0, 0, 0, 0);
   bool live = false;
-  if (tid < NP) {
+  if (tid < NPe) {
     pi = pinfo[tid];
     g = pg[tid];
     const bool a_ok = aq >= 0 && aq < N;
@@ -529,7 +535,8 @@ __device__ inline int plan_run(const PlanArgs &A, int *lds, int *tmp, bool out, 
   // One thread per contiguous range of groups.  Structural errors stop the
   // mapping here; the per-pair checks below need a sound group table.
   int err = 0;
-  if (tid == 0 && (gtp[0] != 0 || gtp[G] != T || gpp[0] != 0 || gpp[G] != NP)) err |= EB_INVAL;
+  // (pairs at or beyond gpp[G] are unused capacity of the arrays)
+  if (tid == 0 && (gtp[0] != 0 || gtp[G] != T || gpp[0] != 0 || gpp[G] > NP)) err |= EB_INVAL;
   const int gper = (G + NT - 1) / NT;
   const int g0 = min(G, tid * gper), g1 = min(G, g0 + gper);
   int local = 0;
@@ -566,6 +573,7 @@ __device__ inline int plan_run(const PlanArgs &A, int *lds, int *tmp, bool out, 
     if (out) plan_fail<NT>(A, TCL_EINVAL, 0);
     return TCL_EINVAL;
   }
+  const int NPe = gpp[G];  // the table's pairs; the rest of the arrays is unused
 
   // ---- pairs: ids, weights, canonical slots, duplicates --------------------
   // One thread per pair.  The slot is the number of the group's pairs with a
@@ -573,7 +581,7 @@ __device__ inline int plan_run(const PlanArgs &A, int *lds, int *tmp, bool out, 
   // (EUNSUPPORTED) and are not searched for duplicates.  The direct path also
   // adds the pair's tuples to its adapter's count here.
   err = 0;
-  for (int q = tid; q < NP; q += NT) {
+  for (int q = tid; q < NPe; q += NT) {
     const int aq = pa[q];
     const bool a_ok = aq >= 0 && aq < N;
     if (!a_ok) err |= EB_INVAL;
@@ -651,7 +659,7 @@ __device__ inline int plan_run(const PlanArgs &A, int *lds, int *tmp, bool out, 
     n_items = st[2];
     n_segs = st[1];
     __syncthreads();
-    for (int q = tid; q < NP; q += NT) {
+    for (int q = tid; q < NPe; q += NT) {
       const int e = sbk[pa[q]] + tkt[q];
       bkt[e] = q;
       bkw[e] = ptl[q];
@@ -734,7 +742,7 @@ __device__ inline int plan_run(const PlanArgs &A, int *lds, int *tmp, bool out, 
   __syncthreads();
 
   // ---- write the tuples and the per-token index ---------------------------
-  for (int q = tid; q < NP; q += NT) {
+  for (int q = tid; q < NPe; q += NT) {
     const int g = grp[q];
     const int t0 = gtp[g], tl = gtp[g + 1] - t0, pl = gpp[g + 1] - gpp[g];
     const int a = pa[q], s = slot[q], gb = gbase[g];

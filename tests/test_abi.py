@@ -335,3 +335,35 @@ def test_bam_load_host_errors(L):
     f32 = tclora.ModuleDesc(4, 16, 16, 8, tclora.F32, 0x1000, 0x2000, None, None)
     assert L.tcl_bam_pool_init(ctypes.byref(f32), 0x3000, 0x6000, 1 << 20, None) == \
         tclora.EUNSUPPORTED
+
+
+def test_host_validation_ignores_the_unused_tail():
+    """Pair entries at or beyond group_pair_ptr[G] are unused capacity: a
+    tail of invalid ids, repeats and NaN weights changes neither the verdict
+    nor the counts, on the host as in the oracle; a table whose pairs end
+    beyond the arrays is EINVAL."""
+    import oracle as O
+    from tenant_composite_lora_amd import workloads as W
+    rng = np.random.default_rng(31)
+    for trial in range(40):
+        T, N = int(rng.integers(1, 30)), int(rng.integers(2, 12))
+        wl = W.random_case(300 + trial, T=T, N=N, d_in=8, d_out=8, r_max=4,
+                           max_pairs=min(4, N), empty_frac=0.2)
+        c = wl.composites
+        gt, gp = c.group_tok_ptr.astype(np.int32), c.group_pair_ptr.astype(np.int32)
+        ad, al = c.pair_adapter.astype(np.int32), c.pair_alpha.astype(np.float32)
+        extra = int(rng.integers(1, 9))
+        ad_t = np.concatenate([ad, rng.choice([-5, N, 10 ** 6, 0], extra).astype(np.int32)])
+        al_t = np.concatenate([al, np.full(extra, np.nan, np.float32)])
+        want_cut = O.validate(gt, gp, ad, al, T, N)
+        want_tail = O.validate(gt, gp, ad_t, al_t, T, N)
+        assert want_cut == want_tail == tclora.OK
+        rc, P, U = tclora.validate_composites(gt, gp, ad_t, al_t, N, n_tokens=T)
+        rc0, P0, U0 = tclora.validate_composites(gt, gp, ad, al, N, n_tokens=T)
+        assert (rc, P, U) == (rc0, P0, U0) == (tclora.OK, P0, U0)
+        # pairs that end beyond the arrays
+        gp_bad = gp.copy()
+        gp_bad[-1] = len(ad_t) + 1
+        assert O.validate(gt, gp_bad, ad_t, al_t, T, N) == O.EINVAL
+        assert tclora.validate_composites(gt, gp_bad, ad_t, al_t, N, n_tokens=T)[0] == \
+            tclora.EINVAL

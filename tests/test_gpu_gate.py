@@ -62,6 +62,7 @@ CASES = {
     "padding": dict(seed=2, T=500, C=8, k=2, pad_frac=0.3),
     "ties": dict(seed=3, T=300, C=8, k=3, tie_frac=0.5),
     "short_and_bad": dict(seed=4, T=400, C=6, k=2, short_frac=0.1, bad_frac=0.1),
+    "short_only": dict(seed=9, T=300, C=6, k=3, short_frac=0.3, pad_frac=0.2),
     "full_wave": dict(seed=5, T=130, C=64, k=64),
     "one_candidate": dict(seed=6, T=77, C=1, k=1),
     "k_equals_C_with_padding": dict(seed=7, T=200, C=5, k=5, pad_frac=0.2),
@@ -103,19 +104,26 @@ def test_gate_reproduces_sparse_prefill_table():
     assert np.max(np.abs(pw - c.pair_alpha) / c.pair_alpha) <= 2e-6
 
 
-def test_gated_step_vs_oracle():
+@pytest.mark.parametrize("T", [40, 300])
+def test_gated_step_vs_oracle(T):
     """Gate -> mapping stage -> shrink -> expand in device memory, against the
-    oracle apply of the oracle gate's table."""
+    oracle apply of the oracle gate's table.  Some tokens have one valid
+    candidate (a one-pair list) and some none (an empty composite, left
+    unchanged): the table ends before its arrays do.  40 tokens run the
+    decode step (mapping inside the shrink launch), 300 the prefill path."""
     rng = np.random.default_rng(11)
-    N, T, C, k = 64, 300, 8, 2
+    N, C, k = 64, 8, 2
     wl = W.random_case(12, T=T, N=N, d_in=256, d_out=264, r_max=16, max_pairs=2)
     refs = [rng.choice(N, int(rng.integers(5, 9)), replace=False) for _ in range(3)]
     cd = np.full((T, C), -1, np.int32)
     for t in range(T):
         r = refs[t * 3 // T]
         cd[t, :len(r)] = r
+    short = rng.choice(T, T // 8, replace=False)
+    cd[short[: len(short) // 2], 1:] = -1          # one valid candidate
+    cd[short[len(short) // 2:], :] = -1            # none
     lg = rng.standard_normal((T, C)).astype(np.float32)
-    banner(f"gated step: T={T} N={N}")
+    banner(f"gated step: T={T} N={N}, {len(short)} short or empty tokens")
     gtp, gpp, pa, pw = tclora.gate_topk(to_dev(lg), to_dev(cd), k)
     plan = tclora.Plan(gtp, gpp, pa, pw, N, n_tokens=T, max_tuples=T * k)
     mod = make_module(wl.modules[0])
@@ -124,24 +132,29 @@ def test_gated_step_vs_oracle():
     call = tclora.FusedCall(plan, [mod], [x], [y])
     call.remap_apply(gtp, gpp, pa, pw, T)
     torch.cuda.synchronize()
-    assert plan.status()[0] == 0
     ogtp, ogpp, opa, opw = O.gate_topk(lg.astype(np.float64), cd, k)
+    assert int(ogpp[-1]) < T * k
+    rc, P, U = plan.status()
+    assert rc == 0 and P == int(ogpp[-1])
     m = wl.modules[0]
     y_ora, d_ora = O.apply(ogtp, ogpp, opa, opw.astype(np.float32), m.A_t, m.B_t, m.k, wl.x[0],
                            wl.y_base[0])
-    err = rel_err(y.double().cpu().numpy() - wl.y_base[0].astype(np.float64), d_ora)
+    got = y.double().cpu().numpy()
+    err = rel_err(got - wl.y_base[0].astype(np.float64), d_ora)
     print(f"  rel {err:.3e}", flush=True)
     assert err <= TOL[wl.dtype]
+    empty = short[len(short) // 2:]
+    assert np.array_equal(got[empty], wl.y_base[0][empty].astype(np.float64))
 
 
-def test_gated_table_with_missing_pairs_is_rejected():
-    """Adapter -1 (too few candidates) reaches the mapping stage, which
-    rejects the table; the step leaves y untouched."""
+def test_gated_table_with_a_nonfinite_logit_is_rejected():
+    """A token with a NaN logit lists adapter -1, which the mapping stage
+    rejects; the step leaves y untouched."""
     T, C, k, N = 40, 4, 2, 16
     lg = np.random.default_rng(13).standard_normal((T, C)).astype(np.float32)
     cd = np.tile(np.arange(C, dtype=np.int32), (T, 1))
-    cd[17, 1:] = -1
-    banner("gated table with a short token")
+    lg[17, 2] = np.nan
+    banner("gated table with a NaN logit")
     gtp, gpp, pa, pw = tclora.gate_topk(to_dev(lg), to_dev(cd), k)
     plan = tclora.Plan(gtp, gpp, pa, pw, N, n_tokens=T, max_tuples=T * k)
     assert plan.status()[0] == tclora.EINVAL

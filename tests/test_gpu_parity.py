@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import make_module, make_plan, rel_err, run_fused, run_split, to_dev
+from gpu_util import (composites_to_dev, make_module, make_plan, rel_err, run_fused, run_split,
+                      to_dev)
 from tenant_composite_lora_amd import tclora
 from tenant_composite_lora_amd import workloads as W
 
@@ -144,6 +145,60 @@ def test_plan_bit_exact(name):
            f"P={wl.composites.n_tuples()}")
     plan = make_plan(wl.composites)
     assert_plan_equal(plan.copy_out(), oracle_plan(wl.composites))
+
+
+def _with_tail(c, extra=7, seed=0):
+    """The same table with pair arrays longer than its pairs: entries past
+    group_pair_ptr[G] hold ids out of range, repeats and NaN weights, which
+    are unused capacity and must not be read."""
+    rng = np.random.default_rng(seed)
+    bad = rng.choice([-5, c.n_adapters, 10 ** 6, 0], extra).astype(np.int32)
+    return W.Composites(c.n_tokens, c.n_adapters, c.group_tok_ptr, c.group_pair_ptr,
+                        np.concatenate([c.pair_adapter.astype(np.int32), bad]),
+                        np.concatenate([c.pair_alpha.astype(np.float32),
+                                        np.full(extra, np.nan, np.float32)]))
+
+
+TAIL_CASES = ["config2", "config3", "config4", "direct_400_groups", "direct_1500_groups",
+              "count_5000_adapters", "count_9000_groups", "empty_tokens", "64_pairs_per_token"]
+
+
+@pytest.mark.parametrize("name", TAIL_CASES)
+def test_plan_ignores_unused_pair_capacity(name):
+    """Every mapping mode reads the table's pairs only (those below
+    group_pair_ptr[G]): with a tail of invalid entries the plan is the
+    oracle's plan of the table, bit for bit."""
+    wl = CASES[name]()
+    ct = _with_tail(wl.composites)
+    banner(f"plan with unused pair capacity {name}: pairs {wl.composites.n_pairs} "
+           f"of {ct.n_pairs}")
+    plan = make_plan(ct)
+    assert plan.status()[0] == 0
+    assert_plan_equal(plan.copy_out(), oracle_plan(wl.composites))
+
+
+@pytest.mark.parametrize("name", ["config2", "config3", "config4"])
+def test_step_ignores_unused_pair_capacity(name):
+    """The whole step (tcl_remap_apply: the decode configs map inside the
+    shrink launch) over a table with unused pair capacity, against the
+    oracle apply of the table."""
+    wl = CASES[name]()
+    ct = _with_tail(wl.composites, seed=1)
+    banner(f"step with unused pair capacity {name}")
+    plan = make_plan(ct)
+    mods = [make_module(m) for m in wl.modules]
+    xs = [to_dev(x) for x in wl.x]
+    ys = [to_dev(y) for y in wl.y_base]
+    call = tclora.FusedCall(plan, mods, xs, ys)
+    gtp, gpp, pa, pw = composites_to_dev(ct)
+    call.remap_apply(gtp, gpp, pa, pw, ct.n_tokens)
+    torch.cuda.synchronize()
+    assert plan.status()[0] == 0
+    for mi in range(len(wl.modules)):
+        _, d_ora = oracle_apply(wl, mi)
+        err = rel_err(ys[mi].double().cpu().numpy() - wl.y_base[mi].astype(np.float64), d_ora)
+        print(f"  module {mi}: rel {err:.3e}", flush=True)
+        assert err <= TOL[wl.dtype]
 
 
 def test_plan_config5_bit_exact():
