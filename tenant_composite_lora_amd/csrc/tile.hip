@@ -325,14 +325,36 @@ __global__ __launch_bounds__(256) void tile_prep(TileArgs e) {
     const int q = last_le(s_c, 0, Q, f);
     const int o = f - s_c[q], j0 = 8 * o, k = s_k[q];
     const float al = s_al[q];
+    // the partial planes in order, eight at a time with every load issued
+    // before the sums (a plane row holds the octet's first four floats, and
+    // the next four when the octet reaches past rank j0 + 4); floats at or
+    // beyond k are dropped below
     float zv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) zv[i] = 0.f;
-    for (int c = 0; c < nkc; ++c) {
-      const float *zr = Z + int64_t(s_p[q]) * zstride + c * zld + j0;
+    const float *zr = Z + int64_t(s_p[q]) * zstride + j0;
+    const bool hi = j0 + 4 < k;
+    for (int c0 = 0; c0 < nkc; c0 += 8) {
+      float4 v[8][2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (j0 + i < k) zv[i] += zr[i];
+      for (int u = 0; u < 8; ++u) {
+        const float4 *src = reinterpret_cast<const float4 *>(zr + (c0 + u) * zld);
+        const bool in = c0 + u < nkc;
+        v[u][0] = in ? src[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[u][1] = in && hi ? src[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u >= nkc) break;
+        zv[0] += v[u][0].x;
+        zv[1] += v[u][0].y;
+        zv[2] += v[u][0].z;
+        zv[3] += v[u][0].w;
+        zv[4] += v[u][1].x;
+        zv[5] += v[u][1].y;
+        zv[6] += v[u][1].z;
+        zv[7] += v[u][1].w;
+      }
     }
     uint32_t pk[4];
 #pragma unroll

@@ -255,3 +255,64 @@ def test_tile_config5_rows(monkeypatch):
         err = rel_err(ys[mi][rows] - base, want - base)
         print(f"  module {mi}: rel {err:.3e}", flush=True)
         assert err <= TOL[W.BF16]
+
+
+def _two_modules(wl, seed):
+    w2 = W.random_case(seed, T=wl.n_tokens, N=wl.n_adapters, d_in=136, d_out=264, r_max=8,
+                       max_pairs=3, with_k=True)
+    wl.modules.append(w2.modules[0])
+    wl.x.append(w2.x[0])
+    wl.y_base.append(w2.y_base[0])
+    return wl
+
+
+def _dense_and_sparse():
+    """Four requests of 64 tokens over three adapters each, then 192 tokens
+    over the whole pool of 64 adapters: tiles with small and large unions."""
+    wl = W.random_case(166, T=448, N=64, d_in=384, d_out=200, r_max=16, max_pairs=4,
+                       with_k=True)
+    rng = np.random.default_rng(167)
+    ads = []
+    for _ in range(4):
+        cand = rng.choice(64, 3, replace=False)
+        for _ in range(64):
+            ads.append(rng.choice(cand, int(rng.integers(1, 3)), replace=False).tolist())
+    for _ in range(192):
+        ads.append(rng.choice(64, int(rng.integers(2, 5)), replace=False).tolist())
+    als = [rng.random(len(a)).astype(np.float32).tolist() for a in ads]
+    wl.composites = W.csr_from_token_lists(ads, als, 64)
+    return wl
+
+
+REQUEST_CASES = {
+    # requests of 64 tokens sharing one composite of up to 6 adapters
+    "rq_requests": lambda: W.random_case(163, T=384, N=30, d_in=512, d_out=264, r_max=16,
+                                         max_pairs=6, tokens_per_group=64, with_k=True),
+    # two modules, d_in not a multiple of 32 and a ragged last tile
+    "rq_two_modules": lambda: _two_modules(W.random_case(164, T=300, N=12, d_in=264, d_out=136,
+                                                         r_max=16, max_pairs=3,
+                                                         tokens_per_group=50, with_k=True), 165),
+    # small-union and large-union tiles in one batch
+    "rq_mixed": _dense_and_sparse,
+}
+
+
+@pytest.mark.parametrize("name", sorted(REQUEST_CASES))
+def test_tile_expand_request_batches(name, monkeypatch):
+    """Request-shaped prefill batches through the token-tile expand."""
+    wl = REQUEST_CASES[name]()
+    banner(f"tile expand {name}: T={wl.n_tokens} modules={len(wl.modules)}")
+    assert wl.n_tokens >= 256
+    _auto(monkeypatch)
+    ys, _, _ = run_fused(wl)
+    _check(wl, ys, "tile")
+
+
+def test_tile_expand_many_partial_planes(monkeypatch):
+    """Ten K-chunk partial planes a tuple (rank 8, d_in 600 in chunks of 64):
+    the expand sums a full group of eight planes and a ragged group of two."""
+    wl = W.random_case(168, T=320, N=24, d_in=600, d_out=264, r_max=8, max_pairs=4, with_k=True)
+    banner("tile expand, 10 partial planes")
+    _auto(monkeypatch, kchunk=64)
+    ys, _, _ = run_fused(wl)
+    _check(wl, ys, "tile 10 planes")
