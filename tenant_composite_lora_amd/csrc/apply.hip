@@ -136,7 +136,7 @@ constexpr int kShrinkSteps = 8;   // 32-element K steps each lane has in flight
 // through LDS in wave order.  z is written final.
 // Jobs job0, job0 + stride, ... of one workgroup (8 waves); each lane keeps
 // STEPS K steps of loads in flight.
-template <int STEPS>
+template <int STEPS, int RT = 1>
 __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int stride,
                                         f32x4_t (*red)[64], const Item *litems = nullptr,
                                         int n_litems = 0) {
@@ -173,32 +173,35 @@ __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int strid
     const bf16_t *Aw = static_cast<const bf16_t *>(s.m[mi].W);
     const bf16_t *Xw = static_cast<const bf16_t *>(s.m[mi].io);
     const int unit = rgg - first;
-    const int rt = unit / nkc, kc = unit - rt * nkc;  // rank tile, K chunk
+    const int rt = unit / nkc, kc = unit - rt * nkc;  // rank tile group, K chunk
     const int zstride = s.m[mi].zstride;
     float *Z = s.m[mi].z + kc * zld;  // this chunk's partial row inside each tuple row
-    const int j0 = rt * 16;
+    const int j0 = rt * 16 * RT;
     const int a = head.x, p0 = head.y, ntok = head.z;
     const int k = eff_rank(k_dev, a, r_max);
     if (j0 >= k) {
-      // whole rank tile beyond the effective rank
-      if (s.zero_tail && w == 0) {
-        const int j = j0 + row;
+      // every rank tile of the job beyond the effective rank
+      if (s.zero_tail && w < RT) {
+        const int j = j0 + 16 * w + row;
         for (int tt = kg; tt < ntok; tt += 4)
           if (j < r_max) Z[int64_t(p0 + tt) * zstride + j] = 0.f;
       }
       continue;
     }
+    const bool hi = RT == 2 && j0 + 16 < k;  // the second rank tile holds ranks
     const int tok = row < ntok ? tokl : -1;
-    const int jr = j0 + row;  // rank row this lane feeds
+    const int jr = j0 + row;  // rank row this lane feeds (and jr + 16)
     const bf16_t *Xr = tok >= 0 ? Xw + int64_t(tok) * ld + kg * 8 : nullptr;
     const bf16_t *Ar = jr < k ? Aw + (int64_t(a) * r_max + jr) * dd + kg * 8 : nullptr;
+    const bf16_t *Ar1 =
+        RT == 2 && jr + 16 < k ? Aw + (int64_t(a) * r_max + jr + 16) * dd + kg * 8 : nullptr;
     // K steps of this chunk, split over the waves
     const int c0 = kc * (kchunk / 32), c1 = min((dd + 31) / 32, c0 + kchunk / 32);
     const int per = (c1 - c0 + kShrinkWaves - 1) / kShrinkWaves;
     const int s0 = c0 + w * per, s1 = min(c1, s0 + per);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int st = s0; st < s1; st += STEPS) {
-      bf16x8_t xv[STEPS], av[STEPS];
+      bf16x8_t xv[STEPS], av[STEPS], av1[RT == 2 ? STEPS : 1];
 #pragma unroll
       for (int u = 0; u < STEPS; ++u) {
         const int e0 = (st + u) * 32 + kg * 8;  // first element of this lane's granule
@@ -208,25 +211,35 @@ __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int strid
         if (in && Ar) ab = *reinterpret_cast<const uint4 *>(Ar + (st + u) * 32);
         xv[u] = __builtin_bit_cast(bf16x8_t, xb);
         av[u] = __builtin_bit_cast(bf16x8_t, ab);
+        if constexpr (RT == 2) {
+          uint4 ab1 = make_uint4(0, 0, 0, 0);
+          if (in && Ar1) ab1 = *reinterpret_cast<const uint4 *>(Ar1 + (st + u) * 32);
+          av1[u] = __builtin_bit_cast(bf16x8_t, ab1);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < STEPS; ++u)
+      for (int u = 0; u < STEPS; ++u) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[u], av[u], acc, 0, 0, 0);
+        if constexpr (RT == 2)
+          if (hi) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[u], av1[u], acc1, 0, 0, 0);
+      }
     }
     red[w][lane] = acc;
+    if constexpr (RT == 2) red[kShrinkWaves + w][lane] = acc1;
     __syncthreads();
-    if (w == 0) {
-      f32x4_t sum = red[0][lane];
+    if (w < RT) {  // wave t finishes rank tile t of the job
+      const int base = w * kShrinkWaves;
+      f32x4_t sum = red[base][lane];
 #pragma unroll
       for (int v = 1; v < kShrinkWaves; ++v) {
-        const f32x4_t o = red[v][lane];
+        const f32x4_t o = red[base + v][lane];
         sum[0] += o[0];
         sum[1] += o[1];
         sum[2] += o[2];
         sum[3] += o[3];
       }
-      // lane holds tokens 4*kg .. 4*kg+3 of rank column j0 + row
-      const int j = j0 + row;
+      // lane holds tokens 4*kg .. 4*kg+3 of rank column j0 + 16 w + row
+      const int j = j0 + 16 * w + row;
       if (j < r_max) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -242,10 +255,10 @@ __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int strid
   }
 }
 
-template <int STEPS>
+template <int STEPS, int RT>
 __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
-  __shared__ f32x4_t red[kShrinkWaves][64];
-  shrink_mfma_jobs<STEPS>(s, blockIdx.x, gridDim.x, red);
+  __shared__ f32x4_t red[RT * kShrinkWaves][64];
+  shrink_mfma_jobs<STEPS, RT>(s, blockIdx.x, gridDim.x, red);
 }
 
 // Item pairs: one job takes work items 2q and 2q + 1 of one (rank tile, K
@@ -257,7 +270,7 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
 // so z is bit for bit that of shrink_mfma.  Half as many jobs, and half the A
 // rows moved into the compute units, for prefill batches whose segments span
 // several items.
-template <int STEPS>
+template <int STEPS, int RT>
 __device__ inline void shrink_pair_body(const ShrinkArgs &s, int rgg, int4 h0, int tok0,
                                         bool two, int4 h1, int tok1, f32x4_t (*red)[64]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -275,13 +288,13 @@ __device__ inline void shrink_pair_body(const ShrinkArgs &s, int rgg, int4 h0, i
   const int rt = unit / nkc, kc = unit - rt * nkc;
   const int zstride = s.m[mi].zstride;
   float *Z = s.m[mi].z + kc * zld;
-  const int j0 = rt * 16;
+  const int j0 = rt * 16 * RT;
   const int a = h0.x;
   const int k = eff_rank(s.m[mi].k_dev, a, r_max);
   const int n0 = h0.z, n1 = two ? h1.z : 0;
   if (j0 >= k) {
-    if (s.zero_tail && w == 0) {
-      const int j = j0 + row;
+    if (s.zero_tail && w < RT) {
+      const int j = j0 + 16 * w + row;
       if (j < r_max) {
         for (int tt = kg; tt < n0; tt += 4) Z[int64_t(h0.y + tt) * zstride + j] = 0.f;
         for (int tt = kg; tt < n1; tt += 4) Z[int64_t(h1.y + tt) * zstride + j] = 0.f;
@@ -289,16 +302,20 @@ __device__ inline void shrink_pair_body(const ShrinkArgs &s, int rgg, int4 h0, i
     }
     return;
   }
+  const bool hi = RT == 2 && j0 + 16 < k;  // the second rank tile holds ranks
   const int jr = j0 + row;
   const bf16_t *X0 = row < n0 ? Xw + int64_t(tok0) * ld + kg * 8 : nullptr;
   const bf16_t *X1 = row < n1 ? Xw + int64_t(tok1) * ld + kg * 8 : nullptr;
   const bf16_t *Ar = jr < k ? Aw + (int64_t(a) * r_max + jr) * dd + kg * 8 : nullptr;
+  const bf16_t *Ar1 =
+      RT == 2 && jr + 16 < k ? Aw + (int64_t(a) * r_max + jr + 16) * dd + kg * 8 : nullptr;
   const int c0 = kc * (kchunk / 32), c1 = min((dd + 31) / 32, c0 + kchunk / 32);
   const int per = (c1 - c0 + kShrinkWaves - 1) / kShrinkWaves;
   const int s0 = c0 + w * per, s1 = min(c1, s0 + per);
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  // [item][rank tile]
+  f32x4_t acc00 = {0.f, 0.f, 0.f, 0.f}, acc10 = acc00, acc01 = acc00, acc11 = acc00;
   for (int st = s0; st < s1; st += STEPS) {
-    bf16x8_t xv0[STEPS], xv1[STEPS], av[STEPS];
+    bf16x8_t xv0[STEPS], xv1[STEPS], av[STEPS], av1[RT == 2 ? STEPS : 1];
 #pragma unroll
     for (int u = 0; u < STEPS; ++u) {
       const int e0 = (st + u) * 32 + kg * 8;
@@ -310,19 +327,36 @@ __device__ inline void shrink_pair_body(const ShrinkArgs &s, int rgg, int4 h0, i
       xv0[u] = __builtin_bit_cast(bf16x8_t, x0);
       xv1[u] = __builtin_bit_cast(bf16x8_t, x1);
       av[u] = __builtin_bit_cast(bf16x8_t, ab);
+      if constexpr (RT == 2) {
+        uint4 ab1 = make_uint4(0, 0, 0, 0);
+        if (in && Ar1) ab1 = *reinterpret_cast<const uint4 *>(Ar1 + (st + u) * 32);
+        av1[u] = __builtin_bit_cast(bf16x8_t, ab1);
+      }
     }
 #pragma unroll
     for (int u = 0; u < STEPS; ++u) {
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv0[u], av[u], acc0, 0, 0, 0);
-      if (two) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv1[u], av[u], acc1, 0, 0, 0);
+      acc00 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv0[u], av[u], acc00, 0, 0, 0);
+      if (two) acc10 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv1[u], av[u], acc10, 0, 0, 0);
+      if constexpr (RT == 2) {
+        if (hi) {
+          acc01 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv0[u], av1[u], acc01, 0, 0, 0);
+          if (two) acc11 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv1[u], av1[u], acc11, 0, 0, 0);
+        }
+      }
     }
   }
-  red[w][lane] = acc0;
-  red[kShrinkWaves + w][lane] = acc1;
+  // partial tiles: slot (item, rank tile) = item * RT + tile, kShrinkWaves rows each
+  red[w][lane] = acc00;
+  red[RT * kShrinkWaves + w][lane] = acc10;
+  if constexpr (RT == 2) {
+    red[kShrinkWaves + w][lane] = acc01;
+    red[3 * kShrinkWaves + w][lane] = acc11;
+  }
   __syncthreads();
-  // wave 0 finishes the first item, wave 1 the second
-  if (w < (two ? 2 : 1)) {
-    const int base = w * kShrinkWaves, p0 = w ? h1.y : h0.y, nt = w ? n1 : n0;
+  // wave it * RT + t finishes rank tile t of item it
+  const int it = w / RT, t = w - it * RT;
+  if (w < (two ? 2 : 1) * RT) {
+    const int base = w * kShrinkWaves, p0 = it ? h1.y : h0.y, nt = it ? n1 : n0;
     f32x4_t sum = red[base][lane];
 #pragma unroll
     for (int v = 1; v < kShrinkWaves; ++v) {
@@ -332,7 +366,7 @@ __device__ inline void shrink_pair_body(const ShrinkArgs &s, int rgg, int4 h0, i
       sum[2] += o[2];
       sum[3] += o[3];
     }
-    const int j = j0 + row;
+    const int j = j0 + 16 * t + row;
     if (j < r_max) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -347,9 +381,9 @@ __device__ inline void shrink_pair_body(const ShrinkArgs &s, int rgg, int4 h0, i
   __syncthreads();
 }
 
-template <int STEPS>
+template <int STEPS, int RT>
 __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma_pair(ShrinkArgs s) {
-  __shared__ f32x4_t red[2 * kShrinkWaves][64];
+  __shared__ f32x4_t red[2 * RT * kShrinkWaves][64];
   const int row = threadIdx.x & 15;
   const int n_items = min(s.status[ST_ITEMS], s.items_cap);
   const int total = (n_items + 1) / 2 * s.rg_total;
@@ -366,10 +400,10 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma_pair(ShrinkArgs
       t1 = s.items[i1].tok[row];
     }
     if (has1 && h1.x == h0.x) {
-      shrink_pair_body<STEPS>(s, rgg, h0, t0, true, h1, t1, red);
+      shrink_pair_body<STEPS, RT>(s, rgg, h0, t0, true, h1, t1, red);
     } else {
-      shrink_pair_body<STEPS>(s, rgg, h0, t0, false, h0, t0, red);
-      if (has1) shrink_pair_body<STEPS>(s, rgg, h1, t1, false, h1, t1, red);
+      shrink_pair_body<STEPS, RT>(s, rgg, h0, t0, false, h0, t0, red);
+      if (has1) shrink_pair_body<STEPS, RT>(s, rgg, h1, t1, false, h1, t1, red);
     }
   }
 }
@@ -843,14 +877,15 @@ static int n_kchunks(const tcl_module *m, int kchunk) {
   return (m->d_in + kchunk - 1) / kchunk;
 }
 
-// Shrink of n (<= kMaxMods) modules in one launch; z[i] is module i's output
-// ([nkc][cap][zld] partial planes when kchunk < d_in).
-// Launch table and grid of the shrink of n (<= kMaxMods) modules.
+// Launch table and grid of the shrink of n (<= kMaxMods) modules; z[i] is
+// module i's output, a row of nkc partial planes of zld[i] floats per tuple
+// when kchunk < d_in.  rt: 16-rank tiles per matrix-core job.
 static int64_t shrink_args(const tcl_plan *p, const tcl_module *mods, int n,
                            const void *const *x, const int64_t *ldx, float *const *z,
-                           const int *zld, int kchunk, int zero_tail, ShrinkArgs &a) {
+                           const int *zld, int kchunk, int zero_tail, ShrinkArgs &a,
+                           int rt = 1) {
   const bool bf = mfma_shrink(mods);
-  const int rows = bf ? 16 : 4;  // rank rows per workgroup job
+  const int rows = bf ? 16 * rt : 4;  // rank rows per workgroup job
   a = ShrinkArgs{};
   a.status = p->d.status;
   a.items = p->d.items;
@@ -887,10 +922,18 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
                          const void *const *x, const int64_t *ldx, float *const *z,
                          const int *zld, int kchunk, int zero_tail, hipStream_t s) {
   const bool bf = mfma_shrink(mods);
+  // Both 16-rank tiles of an item in one job (two accumulators on the same x
+  // fragments, so x is loaded once for 32 ranks) when a module keeps more
+  // than 16 ranks.  Retained-rank batch (r_max 32, item pairs): 141.7 ->
+  // 97.7 us (without item pairs 156.9 -> 131.0 us).  TCL_SHRINK_RT=1 keeps
+  // one tile a job.
+  int r_top = 0;
+  for (int i = 0; i < n; ++i) r_top = mods[i].r_max > r_top ? mods[i].r_max : r_top;
+  const int rt = bf && r_top > 16 && env_int("TCL_SHRINK_RT", 2) == 2 ? 2 : 1;
   ShrinkArgs a;
-  const int64_t grid = shrink_args(p, mods, n, x, ldx, z, zld, kchunk, zero_tail, a);
-  logf("shrink(%s): modules=%d units/item=%d kchunk=%d grid=%lld", bf ? "mfma" : "valu", n,
-       a.rg_total, kchunk, (long long)grid);
+  const int64_t grid = shrink_args(p, mods, n, x, ldx, z, zld, kchunk, zero_tail, a, rt);
+  logf("shrink(%s): modules=%d units/item=%d kchunk=%d rank tiles/job=%d grid=%lld",
+       bf ? "mfma" : "valu", n, a.rg_total, kchunk, rt, (long long)grid);
   // K steps in flight per lane: 8 (95 VGPRs, two workgroups per CU) measured
   // faster than 16 (161 VGPRs, one per CU); TCL_SSTEPS=16 forces the deeper one
   const int steps = env_int("TCL_SSTEPS", kShrinkSteps) == 16 ? 16 : 8;
@@ -906,14 +949,21 @@ static int launch_shrink(const tcl_plan *p, const tcl_module *mods, int n,
   if (bf && pair) {
     if (pg > 32768) pg = 32768;
     if (pg < 1) pg = 1;
-    if (env_int("TCL_PSTEPS", 4) == 8)
-      hipLaunchKernelGGL(shrink_mfma_pair<8>, dim3(int(pg)), dim3(64 * kShrinkWaves), 0, s, a);
+    if (rt == 2)
+      hipLaunchKernelGGL((shrink_mfma_pair<4, 2>), dim3(int(pg)), dim3(64 * kShrinkWaves), 0, s,
+                         a);
+    else if (env_int("TCL_PSTEPS", 4) == 8)
+      hipLaunchKernelGGL((shrink_mfma_pair<8, 1>), dim3(int(pg)), dim3(64 * kShrinkWaves), 0, s,
+                         a);
     else
-      hipLaunchKernelGGL(shrink_mfma_pair<4>, dim3(int(pg)), dim3(64 * kShrinkWaves), 0, s, a);
-  } else if (bf && steps == 8)
-    hipLaunchKernelGGL(shrink_mfma<8>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
+      hipLaunchKernelGGL((shrink_mfma_pair<4, 1>), dim3(int(pg)), dim3(64 * kShrinkWaves), 0, s,
+                         a);
+  } else if (bf && rt == 2)
+    hipLaunchKernelGGL((shrink_mfma<8, 2>), dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
+  else if (bf && steps == 8)
+    hipLaunchKernelGGL((shrink_mfma<8, 1>), dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
   else if (bf)
-    hipLaunchKernelGGL(shrink_mfma<16>, dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
+    hipLaunchKernelGGL((shrink_mfma<16, 1>), dim3(int(grid)), dim3(64 * kShrinkWaves), 0, s, a);
   else if (mods[0].wdtype == TCL_BF16)
     hipLaunchKernelGGL((shrink_valu<bf16_t>), dim3(int(grid)), dim3(256), 0, s, a);
   else

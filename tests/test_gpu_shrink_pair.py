@@ -121,3 +121,32 @@ def test_pair_retained_rank_full_size_bitwise(monkeypatch):
     ys1, _, _ = run_fused(wl)
     for a, b in zip(ys0, ys1):
         assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+@pytest.mark.parametrize("pair", [False, True])
+@pytest.mark.parametrize("name", ["mfma_ranks24", "mx_rank64", "mx_mixed"])
+def test_rank_tile_pairs_bitwise(name, pair, monkeypatch):
+    """Both 16-rank tiles of an item in one job (the default when a module
+    keeps more than 16 ranks: one x load feeds two accumulators) against one
+    tile a job: z and y bit for bit through the public shrink (zero tail) and
+    the fused apply (split-K partial rows too)."""
+    wl = _case(name)
+    assert max(m.r_max for m in wl.modules) > 16
+    banner(f"rank-tile pairs {name}, item pairs {pair}: ranks {[m.r_max for m in wl.modules]}")
+    for mi in range(len(wl.modules)):
+        _mode(monkeypatch, pair)
+        monkeypatch.setenv("TCL_SHRINK_RT", "1")
+        y0, z0, _ = run_split(wl, mi)
+        monkeypatch.delenv("TCL_SHRINK_RT")
+        y1, z1, _ = run_split(wl, mi)
+        assert np.array_equal(z0.view(np.uint64), z1.view(np.uint64)), mi
+        assert np.array_equal(y0.view(np.uint64), y1.view(np.uint64)), mi
+    for kchunk in (None, 64):
+        _mode(monkeypatch, pair, kchunk=kchunk)
+        monkeypatch.setenv("TCL_SHRINK_RT", "1")
+        ys0, _, _ = run_fused(wl)
+        monkeypatch.delenv("TCL_SHRINK_RT")
+        ys1, _, _ = run_fused(wl)
+        for a, b in zip(ys0, ys1):
+            assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+    _check(wl, ys1, "rank-tile pairs")
