@@ -54,6 +54,7 @@ constexpr int kMgPairs = kMgGroups * TCL_MAX_PAIRS_PER_GROUP;
 constexpr int kMgThreads = 256;
 constexpr int kMultiMaxN = 4096;
 constexpr int kMultiMaxBlocks = 128;
+static_assert(kMultiMaxBlocks <= 4 * 32, "plan_m_scan: at most 32 workgroups a lane when G >= 4");
 
 
 int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLayout *L) {
@@ -439,10 +440,19 @@ __global__ __launch_bounds__(kMgThreads) void plan_m_local(MArgs A) {
   }
 }
 
+// Orders the workgroup's LDS accesses around a barrier without waiting for
+// its outstanding global stores (a plain __syncthreads() waits for those too).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_m_scan(MArgs A) {
   constexpr int NT = kPlanThreads;
   __shared__ int tmp[6 * kSlotInts];
   __shared__ int s_tot[kMultiMaxN];
+  __shared__ int s_ib[kMultiMaxN], s_ec[kMultiMaxN], s_en[kMultiMaxN];  // per adapter
   const int tid = threadIdx.x, NB = A.NB, N = A.N;
   // ---- workgroup totals and error bits (NB <= kMultiMaxBlocks <= NT)
   int pb = 0, err = 0;
@@ -468,23 +478,74 @@ __global__ __launch_bounds__(kPlanThreads) void plan_m_scan(MArgs A) {
   }
   // ---- per adapter: prefix over workgroups (in place) and total.  The
   //      counts are stored workgroup-major ([NB][N]), so for each workgroup
-  //      the threads read consecutive adapters: 32 coalesced rows at a time
-  for (int a = tid; a < N; a += NT) {
-    int32_t *h = A.d.m_hist + a;
-    int run = 0;
-    for (int b0 = 0; b0 < NB; b0 += 32) {
-      int v[32];
-#pragma unroll
-      for (int u = 0; u < 32; ++u) v[u] = b0 + u < NB ? h[int64_t(b0 + u) * N] : 0;
+  //      the threads read consecutive adapters.  Pools of at most NT / 4
+  //      adapters: G >= 4 consecutive lanes share an adapter, each loading
+  //      its <= 32 workgroups' counts in one round, a scan across the group
+  //      giving each lane its offset; larger pools: a lane per adapter, 32
+  //      rows at a time (each batch of loads then waits for the stores
+  //      before it).
+  int G = 1;
+  while (G < 64 && 2 * G * N <= NT) G *= 2;
+  if (G >= 4) {
+    const int a = tid / G, sub = tid & (G - 1);
+    const int per = (NB + G - 1) / G;  // <= kMultiMaxBlocks / 4 = 32
+    const int b0 = sub * per, b1 = min(NB, b0 + per);
+    // rows b0 .. b1 - 1 of this adapter's column, through a pointer that
+    // steps by N (offsets u * N kept as constants would each take scalar
+    // registers)
+    int32_t *const h0 = A.d.m_hist + (a < N ? a : 0) + int64_t(b0) * N;
+    int v[32], sum = 0;
+    {
+      const int32_t *q = h0;
 #pragma unroll
       for (int u = 0; u < 32; ++u) {
-        if (b0 + u < NB) h[int64_t(b0 + u) * N] = run;
-        run += v[u];
+        v[u] = a < N && b0 + u < b1 ? *q : 0;
+        sum += v[u];
+        q += N;
       }
     }
-    s_tot[a] = run;
+    int inc = sum;
+    for (int off = 1; off < G; off <<= 1) {
+      const int t = __shfl_up(inc, off, 64);
+      if (sub >= off) inc += t;
+    }
+    int run = inc - sum;
+    if (a < N) {
+      int32_t *q = h0;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        if (b0 + u < b1) *q = run;
+        run += v[u];
+        q += N;
+      }
+      if (sub == G - 1) s_tot[a] = run;
+    }
+  } else {
+    for (int a = tid; a < N; a += NT) {
+      int32_t *h = A.d.m_hist + a;
+      int run = 0;
+      for (int b0 = 0; b0 < NB; b0 += 32) {
+        int v[32];
+        const int32_t *q = h + int64_t(b0) * N;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          v[u] = b0 + u < NB ? *q : 0;
+          q += N;
+        }
+        int32_t *o = h + int64_t(b0) * N;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          if (b0 + u < NB) *o = run;
+          run += v[u];
+          o += N;
+        }
+      }
+      s_tot[a] = run;
+    }
   }
-  __syncthreads();
+  // s_tot complete; the prefixes stored to m_hist are the scatter kernel's
+  // (no need to wait for them here)
+  lds_barrier();
   // ---- segments and work items: one scan over adapters
   const int per = (N + NT - 1) / NT;
   const int a0 = min(N, tid * per), a1 = min(N, a0 + per);
@@ -502,15 +563,31 @@ __global__ __launch_bounds__(kPlanThreads) void plan_m_scan(MArgs A) {
     A.d.m_sst[a] = ec;
     A.d.m_sib[a] = ei;
     A.d.s_seg[a] = en;
+    s_ib[a] = ei;
+    s_ec[a] = ec;
+    s_en[a] = en;
     if (c > 0) {
       A.d.seg_adapter[en] = a;
       A.d.seg_begin[en] = ec;
-      for (int p0 = ec, i = ei; p0 < ec + c; p0 += kTile, ++i)
-        if (i < A.items_cap) A.d.items[i].head = make_int4(a, p0, min(ec + c, p0 + kTile) - p0, en);
       ++en;
       ei += (c + kTile - 1) / kTile;
     }
     ec += c;
+  }
+  lds_barrier();  // the per-adapter arrays in LDS (global stores may still be in flight)
+  // work-item heads, one thread per item: the item's adapter is the last one
+  // whose first item is at or before it (adapters without tuples own none)
+  const int n_items = min(st[2], A.items_cap);
+  for (int i = tid; i < n_items; i += NT) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_ib[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int a = lo, c = s_tot[a], j = i - s_ib[a];
+    const int p0 = s_ec[a] + j * kTile;
+    A.d.items[i].head = make_int4(a, p0, min(c - j * kTile, kTile), s_en[a]);
   }
   if (tid == 0) {
     A.d.seg_begin[st[1]] = P;
