@@ -855,12 +855,17 @@ static int shrink_kchunk(const tcl_plan *p, const tcl_module *mods, int n) {
   } else {
     // measured on decode batches: tiny batches (fewer workgroups than CUs)
     // gain most from 2048-element chunks, larger decode batches from
-    // 4096-element chunks, prefill-sized batches lose from any split
+    // 4096-element chunks, prefill-sized batches lose from any split.
+    // Prefill batches (with token tiles, whose expand sums the partial
+    // planes eight at a time) of fewer than 1024 workgroups take
+    // 2048-element chunks: sparse gated prefill (768 -> 1536 workgroups)
+    // shrink 26.9 -> 23.6 us, step 138.9 -> 136.3 us.
     int64_t est_items = (p->L.cap < p->L.N ? p->L.cap : p->L.N) + p->L.cap / kTile;
     int64_t units = 0;
     for (int i = 0; i < n; ++i) units += (mods[i].r_max + 15) / 16;
     const int64_t wgs = est_items * units;
-    kchunk = wgs < 256 ? 2048 : (wgs < 4096 ? 4096 : (1 << 30));
+    if (p->L.tiles > 0 && wgs < 1024) kchunk = 2048;
+    else kchunk = wgs < 256 ? 2048 : (wgs < 4096 ? 4096 : (1 << 30));
   }
   // keep a tuple's z row (all partial rows) within 128 floats
   for (int i = 0; i < n; ++i) {
