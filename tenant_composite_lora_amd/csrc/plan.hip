@@ -147,6 +147,8 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.o_ttok = take(l.tiles ? size_t(T) * 4 : 4);
   // per-workgroup counts of the tile order's two launches
   l.o_ocnt = take(l.tiles ? (size_t(T + 255) / 256 + size_t(cap + 255) / 256) * 4 : 4);
+  // and per thread of them the item it places (or -1), from the first to the second
+  l.o_oitem = take(l.tiles ? (size_t(T + 255) / 256 + size_t(cap + 255) / 256) * 256 * 4 : 4);
   // device copy of a host-resident composite table: group_tok_ptr,
   // group_pair_ptr (G + 1 each), pair_adapter, pair_alpha (NP each)
   l.o_tab = take((2 * size_t(G) + 2 + 2 * size_t(NP)) * 4);
@@ -167,9 +169,10 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
 // rare ones, in (adapter, token) order, are the tuples of the sorted plan
 // that are their token's last slot and belong to a rare segment.
 // Two launches over all tokens (the common ones) and all tuples (the rare
-// ones), one item per thread: the first flags the items and counts them per
-// workgroup, the second adds the counts of the earlier workgroups and writes
-// each flagged item at its place.  Workgroups [0, bt) take tokens, [bt, bt +
+// ones), one item per thread: the first flags the items, keeps each
+// thread's flagged item (or -1) and counts them per workgroup, the second
+// adds the counts of the earlier workgroups and writes each flagged item at
+// its place.  Workgroups [0, bt) take tokens, [bt, bt +
 // bp) tuples, so the common tokens come first.
 constexpr int kOrdThreads = 256;
 
@@ -197,6 +200,7 @@ __global__ __launch_bounds__(kOrdThreads) void tile_order_count(PlanDev d, int32
   const int P = ok ? d.status[ST_TUPLES] : 0;
   int item = 0;
   const bool f = ok && ord_flag(d, blockIdx.x, bt, T, P, max(T / kXTok, 1), &item);
+  d.ord_item[blockIdx.x * kOrdThreads + threadIdx.x] = f ? item : -1;
   const uint64_t m = __ballot(f);
   if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = __popcll(m);
   __syncthreads();
@@ -212,8 +216,9 @@ __global__ __launch_bounds__(kOrdThreads) void tile_order_place(PlanDev d, int32
   __shared__ int tmp[kOrdThreads / 64];
   __shared__ int wsum[kOrdThreads / 64];
   const bool ok = d.status[ST_CODE] == TCL_OK;
-  const int P = ok ? d.status[ST_TUPLES] : 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // this thread's item, as the first launch flagged it (-1: none)
+  const int item = d.ord_item[blockIdx.x * kOrdThreads + threadIdx.x];
   // items of the earlier workgroups, and of all of them
   int before = 0, all = 0;
   for (int j = threadIdx.x; j < int(gridDim.x); j += kOrdThreads) {
@@ -238,8 +243,7 @@ __global__ __launch_bounds__(kOrdThreads) void tile_order_place(PlanDev d, int32
     total += wsum[j];
   }
   __syncthreads();
-  int item = 0;
-  const bool f = ok && ord_flag(d, blockIdx.x, bt, T, P, max(T / kXTok, 1), &item);
+  const bool f = item >= 0;
   const uint64_t m = __ballot(f);
   if (lane == 0) tmp[w] = __popcll(m);
   __syncthreads();
@@ -725,6 +729,7 @@ static void bind(tcl_plan *p) {
   d.m_sib = reinterpret_cast<int32_t *>(b + L.o_msib);
   d.tile_tok = reinterpret_cast<int32_t *>(b + L.o_ttok);
   d.ord_cnt = reinterpret_cast<int32_t *>(b + L.o_ocnt);
+  d.ord_item = reinterpret_cast<int32_t *>(b + L.o_oitem);
 }
 
 void plan_fill_args(const tcl_plan *p, const tcl_composites *c, PlanArgs *out) {

@@ -70,7 +70,7 @@ struct PlanLayout {
   // byte offsets inside the device buffer
   size_t o_status, o_tok, o_ad, o_slot, o_alpha, o_toktuple, o_tokrec, o_tokn, o_tokptr,
       o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_sseg, o_ttok, o_ocnt,
-      o_mhist, o_mblk, o_msst, o_msib, o_tab, total;
+      o_oitem, o_mhist, o_mblk, o_msst, o_msib, o_tab, total;
 };
 
 // Mapping-stage algorithms: small tables run in one workgroup with the table
@@ -113,6 +113,7 @@ struct PlanDev {
   int32_t *m_hist, *m_blk, *m_sst, *m_sib;
   int32_t *tile_tok;  // [T]: token order of the prefill expand's tiles (ST_BUSY entries)
   int32_t *ord_cnt;   // per-workgroup counts of the tile order launches
+  int32_t *ord_item;  // per thread of those launches: the item it places, or -1
 };
 
 }  // namespace tcl
