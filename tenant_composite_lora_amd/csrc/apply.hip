@@ -2,8 +2,8 @@
 //
 //   shrink  (LoRAForge approach (4), segmented shrink): z_p = A_a[:, :k]^T
 //           x_{t_p} for one work item (an adapter and up to kTile consecutive
-//           tuples of its segment) and one tile of 16 rank rows, on the
-//           matrix cores in bf16 (shrink_mfma, shrink_mfma_pair, plan_shrink)
+//           tuples of its segment) and one or two tiles of 16 rank rows, on
+//           the matrix cores in bf16 (shrink_mfma, shrink_mfma_pair, plan_shrink)
 //           or with fp32 dot products and a wave butterfly (shrink_valu).
 //           Decode batches split d_in into K chunks whose partial z rows the
 //           expand adds in chunk order.
@@ -126,8 +126,9 @@ constexpr int kShrinkWaves = 8;   // waves per workgroup, splitting d_in
 constexpr int kShrinkSteps = 8;   // 32-element K steps each lane has in flight
 
 // z[tokens x ranks] = X[tokens x d_in] . A_a^T[d_in x ranks] for one work item
-// (up to 16 tuples of one adapter) and one tile of 16 rank rows, with
-// v_mfma_f32_16x16x32_bf16.  Both operands load straight from memory: lane l
+// (up to 16 tuples of one adapter) and RT tiles of 16 rank rows (RT = 2: two
+// accumulators on the same x fragments, so x is loaded once for 32 ranks),
+// with v_mfma_f32_16x16x32_bf16.  Both operands load straight from memory: lane l
 // holds 8 consecutive d of token row (l % 16) for the first operand and of rank
 // row (l % 16) of A_a^T (rank-major, so 16 contiguous bytes) for the second;
 // rows past the item's tuple count or the adapter's effective rank are zero
@@ -261,8 +262,8 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void shrink_mfma(ShrinkArgs s) {
   shrink_mfma_jobs<STEPS, RT>(s, blockIdx.x, gridDim.x, red);
 }
 
-// Item pairs: one job takes work items 2q and 2q + 1 of one (rank tile, K
-// chunk, module) unit.  When both belong to the same adapter (consecutive
+// Item pairs: one job takes work items 2q and 2q + 1 of one (RT rank tiles,
+// K chunk, module) unit.  When both belong to the same adapter (consecutive
 // items of one segment) they share every A-row load and run two matrix-core
 // accumulators, one per item; otherwise the items run one after the other.
 // Each accumulator sees the same K steps in the same order as in
