@@ -451,8 +451,12 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
   if (tid < kROctA / 4)
     reinterpret_cast<uint4 *>(rl)[tid] = reinterpret_cast<const uint4 *>(rg)[tid];
   __syncthreads();
-  const int Q = rl[0], H = rl[1], fast = rl[2], C = rl[3], U = rl[4];
-  const int oidx = rl[5], ocoef = rl[6];
+  // (the header is the same for every lane: scalar registers make the
+  // step loop's trip count uniform and its branches scalar)
+  const int Q = __builtin_amdgcn_readfirstlane(rl[0]), H = __builtin_amdgcn_readfirstlane(rl[1]);
+  const int fast = __builtin_amdgcn_readfirstlane(rl[2]), C = __builtin_amdgcn_readfirstlane(rl[3]);
+  const int U = __builtin_amdgcn_readfirstlane(rl[4]);
+  const int oidx = __builtin_amdgcn_readfirstlane(rl[5]), ocoef = __builtin_amdgcn_readfirstlane(rl[6]);
   if (Q == 0) return;
   if (!fast) {
     tile_fallback<TY>(e, sel, rl + kRTok, cw);
@@ -531,7 +535,11 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
   // B three steps ahead of the matrix cores, the coefficients one step
   // ahead.  Scheduling barriers keep the loads in program order, so that
   // each step waits only for its own operands (the memory counter is in
-  // order) and the later steps' loads stay in flight.
+  // order) and the later steps' loads stay in flight.  The loop runs whole
+  // groups of six steps (the register rotation's period) and leaves by its
+  // latch alone, the last steps following it: an exit from inside the body
+  // makes the compiler merge that exit's counter state into the top of the
+  // loop, which then waits for every load in flight once a pass.
   uint4 a0[4], a1[4], a2[4], b0[4], b1[4];
   load(a0, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -547,18 +555,27 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
     load(a, st + 3);
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int st = 0; st < nsteps; st += 6) {
+  int st = 0;
+  for (; st + 6 <= nsteps; st += 6) {
     step(a0, b0, b1, st);
-    if (st + 1 >= nsteps) break;
     step(a1, b1, b0, st + 1);
-    if (st + 2 >= nsteps) break;
     step(a2, b0, b1, st + 2);
-    if (st + 3 >= nsteps) break;
     step(a0, b1, b0, st + 3);
-    if (st + 4 >= nsteps) break;
     step(a1, b0, b1, st + 4);
-    if (st + 5 >= nsteps) break;
     step(a2, b1, b0, st + 5);
+  }
+  if (st < nsteps) {
+    step(a0, b0, b1, st);
+    if (st + 1 < nsteps) {
+      step(a1, b1, b0, st + 1);
+      if (st + 2 < nsteps) {
+        step(a2, b0, b1, st + 2);
+        if (st + 3 < nsteps) {
+          step(a0, b1, b0, st + 3);
+          if (st + 4 < nsteps) step(a1, b0, b1, st + 4);
+        }
+      }
+    }
   }
   // y = accumulators, for tokens that hold at least one pair
 #pragma unroll
