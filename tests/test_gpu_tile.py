@@ -3,8 +3,8 @@ for bf16 batches of at least 256 tokens) against the fp64 oracle.
 
 The cases reach every path of the two kernels: tiles with many union entries
 (several hundred adapters), rank-64 adapters (eight octets each) and
-zero-rank adapters, ragged token tiles and column blocks, tokens without
-pairs, static groups, split-K partial z rows, bf16 y, several modules in one
+zero-rank adapters, ragged token tiles and column blocks, every K-loop
+step count from 1 to 14, tokens without pairs, static groups, split-K partial z rows, bf16 y, several modules in one
 launch, and tiles beyond the record's limits (more than 1024 tuples, more
 than 128 union entries, more than 1024 coefficient octets), whose jobs
 run the per-token fp32 loop; those are also compared bit for bit with the
@@ -316,3 +316,61 @@ def test_tile_expand_many_partial_planes(monkeypatch):
     _auto(monkeypatch, kchunk=64)
     ys, _, _ = run_fused(wl)
     _check(wl, ys, "tile 10 planes")
+
+
+def _step_count_case():
+    """Fourteen 64-token tiles whose unions hold 4 g + 4 - (g mod 3) rank
+    octets (g = 0..13): the K loop runs 1..14 steps of four octets, so whole
+    groups of six steps run 0, 1 and 2 times and every tail length 0..5
+    follows them, some with a last step of fewer than four octets.  Each
+    tile is one request of its own adapters (each token holds two of them,
+    or the one), ranks 8 o - 3 for o octets, rows at or beyond k NaN."""
+    T, r_max = 14 * 64, 64
+    octs, ads = [], []
+    for g in range(14):
+        H = 4 * (g + 1) - g % 3
+        own = [8] * (H // 8) + ([H % 8] if H % 8 else [])
+        base = len(octs)
+        octs += own
+        n = len(own)
+        for i in range(64):
+            ads.append([base + i % n] if n == 1 else [base + i % n, base + (i + 1) % n])
+    N = len(octs)
+    wl = W.random_case(169, T=T, N=N, d_in=64, d_out=264, r_max=r_max, max_pairs=2)
+    rng = np.random.default_rng(169)
+    als = [rng.random(len(a)).astype(np.float32).tolist() for a in ads]
+    wl.composites = W.csr_from_token_lists(ads, als, N)
+    m = wl.modules[0]
+    m.k = np.array([8 * o - 3 for o in octs], np.int32)
+    pad = np.arange(r_max)[None, :, None] >= m.k[:, None, None]
+    m.A_t = np.where(pad, BF16_NAN, m.A_t).astype(np.uint16)
+    m.B_t = np.where(pad, BF16_NAN, m.B_t).astype(np.uint16)
+    return wl
+
+
+@pytest.mark.parametrize("y16", [False, True])
+def test_tile_expand_every_step_count(y16, monkeypatch):
+    """The tile expand's K loop (whole groups of six steps, then the last
+    steps after the loop) at 1..14 steps a tile, fp32 and bf16 y (the two
+    instances of the kernel)."""
+    wl = _step_count_case()
+    c, m = wl.composites, wl.modules[0]
+    order, comps = tile_order(c)
+    steps = []
+    for t0 in range(0, len(order), 64):
+        union = sorted(set(a for t in order[t0:t0 + 64] for a in comps[t]))
+        steps.append((sum((int(m.k[a]) + 7) // 8 for a in union) + 3) // 4)
+    assert steps == list(range(1, 15)), steps
+    assert not any(h for _, h in tile_limits_hit(wl))
+    banner(f"tile expand, 1..14 K steps a tile (bf16 y {y16}): T={wl.n_tokens} N={wl.n_adapters}")
+    _auto(monkeypatch)
+    if not y16:
+        ys, _, _ = run_fused(wl)
+        _check(wl, ys, "tile steps 1..14")
+        return
+    wl.y_base = [W.bf16_bits_to_f32(W.f32_to_bf16_bits(y)) for y in wl.y_base]
+    ys, _, _ = run_fused(wl, y_dtype=torch.bfloat16)
+    _, d_ora = oracle_apply(wl, 0)
+    y_ora = wl.y_base[0].astype(np.float64) + d_ora
+    bound = np.abs(y_ora) * 2.0 ** -8 + TOL[W.BF16] * np.max(np.abs(d_ora))
+    assert np.all(np.abs(ys[0] - y_ora) <= bound)
