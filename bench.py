@@ -615,8 +615,9 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
+    fl = floors(dev, stream)
     head = measure(wl, dev, stream, args.steps, args.warmup, args.eager, args.replicas,
-                   latency=True)
+                   latency=True, copy_gbs=fl["copy_gbs"])
     nested = {}
     if not args.no_nested:
         for ci in NESTED_CONFIGS:
@@ -624,7 +625,8 @@ def main():
                 continue
             print(f"[bench] generating config {ci} (nested)", file=sys.stderr, flush=True)
             wn = W.make(ci)
-            r = measure(wn, dev, stream, None, None, args.eager, 0, latency=True)
+            r = measure(wn, dev, stream, None, None, args.eager, 0, latency=True,
+                        copy_gbs=fl["copy_gbs"])
             nested[wn.name] = r
             del wn
             torch.cuda.empty_cache()
@@ -646,6 +648,7 @@ def main():
         "config": {k: v for k, v in head.items() if not k.startswith("_") and k != "roofline"},
         "roofline": head["roofline"],
     }
+    out["config"]["floors"] = fl
     if nested:
         out["config"]["nested"] = {k: {kk: vv for kk, vv in v.items() if not kk.startswith("_")}
                                    for k, v in nested.items()}
@@ -669,7 +672,8 @@ def main():
 NESTED_CONFIGS = (2, 3, 4)
 
 
-def measure(wl, dev, stream, steps, warmup, eager, replicas, latency=False) -> dict:
+def measure(wl, dev, stream, steps, warmup, eager, replicas, latency=False,
+            copy_gbs=None) -> dict:
     """Times one workload on the GPU.  A step is tcl_remap_apply (mapping
     stage, shrink and expand of every module) on the next of R replicas of
     {pools, x, y}; R x working set >= 4 x the 256 MiB Infinity Cache, so the
@@ -863,7 +867,8 @@ def measure(wl, dev, stream, steps, warmup, eager, replicas, latency=False) -> d
         "apply_tokens_per_s": T / per["apply"],
         "apply_gbs": apply_bytes / per["apply"] / 1e9,
         "apply_frac": apply_bytes / per["apply"] / 1e9 / HBM_PEAK_GBS,
-        "apply_frac_of_streaming": apply_bytes / per["apply"] / 1e9 / STREAM_PEAK_GBS,
+        **({"apply_frac_of_copy": apply_bytes / per["apply"] / 1e9 / copy_gbs}
+           if copy_gbs else {}),
         **({"latency_us": lat} if lat is not None else {}),
         "kernel_us": {n: per[n] * 1e6 for n in ("plan", "shrink", "expand")},
         "kernel_alg_bytes": kb,
@@ -882,9 +887,45 @@ def measure(wl, dev, stream, steps, warmup, eager, replicas, latency=False) -> d
     return res
 
 
-# A plain streaming read measured on the box (reads of 512 MiB and more):
-# the practical HBM ceiling the apply is also reported against.
-STREAM_PEAK_GBS = 6400.0
+def floors(dev, stream) -> dict:
+    """Two floors measured in the same run, outside the timed steps: a
+    kernel launch that does nothing useful (a one-element fill, 256 launches
+    in one HIP graph, per launch), and the streaming bandwidth of a plain
+    1 GiB device copy (bytes read plus bytes written per second), the
+    practical HBM ceiling the apply is also reported against."""
+    import torch
+    one = torch.zeros(1, dtype=torch.float32, device=dev)
+    src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            one.fill_(1.0)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(256):
+                one.fill_(1.0)
+        g.replay()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+        launch_us = e0.elapsed_time(e1) * 1e3 / 256
+        for _ in range(2):
+            dst.copy_(src)
+        best = None
+        for _ in range(5):
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            e1.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+    copy_gbs = 2 * src.numel() * 4 / (best * 1e-3) / 1e9
+    del g, src, dst, one
+    torch.cuda.empty_cache()
+    return {"empty_kernel_us_in_graph": launch_us, "copy_gbs": copy_gbs,
+            "copy_bytes": 2 << 30}
 
 
 def kernel_names(wl, fused: bool) -> dict:
