@@ -135,12 +135,54 @@ constexpr int kShrinkSteps = 8;   // 32-element K steps each lane has in flight
 // and never read.  The 8 waves split the K steps of d_in, each keeping
 // kShrinkSteps steps of loads in flight, and their partial tiles are summed
 // through LDS in wave order.  z is written final.
+// The A fragments of the first STEPS K steps of job `job` (rank tile of one
+// 16-row tile, the calling lane's rank row and granule), as the job loop
+// below loads them: zero where the row is at or beyond the adapter's
+// effective rank or the step is past the wave's share or d_in.  A caller
+// that knows the job's item before its token lists (the decode step's
+// mapping stage) issues these loads early and hands them to the loop.
+template <int STEPS>
+__device__ inline void shrink_first_a(const ShrinkArgs &s, int job, int4 head,
+                                      uint4 (&pa)[STEPS]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int item = job / s.rg_total, rgg = job - item * s.rg_total;
+  (void)item;
+  int mi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMods; ++i)
+    if (i < s.n_mods && rgg >= s.m[i].first) mi = i;
+  const int dd = s.m[mi].d, r_max = s.m[mi].r_max;
+  const int nkc = s.m[mi].nkc, kchunk = s.m[mi].kchunk;
+  const int unit = rgg - s.m[mi].first;
+  const int rt = unit / nkc, kc = unit - rt * nkc;
+  const int j0 = rt * 16;
+  const int k = eff_rank(s.m[mi].k_dev, head.x, r_max);
+  const int jr = j0 + row;
+  const bf16_t *Aw = static_cast<const bf16_t *>(s.m[mi].W);
+  const bf16_t *Ar = j0 < k && jr < k ? Aw + (int64_t(head.x) * r_max + jr) * dd + kg * 8 : nullptr;
+  const int c0 = kc * (kchunk / 32), c1 = min((dd + 31) / 32, c0 + kchunk / 32);
+  const int per = (c1 - c0 + kShrinkWaves - 1) / kShrinkWaves;
+  const int s0 = c0 + w * per, s1 = min(c1, s0 + per);
+#pragma unroll
+  for (int u = 0; u < STEPS; ++u) {
+    const int e0 = (s0 + u) * 32 + kg * 8;
+    uint4 ab = make_uint4(0, 0, 0, 0);
+    if (s0 + u < s1 && e0 < dd && Ar) ab = *reinterpret_cast<const uint4 *>(Ar + (s0 + u) * 32);
+    pa[u] = ab;
+  }
+}
+
 // Jobs job0, job0 + stride, ... of one workgroup (8 waves); each lane keeps
-// STEPS K steps of loads in flight.
-template <int STEPS, int RT = 1>
-__device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int stride,
-                                        f32x4_t (*red)[64], const Item *litems = nullptr,
-                                        int n_litems = 0) {
+// STEPS K steps of loads in flight.  With has_pre, pre holds the A fragments
+// of job0's first STEPS K steps, loaded by shrink_first_a (one rank tile a
+// job only).  LOCAL: the work items are litems, in this workgroup's LDS
+// (its own mapping stage), read with LDS loads; else the plan's item table.
+template <int STEPS, int RT = 1, bool LOCAL = false>
+__device__ inline void shrink_mfma_jobs_pre(const ShrinkArgs &s, int job0, int stride,
+                                            f32x4_t (*red)[64], const Item *litems,
+                                            int n_litems, const uint4 (&pre)[STEPS],
+                                            bool has_pre) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   // The item record of the first job is fetched together with the item count
@@ -148,13 +190,13 @@ __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int strid
   // one dependent memory round trip.
   // litems: the work items in LDS (a mapping stage run by this workgroup),
   // else the plan's item table
-  const Item *items = litems ? litems : s.items;
-  const int cap = litems ? max(n_litems, 1) : s.items_cap;
+  const Item *items = LOCAL ? litems : s.items;
+  const int cap = LOCAL ? max(n_litems, 1) : s.items_cap;
   int job = job0;
   const int item0 = min(job / s.rg_total, cap - 1);
   int4 head = items[item0].head;
   int tokl = items[item0].tok[row];
-  const int n_items = litems ? n_litems : s.status[ST_ITEMS];
+  const int n_items = LOCAL ? n_litems : s.status[ST_ITEMS];
   const int total = n_items * s.rg_total;
 
   for (; job < total; job += stride) {
@@ -203,26 +245,46 @@ __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int strid
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int st = s0; st < s1; st += STEPS) {
       bf16x8_t xv[STEPS], av[STEPS], av1[RT == 2 ? STEPS : 1];
+      auto mult = [&]() {
 #pragma unroll
-      for (int u = 0; u < STEPS; ++u) {
-        const int e0 = (st + u) * 32 + kg * 8;  // first element of this lane's granule
-        const bool in = st + u < s1 && e0 < dd;
-        uint4 xb = make_uint4(0, 0, 0, 0), ab = make_uint4(0, 0, 0, 0);
-        if (in && Xr) xb = *reinterpret_cast<const uint4 *>(Xr + (st + u) * 32);
-        if (in && Ar) ab = *reinterpret_cast<const uint4 *>(Ar + (st + u) * 32);
-        xv[u] = __builtin_bit_cast(bf16x8_t, xb);
-        av[u] = __builtin_bit_cast(bf16x8_t, ab);
-        if constexpr (RT == 2) {
-          uint4 ab1 = make_uint4(0, 0, 0, 0);
-          if (in && Ar1) ab1 = *reinterpret_cast<const uint4 *>(Ar1 + (st + u) * 32);
-          av1[u] = __builtin_bit_cast(bf16x8_t, ab1);
+        for (int u = 0; u < STEPS; ++u) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[u], av[u], acc, 0, 0, 0);
+          if constexpr (RT == 2)
+            if (hi) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[u], av1[u], acc1, 0, 0, 0);
         }
-      }
+      };
+      if (RT == 1 && has_pre && job == job0 && st == s0) {
+        // the A fragments are in flight already: issue the x loads, then
+        // multiply.  This path has its own multiply, so that the compiler's
+        // wait analysis does not merge it with the other path's loads (it
+        // would then wait for every load in flight before the first x load).
 #pragma unroll
-      for (int u = 0; u < STEPS; ++u) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[u], av[u], acc, 0, 0, 0);
-        if constexpr (RT == 2)
-          if (hi) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[u], av1[u], acc1, 0, 0, 0);
+        for (int u = 0; u < STEPS; ++u) {
+          const int e0 = (st + u) * 32 + kg * 8;
+          uint4 xb = make_uint4(0, 0, 0, 0);
+          if (st + u < s1 && e0 < dd && Xr) xb = *reinterpret_cast<const uint4 *>(Xr + (st + u) * 32);
+          xv[u] = __builtin_bit_cast(bf16x8_t, xb);
+        }
+#pragma unroll
+        for (int u = 0; u < STEPS; ++u) av[u] = __builtin_bit_cast(bf16x8_t, pre[u]);
+        mult();
+      } else {
+#pragma unroll
+        for (int u = 0; u < STEPS; ++u) {
+          const int e0 = (st + u) * 32 + kg * 8;  // first element of this lane's granule
+          const bool in = st + u < s1 && e0 < dd;
+          uint4 xb = make_uint4(0, 0, 0, 0), ab = make_uint4(0, 0, 0, 0);
+          if (in && Xr) xb = *reinterpret_cast<const uint4 *>(Xr + (st + u) * 32);
+          if (in && Ar) ab = *reinterpret_cast<const uint4 *>(Ar + (st + u) * 32);
+          xv[u] = __builtin_bit_cast(bf16x8_t, xb);
+          av[u] = __builtin_bit_cast(bf16x8_t, ab);
+          if constexpr (RT == 2) {
+            uint4 ab1 = make_uint4(0, 0, 0, 0);
+            if (in && Ar1) ab1 = *reinterpret_cast<const uint4 *>(Ar1 + (st + u) * 32);
+            av1[u] = __builtin_bit_cast(bf16x8_t, ab1);
+          }
+        }
+        mult();
       }
     }
     red[w][lane] = acc;
@@ -254,6 +316,13 @@ __device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int strid
     }
     __syncthreads();
   }
+}
+
+template <int STEPS, int RT = 1>
+__device__ inline void shrink_mfma_jobs(const ShrinkArgs &s, int job0, int stride,
+                                        f32x4_t (*red)[64]) {
+  const uint4 none[STEPS] = {};
+  shrink_mfma_jobs_pre<STEPS, RT, false>(s, job0, stride, red, nullptr, 0, none, false);
 }
 
 template <int STEPS, int RT>
@@ -428,7 +497,9 @@ constexpr int kFusedLdsInts = 12288;  // direct-mode mapping scratch (48 KiB)
 constexpr int kFusedItems = 192;      // work items held in LDS (15 KiB)
 
 template <int STEPS>
-__global__ __launch_bounds__(64 * kShrinkWaves) void plan_shrink(PlanArgs A, ShrinkArgs s) {
+__global__ __launch_bounds__(64 * kShrinkWaves)
+__attribute__((amdgpu_waves_per_eu(STEPS <= 8 ? 4 : 1))) void plan_shrink(PlanArgs A,
+                                                                          ShrinkArgs s) {
   __shared__ __align__(16) int lds[kFusedLdsInts];
   __shared__ int tmp[6 * kSlotInts];
   __shared__ Item li[kFusedItems];
@@ -444,6 +515,12 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void plan_shrink(PlanArgs A, Shr
                                            small && !lead);
   if (rc != TCL_OK || lead) return;
   const int job0 = blockIdx.x - 1, stride = gridDim.x - 1;
+  // the first job's A fragments depend only on its item's head: issue them
+  // now, so that their latency overlaps the token lists below
+  // (8 K steps: 32 more registers, within four waves a SIMD)
+  const bool pre = STEPS <= 8 && job0 < n_items * s.rg_total;
+  uint4 pa[STEPS] = {};
+  if (pre) shrink_first_a<STEPS>(s, job0, li[job0 / s.rg_total].head, pa);
   if (small) {
     const int total = n_items * s.rg_total;
     int last = -1, calls = 0;
@@ -456,7 +533,7 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void plan_shrink(PlanArgs A, Shr
     }
   }
   __syncthreads();  // the items in LDS are complete
-  shrink_mfma_jobs<STEPS>(s, job0, stride, red, li, n_items);
+  shrink_mfma_jobs_pre<STEPS, 1, true>(s, job0, stride, red, li, n_items, pa, pre);
 }
 
 // ---------------------------------------------------------------------------
