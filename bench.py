@@ -615,9 +615,11 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
-    fl = floors(dev, stream)
+    # (not in counter runs: their copy calibration takes the run's largest
+    # device copy, which must be the 256 MiB one below)
+    fl = None if args.calibrate_copy else floors(dev, stream)
     head = measure(wl, dev, stream, args.steps, args.warmup, args.eager, args.replicas,
-                   latency=True, copy_gbs=fl["copy_gbs"])
+                   latency=True, copy_gbs=fl["copy_gbs"] if fl else None)
     nested = {}
     if not args.no_nested:
         for ci in NESTED_CONFIGS:
@@ -626,7 +628,7 @@ def main():
             print(f"[bench] generating config {ci} (nested)", file=sys.stderr, flush=True)
             wn = W.make(ci)
             r = measure(wn, dev, stream, None, None, args.eager, 0, latency=True,
-                        copy_gbs=fl["copy_gbs"])
+                        copy_gbs=fl["copy_gbs"] if fl else None)
             nested[wn.name] = r
             del wn
             torch.cuda.empty_cache()
@@ -648,7 +650,8 @@ def main():
         "config": {k: v for k, v in head.items() if not k.startswith("_") and k != "roofline"},
         "roofline": head["roofline"],
     }
-    out["config"]["floors"] = fl
+    if fl:
+        out["config"]["floors"] = fl
     if nested:
         out["config"]["nested"] = {k: {kk: vv for kk, vv in v.items() if not kk.startswith("_")}
                                    for k, v in nested.items()}
