@@ -764,10 +764,38 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
 #pragma unroll
     for (int jb = 0; jb < R; jb += RB) {
       RowN<TW, CPL> bv[SB][RB];
+      // z of the batch (entries at or beyond the effective rank are never
+      // used; a split shrink leaves nkc partial rows per tuple, added in
+      // chunk order).  Batches of four or more slots take it through vector
+      // loads issued before the B rows: lane l holds rank jb + l % RB of slot
+      // l / RB (SB * RB = BR <= 32 lanes), so the batch waits for one memory
+      // round trip.  Through the scalar loads below, each slot's z rows were
+      // waited for before the next slot's B rows were issued: distinct
+      // decode, four slots a batch, 15.0 -> 14.3 us a step.  Batches of two
+      // slots measured faster with the scalar loads (skewed decode, 38.3 vs
+      // 38.5-38.9 us), and keep them.
+      constexpr bool kVecZ = SB >= 4;
       float zv[SB][RB];
-      // all loads of the batch first: B rows of the retained ranks and z
-      // (entries at or beyond the effective rank are never used).  A split
-      // shrink leaves nkc partial rows per tuple, added here in chunk order.
+      float zc[kVecZ ? (SPLIT ? 4 : 1) : 1];
+      bool zin = false;
+      const float *zrow = Z;
+      if constexpr (kVecZ) {
+        const int zb = lane / RB, zj = lane % RB;
+        int zp = 0, zk = 0;
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+          if (zb == b) {
+            zp = pp[b];
+            zk = kk[b];
+          }
+        zin = zb < SB && jb + zj < zk;
+        zrow = Z + int64_t(zp) * (SPLIT ? zstride : zld) + jb + zj;
+#pragma unroll
+        for (int i = 0; i < (SPLIT ? 4 : 1); ++i) {
+          zc[i] = 0.f;
+          if (zin && i < nkc) zc[i] = zrow[i * zld];
+        }
+      }
 #pragma unroll
       for (int b = 0; b < SB; ++b) {
 #pragma unroll
@@ -776,16 +804,18 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
           if (j < kk[b] && active) bv[b][jj].load(B + (int64_t(aa[b]) * r_max + j) * d + n0);
           else bv[b][jj].zero();
         }
-        // y right after the first batch's B rows: its latency then overlaps
-        // theirs instead of the slot records' (the memory counter is in
-        // order, so a load issued before the slot records would be waited
-        // for together with them)
+        // y right after the first batch's first B rows: its latency then
+        // overlaps theirs instead of the slot records' (the memory counter
+        // is in order, so a load issued before the slot records would be
+        // waited for together with them)
         if (sb == 0 && jb == 0 && b == 0 && active) yv.load(Yp);
-        if constexpr (!SPLIT) {
+        if constexpr (kVecZ) {
+          // z came in above
+        } else if constexpr (!SPLIT) {
           // one z row per tuple, read as whole vectors
-          const float *zrow = Z + int64_t(pp[b]) * zld + jb;
+          const float *zr1 = Z + int64_t(pp[b]) * zld + jb;
           if ((zld & 3) == 0) {
-            const float4 *zr = reinterpret_cast<const float4 *>(zrow);
+            const float4 *zr = reinterpret_cast<const float4 *>(zr1);
 #pragma unroll
             for (int jj = 0; jj < RB; jj += 4) {
               float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -797,7 +827,7 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
             }
           } else {
 #pragma unroll
-            for (int jj = 0; jj < RB; ++jj) zv[b][jj] = jb + jj < kk[b] ? zrow[jj] : 0.f;
+            for (int jj = 0; jj < RB; ++jj) zv[b][jj] = jb + jj < kk[b] ? zr1[jj] : 0.f;
           }
         } else {
           // nkc partial rows per tuple (zld is a multiple of 4 here)
@@ -818,11 +848,28 @@ __device__ inline void expand_job(const ExpandArgs &e, int job) {
           }
         }
       }
+      float zl = 0.f;
+      if constexpr (kVecZ) {
+        if constexpr (SPLIT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < nkc) zl += zc[i];
+          for (int c = 4; c < nkc; ++c)  // beyond four chunks, one at a time
+            if (zin) zl += zrow[c * zld];
+        } else {
+          zl = zc[0];
+        }
+      }
 #pragma unroll
       for (int b = 0; b < SB; ++b)
 #pragma unroll
         for (int jj = 0; jj < RB; ++jj)
-          if (jb + jj < kk[b]) bv[b][jj].fma_into(al[b] * zv[b][jj], acc);
+          if (jb + jj < kk[b]) {
+            const float z =
+                kVecZ ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zl), b * RB + jj))
+                      : zv[b][jj];
+            bv[b][jj].fma_into(al[b] * z, acc);
+          }
     }
   }
   if (active) yv.add_store(Yp, acc);
