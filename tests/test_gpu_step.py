@@ -87,11 +87,15 @@ def test_step_paths_agree(name, monkeypatch):
                               np.asarray(cb[k]).view(np.uint32) if k == "tup_alpha" else cb[k]), k
 
 
-def test_step_split_k(monkeypatch):
-    """Partial z rows of the shrink (d_in in 512-element chunks)."""
-    wl = CASES["config3"]()
-    banner("remap_apply with split-K partials")
-    monkeypatch.setenv("TCL_KCHUNK", "512")
+@pytest.mark.parametrize("name,kchunk", [("config3", 512), ("config2", 512), ("config2", 1536)])
+def test_step_split_k(name, kchunk, monkeypatch):
+    """Partial z rows of the shrink: config 3's two-slot expand batches read
+    them through scalar loads, config 2's four-slot batches through vector
+    loads (8 chunks: four issued before the B rows, four after; 3 chunks:
+    a ragged group)."""
+    wl = CASES[name]()
+    banner(f"remap_apply with split-K partials: {name}, {kchunk}-element chunks")
+    monkeypatch.setenv("TCL_KCHUNK", str(kchunk))
     ys, _ = _step(wl)
     _check(wl, ys)
 
