@@ -144,11 +144,12 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.o_msst = take(multi ? size_t(N) * 4 : 4);
   l.o_msib = take(multi ? size_t(N) * 4 : 4);
   l.tiles = T >= kMfmaMinTokens ? (T + kXTok - 1) / kXTok : 0;
-  l.o_ttok = take(l.tiles ? size_t(T) * 4 : 4);
-  // per-workgroup counts of the tile order's two launches
-  l.o_ocnt = take(l.tiles ? (size_t(T + 255) / 256 + size_t(cap + 255) / 256) * 4 : 4);
-  // and per thread of them the item it places (or -1), from the first to the second
-  l.o_oitem = take(l.tiles ? (size_t(T + 255) / 256 + size_t(cap + 255) / 256) * 256 * 4 : 4);
+  // tile order: per workgroup of its flagging launch the count of flagged
+  // items, and a slice of kOrdThreads entries listing them
+  const size_t ord_blocks = (size_t(T) + kOrdThreads - 1) / kOrdThreads +
+                            (size_t(cap) + kOrdThreads - 1) / kOrdThreads;
+  l.o_ocnt = take(l.tiles ? ord_blocks * 4 : 4);
+  l.o_oitem = take(l.tiles ? ord_blocks * kOrdThreads * 4 : 4);
   // device copy of a host-resident composite table: group_tok_ptr,
   // group_pair_ptr (G + 1 each), pair_adapter, pair_alpha (NP each)
   l.o_tab = take((2 * size_t(G) + 2 + 2 * size_t(NP)) * 4);
@@ -157,8 +158,8 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   return TCL_OK;
 }
 
-// Token order of the prefill expand's 64-token tiles (tile_tok, ST_BUSY of
-// them): the tokens that hold at least one pair, first those whose rarest
+// Token order of the prefill expand's 64-token tiles: the tokens that hold
+// at least one pair, first those whose rarest
 // adapter (the last of their slots, adapters ascending) is common -- its
 // segment holds at least T / kXTok tuples, about one per tile -- in token
 // order, then the others grouped by that adapter (ascending), in token order
@@ -168,13 +169,15 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
 // tokens in order keeps the locality a batch of requests already has.  The
 // rare ones, in (adapter, token) order, are the tuples of the sorted plan
 // that are their token's last slot and belong to a rare segment.
-// Two launches over all tokens (the common ones) and all tuples (the rare
-// ones), one item per thread: the first flags the items, keeps each
-// thread's flagged item (or -1) and counts them per workgroup, the second
-// adds the counts of the earlier workgroups and writes each flagged item at
-// its place.  Workgroups [0, bt) take tokens, [bt, bt +
-// bp) tuples, so the common tokens come first.
-constexpr int kOrdThreads = 256;
+// One launch over all tokens (the common ones) and all tuples (the rare
+// ones), one item per thread: it flags the items and writes each
+// workgroup's flagged items, in order, at the start of its 256-entry slice
+// of ord_item, and their count in ord_cnt.  Workgroups [0, bt) take tokens,
+// [bt, bt + bp) tuples, so the common tokens come first.  Position i of the
+// tile order is then entry i - (items of the earlier workgroups) of the
+// workgroup whose items cover i: tile_prep finds the 64 entries of its tile
+// from the counts (the scan of the counts, once a separate launch that
+// wrote the whole order, now runs inside each tile's own workgroup).
 
 __device__ inline bool ord_flag(const PlanDev &d, int wg, int bt, int T, int P, int thr, int *item) {
   const int i = (wg < bt ? wg : wg - bt) * kOrdThreads + threadIdx.x;
@@ -198,61 +201,20 @@ __global__ __launch_bounds__(kOrdThreads) void tile_order_count(PlanDev d, int32
   __shared__ int tmp[kOrdThreads / 64];
   const bool ok = d.status[ST_CODE] == TCL_OK;
   const int P = ok ? d.status[ST_TUPLES] : 0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int item = 0;
   const bool f = ok && ord_flag(d, blockIdx.x, bt, T, P, max(T / kXTok, 1), &item);
-  d.ord_item[blockIdx.x * kOrdThreads + threadIdx.x] = f ? item : -1;
-  const uint64_t m = __ballot(f);
-  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = __popcll(m);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < kOrdThreads / 64; ++j) c += tmp[j];
-    d.ord_cnt[blockIdx.x] = c;
-  }
-}
-
-__global__ __launch_bounds__(kOrdThreads) void tile_order_place(PlanDev d, int32_t T, int32_t bt) {
-  __shared__ int tmp[kOrdThreads / 64];
-  __shared__ int wsum[kOrdThreads / 64];
-  const bool ok = d.status[ST_CODE] == TCL_OK;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // this thread's item, as the first launch flagged it (-1: none)
-  const int item = d.ord_item[blockIdx.x * kOrdThreads + threadIdx.x];
-  // items of the earlier workgroups, and of all of them
-  int before = 0, all = 0;
-  for (int j = threadIdx.x; j < int(gridDim.x); j += kOrdThreads) {
-    const int c = d.ord_cnt[j];
-    if (j < int(blockIdx.x)) before += c;
-    all += c;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    before += __shfl_xor(before, o, 64);
-    all += __shfl_xor(all, o, 64);
-  }
-  if (lane == 0) {
-    tmp[w] = before;
-    wsum[w] = all;
-  }
-  __syncthreads();
-  int base = 0, total = 0;
-#pragma unroll
-  for (int j = 0; j < kOrdThreads / 64; ++j) {
-    base += tmp[j];
-    total += wsum[j];
-  }
-  __syncthreads();
-  const bool f = item >= 0;
   const uint64_t m = __ballot(f);
   if (lane == 0) tmp[w] = __popcll(m);
   __syncthreads();
-  int wb = 0;
+  int wb = 0, c = 0;
 #pragma unroll
-  for (int j = 0; j < kOrdThreads / 64; ++j)
-    if (j < w) wb += tmp[j];
-  if (f) d.tile_tok[base + wb + __popcll(m & ((uint64_t(1) << lane) - 1))] = item;
-  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) d.status[ST_BUSY] = ok ? total : 0;
+  for (int j = 0; j < kOrdThreads / 64; ++j) {
+    wb += j < w ? tmp[j] : 0;
+    c += tmp[j];
+  }
+  if (f) d.ord_item[blockIdx.x * kOrdThreads + wb + __popcll(m & ((uint64_t(1) << lane) - 1))] = item;
+  if (threadIdx.x == 0) d.ord_cnt[blockIdx.x] = c;
 }
 
 // ---------------------------------------------------------------------------
@@ -727,7 +689,6 @@ static void bind(tcl_plan *p) {
   d.m_blk = reinterpret_cast<int32_t *>(b + L.o_mblk);
   d.m_sst = reinterpret_cast<int32_t *>(b + L.o_msst);
   d.m_sib = reinterpret_cast<int32_t *>(b + L.o_msib);
-  d.tile_tok = reinterpret_cast<int32_t *>(b + L.o_ttok);
   d.ord_cnt = reinterpret_cast<int32_t *>(b + L.o_ocnt);
   d.ord_item = reinterpret_cast<int32_t *>(b + L.o_oitem);
 }
@@ -812,7 +773,6 @@ int plan_launch_tile_order(const tcl_plan *p, hipStream_t s) {
   const int bt = (p->L.T + kOrdThreads - 1) / kOrdThreads;
   const int bp = (p->L.cap + kOrdThreads - 1) / kOrdThreads;
   hipLaunchKernelGGL(tile_order_count, dim3(bt + bp), dim3(kOrdThreads), 0, s, p->d, p->L.T, bt);
-  hipLaunchKernelGGL(tile_order_place, dim3(bt + bp), dim3(kOrdThreads), 0, s, p->d, p->L.T, bt);
   TCL_HIP(hipGetLastError());
   return TCL_OK;
 }

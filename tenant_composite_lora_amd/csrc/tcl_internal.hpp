@@ -48,13 +48,16 @@ constexpr int kPlanLdsInts = 32768;
 // count for which a plan orders its tokens into such tiles.
 constexpr int kXTok = 64;
 constexpr int kMfmaMinTokens = 256;
+// Items (tokens, then tuples) per workgroup of the launch that flags the
+// tile order; each workgroup lists its flagged items in a slice this long.
+constexpr int kOrdThreads = 256;
 
 // One apply launch covers up to kMaxMods modules that share the plan (e.g.
 // the seven projections of a transformer layer).
 constexpr int kMaxMods = 8;
 
 // device status words
-enum { ST_CODE = 0, ST_TUPLES = 1, ST_SEGMENTS = 2, ST_ITEMS = 3, ST_BUSY = 4, ST_WORDS = 64 };
+enum { ST_CODE = 0, ST_TUPLES = 1, ST_SEGMENTS = 2, ST_ITEMS = 3, ST_WORDS = 64 };
 
 // error bits raised by the mapping kernel
 enum { EB_INVAL = 1, EB_UNSUP = 2, EB_NOSPC = 4 };
@@ -69,7 +72,7 @@ struct PlanLayout {
   int32_t tiles;    // token tiles of kXTok of the prefill expand (0: none)
   // byte offsets inside the device buffer
   size_t o_status, o_tok, o_ad, o_slot, o_alpha, o_toktuple, o_tokrec, o_tokn, o_tokptr,
-      o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_sseg, o_ttok, o_ocnt,
+      o_segad, o_segbeg, o_items, o_sslot, o_sgroup, o_spos, o_sgbase, o_shist, o_sseg, o_ocnt,
       o_oitem, o_mhist, o_mblk, o_msst, o_msib, o_tab, total;
 };
 
@@ -111,9 +114,10 @@ struct PlanDev {
   // base, -} [blocks][4],
   // per-adapter segment start and first work item [N]
   int32_t *m_hist, *m_blk, *m_sst, *m_sib;
-  int32_t *tile_tok;  // [T]: token order of the prefill expand's tiles (ST_BUSY entries)
-  int32_t *ord_cnt;   // per-workgroup counts of the tile order launches
-  int32_t *ord_item;  // per thread of those launches: the item it places, or -1
+  // tile order: per workgroup of the flagging launch, its flagged items
+  // (first ord_cnt[w] entries of slice w of ord_item, kOrdThreads each)
+  int32_t *ord_cnt;
+  int32_t *ord_item;
 };
 
 }  // namespace tcl

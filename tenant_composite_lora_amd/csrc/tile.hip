@@ -150,7 +150,10 @@ struct TileArgs {
   const int32_t *status;
   const int32_t *tok_n;
   const int4 *tok_rec;     // [T][kSlotPad]
-  const int32_t *tile_tok;  // token order of the tiles (status[ST_BUSY] entries)
+  // the tile order: per workgroup of the plan's flagging launch the count
+  // of its flagged items, listed at the start of its kOrdThreads-entry slice
+  const int32_t *ord_cnt, *ord_item;
+  int32_t ord_blocks;
   int32_t *rec;            // [n_mods][tiles][kRWords]
   int32_t T, N, tiles, n_mods, jobs, jobs_per_xcd;
   // packed pools (tcl_module_pack): per adapter its first 16-byte unit, and
@@ -207,11 +210,36 @@ __global__ __launch_bounds__(256) void tile_prep(TileArgs e) {
   const int32_t *bk_off = e.bk_off[sel];
   int32_t *rec = e.rec + int64_t(blockIdx.x) * kRWords;
   const bool ok = e.status[ST_CODE] == TCL_OK;
-  const int busy = ok ? e.status[ST_BUSY] : 0;
+  // row tid of the tile: position tile * kXTok + tid of the plan's tile
+  // order.  The flagging launch's counts are scanned kOrdThreads at a time
+  // until they pass the tile's last position; each row finds the workgroup
+  // that lists its position with a binary search over the scanned counts
+  // (s_p is free until the tuples are gathered below).
+  int t = -1;
+  {
+    const int want0 = tile * kXTok, want = want0 + tid;
+    int base = 0;
+    for (int c0 = 0; ok && c0 < e.ord_blocks; c0 += kOrdThreads) {
+      const int j = c0 + tid;
+      s_p[tid] = j < e.ord_blocks ? e.ord_cnt[j] : 0;
+      __syncthreads();
+      const int total = lds_scan(s_p, kOrdThreads, tmp);  // exclusive, in place
+      if (tid < kXTok && want >= base && want < base + total) {
+        const int r = want - base;
+        int lo = 0, hi = kOrdThreads - 1;  // the last workgroup listed at or before r
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_p[mid] <= r) lo = mid;
+          else hi = mid - 1;
+        }
+        t = e.ord_item[int64_t(c0 + lo) * kOrdThreads + (r - s_p[lo])];
+      }
+      base += total;
+      __syncthreads();  // s_p is rewritten by the next pass
+      if (base >= want0 + kXTok) break;
+    }
+  }
   if (tid < kXTok) {
-    // row tid of the tile: the plan's tile order
-    const int i = tile * kXTok + tid;
-    const int t = i < busy ? e.tile_tok[i] : -1;
     int n = t >= 0 ? e.tok_n[t] : 0;
     n = n < 0 ? 0 : (n > kSlotPad ? kSlotPad : n);
     s_n[tid] = n;
@@ -597,6 +625,7 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+static_assert(kRMaxQ >= kOrdThreads, "tile_prep scans the tile order's counts in s_p");
 static_assert(32 * kRMaxWords == kTileMaxAdapters, "record bitmap covers the adapter limit");
 
 static int n_tiles(const tcl_plan *p) { return (p->L.T + kXTok - 1) / kXTok; }
@@ -641,7 +670,9 @@ int launch_expand_tile(const tcl_plan *p, const tcl_module *mods, int n, float *
   if (jobs > (int64_t(1) << 30)) return fail(TCL_EUNSUPPORTED, "expand grid too large");
   e.jobs = int32_t(jobs);
   e.jobs_per_xcd = int32_t((jobs + 7) / 8);
-  e.tile_tok = p->d.tile_tok;
+  e.ord_cnt = p->d.ord_cnt;
+  e.ord_item = p->d.ord_item;
+  e.ord_blocks = (p->L.T + kOrdThreads - 1) / kOrdThreads + (p->L.cap + kOrdThreads - 1) / kOrdThreads;
   logf("expand(tile): modules=%d tiles=%d jobs=%lld", n, e.tiles, (long long)jobs);
   hipLaunchKernelGGL(tile_prep, dim3(n * e.tiles), dim3(256), 0, s, e);
   if (yd == TCL_BF16)
