@@ -97,7 +97,7 @@ def kernel_bytes(wl) -> dict:
 # HIP sources each kernel is built from: a stored counter summary is only
 # valid while these are unchanged
 KERNEL_SOURCES = {k: ("plan.hip", "plan_core.hpp", "tcl_internal.hpp")
-                  for k in ("plan_kernel", "tile_order_count", "tile_order_place",
+                  for k in ("plan_kernel", "tile_order_count",
                             "plan_m_local", "plan_m_scan", "plan_m_scatter")}
 KERNEL_SOURCES.update({k: ("tile.hip", "kern_common.hpp", "tcl_internal.hpp")
                        for k in ("tile_prep", "expand_tile")})
@@ -113,7 +113,7 @@ APPLY_SOURCES = ("apply.hip", "kern_common.hpp", "plan_core.hpp", "tcl_internal.
 # library kernels the counter summary keeps apart (whole identifiers of the
 # demangled names)
 PMC_KERNELS = ("plan_shrink", "shrink_mfma", "shrink_mfma_pair", "shrink_valu", "expand_kernel",
-               "tile_prep", "expand_tile", "tile_order_count", "tile_order_place",
+               "tile_prep", "expand_tile", "tile_order_count",
                "pack_offsets_kernel", "pack_b_kernel", "plan_kernel", "plan_m_local",
                "plan_m_scan", "plan_m_scatter", "gate_count_kernel", "gate_scan_kernel",
                "gate_topk_kernel")
