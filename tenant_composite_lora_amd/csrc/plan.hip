@@ -145,11 +145,10 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
   l.o_msib = take(multi ? size_t(N) * 4 : 4);
   l.tiles = T >= kMfmaMinTokens ? (T + kXTok - 1) / kXTok : 0;
   // tile order: per workgroup of its flagging launch the count of flagged
-  // items, and a slice of kOrdThreads entries listing them
-  const size_t ord_blocks = (size_t(T) + kOrdThreads - 1) / kOrdThreads +
-                            (size_t(cap) + kOrdThreads - 1) / kOrdThreads;
-  l.o_ocnt = take(l.tiles ? ord_blocks * 4 : 4);
-  l.o_oitem = take(l.tiles ? ord_blocks * kOrdThreads * 4 : 4);
+  // tokens, and a slice of kOrdThreads entries listing them
+  const size_t ob = size_t(ord_blocks(cap));
+  l.o_ocnt = take(l.tiles ? ob * 4 : 4);
+  l.o_oitem = take(l.tiles ? ob * kOrdThreads * 4 : 4);
   // device copy of a host-resident composite table: group_tok_ptr,
   // group_pair_ptr (G + 1 each), pair_adapter, pair_alpha (NP each)
   l.o_tab = take((2 * size_t(G) + 2 + 2 * size_t(NP)) * 4);
@@ -159,51 +158,39 @@ int plan_layout(int32_t T, int32_t G, int32_t NP, int32_t N, int32_t cap, PlanLa
 }
 
 // Token order of the prefill expand's 64-token tiles: the tokens that hold
-// at least one pair, first those whose rarest
-// adapter (the last of their slots, adapters ascending) is common -- its
-// segment holds at least T / kXTok tuples, about one per tile -- in token
-// order, then the others grouped by that adapter (ascending), in token order
-// within an adapter.  Tokens that share a rare adapter then share a tile,
-// which shrinks the tiles' unions (the adapters whose B rows a tile reads);
-// a common adapter is in most tiles whatever the order, and keeping those
-// tokens in order keeps the locality a batch of requests already has.  The
-// rare ones, in (adapter, token) order, are the tuples of the sorted plan
-// that are their token's last slot and belong to a rare segment.
-// One launch over all tokens (the common ones) and all tuples (the rare
-// ones), one item per thread: it flags the items and writes each
-// workgroup's flagged items, in order, at the start of its 256-entry slice
-// of ord_item, and their count in ord_cnt.  Workgroups [0, bt) take tokens,
-// [bt, bt + bp) tuples, so the common tokens come first.  Position i of the
-// tile order is then entry i - (items of the earlier workgroups) of the
-// workgroup whose items cover i: tile_prep finds the 64 entries of its tile
-// from the counts (the scan of the counts, once a separate launch that
-// wrote the whole order, now runs inside each tile's own workgroup).
+// at least one pair, grouped by their rarest adapter (the last of their
+// slots, adapters ascending), adapters ascending, in token order within an
+// adapter.  Tokens that share their rarest adapter then share a tile, which
+// shrinks the tiles' unions (the adapters whose B rows a tile reads): their
+// other adapters are the more common ones, in many tiles whatever the order.
+// In (adapter, token) order these tokens are the tuples of the sorted plan
+// that are their token's last slot.  (Keeping the tokens whose rarest
+// adapter is common in token order, as before, left the retained-rank
+// batch's expand 20 us slower; the sparse prefill, whose requests already
+// share adapters in token order, is 0.5-0.9 us slower grouped.)
+// One launch over the tuples, one a thread: it flags each token's last slot
+// and writes each workgroup's flagged tokens, in order, at the start of its
+// kOrdThreads-entry slice of ord_item, and their count in ord_cnt.  Position
+// i of the tile order is then entry i - (tokens of the earlier workgroups)
+// of the workgroup whose tokens cover i: tile_prep finds the 64 entries of
+// its tile from the counts.
 
-__device__ inline bool ord_flag(const PlanDev &d, int wg, int bt, int T, int P, int thr, int *item) {
-  const int i = (wg < bt ? wg : wg - bt) * kOrdThreads + threadIdx.x;
-  if (wg < bt) {  // token i, common
-    if (i >= T) return false;
-    const int n = min(d.tok_n[i], kSlotPad);
-    *item = i;
-    if (n <= 0) return false;
-    const int u = d.tok_rec[int64_t(i) * kSlotPad + n - 1].w;
-    return d.seg_begin[u + 1] - d.seg_begin[u] >= thr;
-  }
-  if (i >= P) return false;  // tuple i: the last slot of its token, rare
+// tuple i (in sorted order) when it is its token's last slot: the token
+__device__ inline bool ord_flag(const PlanDev &d, int P, int *item) {
+  const int i = blockIdx.x * kOrdThreads + threadIdx.x;
+  if (i >= P) return false;
   const int t = d.tup_token[i], sl = d.tup_slot[i];
   *item = t;
-  if (sl < 0 || sl >= kSlotPad || sl != d.tok_n[t] - 1) return false;
-  const int u = d.tok_rec[int64_t(t) * kSlotPad + sl].w;
-  return d.seg_begin[u + 1] - d.seg_begin[u] < thr;
+  return sl >= 0 && sl < kSlotPad && sl == d.tok_n[t] - 1;
 }
 
-__global__ __launch_bounds__(kOrdThreads) void tile_order_count(PlanDev d, int32_t T, int32_t bt) {
+__global__ __launch_bounds__(kOrdThreads) void tile_order_count(PlanDev d) {
   __shared__ int tmp[kOrdThreads / 64];
   const bool ok = d.status[ST_CODE] == TCL_OK;
   const int P = ok ? d.status[ST_TUPLES] : 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int item = 0;
-  const bool f = ok && ord_flag(d, blockIdx.x, bt, T, P, max(T / kXTok, 1), &item);
+  const bool f = ok && ord_flag(d, P, &item);
   const uint64_t m = __ballot(f);
   if (lane == 0) tmp[w] = __popcll(m);
   __syncthreads();
@@ -770,9 +757,7 @@ int plan_launch(tcl_plan *p, const tcl_composites *c, hipStream_t s) { return la
 
 int plan_launch_tile_order(const tcl_plan *p, hipStream_t s) {
   if (p->L.tiles == 0) return TCL_OK;
-  const int bt = (p->L.T + kOrdThreads - 1) / kOrdThreads;
-  const int bp = (p->L.cap + kOrdThreads - 1) / kOrdThreads;
-  hipLaunchKernelGGL(tile_order_count, dim3(bt + bp), dim3(kOrdThreads), 0, s, p->d, p->L.T, bt);
+  hipLaunchKernelGGL(tile_order_count, dim3(ord_blocks(p->L.cap)), dim3(kOrdThreads), 0, s, p->d);
   TCL_HIP(hipGetLastError());
   return TCL_OK;
 }

@@ -48,9 +48,10 @@ constexpr int kPlanLdsInts = 32768;
 // count for which a plan orders its tokens into such tiles.
 constexpr int kXTok = 64;
 constexpr int kMfmaMinTokens = 256;
-// Items (tokens, then tuples) per workgroup of the launch that flags the
-// tile order; each workgroup lists its flagged items in a slice this long.
+// Tuples per workgroup of the launch that flags the tile order; each
+// workgroup lists its flagged tokens in a slice this long.
 constexpr int kOrdThreads = 256;
+inline int ord_blocks(int cap) { return (cap + kOrdThreads - 1) / kOrdThreads; }
 
 // One apply launch covers up to kMaxMods modules that share the plan (e.g.
 // the seven projections of a transformer layer).

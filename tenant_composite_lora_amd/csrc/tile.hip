@@ -672,7 +672,7 @@ int launch_expand_tile(const tcl_plan *p, const tcl_module *mods, int n, float *
   e.jobs_per_xcd = int32_t((jobs + 7) / 8);
   e.ord_cnt = p->d.ord_cnt;
   e.ord_item = p->d.ord_item;
-  e.ord_blocks = (p->L.T + kOrdThreads - 1) / kOrdThreads + (p->L.cap + kOrdThreads - 1) / kOrdThreads;
+  e.ord_blocks = ord_blocks(p->L.cap);
   logf("expand(tile): modules=%d tiles=%d jobs=%lld", n, e.tiles, (long long)jobs);
   hipLaunchKernelGGL(tile_prep, dim3(n * e.tiles), dim3(256), 0, s, e);
   if (yd == TCL_BF16)

@@ -97,21 +97,14 @@ def _case(name):
 
 
 def tile_order(c):
-    """The plan's token order for the tiles: tokens with pairs, first those
-    whose rarest adapter (largest id of the composite) owns at least T / 64
-    tuples, in token order, then the others by (that adapter, token)."""
+    """The plan's token order for the tiles: tokens with pairs, grouped by
+    their rarest adapter (largest id of the composite), adapters ascending,
+    in token order within an adapter."""
     owner = np.repeat(np.arange(c.n_groups), np.diff(c.group_tok_ptr))
     comps = [sorted(int(a) for a in c.pair_adapter[c.group_pair_ptr[g]:c.group_pair_ptr[g + 1]])
              for g in owner]
-    seg = np.zeros(c.n_adapters, np.int64)
-    for cp in comps:
-        for a in cp:
-            seg[a] += 1
-    thr = max(c.n_tokens // 64, 1)
     busy = [t for t in range(c.n_tokens) if comps[t]]
-    common = [t for t in busy if seg[comps[t][-1]] >= thr]
-    rare = sorted((t for t in busy if seg[comps[t][-1]] < thr), key=lambda t: (comps[t][-1], t))
-    return common + rare, comps
+    return sorted(busy, key=lambda t: (comps[t][-1], t)), comps
 
 
 def tile_limits_hit(wl, mi=0):
