@@ -461,10 +461,10 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
   // XCD-aware job index: each XCD takes a contiguous range of jobs, which
   // run the tiles of one column block in turn (its packed B columns stay in
   // that XCD's L2).  A column block's tiles run last to first: the plan's
-  // tile order ends with the tokens grouped by a rare adapter, whose tiles
-  // have the widest unions (on the retained-rank batch about three times
-  // the K steps of the first tiles), so the jobs that start last, and set
-  // the kernel's tail, are the short ones.
+  // tile order groups the tokens by their rarest adapter, adapters
+  // ascending, so the later tiles, of rarer adapters, have the wider unions
+  // (on the retained-rank batch from 1 to 48 K steps), and the jobs that
+  // start last, and set the kernel's tail, are the short ones.
   const int job = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
   if (job >= e.jobs) return;
   int sel = 0;
