@@ -460,11 +460,9 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
   // XCD-aware job index: each XCD takes a contiguous range of jobs, which
   // run the tiles of one column block in turn (its packed B columns stay in
-  // that XCD's L2).  A column block's tiles run last to first: the plan's
-  // tile order groups the tokens by their rarest adapter, adapters
-  // ascending, so the later tiles, of rarer adapters, have the wider unions
-  // (on the retained-rank batch from 1 to 48 K steps), and the jobs that
-  // start last, and set the kernel's tail, are the short ones.
+  // that XCD's L2).  A column block's tiles run in the plan's tile order:
+  // tokens grouped by their rarest adapter, so neighbouring tiles, running
+  // together, share most of their unions' B octets in L2.
   const int job = (blockIdx.x & 7) * e.jobs_per_xcd + (blockIdx.x >> 3);
   if (job >= e.jobs) return;
   int sel = 0;
@@ -476,7 +474,7 @@ __global__ __launch_bounds__(256) void expand_tile(TileArgs e) {
   const uint4 *Bk = e.bk_data[sel];
   TY *Y = static_cast<TY *>(e.m[sel].io);
   const int local = job - first;
-  const int ct = local / e.tiles, tile = e.tiles - 1 - (local - ct * e.tiles);
+  const int ct = local / e.tiles, tile = local - ct * e.tiles;
   const int cw = ct * kXCols + 64 * w;
   const int32_t *rg = e.rec + (int64_t(sel) * e.tiles + tile) * kRWords;
   // header, tokens and slot counts, then the rest of the record that is in use
